@@ -1,0 +1,174 @@
+"""fp64 CPU oracle for the fused classifier-head + cross-entropy (CCE).
+
+TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import this package.  The HIP path never
+imports or calls it and shares no code with it; the two meet only in the
+seeded input generator.
+
+The arithmetic lives in cce_oracle.c (plain definition in double precision,
+see its header).  This wrapper converts the stored input bits to float64
+exactly, calls the C library, and sorts vocabulary keys with a library sort.
+
+Sources: the lit note "The loss and the mask: Cut Cross-Entropy +
+FlexAttention", section "Contribution"; the paper summary "Cut Your Losses in
+Large-Vocabulary Language Models", section "Approach".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libcce_oracle.so")
+_lib = None
+
+_d = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.POINTER(ctypes.c_int64)
+
+
+def build() -> str:
+    """Compile the C oracle with the host compiler (make)."""
+    subprocess.run(["make", "-s", "-C", _HERE], check=True)
+    return _LIB_PATH
+
+
+def use_library(path=None):
+    """Point the wrapper at another build of cce_oracle.c (the mutation tests
+    load deliberately broken copies); None restores the default library."""
+    global _lib, _lib_override
+    _lib_override = path
+    _lib = None
+
+
+_lib_override = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = _lib_override
+    if path is None:
+        path = _LIB_PATH
+        src = os.path.join(_HERE, "cce_oracle.c")
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(src):
+            build()
+    lib = ctypes.CDLL(path)
+    lib.cce_oracle_rows.argtypes = [_d, _d, _i64, _d, _i64, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_int64, _d, _d, _d]
+    lib.cce_oracle_rows.restype = ctypes.c_int
+    lib.cce_oracle_dE.argtypes = [_d, _d, _i64, _d, _d, ctypes.c_int64, _i64, ctypes.c_int64,
+                                  ctypes.c_int64, ctypes.c_int64, _d]
+    lib.cce_oracle_dE.restype = ctypes.c_int
+    lib.cce_oracle_mean_logit.argtypes = [_d, _d, _i64, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int64, _d]
+    lib.cce_oracle_mean_logit.restype = ctypes.c_int
+    lib.cce_oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.cce_oracle_max_threads.restype = ctypes.c_int
+    ncpu = len(os.sched_getaffinity(0))
+    lib.cce_oracle_set_threads(min(ncpu, 16))
+    _lib = lib
+    return lib
+
+
+def threads() -> int:
+    return _load().cce_oracle_max_threads()
+
+
+def set_threads(n: int) -> None:
+    _load().cce_oracle_set_threads(int(n))
+
+
+def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored input -> exact float64 values.  bf16 inputs arrive as uint16
+    bit patterns (the upper half of an IEEE float32)."""
+    if dtype == "bf16":
+        return (np.asarray(x).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "f64":
+        return np.ascontiguousarray(x, dtype=np.float64)
+    raise ValueError(dtype)
+
+
+def _p(a, t):
+    return a.ctypes.data_as(t)
+
+
+def _c64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def rows(H64, E64, labels, dloss, row_ids, ignore_index=-100, want_dH=True):
+    """lse, loss (and dH rows) for the listed rows; full logit rows in fp64."""
+    lib = _load()
+    H64, E64 = _c64(H64), _c64(E64)
+    N, D = H64.shape
+    V = E64.shape[0]
+    labels = np.ascontiguousarray(labels, dtype=np.int64)
+    dloss = _c64(np.zeros(N) if dloss is None else dloss)
+    row_ids = np.ascontiguousarray(row_ids, dtype=np.int64)
+    n = row_ids.size
+    lse = np.empty(n)
+    loss = np.empty(n)
+    dH = np.empty((n, D)) if want_dH else None
+    rc = lib.cce_oracle_rows(_p(H64, _d), _p(E64, _d), _p(labels, _i64), _p(dloss, _d),
+                             _p(row_ids, _i64), n, D, V, int(ignore_index),
+                             _p(lse, _d), _p(loss, _d), _p(dH, _d) if want_dH else None)
+    if rc != 0:
+        raise MemoryError("oracle: cannot allocate a logit row")
+    return lse, loss, dH
+
+
+def forward(H64, E64, labels, ignore_index=-100):
+    """Per-token loss and lse for every row (fp64)."""
+    N = H64.shape[0]
+    lse, loss, _ = rows(H64, E64, labels, None, np.arange(N), ignore_index, want_dH=False)
+    return loss, lse
+
+
+def dE_rows(H64, E64, labels, lse, dloss, vids, ignore_index=-100):
+    """Rows vids of dE = sum_i g_iv h_i, given every row's lse."""
+    lib = _load()
+    H64, E64 = _c64(H64), _c64(E64)
+    N, D = H64.shape
+    labels = np.ascontiguousarray(labels, dtype=np.int64)
+    lse, dloss = _c64(lse), _c64(dloss)
+    vids = np.ascontiguousarray(vids, dtype=np.int64)
+    out = np.empty((vids.size, D))
+    lib.cce_oracle_dE(_p(H64, _d), _p(E64, _d), _p(labels, _i64), _p(lse, _d), _p(dloss, _d), N,
+                      _p(vids, _i64), vids.size, D, int(ignore_index), _p(out, _d))
+    return out
+
+
+def backward(H64, E64, labels, dloss, ignore_index=-100):
+    """Full forward + unfiltered gradient: loss, lse, dH [N,D], dE [V,D] (fp64)."""
+    N = H64.shape[0]
+    V = E64.shape[0]
+    lse, loss, dH = rows(H64, E64, labels, dloss, np.arange(N), ignore_index, want_dH=True)
+    dE = dE_rows(H64, E64, labels, lse, dloss, np.arange(V), ignore_index)
+    return loss, lse, dH, dE
+
+
+def mean_logit(H64, E64, labels, ignore_index=-100):
+    """key_v = mean over non-ignored rows of z_iv (fp64, from the definition)."""
+    lib = _load()
+    H64, E64 = _c64(H64), _c64(E64)
+    N, D = H64.shape
+    V = E64.shape[0]
+    labels = np.ascontiguousarray(labels, dtype=np.int64)
+    key = np.empty(V)
+    lib.cce_oracle_mean_logit(_p(H64, _d), _p(E64, _d), _p(labels, _i64), N, D, V,
+                              int(ignore_index), _p(key, _d))
+    return key
+
+
+def vocab_order(keys):
+    """Vocabulary permutation: descending key, ties by ascending id (a stable
+    sort).  perm[k] is the original id at sorted position k."""
+    keys = np.asarray(keys)
+    ids = np.arange(keys.size)
+    return np.lexsort((ids, -keys)).astype(np.int64)
