@@ -1,0 +1,192 @@
+"""Benchmark: fwd+bwd tokens/s of the fused classifier head + cross-entropy at
+the Gemma-2-2B head shape (N = 8192 tokens, D = 2304, V = 256 000, bf16,
+peaked softmax, Zipf labels, gradient filter at 2^-12) on one MI355X, and the
+fraction of the bf16 dense MFMA peak its dominant kernel reaches.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+One step = cce_forward + cce_backward (dloss = 1 / N_valid) on inputs that
+are already resident in device memory; warm-up steps are not timed.  The
+dominant kernel is the forward logit/log-sum-exp kernel; its duration is
+taken with HIP events around cce_forward on the stream the work is enqueued
+on (the bracket also holds the valid-row compaction and the ordered merge,
+two single-pass kernels of a few microseconds).  The CPU baseline times the
+fp64 oracle on a bounded sample of rows of the same workload.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (published)
+METRIC = "fwd+bwd tokens/sec of fused linear-CE at Gemma-2-2B shape; % MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, help="1..5 (2 = Gemma-2-2B head)")
+    ap.add_argument("--eps", type=float, default=None, help="filter threshold (default: the workload's)")
+    ap.add_argument("--sort", action="store_true", help="vocabulary sort before the backward")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = about 20 s of work)")
+    return ap.parse_args()
+
+
+def cpu_baseline(x, n_rows_hint):
+    """The fp64 oracle, as it stands, on a sample of rows: their lse, loss,
+    dH rows, and their contributions to every dE row (the whole backward of
+    those rows).  Scaled to tokens/s."""
+    import numpy as np
+
+    import oracle
+    H64 = oracle.as_f64(x.H, x.dtype)
+    E64 = oracle.as_f64(x.E, x.dtype)
+    threads = oracle.threads()
+    per_row_flops = 8.0 * x.D * x.V  # logits twice, dH row, dE contributions
+    rows_n = n_rows_hint or max(threads, int(round(20.0 * threads * 1.2e9 / per_row_flops)))
+    rows_n = max(1, min(rows_n, x.N))
+    rng = np.random.default_rng(0)
+    valid = np.nonzero(x.labels != x.ignore_index)[0]
+    rows = np.sort(rng.choice(valid, size=min(rows_n, valid.size), replace=False))
+    dl = np.full(x.N, 1.0 / max(x.n_valid, 1))
+    t0 = time.perf_counter()
+    lse, loss, dH = oracle.rows(H64, E64, x.labels, dl, rows, x.ignore_index)
+    sub_lse = np.zeros(x.N)
+    sub_lse[rows] = lse
+    sub_labels = np.full(x.N, x.ignore_index, dtype=np.int64)
+    sub_labels[rows] = x.labels[rows]
+    # dE contributions of the sampled rows only: rows outside the sample are ignored
+    Hs = H64[rows]
+    dE = oracle.dE_rows(Hs, E64, sub_labels[rows], sub_lse[rows], dl[rows], np.arange(x.V), x.ignore_index)
+    t = time.perf_counter() - t0
+    del dE, dH
+    return {"value": len(rows) / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {x.N} rows (full D={x.D}, V={x.V}): lse, loss, dH rows and their dE "
+                      f"contributions over all V, fp64, {t:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from linear_cross_entropy_cce_amd import binding as B
+    from linear_cross_entropy_cce_amd import inputs
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    print(f"[bench] generating workload {a.workload}", file=sys.stderr, flush=True)
+    x = inputs.make_workload(a.workload)
+    eps = x.eps if a.eps is None else a.eps
+    to = (lambda arr: torch.from_numpy(arr).view(torch.bfloat16).to(dev)) if x.dtype == "bf16" else \
+        (lambda arr: torch.from_numpy(arr).to(dev))
+    H, E = to(x.H), to(x.E)
+    y = torch.from_numpy(x.labels).to(dev)
+    N, D, V = x.N, x.D, x.V
+    nv = x.n_valid
+    dt = B.CCE_BF16 if x.dtype == "bf16" else B.CCE_F32
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    dl = torch.from_numpy(np.where(x.labels != x.ignore_index, 1.0 / max(nv, 1), 0.0).astype(np.float32)).to(dev)
+    dH = torch.empty_like(H)
+    dE = torch.empty_like(E)
+    stats = torch.zeros(4, dtype=torch.int64, device=dev)
+    ws_f = torch.empty(B.forward_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(B.backward_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(B.vocab_order_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev) if a.sort else None
+    perm = torch.empty(V, dtype=torch.int32, device=dev) if a.sort else None
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        B.cce_forward(H, E, y, x.ignore_index, loss=loss, lse=lse, ws=ws_f)
+        if ev is not None:
+            ev[1].record(stream)
+        if a.sort:
+            B.cce_vocab_order(H, E, y, x.ignore_index, perm=perm, ws=ws_s)
+        B.cce_backward(H, E, y, lse, dl, eps, x.ignore_index, perm, 0, dH=dH, dE=dE, stats=stats, ws=ws_b)
+        if ev is not None:
+            ev[2].record(stream)
+
+    print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(a.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = wall * 1e3 / a.steps
+    st = stats.cpu().numpy()
+    n_live, n_label, n_total = int(st[0]), int(st[1]), int(st[2])
+    br, bv = B.filter_block()
+    # algorithmic work: logits twice, dH and dE on kept blocks
+    f_logits = 2.0 * nv * D * V
+    kept_cols = (n_live + n_label) * br * bv  # upper bound on kept (row, vocab) pairs
+    f_exec = 2 * f_logits + 4.0 * D * kept_cols
+    peak = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_FP32_TFLOPS
+    fwd_avg = float(np.mean(fwd_ms))
+    achieved = f_logits / (fwd_avg * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": N / (step_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": x.dtype,
+        "data": "synthetic (seeded; head shape of the named model, random values)",
+        "config": {"workload": f"{x.name} (N={N}, D={D}, V={V}, {x.dtype}, eps={eps:g}, sort={a.sort})",
+                   "N": N, "D": D, "V": V, "n_valid": nv, "filter_eps": eps, "sort_vocab": a.sort,
+                   "filter_block": [br, bv]},
+        "roofline": {"kernel": "k_fwd (cce_forward bracket)", "bound": "mfma", "achieved": achieved,
+                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None},
+        "detail": {
+            "fwd_ms_mean": fwd_avg, "bwd_ms_mean": float(np.mean(bwd_ms)),
+            "fwd_ms_min": float(np.min(fwd_ms)), "bwd_ms_min": float(np.min(bwd_ms)),
+            "blocks_softmax_kept": n_live, "blocks_label_only": n_label, "blocks_total": n_total,
+            "kept_frac": (n_live + n_label) / max(n_total, 1),
+            "F_exec_TF": f_exec / 1e12, "F_exec_frac_peak": f_exec / (step_ms * 1e-3) / (peak * 1e12),
+            "F6_TF": (f_logits + 4.0 * D * kept_cols) / 1e12,
+            "workspace_MB": (ws_f.numel() + ws_b.numel()) / 1e6,
+            "extra_alloc_MB": (torch.cuda.max_memory_allocated() - mem0) / 1e6,
+            "valid_tokens_per_s": nv / (step_ms * 1e-3),
+        },
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(x, a.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

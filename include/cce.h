@@ -1,0 +1,156 @@
+/*
+ * cce.h -- C ABI of libcce.so: fused classifier-head matmul + cross-entropy
+ * ("Cut Cross-Entropy", CCE) forward and backward on one AMD MI355X (gfx950).
+ *
+ * What is computed (per non-ignored row i, classifier row e_v, label y_i):
+ *   z_iv   = <h_i, e_v>                       (never stored in device memory)
+ *   lse_i  = log sum_v exp(z_iv)
+ *   loss_i = lse_i - z_{i,y_i}
+ *   dH_i   = sum_v g_iv e_v,   dE_v = sum_i g_iv h_i,
+ *   g_iv   = dloss_i * (p_iv * [block(i,v) survives] - [v == y_i]),
+ *   p_iv   = exp(z_iv - lse_i).
+ * Cross-entropy needs only the correct-token logit (an indexed matmul) and the
+ * log-sum-exp over the vocabulary, computed blockwise on chip without writing
+ * the [rows x vocabulary] product to memory (lit note "The loss and the mask:
+ * Cut Cross-Entropy + FlexAttention", section "Contribution").  The backward
+ * recomputes logits blockwise and skips blocks whose softmax entries all fall
+ * below a threshold (gradient filtering; a vocabulary sort clusters the
+ * surviving blocks) -- CCE paper summary "Cut Your Losses in Large-Vocabulary
+ * Language Models", section "Approach".  The classifier gradient is
+ * accumulated across blocks with Kahan compensation (same summary, section
+ * "Limitations").
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer is a DEVICE pointer owned by the caller, except where a
+ *    comment says otherwise.  The library allocates and frees nothing and keeps
+ *    no mutable global state; calls are reentrant.  Calls that run at the same
+ *    time must not share a workspace.
+ *  - H is [N, D] and E is [V, D], row-major with D innermost, both of one dtype
+ *    (cce_dtype).  D % 8 == 0; H, E, dH, dE and the workspace are 16-byte
+ *    aligned.  1 <= N < 2^31, 1 <= V < 2^31, 8 <= D <= 65536.
+ *  - labels are int64 [N]; a row whose label equals ignore_index is ignored.
+ *    Any other label outside [0, V) is undefined behaviour (cce_check_labels
+ *    detects it).
+ *  - loss, lse and dloss are fp32 [N].  dH and dE take the input dtype and are
+ *    overwritten (not accumulated into).
+ *  - stream is a hipStream_t passed as void* (NULL = the default stream).  All
+ *    work is enqueued on it; no entry point synchronises the host.
+ *  - Errors in the arguments are reported before any work is enqueued, and the
+ *    outputs are then left untouched.  CCE_ERR_HIP reports a failed launch.
+ *    Faults inside a kernel surface at the caller's next synchronisation, as
+ *    for any asynchronous HIP work.
+ *  - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef CCE_H_
+#define CCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CCE_OK = 0,
+    CCE_ERR_NULL = 1,       /* a required pointer is NULL */
+    CCE_ERR_SHAPE = 2,      /* N, D or V out of the supported range */
+    CCE_ERR_DTYPE = 3,      /* unknown cce_dtype */
+    CCE_ERR_ALIGN = 4,      /* a pointer is not 16-byte aligned */
+    CCE_ERR_WORKSPACE = 5,  /* workspace smaller than the *_workspace_bytes query */
+    CCE_ERR_HIP = 6,        /* a HIP launch failed */
+    CCE_ERR_ARG = 7         /* another argument is invalid (e.g. NaN or negative filter_eps) */
+} cce_status;
+
+typedef enum { CCE_F32 = 0, CCE_BF16 = 1 } cce_dtype;
+
+/* cce_backward flags. */
+#define CCE_BWD_NO_KAHAN 1u /* plain fp32 accumulation of dE across blocks (numerics studies) */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *cce_status_string(cce_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int cce_version(void);
+
+/*
+ * Block geometry of the gradient filter, written to host ints (either may be
+ * NULL): rows (valid tokens, in order) x vocabulary entries (in processing
+ * order: sorted order when a permutation is given) per filter block.
+ */
+void cce_filter_block(int *block_rows, int *block_vocab);
+
+/* Workspace bytes for cce_forward with these sizes (0 on invalid sizes). */
+size_t cce_forward_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtype dtype);
+
+/* Workspace bytes for cce_backward with these sizes (0 on invalid sizes).
+ * It grows linearly in N and in V: a fixed-width slice of the logit gradient
+ * (rows x a bounded number of vocabulary columns) and fp32 dH accumulators;
+ * never rows x vocabulary. */
+size_t cce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtype dtype);
+
+/* Workspace bytes for cce_vocab_order (0 on invalid sizes). */
+size_t cce_vocab_order_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtype dtype);
+
+/*
+ * Forward: loss[i] and lse[i] for every row (fp32, device, [N]).
+ * Ignored rows get loss = lse = 0.  The log-sum-exp is accumulated per
+ * vocabulary split on chip (online max / sum-exp) and the splits are merged in
+ * a fixed order, so the result does not depend on scheduling.
+ * ws: device scratch of at least cce_forward_workspace_bytes bytes.
+ */
+cce_status cce_forward(const void *H, const void *E, const int64_t *labels,
+                       int64_t N, int64_t D, int64_t V, cce_dtype dtype,
+                       int64_t ignore_index, float *loss, float *lse,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Vocabulary order for the backward (optional): key_v = mean over
+ * non-ignored rows of z_iv = <mean_i h_i, e_v>, sorted descending, ties by
+ * ascending id (stable).  perm[k] (int32, device, [V]) receives the original
+ * id at sorted position k.  keys (fp32, device, [V]) may be NULL; if given it
+ * receives key_v indexed by original id.  With no valid row all keys are 0 and
+ * perm is the identity.
+ * The lit note's "Contribution": a vocabulary sort groups the surviving
+ * blocks so that skipping at block granularity pays.
+ */
+cce_status cce_vocab_order(const void *H, const void *E, const int64_t *labels,
+                           int64_t N, int64_t D, int64_t V, cce_dtype dtype,
+                           int64_t ignore_index, int32_t *perm, float *keys,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward: dH [N, D] and dE [V, D] (input dtype, device) of
+ * L = sum_i dloss[i] * loss_i, given lse from cce_forward.
+ *  - dloss: fp32 [N]; it carries the caller's reduction (1/N_valid for a mean).
+ *  - filter_eps >= 0: a filter block (see cce_filter_block) is skipped when
+ *    every p_iv in it is < filter_eps; 0 disables filtering.  Only the
+ *    softmax part is filtered: the -dloss_i at (i, y_i) is always applied.
+ *  - perm: NULL, or the permutation from cce_vocab_order (int32 [V]); it only
+ *    changes which vocabulary entries share a filter block.
+ *  - flags: 0 or CCE_BWD_NO_KAHAN.
+ *  - stats: NULL, or device int64 [4] that receives (softmax-surviving blocks,
+ *    label-only blocks, total blocks, valid rows).
+ * Ignored rows get dH = 0 and add nothing to dE.
+ * ws: device scratch of at least cce_backward_workspace_bytes bytes.
+ */
+cce_status cce_backward(const void *H, const void *E, const int64_t *labels,
+                        const float *lse, const float *dloss,
+                        int64_t N, int64_t D, int64_t V, cce_dtype dtype,
+                        int64_t ignore_index, float filter_eps,
+                        const int32_t *perm, unsigned flags,
+                        void *dH, void *dE, int64_t *stats,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Debug check of the labels: *n_bad (device int64) receives the number of rows
+ * whose label is neither ignore_index nor in [0, V).
+ */
+cce_status cce_check_labels(const int64_t *labels, int64_t N, int64_t V,
+                            int64_t ignore_index, int64_t *n_bad, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCE_H_ */

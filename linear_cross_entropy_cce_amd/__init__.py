@@ -1,6 +1,19 @@
 """MI355X-native fused classifier-head + cross-entropy (Cut Cross-Entropy).
 
 The compute path is the HIP library libcce.so (hand-written gfx950 kernels
-behind a C ABI declared in include/cce.h); the Python layer only marshals
-arguments and allocates device memory through PyTorch.
+behind the C ABI declared in include/cce.h); the Python layer only marshals
+arguments and allocates device memory through PyTorch.  Nothing here falls
+back to another implementation: without the library every call raises.
 """
+from .binding import (CCEError, cce_backward, cce_check_labels, cce_forward,  # noqa: F401
+                      cce_vocab_order, filter_block)
+from .inputs import IGNORE_INDEX  # noqa: F401
+
+
+def linear_cross_entropy(*args, **kwargs):
+    from .autograd import linear_cross_entropy as f
+    return f(*args, **kwargs)
+
+
+__all__ = ["cce_forward", "cce_backward", "cce_vocab_order", "cce_check_labels", "filter_block",
+           "linear_cross_entropy", "CCEError", "IGNORE_INDEX"]

@@ -1,0 +1,52 @@
+"""PyTorch autograd wrapper over the C ABI: a drop-in for
+cross_entropy(H @ E.T, labels) that never forms the logits.
+
+The per-token loss comes from cce_forward; the reduction is the caller's
+and reaches the backward as dloss (mean over non-ignored rows, or sum).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding
+
+
+class _LinearCrossEntropy(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, H, E, labels, ignore_index, filter_eps, sort_vocab):
+        loss, lse = binding.cce_forward(H, E, labels, ignore_index)
+        ctx.save_for_backward(H, E, labels, lse)
+        ctx.ignore_index = ignore_index
+        ctx.filter_eps = filter_eps
+        ctx.sort_vocab = sort_vocab
+        ctx.mark_non_differentiable(lse)
+        return loss, lse
+
+    @staticmethod
+    def backward(ctx, dloss, _dlse):
+        H, E, labels, lse = ctx.saved_tensors
+        perm = binding.cce_vocab_order(H, E, labels, ctx.ignore_index) if ctx.sort_vocab else None
+        dH, dE = binding.cce_backward(H, E, labels, lse, dloss.float().contiguous(), ctx.filter_eps,
+                                      ctx.ignore_index, perm)
+        return dH, dE, None, None, None, None
+
+
+def linear_cross_entropy(H, E, labels, ignore_index=-100, reduction="mean", filter_eps=2.0 ** -12,
+                         sort_vocab=False):
+    """Cross-entropy of the logits H @ E.T against labels, without the logits.
+
+    H [N, D] and E [V, D] (bf16 or fp32, on the GPU); labels int64 [N].
+    reduction: "none" (per-token fp32 loss), "sum", or "mean" over the rows
+    whose label is not ignore_index.  filter_eps: gradient-filter threshold
+    (0 disables filtering).  sort_vocab: reorder the vocabulary by mean logit
+    before the backward so that surviving blocks cluster.
+    """
+    loss, _ = _LinearCrossEntropy.apply(H, E, labels, int(ignore_index), float(filter_eps), bool(sort_vocab))
+    if reduction == "none":
+        return loss
+    if reduction == "sum":
+        return loss.sum()
+    if reduction == "mean":
+        n = (labels != ignore_index).sum().clamp_min(1)
+        return loss.sum() / n
+    raise ValueError(f"unknown reduction {reduction!r}")

@@ -1,0 +1,210 @@
+"""ctypes binding of libcce.so, with the C ABI's names (include/cce.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the ABI.  PyTorch supplies device memory (outputs and
+workspace) and the current stream.  If the library is missing or cannot be
+loaded, every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcce.so")
+
+CCE_OK = 0
+CCE_ERR_NULL = 1
+CCE_ERR_SHAPE = 2
+CCE_ERR_DTYPE = 3
+CCE_ERR_ALIGN = 4
+CCE_ERR_WORKSPACE = 5
+CCE_ERR_HIP = 6
+CCE_ERR_ARG = 7
+
+CCE_F32 = 0
+CCE_BF16 = 1
+
+CCE_BWD_NO_KAHAN = 1
+
+# Every entry point include/cce.h declares.
+EXPORTS = (
+    "cce_status_string", "cce_version", "cce_filter_block",
+    "cce_forward_workspace_bytes", "cce_backward_workspace_bytes", "cce_vocab_order_workspace_bytes",
+    "cce_forward", "cce_vocab_order", "cce_backward", "cce_check_labels",
+)
+
+
+class CCEError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcce.so (built in-tree by linear_cross_entropy_cce_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libcce.so not found at {LIB_PATH}; build it with "
+                           "`python -m linear_cross_entropy_cce_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.cce_status_string.argtypes = [ctypes.c_int]
+    L.cce_status_string.restype = ctypes.c_char_p
+    L.cce_version.restype = ctypes.c_int
+    L.cce_filter_block.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    L.cce_filter_block.restype = None
+    for f in ("cce_forward_workspace_bytes", "cce_backward_workspace_bytes", "cce_vocab_order_workspace_bytes"):
+        getattr(L, f).argtypes = [_i64, _i64, _i64, ctypes.c_int]
+        getattr(L, f).restype = ctypes.c_size_t
+    L.cce_forward.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp,
+                              ctypes.c_size_t, _vp]
+    L.cce_forward.restype = ctypes.c_int
+    L.cce_vocab_order.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp,
+                                  ctypes.c_size_t, _vp]
+    L.cce_vocab_order.restype = ctypes.c_int
+    L.cce_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _i64, ctypes.c_float,
+                               _vp, ctypes.c_uint, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.cce_backward.restype = ctypes.c_int
+    L.cce_check_labels.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp]
+    L.cce_check_labels.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(s: int) -> str:
+    return lib().cce_status_string(int(s)).decode()
+
+
+def _check(fn, s):
+    if s != CCE_OK:
+        raise CCEError(fn, s, status_string(s))
+
+
+def version() -> int:
+    return lib().cce_version()
+
+
+def filter_block() -> tuple[int, int]:
+    """(rows, vocabulary entries) of one gradient-filter block."""
+    r, v = ctypes.c_int(), ctypes.c_int()
+    lib().cce_filter_block(ctypes.byref(r), ctypes.byref(v))
+    return r.value, v.value
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return CCE_BF16
+    if t.dtype == torch.float32:
+        return CCE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def forward_workspace_bytes(N, D, V, dtype_code) -> int:
+    return lib().cce_forward_workspace_bytes(N, D, V, dtype_code)
+
+
+def backward_workspace_bytes(N, D, V, dtype_code) -> int:
+    return lib().cce_backward_workspace_bytes(N, D, V, dtype_code)
+
+
+def vocab_order_workspace_bytes(N, D, V, dtype_code) -> int:
+    return lib().cce_vocab_order_workspace_bytes(N, D, V, dtype_code)
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _workspace(nbytes, device, ws):
+    import torch
+    if ws is not None:
+        return ws
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _shapes(H, E, labels):
+    if H.dim() != 2 or E.dim() != 2 or H.shape[1] != E.shape[1]:
+        raise ValueError(f"H must be [N, D] and E [V, D]; got {tuple(H.shape)} and {tuple(E.shape)}")
+    if H.dtype != E.dtype:
+        raise TypeError("H and E must share one dtype")
+    if labels.dim() != 1 or labels.shape[0] != H.shape[0]:
+        raise ValueError("labels must be [N]")
+    for name, t in (("H", H), ("E", E), ("labels", labels)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    import torch
+    if labels.dtype != torch.int64:
+        raise TypeError("labels must be int64")
+    return H.shape[0], H.shape[1], E.shape[0]
+
+
+def cce_forward(H, E, labels, ignore_index=-100, loss=None, lse=None, ws=None, stream=None):
+    """loss, lse (fp32 [N]) of the fused head + cross-entropy."""
+    import torch
+    N, D, V = _shapes(H, E, labels)
+    dt = _dtype_code(H)
+    loss = torch.empty(N, dtype=torch.float32, device=H.device) if loss is None else loss
+    lse = torch.empty(N, dtype=torch.float32, device=H.device) if lse is None else lse
+    need = forward_workspace_bytes(N, D, V, dt)
+    ws = _workspace(need, H.device, ws)
+    s = lib().cce_forward(_ptr(H), _ptr(E), _ptr(labels), N, D, V, dt, int(ignore_index), _ptr(loss), _ptr(lse),
+                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("cce_forward", s)
+    return loss, lse
+
+
+def cce_vocab_order(H, E, labels, ignore_index=-100, perm=None, keys=None, want_keys=False, ws=None, stream=None):
+    """perm (int32 [V]): vocabulary ids by descending mean logit (stable)."""
+    import torch
+    N, D, V = _shapes(H, E, labels)
+    dt = _dtype_code(H)
+    perm = torch.empty(V, dtype=torch.int32, device=H.device) if perm is None else perm
+    if want_keys and keys is None:
+        keys = torch.empty(V, dtype=torch.float32, device=H.device)
+    ws = _workspace(vocab_order_workspace_bytes(N, D, V, dt), H.device, ws)
+    s = lib().cce_vocab_order(_ptr(H), _ptr(E), _ptr(labels), N, D, V, dt, int(ignore_index), _ptr(perm),
+                              _ptr(keys), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("cce_vocab_order", s)
+    return (perm, keys) if want_keys else perm
+
+
+def cce_backward(H, E, labels, lse, dloss, filter_eps=2.0 ** -12, ignore_index=-100, perm=None, flags=0,
+                 dH=None, dE=None, stats=None, ws=None, stream=None):
+    """dH [N, D], dE [V, D] (input dtype) of sum_i dloss_i loss_i."""
+    import torch
+    N, D, V = _shapes(H, E, labels)
+    dt = _dtype_code(H)
+    dH = torch.empty_like(H) if dH is None else dH
+    dE = torch.empty_like(E) if dE is None else dE
+    ws = _workspace(backward_workspace_bytes(N, D, V, dt), H.device, ws)
+    s = lib().cce_backward(_ptr(H), _ptr(E), _ptr(labels), _ptr(lse), _ptr(dloss), N, D, V, dt, int(ignore_index),
+                           float(filter_eps), _ptr(perm), int(flags), _ptr(dH), _ptr(dE), _ptr(stats), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(stream))
+    _check("cce_backward", s)
+    return dH, dE
+
+
+def cce_check_labels(labels, V, ignore_index=-100, stream=None) -> int:
+    """Number of labels neither ignore_index nor in [0, V)."""
+    import torch
+    n_bad = torch.empty(1, dtype=torch.int64, device=labels.device)
+    s = lib().cce_check_labels(_ptr(labels), labels.shape[0], int(V), int(ignore_index), _ptr(n_bad),
+                               _stream(stream))
+    _check("cce_check_labels", s)
+    return int(n_bad.item())

@@ -1,0 +1,108 @@
+// Host-side plumbing shared by the launch code and the C ABI of libcce.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "cce.h"
+
+namespace cce {
+
+// Filter block = tile of the logit kernels: kBlockVocab vocabulary entries
+// (MFMA M side) x kBlockRows valid tokens (MFMA N side).
+constexpr int kBlockVocab = 128;
+constexpr int kBlockRows = 128;
+// The backward materialises the logit gradient for at most this many
+// vocabulary columns at a time (a multiple of kBlockVocab).
+constexpr int kChunkVocab = 8192;
+// Upper bound on the forward's vocabulary splits (merged per row in order).
+constexpr int kMaxSplits = 64;
+// Workgroups the forward aims to launch (several per compute unit).
+constexpr int kFwdTargetGroups = 1024;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Carves a caller workspace into aligned regions (or only sizes it when the
+// base is null).
+struct Carver {
+    char *base;
+    size_t off = 0;
+    explicit Carver(void *b) : base(static_cast<char *>(b)) {}
+    template <typename T>
+    T *take(size_t count) {
+        T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+        off = align256(off + count * sizeof(T));
+        return p;
+    }
+};
+
+struct FwdShape {
+    int64_t N, D, V;
+    int n_vtiles;  // vocabulary tiles of kBlockVocab
+    int n_rtiles;  // token tiles of kBlockRows (upper bound, from N)
+    int S;         // vocabulary splits
+};
+FwdShape fwd_shape(int64_t N, int64_t D, int64_t V);
+
+struct FwdWs {
+    int32_t *idx;      // [N] compacted valid-row indices
+    int32_t *nvalid;   // [1]
+    float *part_m;     // [S, N] running max (log2 units)
+    float *part_s;     // [S, N] running sum of 2^(z log2e - m)
+};
+FwdWs fwd_ws(void *ws, const FwdShape &s, size_t *bytes);
+
+struct BwdShape {
+    int64_t N, D, V;
+    int64_t Np;        // N rounded up to kBlockRows
+    int Vc;            // vocabulary columns per chunk (multiple of kBlockVocab)
+    int n_chunks;
+    int n_rtiles;
+};
+BwdShape bwd_shape(int64_t N, int64_t D, int64_t V);
+
+struct BwdWs {
+    int32_t *idx;      // [N]
+    int32_t *nvalid;   // [1]
+    int32_t *inv_perm; // [V] processing position of each vocabulary id
+    uint8_t *live;     // [n_rtiles, Vc / kBlockVocab] block status of the current chunk
+    float *dh_acc;     // [Np, D] fp32 dH accumulators (valid-row order)
+    void *Ht;          // [D, Np] valid rows of H, transposed
+    void *Gt;          // [Vc, Np] logit gradient of the chunk, vocabulary-major
+    void *Gn;          // [Np, Vc] the same, row-major
+    void *Et;          // [D, Vc] classifier rows of the chunk, transposed
+};
+BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes);
+
+struct SortWs {
+    float *hsum_part;  // [P, D] partial column sums of valid H rows
+    float *hbar;       // [D]
+    float *keys;       // [V]
+    uint32_t *ukeys[2];
+    int32_t *vals[2];
+    uint32_t *hist;    // [tiles * 256]
+    int32_t *idx;      // [N] compacted valid-row indices
+    int32_t *nvalid;   // [1]
+};
+SortWs sort_ws(void *ws, int64_t N, int64_t D, int64_t V, size_t *bytes);
+
+// ---- launchers (return hipGetLastError() after enqueuing) ----
+hipError_t launch_compact(const int64_t *labels, int64_t N, int64_t ignore_index, int32_t *idx,
+                          int32_t *nvalid, hipStream_t st);
+hipError_t launch_check_labels(const int64_t *labels, int64_t N, int64_t V, int64_t ignore_index,
+                               int64_t *n_bad, hipStream_t st);
+hipError_t launch_forward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
+                          const FwdShape &s, int64_t ignore_index, const FwdWs &w, float *loss,
+                          float *lse, hipStream_t st);
+hipError_t launch_backward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
+                           const float *lse, const float *dloss, const BwdShape &s,
+                           int64_t ignore_index, float eps, const int32_t *perm, unsigned flags,
+                           void *dH, void *dE, int64_t *stats, const BwdWs &w, hipStream_t st);
+hipError_t launch_vocab_order(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
+                              int64_t N, int64_t D, int64_t V, int64_t ignore_index, int32_t *perm,
+                              float *keys_out, const SortWs &w, hipStream_t st);
+
+}  // namespace cce

@@ -1,0 +1,309 @@
+// Forward of the fused classifier-head + cross-entropy on gfx950.
+//
+//  k_compact      valid-row compaction (rows whose label is not ignore_index)
+//  k_fwd          logit tiles Z^T = E_tile * H_tile^T on bf16/fp32 MFMA, kept in
+//                 registers; per token and vocabulary split an online running
+//                 max / sum-exp (log2 domain); partials written per split
+//  k_merge        per row: merge of the split partials in split order -> lse;
+//                 label logit <h_i, e_{y_i}> (the indexed matmul) -> loss
+//
+// The method: cross-entropy needs only the correct-token logit and the
+// log-sum-exp over the vocabulary, computed blockwise on chip while streaming
+// vocabulary tiles, never writing the [rows x vocabulary] logits to memory
+// (lit note "The loss and the mask: Cut Cross-Entropy + FlexAttention",
+// section "Contribution"; CCE paper summary "Cut Your Losses in
+// Large-Vocabulary Language Models", section "Approach").  The pages' kernel
+// merges partial results with a concurrent log-add-exp at block granularity
+// (summary, section "Limitations"); here the partials of each vocabulary split
+// go to a small [splits x rows] buffer and one ordered pass merges them, so
+// the result is independent of scheduling.
+#include "cce_device.hpp"
+#include "cce_internal.hpp"
+
+namespace cce {
+
+using TileFR = Tile<kBlockVocab, kBlockRows, 2, 2>;  // A = vocabulary rows, B = token rows
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ------------------------------------------------------------- compaction
+// One workgroup of 1024 threads; thread t owns a contiguous segment of rows.
+__global__ __launch_bounds__(1024) void k_compact(const int64_t *__restrict__ labels, int64_t N,
+                                                  int64_t ignore_index, int32_t *__restrict__ idx,
+                                                  int32_t *__restrict__ nvalid) {
+    __shared__ int wave_tot[16];
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int64_t seg = (N + 1023) / 1024;
+    const int64_t r0 = t * seg;
+    const int64_t r1 = r0 + seg < N ? r0 + seg : N;
+    int cnt = 0;
+    for (int64_t r = r0; r < r1; ++r) cnt += labels[r] != ignore_index;
+    // inclusive scan of cnt inside the wave
+    int x = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wave_tot[wave] = x;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += wave_tot[w];
+    int pos = base + x - cnt;
+    for (int64_t r = r0; r < r1; ++r)
+        if (labels[r] != ignore_index) idx[pos++] = (int32_t)r;
+    if (t == 1023) *nvalid = base + x;
+}
+
+// -------------------------------------------------------------- label check
+__global__ __launch_bounds__(1024) void k_check_labels(const int64_t *__restrict__ labels, int64_t N,
+                                                       int64_t V, int64_t ignore_index,
+                                                       int64_t *__restrict__ n_bad) {
+    __shared__ int64_t part[16];
+    int64_t c = 0;
+    for (int64_t r = threadIdx.x; r < N; r += 1024) {
+        const int64_t y = labels[r];
+        c += (y != ignore_index) && (y < 0 || y >= V);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int64_t s = 0;
+        for (int w = 0; w < 16; ++w) s += part[w];
+        *n_bad = s;
+    }
+}
+
+// ------------------------------------------------------------ logit + LSE
+// Workgroup (split s, token tile rt) streams the vocabulary tiles of split s.
+// Each lane owns TN token columns; for each it keeps m (running max of
+// z log2 e) and l (running sum of 2^(z log2 e - m)) over the vocabulary rows
+// it holds.  At the end the two half-waves and the WM waves that hold the same
+// tokens are merged in a fixed order.
+template <typename T>
+__global__ __launch_bounds__(TileFR::kThreads) void k_fwd(
+    const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ nvalid_p, int D, int V, int64_t N, int n_vtiles, int S,
+    float *__restrict__ part_m, float *__restrict__ part_s) {
+    using TL = TileFR;
+    __shared__ u32x4 lds[TL::kLdsChunks];
+    const int nv = *nvalid_p;
+    const int split = blockIdx.x % S;
+    const int rt = blockIdx.x / S;
+    const int tok0 = rt * TL::BN;
+    if (tok0 >= nv) return;
+    const int t0 = (int)((int64_t)n_vtiles * split / S);
+    const int t1 = (int)((int64_t)n_vtiles * (split + 1) / S);
+    const int tid = threadIdx.x;
+    const size_t rowb = (size_t)D * sizeof(T);
+    const int kvalid = D * (int)sizeof(T);
+    const int nsteps = (kvalid + TL::kStageBytes - 1) / TL::kStageBytes;
+
+    Stager<TL::kALoads, TL::kBLoads> st;
+    stager_slots<TL>(st, tid);
+#pragma unroll
+    for (int j = 0; j < TL::kBLoads; ++j) {
+        const int tok = tok0 + stage_row_b<TL>(tid, j);
+        st.b[j] = tok < nv ? reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb : nullptr;
+    }
+
+    float m[TL::TN], l[TL::TN];
+#pragma unroll
+    for (int tn = 0; tn < TL::TN; ++tn) { m[tn] = kNegInf; l[tn] = 0.f; }
+
+    f32x16 acc[TL::TM][TL::TN];
+    for (int vt = t0; vt < t1; ++vt) {
+        const int v0 = vt * TL::BM;
+#pragma unroll
+        for (int j = 0; j < TL::kALoads; ++j) {
+            const int v = v0 + stage_row_a<TL>(tid, j);
+            st.a[j] = v < V ? reinterpret_cast<const char *>(E) + (size_t)v * rowb : nullptr;
+        }
+        zero_acc<TL>(acc);
+        mainloop<T, TL>(acc, st, nsteps, [](int s) { return s * TL::kStageBytes; }, kvalid,
+                        [](int) {}, lds);
+#pragma unroll
+        for (int tn = 0; tn < TL::TN; ++tn) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int tm = 0; tm < TL::TM; ++tm)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int v = v0 + tile_row<TL>(tm, r);
+                    const float z = v < V ? acc[tm][tn][r] * kLog2e : kNegInf;
+                    acc[tm][tn][r] = z;
+                    mx = fmaxf(mx, z);
+                }
+            const float mn = fmaxf(m[tn], mx);
+            if (mn == kNegInf) continue;
+            float sum = 0.f;
+#pragma unroll
+            for (int tm = 0; tm < TL::TM; ++tm)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(acc[tm][tn][r] - mn);
+            l[tn] = l[tn] * __builtin_amdgcn_exp2f(m[tn] - mn) + sum;
+            m[tn] = mn;
+        }
+    }
+
+    // Merge the two half-waves (same tokens, different vocabulary rows).
+#pragma unroll
+    for (int tn = 0; tn < TL::TN; ++tn) {
+        const float mo = __shfl_xor(m[tn], 32, 64);
+        const float lo = __shfl_xor(l[tn], 32, 64);
+        const float M = fmaxf(m[tn], mo);
+        if (M != kNegInf) {
+            l[tn] = l[tn] * __builtin_amdgcn_exp2f(m[tn] - M) + lo * __builtin_amdgcn_exp2f(mo - M);
+            m[tn] = M;
+        }
+    }
+    // Merge the WM waves along the vocabulary side, in wave order.
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(lds);  // [WM][BN][2]
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % TL::WM;
+    if (lane < 32) {
+#pragma unroll
+        for (int tn = 0; tn < TL::TN; ++tn) {
+            const int c = tile_col<TL>(tn);
+            red[(wm * TL::BN + c) * 2 + 0] = m[tn];
+            red[(wm * TL::BN + c) * 2 + 1] = l[tn];
+        }
+    }
+    __syncthreads();
+    for (int c = tid; c < TL::BN; c += TL::kThreads) {
+        const int tok = tok0 + c;
+        if (tok >= nv) continue;
+        float M = kNegInf;
+        for (int w = 0; w < TL::WM; ++w) M = fmaxf(M, red[(w * TL::BN + c) * 2]);
+        float L = 0.f;
+        if (M != kNegInf)
+            for (int w = 0; w < TL::WM; ++w)
+                L += red[(w * TL::BN + c) * 2 + 1] * __builtin_amdgcn_exp2f(red[(w * TL::BN + c) * 2] - M);
+        const int64_t row = idx[tok];
+        part_m[(int64_t)split * N + row] = M;
+        part_s[(int64_t)split * N + row] = L;
+    }
+}
+
+// ------------------------------------------------------ merge + label gather
+// One wave per row.  Lane s reads split s's partial; the max and the scaled
+// sum are butterfly reductions (every lane ends with the same bits).
+template <typename T>
+__global__ __launch_bounds__(256) void k_merge(const T *__restrict__ H, const T *__restrict__ E,
+                                               const int64_t *__restrict__ labels,
+                                               const float *__restrict__ part_m,
+                                               const float *__restrict__ part_s, int S, int64_t N,
+                                               int D, int64_t V, int64_t ignore_index, float *__restrict__ loss,
+                                               float *__restrict__ lse) {
+    const int lane = threadIdx.x & 63;
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= N) return;
+    const int64_t y = labels[i];
+    if (y == ignore_index) {
+        if (lane == 0) { loss[i] = 0.f; lse[i] = 0.f; }
+        return;
+    }
+    if (y < 0 || y >= V) {  // not a valid label: undefined by contract; flag it, touch nothing
+        if (lane == 0) { loss[i] = __builtin_nanf(""); lse[i] = __builtin_nanf(""); }
+        return;
+    }
+    const float pm = lane < S ? part_m[(int64_t)lane * N + i] : kNegInf;
+    const float ps = lane < S ? part_s[(int64_t)lane * N + i] : 0.f;
+    float M = pm;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float L = (pm == kNegInf) ? 0.f : ps * __builtin_amdgcn_exp2f(pm - M);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+
+    // z_{i, y_i} = <h_i, e_{y_i}>, fp32 accumulation of exact products.
+    constexpr int CE = ChunkElems<T>::value;
+    const char *h = reinterpret_cast<const char *>(H + i * (int64_t)D);
+    const char *e = reinterpret_cast<const char *>(E + y * (int64_t)D);
+    float dot = 0.f;
+    for (int k = lane * CE; k < D; k += 64 * CE) {
+        const u32x4 hv = ld16(h + k * sizeof(T));
+        const u32x4 ev = ld16(e + k * sizeof(T));
+        const T *hp = reinterpret_cast<const T *>(&hv);
+        const T *ep = reinterpret_cast<const T *>(&ev);
+#pragma unroll
+        for (int q = 0; q < CE; ++q) dot += to_f32(hp[q]) * to_f32(ep[q]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
+    if (lane == 0) {
+        const float l = (M + log2f(L)) * kLn2;
+        lse[i] = l;
+        loss[i] = l - dot;
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+FwdShape fwd_shape(int64_t N, int64_t D, int64_t V) {
+    FwdShape s;
+    s.N = N;
+    s.D = D;
+    s.V = V;
+    s.n_vtiles = (int)ceil_div(V, kBlockVocab);
+    s.n_rtiles = (int)ceil_div(N, kBlockRows);
+    int S = (int)ceil_div(kFwdTargetGroups, s.n_rtiles);
+    if (S > kMaxSplits) S = kMaxSplits;
+    if (S > s.n_vtiles) S = s.n_vtiles;
+    if (S < 1) S = 1;
+    s.S = S;
+    return s;
+}
+
+FwdWs fwd_ws(void *ws, const FwdShape &s, size_t *bytes) {
+    Carver c(ws);
+    FwdWs w;
+    w.idx = c.take<int32_t>(s.N);
+    w.nvalid = c.take<int32_t>(1);
+    w.part_m = c.take<float>((size_t)s.S * s.N);
+    w.part_s = c.take<float>((size_t)s.S * s.N);
+    if (bytes) *bytes = c.off;
+    return w;
+}
+
+hipError_t launch_compact(const int64_t *labels, int64_t N, int64_t ignore_index, int32_t *idx,
+                          int32_t *nvalid, hipStream_t st) {
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, labels, N, ignore_index, idx, nvalid);
+    return hipGetLastError();
+}
+
+hipError_t launch_check_labels(const int64_t *labels, int64_t N, int64_t V, int64_t ignore_index,
+                               int64_t *n_bad, hipStream_t st) {
+    hipLaunchKernelGGL(k_check_labels, dim3(1), dim3(1024), 0, st, labels, N, V, ignore_index, n_bad);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t forward_t(const T *H, const T *E, const int64_t *labels, const FwdShape &s,
+                            int64_t ignore_index, const FwdWs &w, float *loss, float *lse,
+                            hipStream_t st) {
+    hipError_t e = launch_compact(labels, s.N, ignore_index, w.idx, w.nvalid, st);
+    if (e != hipSuccess) return e;
+    const int groups = s.S * s.n_rtiles;
+    hipLaunchKernelGGL(k_fwd<T>, dim3(groups), dim3(TileFR::kThreads), 0, st, H, E, w.idx, w.nvalid,
+                       (int)s.D, (int)s.V, s.N, s.n_vtiles, s.S, w.part_m, w.part_s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_merge<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, H, E, labels,
+                       w.part_m, w.part_s, s.S, s.N, (int)s.D, s.V, ignore_index, loss, lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_forward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
+                          const FwdShape &s, int64_t ignore_index, const FwdWs &w, float *loss,
+                          float *lse, hipStream_t st) {
+    if (dt == CCE_BF16)
+        return forward_t<bf16_t>(static_cast<const bf16_t *>(H), static_cast<const bf16_t *>(E), labels,
+                                 s, ignore_index, w, loss, lse, st);
+    return forward_t<float>(static_cast<const float *>(H), static_cast<const float *>(E), labels, s,
+                            ignore_index, w, loss, lse, st);
+}
+
+}  // namespace cce

@@ -1,0 +1,146 @@
+"""The C ABI on the host: the library loads, exports every entry point the
+header declares, sizes its workspace without an N x V term, and rejects bad
+arguments before enqueuing anything.  Nothing here runs a kernel: every
+argument error is detected on the host, and pointers passed are never
+dereferenced (they are fake, suitably aligned addresses)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_cross_entropy_cce_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # aligned, never dereferenced
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "cce.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cce_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = B.lib()
+    declared = _header_functions()
+    assert declared == sorted(B.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_block():
+    assert B.version() >= 10000
+    r, v = B.filter_block()
+    assert r > 0 and v > 0 and r % 32 == 0 and v % 32 == 0
+
+
+def test_status_strings():
+    for s in range(8):
+        assert len(B.status_string(s)) > 0
+    assert B.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("dt", [B.CCE_F32, B.CCE_BF16])
+def test_workspace_has_no_rows_times_vocab_term(dt):
+    # Doubling V at fixed N (or N at fixed V) at most roughly doubles the
+    # workspace; an N x V term would quadruple it when both double.
+    f = B.backward_workspace_bytes
+    D = 2048
+    a = f(8192, D, 256000, dt)
+    b = f(16384, D, 512000, dt)
+    assert a > 0 and b < 2.2 * a
+    g = B.forward_workspace_bytes
+    assert g(16384, D, 512000, dt) < 2.2 * g(8192, D, 256000, dt)
+    # linear in N at fixed V, and bounded by a few bytes x (N x D + V + D x chunk)
+    elem = 4 if dt == B.CCE_F32 else 2
+    assert a < 4 * 8192 * D + 2 * elem * 8192 * 8192 + 2 * elem * D * 8192 + elem * D * 8192 + 64 * 256000 + (1 << 20)
+
+
+def test_workspace_invalid_sizes_return_zero():
+    for args in [(0, 64, 10), (10, 0, 10), (10, 12, 10), (10, 64, 0), (10, 64, 1 << 31), (10, 64, 10)]:
+        n, d, v = args
+        want_zero = not (n >= 1 and v >= 1 and v < (1 << 31) and d >= 8 and d % 8 == 0)
+        assert (B.forward_workspace_bytes(n, d, v, 1) == 0) == want_zero
+    assert B.forward_workspace_bytes(10, 64, 10, 7) == 0
+
+
+def _fwd(**kw):
+    a = dict(H=FAKE, E=FAKE, labels=FAKE, N=16, D=64, V=100, dt=B.CCE_BF16, ign=-100, loss=FAKE, lse=FAKE,
+             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return B.lib().cce_forward(a["H"], a["E"], a["labels"], a["N"], a["D"], a["V"], a["dt"], a["ign"], a["loss"],
+                               a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _bwd(**kw):
+    a = dict(H=FAKE, E=FAKE, labels=FAKE, lse=FAKE, dloss=FAKE, N=16, D=64, V=100, dt=B.CCE_BF16, ign=-100,
+             eps=0.0, perm=None, flags=0, dH=FAKE, dE=FAKE, stats=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return B.lib().cce_backward(a["H"], a["E"], a["labels"], a["lse"], a["dloss"], a["N"], a["D"], a["V"], a["dt"],
+                                a["ign"], a["eps"], a["perm"], a["flags"], a["dH"], a["dE"], a["stats"], a["ws"],
+                                a["ws_bytes"], a["stream"])
+
+
+def _vord(**kw):
+    a = dict(H=FAKE, E=FAKE, labels=FAKE, N=16, D=64, V=100, dt=B.CCE_BF16, ign=-100, perm=FAKE, keys=None,
+             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return B.lib().cce_vocab_order(a["H"], a["E"], a["labels"], a["N"], a["D"], a["V"], a["dt"], a["ign"],
+                                   a["perm"], a["keys"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("call", [_fwd, _bwd, _vord])
+def test_argument_errors_before_launch(call):
+    assert call(H=None) == B.CCE_ERR_NULL
+    assert call(E=None) == B.CCE_ERR_NULL
+    assert call(labels=None) == B.CCE_ERR_NULL
+    assert call(ws=None) == B.CCE_ERR_NULL
+    assert call(N=0) == B.CCE_ERR_SHAPE
+    assert call(V=0) == B.CCE_ERR_SHAPE
+    assert call(D=12) == B.CCE_ERR_SHAPE
+    assert call(D=0) == B.CCE_ERR_SHAPE
+    assert call(V=1 << 31) == B.CCE_ERR_SHAPE
+    assert call(dt=5) == B.CCE_ERR_DTYPE
+    assert call(H=FAKE + 8) == B.CCE_ERR_ALIGN
+    assert call(E=FAKE + 4) == B.CCE_ERR_ALIGN
+    assert call(ws=FAKE + 2) == B.CCE_ERR_ALIGN
+    assert call(ws_bytes=16) == B.CCE_ERR_WORKSPACE
+
+
+def test_forward_specific_errors():
+    assert _fwd(loss=None) == B.CCE_ERR_NULL
+    assert _fwd(lse=None) == B.CCE_ERR_NULL
+    assert _fwd(lse=FAKE + 2) == B.CCE_ERR_ALIGN
+    need = B.forward_workspace_bytes(16, 64, 100, B.CCE_BF16)
+    assert _fwd(ws_bytes=need - 1) == B.CCE_ERR_WORKSPACE
+
+
+def test_backward_specific_errors():
+    assert _bwd(dH=None) == B.CCE_ERR_NULL
+    assert _bwd(dE=None) == B.CCE_ERR_NULL
+    assert _bwd(lse=None) == B.CCE_ERR_NULL
+    assert _bwd(dloss=None) == B.CCE_ERR_NULL
+    assert _bwd(eps=-1.0) == B.CCE_ERR_ARG
+    assert _bwd(eps=float("nan")) == B.CCE_ERR_ARG
+    assert _bwd(eps=float("inf")) == B.CCE_ERR_ARG
+    assert _bwd(flags=2) == B.CCE_ERR_ARG
+    assert _bwd(dE=FAKE + 8) == B.CCE_ERR_ALIGN
+    assert _bwd(perm=FAKE + 2) == B.CCE_ERR_ALIGN
+    assert _bwd(stats=FAKE + 4) == B.CCE_ERR_ALIGN
+    need = B.backward_workspace_bytes(16, 64, 100, B.CCE_BF16)
+    assert _bwd(ws_bytes=need - 1) == B.CCE_ERR_WORKSPACE
+
+
+def test_check_labels_errors():
+    L = B.lib()
+    assert L.cce_check_labels(None, 10, 10, -100, FAKE, None) == B.CCE_ERR_NULL
+    assert L.cce_check_labels(FAKE, 0, 10, -100, FAKE, None) == B.CCE_ERR_SHAPE
+    assert L.cce_check_labels(FAKE + 4, 10, 10, -100, FAKE, None) == B.CCE_ERR_ALIGN
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="libcce.so not found"):
+        B.lib()
