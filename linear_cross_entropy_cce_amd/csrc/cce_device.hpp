@@ -24,13 +24,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
-// float -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
-}
+// float -> bfloat16, round to nearest, ties to even (gfx950 converts in
+// hardware: v_cvt_pk_bf16_f32; NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 template <typename T> __device__ __forceinline__ T from_f32(float f);
 template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
@@ -98,107 +94,207 @@ struct Tile {
     static_assert(kAChunks % kThreads == 0 && kBChunks % kThreads == 0, "stage must split evenly");
 };
 
-// LDS position (in 16-byte chunks) of chunk c of row r: rows are 128 bytes,
-// chunks XOR-swizzled by the row so that 8 consecutive rows read at the same
-// logical chunk hit 8 different bank groups.
-__device__ __forceinline__ int lds_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
-
-// The rows of A and B that one thread stages, for the whole K loop.  A null
-// row pointer stages zeros (rows past the end of the operand).
-template <int NA, int NB>
-struct Stager {
-    const char *a[NA];
-    const char *b[NB];
-    int cA[NA], cB[NB];  // 16-byte chunk of the row this thread loads
-    int sA[NA], sB[NB];  // LDS slot
-};
-
-template <class TL>
-__device__ __forceinline__ void stager_slots(Stager<TL::kALoads, TL::kBLoads> &st, int tid) {
-#pragma unroll
-    for (int j = 0; j < TL::kALoads; ++j) {
-        const int q = tid + TL::kThreads * j;
-        st.cA[j] = q & 7;
-        st.sA[j] = lds_slot(q >> 3, q & 7);
-    }
-#pragma unroll
-    for (int j = 0; j < TL::kBLoads; ++j) {
-        const int q = tid + TL::kThreads * j;
-        st.cB[j] = q & 7;
-        st.sB[j] = TL::kAChunks + lds_slot(q >> 3, q & 7);
-    }
-}
-
-// Row (within the tile) that load j of thread tid stages.
-template <class TL>
-__device__ __forceinline__ int stage_row_a(int tid, int j) { return (tid + TL::kThreads * j) >> 3; }
-template <class TL>
-__device__ __forceinline__ int stage_row_b(int tid, int j) { return (tid + TL::kThreads * j) >> 3; }
+// LDS position (in 16-byte chunks) of chunk c of row r.  Rows are 128 bytes;
+// the chunk is XOR-swizzled with f(r) = (r & 7) ^ ((r >> 3) & 1), so that the
+// 8 or 16 rows one ds_read_b128 services together (lanes l % 32 = row) all
+// fall in distinct 16-byte bank groups, whether the LDS serves 128 or 256
+// bytes per clock.
+__device__ __forceinline__ int lds_slot(int r, int c) { return r * 8 + (c ^ ((r & 7) ^ ((r >> 3) & 1))); }
 
 __device__ __forceinline__ u32x4 ld16(const char *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-// The K loop.  nsteps stages; koff(s) gives the byte offset along K of stage
-// s; chunks at or beyond kvalid bytes read as zero.  after(s) runs once the
-// MFMAs of stage s are issued (used to close Kahan blocks).
-template <typename T, class TL, class KOff, class After>
-__device__ __forceinline__ void mainloop(f32x16 (&acc)[TL::TM][TL::TN],
-                                         const Stager<TL::kALoads, TL::kBLoads> &st, int nsteps,
-                                         KOff koff, int kvalid, After after, u32x4 *lds) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave % TL::WM;
-    const int wn = wave / TL::WM;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 ra[TL::kALoads], rb[TL::kBLoads];
+// One workgroup's side of the K loop: global -> registers -> LDS staging of
+// the A and B rows, and the MFMA over one LDS stage.
+//  - Thread t stages 16-byte chunk (t & 7) of rows (t >> 3) + (threads / 8) j.
+//  - pa[j] / pb[j] are the row base pointers of load j for the current tile
+//    (null = row past the end: stages zeros).
+//  - load(kb, kvalid): chunk at byte kb + 16 (t & 7) of every row, zero at or
+//    beyond kvalid bytes.
+template <typename T, class TL>
+struct Engine {
+    static constexpr int NA = TL::kALoads, NB = TL::kBLoads;
+    static constexpr int kRowStep = TL::kThreads / 8;
+    const char *pa[NA];
+    const char *pb[NB];
+    u32x4 ra[NA], rb[NB];
+    int c16, slot0;
 
-    auto gload = [&](int s) {
-        const int kb = koff(s);
-#pragma unroll
-        for (int j = 0; j < TL::kALoads; ++j) {
-            const int off = kb + st.cA[j] * 16;
-            ra[j] = (st.a[j] && off < kvalid) ? ld16(st.a[j] + off) : zero;
-        }
-#pragma unroll
-        for (int j = 0; j < TL::kBLoads; ++j) {
-            const int off = kb + st.cB[j] * 16;
-            rb[j] = (st.b[j] && off < kvalid) ? ld16(st.b[j] + off) : zero;
-        }
-    };
-    auto sstore = [&](int stage) {
-        u32x4 *base = lds + stage * TL::kStage;
-#pragma unroll
-        for (int j = 0; j < TL::kALoads; ++j) base[st.sA[j]] = ra[j];
-#pragma unroll
-        for (int j = 0; j < TL::kBLoads; ++j) base[st.sB[j]] = rb[j];
-    };
+    __device__ __forceinline__ Engine() {
+        const int t = threadIdx.x;
+        c16 = (t & 7) * 16;
+        slot0 = lds_slot(t >> 3, t & 7);  // row r0 + kRowStep j keeps r0's swizzle (kRowStep % 16 == 0)
+        static_assert(kRowStep % 16 == 0, "row step must preserve the swizzle phase");
+    }
+    static __device__ __forceinline__ int row(int j) { return (threadIdx.x >> 3) + kRowStep * j; }
 
-    if (nsteps <= 0) return;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-        if (s + 1 < nsteps) gload(s + 1);
-        const u32x4 *A = lds + (s & 1) * TL::kStage;
-        const u32x4 *B = A + TL::kAChunks;
+    __device__ __forceinline__ void load(int kb, int kvalid) {
+        const int off = kb + c16;
+        const bool kok = off < kvalid;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < NA; ++j) ra[j] = (pa[j] && kok) ? ld16(pa[j] + off) : z;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) rb[j] = (pb[j] && kok) ? ld16(pb[j] + off) : z;
+    }
+    __device__ __forceinline__ void store(u32x4 *stage) const {
+#pragma unroll
+        for (int j = 0; j < NA; ++j) stage[slot0 + 8 * kRowStep * j] = ra[j];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) stage[TL::kAChunks + slot0 + 8 * kRowStep * j] = rb[j];
+    }
+    __device__ __forceinline__ void compute(const u32x4 *stage, f32x16 (&acc)[TL::TM][TL::TN]) const {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int ra0 = (wave % TL::WM) * TL::kWaveM + (lane & 31);
+        const int rb0 = (wave / TL::WM) * TL::kWaveN + (lane & 31);
+        const u32x4 *A = stage;
+        const u32x4 *B = stage + TL::kAChunks;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int c = 2 * kk + (lane >> 5);
             u32x4 fa[TL::TM], fb[TL::TN];
 #pragma unroll
-            for (int tm = 0; tm < TL::TM; ++tm) fa[tm] = A[lds_slot(wm * TL::kWaveM + tm * 32 + (lane & 31), c)];
+            for (int tm = 0; tm < TL::TM; ++tm) fa[tm] = A[lds_slot(ra0 + tm * 32, c)];
 #pragma unroll
-            for (int tn = 0; tn < TL::TN; ++tn) fb[tn] = B[lds_slot(wn * TL::kWaveN + tn * 32 + (lane & 31), c)];
+            for (int tn = 0; tn < TL::TN; ++tn) fb[tn] = B[lds_slot(rb0 + tn * 32, c)];
 #pragma unroll
             for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
                 for (int tn = 0; tn < TL::TN; ++tn) Mfma<T>::step(fa[tm], fb[tn], acc[tm][tn]);
         }
-        after(s);
-        if (s + 1 < nsteps) sstore((s + 1) & 1);
-        __syncthreads();
     }
+};
+
+// ------------------------------------------------------- DMA K pipeline
+// gfx950 moves 16 bytes per lane straight from global memory into LDS
+// (global_load_lds_dwordx4): lane i of a wave-instruction lands at
+// base + 16 i.  The pipeline keeps kStages LDS stages of kRowBytes K-bytes per
+// row and kStages - 1 of them in flight, so no VGPR staging is needed.
+//
+// Stage layout: rows of kRowBytes (64 or 128 bytes, 4 or 8 chunks of 16);
+// chunk c of row r sits at position c ^ g(r), chosen so that the 8 or 16
+// rows one ds_read_b128 services together fall in distinct bank groups
+// (64-byte rows: g(r) = ((r >> 1) ^ (r >> 2)) & 3; 128-byte rows:
+// g(r) = (r & 7) ^ ((r >> 3) & 1)).  The swizzle is applied on the global
+// side: lane i of an instruction fetches the logical chunk that belongs at
+// slot base + i.
+//
+// Synchronisation: each wave waits for its own DMAs of the stage with
+// s_waitcnt vmcnt, then s_barrier; the barrier also certifies that every wave
+// finished reading the stage the next DMA overwrites.  The empty asm
+// statements keep the compiler from moving memory operations across.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int kRowBytes>
+__device__ __forceinline__ int dma_swz(int r) {
+    if constexpr (kRowBytes == 64) return ((r >> 1) ^ (r >> 2)) & 3;
+    else return (r & 7) ^ ((r >> 3) & 1);
 }
+template <int kRowBytes>
+__device__ __forceinline__ int dma_slot(int r, int c) {
+    return r * (kRowBytes / 16) + (c ^ dma_swz<kRowBytes>(r));
+}
+
+// One wave-instruction of global -> LDS DMA: this lane's 16 bytes at src go
+// to wave_dst + 16 * lane (wave_dst is the same for the whole wave).  Issued
+// as inline assembly so that the compiler's wait-count pass does not treat
+// every later LDS read as dependent on it; the pipeline waits explicitly.
+// M0 holds the LDS address; nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const char *src, u32x4 *wave_dst) {
+    const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)wave_dst);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x3F70 | (N & 0xF) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void block_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <typename T, class TL, int kRowBytes_ = 64, int kStages_ = 4>
+struct DmaEngine {
+    static constexpr int kStages = kStages_;
+    static constexpr int kDepth = kStages - 1;  // stages in flight ahead of the one computed
+    static constexpr int kStageBytes = kRowBytes_;
+    static constexpr int kCpr = kRowBytes_ / 16;  // chunks per row
+    static constexpr int kStageA = TL::BM * kCpr;  // chunks of A per stage
+    static constexpr int kStageB = TL::BN * kCpr;
+    static constexpr int kStage = kStageA + kStageB;
+    static constexpr int kLdsChunks = kStages * kStage;
+    static constexpr int NIA = kStageA / 64 / TL::kWaves;  // DMA instructions per wave per stage
+    static constexpr int NIB = kStageB / 64 / TL::kWaves;
+    static constexpr int NI = NIA + NIB;
+    static_assert(kRowBytes_ == 64 || kRowBytes_ == 128, "64- or 128-byte stage rows");
+    static_assert(kStages >= 2 && kStages <= 4, "2 to 4 stages");
+    static_assert(NIA * 64 * TL::kWaves == kStageA && NIB * 64 * TL::kWaves == kStageB,
+                  "tile rows must split into whole wave-instructions");
+
+    const char *pa[NIA];  // this lane's source address (row base + swizzled chunk) at K offset 0
+    const char *pb[NIB];
+    u32x4 *lds;
+
+    __device__ __forceinline__ explicit DmaEngine(u32x4 *l) : lds(l) {}
+
+    // Tile row fed by this lane in instruction j, and its chunk byte offset.
+    static __device__ __forceinline__ int row_a(int j) {
+        return (64 * (j * TL::kWaves + (threadIdx.x >> 6)) + (threadIdx.x & 63)) / kCpr;
+    }
+    static __device__ __forceinline__ int row_b(int j) { return row_a(j); }
+    static __device__ __forceinline__ int chunk_off(int r) {
+        return 16 * ((threadIdx.x & (kCpr - 1)) ^ dma_swz<kRowBytes_>(r));
+    }
+
+    __device__ __forceinline__ void issue(int buf, int kb) const {
+        const int w = threadIdx.x >> 6;
+        u32x4 *st = lds + buf * kStage;
+#pragma unroll
+        for (int j = 0; j < NIA; ++j) dma16(pa[j] + kb, st + 64 * (j * TL::kWaves + w));
+#pragma unroll
+        for (int j = 0; j < NIB; ++j) dma16(pb[j] + kb, st + kStageA + 64 * (j * TL::kWaves + w));
+    }
+
+    // Wait until at most `ahead` later stages are still in flight for this
+    // wave (ahead <= kDepth - 1), then barrier.
+    __device__ __forceinline__ void wait_stage(int ahead) const {
+        if constexpr (kDepth >= 3) {
+            if (ahead >= 2) { wait_vmcnt<2 * NI>(); block_sync(); return; }
+        }
+        if constexpr (kDepth >= 2) {
+            if (ahead >= 1) { wait_vmcnt<NI>(); block_sync(); return; }
+        }
+        wait_vmcnt<0>();
+        block_sync();
+    }
+    __device__ __forceinline__ int clamp_ahead(int ahead) const { return ahead < kDepth - 1 ? ahead : kDepth - 1; }
+
+    __device__ __forceinline__ void compute(int buf, f32x16 (&acc)[TL::TM][TL::TN]) const {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int ra0 = (wave % TL::WM) * TL::kWaveM + (lane & 31);
+        const int rb0 = (wave / TL::WM) * TL::kWaveN + (lane & 31);
+        const u32x4 *A = lds + buf * kStage;
+        const u32x4 *B = A + kStageA;
+#pragma unroll
+        for (int kk = 0; kk < kCpr / 2; ++kk) {
+            const int c = 2 * kk + (lane >> 5);
+            u32x4 fa[TL::TM], fb[TL::TN];
+#pragma unroll
+            for (int tm = 0; tm < TL::TM; ++tm) fa[tm] = A[dma_slot<kRowBytes_>(ra0 + tm * 32, c)];
+#pragma unroll
+            for (int tn = 0; tn < TL::TN; ++tn) fb[tn] = B[dma_slot<kRowBytes_>(rb0 + tn * 32, c)];
+#pragma unroll
+            for (int tm = 0; tm < TL::TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TL::TN; ++tn) Mfma<T>::step(fa[tm], fb[tn], acc[tm][tn]);
+        }
+    }
+};
 
 template <class TL>
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[TL::TM][TL::TN]) {
@@ -217,6 +313,19 @@ __device__ __forceinline__ int tile_row(int tm, int r) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     return (wave % TL::WM) * TL::kWaveM + tm * 32 + acc_row(r, lane);
 }
+// Row of register r of acc[tm][*] within the wave's sub-tile, without the
+// lane term: tile_row = wave row base + 4 (lane / 32) + acc_row_const(tm, r).
+// A compile-time constant, so a bound check against a per-lane limit costs
+// one compare with an immediate.
+__device__ __forceinline__ constexpr int acc_row_const(int tm, int r) { return tm * 32 + 8 * (r >> 2) + (r & 3); }
+
+// Per-lane limit: acc[tm][*][r] holds tile row < rows iff acc_row_const(tm, r) < row_limit(rows).
+template <class TL>
+__device__ __forceinline__ int row_limit(int rows) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return rows - (wave % TL::WM) * TL::kWaveM - 4 * (lane >> 5);
+}
+
 template <class TL>
 __device__ __forceinline__ int tile_col(int tn) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

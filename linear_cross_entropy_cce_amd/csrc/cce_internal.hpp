@@ -9,8 +9,15 @@
 
 namespace cce {
 
-// Filter block = tile of the logit kernels: kBlockVocab vocabulary entries
-// (MFMA M side) x kBlockRows valid tokens (MFMA N side).
+// Logit tile of the forward and of the backward recompute: kTileVocab
+// vocabulary entries (MFMA M side) x kTileRows valid tokens (MFMA N side).
+constexpr int kTileVocab = 256;
+constexpr int kTileRows = 256;
+// K pipeline of the logit kernels: LDS stages of kLogitRowBytes per row,
+// kLogitStages of them (kLogitStages - 1 in flight).
+constexpr int kLogitRowBytes = 128;
+constexpr int kLogitStages = 2;
+// Gradient-filter block: a quarter of the logit tile.
 constexpr int kBlockVocab = 128;
 constexpr int kBlockRows = 128;
 // The backward materialises the logit gradient for at most this many
@@ -18,8 +25,8 @@ constexpr int kBlockRows = 128;
 constexpr int kChunkVocab = 8192;
 // Upper bound on the forward's vocabulary splits (merged per row in order).
 constexpr int kMaxSplits = 64;
-// Workgroups the forward aims to launch (several per compute unit).
-constexpr int kFwdTargetGroups = 1024;
+// Workgroups the forward aims to launch (two per compute unit).
+constexpr int kFwdTargetGroups = 512;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -41,8 +48,8 @@ struct Carver {
 
 struct FwdShape {
     int64_t N, D, V;
-    int n_vtiles;  // vocabulary tiles of kBlockVocab
-    int n_rtiles;  // token tiles of kBlockRows (upper bound, from N)
+    int n_vtiles;  // vocabulary tiles of kTileVocab
+    int n_rtiles;  // token tiles of kTileRows (upper bound, from N)
     int S;         // vocabulary splits
 };
 FwdShape fwd_shape(int64_t N, int64_t D, int64_t V);

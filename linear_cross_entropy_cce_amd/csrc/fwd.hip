@@ -22,7 +22,9 @@
 
 namespace cce {
 
-using TileFR = Tile<kBlockVocab, kBlockRows, 2, 2>;  // A = vocabulary rows, B = token rows
+using TileF = Tile<kTileVocab, kTileRows, 2, 4>;   // A = vocabulary rows, B = token rows; 8 waves
+using TileF4 = Tile<kTileVocab, kTileRows, 2, 2>;  // the same tile on 4 waves of 128 x 128
+using TileFD = TileF;                              // tile of the DMA logit kernels
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -78,78 +80,78 @@ __global__ __launch_bounds__(1024) void k_check_labels(const int64_t *__restrict
 }
 
 // ------------------------------------------------------------ logit + LSE
-// Workgroup (split s, token tile rt) streams the vocabulary tiles of split s.
+// Workgroup (split s, token tile rt) streams the vocabulary tiles of split s
+// through one continuous double-buffered K pipeline: the loads of the next
+// tile's first stage are in flight while the current tile's epilogue runs.
 // Each lane owns TN token columns; for each it keeps m (running max of
 // z log2 e) and l (running sum of 2^(z log2 e - m)) over the vocabulary rows
 // it holds.  At the end the two half-waves and the WM waves that hold the same
 // tokens are merged in a fixed order.
-template <typename T>
-__global__ __launch_bounds__(TileFR::kThreads) void k_fwd(
-    const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ nvalid_p, int D, int V, int64_t N, int n_vtiles, int S,
-    float *__restrict__ part_m, float *__restrict__ part_s) {
-    using TL = TileFR;
-    __shared__ u32x4 lds[TL::kLdsChunks];
-    const int nv = *nvalid_p;
-    const int split = blockIdx.x % S;
-    const int rt = blockIdx.x / S;
-    const int tok0 = rt * TL::BN;
-    if (tok0 >= nv) return;
-    const int t0 = (int)((int64_t)n_vtiles * split / S);
-    const int t1 = (int)((int64_t)n_vtiles * (split + 1) / S);
-    const int tid = threadIdx.x;
-    const size_t rowb = (size_t)D * sizeof(T);
-    const int kvalid = D * (int)sizeof(T);
-    const int nsteps = (kvalid + TL::kStageBytes - 1) / TL::kStageBytes;
-
-    Stager<TL::kALoads, TL::kBLoads> st;
-    stager_slots<TL>(st, tid);
-#pragma unroll
-    for (int j = 0; j < TL::kBLoads; ++j) {
-        const int tok = tok0 + stage_row_b<TL>(tid, j);
-        st.b[j] = tok < nv ? reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb : nullptr;
+//
+// Placement: hardware workgroup b runs on XCD b % 8.  When the grid allows it,
+// the 32 workgroups an XCD holds at once are 4 splits x 8 token tiles, so each
+// classifier tile in flight is shared by 8 workgroups and each hidden-state
+// tile by 4, in that XCD's L2.
+__device__ __forceinline__ void fwd_place(int b, int G, int S, int R, int &split, int &rt) {
+    if (G % 8 == 0 && S % 4 == 0 && R % 8 == 0) {
+        const int L = (b % 8) * (G / 8) + b / 8;  // consecutive L share an XCD
+        const int g = L / 32, w = L % 32;
+        const int sg = S / 4;
+        split = (g % sg) * 4 + (w % 4);
+        rt = (g / sg) * 8 + (w / 4);
+    } else {
+        split = b % S;
+        rt = b / S;
     }
+}
 
-    float m[TL::TN], l[TL::TN];
+// Online update of (m, l) with one finished logit tile (raw z in acc; rows
+// v0 + tile_row are vocabulary entries, rows >= V do not exist).  The tile's
+// max is taken on z and scaled once; each entry costs one FMA and one exp2.
+template <class TL>
+__device__ __forceinline__ void fwd_tile_update(f32x16 (&acc)[TL::TM][TL::TN], int v0, int V, float (&m)[TL::TN],
+                                                float (&l)[TL::TN]) {
+    const bool full = v0 + TL::BM <= V;
+    // One token column at a time keeps at most TM x 16 values in VGPRs; the
+    // scheduling barriers stop the compiler from hoisting every column's
+    // accumulator reads to the top (which would spill).
 #pragma unroll
-    for (int tn = 0; tn < TL::TN; ++tn) { m[tn] = kNegInf; l[tn] = 0.f; }
-
-    f32x16 acc[TL::TM][TL::TN];
-    for (int vt = t0; vt < t1; ++vt) {
-        const int v0 = vt * TL::BM;
+    for (int tn = 0; tn < TL::TN; ++tn) {
+        __builtin_amdgcn_sched_barrier(0);
+        float mx = kNegInf;
+        if (full) {
 #pragma unroll
-        for (int j = 0; j < TL::kALoads; ++j) {
-            const int v = v0 + stage_row_a<TL>(tid, j);
-            st.a[j] = v < V ? reinterpret_cast<const char *>(E) + (size_t)v * rowb : nullptr;
-        }
-        zero_acc<TL>(acc);
-        mainloop<T, TL>(acc, st, nsteps, [](int s) { return s * TL::kStageBytes; }, kvalid,
-                        [](int) {}, lds);
+            for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < TL::TN; ++tn) {
-            float mx = kNegInf;
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[tm][tn][r]);
+        } else {
+            const int lim = row_limit<TL>(V - v0);
 #pragma unroll
             for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int v = v0 + tile_row<TL>(tm, r);
-                    const float z = v < V ? acc[tm][tn][r] * kLog2e : kNegInf;
-                    acc[tm][tn][r] = z;
-                    mx = fmaxf(mx, z);
+                    if (acc_row_const(tm, r) >= lim) acc[tm][tn][r] = kNegInf;
+                    mx = fmaxf(mx, acc[tm][tn][r]);
                 }
-            const float mn = fmaxf(m[tn], mx);
-            if (mn == kNegInf) continue;
-            float sum = 0.f;
-#pragma unroll
-            for (int tm = 0; tm < TL::TM; ++tm)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(acc[tm][tn][r] - mn);
-            l[tn] = l[tn] * __builtin_amdgcn_exp2f(m[tn] - mn) + sum;
-            m[tn] = mn;
         }
+        const float mn = fmaxf(m[tn], mx * kLog2e);
+        if (mn == kNegInf) continue;
+        float sum = 0.f;
+#pragma unroll
+        for (int tm = 0; tm < TL::TM; ++tm)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[tm][tn][r], kLog2e, -mn));
+        l[tn] = l[tn] * __builtin_amdgcn_exp2f(m[tn] - mn) + sum;
+        m[tn] = mn;
     }
+}
 
-    // Merge the two half-waves (same tokens, different vocabulary rows).
+// Merges (m, l) over the two half-waves and the WM waves that hold the same
+// tokens, in a fixed order, and writes the split's partials for valid tokens.
+template <class TL>
+__device__ __forceinline__ void fwd_write_partials(float (&m)[TL::TN], float (&l)[TL::TN], float *red, int tok0,
+                                                   int nv, const int32_t *__restrict__ idx, int split, int64_t N,
+                                                   float *__restrict__ part_m, float *__restrict__ part_s) {
 #pragma unroll
     for (int tn = 0; tn < TL::TN; ++tn) {
         const float mo = __shfl_xor(m[tn], 32, 64);
@@ -160,10 +162,8 @@ __global__ __launch_bounds__(TileFR::kThreads) void k_fwd(
             m[tn] = M;
         }
     }
-    // Merge the WM waves along the vocabulary side, in wave order.
     __syncthreads();
-    float *red = reinterpret_cast<float *>(lds);  // [WM][BN][2]
-    const int lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % TL::WM;
     if (lane < 32) {
 #pragma unroll
@@ -187,6 +187,145 @@ __global__ __launch_bounds__(TileFR::kThreads) void k_fwd(
         part_m[(int64_t)split * N + row] = M;
         part_s[(int64_t)split * N + row] = L;
     }
+}
+
+template <typename T>
+__global__ __launch_bounds__(TileF::kThreads) void k_fwd(
+    const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ nvalid_p, int D, int V, int64_t N, int n_vtiles, int S, int R,
+    float *__restrict__ part_m, float *__restrict__ part_s) {
+    using TL = TileF;
+    __shared__ u32x4 lds[TL::kLdsChunks];
+    const int nv = *nvalid_p;
+    int split, rt;
+    fwd_place(blockIdx.x, gridDim.x, S, R, split, rt);
+    const int tok0 = rt * TL::BN;
+    if (tok0 >= nv) return;
+    const int t0 = (int)((int64_t)n_vtiles * split / S);
+    const int t1 = (int)((int64_t)n_vtiles * (split + 1) / S);
+    const int ntile = t1 - t0;
+    const int tid = threadIdx.x;
+    const size_t rowb = (size_t)D * sizeof(T);
+    const int kvalid = D * (int)sizeof(T);
+    const int ns = (kvalid + TL::kStageBytes - 1) / TL::kStageBytes;
+
+    Engine<T, TL> eng;
+#pragma unroll
+    for (int j = 0; j < Engine<T, TL>::NB; ++j) {
+        const int tok = tok0 + eng.row(j);
+        eng.pb[j] = tok < nv ? reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb : nullptr;
+    }
+    auto set_tile = [&](int vt) {
+        const int v0 = vt * TL::BM;
+#pragma unroll
+        for (int j = 0; j < Engine<T, TL>::NA; ++j) {
+            const int v = v0 + eng.row(j);
+            eng.pa[j] = v < V ? reinterpret_cast<const char *>(E) + (size_t)v * rowb : nullptr;
+        }
+    };
+
+    float m[TL::TN], l[TL::TN];
+#pragma unroll
+    for (int tn = 0; tn < TL::TN; ++tn) { m[tn] = kNegInf; l[tn] = 0.f; }
+    f32x16 acc[TL::TM][TL::TN];
+    zero_acc<TL>(acc);
+
+    const int total = ntile * ns;
+    if (total > 0) {
+        int lt = 0, lk = 0;  // tile / stage of the next load
+        set_tile(t0);
+        eng.load(0, kvalid);
+        eng.store(lds);
+        if (++lk == ns) { lk = 0; if (++lt < ntile) set_tile(t0 + lt); }
+        __syncthreads();
+        int ck = 0, ct = 0;  // stage / tile being computed
+        for (int s = 0; s < total; ++s) {
+            const bool more = s + 1 < total;
+            if (more) eng.load(lk * TL::kStageBytes, kvalid);
+            eng.compute(lds + (s & 1) * TL::kStage, acc);
+            if (++ck == ns) {
+                ck = 0;
+                fwd_tile_update<TL>(acc, (t0 + ct) * TL::BM, V, m, l);
+                ++ct;
+                zero_acc<TL>(acc);
+            }
+            if (more) {
+                eng.store(lds + ((s + 1) & 1) * TL::kStage);
+                if (++lk == ns) { lk = 0; if (++lt < ntile) set_tile(t0 + lt); }
+            }
+            __syncthreads();
+        }
+    }
+
+    fwd_write_partials<TL>(m, l, reinterpret_cast<float *>(lds), tok0, nv, idx, split, N, part_m, part_s);
+}
+
+// The same computation on the DMA pipeline (DmaEngine): 4 LDS stages of 64
+// K-bytes, 3 in flight.  Rows past the end of an operand are clamped to its
+// last row: their logits are finite and masked (vocabulary) or never
+// written (tokens).  Needs D * sizeof(T) to be a multiple of 64.
+template <typename T, class TL>
+__global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
+    const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ nvalid_p, int D, int V, int64_t N, int n_vtiles, int S, int R,
+    float *__restrict__ part_m, float *__restrict__ part_s) {
+    using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
+    __shared__ u32x4 lds[DE::kLdsChunks];
+    const int nv = *nvalid_p;
+    int split, rt;
+    fwd_place(blockIdx.x, gridDim.x, S, R, split, rt);
+    const int tok0 = rt * TL::BN;
+    if (tok0 >= nv) return;
+    const int t0 = (int)((int64_t)n_vtiles * split / S);
+    const int t1 = (int)((int64_t)n_vtiles * (split + 1) / S);
+    const int ntile = t1 - t0;
+    const size_t rowb = (size_t)D * sizeof(T);
+    const int ns = D * (int)sizeof(T) / DE::kStageBytes;
+
+    DE eng(lds);
+#pragma unroll
+    for (int j = 0; j < DE::NIB; ++j) {
+        const int r = DE::row_b(j);
+        const int tok = min(tok0 + r, nv - 1);
+        eng.pb[j] = reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb + DE::chunk_off(r);
+    }
+    auto set_tile = [&](int vt) {
+#pragma unroll
+        for (int j = 0; j < DE::NIA; ++j) {
+            const int r = DE::row_a(j);
+            const int v = min(vt * TL::BM + r, V - 1);
+            eng.pa[j] = reinterpret_cast<const char *>(E) + (size_t)v * rowb + DE::chunk_off(r);
+        }
+    };
+
+    float m[TL::TN], l[TL::TN];
+#pragma unroll
+    for (int tn = 0; tn < TL::TN; ++tn) { m[tn] = kNegInf; l[tn] = 0.f; }
+    f32x16 acc[TL::TM][TL::TN];
+    zero_acc<TL>(acc);
+
+    const int total = ntile * ns;
+    int lt = 0, lk = 0;  // tile / stage of the next DMA
+    if (total > 0) set_tile(t0);
+    auto issue_next = [&](int q) {
+        eng.issue(q % DE::kStages, lk * DE::kStageBytes);
+        if (++lk == ns) { lk = 0; if (++lt < ntile) set_tile(t0 + lt); }
+    };
+#pragma unroll
+    for (int q = 0; q < DE::kDepth; ++q)
+        if (q < total) issue_next(q);
+    int s = 0;  // global stage counter (the DMA cursor runs kDepth stages ahead, across tiles)
+    for (int ct = 0; ct < ntile; ++ct) {
+        for (int k = 0; k < ns; ++k, ++s) {
+            const int ahead = total - 1 - s;
+            eng.wait_stage(eng.clamp_ahead(ahead));
+            if (s + DE::kDepth < total) issue_next(s + DE::kDepth);
+            eng.compute(s % DE::kStages, acc);
+        }
+        fwd_tile_update<TL>(acc, (t0 + ct) * TL::BM, V, m, l);
+        zero_acc<TL>(acc);
+    }
+    fwd_write_partials<TL>(m, l, reinterpret_cast<float *>(lds), tok0, nv, idx, split, N, part_m, part_s);
 }
 
 // ------------------------------------------------------ merge + label gather
@@ -248,10 +387,11 @@ FwdShape fwd_shape(int64_t N, int64_t D, int64_t V) {
     s.N = N;
     s.D = D;
     s.V = V;
-    s.n_vtiles = (int)ceil_div(V, kBlockVocab);
-    s.n_rtiles = (int)ceil_div(N, kBlockRows);
+    s.n_vtiles = (int)ceil_div(V, kTileVocab);
+    s.n_rtiles = (int)ceil_div(N, kTileRows);
     int S = (int)ceil_div(kFwdTargetGroups, s.n_rtiles);
     if (S > kMaxSplits) S = kMaxSplits;
+    if (S > 4) S &= ~3;  // a multiple of 4 lets the XCD placement group splits
     if (S > s.n_vtiles) S = s.n_vtiles;
     if (S < 1) S = 1;
     s.S = S;
@@ -288,8 +428,12 @@ static hipError_t forward_t(const T *H, const T *E, const int64_t *labels, const
     hipError_t e = launch_compact(labels, s.N, ignore_index, w.idx, w.nvalid, st);
     if (e != hipSuccess) return e;
     const int groups = s.S * s.n_rtiles;
-    hipLaunchKernelGGL(k_fwd<T>, dim3(groups), dim3(TileFR::kThreads), 0, st, H, E, w.idx, w.nvalid,
-                       (int)s.D, (int)s.V, s.N, s.n_vtiles, s.S, w.part_m, w.part_s);
+    if ((s.D * (int64_t)sizeof(T)) % kLogitRowBytes == 0)
+        hipLaunchKernelGGL((k_fwd_dma<T, TileFD>), dim3(groups), dim3(TileFD::kThreads), 0, st, H, E, w.idx, w.nvalid,
+                           (int)s.D, (int)s.V, s.N, s.n_vtiles, s.S, s.n_rtiles, w.part_m, w.part_s);
+    else
+        hipLaunchKernelGGL(k_fwd<T>, dim3(groups), dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid,
+                           (int)s.D, (int)s.V, s.N, s.n_vtiles, s.S, s.n_rtiles, w.part_m, w.part_s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_merge<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, H, E, labels,
                        w.part_m, w.part_s, s.S, s.N, (int)s.D, s.V, ignore_index, loss, lse);
