@@ -172,3 +172,21 @@ def vocab_order(keys):
     keys = np.asarray(keys)
     ids = np.arange(keys.size)
     return np.lexsort((ids, -keys)).astype(np.int64)
+
+
+def lse_matmul(H64, E64, labels, ignore_index=-100, row_chunk=512):
+    """lse_i for every row, with a library matrix product (numpy, float64)
+    as the logit step: z = H E^T in row chunks, then the definition
+    lse = m + log sum exp(z - m).  Used where the full C loop would take
+    minutes (full-size workloads); ignored rows get 0."""
+    H64, E64 = _c64(H64), _c64(E64)
+    N = H64.shape[0]
+    out = np.zeros(N)
+    Et = np.ascontiguousarray(E64.T)
+    for r0 in range(0, N, row_chunk):
+        z = H64[r0:r0 + row_chunk] @ Et
+        m = z.max(axis=1, keepdims=True)
+        out[r0:r0 + row_chunk] = (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))[:, 0]
+    out[np.asarray(labels) == ignore_index] = 0.0
+    return out
+

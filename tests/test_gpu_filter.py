@@ -1,0 +1,79 @@
+"""Gradient filter contract (skip a block when every softmax entry in it is
+below eps; the -dloss one-hot part is never filtered), checked against the
+fp64 oracle and closed forms."""
+import numpy as np
+import pytest
+
+import oracle
+from linear_cross_entropy_cce_amd import inputs
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _pow2_dloss(x, k=10):
+    return np.where(x.labels != x.ignore_index, 2.0 ** -k, 0.0).astype(np.float32)
+
+
+def test_eps_above_one_is_the_label_term_closed_form():
+    # eps > 1 > every p: no softmax part survives, so dH_i = -dloss_i e_{y_i}
+    # and dE_v = -sum_{i: y_i = v} dloss_i h_i.  With dloss a power of two
+    # the dH rows are exact in bf16.
+    x = inputs.make_workload(4, N=600, D=256, V=3000)
+    G.say("filter eps=2 closed form")
+    dl = _pow2_dloss(x)
+    out = G.run_gpu(x, dl, eps=2.0)
+    assert out["stats"][0] == 0 and out["stats"][1] > 0
+    H = oracle.as_f64(x.H, x.dtype)
+    E = oracle.as_f64(x.E, x.dtype)
+    valid = x.labels != x.ignore_index
+    want_dH = np.zeros_like(H)
+    want_dH[valid] = -dl[valid, None].astype(np.float64) * E[x.labels[valid]]
+    assert np.array_equal(out["dH"], want_dH)
+    want_dE = np.zeros_like(E)
+    np.add.at(want_dE, x.labels[valid], -dl[valid, None].astype(np.float64) * H[valid])
+    err = np.abs(out["dE"] - want_dE)
+    assert np.all(err <= 2.0 ** -8 * np.abs(want_dE) + 1e-12), float(err.max())
+
+
+def test_kept_blocks_do_not_grow_with_eps():
+    x = inputs.make_workload(2, N=640, D=128, V=6000)  # peaked at small D: partial filtering
+    dl = G.mean_dloss(x)
+    kept = []
+    for eps in (0.0, 2.0 ** -24, 2.0 ** -16, 2.0 ** -12, 2.0 ** -8, 0.5, 2.0):
+        G.say(f"filter monotone eps={eps}")
+        out = G.run_gpu(x, dl, eps=eps)
+        kept.append(int(out["stats"][0]))
+        assert out["stats"][0] + out["stats"][1] <= out["stats"][2]
+    assert all(a >= b for a, b in zip(kept, kept[1:])), kept
+    assert kept[0] == out["stats"][2] and kept[-1] == 0
+
+
+@pytest.mark.parametrize("k,N,D,V,eps", [(3, 600, 512, 5000, 2.0 ** -8), (4, 512, 384, 3000, 2.0 ** -8),
+                                         (2, 700, 256, 9000, 2.0 ** -12)])
+def test_filtered_error_within_bound(k, N, D, V, eps):
+    # Every skipped entry has p < eps, so elementwise
+    #   |dH_gpu - dH| <= dloss_i (eps sum_v |e_vd| + 2^-8 max_v |e_vd|) + 2^-8 |dH|
+    #   |dE_gpu - dE| <= eps sum_i dloss_i |h_id| + 2^-8 max_i |h_id| sum_i |g_iv| + 2^-8 |dE|
+    # where the 2^-8 terms cover bf16 rounding of the gradient tile and of
+    # the outputs.  The bound does not depend on the block geometry.
+    x = inputs.make_workload(k, N=N, D=D, V=V)
+    G.say(f"filter bound w{k} eps={eps}")
+    dl = G.mean_dloss(x)
+    out = G.run_gpu(x, dl, eps=eps)
+    _, lse, dH, dE = G.oracle_full(x, dl, "mean")
+    H = oracle.as_f64(x.H, x.dtype)
+    E = oracle.as_f64(x.E, x.dtype)
+    valid = x.labels != x.ignore_index
+    dl64 = dl.astype(np.float64)
+    bH = dl64[:, None] * (eps * np.abs(E).sum(axis=0)[None, :] + 2.0 ** -8 * np.abs(E).max(axis=0)[None, :]) \
+        + 2.0 ** -8 * np.abs(dH)
+    assert np.all(np.abs(out["dH"] - dH) <= bH + 1e-12)
+    P = np.exp(H[valid] @ E.T - lse[valid, None])
+    onehot = np.zeros_like(P)
+    onehot[np.arange(P.shape[0]), x.labels[valid]] = 1.0
+    gabs = (dl64[valid, None] * (P + onehot)).sum(axis=0)  # sum_i |g_iv|
+    bE = eps * (dl64[valid, None] * np.abs(H[valid])).sum(axis=0)[None, :] \
+        + 2.0 ** -8 * gabs[:, None] * np.abs(H[valid]).max(axis=0)[None, :] + 2.0 ** -8 * np.abs(dE)
+    assert np.all(np.abs(out["dE"] - dE) <= bE + 1e-12)
+    assert out["stats"][0] < out["stats"][2] or eps < 2.0 ** -10  # something was skipped at 2^-8

@@ -1,0 +1,59 @@
+"""The five workloads at their full sizes, in the launch configuration the
+benchmark times.  The oracle computes sampled outputs one by one (lse, loss
+and dH rows; dE rows where every row's lse is affordable) and properties that
+hold at any size check the rest:
+  sum_v dE_v = 0 (every logit-gradient row sums to zero), and
+  sum_v <dE_v, e_v> = sum_i <dH_i, h_i> (both are sum_iv g_iv z_iv)."""
+import numpy as np
+import pytest
+
+import oracle
+from linear_cross_entropy_cce_amd import inputs
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_full_size(k):
+    x = inputs.make_workload(k)
+    eps = x.eps
+    sort = k == 5
+    G.say(f"full size w{k} N={x.N} D={x.D} V={x.V} eps={eps} sort={sort}")
+    dl = G.mean_dloss(x)
+    out = G.run_gpu(x, dl, eps=eps, sort=sort)
+    H = oracle.as_f64(x.H, x.dtype)
+    E = oracle.as_f64(x.E, x.dtype)
+    valid = x.labels != x.ignore_index
+    rng = np.random.default_rng(k)
+    vrows = np.nonzero(valid)[0]
+    rows = np.unique(np.concatenate([vrows[:2], vrows[-2:], rng.choice(vrows, 8, replace=False)]))
+    lse, loss, dH = oracle.rows(H, E, x.labels, dl.astype(np.float64), rows, x.ignore_index)
+    tol = G.lse_tol(x)
+    m = np.ones(rows.size, dtype=bool)
+    G.assert_rows("lse", out["lse"][rows], lse, m, tol)
+    G.assert_rows("loss", out["loss"][rows], loss, m, tol, lse)
+    assert np.all(out["lse"][~valid] == 0) and np.all(out["loss"][~valid] == 0)
+    assert np.all(out["dH"][~valid] == 0)
+    # dH rows: relative Frobenius over the sample, floor = label term
+    LH = -dl[rows, None].astype(np.float64) * E[x.labels[rows]]
+    G.assert_grad("dH rows", out["dH"][rows], dH, LH, 2e-2)
+    # properties over the whole of dE
+    dEg, dHg = out["dE"], out["dH"]
+    label_scale = np.linalg.norm((dl[valid, None].astype(np.float64) * H[valid]).sum(axis=0)) + \
+        np.sqrt((dl[valid].astype(np.float64) ** 2 * (H[valid] ** 2).sum(axis=1)).sum())
+    assert np.linalg.norm(dEg.sum(axis=0)) <= 2e-2 * label_scale
+    s_e = float(np.sum(dEg * E))
+    s_h = float(np.sum(dHg * H))
+    scale = float(np.sum(dl[valid].astype(np.float64) * np.abs((H[valid] * E[x.labels[valid]]).sum(axis=1))))
+    assert abs(s_e - s_h) <= 2e-2 * max(scale, 1e-30), (s_e, s_h, scale)
+    if k in (1, 4):
+        # every row's lse is affordable here: sample dE rows from the oracle
+        lse_all = oracle.lse_matmul(H, E, x.labels, x.ignore_index)
+        vids = np.unique(np.concatenate([x.labels[vrows[:6]], rng.integers(0, x.V, 6)]))
+        dE = oracle.dE_rows(H, E, x.labels, lse_all, dl.astype(np.float64), vids, x.ignore_index)
+        LE = np.zeros_like(dE)
+        for j, v in enumerate(vids):
+            sel = x.labels == v
+            LE[j] = -(dl[sel, None].astype(np.float64) * H[sel]).sum(axis=0)
+        G.assert_grad("dE rows", dEg[vids], dE, LE, 2e-2)

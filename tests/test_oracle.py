@@ -205,3 +205,18 @@ def test_bf16_conversion_is_exact():
     bits = np.array([0x3F80, 0xBF80, 0x0001, 0x7F7F, 0x4049], dtype=np.uint16)
     want = [1.0, -1.0, 2.0 ** -133, 3.3895313892515355e38, 3.140625]
     np.testing.assert_array_equal(oracle.as_f64(bits, "bf16"), want)
+
+
+def test_lse_matmul_against_torch(rng):
+    # The matmul-based lse (used for full-size checks) is the same definition:
+    # pin it to torch.logsumexp and to the loop oracle.
+    N, D, V = 70, 16, 300
+    H, E, y, _ = _rand(rng, N, D, V, ign_rows=(4,), scale=3.0)
+    got = oracle.lse_matmul(H, E, y, IGN, row_chunk=32)
+    want = torch.logsumexp(torch.tensor(H) @ torch.tensor(E).T, dim=1).numpy()
+    valid = y != IGN
+    np.testing.assert_allclose(got[valid], want[valid], rtol=1e-13, atol=1e-13)
+    assert got[4] == 0
+    _, lse_loop = oracle.forward(H, E, y, IGN)
+    np.testing.assert_allclose(got, lse_loop, rtol=1e-12, atol=1e-12)
+
