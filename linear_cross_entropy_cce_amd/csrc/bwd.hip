@@ -327,14 +327,16 @@ __global__ __launch_bounds__(TL::kThreads) void k_bwd_g_dma(
     }
     f32x16 acc[TL::TM][TL::TN];
     zero_acc<TL>(acc);
+    {
 #pragma unroll
-    for (int q = 0; q < DE::kDepth; ++q)
-        if (q < ns) eng.issue(q, q * DE::kStageBytes);
-    for (int s = 0; s < ns; ++s) {
-        const int ahead = ns - 1 - s;
-        eng.wait_stage(eng.clamp_ahead(ahead));
-        if (s + DE::kDepth < ns) eng.issue((s + DE::kDepth) % DE::kStages, (s + DE::kDepth) * DE::kStageBytes);
-        eng.compute(s % DE::kStages, acc);
+        for (int q = 0; q < DE::kDepth; ++q)
+            if (q < ns) eng.issue(q, q * DE::kStageBytes);
+        for (int s = 0; s < ns; ++s) {
+            const int ahead = ns - 1 - s;
+            eng.wait_stage(eng.clamp_ahead(ahead));
+            if (s + DE::kDepth < ns) eng.issue((s + DE::kDepth) % DE::kStages, (s + DE::kDepth) * DE::kStageBytes);
+            eng.compute(s % DE::kStages, acc);
+        }
     }
     __syncthreads();
     bwd_g_epilogue<T, TL>(acc, tok0, nv, p0, V, ct, rt, live_ld, eps, idx, perm, inv_perm, labels, lse, dloss, Gt,
