@@ -24,6 +24,8 @@
 // The slice costs 2 bytes per logit to write and 4 to read back, against
 // about 8 D flops per logit, and its size is bounded (rows x kChunkVocab), so
 // extra memory is linear in N and V and never rows x vocabulary.
+#include <math.h>
+
 #include "cce_device.hpp"
 #include "cce_internal.hpp"
 
@@ -44,7 +46,34 @@ __global__ void k_inv_perm(const int32_t *__restrict__ perm, int V, int32_t *__r
 }
 
 __global__ void k_stats_init(int64_t *stats) {
-    if (threadIdx.x < 4) stats[threadIdx.x] = 0;
+    if (threadIdx.x < 5) stats[threadIdx.x] = 0;
+}
+
+// lmin[rt] = smallest lse over the valid tokens of token tile rt (+inf if none).
+__global__ __launch_bounds__(256) void k_lse_min(const float *__restrict__ lse, const int32_t *__restrict__ idx,
+                                                 const int32_t *__restrict__ nvalid_p, float *__restrict__ lmin) {
+    __shared__ float part[4];
+    const int tok = blockIdx.x * kTileRows + threadIdx.x;
+    float v = tok < *nvalid_p ? lse[idx[tok]] : __builtin_huge_valf();
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) lmin[blockIdx.x] = fminf(fminf(part[0], part[1]), fminf(part[2], part[3]));
+}
+
+// True when every p in logit tile (rt, vocabulary tile vt) is provably below
+// eps / 2: the tile's largest logit T minus the smallest lse L of its tokens
+// is below thr = ln(eps / 2), with a relative margin for fp32 rounding of the
+// recomputed logits and of T - L.  The filter then keeps nothing of the
+// tile's softmax part, so its recompute can be left out without changing a
+// bit of the result.  NaN never skips.
+__device__ __forceinline__ bool tile_below(const float *__restrict__ tbound, int64_t tb_ld, const float *__restrict__ lmin,
+                                           float thr, int rt, int vt) {
+    if (!tbound) return false;
+    const float T = tbound[(int64_t)rt * tb_ld + vt];
+    const float L = lmin[rt];
+    return (T - L) + 0x1p-10f * (fabsf(T) + fabsf(L)) < thr;
 }
 
 __global__ void k_stats_fin(int64_t *stats, const int32_t *__restrict__ nvalid_p, int64_t n_vtiles) {
@@ -148,7 +177,7 @@ __device__ __forceinline__ void bwd_g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], in
                                                const int64_t *__restrict__ labels, const float *__restrict__ lse,
                                                const float *__restrict__ dloss, T *__restrict__ Gt, int64_t ldt,
                                                T *__restrict__ Gn, int64_t ldn, uint8_t *__restrict__ live,
-                                               int64_t *__restrict__ stats, int *qflag) {
+                                               int64_t *__restrict__ stats, int *qflag, bool no_softmax) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave % TL::WM, wn = wave / TL::WM;
@@ -177,17 +206,19 @@ __device__ __forceinline__ void bwd_g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], in
         }
     }
     const int vlim = row_limit<TL>(V - p0);  // entry (tm, r) is a real vocabulary row iff acc_row_const < vlim
+    if (!no_softmax) {
 #pragma unroll
-    for (int tn = 0; tn < TL::TN; ++tn)
+        for (int tn = 0; tn < TL::TN; ++tn)
 #pragma unroll
-        for (int tm = 0; tm < TL::TM; ++tm)
+            for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const bool ok = tok_ok[tn] && (acc_row_const(tm, r) < vlim);
-                const float p = ok ? __builtin_amdgcn_exp2f((acc[tm][tn][r] - lse_t[tn]) * kLog2e) : 0.f;
-                acc[tm][tn][r] = p;
-                any_live |= ok && (p >= eps);
-            }
+                for (int r = 0; r < 16; ++r) {
+                    const bool ok = tok_ok[tn] && (acc_row_const(tm, r) < vlim);
+                    const float p = ok ? __builtin_amdgcn_exp2f((acc[tm][tn][r] - lse_t[tn]) * kLog2e) : 0.f;
+                    acc[tm][tn][r] = p;
+                    any_live |= ok && (p >= eps);
+                }
+    }
     const uint64_t bl = __ballot(any_live), bb = __ballot(any_label);
     if (lane == 0 && (bl | bb)) atomicOr(&qflag[quad], (bl ? 1 : 0) | (bb ? 2 : 0));
     __syncthreads();
@@ -197,6 +228,9 @@ __device__ __forceinline__ void bwd_g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], in
         const int rb = 2 * rt + (tid & 1), cb = 2 * ct + (tid >> 1);
         live[(int64_t)rb * live_ld + cb] = (uint8_t)st;
         if (stats && st) atomicAdd(reinterpret_cast<unsigned long long *>(stats + (st == 1 ? 0 : 1)), 1ull);
+        // filter blocks whose logits were recomputed (real rows and vocabulary entries only)
+        if (stats && !no_softmax && rb * kBlockRows < nv && p0 + (tid >> 1) * kBlockVocab < V)
+            atomicAdd(reinterpret_cast<unsigned long long *>(stats + 4), 1ull);
     }
     const int qf = qflag[quad];
     const int status = (qf & 1) ? 1 : ((qf & 2) ? 2 : 0);
@@ -241,7 +275,8 @@ __global__ __launch_bounds__(TileF::kThreads) void k_bwd_g(
     const int32_t *__restrict__ inv_perm, const int64_t *__restrict__ labels,
     const float *__restrict__ lse, const float *__restrict__ dloss, int D, int V, int chunk_v0, int n_ct,
     int live_ld, float eps, T *__restrict__ Gt, int64_t ldt, T *__restrict__ Gn, int64_t ldn,
-    uint8_t *__restrict__ live, int64_t *__restrict__ stats) {
+    uint8_t *__restrict__ live, int64_t *__restrict__ stats, const float *__restrict__ tbound, int64_t tb_ld,
+    const float *__restrict__ lmin, float thr) {
     using TL = TileF;
     __shared__ u32x4 lds[TL::kLdsChunks];
     __shared__ int qflag[4];  // bit 0: some p >= eps, bit 1: a label in the block
@@ -256,6 +291,15 @@ __global__ __launch_bounds__(TileF::kThreads) void k_bwd_g(
     const int kvalid = D * (int)sizeof(T);
     const int ns = (kvalid + TL::kStageBytes - 1) / TL::kStageBytes;
     if (tid < 4) qflag[tid] = 0;
+    const bool skip = tile_below(tbound, tb_ld, lmin, thr, rt, p0 / kTileVocab);
+    f32x16 acc[TL::TM][TL::TN];
+    zero_acc<TL>(acc);
+    if (skip) {
+        __syncthreads();
+        bwd_g_epilogue<T, TL>(acc, tok0, nv, p0, V, ct, rt, live_ld, eps, idx, perm, inv_perm, labels, lse, dloss,
+                              Gt, ldt, Gn, ldn, live, stats, qflag, true);
+        return;
+    }
 
     Engine<T, TL> eng;
 #pragma unroll
@@ -269,8 +313,6 @@ __global__ __launch_bounds__(TileF::kThreads) void k_bwd_g(
         const int tok = tok0 + eng.row(j);
         eng.pb[j] = tok < nv ? reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb : nullptr;
     }
-    f32x16 acc[TL::TM][TL::TN];
-    zero_acc<TL>(acc);
     eng.load(0, kvalid);
     eng.store(lds);
     __syncthreads();
@@ -283,7 +325,7 @@ __global__ __launch_bounds__(TileF::kThreads) void k_bwd_g(
     }
 
     bwd_g_epilogue<T, TL>(acc, tok0, nv, p0, V, ct, rt, live_ld, eps, idx, perm, inv_perm, labels, lse, dloss, Gt,
-                          ldt, Gn, ldn, live, stats, qflag);
+                          ldt, Gn, ldn, live, stats, qflag, false);
 }
 
 // The recompute on the DMA pipeline (needs D * sizeof(T) % 64 == 0).  Rows
@@ -296,7 +338,8 @@ __global__ __launch_bounds__(TL::kThreads) void k_bwd_g_dma(
     const int32_t *__restrict__ inv_perm, const int64_t *__restrict__ labels,
     const float *__restrict__ lse, const float *__restrict__ dloss, int D, int V, int chunk_v0, int n_ct,
     int live_ld, float eps, T *__restrict__ Gt, int64_t ldt, T *__restrict__ Gn, int64_t ldn,
-    uint8_t *__restrict__ live, int64_t *__restrict__ stats) {
+    uint8_t *__restrict__ live, int64_t *__restrict__ stats, const float *__restrict__ tbound, int64_t tb_ld,
+    const float *__restrict__ lmin, float thr) {
     using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
     __shared__ u32x4 lds[DE::kLdsChunks];
     __shared__ int qflag[4];
@@ -309,6 +352,14 @@ __global__ __launch_bounds__(TL::kThreads) void k_bwd_g_dma(
     const size_t rowb = (size_t)D * sizeof(T);
     const int ns = D * (int)sizeof(T) / DE::kStageBytes;
     if (threadIdx.x < 4) qflag[threadIdx.x] = 0;
+    f32x16 acc[TL::TM][TL::TN];
+    zero_acc<TL>(acc);
+    if (tile_below(tbound, tb_ld, lmin, thr, rt, p0 / kTileVocab)) {
+        __syncthreads();
+        bwd_g_epilogue<T, TL>(acc, tok0, nv, p0, V, ct, rt, live_ld, eps, idx, perm, inv_perm, labels, lse, dloss,
+                              Gt, ldt, Gn, ldn, live, stats, qflag, true);
+        return;
+    }
 
     DE eng(lds);
 #pragma unroll
@@ -325,8 +376,6 @@ __global__ __launch_bounds__(TL::kThreads) void k_bwd_g_dma(
         const int tok = min(tok0 + r, nv - 1);
         eng.pb[j] = reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb + DE::chunk_off(r);
     }
-    f32x16 acc[TL::TM][TL::TN];
-    zero_acc<TL>(acc);
     {
 #pragma unroll
         for (int q = 0; q < DE::kDepth; ++q)
@@ -340,7 +389,7 @@ __global__ __launch_bounds__(TL::kThreads) void k_bwd_g_dma(
     }
     __syncthreads();
     bwd_g_epilogue<T, TL>(acc, tok0, nv, p0, V, ct, rt, live_ld, eps, idx, perm, inv_perm, labels, lse, dloss, Gt,
-                          ldt, Gn, ldn, live, stats, qflag);
+                          ldt, Gn, ldn, live, stats, qflag, false);
 }
 
 // ------------------------------------------------------------- dE (Kahan)
@@ -583,6 +632,7 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     w.nvalid = c.take<int32_t>(1);
     w.inv_perm = c.take<int32_t>(s.V);
     w.live = c.take<uint8_t>((size_t)(s.Np / kBlockRows) * (s.Vc / kBlockVocab));
+    w.lmin = c.take<float>((size_t)s.n_rtiles);
     w.dh_acc = s.n_chunks > 1 ? c.take<float>((size_t)s.Np * s.D) : nullptr;
     w.Ht = c.take<char>(elem * (size_t)s.D * s.Np);
     w.Gt = c.take<char>(elem * (size_t)s.Vc * s.Np);
@@ -601,11 +651,23 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
 
 template <typename T>
 static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, const float *lse,
-                             const float *dloss, const BwdShape &s, int64_t ignore_index, float eps,
-                             const int32_t *perm, unsigned flags, T *dH, T *dE, int64_t *stats,
+                             const float *dloss, const float *tile_bound, const BwdShape &s, int64_t ignore_index,
+                             float eps, const int32_t *perm, unsigned flags, T *dH, T *dE, int64_t *stats,
                              const BwdWs &w, hipStream_t st) {
     const int D = (int)s.D, V = (int)s.V;
     CCE_TRY(launch_compact(labels, s.N, ignore_index, w.idx, w.nvalid, st));
+    // The tile bound is in the natural vocabulary order and only says something
+    // when filtering is on.  thr = ln(eps / 2), rounded towards -inf.
+    const float *tb = (tile_bound && !perm && eps > 0.f) ? tile_bound : nullptr;
+    float thr = 0.f;
+    if (tb) {
+        thr = (float)(log((double)eps) - log(2.0));
+        thr = nextafterf(thr, -__builtin_huge_valf());
+        hipLaunchKernelGGL(k_lse_min, dim3((unsigned)s.n_rtiles), dim3(kTileRows), 0, st, lse, w.idx, w.nvalid,
+                           w.lmin);
+        CCE_LAUNCHED();
+    }
+    const int64_t tb_ld = ceil_div(s.V, kTileVocab);
     if (perm) {
         hipLaunchKernelGGL(k_inv_perm, dim3((unsigned)ceil_div(V, 256)), dim3(256), 0, st, perm, V, w.inv_perm);
         CCE_LAUNCHED();
@@ -648,11 +710,13 @@ static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, cons
         if (dma_g)
             hipLaunchKernelGGL((k_bwd_g_dma<T, TileFD>), dim3((unsigned)(n_ct * s.n_rtiles)), dim3(TileFD::kThreads), 0, st, H,
                                E, w.idx, w.nvalid, perm, perm ? w.inv_perm : nullptr, labels, lse, dloss, D, V, cv0,
-                               n_ct, live_ld, eps, Gt, (int64_t)s.Np, Gn, (int64_t)s.Vc, w.live, stats);
+                               n_ct, live_ld, eps, Gt, (int64_t)s.Np, Gn, (int64_t)s.Vc, w.live, stats, tb, tb_ld,
+                               w.lmin, thr);
         else
             hipLaunchKernelGGL(k_bwd_g<T>, dim3((unsigned)(n_ct * s.n_rtiles)), dim3(TileF::kThreads), 0, st, H, E,
                                w.idx, w.nvalid, perm, perm ? w.inv_perm : nullptr, labels, lse, dloss, D, V, cv0,
-                               n_ct, live_ld, eps, Gt, (int64_t)s.Np, Gn, (int64_t)s.Vc, w.live, stats);
+                               n_ct, live_ld, eps, Gt, (int64_t)s.Np, Gn, (int64_t)s.Vc, w.live, stats, tb, tb_ld,
+                               w.lmin, thr);
         CCE_LAUNCHED();
         if (flags & CCE_BWD_NO_KAHAN)
             hipLaunchKernelGGL((k_de<T, false>), dim3((unsigned)(n_cb * n_dt)), dim3(TileG::kThreads), 0, st, Gt,
@@ -678,16 +742,16 @@ static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, cons
 }
 
 hipError_t launch_backward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
-                           const float *lse, const float *dloss, const BwdShape &s,
+                           const float *lse, const float *dloss, const float *tile_bound, const BwdShape &s,
                            int64_t ignore_index, float eps, const int32_t *perm, unsigned flags,
                            void *dH, void *dE, int64_t *stats, const BwdWs &w, hipStream_t st) {
     if (dt == CCE_BF16)
         return backward_t<bf16_t>(static_cast<const bf16_t *>(H), static_cast<const bf16_t *>(E), labels, lse,
-                                  dloss, s, ignore_index, eps, perm, flags, static_cast<bf16_t *>(dH),
+                                  dloss, tile_bound, s, ignore_index, eps, perm, flags, static_cast<bf16_t *>(dH),
                                   static_cast<bf16_t *>(dE), stats, w, st);
-    return backward_t<float>(static_cast<const float *>(H), static_cast<const float *>(E), labels, lse, dloss, s,
-                             ignore_index, eps, perm, flags, static_cast<float *>(dH), static_cast<float *>(dE),
-                             stats, w, st);
+    return backward_t<float>(static_cast<const float *>(H), static_cast<const float *>(E), labels, lse, dloss,
+                             tile_bound, s, ignore_index, eps, perm, flags, static_cast<float *>(dH),
+                             static_cast<float *>(dE), stats, w, st);
 }
 
 }  // namespace cce

@@ -32,6 +32,29 @@ template <typename T> __device__ __forceinline__ T from_f32(float f);
 template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) { return f32_to_bf16(f); }
 
+// Order-preserving map of fp32 onto int32 (for non-NaN values): a < b as
+// floats iff enc(a) < enc(b) as signed integers, so an integer atomic max
+// computes a float max.  dec inverts enc.
+__device__ __forceinline__ int bound_enc(float f) {
+    const int i = __float_as_int(f);
+    return i < 0 ? i ^ 0x7FFFFFFF : i;
+}
+__device__ __forceinline__ float bound_dec(int i) { return __int_as_float(i < 0 ? i ^ 0x7FFFFFFF : i); }
+
+// Largest of the 64 lanes' values, returned to every lane (a wave-uniform
+// value).  DPP row operations of the GFX9 family: max within quads, within
+// half-rows and rows by mirroring, then across the four rows by the row-15
+// and row-31 broadcasts, which leave the wave maximum in lane 63.
+__device__ __forceinline__ int wave_max_i32(int v) {
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1, 0, 3, 2]
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2, 3, 0, 1]
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));  // row_mirror
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xA, 0xF, false));  // row_bcast:15 into rows 1, 3
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xC, 0xF, false));  // row_bcast:31 into rows 2, 3
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 // Elements of T per 16-byte chunk.
 template <typename T> struct ChunkElems;
 template <> struct ChunkElems<float> { static constexpr int value = 4; };

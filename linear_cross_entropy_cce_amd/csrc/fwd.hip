@@ -106,10 +106,12 @@ __device__ __forceinline__ void fwd_place(int b, int G, int S, int R, int &split
     }
 }
 
+// Returns the largest logit this lane holds in the tile (rows past V excluded).
 template <class TL>
-__device__ __forceinline__ void fwd_tile_update(f32x16 (&acc)[TL::TM][TL::TN], int v0, int V, float (&m)[TL::TN],
-                                                float (&l)[TL::TN]) {
+__device__ __forceinline__ float fwd_tile_update(f32x16 (&acc)[TL::TM][TL::TN], int v0, int V, float (&m)[TL::TN],
+                                                 float (&l)[TL::TN]) {
     const bool full = v0 + TL::BM <= V;
+    float tmax = kNegInf;
     // One token column at a time keeps at most TM x 16 values in VGPRs; the
     // scheduling barriers stop the compiler from hoisting every column's
     // accumulator reads to the top (which would spill).
@@ -132,6 +134,7 @@ __device__ __forceinline__ void fwd_tile_update(f32x16 (&acc)[TL::TM][TL::TN], i
                     mx = fmaxf(mx, acc[tm][tn][r]);
                 }
         }
+        tmax = fmaxf(tmax, mx);
         const float mn = fmaxf(m[tn], mx * kLog2e);
         if (mn == kNegInf) continue;
         float sum = 0.f;
@@ -142,6 +145,37 @@ __device__ __forceinline__ void fwd_tile_update(f32x16 (&acc)[TL::TM][TL::TN], i
         l[tn] = l[tn] * __builtin_amdgcn_exp2f(m[tn] - mn) + sum;
         m[tn] = mn;
     }
+    return tmax;
+}
+
+// Tile-bound table: the largest logit of every (256-token tile, 256-entry
+// vocabulary tile), combined over the workgroup's waves with an integer atomic
+// max on the order-preserving encoding.  Lane j of each wave keeps the maximum
+// of the j-th tile of a group of 64 and the wave writes the group with one
+// vector atomic, so the table costs one memory instruction per 64 tiles.
+struct BoundSink {
+    int *row;   // table row of this token tile, from the split's first vocabulary tile; null: no table
+    int keep = 0;
+    __device__ __forceinline__ void tile(int ct, float lane_max, bool last) {
+        if (!row) return;
+        const int m = wave_max_i32(bound_enc(lane_max));
+        const int lane = threadIdx.x & 63;
+        const int j = ct & 63;
+        if (lane == j) keep = m;
+        if (j == 63 || last) {
+            if (lane <= j) atomicMax(row + (ct - j) + lane, keep);
+        }
+    }
+};
+
+__global__ __launch_bounds__(256) void k_bound_init(int *__restrict__ t, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) t[i] = bound_enc(kNegInf);
+}
+
+__global__ __launch_bounds__(256) void k_bound_decode(int *__restrict__ t, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) reinterpret_cast<float *>(t)[i] = bound_dec(t[i]);
 }
 
 // Merges (m, l) over the two half-waves and the WM waves that hold the same
@@ -191,7 +225,7 @@ template <typename T>
 __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
     const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nvalid_p, int D, int V, int64_t N, int n_vtiles, int S, int R,
-    float *__restrict__ part_m, float *__restrict__ part_s) {
+    float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
     using TL = TileF;
     __shared__ u32x4 lds[TL::kLdsChunks];
     const int nv = *nvalid_p;
@@ -206,6 +240,7 @@ __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
     const size_t rowb = (size_t)D * sizeof(T);
     const int kvalid = D * (int)sizeof(T);
     const int ns = (kvalid + TL::kStageBytes - 1) / TL::kStageBytes;
+    BoundSink bs{tbound ? tbound + (int64_t)rt * n_vtiles + t0 : nullptr};
 
     Engine<T, TL> eng;
 #pragma unroll
@@ -243,7 +278,7 @@ __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
             eng.compute(lds + (s & 1) * TL::kStage, acc);
             if (++ck == ns) {
                 ck = 0;
-                fwd_tile_update<TL>(acc, (t0 + ct) * TL::BM, V, m, l);
+                bs.tile(ct, fwd_tile_update<TL>(acc, (t0 + ct) * TL::BM, V, m, l), ct == ntile - 1);
                 ++ct;
                 zero_acc<TL>(acc);
             }
@@ -266,7 +301,7 @@ template <typename T, class TL>
 __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
     const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nvalid_p, int D, int V, int64_t N, int n_vtiles, int S, int R,
-    float *__restrict__ part_m, float *__restrict__ part_s) {
+    float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
     using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
     __shared__ u32x4 lds[DE::kLdsChunks];
     const int nv = *nvalid_p;
@@ -279,6 +314,7 @@ __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
     const int ntile = t1 - t0;
     const size_t rowb = (size_t)D * sizeof(T);
     const int ns = D * (int)sizeof(T) / DE::kStageBytes;
+    BoundSink bs{tbound ? tbound + (int64_t)rt * n_vtiles + t0 : nullptr};
 
     DE eng(lds);
 #pragma unroll
@@ -321,7 +357,7 @@ __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
                 if (s + DE::kDepth < total) issue_at(s + DE::kDepth);
                 eng.compute(s % DE::kStages, acc);
             }
-            fwd_tile_update<TL>(acc, (t0 + ct) * TL::BM, V, m, l);
+            bs.tile(ct, fwd_tile_update<TL>(acc, (t0 + ct) * TL::BM, V, m, l), ct == ntile - 1);
             zero_acc<TL>(acc);
         }
     }
@@ -423,31 +459,39 @@ hipError_t launch_check_labels(const int64_t *labels, int64_t N, int64_t V, int6
 
 template <typename T>
 static hipError_t forward_t(const T *H, const T *E, const int64_t *labels, const FwdShape &s,
-                            int64_t ignore_index, const FwdWs &w, float *loss, float *lse,
+                            int64_t ignore_index, const FwdWs &w, float *loss, float *lse, float *tile_bound,
                             hipStream_t st) {
     hipError_t e = launch_compact(labels, s.N, ignore_index, w.idx, w.nvalid, st);
     if (e != hipSuccess) return e;
+    int *tb = reinterpret_cast<int *>(tile_bound);
+    const int64_t nb = (int64_t)s.n_rtiles * s.n_vtiles;
+    if (tb) {
+        hipLaunchKernelGGL(k_bound_init, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, st, tb, nb);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const int groups = s.S * s.n_rtiles;
     if ((s.D * (int64_t)sizeof(T)) % kLogitRowBytes == 0)
         hipLaunchKernelGGL((k_fwd_dma<T, TileFD>), dim3(groups), dim3(TileFD::kThreads), 0, st, H, E, w.idx, w.nvalid,
-                           (int)s.D, (int)s.V, s.N, s.n_vtiles, s.S, s.n_rtiles, w.part_m, w.part_s);
+                           (int)s.D, (int)s.V, s.N, s.n_vtiles, s.S, s.n_rtiles, w.part_m, w.part_s, tb);
     else
         hipLaunchKernelGGL(k_fwd<T>, dim3(groups), dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid,
-                           (int)s.D, (int)s.V, s.N, s.n_vtiles, s.S, s.n_rtiles, w.part_m, w.part_s);
+                           (int)s.D, (int)s.V, s.N, s.n_vtiles, s.S, s.n_rtiles, w.part_m, w.part_s, tb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_merge<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, H, E, labels,
                        w.part_m, w.part_s, s.S, s.N, (int)s.D, s.V, ignore_index, loss, lse);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (tb) hipLaunchKernelGGL(k_bound_decode, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, st, tb, nb);
     return hipGetLastError();
 }
 
 hipError_t launch_forward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
                           const FwdShape &s, int64_t ignore_index, const FwdWs &w, float *loss,
-                          float *lse, hipStream_t st) {
+                          float *lse, float *tile_bound, hipStream_t st) {
     if (dt == CCE_BF16)
         return forward_t<bf16_t>(static_cast<const bf16_t *>(H), static_cast<const bf16_t *>(E), labels,
-                                 s, ignore_index, w, loss, lse, st);
+                                 s, ignore_index, w, loss, lse, tile_bound, st);
     return forward_t<float>(static_cast<const float *>(H), static_cast<const float *>(E), labels, s,
-                            ignore_index, w, loss, lse, st);
+                            ignore_index, w, loss, lse, tile_bound, st);
 }
 
 }  // namespace cce

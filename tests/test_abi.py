@@ -67,19 +67,20 @@ def test_workspace_invalid_sizes_return_zero():
 
 def _fwd(**kw):
     a = dict(H=FAKE, E=FAKE, labels=FAKE, N=16, D=64, V=100, dt=B.CCE_BF16, ign=-100, loss=FAKE, lse=FAKE,
-             ws=FAKE, ws_bytes=1 << 40, stream=None)
+             tb=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
     a.update(kw)
     return B.lib().cce_forward(a["H"], a["E"], a["labels"], a["N"], a["D"], a["V"], a["dt"], a["ign"], a["loss"],
-                               a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+                               a["lse"], a["tb"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 def _bwd(**kw):
-    a = dict(H=FAKE, E=FAKE, labels=FAKE, lse=FAKE, dloss=FAKE, N=16, D=64, V=100, dt=B.CCE_BF16, ign=-100,
-             eps=0.0, perm=None, flags=0, dH=FAKE, dE=FAKE, stats=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a = dict(H=FAKE, E=FAKE, labels=FAKE, lse=FAKE, dloss=FAKE, tb=None, N=16, D=64, V=100, dt=B.CCE_BF16,
+             ign=-100, eps=0.0, perm=None, flags=0, dH=FAKE, dE=FAKE, stats=None, ws=FAKE, ws_bytes=1 << 40,
+             stream=None)
     a.update(kw)
-    return B.lib().cce_backward(a["H"], a["E"], a["labels"], a["lse"], a["dloss"], a["N"], a["D"], a["V"], a["dt"],
-                                a["ign"], a["eps"], a["perm"], a["flags"], a["dH"], a["dE"], a["stats"], a["ws"],
-                                a["ws_bytes"], a["stream"])
+    return B.lib().cce_backward(a["H"], a["E"], a["labels"], a["lse"], a["dloss"], a["tb"], a["N"], a["D"], a["V"],
+                                a["dt"], a["ign"], a["eps"], a["perm"], a["flags"], a["dH"], a["dE"], a["stats"],
+                                a["ws"], a["ws_bytes"], a["stream"])
 
 
 def _vord(**kw):
@@ -112,6 +113,7 @@ def test_forward_specific_errors():
     assert _fwd(loss=None) == B.CCE_ERR_NULL
     assert _fwd(lse=None) == B.CCE_ERR_NULL
     assert _fwd(lse=FAKE + 2) == B.CCE_ERR_ALIGN
+    assert _fwd(tb=FAKE + 2) == B.CCE_ERR_ALIGN
     need = B.forward_workspace_bytes(16, 64, 100, B.CCE_BF16)
     assert _fwd(ws_bytes=need - 1) == B.CCE_ERR_WORKSPACE
 
@@ -128,8 +130,20 @@ def test_backward_specific_errors():
     assert _bwd(dE=FAKE + 8) == B.CCE_ERR_ALIGN
     assert _bwd(perm=FAKE + 2) == B.CCE_ERR_ALIGN
     assert _bwd(stats=FAKE + 4) == B.CCE_ERR_ALIGN
+    assert _bwd(tb=FAKE + 2) == B.CCE_ERR_ALIGN
     need = B.backward_workspace_bytes(16, 64, 100, B.CCE_BF16)
     assert _bwd(ws_bytes=need - 1) == B.CCE_ERR_WORKSPACE
+
+
+def test_tile_bound_elems():
+    # one entry per 256-token x 256-vocabulary tile; 0 on invalid sizes
+    assert B.tile_bound_elems(1, 1) == 1
+    assert B.tile_bound_elems(256, 256) == 1
+    assert B.tile_bound_elems(257, 256) == 2
+    assert B.tile_bound_elems(8192, 256000) == 32 * 1000
+    assert B.tile_bound_elems(24576, 248320) == 96 * 970
+    assert B.tile_bound_elems(0, 10) == 0
+    assert B.tile_bound_elems(10, 0) == 0
 
 
 def test_check_labels_errors():
