@@ -19,8 +19,9 @@ bool shape_ok(int64_t N, int64_t D, int64_t V) {
     if (N < 1 || N >= (int64_t(1) << 31)) return false;
     if (V < 1 || V >= (int64_t(1) << 31)) return false;
     if (D < 8 || D > 65536 || D % 8 != 0) return false;
-    // grid sizes stay below 2^31 workgroups
+    // grid sizes stay below 2^31 workgroups, and logit tiles are indexed with 32 bits
     if (ceil_div(N, kBlockRows) * ceil_div(D, 128) >= (int64_t(1) << 31)) return false;
+    if (ceil_div(N, kTileRows) * ceil_div(V, kTileVocab) >= (int64_t(1) << 31)) return false;
     return true;
 }
 

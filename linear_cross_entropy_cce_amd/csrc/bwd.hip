@@ -8,22 +8,30 @@
 // Cross-Entropy + FlexAttention", section "Contribution").
 //
 // Layout of the work.  D (2048-4096 for the heads of interest) is far wider
-// than an attention head, so dH_i and dE_v rows cannot live on chip while the
-// other dimension is swept.  The vocabulary is therefore processed in chunks
-// of at most kChunkVocab columns:
+// than an attention head, so dH_i and dE_v rows cannot stay on chip while the
+// other dimension is swept.  The gradient G = dloss (p - onehot) of every
+// kept 128 x 128 filter block is therefore written once, in two layouts, to a
+// block store, and the two gradient products read it back:
 //
-//   k_bwd_g   recompute the logit tile (MFMA, same code and K order as the
-//             forward), p = exp(z - lse), block filter, and for surviving
-//             blocks the gradient tile G = dloss (p - onehot) rounded to the
-//             input dtype, written into a [rows x chunk] slice in two layouts
-//   k_de      dE_v = sum over surviving row blocks of G^T H (MFMA), Kahan-
-//             compensated across row blocks, written once in the output dtype
-//   k_dh      dH_i += sum over surviving vocabulary blocks of G E (MFMA), fp32
-//             accumulators carried across chunks, output dtype on the last
+//   plan        which 256 x 256 logit tiles may keep a block: all of them, or,
+//               with the forward's tile-bound table, only tiles whose largest
+//               logit comes near the smallest lse of their rows, plus tiles
+//               holding a label; the listed tiles are cut, in vocabulary
+//               order, into passes whose blocks fit the store
+//   k_g_pass    per listed tile: recompute the logits (MFMA, the forward's
+//               code and K order), p = exp(z - lse), block filter, and the
+//               kept blocks' G into the store
+//   k_grad_pass both products of the pass in one launch:
+//               dE_v = sum over kept row blocks of G^T H (MFMA), Kahan-
+//               compensated across row blocks, written once;
+//               dH_i = sum over kept vocabulary blocks of G E (MFMA with E
+//               read through the LDS transpose loads), the running sum kept
+//               in fp32 across passes
 //
-// The slice costs 2 bytes per logit to write and 4 to read back, against
-// about 8 D flops per logit, and its size is bounded (rows x kChunkVocab), so
-// extra memory is linear in N and V and never rows x vocabulary.
+// When the softmax is peaked almost every tile is dropped before its logits
+// are formed and one pass holds every kept block; when it is flat the passes
+// stream through the vocabulary like dense chunks.  Extra memory is linear in
+// N and V (store, transposed H) plus one byte-sized entry per block.
 #include <math.h>
 
 #include "cce_device.hpp"
@@ -35,6 +43,22 @@ using TileF = Tile<kTileVocab, kTileRows, 2, 4>;   // logit tile: A = vocabulary
 using TileFD = TileF;                             // tile of the DMA recompute
 using TileG = Tile<128, 256, 2, 4>;               // dE / dH tile: A = a 128-row gradient block, B = 256 features
 static_assert(TileG::BM == kBlockVocab && TileG::BM == kBlockRows, "gradient GEMM rows = one filter block");
+static_assert(kTileVocab == 2 * kBlockVocab && kTileRows == 2 * kBlockRows, "a logit tile holds 2 x 2 blocks");
+
+constexpr int kBlockElems = kBlockRows * kBlockVocab;  // elements of one stored block
+constexpr int kListCap = 512;
+constexpr int kDeGroups = 2 * kPassGroups;  // persistent dE workgroups of the gradient-product kernel
+
+// Plan record: P, number of listed tiles, first vocabulary tile of each pass
+// [max_passes + 1], first list entry of each pass [max_passes + 1], store
+// slot counter of each pass [max_passes].
+struct PlanView {
+    int32_t *P, *n_active, *vt_begin, *list_begin, *counter;
+};
+__device__ __forceinline__ PlanView plan_view(int32_t *plan, int max_passes) {
+    return {plan, plan + 1, plan + 2, plan + 3 + max_passes, plan + 4 + 2 * max_passes};
+}
+static int plan_ints(int max_passes) { return 4 + 3 * max_passes; }
 
 // ------------------------------------------------------------ small kernels
 __global__ void k_inv_perm(const int32_t *__restrict__ perm, int V, int32_t *__restrict__ inv) {
@@ -47,6 +71,24 @@ __global__ void k_inv_perm(const int32_t *__restrict__ perm, int V, int32_t *__r
 
 __global__ void k_stats_init(int64_t *stats) {
     if (threadIdx.x < 5) stats[threadIdx.x] = 0;
+}
+
+__global__ void k_stats_fin(int64_t *stats, const int32_t *__restrict__ nvalid_p, int64_t n_vblocks) {
+    if (threadIdx.x == 0) {
+        const int64_t nv = *nvalid_p;
+        stats[2] = ((nv + kBlockRows - 1) / kBlockRows) * n_vblocks;
+        stats[3] = nv;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t *__restrict__ p, int64_t n, uint32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero(float *__restrict__ p, int64_t n) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i < n) *reinterpret_cast<f32x4 *>(p + i) = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // lmin[rt] = smallest lse over the valid tokens of token tile rt (+inf if none).
@@ -68,20 +110,12 @@ __global__ __launch_bounds__(256) void k_lse_min(const float *__restrict__ lse, 
 // recomputed logits and of T - L.  The filter then keeps nothing of the
 // tile's softmax part, so its recompute can be left out without changing a
 // bit of the result.  NaN never skips.
-__device__ __forceinline__ bool tile_below(const float *__restrict__ tbound, int64_t tb_ld, const float *__restrict__ lmin,
-                                           float thr, int rt, int vt) {
+__device__ __forceinline__ bool tile_below(const float *__restrict__ tbound, int64_t tb_ld,
+                                           const float *__restrict__ lmin, float thr, int rt, int vt) {
     if (!tbound) return false;
     const float T = tbound[(int64_t)rt * tb_ld + vt];
     const float L = lmin[rt];
     return (T - L) + 0x1p-10f * (fabsf(T) + fabsf(L)) < thr;
-}
-
-__global__ void k_stats_fin(int64_t *stats, const int32_t *__restrict__ nvalid_p, int64_t n_vtiles) {
-    if (threadIdx.x == 0) {
-        const int64_t nv = *nvalid_p;
-        stats[2] = ((nv + kBlockRows - 1) / kBlockRows) * n_vtiles;
-        stats[3] = nv;
-    }
 }
 
 // dst[c][j] = src[row(j)][c] for c < cols, j < n_out; rows j >= n_rows give 0.
@@ -96,7 +130,6 @@ __global__ __launch_bounds__(256) void k_transpose(const T *__restrict__ src, in
     const int n_rows = n_rows_dev ? *n_rows_dev : n_rows_host;
     const int j0 = blockIdx.x * 64;
     const int c0 = blockIdx.y * 64;
-    // load: 64 rows x (64 / CE) chunks
     for (int q = threadIdx.x; q < 64 * (64 / CE); q += 256) {
         const int jj = q / (64 / CE);
         const int cc = (q % (64 / CE)) * CE;
@@ -112,7 +145,6 @@ __global__ __launch_bounds__(256) void k_transpose(const T *__restrict__ src, in
         for (int k = 0; k < CE; ++k) tile[jj][cc + k] = e[k];
     }
     __syncthreads();
-    // store: 64 output rows (features c) x (64 / CE) chunks of j
     for (int q = threadIdx.x; q < 64 * (64 / CE); q += 256) {
         const int cc = q / (64 / CE);
         const int jj = (q % (64 / CE)) * CE;
@@ -165,30 +197,158 @@ __device__ __forceinline__ int build_list(int n, Flag flag, int *list, int *wcnt
     return total;
 }
 
-// Epilogue of the recompute: p = exp(z - lse) per entry, the status of this
-// wave's 128 x 128 filter block (1 = some p >= eps, 2 = only a label in it,
-// 0 = skipped), then for kept blocks the gradient entries
-// g = dloss (p [status 1] - [v == y]) in both slice layouts.
-template <typename T, class TL>
-__device__ __forceinline__ void bwd_g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int tok0, int nv, int p0, int V,
-                                               int ct, int rt, int live_ld, float eps,
-                                               const int32_t *__restrict__ idx, const int32_t *__restrict__ perm,
-                                               const int32_t *__restrict__ inv_perm,
-                                               const int64_t *__restrict__ labels, const float *__restrict__ lse,
-                                               const float *__restrict__ dloss, T *__restrict__ Gt, int64_t ldt,
-                                               T *__restrict__ Gn, int64_t ldn, uint8_t *__restrict__ live,
-                                               int64_t *__restrict__ stats, int *qflag, bool no_softmax) {
-    const int tid = threadIdx.x;
+// ------------------------------------------------------------------ plan
+// lab[rb][cb] = 1 where the label of a valid token of row block rb falls in
+// vocabulary block cb (processing order).
+__global__ __launch_bounds__(256) void k_label_map(const int64_t *__restrict__ labels, const int32_t *__restrict__ idx,
+                                                   const int32_t *__restrict__ nvalid_p,
+                                                   const int32_t *__restrict__ inv_perm, int64_t V, int cbp,
+                                                   uint8_t *__restrict__ lab) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= *nvalid_p) return;
+    const int64_t y = labels[idx[t]];
+    if (y < 0 || y >= V) return;  // not a valid label: undefined by contract
+    const int64_t pos = inv_perm ? inv_perm[y] : y;
+    lab[(t / kBlockRows) * cbp + pos / kBlockVocab] = 1;
+}
+
+// Per tile (vocabulary-tile-major index vt * n_rt + rt): the number of its
+// blocks that may be kept (bits 0-2) and whether its logits are recomputed
+// (bit 7).  A recomputed tile reserves all its real blocks; a tile left out
+// by the bound keeps only the blocks that hold a label.
+__global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ nvalid_p, int64_t V, int n_rt,
+                                                    int n_vt, int cbp, const uint8_t *__restrict__ lab,
+                                                    const float *__restrict__ tbound, const float *__restrict__ lmin,
+                                                    float thr, uint8_t *__restrict__ tneed) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)n_rt * n_vt) return;
+    const int vt = (int)(i / n_rt), rt = (int)(i % n_rt);
+    const int nv = *nvalid_p;
+    if ((int64_t)rt * kTileRows >= nv) {
+        tneed[i] = 0;
+        return;
+    }
+    const bool rec = !tile_below(tbound, n_vt, lmin, thr, rt, vt);
+    int need = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int rb = 2 * rt + (q & 1), cb = 2 * vt + (q >> 1);
+        if ((int64_t)rb * kBlockRows >= nv || (int64_t)cb * kBlockVocab >= V) continue;
+        need += (rec || lab[(int64_t)rb * cbp + cb]) ? 1 : 0;
+    }
+    tneed[i] = (uint8_t)(need | (rec ? 0x80 : 0));
+}
+
+// One workgroup: per vocabulary tile the blocks it may keep and its listed
+// tiles, their prefix sums, the pass of each vocabulary tile, the per-pass
+// ranges and the tile list (vocabulary-tile-major, token tiles in order).
+// Passes: one if every block fits the store, else pass(vt) =
+// floor(cum(vt) / cap_eff) with cum the inclusive block count; a vocabulary
+// tile adds at most cap - cap_eff blocks, so no pass exceeds cap.
+__global__ __launch_bounds__(1024) void k_plan(const uint8_t *__restrict__ tneed, int n_rt, int n_vt, int64_t cap,
+                                               int64_t cap_eff, int max_passes, int32_t *__restrict__ plan,
+                                               int64_t *__restrict__ cum, int32_t *__restrict__ act,
+                                               int32_t *__restrict__ tlist) {
+    __shared__ int64_t wsum[16];
+    __shared__ int32_t wact[16];
+    __shared__ int64_t carry_n;
+    __shared__ int32_t carry_a;
+    const PlanView pv = plan_view(plan, max_passes);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    if (t == 0) { carry_n = 0; carry_a = 0; }
+    __syncthreads();
+    for (int base = 0; base < n_vt; base += 1024) {
+        const int vt = base + t;
+        int64_t nd = 0;
+        int ac = 0;
+        if (vt < n_vt) {
+            const uint8_t *row = tneed + (int64_t)vt * n_rt;
+            for (int rt = 0; rt < n_rt; ++rt) {
+                const int q = row[rt] & 7;
+                nd += q;
+                ac += q > 0;
+            }
+        }
+        int64_t xs = nd;
+        int xa = ac;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t ys = __shfl_up(xs, o, 64);
+            const int ya = __shfl_up(xa, o, 64);
+            if (lane >= o) { xs += ys; xa += ya; }
+        }
+        if (lane == 63) { wsum[w] = xs; wact[w] = xa; }
+        __syncthreads();
+        int64_t off = carry_n;
+        int offa = carry_a;
+        for (int k = 0; k < w; ++k) { off += wsum[k]; offa += wact[k]; }
+        if (vt < n_vt) {
+            cum[vt] = off + xs;          // inclusive
+            act[vt] = offa + xa - ac;    // exclusive
+        }
+        __syncthreads();
+        if (t == 1023) { carry_n = off + xs; carry_a = offa + xa; }
+        __syncthreads();
+    }
+    const int64_t total = carry_n;
+    const int n_active = carry_a;
+    auto pass_of = [&](int vt) -> int {
+        if (total <= cap) return 0;
+        const int64_t q = cum[vt] / cap_eff;
+        return q < max_passes - 1 ? (int)q : max_passes - 1;
+    };
+    for (int vt = t; vt < n_vt; vt += 1024) {
+        const int p = pass_of(vt);
+        const int pp = vt ? pass_of(vt - 1) : -1;
+        for (int q = pp + 1; q <= p; ++q) {
+            pv.vt_begin[q] = vt;
+            pv.list_begin[q] = act[vt];
+        }
+        int pos = act[vt];
+        const uint8_t *row = tneed + (int64_t)vt * n_rt;
+        for (int rt = 0; rt < n_rt; ++rt)
+            if (row[rt] & 7) tlist[pos++] = vt * n_rt + rt;
+    }
+    if (t == 0) {
+        const int P = pass_of(n_vt - 1) + 1;
+        *pv.P = P;
+        *pv.n_active = n_active;
+        for (int q = P; q <= max_passes; ++q) {
+            pv.vt_begin[q] = n_vt;
+            pv.list_begin[q] = n_active;
+        }
+    }
+    for (int q = t; q < max_passes; q += 1024) pv.counter[q] = 0;
+}
+
+// ------------------------------------------------------- recompute + G
+// Epilogue of a listed tile.  SOFTMAX: acc holds the recomputed logits and
+// p = exp(z - lse) decides each 128 x 128 block's status (1 = some p >= eps,
+// 2 = none but a label in it, 0 = dropped); otherwise (a tile left out by
+// the bound; acc is not read) only labels decide.  Kept blocks take a store slot and their
+// gradient g = dloss (p [status 1] - [v == y]) is written in both layouts:
+// Gt[slot][v][row] and Gn[slot][row][v].
+template <typename T, class TL, bool SOFTMAX>
+__device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int tok0, int nv, int p0,
+                                           int V, int rt, int vt, int cbp, float eps,
+                                           const int32_t *__restrict__ idx, const int32_t *__restrict__ inv_perm,
+                                           const int64_t *__restrict__ labels, const float *__restrict__ lse,
+                                           const float *__restrict__ dloss, T *__restrict__ Gt, T *__restrict__ Gn,
+                                           int64_t cap, int32_t *__restrict__ counter, uint8_t *__restrict__ st,
+                                           int32_t *__restrict__ slotm, int64_t *__restrict__ stats, int *qflag,
+                                           int *qstat, int *qslot) {
+    const int tid = opaque_tid();  // fresh per tile: see tile_row
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave % TL::WM, wn = wave / TL::WM;
-    const int quad = wm * 2 + ((wn * TL::kWaveN) >> 7);  // this wave's 128 x 128 filter block
+    const int th = (wn * TL::kWaveN) / kBlockRows;  // token half of this wave
+    const int quad = wm * 2 + th;                   // this wave's block: vocabulary half wm, token half th
     float lse_t[TL::TN], dl_t[TL::TN];
     int lab_t[TL::TN];
     bool tok_ok[TL::TN];
     bool any_live = false, any_label = false;
 #pragma unroll
     for (int tn = 0; tn < TL::TN; ++tn) {
-        const int tok = tok0 + tile_col<TL>(tn);
+        const int tok = tok0 + tile_col<TL>(tn, tid);
         tok_ok[tn] = tok < nv;
         lse_t[tn] = 0.f;
         dl_t[tn] = 0.f;
@@ -199,14 +359,14 @@ __device__ __forceinline__ void bwd_g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], in
             dl_t[tn] = dloss[row];
             const int64_t y = labels[row];
             const bool y_ok = y >= 0 && y < V;  // other labels are undefined by contract
-            const int ypos = y_ok ? (perm ? inv_perm[y] : (int)y) : -(1 << 30);
+            const int ypos = y_ok ? (inv_perm ? inv_perm[y] : (int)y) : -(1 << 30);
             const int lr = ypos - p0 - wm * TL::kWaveM;  // row within this wave's 128 vocabulary rows
             lab_t[tn] = (lr >= 0 && lr < TL::kWaveM) ? ypos - p0 : -1;
             any_label |= lab_t[tn] >= 0;
         }
     }
-    const int vlim = row_limit<TL>(V - p0);  // entry (tm, r) is a real vocabulary row iff acc_row_const < vlim
-    if (!no_softmax) {
+    const int vlim = row_limit<TL>(V - p0, tid);  // entry (tm, r) is a real vocabulary row iff acc_row_const < vlim
+    if constexpr (SOFTMAX) {
 #pragma unroll
         for (int tn = 0; tn < TL::TN; ++tn)
 #pragma unroll
@@ -224,21 +384,33 @@ __device__ __forceinline__ void bwd_g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], in
     __syncthreads();
     if (tid < 4) {
         const int f = qflag[tid];
-        const int st = (f & 1) ? 1 : ((f & 2) ? 2 : 0);
-        const int rb = 2 * rt + (tid & 1), cb = 2 * ct + (tid >> 1);
-        live[(int64_t)rb * live_ld + cb] = (uint8_t)st;
-        if (stats && st) atomicAdd(reinterpret_cast<unsigned long long *>(stats + (st == 1 ? 0 : 1)), 1ull);
-        // filter blocks whose logits were recomputed (real rows and vocabulary entries only)
-        if (stats && !no_softmax && rb * kBlockRows < nv && p0 + (tid >> 1) * kBlockVocab < V)
-            atomicAdd(reinterpret_cast<unsigned long long *>(stats + 4), 1ull);
+        int sv = (f & 1) ? 1 : ((f & 2) ? 2 : 0);
+        const int rb = 2 * rt + (tid & 1), cb = 2 * vt + (tid >> 1);
+        int s = -1;
+        if (sv) {
+            s = atomicAdd(counter, 1);
+            if (s >= cap) { s = -1; sv = 0; }  // cannot happen: the plan bounds every pass by cap
+        }
+        qstat[tid] = sv;
+        qslot[tid] = s;
+        st[(int64_t)rb * cbp + cb] = (uint8_t)sv;
+        if (sv) slotm[(int64_t)rb * cbp + cb] = s;
+        if (stats) {
+            if (sv) atomicAdd(reinterpret_cast<unsigned long long *>(stats + (sv == 1 ? 0 : 1)), 1ull);
+            // blocks whose logits were recomputed (real rows and vocabulary entries only)
+            if (SOFTMAX && rb * kBlockRows < nv && (int64_t)cb * kBlockVocab < V)
+                atomicAdd(reinterpret_cast<unsigned long long *>(stats + 4), 1ull);
+        }
     }
-    const int qf = qflag[quad];
-    const int status = (qf & 1) ? 1 : ((qf & 2) ? 2 : 0);
+    __syncthreads();
+    const int status = qstat[quad];
     if (status == 0) return;  // wave-uniform
+    T *gt = Gt + (int64_t)qslot[quad] * kBlockElems;
+    T *gn = Gn + (int64_t)qslot[quad] * kBlockElems;
 
 #pragma unroll
     for (int tn = 0; tn < TL::TN; ++tn) {
-        const int64_t tok = tok0 + tile_col<TL>(tn);
+        const int tl = tile_col<TL>(tn, tid) - th * kBlockRows;  // token within the block
 #pragma unroll
         for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
@@ -247,60 +419,70 @@ __device__ __forceinline__ void bwd_g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], in
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int r = r4 * 4 + q;
-                    const int rl = tile_row<TL>(tm, r);
+                    const int rl = tile_row<TL>(tm, r, tid);
                     const bool ok = tok_ok[tn] && (acc_row_const(tm, r) < vlim);
-                    const float pk = status == 1 ? acc[tm][tn][r] : 0.f;
+                    const float pk = (SOFTMAX && status == 1) ? acc[tm][tn][r] : 0.f;
                     const float g = ok ? dl_t[tn] * (pk - (rl == lab_t[tn] ? 1.f : 0.f)) : 0.f;
                     g4[q] = from_f32<T>(g);
-                    Gt[(int64_t)(ct * TL::BM + rl) * ldt + tok] = g4[q];
+                    gt[(rl - wm * kBlockVocab) * kBlockRows + tl] = g4[q];
                 }
                 // rows r4*4 .. r4*4+3 are consecutive vocabulary entries
-                T *dst = Gn + tok * ldn + ct * TL::BM + tile_row<TL>(tm, r4 * 4);
+                T *dst = gn + tl * kBlockVocab + tile_row<TL>(tm, r4 * 4, tid) - wm * kBlockVocab;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) dst[q] = g4[q];
             }
     }
 }
 
-// ------------------------------------------- recompute + filter + G tile
-// Workgroup (256-entry vocabulary tile ct of the chunk, 256-token tile rt).
-// The logit tile is recomputed with the forward's code and K order, then
-// p = exp(z - lse).  Each 128 x 128 quadrant is a filter block with status
-// 1 = some p >= eps (softmax part kept), 2 = no p >= eps but a label falls in
-// it (only the -dloss one-hot entries are kept), 0 = skipped.
-template <typename T>
-__global__ __launch_bounds__(TileF::kThreads) void k_bwd_g(
-    const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm,
-    const int32_t *__restrict__ inv_perm, const int64_t *__restrict__ labels,
-    const float *__restrict__ lse, const float *__restrict__ dloss, int D, int V, int chunk_v0, int n_ct,
-    int live_ld, float eps, T *__restrict__ Gt, int64_t ldt, T *__restrict__ Gn, int64_t ldn,
-    uint8_t *__restrict__ live, int64_t *__restrict__ stats, const float *__restrict__ tbound, int64_t tb_ld,
-    const float *__restrict__ lmin, float thr) {
-    using TL = TileF;
-    __shared__ u32x4 lds[TL::kLdsChunks];
-    __shared__ int qflag[4];  // bit 0: some p >= eps, bit 1: a label in the block
-    const int nv = *nvalid_p;
-    const int ct = blockIdx.x % n_ct;
-    const int rt = blockIdx.x / n_ct;
-    const int tok0 = rt * TL::BN;
-    if (tok0 >= nv) return;
-    const int p0 = chunk_v0 + ct * TL::BM;  // first vocabulary position (processing order)
-    const int tid = threadIdx.x;
+// Recompute of logit tile (rt, vt) on the DMA pipeline (needs
+// D * sizeof(T) % kLogitRowBytes == 0): the forward's engine, tile shape and
+// K order.  Rows past the end of an operand are clamped to a valid row: their
+// logits are finite and the epilogue masks them.
+template <typename T, class TL>
+__device__ __forceinline__ void recompute_dma(const T *__restrict__ H, const T *__restrict__ E,
+                                              const int32_t *__restrict__ idx, int nv,
+                                              const int32_t *__restrict__ perm, int D, int V, int tok0, int p0,
+                                              u32x4 *lds, f32x16 (&acc)[TL::TM][TL::TN]) {
+    using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
+    const size_t rowb = (size_t)D * sizeof(T);
+    const int ns = D * (int)sizeof(T) / DE::kStageBytes;
+    const int tid = opaque_tid();  // per-tile address arithmetic stays in this tile's code
+    DE eng(lds);
+#pragma unroll
+    for (int j = 0; j < DE::NIA; ++j) {
+        const int r = DE::row_a(j, tid);
+        const int pos = min(p0 + r, V - 1);
+        int vid = perm ? perm[pos] : pos;
+        vid = (vid >= 0 && vid < V) ? vid : 0;
+        eng.pa[j] = reinterpret_cast<const char *>(E) + (size_t)vid * rowb + DE::chunk_off(r, tid);
+    }
+#pragma unroll
+    for (int j = 0; j < DE::NIB; ++j) {
+        const int r = DE::row_b(j, tid);
+        const int tok = min(tok0 + r, nv - 1);
+        eng.pb[j] = reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb + DE::chunk_off(r, tid);
+    }
+#pragma unroll
+    for (int q = 0; q < DE::kDepth; ++q)
+        if (q < ns) eng.issue(q, q * DE::kStageBytes);
+    for (int s = 0; s < ns; ++s) {
+        const int ahead = ns - 1 - s;
+        eng.wait_stage(eng.clamp_ahead(ahead));
+        if (s + DE::kDepth < ns) eng.issue((s + DE::kDepth) % DE::kStages, (s + DE::kDepth) * DE::kStageBytes);
+        eng.compute(s % DE::kStages, acc);
+    }
+}
+
+// The same on the VGPR-staged engine (any D % 8 == 0), as the forward's
+// fallback kernel computes it.
+template <typename T, class TL>
+__device__ __forceinline__ void recompute_vgpr(const T *__restrict__ H, const T *__restrict__ E,
+                                               const int32_t *__restrict__ idx, int nv,
+                                               const int32_t *__restrict__ perm, int D, int V, int tok0, int p0,
+                                               u32x4 *lds, f32x16 (&acc)[TL::TM][TL::TN]) {
     const size_t rowb = (size_t)D * sizeof(T);
     const int kvalid = D * (int)sizeof(T);
     const int ns = (kvalid + TL::kStageBytes - 1) / TL::kStageBytes;
-    if (tid < 4) qflag[tid] = 0;
-    const bool skip = tile_below(tbound, tb_ld, lmin, thr, rt, p0 / kTileVocab);
-    f32x16 acc[TL::TM][TL::TN];
-    zero_acc<TL>(acc);
-    if (skip) {
-        __syncthreads();
-        bwd_g_epilogue<T, TL>(acc, tok0, nv, p0, V, ct, rt, live_ld, eps, idx, perm, inv_perm, labels, lse, dloss,
-                              Gt, ldt, Gn, ldn, live, stats, qflag, true);
-        return;
-    }
-
     Engine<T, TL> eng;
 #pragma unroll
     for (int j = 0; j < Engine<T, TL>::NA; ++j) {
@@ -323,105 +505,217 @@ __global__ __launch_bounds__(TileF::kThreads) void k_bwd_g(
         if (more) eng.store(lds + ((s + 1) & 1) * TL::kStage);
         __syncthreads();
     }
-
-    bwd_g_epilogue<T, TL>(acc, tok0, nv, p0, V, ct, rt, live_ld, eps, idx, perm, inv_perm, labels, lse, dloss, Gt,
-                          ldt, Gn, ldn, live, stats, qflag, false);
 }
 
-// The recompute on the DMA pipeline (needs D * sizeof(T) % 64 == 0).  Rows
-// past the end of an operand are clamped to a valid row: their logits are
-// finite and the epilogue masks them.
-template <typename T, class TL>
-__global__ __launch_bounds__(TL::kThreads) void k_bwd_g_dma(
-    const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm,
-    const int32_t *__restrict__ inv_perm, const int64_t *__restrict__ labels,
-    const float *__restrict__ lse, const float *__restrict__ dloss, int D, int V, int chunk_v0, int n_ct,
-    int live_ld, float eps, T *__restrict__ Gt, int64_t ldt, T *__restrict__ Gn, int64_t ldn,
-    uint8_t *__restrict__ live, int64_t *__restrict__ stats, const float *__restrict__ tbound, int64_t tb_ld,
-    const float *__restrict__ lmin, float thr) {
-    using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
-    __shared__ u32x4 lds[DE::kLdsChunks];
-    __shared__ int qflag[4];
-    const int nv = *nvalid_p;
-    const int ct = blockIdx.x % n_ct;
-    const int rt = blockIdx.x / n_ct;
-    const int tok0 = rt * TL::BN;
-    if (tok0 >= nv) return;
-    const int p0 = chunk_v0 + ct * TL::BM;
-    const size_t rowb = (size_t)D * sizeof(T);
-    const int ns = D * (int)sizeof(T) / DE::kStageBytes;
-    if (threadIdx.x < 4) qflag[threadIdx.x] = 0;
-    f32x16 acc[TL::TM][TL::TN];
-    zero_acc<TL>(acc);
-    if (tile_below(tbound, tb_ld, lmin, thr, rt, p0 / kTileVocab)) {
-        __syncthreads();
-        bwd_g_epilogue<T, TL>(acc, tok0, nv, p0, V, ct, rt, live_ld, eps, idx, perm, inv_perm, labels, lse, dloss,
-                              Gt, ldt, Gn, ldn, live, stats, qflag, true);
-        return;
-    }
+template <typename T, bool DMA>
+struct GPassLds {
+    static constexpr int value = DMA ? DmaEngine<T, TileFD, kLogitRowBytes, kLogitStages>::kLdsChunks
+                                     : TileF::kLdsChunks;
+};
 
-    DE eng(lds);
-#pragma unroll
-    for (int j = 0; j < DE::NIA; ++j) {
-        const int r = DE::row_a(j);
-        const int pos = min(p0 + r, V - 1);
-        int vid = perm ? perm[pos] : pos;
-        vid = (vid >= 0 && vid < V) ? vid : 0;
-        eng.pa[j] = reinterpret_cast<const char *>(E) + (size_t)vid * rowb + DE::chunk_off(r);
-    }
-#pragma unroll
-    for (int j = 0; j < DE::NIB; ++j) {
-        const int r = DE::row_b(j);
-        const int tok = min(tok0 + r, nv - 1);
-        eng.pb[j] = reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb + DE::chunk_off(r);
-    }
-    {
-#pragma unroll
-        for (int q = 0; q < DE::kDepth; ++q)
-            if (q < ns) eng.issue(q, q * DE::kStageBytes);
-        for (int s = 0; s < ns; ++s) {
-            const int ahead = ns - 1 - s;
-            eng.wait_stage(eng.clamp_ahead(ahead));
-            if (s + DE::kDepth < ns) eng.issue((s + DE::kDepth) % DE::kStages, (s + DE::kDepth) * DE::kStageBytes);
-            eng.compute(s % DE::kStages, acc);
+// Persistent over the listed tiles of pass p.  Hardware workgroup b runs on
+// XCD b % 8; the list is cut into 8 contiguous parts, one per XCD, so tiles
+// that share a vocabulary tile (adjacent in the list) share that XCD's L2.
+template <typename T, bool DMA>
+__global__ __launch_bounds__(TileF::kThreads) void k_g_pass(
+    int p, int32_t *__restrict__ plan, int max_passes, const int32_t *__restrict__ tlist,
+    const uint8_t *__restrict__ tneed, int n_rt, const T *__restrict__ H, const T *__restrict__ E,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm,
+    const int32_t *__restrict__ inv_perm, const int64_t *__restrict__ labels, const float *__restrict__ lse,
+    const float *__restrict__ dloss, int D, int V, int cbp, float eps, T *__restrict__ Gt, T *__restrict__ Gn,
+    int64_t cap, uint8_t *__restrict__ st, int32_t *__restrict__ slotm, int64_t *__restrict__ stats) {
+    using TL = TileF;
+    __shared__ u32x4 lds[GPassLds<T, DMA>::value];
+    __shared__ int qflag[4], qstat[4], qslot[4];
+    const PlanView pv = plan_view(plan, max_passes);
+    if (p >= *pv.P) return;
+    const int nv = *nvalid_p;
+    const int lb = pv.list_begin[p], le = pv.list_begin[p + 1];
+    const int nx = gridDim.x / 8;  // workgroups per XCD (the grid is a multiple of 8)
+    const int x = blockIdx.x % 8, wx = blockIdx.x / 8;
+    const int pb = lb + (int)((int64_t)(le - lb) * x / 8), pe = lb + (int)((int64_t)(le - lb) * (x + 1) / 8);
+    for (int i = pb + wx; i < pe; i += nx) {
+        const int tile = tlist[i];
+        const int vt = tile / n_rt, rt = tile % n_rt;
+        const bool rec = (tneed[tile] & 0x80) != 0;
+        const int tok0 = rt * TL::BN, p0 = vt * TL::BM;
+        if (threadIdx.x < 4) qflag[threadIdx.x] = 0;
+        __syncthreads();
+        f32x16 acc[TL::TM][TL::TN];
+        if (rec) {
+            zero_acc<TL>(acc);
+            if constexpr (DMA) recompute_dma<T, TL>(H, E, idx, nv, perm, D, V, tok0, p0, lds, acc);
+            else recompute_vgpr<T, TL>(H, E, idx, nv, perm, D, V, tok0, p0, lds, acc);
+            __syncthreads();
+            g_epilogue<T, TL, true>(acc, tok0, nv, p0, V, rt, vt, cbp, eps, idx, inv_perm, labels, lse, dloss, Gt, Gn,
+                                    cap, pv.counter + p, st, slotm, stats, qflag, qstat, qslot);
+        } else {
+            g_epilogue<T, TL, false>(acc, tok0, nv, p0, V, rt, vt, cbp, eps, idx, inv_perm, labels, lse, dloss, Gt,
+                                     Gn, cap, pv.counter + p, st, slotm, stats, qflag, qstat, qslot);
         }
     }
-    __syncthreads();
-    bwd_g_epilogue<T, TL>(acc, tok0, nv, p0, V, ct, rt, live_ld, eps, idx, perm, inv_perm, labels, lse, dloss, Gt,
-                          ldt, Gn, ldn, live, stats, qflag, false);
 }
 
-// ------------------------------------------------------------- dE (Kahan)
-// Workgroup (128-entry vocabulary block cb of the chunk, 256-feature tile).
-// K runs over the valid tokens of the row blocks kept for this vocabulary
-// block (DMA pipeline, 64 K-bytes per stage).  Each row block's product is
-// formed in a fresh fp32 MFMA accumulator and then added into
-// (sum, compensation) with Kahan's rule; the result is written once.
-constexpr int kListCap = 512;
+// ------------------------------------------------------------------- dH
+// dH rows of a 128-token block, 256 features: C[row][d] = sum_v G[row][v]
+// E[v][d], K = the vocabulary entries of the kept blocks.  A = the stored
+// block Gn[slot] (rows x v, v contiguous) through the usual 64-byte LDS rows.
+// B = E rows, v-major with d contiguous, copied as they are into LDS and read
+// transposed: bf16 with ds_read_b64_tr_b16, which gives each lane 4
+// consecutive rows at one column (two of them make the 8 K values of the
+// 32x32x16 MFMA operand); fp32 needs one value per lane per MFMA and reads it
+// directly.  B rows are kRowB bytes with chunk c of row r stored at
+// c ^ 4 (r & 3), so the 4 rows one transposed read touches are 64 bytes apart
+// in the bank space.
+template <typename T>
+struct DhEngine {
+    using TL = TileG;
+    static constexpr int kKv = sizeof(T) == 2 ? 32 : 16;  // vocabulary entries per stage
+    static constexpr int kSpb = kBlockVocab / kKv;        // stages per block
+    static constexpr int kStages = 4, kDepth = 3;
+    static constexpr int kStageBytes = 64;                // A row bytes per stage
+    static constexpr int kStageA = TL::BM * 4;            // chunks
+    static constexpr int kRowB = TL::BN * (int)sizeof(T); // bytes of one B row (256 features)
+    static constexpr int kCprB = kRowB / 16;
+    static constexpr int kStageB = kKv * kCprB;
+    static constexpr int kStage = kStageA + kStageB;
+    static constexpr int kLdsChunks = kStages * kStage;
+    static constexpr int NIA = kStageA / 64 / TL::kWaves;
+    static constexpr int NIB = kStageB / 64 / TL::kWaves;
+    static constexpr int NI = NIA + NIB;
+    static_assert(NIA == 1 && NIB == 2, "stage split");
+    static_assert(kStageBytes == kKv * (int)sizeof(T), "A stage = kKv entries");
 
+    u32x4 *lds;
+    uint32_t lds0;      // LDS byte address of the stages (wave-uniform)
+    int a_off;          // this lane's A source offset within a stored block (row + swizzled chunk)
+    int b_row[NIB];     // B row (vocabulary entry within the stage) this lane feeds
+    int b_off[NIB];     // byte offset of its chunk within an E row (clamped to the last chunk < D)
+
+    __device__ __forceinline__ DhEngine(u32x4 *l, int d0, int D) : lds(l), lds0(lds_addr(l)) {
+        const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        const int sa = 64 * w + lane;
+        const int ra = sa / 4;
+        a_off = ra * kBlockVocab * (int)sizeof(T) + 16 * ((sa & 3) ^ dma_swz<64>(ra));
+        constexpr int kElemsPerChunk = 16 / (int)sizeof(T);
+#pragma unroll
+        for (int j = 0; j < NIB; ++j) {
+            const int sb = 64 * (j * TL::kWaves + w) + lane;
+            const int r = sb / kCprB, cs = sb % kCprB;
+            const int lc = cs ^ (4 * (r & 3));
+            b_row[j] = r;
+            b_off[j] = min(d0 + lc * kElemsPerChunk, D - kElemsPerChunk) * (int)sizeof(T);
+        }
+    }
+
+    // Stage kq of the block with store slot `slot` and first vocabulary
+    // position pos0, into LDS buffer buf.
+    __device__ __forceinline__ void issue(int buf, const T *Gn, int64_t slot, const T *E, const int32_t *perm,
+                                          int pos0, int kq, int V, size_t rowb) const {
+        const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const uint32_t st = lds0 + (uint32_t)(buf * kStage) * 16u;
+        dma16_at(reinterpret_cast<const char *>(Gn + slot * kBlockElems) + a_off + kq * kStageBytes, st + 1024u * w);
+#pragma unroll
+        for (int j = 0; j < NIB; ++j) {
+            const int pos = pos0 + kq * kKv + b_row[j];
+            int vid = pos < V ? (perm ? perm[pos] : pos) : V - 1;
+            vid = (vid >= 0 && vid < V) ? vid : 0;
+            dma16_at(reinterpret_cast<const char *>(E) + (size_t)vid * rowb + b_off[j],
+                     st + 16u * kStageA + 1024u * (j * TL::kWaves + w));
+        }
+    }
+
+    __device__ __forceinline__ void wait_stage(int ahead) const {
+        if (ahead >= 2) { wait_vmcnt<2 * NI>(); block_sync(); return; }
+        if (ahead >= 1) { wait_vmcnt<NI>(); block_sync(); return; }
+        wait_vmcnt<0>();
+        block_sync();
+    }
+    __device__ __forceinline__ int clamp_ahead(int ahead) const { return ahead < kDepth - 1 ? ahead : kDepth - 1; }
+
+    __device__ __forceinline__ void compute(int buf, f32x16 (&acc)[TL::TM][TL::TN]) const {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int ra0 = (wave % TL::WM) * TL::kWaveM + (lane & 31);
+        const int nb0 = (wave / TL::WM) * TL::kWaveN;
+        const u32x4 *A = lds + buf * kStage;
+        const char *Bb = reinterpret_cast<const char *>(A + kStageA);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int c = 2 * kk + (lane >> 5);
+            u32x4 fa[TL::TM], fb[TL::TN];
+#pragma unroll
+            for (int tm = 0; tm < TL::TM; ++tm) fa[tm] = A[dma_slot<64>(ra0 + tm * 32, c)];
+#pragma unroll
+            for (int tn = 0; tn < TL::TN; ++tn) {
+                const int n0 = nb0 + tn * 32;
+                if constexpr (sizeof(T) == 2) {
+                    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+                    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+                    bf16x4 h[2];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const int row = 16 * kk + 8 * (lane >> 5) + 4 * t + ((lane & 15) >> 2);
+                        const int col = n0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                        const char *a = Bb + row * kRowB + (((col >> 3) ^ (4 * (row & 3))) << 4) + (col & 7) * 2;
+                        h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(a));
+                    }
+                    const u32x2 lo = __builtin_bit_cast(u32x2, h[0]), hi = __builtin_bit_cast(u32x2, h[1]);
+                    fb[tn] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                } else {
+                    const int col = n0 + (lane & 31);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int row = 8 * kk + 4 * (lane >> 5) + j;
+                        fb[tn][j] = *reinterpret_cast<const uint32_t *>(
+                            Bb + row * kRowB + (((col >> 2) ^ (4 * (row & 3))) << 4) + (col & 3) * 4);
+                    }
+                }
+            }
+#pragma unroll
+            for (int tm = 0; tm < TL::TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TL::TN; ++tn) Mfma<T>::step(fa[tm], fb[tn], acc[tm][tn]);
+        }
+    }
+};
+
+// ------------------------------------------------------------- dE (Kahan)
+// Shared memory of the gradient-product kernel: the K pipeline's stages,
+// reused after the K loop for the output tile, and the block lists.
+template <typename T>
+struct GradLds {
+    static constexpr int kStageChunks = DmaEngine<T, TileG>::kLdsChunks > DhEngine<T>::kLdsChunks
+                                            ? DmaEngine<T, TileG>::kLdsChunks
+                                            : DhEngine<T>::kLdsChunks;
+    u32x4 stages[kStageChunks];
+    int list[kListCap];
+    int lslot[kListCap];
+    int wcnt[TileG::kWaves];
+};
+
+// dE for one (vocabulary block cb, 256-feature tile d0) item of a pass.  K
+// runs over the valid tokens of the row blocks kept for cb, in order (DMA
+// pipeline, 64 K-bytes per stage): A = the stored block Gt[slot] (128
+// vocabulary rows x 128 tokens), B = H^T.  Each row block's product is formed
+// in a fresh fp32 accumulator and then added into (sum, compensation) with
+// Kahan's rule; the result is written once, through LDS as 16-byte row
+// segments (bf16).  A vocabulary block with nothing kept gets dE = 0.
 template <typename T, bool KAHAN>
-__global__ __launch_bounds__(TileG::kThreads) void k_de(
-    const T *__restrict__ Gt, int64_t ldt, const T *__restrict__ Ht, int64_t ldh,
-    const uint8_t *__restrict__ live, int live_ld, const int32_t *__restrict__ nvalid_p,
-    const int32_t *__restrict__ perm, int n_cb, int D, int V, int chunk_v0, T *__restrict__ dE) {
+__device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb, const uint8_t *__restrict__ st,
+                                        const int32_t *__restrict__ slotm, int cbp, const T *__restrict__ Gt,
+                                        const T *__restrict__ Ht, int64_t ldh, const int32_t *__restrict__ perm,
+                                        int D, int V, T *__restrict__ dE) {
     using TL = TileG;
     using DE = DmaEngine<T, TL>;
-    __shared__ u32x4 lds[DE::kLdsChunks];
-    __shared__ int list[kListCap];
-    __shared__ int wcnt[TL::kWaves];
-    const int nv = *nvalid_p;
-    const int n_rb = (nv + kBlockRows - 1) / kBlockRows;
-    const int cb = blockIdx.x % n_cb;
-    const int d0 = (blockIdx.x / n_cb) * TL::BN;
-    constexpr int kBlockBytes = kBlockRows * (int)sizeof(T);
-    constexpr int kSpb = kBlockBytes / DE::kStageBytes;  // stages per row block
-
-    DE eng(lds);
+    constexpr int kBlockBytes = kBlockRows * (int)sizeof(T);  // K bytes of one row block
+    constexpr int kSpb = kBlockBytes / DE::kStageBytes;       // stages per row block
+    constexpr int64_t kStoreBytes = (int64_t)kBlockElems * sizeof(T);
+    constexpr int CE = ChunkElems<T>::value;
+    DE eng(sh.stages);
 #pragma unroll
     for (int j = 0; j < DE::NIA; ++j) {
         const int r = DE::row_a(j);
-        eng.pa[j] = reinterpret_cast<const char *>(Gt + (int64_t)(cb * TL::BM + r) * ldt) + DE::chunk_off(r);
+        eng.pa[j] = reinterpret_cast<const char *>(Gt + (int64_t)r * kBlockRows) + DE::chunk_off(r);
     }
 #pragma unroll
     for (int j = 0; j < DE::NIB; ++j) {
@@ -429,25 +723,31 @@ __global__ __launch_bounds__(TileG::kThreads) void k_de(
         const int d = min(d0 + r, D - 1);
         eng.pb[j] = reinterpret_cast<const char *>(Ht + (int64_t)d * ldh) + DE::chunk_off(r);
     }
-
     f32x16 acc[TL::TM][TL::TN], sum[TL::TM][TL::TN], comp[TL::TM][TL::TN];
     zero_acc<TL>(acc);
     zero_acc<TL>(sum);
     zero_acc<TL>(comp);
 
+    bool any = false;
     for (int base = 0; base < n_rb; base += kListCap) {
         const int cnt = n_rb - base < kListCap ? n_rb - base : kListCap;
         const int n = build_list<TL::kThreads>(
-            cnt, [&](int i) { return live[(int64_t)(base + i) * live_ld + cb] != 0; }, list, wcnt);
+            cnt, [&](int i) { return st[(int64_t)(base + i) * cbp + cb] != 0; }, sh.list, sh.wcnt);
+        for (int i = threadIdx.x; i < n; i += TL::kThreads) sh.lslot[i] = slotm[(int64_t)(base + sh.list[i]) * cbp + cb];
+        __syncthreads();
+        any |= n > 0;
         const int total = n * kSpb;
-        auto kb = [&](int q) { return (base + list[q / kSpb]) * kBlockBytes + (q % kSpb) * DE::kStageBytes; };
+        auto issue = [&](int buf, int q) {
+            const int b = q / kSpb, k = (q % kSpb) * DE::kStageBytes;
+            eng.issue2(buf, sh.lslot[b] * kStoreBytes + k, (int64_t)(base + sh.list[b]) * kBlockBytes + k);
+        };
 #pragma unroll
         for (int q = 0; q < DE::kDepth; ++q)
-            if (q < total) eng.issue(q, kb(q));
+            if (q < total) issue(q, q);
         for (int s = 0; s < total; ++s) {
             const int ahead = total - 1 - s;
             eng.wait_stage(eng.clamp_ahead(ahead));
-            if (s + DE::kDepth < total) eng.issue((s + DE::kDepth) % DE::kStages, kb(s + DE::kDepth));
+            if (s + DE::kDepth < total) issue((s + DE::kDepth) % DE::kStages, s + DE::kDepth);
             eng.compute(s % DE::kStages, acc);
             if (KAHAN && (s % kSpb) == kSpb - 1) {
 #pragma clang fp contract(off)
@@ -465,86 +765,142 @@ __global__ __launch_bounds__(TileG::kThreads) void k_de(
                         }
             }
         }
-        __syncthreads();  // list[] and the LDS stages are reused by the next batch
+        __syncthreads();  // list[], lslot[] and the LDS stages are reused next
     }
 
-    int vid[TL::TM][16];  // output row of each accumulator row (-1: none), loaded once
-#pragma unroll
-    for (int tm = 0; tm < TL::TM; ++tm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int pos = chunk_v0 + cb * TL::BM + tile_row<TL>(tm, r);
+    // Output rows: 128 vocabulary entries x 256 features, in 16-byte segments.
+    constexpr int kSeg = TL::BN / CE;  // segments per row
+    if (!any) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int q = threadIdx.x; q < TL::BM * kSeg; q += TL::kThreads) {
+            const int row = q / kSeg, d = d0 + (q % kSeg) * CE;
+            const int pos = cb * TL::BM + row;
             const int v = pos < V ? (perm ? perm[pos] : pos) : -1;
-            vid[tm][r] = (v >= 0 && v < V) ? v : -1;
+            if (v >= 0 && v < V && d < D) *reinterpret_cast<u32x4 *>(dE + (int64_t)v * D + d) = z;
         }
+        return;
+    }
+    if constexpr (sizeof(T) == 2) {
+        // stage the tile in LDS (row stride 256 + 8 elements), then write rows
+        constexpr int kLd = TL::BN + 8;
+        T *tile = reinterpret_cast<T *>(sh.stages);
 #pragma unroll
-    for (int tm = 0; tm < TL::TM; ++tm)
+        for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < TL::TN; ++tn) {
-            const int d = d0 + tile_col<TL>(tn);
+            for (int tn = 0; tn < TL::TN; ++tn) {
+                const int col = tile_col<TL>(tn);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float val = KAHAN ? sum[tm][tn][r] - comp[tm][tn][r] : acc[tm][tn][r];
+                    tile[tile_row<TL>(tm, r) * kLd + col] = from_f32<T>(val);
+                }
+            }
+        __syncthreads();
+        for (int q = threadIdx.x; q < TL::BM * kSeg; q += TL::kThreads) {
+            const int row = q / kSeg, c = q % kSeg, d = d0 + c * CE;
+            const int pos = cb * TL::BM + row;
+            const int v = pos < V ? (perm ? perm[pos] : pos) : -1;
+            if (v >= 0 && v < V && d < D)
+                *reinterpret_cast<u32x4 *>(dE + (int64_t)v * D + d) =
+                    *reinterpret_cast<const u32x4 *>(tile + row * kLd + c * CE);
+        }
+        __syncthreads();  // the stages are reused by the next item
+    } else {
+        int vid[TL::TM][16];  // output row of each accumulator row (-1: none), loaded once
+#pragma unroll
+        for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float val = KAHAN ? sum[tm][tn][r] - comp[tm][tn][r] : acc[tm][tn][r];
-                if (vid[tm][r] >= 0 && d < D) dE[(int64_t)vid[tm][r] * D + d] = from_f32<T>(val);
+                const int pos = cb * TL::BM + tile_row<TL>(tm, r);
+                const int v = pos < V ? (perm ? perm[pos] : pos) : -1;
+                vid[tm][r] = (v >= 0 && v < V) ? v : -1;
             }
-        }
+#pragma unroll
+        for (int tm = 0; tm < TL::TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TL::TN; ++tn) {
+                const int d = d0 + tile_col<TL>(tn);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float val = KAHAN ? sum[tm][tn][r] - comp[tm][tn][r] : acc[tm][tn][r];
+                    if (vid[tm][r] >= 0 && d < D) dE[(int64_t)vid[tm][r] * D + d] = from_f32<T>(val);
+                }
+            }
+    }
 }
 
-// ------------------------------------------------------------------- dH
-// Workgroup (128-token block rb, 256-feature tile).  K runs over the kept
-// vocabulary blocks of the chunk.  With one chunk the result is written to dH
-// directly.  Otherwise fp32 partial sums are added into dh_acc (zeroed before
-// the first chunk) and a row block with no kept block in this chunk returns
-// at once; k_dh_final converts dh_acc after the last chunk.
+// dH for one (128-token block rb, 256-feature tile d0) item of a pass.  K
+// runs over the kept vocabulary blocks of the pass in order.  Each block's
+// product is formed in a fresh accumulator and added to the running sum,
+// which starts from the previous passes' fp32 sum, so the result does not
+// depend on where the passes are cut.  The last pass writes dH in the output
+// dtype.
 template <typename T>
-__global__ __launch_bounds__(TileG::kThreads) void k_dh(
-    const T *__restrict__ Gn, int64_t ldn, const T *__restrict__ Et, int64_t lde,
-    const uint8_t *__restrict__ live, int live_ld, const int32_t *__restrict__ nvalid_p,
-    const int32_t *__restrict__ idx, int n_cb, int n_rb_grid, int D, float *__restrict__ dh_acc, int direct,
-    T *__restrict__ dH) {
+__device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool multi, bool last, int cb0, int cb1,
+                                        const uint8_t *__restrict__ st, const int32_t *__restrict__ slotm, int cbp,
+                                        int nv, const int32_t *__restrict__ idx, const T *__restrict__ Gn,
+                                        const T *__restrict__ E, const int32_t *__restrict__ perm, int D, int V,
+                                        float *__restrict__ dh_acc, T *__restrict__ dH) {
     using TL = TileG;
-    using DE = DmaEngine<T, TL>;
-    __shared__ u32x4 lds[DE::kLdsChunks];
-    __shared__ int list[kChunkVocab / kBlockVocab];
-    __shared__ int wcnt[TL::kWaves];
-    const int nv = *nvalid_p;
-    const int rb = blockIdx.x % n_rb_grid;
-    const int d0 = (blockIdx.x / n_rb_grid) * TL::BN;
+    using DH = DhEngine<T>;
     const int tok0 = rb * TL::BM;
-    if (tok0 >= nv) return;
-    constexpr int kBlockBytes = kBlockVocab * (int)sizeof(T);
-    constexpr int kSpb = kBlockBytes / DE::kStageBytes;
+    const size_t rowb = (size_t)D * sizeof(T);
 
-    const int n = build_list<TL::kThreads>(
-        n_cb, [&](int i) { return live[(int64_t)rb * live_ld + i] != 0; }, list, wcnt);
-    if (n == 0 && !direct) return;  // nothing to add in this chunk
-    DE eng(lds);
-#pragma unroll
-    for (int j = 0; j < DE::NIA; ++j) {
-        const int r = DE::row_a(j);
-        eng.pa[j] = reinterpret_cast<const char *>(Gn + (int64_t)(tok0 + r) * ldn) + DE::chunk_off(r);
-    }
-#pragma unroll
-    for (int j = 0; j < DE::NIB; ++j) {
-        const int r = DE::row_b(j);
-        const int d = min(d0 + r, D - 1);
-        eng.pb[j] = reinterpret_cast<const char *>(Et + (int64_t)d * lde) + DE::chunk_off(r);
-    }
-    f32x16 acc[TL::TM][TL::TN];
+    f32x16 acc[TL::TM][TL::TN], sum[TL::TM][TL::TN];
     zero_acc<TL>(acc);
-    const int total = n * kSpb;
-    auto kb = [&](int q) { return list[q / kSpb] * kBlockBytes + (q % kSpb) * DE::kStageBytes; };
+    if (multi) {
 #pragma unroll
-    for (int q = 0; q < DE::kDepth; ++q)
-        if (q < total) eng.issue(q, kb(q));
-    for (int s = 0; s < total; ++s) {
-        const int ahead = total - 1 - s;
-        eng.wait_stage(eng.clamp_ahead(ahead));
-        if (s + DE::kDepth < total) eng.issue((s + DE::kDepth) % DE::kStages, kb(s + DE::kDepth));
-        eng.compute(s % DE::kStages, acc);
+        for (int tm = 0; tm < TL::TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TL::TN; ++tn) {
+                const int d = min(d0 + tile_col<TL>(tn), D - 1);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)  // dh_acc is [Np, D]: every tok < Np is in bounds
+                    sum[tm][tn][r] = dh_acc[(int64_t)(tok0 + tile_row<TL>(tm, r)) * D + d];
+            }
+    } else {
+        zero_acc<TL>(sum);
     }
 
-    if (direct) {
+    DH eng(sh.stages, d0, D);
+    bool any = false;
+    for (int base = cb0; base < cb1; base += kListCap) {
+        const int cnt = cb1 - base < kListCap ? cb1 - base : kListCap;
+        const int n = build_list<TL::kThreads>(
+            cnt, [&](int i) { return st[(int64_t)rb * cbp + base + i] != 0; }, sh.list, sh.wcnt);
+        for (int i = threadIdx.x; i < n; i += TL::kThreads) sh.lslot[i] = slotm[(int64_t)rb * cbp + base + sh.list[i]];
+        __syncthreads();
+        any |= n > 0;
+        const int total = n * DH::kSpb;
+        auto issue = [&](int buf, int q) {
+            const int b = q / DH::kSpb;
+            eng.issue(buf, Gn, sh.lslot[b], E, perm, (base + sh.list[b]) * kBlockVocab, q % DH::kSpb, V, rowb);
+        };
+#pragma unroll
+        for (int q = 0; q < DH::kDepth; ++q)
+            if (q < total) issue(q, q);
+        for (int s = 0; s < total; ++s) {
+            const int ahead = total - 1 - s;
+            eng.wait_stage(eng.clamp_ahead(ahead));
+            if (s + DH::kDepth < total) issue((s + DH::kDepth) % DH::kStages, s + DH::kDepth);
+            eng.compute(s % DH::kStages, acc);
+            if ((s % DH::kSpb) == DH::kSpb - 1) {
+#pragma unroll
+                for (int tm = 0; tm < TL::TM; ++tm)
+#pragma unroll
+                    for (int tn = 0; tn < TL::TN; ++tn)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            sum[tm][tn][r] += acc[tm][tn][r];
+                            acc[tm][tn][r] = 0.f;
+                        }
+            }
+        }
+        __syncthreads();  // list[], lslot[] and the LDS stages are reused next
+    }
+    if (!any && !last) return;  // nothing added in this pass
+
+    if (last) {
         int row[TL::TM][16];  // output row of each accumulator row, loaded once
 #pragma unroll
         for (int tm = 0; tm < TL::TM; ++tm)
@@ -558,57 +914,58 @@ __global__ __launch_bounds__(TileG::kThreads) void k_dh(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int tok = tok0 + tile_row<TL>(tm, r);
-                    if (tok < nv && d < D) dH[(int64_t)row[tm][r] * D + d] = from_f32<T>(acc[tm][tn][r]);
+                    if (tok < nv && d < D) dH[(int64_t)row[tm][r] * D + d] = from_f32<T>(sum[tm][tn][r]);
                 }
             }
-        return;
-    }
-    // Read every partial sum first, then write: the loads overlap instead of
-    // each waiting behind the previous store.
-    float old[TL::TM][TL::TN][16];
+    } else {
 #pragma unroll
-    for (int tm = 0; tm < TL::TM; ++tm)
+        for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < TL::TN; ++tn) {
-            const int d = d0 + tile_col<TL>(tn);
+            for (int tn = 0; tn < TL::TN; ++tn) {
+                const int d = d0 + tile_col<TL>(tn);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int tok = tok0 + tile_row<TL>(tm, r);
-                // unconditional load from a clamped in-bounds address (dh_acc is [Np, D], tok < Np)
-                old[tm][tn][r] = __builtin_nontemporal_load(dh_acc + (int64_t)tok * D + min(d, D - 1));
+                for (int r = 0; r < 16; ++r) {
+                    const int tok = tok0 + tile_row<TL>(tm, r);
+                    if (tok < nv && d < D) dh_acc[(int64_t)tok * D + d] = sum[tm][tn][r];
+                }
             }
-        }
-#pragma unroll
-    for (int tm = 0; tm < TL::TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TL::TN; ++tn) {
-            const int d = d0 + tile_col<TL>(tn);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int tok = tok0 + tile_row<TL>(tm, r);
-                if (tok < nv && d < D) dh_acc[(int64_t)tok * D + d] = old[tm][tn][r] + acc[tm][tn][r];
-            }
-        }
-}
-
-// dH[idx[t]] = dh_acc[t] in the output dtype, for the valid tokens.
-template <typename T>
-__global__ __launch_bounds__(256) void k_dh_final(const float *__restrict__ dh_acc, const int32_t *__restrict__ idx,
-                                                  const int32_t *__restrict__ nvalid_p, int D, T *__restrict__ dH) {
-    const int64_t tok = blockIdx.x;
-    if (tok >= *nvalid_p) return;
-    const float *src = dh_acc + tok * D;
-    T *dst = dH + (int64_t)idx[tok] * D;
-    for (int d = threadIdx.x * 4; d < D; d += 256 * 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(src + d);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dst[d + q] = from_f32<T>(v[q]);
     }
 }
 
-__global__ __launch_bounds__(256) void k_fill_zero(float *__restrict__ p, int64_t n) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i < n) *reinterpret_cast<f32x4 *>(p + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+// --------------------------------------------------- gradient products
+// Both products of pass p in one launch: workgroups below n_de are
+// persistent over the pass's (vocabulary block, feature tile) dE items; the
+// others each take one (row block, feature tile) dH item.
+template <typename T, bool KAHAN>
+__global__ __launch_bounds__(TileG::kThreads) void k_grad_pass(
+    int p, int32_t *__restrict__ plan, int max_passes, int n_de, const uint8_t *__restrict__ st,
+    const int32_t *__restrict__ slotm, int cbp, const int32_t *__restrict__ nvalid_p,
+    const int32_t *__restrict__ idx, const T *__restrict__ Gt, const T *__restrict__ Gn, const T *__restrict__ Ht,
+    int64_t ldh, const T *__restrict__ E, const int32_t *__restrict__ perm, int D, int V, int n_rb_grid,
+    float *__restrict__ dh_acc, T *__restrict__ dE, T *__restrict__ dH) {
+    using TL = TileG;
+    __shared__ GradLds<T> sh;
+    const PlanView pv = plan_view(plan, max_passes);
+    const int P = *pv.P;
+    if (p >= P) return;
+    const int nv = *nvalid_p;
+    const int CB = (V + kBlockVocab - 1) / kBlockVocab;
+    const int cb0 = 2 * pv.vt_begin[p];
+    const int cb1 = min(2 * pv.vt_begin[p + 1], CB);
+    const int n_dt = (D + TL::BN - 1) / TL::BN;
+    if ((int)blockIdx.x < n_de) {
+        const int n_rb = (nv + kBlockRows - 1) / kBlockRows;
+        const int64_t items = cb1 > cb0 ? (int64_t)(cb1 - cb0) * n_dt : 0;
+        for (int64_t it = blockIdx.x; it < items; it += n_de)
+            de_item<T, KAHAN>(sh, cb0 + (int)(it / n_dt), (int)(it % n_dt) * TL::BN, n_rb, st, slotm, cbp, Gt, Ht, ldh,
+                              perm, D, V, dE);
+    } else {
+        const int b = blockIdx.x - n_de;
+        const int rb = b % n_rb_grid;
+        if (rb * TL::BM >= nv) return;
+        dh_item<T>(sh, rb, (b / n_rb_grid) * TL::BN, P > 1, p == P - 1, cb0, cb1, st, slotm, cbp, nv, idx, Gn, E,
+                   perm, D, V, dh_acc, dH);
+    }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -618,26 +975,47 @@ BwdShape bwd_shape(int64_t N, int64_t D, int64_t V) {
     s.D = D;
     s.V = V;
     s.Np = round_up(N, kTileRows);
-    const int64_t Vp = round_up(V, kTileVocab);
-    s.Vc = (int)(Vp < kChunkVocab ? Vp : kChunkVocab);
-    s.n_chunks = (int)ceil_div(V, s.Vc);
     s.n_rtiles = (int)(s.Np / kTileRows);
+    s.n_vtiles = (int)ceil_div(V, kTileVocab);
+    s.n_rb = (int)(s.Np / kBlockRows);
+    s.cbp = 2 * s.n_vtiles;
+    const int64_t total = (int64_t)s.n_rb * s.cbp;
+    const int64_t vp = round_up(V, kTileVocab);
+    const int64_t slice_cb = (vp < kStoreVocab ? vp : kStoreVocab) / kBlockVocab;
+    s.cap = (int64_t)s.n_rb * slice_cb;
+    if (total <= s.cap) {
+        s.cap = total;
+        s.cap_eff = total;
+        s.max_passes = 1;
+    } else {
+        s.cap_eff = s.cap - 2 * (int64_t)s.n_rb;
+        s.max_passes = (int)(total / s.cap_eff) + 1;
+    }
+    s.plan_ints = plan_ints(s.max_passes);
     return s;
 }
 
 BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     Carver c(ws);
     BwdWs w;
+    const size_t nblk = (size_t)s.n_rb * s.cbp;
+    const size_t ntile = (size_t)s.n_rtiles * s.n_vtiles;
     w.idx = c.take<int32_t>(s.N);
     w.nvalid = c.take<int32_t>(1);
     w.inv_perm = c.take<int32_t>(s.V);
-    w.live = c.take<uint8_t>((size_t)(s.Np / kBlockRows) * (s.Vc / kBlockVocab));
     w.lmin = c.take<float>((size_t)s.n_rtiles);
-    w.dh_acc = s.n_chunks > 1 ? c.take<float>((size_t)s.Np * s.D) : nullptr;
+    w.lab = c.take<uint8_t>(nblk);
+    w.st = c.take<uint8_t>(nblk);
+    w.slot = c.take<int32_t>(nblk);
+    w.tneed = c.take<uint8_t>(ntile);
+    w.cum = c.take<int64_t>((size_t)s.n_vtiles);
+    w.act = c.take<int32_t>((size_t)s.n_vtiles);
+    w.tlist = c.take<int32_t>(ntile);
+    w.plan = c.take<int32_t>((size_t)s.plan_ints);
+    w.dh_acc = s.max_passes > 1 ? c.take<float>((size_t)s.Np * s.D) : nullptr;
     w.Ht = c.take<char>(elem * (size_t)s.D * s.Np);
-    w.Gt = c.take<char>(elem * (size_t)s.Vc * s.Np);
-    w.Gn = c.take<char>(elem * (size_t)s.Np * s.Vc);
-    w.Et = c.take<char>(elem * (size_t)s.D * s.Vc);
+    w.Gt = c.take<char>(elem * (size_t)s.cap * kBlockElems);
+    w.Gn = c.take<char>(elem * (size_t)s.cap * kBlockElems);
     if (bytes) *bytes = c.off;
     return w;
 }
@@ -649,6 +1027,14 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     } while (0)
 #define CCE_LAUNCHED() CCE_TRY(hipGetLastError())
 
+// Zeroes a carved region (256-byte aligned, so whole 32-bit words).
+static hipError_t fill_bytes_zero(void *p, size_t nbytes, hipStream_t st) {
+    const int64_t n = (int64_t)(align256(nbytes) / 4);
+    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, static_cast<uint32_t *>(p), n,
+                       0u);
+    return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, const float *lse,
                              const float *dloss, const float *tile_bound, const BwdShape &s, int64_t ignore_index,
@@ -656,6 +1042,33 @@ static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, cons
                              const BwdWs &w, hipStream_t st) {
     const int D = (int)s.D, V = (int)s.V;
     CCE_TRY(launch_compact(labels, s.N, ignore_index, w.idx, w.nvalid, st));
+    if (perm) {
+        hipLaunchKernelGGL(k_inv_perm, dim3((unsigned)ceil_div(V, 256)), dim3(256), 0, st, perm, V, w.inv_perm);
+        CCE_LAUNCHED();
+    }
+    if (stats) {
+        hipLaunchKernelGGL(k_stats_init, dim3(1), dim3(64), 0, st, stats);
+        CCE_LAUNCHED();
+    }
+    const size_t nblk = (size_t)s.n_rb * s.cbp;
+    CCE_TRY(fill_bytes_zero(w.lab, nblk, st));
+    CCE_TRY(fill_bytes_zero(w.st, nblk, st));
+    if (s.max_passes > 1) {
+        const int64_t n = s.Np * (int64_t)D;  // D % 8 == 0: whole f32x4 groups
+        hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)ceil_div(n, 1024)), dim3(256), 0, st, w.dh_acc, n);
+        CCE_LAUNCHED();
+    }
+    T *Ht = static_cast<T *>(w.Ht);
+    T *Gt = static_cast<T *>(w.Gt);
+    T *Gn = static_cast<T *>(w.Gn);
+    // H^T of the valid rows: [D, Np], zero beyond the valid rows.
+    hipLaunchKernelGGL(k_transpose<T>, dim3((unsigned)ceil_div(s.Np, 64), (unsigned)ceil_div(D, 64)), dim3(256),
+                       0, st, H, (int64_t)D, s.N, w.idx, (int64_t)0, w.nvalid, 0, D, (int)s.Np, Ht, (int64_t)s.Np);
+    CCE_LAUNCHED();
+    hipLaunchKernelGGL(k_zero_ignored<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, labels, s.N, D,
+                       ignore_index, dH);
+    CCE_LAUNCHED();
+
     // The tile bound is in the natural vocabulary order and only says something
     // when filtering is on.  thr = ln(eps / 2), rounded towards -inf.
     const float *tb = (tile_bound && !perm && eps > 0.f) ? tile_bound : nullptr;
@@ -667,71 +1080,39 @@ static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, cons
                            w.lmin);
         CCE_LAUNCHED();
     }
-    const int64_t tb_ld = ceil_div(s.V, kTileVocab);
-    if (perm) {
-        hipLaunchKernelGGL(k_inv_perm, dim3((unsigned)ceil_div(V, 256)), dim3(256), 0, st, perm, V, w.inv_perm);
-        CCE_LAUNCHED();
-    }
-    if (stats) {
-        hipLaunchKernelGGL(k_stats_init, dim3(1), dim3(64), 0, st, stats);
-        CCE_LAUNCHED();
-    }
-    T *Ht = static_cast<T *>(w.Ht);
-    T *Gt = static_cast<T *>(w.Gt);
-    T *Gn = static_cast<T *>(w.Gn);
-    T *Et = static_cast<T *>(w.Et);
-    // H^T of the valid rows: [D, Np], zero beyond the valid rows.
-    hipLaunchKernelGGL(k_transpose<T>, dim3((unsigned)ceil_div(s.Np, 64), (unsigned)ceil_div(D, 64)), dim3(256),
-                       0, st, H, (int64_t)D, s.N, w.idx, (int64_t)0, w.nvalid, 0, D, (int)s.Np, Ht, (int64_t)s.Np);
+    const int32_t *invp = perm ? w.inv_perm : nullptr;
+    hipLaunchKernelGGL(k_label_map, dim3((unsigned)ceil_div(s.N, 256)), dim3(256), 0, st, labels, w.idx, w.nvalid,
+                       invp, s.V, s.cbp, w.lab);
     CCE_LAUNCHED();
-    hipLaunchKernelGGL(k_zero_ignored<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, labels, s.N, D,
-                       ignore_index, dH);
+    const int64_t ntile = (int64_t)s.n_rtiles * s.n_vtiles;
+    hipLaunchKernelGGL(k_tile_class, dim3((unsigned)ceil_div(ntile, 256)), dim3(256), 0, st, w.nvalid, s.V,
+                       s.n_rtiles, s.n_vtiles, s.cbp, w.lab, tb, w.lmin, thr, w.tneed);
+    CCE_LAUNCHED();
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, w.tneed, s.n_rtiles, s.n_vtiles, s.cap, s.cap_eff,
+                       s.max_passes, w.plan, w.cum, w.act, w.tlist);
     CCE_LAUNCHED();
 
     const bool dma_g = ((int64_t)D * (int64_t)sizeof(T)) % kLogitRowBytes == 0;
-    if (s.n_chunks > 1) {
-        const int64_t n = s.Np * (int64_t)D;  // D % 8 == 0: whole f32x4 groups
-        hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)ceil_div(n, 1024)), dim3(256), 0, st, w.dh_acc, n);
-        CCE_LAUNCHED();
-    }
     const int n_dt = (int)ceil_div(D, TileG::BN);
-    const int live_ld = s.Vc / kBlockVocab;
-    const int n_rb_grid = (int)(s.Np / kBlockRows);
-    for (int c = 0; c < s.n_chunks; ++c) {
-        const int cv0 = c * s.Vc;
-        const int clen = (int)((V - cv0) < s.Vc ? (V - cv0) : s.Vc);
-        const int n_ct = (int)ceil_div(clen, kTileVocab);   // logit tiles in the chunk
-        const int n_cb = (int)ceil_div(clen, kBlockVocab);  // filter blocks in the chunk
-        // E^T of the chunk (processing order): [D, Vc], zero beyond clen.
-        hipLaunchKernelGGL(k_transpose<T>, dim3((unsigned)ceil_div(n_ct * kTileVocab, 64), (unsigned)ceil_div(D, 64)),
-                           dim3(256), 0, st, E, (int64_t)D, s.V, perm, (int64_t)cv0, (const int32_t *)nullptr, clen, D,
-                           n_ct * kTileVocab, Et, (int64_t)s.Vc);
-        CCE_LAUNCHED();
+    for (int p = 0; p < s.max_passes; ++p) {
         if (dma_g)
-            hipLaunchKernelGGL((k_bwd_g_dma<T, TileFD>), dim3((unsigned)(n_ct * s.n_rtiles)), dim3(TileFD::kThreads), 0, st, H,
-                               E, w.idx, w.nvalid, perm, perm ? w.inv_perm : nullptr, labels, lse, dloss, D, V, cv0,
-                               n_ct, live_ld, eps, Gt, (int64_t)s.Np, Gn, (int64_t)s.Vc, w.live, stats, tb, tb_ld,
-                               w.lmin, thr);
+            hipLaunchKernelGGL((k_g_pass<T, true>), dim3(kPassGroups), dim3(TileF::kThreads), 0, st, p, w.plan,
+                               s.max_passes, w.tlist, w.tneed, s.n_rtiles, H, E, w.idx, w.nvalid, perm, invp, labels,
+                               lse, dloss, D, V, s.cbp, eps, Gt, Gn, s.cap, w.st, w.slot, stats);
         else
-            hipLaunchKernelGGL(k_bwd_g<T>, dim3((unsigned)(n_ct * s.n_rtiles)), dim3(TileF::kThreads), 0, st, H, E,
-                               w.idx, w.nvalid, perm, perm ? w.inv_perm : nullptr, labels, lse, dloss, D, V, cv0,
-                               n_ct, live_ld, eps, Gt, (int64_t)s.Np, Gn, (int64_t)s.Vc, w.live, stats, tb, tb_ld,
-                               w.lmin, thr);
+            hipLaunchKernelGGL((k_g_pass<T, false>), dim3(kPassGroups), dim3(TileF::kThreads), 0, st, p, w.plan,
+                               s.max_passes, w.tlist, w.tneed, s.n_rtiles, H, E, w.idx, w.nvalid, perm, invp, labels,
+                               lse, dloss, D, V, s.cbp, eps, Gt, Gn, s.cap, w.st, w.slot, stats);
         CCE_LAUNCHED();
+        const unsigned grid = (unsigned)(kDeGroups + s.n_rb * n_dt);
         if (flags & CCE_BWD_NO_KAHAN)
-            hipLaunchKernelGGL((k_de<T, false>), dim3((unsigned)(n_cb * n_dt)), dim3(TileG::kThreads), 0, st, Gt,
-                               (int64_t)s.Np, Ht, (int64_t)s.Np, w.live, live_ld, w.nvalid, perm, n_cb, D, V, cv0, dE);
+            hipLaunchKernelGGL((k_grad_pass<T, false>), dim3(grid), dim3(TileG::kThreads), 0, st, p, w.plan,
+                               s.max_passes, kDeGroups, w.st, w.slot, s.cbp, w.nvalid, w.idx, Gt, Gn, Ht,
+                               (int64_t)s.Np, E, perm, D, V, s.n_rb, w.dh_acc, dE, dH);
         else
-            hipLaunchKernelGGL((k_de<T, true>), dim3((unsigned)(n_cb * n_dt)), dim3(TileG::kThreads), 0, st, Gt,
-                               (int64_t)s.Np, Ht, (int64_t)s.Np, w.live, live_ld, w.nvalid, perm, n_cb, D, V, cv0, dE);
-        CCE_LAUNCHED();
-        hipLaunchKernelGGL(k_dh<T>, dim3((unsigned)(n_rb_grid * n_dt)), dim3(TileG::kThreads), 0, st, Gn,
-                           (int64_t)s.Vc, Et, (int64_t)s.Vc, w.live, live_ld, w.nvalid, w.idx, n_cb, n_rb_grid, D,
-                           w.dh_acc, s.n_chunks == 1 ? 1 : 0, dH);
-        CCE_LAUNCHED();
-    }
-    if (s.n_chunks > 1) {
-        hipLaunchKernelGGL(k_dh_final<T>, dim3((unsigned)s.N), dim3(256), 0, st, w.dh_acc, w.idx, w.nvalid, D, dH);
+            hipLaunchKernelGGL((k_grad_pass<T, true>), dim3(grid), dim3(TileG::kThreads), 0, st, p, w.plan,
+                               s.max_passes, kDeGroups, w.st, w.slot, s.cbp, w.nvalid, w.idx, Gt, Gn, Ht,
+                               (int64_t)s.Np, E, perm, D, V, s.n_rb, w.dh_acc, dE, dH);
         CCE_LAUNCHED();
     }
     if (stats) {

@@ -32,6 +32,14 @@ template <typename T> __device__ __forceinline__ T from_f32(float f);
 template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) { return f32_to_bf16(f); }
 
+// threadIdx.x through an empty asm: the compiler cannot treat values derived
+// from it as loop-invariant.
+__device__ __forceinline__ int opaque_tid() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 // Order-preserving map of fp32 onto int32 (for non-NaN values): a < b as
 // floats iff enc(a) < enc(b) as signed integers, so an integer atomic max
 // computes a float max.  dec inverts enc.
@@ -224,10 +232,14 @@ __device__ __forceinline__ int dma_slot(int r, int c) {
 // M0 holds the LDS address; nothing else in these kernels uses M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const char *src, u32x4 *wave_dst) {
-    const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)wave_dst);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(src) : "memory", "m0");
+__device__ __forceinline__ void dma16_at(const char *src, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(src) : "memory", "m0");
 }
+// LDS byte address (32 bits, wave-uniform) of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t *)p);
+}
+__device__ __forceinline__ void dma16(const char *src, u32x4 *wave_dst) { dma16_at(src, lds_addr(wave_dst)); }
 #pragma clang diagnostic pop
 
 template <int N>
@@ -262,25 +274,28 @@ struct DmaEngine {
     const char *pa[NIA];  // this lane's source address (row base + swizzled chunk) at K offset 0
     const char *pb[NIB];
     u32x4 *lds;
+    uint32_t lds0;        // LDS byte address of the stages (wave-uniform)
 
-    __device__ __forceinline__ explicit DmaEngine(u32x4 *l) : lds(l) {}
+    __device__ __forceinline__ explicit DmaEngine(u32x4 *l) : lds(l), lds0(lds_addr(l)) {}
 
     // Tile row fed by this lane in instruction j, and its chunk byte offset.
-    static __device__ __forceinline__ int row_a(int j) {
-        return (64 * (j * TL::kWaves + (threadIdx.x >> 6)) + (threadIdx.x & 63)) / kCpr;
+    static __device__ __forceinline__ int row_a(int j, int tid = threadIdx.x) {
+        return (64 * (j * TL::kWaves + (tid >> 6)) + (tid & 63)) / kCpr;
     }
-    static __device__ __forceinline__ int row_b(int j) { return row_a(j); }
-    static __device__ __forceinline__ int chunk_off(int r) {
-        return 16 * ((threadIdx.x & (kCpr - 1)) ^ dma_swz<kRowBytes_>(r));
+    static __device__ __forceinline__ int row_b(int j, int tid = threadIdx.x) { return row_a(j, tid); }
+    static __device__ __forceinline__ int chunk_off(int r, int tid = threadIdx.x) {
+        return 16 * ((tid & (kCpr - 1)) ^ dma_swz<kRowBytes_>(r));
     }
 
-    __device__ __forceinline__ void issue(int buf, int kb) const {
-        const int w = threadIdx.x >> 6;
-        u32x4 *st = lds + buf * kStage;
+    __device__ __forceinline__ void issue(int buf, int kb) const { issue2(buf, kb, kb); }
+    // The same with separate byte offsets for the A and the B rows.
+    __device__ __forceinline__ void issue2(int buf, int64_t kba, int64_t kbb) const {
+        const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const uint32_t st = lds0 + (uint32_t)(buf * kStage) * 16u;
 #pragma unroll
-        for (int j = 0; j < NIA; ++j) dma16(pa[j] + kb, st + 64 * (j * TL::kWaves + w));
+        for (int j = 0; j < NIA; ++j) dma16_at(pa[j] + kba, st + 1024u * (j * TL::kWaves + w));
 #pragma unroll
-        for (int j = 0; j < NIB; ++j) dma16(pb[j] + kb, st + kStageA + 64 * (j * TL::kWaves + w));
+        for (int j = 0; j < NIB; ++j) dma16_at(pb[j] + kbb, st + 16u * kStageA + 1024u * (j * TL::kWaves + w));
     }
 
     // Wait until at most `ahead` later stages are still in flight for this
@@ -331,9 +346,12 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[TL::TM][TL::TN]) {
 
 // Row of the workgroup tile (M index) held by register r of acc[tm][*] in
 // this lane, and column (N index) held by acc[*][tn].
+// The tid argument lets a caller pass a thread index it has made opaque
+// (so that per-lane address arithmetic is redone in each iteration of a
+// persistent loop instead of being hoisted into registers for all of it).
 template <class TL>
-__device__ __forceinline__ int tile_row(int tm, int r) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ int tile_row(int tm, int r, int tid = threadIdx.x) {
+    const int lane = tid & 63, wave = tid >> 6;
     return (wave % TL::WM) * TL::kWaveM + tm * 32 + acc_row(r, lane);
 }
 // Row of register r of acc[tm][*] within the wave's sub-tile, without the
@@ -344,14 +362,14 @@ __device__ __forceinline__ constexpr int acc_row_const(int tm, int r) { return t
 
 // Per-lane limit: acc[tm][*][r] holds tile row < rows iff acc_row_const(tm, r) < row_limit(rows).
 template <class TL>
-__device__ __forceinline__ int row_limit(int rows) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ int row_limit(int rows, int tid = threadIdx.x) {
+    const int lane = tid & 63, wave = tid >> 6;
     return rows - (wave % TL::WM) * TL::kWaveM - 4 * (lane >> 5);
 }
 
 template <class TL>
-__device__ __forceinline__ int tile_col(int tn) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ int tile_col(int tn, int tid = threadIdx.x) {
+    const int lane = tid & 63, wave = tid >> 6;
     return (wave / TL::WM) * TL::kWaveN + tn * 32 + acc_col(lane);
 }
 

@@ -20,9 +20,11 @@ constexpr int kLogitStages = 2;
 // Gradient-filter block: a quarter of the logit tile.
 constexpr int kBlockVocab = 128;
 constexpr int kBlockRows = 128;
-// The backward materialises the logit gradient for at most this many
-// vocabulary columns at a time (a multiple of kBlockVocab).
-constexpr int kChunkVocab = 8192;
+// The backward's store of kept gradient blocks holds as many blocks as a
+// dense [rows x kStoreVocab] slice would (a multiple of 2 kBlockVocab).
+constexpr int kStoreVocab = 8192;
+// Workgroups of the persistent backward kernels.
+constexpr int kPassGroups = 256;
 // Upper bound on the forward's vocabulary splits (merged per row in order).
 constexpr int kMaxSplits = 64;
 // Workgroups the forward aims to launch (two per compute unit).
@@ -64,12 +66,22 @@ struct FwdWs {
 };
 FwdWs fwd_ws(void *ws, const FwdShape &s, size_t *bytes);
 
+// Backward plan.  Work is organised by 256 x 256 logit tiles (token tile rt
+// of the valid rows, vocabulary tile vt of the processing order) and their
+// four 128 x 128 filter blocks.  Tiles that may keep a block are listed
+// vocabulary-tile-major and cut into passes whose kept blocks fit the block
+// store (cap blocks); every pass runs recompute -> dE -> dH on its range.
 struct BwdShape {
     int64_t N, D, V;
-    int64_t Np;        // N rounded up to kBlockRows
-    int Vc;            // vocabulary columns per chunk (multiple of kBlockVocab)
-    int n_chunks;
-    int n_rtiles;
+    int64_t Np;        // N rounded up to kTileRows
+    int n_rtiles;      // Np / kTileRows
+    int n_vtiles;      // ceil(V / kTileVocab)
+    int n_rb;          // Np / kBlockRows
+    int cbp;           // 2 n_vtiles: row width of the block maps
+    int64_t cap;       // block-store capacity (blocks)
+    int64_t cap_eff;   // cap - 2 n_rb: pass packing bound (a vocabulary tile adds at most 2 n_rb blocks)
+    int max_passes;
+    int plan_ints;     // size of the plan record
 };
 BwdShape bwd_shape(int64_t N, int64_t D, int64_t V);
 
@@ -77,13 +89,19 @@ struct BwdWs {
     int32_t *idx;      // [N]
     int32_t *nvalid;   // [1]
     int32_t *inv_perm; // [V] processing position of each vocabulary id
-    uint8_t *live;     // [n_rtiles, Vc / kBlockVocab] block status of the current chunk
     float *lmin;       // [n_rtiles] smallest lse of each token tile (for the tile bound)
-    float *dh_acc;     // [Np, D] fp32 dH accumulators (valid-row order)
+    uint8_t *lab;      // [n_rb, cbp] 1 where a label falls in the block
+    uint8_t *st;       // [n_rb, cbp] block status: 0 dropped, 1 softmax kept, 2 label only
+    int32_t *slot;     // [n_rb, cbp] store slot of a kept block
+    uint8_t *tneed;    // [n_vtiles, n_rtiles] blocks the tile may keep (bits 0-2), recompute flag (bit 7)
+    int64_t *cum;      // [n_vtiles] plan scratch: cumulative blocks
+    int32_t *act;      // [n_vtiles] plan scratch: active tiles before each vocabulary tile
+    int32_t *tlist;    // [n_vtiles * n_rtiles] active tiles, vocabulary-tile-major
+    int32_t *plan;     // [plan_ints] passes, active tiles, per-pass ranges and slot counters
+    float *dh_acc;     // [Np, D] fp32 running dH across passes (max_passes > 1)
     void *Ht;          // [D, Np] valid rows of H, transposed
-    void *Gt;          // [Vc, Np] logit gradient of the chunk, vocabulary-major
-    void *Gn;          // [Np, Vc] the same, row-major
-    void *Et;          // [D, Vc] classifier rows of the chunk, transposed
+    void *Gt;          // [cap, 128, 128] kept gradient blocks, vocabulary-major
+    void *Gn;          // [cap, 128, 128] the same blocks, row-major
 };
 BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes);
 

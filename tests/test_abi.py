@@ -42,9 +42,10 @@ def test_status_strings():
 
 
 @pytest.mark.parametrize("dt", [B.CCE_F32, B.CCE_BF16])
-def test_workspace_has_no_rows_times_vocab_term(dt):
-    # Doubling V at fixed N (or N at fixed V) at most roughly doubles the
-    # workspace; an N x V term would quadruple it when both double.
+def test_workspace_has_no_per_logit_term(dt):
+    # Doubling N and V together at most roughly doubles the workspace: the
+    # buffers are O((N + V) D) plus byte-sized maps, one entry per 128 x 128
+    # logit block (6 bytes) and per 256 x 256 tile (5 bytes).
     f = B.backward_workspace_bytes
     D = 2048
     a = f(8192, D, 256000, dt)
@@ -52,9 +53,18 @@ def test_workspace_has_no_rows_times_vocab_term(dt):
     assert a > 0 and b < 2.2 * a
     g = B.forward_workspace_bytes
     assert g(16384, D, 512000, dt) < 2.2 * g(8192, D, 256000, dt)
-    # linear in N at fixed V, and bounded by a few bytes x (N x D + V + D x chunk)
+    # per vocabulary entry at fixed N: inverse permutation (4 bytes), the
+    # block and tile maps (N / 16384 blocks x 6 bytes, N / 65536 tiles x 5
+    # bytes) and the plan's per-tile scratch; nothing per logit
+    N = 8192
+    per_v = (f(N, D, 512000, dt) - f(N, D, 256000, dt)) / 256000
+    assert per_v <= 4 + 6 * N / 16384 + 5 * N / 65536 + 1
+    # per row at fixed V: the fp32 dH accumulator, H^T and the block store
+    # (as many blocks as a dense slice of 8192 vocabulary columns, two layouts)
     elem = 4 if dt == B.CCE_F32 else 2
-    assert a < 4 * 8192 * D + 2 * elem * 8192 * 8192 + 2 * elem * D * 8192 + elem * D * 8192 + 64 * 256000 + (1 << 20)
+    V = 256000
+    per_n = (f(2 * N, D, V, dt) - f(N, D, V, dt)) / N
+    assert per_n <= 4 * D + elem * D + 2 * elem * 8192 + 6 * V / 16384 + 5 * V / 65536 + 16
 
 
 def test_workspace_invalid_sizes_return_zero():
