@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, help="1..5 (2 = Gemma-2-2B head)")
     ap.add_argument("--eps", type=float, default=None, help="filter threshold (default: the workload's)")
     ap.add_argument("--sort", action="store_true", help="vocabulary sort before the backward")
-    ap.add_argument("--no-bound", action="store_true", help="backward without the forward's tile-bound table")
+    ap.add_argument("--no-bound", action="store_true", help="backward without the forward's block-max table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = about 20 s of work)")
     return ap.parse_args()
@@ -108,12 +108,13 @@ def main():
     dH = torch.empty_like(H)
     dE = torch.empty_like(E)
     stats = torch.zeros(5, dtype=torch.int64, device=dev)
-    # tile-bound table (one float per 256 x 256 logit tile), as the autograd wrapper uses it
-    tb = None if (a.sort or a.no_bound) else torch.empty(B.tile_bound_elems(N, V), dtype=torch.float32, device=dev)
+    # block-max table (one float per 128 x 128 logit block), as the autograd wrapper uses it
+    tb = None if (a.sort or a.no_bound) else torch.empty(B.block_max_elems(N, V), dtype=torch.float32, device=dev)
     ws_f = torch.empty(B.forward_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(B.backward_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev)
     ws_s = torch.empty(B.vocab_order_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev) if a.sort else None
     perm = torch.empty(V, dtype=torch.int32, device=dev) if a.sort else None
+    bwd_flags = 0
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     mem0 = torch.cuda.memory_allocated()
@@ -121,13 +122,13 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        B.cce_forward(H, E, y, x.ignore_index, loss=loss, lse=lse, tile_bound=tb, ws=ws_f)
+        B.cce_forward(H, E, y, x.ignore_index, loss=loss, lse=lse, block_max=tb, ws=ws_f)
         if ev is not None:
             ev[1].record(stream)
         if a.sort:
             B.cce_vocab_order(H, E, y, x.ignore_index, perm=perm, ws=ws_s)
-        B.cce_backward(H, E, y, lse, dl, eps, x.ignore_index, perm, 0, dH=dH, dE=dE, stats=stats, ws=ws_b,
-                       tile_bound=tb)
+        B.cce_backward(H, E, y, lse, dl, eps, x.ignore_index, perm, bwd_flags, dH=dH, dE=dE, stats=stats, ws=ws_b,
+                       block_max=tb)
         if ev is not None:
             ev[2].record(stream)
 
@@ -181,11 +182,11 @@ def main():
             "blocks_softmax_kept": n_live, "blocks_label_only": n_label, "blocks_total": n_total,
             "kept_frac": (n_live + n_label) / max(n_total, 1),
             "blocks_recomputed": n_recomp, "recomputed_frac": n_recomp / max(n_total, 1),
-            "tile_bound": tb is not None,
+            "block_max": tb is not None,
             "F_exec_TF": f_exec / 1e12, "F_exec_frac_peak": f_exec / (step_ms * 1e-3) / (peak * 1e12),
             "F6_TF": (f_logits + 4.0 * D * kept_cols) / 1e12,
             "workspace_MB": (ws_f.numel() + ws_b.numel()) / 1e6,
-            "tile_bound_MB": 0.0 if tb is None else tb.numel() * 4 / 1e6,
+            "block_max_MB": 0.0 if tb is None else tb.numel() * 4 / 1e6,
             "extra_alloc_MB": (torch.cuda.max_memory_allocated() - mem0) / 1e6,
             "valid_tokens_per_s": nv / (step_ms * 1e-3),
         },

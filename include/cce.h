@@ -92,25 +92,25 @@ size_t cce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtype d
 /* Workspace bytes for cce_vocab_order (0 on invalid sizes). */
 size_t cce_vocab_order_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtype dtype);
 
-/* Elements (fp32) of the optional tile-bound table of cce_forward /
- * cce_backward: ceil(N / 256) * ceil(V / 256), one per 256 x 256 logit tile
- * (0 on invalid sizes). */
-size_t cce_tile_bound_elems(int64_t N, int64_t V);
+/* Elements (fp32) of the optional block-max table of cce_forward /
+ * cce_backward: 4 * ceil(N / 256) * ceil(V / 256), one per 128 x 128 block of
+ * the logit matrix (0 on invalid sizes). */
+size_t cce_block_max_elems(int64_t N, int64_t V);
 
 /*
  * Forward: loss[i] and lse[i] for every row (fp32, device, [N]).
  * Ignored rows get loss = lse = 0.  The log-sum-exp is accumulated per
  * vocabulary split on chip (online max / sum-exp) and the splits are merged in
  * a fixed order, so the result does not depend on scheduling.
- * tile_bound: NULL, or device fp32 [cce_tile_bound_elems(N, V)] that receives,
- *   for every 256-row tile of the non-ignored rows (in order) x 256-entry
- *   vocabulary tile, the largest logit in that tile (an opaque order-preserving
- *   encoding; pass it unchanged to cce_backward).
+ * block_max: NULL, or device fp32 [cce_block_max_elems(N, V)] that receives
+ *   the largest logit of every 128 x 128 block of the logit matrix of the
+ *   non-ignored rows (in order), row-major over [2 ceil(N / 256) row blocks,
+ *   2 ceil(V / 256) vocabulary blocks]; blocks with no valid row get -inf.
  * ws: device scratch of at least cce_forward_workspace_bytes bytes.
  */
 cce_status cce_forward(const void *H, const void *E, const int64_t *labels,
                        int64_t N, int64_t D, int64_t V, cce_dtype dtype,
-                       int64_t ignore_index, float *loss, float *lse, float *tile_bound,
+                       int64_t ignore_index, float *loss, float *lse, float *block_max,
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
@@ -132,11 +132,12 @@ cce_status cce_vocab_order(const void *H, const void *E, const int64_t *labels,
  * Backward: dH [N, D] and dE [V, D] (input dtype, device) of
  * L = sum_i dloss[i] * loss_i, given lse from cce_forward.
  *  - dloss: fp32 [N]; it carries the caller's reduction (1/N_valid for a mean).
- *  - tile_bound: NULL, or the table cce_forward wrote for these same H, E and
- *    labels.  With it (and perm == NULL), a 256 x 256 logit tile whose largest
- *    logit is so far below the smallest lse of its rows that every p_iv in it
- *    is < filter_eps / 2 is not recomputed; the filter would drop all of it,
- *    so the outputs are bit-identical to the run without the table.
+ *  - block_max: NULL, or the table cce_forward wrote for these same H, E and
+ *    labels.  With it (and perm == NULL, filter_eps > 0), a 128 x 128 block
+ *    whose largest logit is so far below the smallest lse of its rows that
+ *    every p_iv in it is < filter_eps / 2 cannot keep its softmax part, and a
+ *    256 x 256 logit tile made only of such blocks is not recomputed; the
+ *    outputs are bit-identical to the run without the table.
  *  - filter_eps >= 0: a filter block (see cce_filter_block) is skipped when
  *    every p_iv in it is < filter_eps; 0 disables filtering.  Only the
  *    softmax part is filtered: the -dloss_i at (i, y_i) is always applied.
@@ -149,7 +150,7 @@ cce_status cce_vocab_order(const void *H, const void *E, const int64_t *labels,
  * ws: device scratch of at least cce_backward_workspace_bytes bytes.
  */
 cce_status cce_backward(const void *H, const void *E, const int64_t *labels,
-                        const float *lse, const float *dloss, const float *tile_bound,
+                        const float *lse, const float *dloss, const float *block_max,
                         int64_t N, int64_t D, int64_t V, cce_dtype dtype,
                         int64_t ignore_index, float filter_eps,
                         const int32_t *perm, unsigned flags,

@@ -14,12 +14,12 @@ from . import binding
 class _LinearCrossEntropy(torch.autograd.Function):
     @staticmethod
     def forward(ctx, H, E, labels, ignore_index, filter_eps, sort_vocab):
-        # The tile-bound table (one float per 256 x 256 logit tile) lets the
+        # The block-max table (one float per 128 x 128 logit block) lets the
         # backward leave out tiles the gradient filter would drop entirely.
         tb = None
         if filter_eps > 0 and not sort_vocab:
-            tb = torch.empty(binding.tile_bound_elems(H.shape[0], E.shape[0]), dtype=torch.float32, device=H.device)
-        loss, lse = binding.cce_forward(H, E, labels, ignore_index, tile_bound=tb)
+            tb = torch.empty(binding.block_max_elems(H.shape[0], E.shape[0]), dtype=torch.float32, device=H.device)
+        loss, lse = binding.cce_forward(H, E, labels, ignore_index, block_max=tb)
         ctx.save_for_backward(H, E, labels, lse, tb)
         ctx.ignore_index = ignore_index
         ctx.filter_eps = filter_eps
@@ -32,7 +32,7 @@ class _LinearCrossEntropy(torch.autograd.Function):
         H, E, labels, lse, tb = ctx.saved_tensors
         perm = binding.cce_vocab_order(H, E, labels, ctx.ignore_index) if ctx.sort_vocab else None
         dH, dE = binding.cce_backward(H, E, labels, lse, dloss.float().contiguous(), ctx.filter_eps,
-                                      ctx.ignore_index, perm, tile_bound=tb)
+                                      ctx.ignore_index, perm, block_max=tb)
         return dH, dE, None, None, None, None
 
 

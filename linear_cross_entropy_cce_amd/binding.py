@@ -31,7 +31,7 @@ CCE_BWD_NO_KAHAN = 1
 EXPORTS = (
     "cce_status_string", "cce_version", "cce_filter_block",
     "cce_forward_workspace_bytes", "cce_backward_workspace_bytes", "cce_vocab_order_workspace_bytes",
-    "cce_tile_bound_elems", "cce_forward", "cce_vocab_order", "cce_backward", "cce_check_labels",
+    "cce_block_max_elems", "cce_forward", "cce_vocab_order", "cce_backward", "cce_check_labels",
 )
 
 
@@ -63,8 +63,8 @@ def lib() -> ctypes.CDLL:
     for f in ("cce_forward_workspace_bytes", "cce_backward_workspace_bytes", "cce_vocab_order_workspace_bytes"):
         getattr(L, f).argtypes = [_i64, _i64, _i64, ctypes.c_int]
         getattr(L, f).restype = ctypes.c_size_t
-    L.cce_tile_bound_elems.argtypes = [_i64, _i64]
-    L.cce_tile_bound_elems.restype = ctypes.c_size_t
+    L.cce_block_max_elems.argtypes = [_i64, _i64]
+    L.cce_block_max_elems.restype = ctypes.c_size_t
     L.cce_forward.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp, _vp,
                               ctypes.c_size_t, _vp]
     L.cce_forward.restype = ctypes.c_int
@@ -121,9 +121,9 @@ def vocab_order_workspace_bytes(N, D, V, dtype_code) -> int:
     return lib().cce_vocab_order_workspace_bytes(N, D, V, dtype_code)
 
 
-def tile_bound_elems(N, V) -> int:
-    """fp32 entries of the tile-bound table (one per 256 x 256 logit tile)."""
-    return lib().cce_tile_bound_elems(N, V)
+def block_max_elems(N, V) -> int:
+    """fp32 entries of the block-max table (one per 128 x 128 logit block)."""
+    return lib().cce_block_max_elems(N, V)
 
 
 def _stream(stream):
@@ -161,22 +161,22 @@ def _shapes(H, E, labels):
     return H.shape[0], H.shape[1], E.shape[0]
 
 
-def cce_forward(H, E, labels, ignore_index=-100, loss=None, lse=None, tile_bound=None, ws=None, stream=None):
-    """loss, lse (fp32 [N]) of the fused head + cross-entropy.  tile_bound:
-    None, or an fp32 tensor of tile_bound_elems(N, V) entries to receive the
-    largest logit of every 256 x 256 tile (for cce_backward)."""
+def cce_forward(H, E, labels, ignore_index=-100, loss=None, lse=None, block_max=None, ws=None, stream=None):
+    """loss, lse (fp32 [N]) of the fused head + cross-entropy.  block_max:
+    None, or an fp32 tensor of block_max_elems(N, V) entries to receive the
+    largest logit of every 128 x 128 block of the logits (for cce_backward)."""
     import torch
     N, D, V = _shapes(H, E, labels)
     dt = _dtype_code(H)
     loss = torch.empty(N, dtype=torch.float32, device=H.device) if loss is None else loss
     lse = torch.empty(N, dtype=torch.float32, device=H.device) if lse is None else lse
-    if tile_bound is not None and (tile_bound.dtype != torch.float32 or
-                                   tile_bound.numel() < tile_bound_elems(N, V) or not tile_bound.is_contiguous()):
-        raise ValueError(f"tile_bound must be contiguous fp32 with at least {tile_bound_elems(N, V)} entries")
+    if block_max is not None and (block_max.dtype != torch.float32 or
+                                  block_max.numel() < block_max_elems(N, V) or not block_max.is_contiguous()):
+        raise ValueError(f"block_max must be contiguous fp32 with at least {block_max_elems(N, V)} entries")
     need = forward_workspace_bytes(N, D, V, dt)
     ws = _workspace(need, H.device, ws)
     s = lib().cce_forward(_ptr(H), _ptr(E), _ptr(labels), N, D, V, dt, int(ignore_index), _ptr(loss), _ptr(lse),
-                          _ptr(tile_bound), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+                          _ptr(block_max), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("cce_forward", s)
     return loss, lse
 
@@ -197,9 +197,9 @@ def cce_vocab_order(H, E, labels, ignore_index=-100, perm=None, keys=None, want_
 
 
 def cce_backward(H, E, labels, lse, dloss, filter_eps=2.0 ** -12, ignore_index=-100, perm=None, flags=0,
-                 dH=None, dE=None, stats=None, ws=None, stream=None, tile_bound=None):
+                 dH=None, dE=None, stats=None, ws=None, stream=None, block_max=None):
     """dH [N, D], dE [V, D] (input dtype) of sum_i dloss_i loss_i.  stats:
-    None or int64 [5] (see include/cce.h); tile_bound: None or the table
+    None or int64 [5] (see include/cce.h); block_max: None or the table
     cce_forward wrote for the same H, E and labels."""
     import torch
     N, D, V = _shapes(H, E, labels)
@@ -208,10 +208,10 @@ def cce_backward(H, E, labels, lse, dloss, filter_eps=2.0 ** -12, ignore_index=-
     dE = torch.empty_like(E) if dE is None else dE
     if stats is not None and (stats.dtype != torch.int64 or stats.numel() < 5):
         raise ValueError("stats must be int64 with at least 5 entries")
-    if tile_bound is not None and (tile_bound.dtype != torch.float32 or tile_bound.numel() < tile_bound_elems(N, V)):
-        raise ValueError(f"tile_bound must be fp32 with at least {tile_bound_elems(N, V)} entries")
+    if block_max is not None and (block_max.dtype != torch.float32 or block_max.numel() < block_max_elems(N, V)):
+        raise ValueError(f"block_max must be fp32 with at least {block_max_elems(N, V)} entries")
     ws = _workspace(backward_workspace_bytes(N, D, V, dt), H.device, ws)
-    s = lib().cce_backward(_ptr(H), _ptr(E), _ptr(labels), _ptr(lse), _ptr(dloss), _ptr(tile_bound), N, D, V, dt,
+    s = lib().cce_backward(_ptr(H), _ptr(E), _ptr(labels), _ptr(lse), _ptr(dloss), _ptr(block_max), N, D, V, dt,
                            int(ignore_index),
                            float(filter_eps), _ptr(perm), int(flags), _ptr(dH), _ptr(dE), _ptr(stats), _ptr(ws),
                            ws.numel() * ws.element_size(), _stream(stream))

@@ -69,9 +69,9 @@ size_t cce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtype d
     return b;
 }
 
-size_t cce_tile_bound_elems(int64_t N, int64_t V) {
+size_t cce_block_max_elems(int64_t N, int64_t V) {
     if (!shape_ok(N, 8, V)) return 0;
-    return (size_t)tile_bound_elems(N, V);
+    return (size_t)block_max_elems(N, V);
 }
 
 size_t cce_vocab_order_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtype dtype) {
@@ -82,19 +82,19 @@ size_t cce_vocab_order_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtyp
 }
 
 cce_status cce_forward(const void *H, const void *E, const int64_t *labels, int64_t N, int64_t D, int64_t V,
-                       cce_dtype dtype, int64_t ignore_index, float *loss, float *lse, float *tile_bound, void *ws,
+                       cce_dtype dtype, int64_t ignore_index, float *loss, float *lse, float *block_max, void *ws,
                        size_t ws_bytes, void *stream) {
     if (!H || !E || !labels || !loss || !lse || !ws) return CCE_ERR_NULL;
     if (!dtype_ok(dtype)) return CCE_ERR_DTYPE;
     if (!shape_ok(N, D, V)) return CCE_ERR_SHAPE;
     if (!aligned(H, 16) || !aligned(E, 16) || !aligned(ws, 16) || !aligned(labels, 8) || !aligned(loss, 4) ||
-        !aligned(lse, 4) || !aligned(tile_bound, 4))
+        !aligned(lse, 4) || !aligned(block_max, 4))
         return CCE_ERR_ALIGN;
     const FwdShape s = fwd_shape(N, D, V);
     size_t need = 0;
     const FwdWs w = fwd_ws(ws, s, &need);
     if (ws_bytes < need) return CCE_ERR_WORKSPACE;
-    return hip_status(launch_forward(dtype, H, E, labels, s, ignore_index, w, loss, lse, tile_bound,
+    return hip_status(launch_forward(dtype, H, E, labels, s, ignore_index, w, loss, lse, block_max,
                                      static_cast<hipStream_t>(stream)));
 }
 
@@ -115,7 +115,7 @@ cce_status cce_vocab_order(const void *H, const void *E, const int64_t *labels, 
 }
 
 cce_status cce_backward(const void *H, const void *E, const int64_t *labels, const float *lse, const float *dloss,
-                        const float *tile_bound, int64_t N, int64_t D, int64_t V, cce_dtype dtype,
+                        const float *block_max, int64_t N, int64_t D, int64_t V, cce_dtype dtype,
                         int64_t ignore_index, float filter_eps, const int32_t *perm, unsigned flags, void *dH,
                         void *dE, int64_t *stats, void *ws, size_t ws_bytes, void *stream) {
     if (!H || !E || !labels || !lse || !dloss || !dH || !dE || !ws) return CCE_ERR_NULL;
@@ -125,13 +125,13 @@ cce_status cce_backward(const void *H, const void *E, const int64_t *labels, con
     if (flags & ~CCE_BWD_NO_KAHAN) return CCE_ERR_ARG;
     if (!aligned(H, 16) || !aligned(E, 16) || !aligned(dH, 16) || !aligned(dE, 16) || !aligned(ws, 16) ||
         !aligned(labels, 8) || !aligned(lse, 4) || !aligned(dloss, 4) || !aligned(perm, 4) || !aligned(stats, 8) ||
-        !aligned(tile_bound, 4))
+        !aligned(block_max, 4))
         return CCE_ERR_ALIGN;
     const BwdShape s = bwd_shape(N, D, V);
     size_t need = 0;
     const BwdWs w = bwd_ws(ws, s, elem_size(dtype), &need);
     if (ws_bytes < need) return CCE_ERR_WORKSPACE;
-    return hip_status(launch_backward(dtype, H, E, labels, lse, dloss, tile_bound, s, ignore_index, filter_eps, perm,
+    return hip_status(launch_backward(dtype, H, E, labels, lse, dloss, block_max, s, ignore_index, filter_eps, perm,
                                       flags, dH, dE, stats, w, static_cast<hipStream_t>(stream)));
 }
 

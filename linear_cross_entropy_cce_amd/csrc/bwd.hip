@@ -13,11 +13,12 @@
 // kept 128 x 128 filter block is therefore written once, in two layouts, to a
 // block store, and the two gradient products read it back:
 //
-//   plan        which 256 x 256 logit tiles may keep a block: all of them, or,
-//               with the forward's tile-bound table, only tiles whose largest
-//               logit comes near the smallest lse of their rows, plus tiles
-//               holding a label; the listed tiles are cut, in vocabulary
-//               order, into passes whose blocks fit the store
+//   plan        which 128 x 128 blocks may be kept: all of them, or, with the
+//               forward's block-max table, only blocks whose largest logit
+//               comes near the smallest lse of their rows, plus blocks holding
+//               a label; the 256 x 256 logit tiles holding such blocks are
+//               listed and cut, in vocabulary order, into passes whose blocks
+//               fit the store
 //   k_g_pass    per listed tile: recompute the logits (MFMA, the forward's
 //               code and K order), p = exp(z - lse), block filter, and the
 //               kept blocks' G into the store
@@ -58,7 +59,49 @@ struct PlanView {
 __device__ __forceinline__ PlanView plan_view(int32_t *plan, int max_passes) {
     return {plan, plan + 1, plan + 2, plan + 3 + max_passes, plan + 4 + 2 * max_passes};
 }
-static int plan_ints(int max_passes) { return 4 + 3 * max_passes; }
+// After the record, per pass kQueues work-queue counters (8 for the
+// recompute phase, one per XCD part of the tile list, and 1 for the gradient
+// phase).
+constexpr int kQueues = 9;
+static int plan_ints(int max_passes) { return 4 + (3 + kQueues) * max_passes; }
+__device__ __forceinline__ int32_t *plan_queues(int32_t *plan, int max_passes, int p) {
+    return plan + 4 + 3 * max_passes + kQueues * p;
+}
+
+// Next item of a work queue for the whole workgroup: thread 0 takes a
+// ticket, the others read it from LDS.  Items go to whichever workgroup asks
+// first; what an item computes does not depend on which one runs it.
+__device__ __forceinline__ int take_ticket(int32_t *counter, int *slot) {
+    if (threadIdx.x == 0) *slot = atomicAdd(counter, 1);
+    __syncthreads();
+    const int t = *slot;
+    __syncthreads();  // every thread has read the ticket before the next one overwrites it
+    return t;
+}
+
+// Everything the pass kernels read or write.
+template <typename T>
+struct BwdArgs {
+    int32_t *plan;
+    int max_passes;
+    const int32_t *tlist;
+    const uint8_t *tneed;
+    int n_rt;
+    const T *H, *E, *Ht;
+    int64_t ldh;  // Np
+    const int32_t *idx, *nvalid, *perm, *inv_perm;
+    const int64_t *labels;
+    const float *lse, *dloss;
+    int D, V, cbp, n_rb;
+    float eps;
+    T *Gt, *Gn;
+    int64_t cap;
+    uint8_t *st;
+    int32_t *slot;
+    int64_t *stats;
+    float *dh_acc;
+    T *dE, *dH;
+};
 
 // ------------------------------------------------------------ small kernels
 __global__ void k_inv_perm(const int32_t *__restrict__ perm, int V, int32_t *__restrict__ inv) {
@@ -91,30 +134,29 @@ __global__ __launch_bounds__(256) void k_fill_zero(float *__restrict__ p, int64_
     if (i < n) *reinterpret_cast<f32x4 *>(p + i) = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// lmin[rt] = smallest lse over the valid tokens of token tile rt (+inf if none).
-__global__ __launch_bounds__(256) void k_lse_min(const float *__restrict__ lse, const int32_t *__restrict__ idx,
+// lmin[rb] = smallest lse over the valid tokens of 128-token block rb (+inf if none).
+__global__ __launch_bounds__(128) void k_lse_min(const float *__restrict__ lse, const int32_t *__restrict__ idx,
                                                  const int32_t *__restrict__ nvalid_p, float *__restrict__ lmin) {
-    __shared__ float part[4];
-    const int tok = blockIdx.x * kTileRows + threadIdx.x;
+    __shared__ float part[2];
+    const int tok = blockIdx.x * kBlockRows + threadIdx.x;
     float v = tok < *nvalid_p ? lse[idx[tok]] : __builtin_huge_valf();
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
     __syncthreads();
-    if (threadIdx.x == 0) lmin[blockIdx.x] = fminf(fminf(part[0], part[1]), fminf(part[2], part[3]));
+    if (threadIdx.x == 0) lmin[blockIdx.x] = fminf(part[0], part[1]);
 }
 
-// True when every p in logit tile (rt, vocabulary tile vt) is provably below
-// eps / 2: the tile's largest logit T minus the smallest lse L of its tokens
-// is below thr = ln(eps / 2), with a relative margin for fp32 rounding of the
+// True when every p in block (rb, cb) is provably below eps / 2: the block's
+// largest logit T minus the smallest lse L of its tokens is below
+// thr = ln(eps / 2), with a relative margin for fp32 rounding of the
 // recomputed logits and of T - L.  The filter then keeps nothing of the
-// tile's softmax part, so its recompute can be left out without changing a
-// bit of the result.  NaN never skips.
-__device__ __forceinline__ bool tile_below(const float *__restrict__ tbound, int64_t tb_ld,
-                                           const float *__restrict__ lmin, float thr, int rt, int vt) {
-    if (!tbound) return false;
-    const float T = tbound[(int64_t)rt * tb_ld + vt];
-    const float L = lmin[rt];
+// block's softmax part.  NaN never passes.
+__device__ __forceinline__ bool block_below(const float *__restrict__ bmax, int64_t ld,
+                                            const float *__restrict__ lmin, float thr, int rb, int cb) {
+    if (!bmax) return false;
+    const float T = bmax[(int64_t)rb * ld + cb];
+    const float L = lmin[rb];
     return (T - L) + 0x1p-10f * (fabsf(T) + fabsf(L)) < thr;
 }
 
@@ -214,11 +256,12 @@ __global__ __launch_bounds__(256) void k_label_map(const int64_t *__restrict__ l
 
 // Per tile (vocabulary-tile-major index vt * n_rt + rt): the number of its
 // blocks that may be kept (bits 0-2) and whether its logits are recomputed
-// (bit 7).  A recomputed tile reserves all its real blocks; a tile left out
-// by the bound keeps only the blocks that hold a label.
+// (bit 7).  A block may keep its softmax part unless the bound rules it out,
+// and may keep its label entries if it holds a label; the tile's logits are
+// recomputed when any of its real blocks may keep a softmax part.
 __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ nvalid_p, int64_t V, int n_rt,
                                                     int n_vt, int cbp, const uint8_t *__restrict__ lab,
-                                                    const float *__restrict__ tbound, const float *__restrict__ lmin,
+                                                    const float *__restrict__ bmax, const float *__restrict__ lmin,
                                                     float thr, uint8_t *__restrict__ tneed) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)n_rt * n_vt) return;
@@ -228,13 +271,15 @@ __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ 
         tneed[i] = 0;
         return;
     }
-    const bool rec = !tile_below(tbound, n_vt, lmin, thr, rt, vt);
+    bool rec = false;
     int need = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int rb = 2 * rt + (q & 1), cb = 2 * vt + (q >> 1);
         if ((int64_t)rb * kBlockRows >= nv || (int64_t)cb * kBlockVocab >= V) continue;
-        need += (rec || lab[(int64_t)rb * cbp + cb]) ? 1 : 0;
+        const bool soft = !block_below(bmax, cbp, lmin, thr, rb, cb);
+        rec |= soft;
+        need += (soft || lab[(int64_t)rb * cbp + cb]) ? 1 : 0;
     }
     tneed[i] = (uint8_t)(need | (rec ? 0x80 : 0));
 }
@@ -319,6 +364,7 @@ __global__ __launch_bounds__(1024) void k_plan(const uint8_t *__restrict__ tneed
         }
     }
     for (int q = t; q < max_passes; q += 1024) pv.counter[q] = 0;
+    for (int q = t; q < kQueues * max_passes; q += 1024) plan_queues(plan, max_passes, 0)[q] = 0;
 }
 
 // ------------------------------------------------------- recompute + G
@@ -513,45 +559,48 @@ struct GPassLds {
                                      : TileF::kLdsChunks;
 };
 
-// Persistent over the listed tiles of pass p.  Hardware workgroup b runs on
-// XCD b % 8; the list is cut into 8 contiguous parts, one per XCD, so tiles
-// that share a vocabulary tile (adjacent in the list) share that XCD's L2.
+// Recompute phase of pass p on workgroups bid = 0 .. nbid - 1, which take
+// the pass's listed tiles from work queues.  Workgroup b runs on XCD b % 8;
+// with a grid that is a multiple of 8 the list is cut into 8 contiguous
+// parts and workgroup b starts on part b % 8 (tiles that share a vocabulary
+// tile are adjacent in the list, so they share that XCD's L2), then helps
+// with the other parts.
 template <typename T, bool DMA>
-__global__ __launch_bounds__(TileF::kThreads) void k_g_pass(
-    int p, int32_t *__restrict__ plan, int max_passes, const int32_t *__restrict__ tlist,
-    const uint8_t *__restrict__ tneed, int n_rt, const T *__restrict__ H, const T *__restrict__ E,
-    const int32_t *__restrict__ idx, const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm,
-    const int32_t *__restrict__ inv_perm, const int64_t *__restrict__ labels, const float *__restrict__ lse,
-    const float *__restrict__ dloss, int D, int V, int cbp, float eps, T *__restrict__ Gt, T *__restrict__ Gn,
-    int64_t cap, uint8_t *__restrict__ st, int32_t *__restrict__ slotm, int64_t *__restrict__ stats) {
+__device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int nbid, u32x4 *lds, int *qflag,
+                                        int *qstat, int *qslot) {
     using TL = TileF;
-    __shared__ u32x4 lds[GPassLds<T, DMA>::value];
-    __shared__ int qflag[4], qstat[4], qslot[4];
-    const PlanView pv = plan_view(plan, max_passes);
-    if (p >= *pv.P) return;
-    const int nv = *nvalid_p;
+    const PlanView pv = plan_view(a.plan, a.max_passes);
+    int32_t *queues = plan_queues(a.plan, a.max_passes, p);
+    const int nv = *a.nvalid;
     const int lb = pv.list_begin[p], le = pv.list_begin[p + 1];
-    const int nx = gridDim.x / 8;  // workgroups per XCD (the grid is a multiple of 8)
-    const int x = blockIdx.x % 8, wx = blockIdx.x / 8;
-    const int pb = lb + (int)((int64_t)(le - lb) * x / 8), pe = lb + (int)((int64_t)(le - lb) * (x + 1) / 8);
-    for (int i = pb + wx; i < pe; i += nx) {
-        const int tile = tlist[i];
-        const int vt = tile / n_rt, rt = tile % n_rt;
-        const bool rec = (tneed[tile] & 0x80) != 0;
-        const int tok0 = rt * TL::BN, p0 = vt * TL::BM;
-        if (threadIdx.x < 4) qflag[threadIdx.x] = 0;
-        __syncthreads();
-        f32x16 acc[TL::TM][TL::TN];
-        if (rec) {
-            zero_acc<TL>(acc);
-            if constexpr (DMA) recompute_dma<T, TL>(H, E, idx, nv, perm, D, V, tok0, p0, lds, acc);
-            else recompute_vgpr<T, TL>(H, E, idx, nv, perm, D, V, tok0, p0, lds, acc);
+    const int nparts = nbid % 8 == 0 ? 8 : 1;
+    for (int k = 0; k < nparts; ++k) {
+        const int part = (bid + k) % nparts;
+        const int pb = lb + (int)((int64_t)(le - lb) * part / nparts);
+        const int pe = lb + (int)((int64_t)(le - lb) * (part + 1) / nparts);
+        for (;;) {
+            const int i = pb + take_ticket(queues + part, qslot);
+            if (i >= pe) break;
+            const int tile = a.tlist[i];
+            const int vt = tile / a.n_rt, rt = tile % a.n_rt;
+            const bool rec = (a.tneed[tile] & 0x80) != 0;
+            const int tok0 = rt * TL::BN, p0 = vt * TL::BM;
+            if (threadIdx.x < 4) qflag[threadIdx.x] = 0;
             __syncthreads();
-            g_epilogue<T, TL, true>(acc, tok0, nv, p0, V, rt, vt, cbp, eps, idx, inv_perm, labels, lse, dloss, Gt, Gn,
-                                    cap, pv.counter + p, st, slotm, stats, qflag, qstat, qslot);
-        } else {
-            g_epilogue<T, TL, false>(acc, tok0, nv, p0, V, rt, vt, cbp, eps, idx, inv_perm, labels, lse, dloss, Gt,
-                                     Gn, cap, pv.counter + p, st, slotm, stats, qflag, qstat, qslot);
+            f32x16 acc[TL::TM][TL::TN];
+            if (rec) {
+                zero_acc<TL>(acc);
+                if constexpr (DMA) recompute_dma<T, TL>(a.H, a.E, a.idx, nv, a.perm, a.D, a.V, tok0, p0, lds, acc);
+                else recompute_vgpr<T, TL>(a.H, a.E, a.idx, nv, a.perm, a.D, a.V, tok0, p0, lds, acc);
+                __syncthreads();
+                g_epilogue<T, TL, true>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
+                                        a.lse, a.dloss, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
+                                        qflag, qstat, qslot);
+            } else {
+                g_epilogue<T, TL, false>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
+                                         a.lse, a.dloss, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
+                                         qflag, qstat, qslot);
+            }
         }
     }
 }
@@ -592,8 +641,8 @@ struct DhEngine {
     int b_row[NIB];     // B row (vocabulary entry within the stage) this lane feeds
     int b_off[NIB];     // byte offset of its chunk within an E row (clamped to the last chunk < D)
 
-    __device__ __forceinline__ DhEngine(u32x4 *l, int d0, int D) : lds(l), lds0(lds_addr(l)) {
-        const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __device__ __forceinline__ DhEngine(u32x4 *l, int d0, int D, int tid) : lds(l), lds0(lds_addr(l)) {
+        const int w = tid >> 6, lane = tid & 63;
         const int sa = 64 * w + lane;
         const int ra = sa / 4;
         a_off = ra * kBlockVocab * (int)sizeof(T) + 16 * ((sa & 3) ^ dma_swz<64>(ra));
@@ -633,8 +682,8 @@ struct DhEngine {
     }
     __device__ __forceinline__ int clamp_ahead(int ahead) const { return ahead < kDepth - 1 ? ahead : kDepth - 1; }
 
-    __device__ __forceinline__ void compute(int buf, f32x16 (&acc)[TL::TM][TL::TN]) const {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __device__ __forceinline__ void compute(int buf, f32x16 (&acc)[TL::TM][TL::TN], int tid) const {
+        const int lane = tid & 63, wave = tid >> 6;
         const int ra0 = (wave % TL::WM) * TL::kWaveM + (lane & 31);
         const int nb0 = (wave / TL::WM) * TL::kWaveN;
         const u32x4 *A = lds + buf * kStage;
@@ -711,17 +760,18 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
     constexpr int kSpb = kBlockBytes / DE::kStageBytes;       // stages per row block
     constexpr int64_t kStoreBytes = (int64_t)kBlockElems * sizeof(T);
     constexpr int CE = ChunkElems<T>::value;
+    const int tid = opaque_tid();  // per-item lane arithmetic is redone per item, not held in registers
     DE eng(sh.stages);
 #pragma unroll
     for (int j = 0; j < DE::NIA; ++j) {
-        const int r = DE::row_a(j);
-        eng.pa[j] = reinterpret_cast<const char *>(Gt + (int64_t)r * kBlockRows) + DE::chunk_off(r);
+        const int r = DE::row_a(j, tid);
+        eng.pa[j] = reinterpret_cast<const char *>(Gt + (int64_t)r * kBlockRows) + DE::chunk_off(r, tid);
     }
 #pragma unroll
     for (int j = 0; j < DE::NIB; ++j) {
-        const int r = DE::row_b(j);
+        const int r = DE::row_b(j, tid);
         const int d = min(d0 + r, D - 1);
-        eng.pb[j] = reinterpret_cast<const char *>(Ht + (int64_t)d * ldh) + DE::chunk_off(r);
+        eng.pb[j] = reinterpret_cast<const char *>(Ht + (int64_t)d * ldh) + DE::chunk_off(r, tid);
     }
     f32x16 acc[TL::TM][TL::TN], sum[TL::TM][TL::TN], comp[TL::TM][TL::TN];
     zero_acc<TL>(acc);
@@ -748,7 +798,7 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
             const int ahead = total - 1 - s;
             eng.wait_stage(eng.clamp_ahead(ahead));
             if (s + DE::kDepth < total) issue((s + DE::kDepth) % DE::kStages, s + DE::kDepth);
-            eng.compute(s % DE::kStages, acc);
+            eng.compute(s % DE::kStages, acc, tid);
             if (KAHAN && (s % kSpb) == kSpb - 1) {
 #pragma clang fp contract(off)
 #pragma unroll
@@ -788,11 +838,11 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
         for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
             for (int tn = 0; tn < TL::TN; ++tn) {
-                const int col = tile_col<TL>(tn);
+                const int col = tile_col<TL>(tn, tid);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float val = KAHAN ? sum[tm][tn][r] - comp[tm][tn][r] : acc[tm][tn][r];
-                    tile[tile_row<TL>(tm, r) * kLd + col] = from_f32<T>(val);
+                    tile[tile_row<TL>(tm, r, tid) * kLd + col] = from_f32<T>(val);
                 }
             }
         __syncthreads();
@@ -811,7 +861,7 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
         for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int pos = cb * TL::BM + tile_row<TL>(tm, r);
+                const int pos = cb * TL::BM + tile_row<TL>(tm, r, tid);
                 const int v = pos < V ? (perm ? perm[pos] : pos) : -1;
                 vid[tm][r] = (v >= 0 && v < V) ? v : -1;
             }
@@ -819,7 +869,7 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
         for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
             for (int tn = 0; tn < TL::TN; ++tn) {
-                const int d = d0 + tile_col<TL>(tn);
+                const int d = d0 + tile_col<TL>(tn, tid);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float val = KAHAN ? sum[tm][tn][r] - comp[tm][tn][r] : acc[tm][tn][r];
@@ -845,6 +895,7 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
     using DH = DhEngine<T>;
     const int tok0 = rb * TL::BM;
     const size_t rowb = (size_t)D * sizeof(T);
+    const int tid = opaque_tid();  // per-item lane arithmetic is redone per item, not held in registers
 
     f32x16 acc[TL::TM][TL::TN], sum[TL::TM][TL::TN];
     zero_acc<TL>(acc);
@@ -853,16 +904,16 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
         for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
             for (int tn = 0; tn < TL::TN; ++tn) {
-                const int d = min(d0 + tile_col<TL>(tn), D - 1);
+                const int d = min(d0 + tile_col<TL>(tn, tid), D - 1);
 #pragma unroll
                 for (int r = 0; r < 16; ++r)  // dh_acc is [Np, D]: every tok < Np is in bounds
-                    sum[tm][tn][r] = dh_acc[(int64_t)(tok0 + tile_row<TL>(tm, r)) * D + d];
+                    sum[tm][tn][r] = dh_acc[(int64_t)(tok0 + tile_row<TL>(tm, r, tid)) * D + d];
             }
     } else {
         zero_acc<TL>(sum);
     }
 
-    DH eng(sh.stages, d0, D);
+    DH eng(sh.stages, d0, D, tid);
     bool any = false;
     for (int base = cb0; base < cb1; base += kListCap) {
         const int cnt = cb1 - base < kListCap ? cb1 - base : kListCap;
@@ -883,7 +934,7 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
             const int ahead = total - 1 - s;
             eng.wait_stage(eng.clamp_ahead(ahead));
             if (s + DH::kDepth < total) issue((s + DH::kDepth) % DH::kStages, s + DH::kDepth);
-            eng.compute(s % DH::kStages, acc);
+            eng.compute(s % DH::kStages, acc, tid);
             if ((s % DH::kSpb) == DH::kSpb - 1) {
 #pragma unroll
                 for (int tm = 0; tm < TL::TM; ++tm)
@@ -905,15 +956,15 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
 #pragma unroll
         for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) row[tm][r] = idx[min(tok0 + tile_row<TL>(tm, r), nv - 1)];
+            for (int r = 0; r < 16; ++r) row[tm][r] = idx[min(tok0 + tile_row<TL>(tm, r, tid), nv - 1)];
 #pragma unroll
         for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
             for (int tn = 0; tn < TL::TN; ++tn) {
-                const int d = d0 + tile_col<TL>(tn);
+                const int d = d0 + tile_col<TL>(tn, tid);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int tok = tok0 + tile_row<TL>(tm, r);
+                    const int tok = tok0 + tile_row<TL>(tm, r, tid);
                     if (tok < nv && d < D) dH[(int64_t)row[tm][r] * D + d] = from_f32<T>(sum[tm][tn][r]);
                 }
             }
@@ -922,10 +973,10 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
         for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
             for (int tn = 0; tn < TL::TN; ++tn) {
-                const int d = d0 + tile_col<TL>(tn);
+                const int d = d0 + tile_col<TL>(tn, tid);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int tok = tok0 + tile_row<TL>(tm, r);
+                    const int tok = tok0 + tile_row<TL>(tm, r, tid);
                     if (tok < nv && d < D) dh_acc[(int64_t)tok * D + d] = sum[tm][tn][r];
                 }
             }
@@ -933,39 +984,54 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
 }
 
 // --------------------------------------------------- gradient products
-// Both products of pass p in one launch: workgroups below n_de are
-// persistent over the pass's (vocabulary block, feature tile) dE items; the
-// others each take one (row block, feature tile) dH item.
+// Gradient phase of pass p on workgroups bid = 0 .. nbid - 1, which take
+// items from a work queue: first the (row block, feature tile) dH items,
+// which carry the longer K loops, then the (vocabulary block, feature tile)
+// dE items.
 template <typename T, bool KAHAN>
-__global__ __launch_bounds__(TileG::kThreads) void k_grad_pass(
-    int p, int32_t *__restrict__ plan, int max_passes, int n_de, const uint8_t *__restrict__ st,
-    const int32_t *__restrict__ slotm, int cbp, const int32_t *__restrict__ nvalid_p,
-    const int32_t *__restrict__ idx, const T *__restrict__ Gt, const T *__restrict__ Gn, const T *__restrict__ Ht,
-    int64_t ldh, const T *__restrict__ E, const int32_t *__restrict__ perm, int D, int V, int n_rb_grid,
-    float *__restrict__ dh_acc, T *__restrict__ dE, T *__restrict__ dH) {
+__device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, GradLds<T> &sh, int *ticket) {
     using TL = TileG;
-    __shared__ GradLds<T> sh;
-    const PlanView pv = plan_view(plan, max_passes);
-    const int P = *pv.P;
-    if (p >= P) return;
-    const int nv = *nvalid_p;
-    const int CB = (V + kBlockVocab - 1) / kBlockVocab;
+    const PlanView pv = plan_view(a.plan, a.max_passes);
+    int32_t *queue = plan_queues(a.plan, a.max_passes, p) + 8;
+    const int nv = *a.nvalid;
+    const int CB = (a.V + kBlockVocab - 1) / kBlockVocab;
     const int cb0 = 2 * pv.vt_begin[p];
     const int cb1 = min(2 * pv.vt_begin[p + 1], CB);
-    const int n_dt = (D + TL::BN - 1) / TL::BN;
-    if ((int)blockIdx.x < n_de) {
-        const int n_rb = (nv + kBlockRows - 1) / kBlockRows;
-        const int64_t items = cb1 > cb0 ? (int64_t)(cb1 - cb0) * n_dt : 0;
-        for (int64_t it = blockIdx.x; it < items; it += n_de)
-            de_item<T, KAHAN>(sh, cb0 + (int)(it / n_dt), (int)(it % n_dt) * TL::BN, n_rb, st, slotm, cbp, Gt, Ht, ldh,
-                              perm, D, V, dE);
-    } else {
-        const int b = blockIdx.x - n_de;
-        const int rb = b % n_rb_grid;
-        if (rb * TL::BM >= nv) return;
-        dh_item<T>(sh, rb, (b / n_rb_grid) * TL::BN, P > 1, p == P - 1, cb0, cb1, st, slotm, cbp, nv, idx, Gn, E,
-                   perm, D, V, dh_acc, dH);
+    const int n_dt = (a.D + TL::BN - 1) / TL::BN;
+    const int n_rbv = (nv + kBlockRows - 1) / kBlockRows;
+    const int64_t n_dh = (int64_t)n_rbv * n_dt;
+    const int64_t n_de = cb1 > cb0 ? (int64_t)(cb1 - cb0) * n_dt : 0;
+    // two loops rather than one with a branch: each keeps its own registers
+    int64_t it = take_ticket(queue, ticket);
+    while (it < n_dh) {
+        dh_item<T>(sh, (int)(it % n_rbv), (int)(it / n_rbv) * TL::BN, P > 1, p == P - 1, cb0, cb1, a.st, a.slot, a.cbp,
+                   nv, a.idx, a.Gn, a.E, a.perm, a.D, a.V, a.dh_acc, a.dH);
+        it = take_ticket(queue, ticket);
     }
+    while (it < n_dh + n_de) {
+        const int64_t q = it - n_dh;
+        de_item<T, KAHAN>(sh, cb0 + (int)(q / n_dt), (int)(q % n_dt) * TL::BN, n_rbv, a.st, a.slot, a.cbp, a.Gt, a.Ht,
+                          a.ldh, a.perm, a.D, a.V, a.dE);
+        it = take_ticket(queue, ticket);
+    }
+}
+
+// One launch per pass and phase.
+template <typename T, bool DMA>
+__global__ __launch_bounds__(TileF::kThreads) void k_g_pass(BwdArgs<T> a, int p) {
+    __shared__ u32x4 lds[GPassLds<T, DMA>::value];
+    __shared__ int qflag[4], qstat[4], qslot[4];
+    if (p >= *plan_view(a.plan, a.max_passes).P) return;
+    g_phase<T, DMA>(a, p, blockIdx.x, gridDim.x, lds, qflag, qstat, qslot);
+}
+
+template <typename T, bool KAHAN>
+__global__ __launch_bounds__(TileG::kThreads) void k_grad_pass(BwdArgs<T> a, int p) {
+    __shared__ GradLds<T> sh;
+    __shared__ int ticket;
+    const int P = *plan_view(a.plan, a.max_passes).P;
+    if (p >= P) return;
+    grad_phase<T, KAHAN>(a, p, P, sh, &ticket);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1003,7 +1069,7 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     w.idx = c.take<int32_t>(s.N);
     w.nvalid = c.take<int32_t>(1);
     w.inv_perm = c.take<int32_t>(s.V);
-    w.lmin = c.take<float>((size_t)s.n_rtiles);
+    w.lmin = c.take<float>((size_t)s.n_rb);
     w.lab = c.take<uint8_t>(nblk);
     w.st = c.take<uint8_t>(nblk);
     w.slot = c.take<int32_t>(nblk);
@@ -1037,7 +1103,7 @@ static hipError_t fill_bytes_zero(void *p, size_t nbytes, hipStream_t st) {
 
 template <typename T>
 static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, const float *lse,
-                             const float *dloss, const float *tile_bound, const BwdShape &s, int64_t ignore_index,
+                             const float *dloss, const float *block_max, const BwdShape &s, int64_t ignore_index,
                              float eps, const int32_t *perm, unsigned flags, T *dH, T *dE, int64_t *stats,
                              const BwdWs &w, hipStream_t st) {
     const int D = (int)s.D, V = (int)s.V;
@@ -1069,15 +1135,14 @@ static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, cons
                        ignore_index, dH);
     CCE_LAUNCHED();
 
-    // The tile bound is in the natural vocabulary order and only says something
-    // when filtering is on.  thr = ln(eps / 2), rounded towards -inf.
-    const float *tb = (tile_bound && !perm && eps > 0.f) ? tile_bound : nullptr;
+    // The block maxima are in the natural vocabulary order and only say
+    // something when filtering is on.  thr = ln(eps / 2), rounded towards -inf.
+    const float *tb = (block_max && !perm && eps > 0.f) ? block_max : nullptr;
     float thr = 0.f;
     if (tb) {
         thr = (float)(log((double)eps) - log(2.0));
         thr = nextafterf(thr, -__builtin_huge_valf());
-        hipLaunchKernelGGL(k_lse_min, dim3((unsigned)s.n_rtiles), dim3(kTileRows), 0, st, lse, w.idx, w.nvalid,
-                           w.lmin);
+        hipLaunchKernelGGL(k_lse_min, dim3((unsigned)s.n_rb), dim3(kBlockRows), 0, st, lse, w.idx, w.nvalid, w.lmin);
         CCE_LAUNCHED();
     }
     const int32_t *invp = perm ? w.inv_perm : nullptr;
@@ -1092,27 +1157,49 @@ static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, cons
                        s.max_passes, w.plan, w.cum, w.act, w.tlist);
     CCE_LAUNCHED();
 
+    BwdArgs<T> a;
+    a.plan = w.plan;
+    a.max_passes = s.max_passes;
+    a.tlist = w.tlist;
+    a.tneed = w.tneed;
+    a.n_rt = s.n_rtiles;
+    a.H = H;
+    a.E = E;
+    a.Ht = Ht;
+    a.ldh = s.Np;
+    a.idx = w.idx;
+    a.nvalid = w.nvalid;
+    a.perm = perm;
+    a.inv_perm = invp;
+    a.labels = labels;
+    a.lse = lse;
+    a.dloss = dloss;
+    a.D = D;
+    a.V = V;
+    a.cbp = s.cbp;
+    a.n_rb = s.n_rb;
+    a.eps = eps;
+    a.Gt = Gt;
+    a.Gn = Gn;
+    a.cap = s.cap;
+    a.st = w.st;
+    a.slot = w.slot;
+    a.stats = stats;
+    a.dh_acc = w.dh_acc;
+    a.dE = dE;
+    a.dH = dH;
     const bool dma_g = ((int64_t)D * (int64_t)sizeof(T)) % kLogitRowBytes == 0;
-    const int n_dt = (int)ceil_div(D, TileG::BN);
+    const bool kahan = !(flags & CCE_BWD_NO_KAHAN);
     for (int p = 0; p < s.max_passes; ++p) {
         if (dma_g)
-            hipLaunchKernelGGL((k_g_pass<T, true>), dim3(kPassGroups), dim3(TileF::kThreads), 0, st, p, w.plan,
-                               s.max_passes, w.tlist, w.tneed, s.n_rtiles, H, E, w.idx, w.nvalid, perm, invp, labels,
-                               lse, dloss, D, V, s.cbp, eps, Gt, Gn, s.cap, w.st, w.slot, stats);
+            hipLaunchKernelGGL((k_g_pass<T, true>), dim3(kPassGroups), dim3(TileF::kThreads), 0, st, a, p);
         else
-            hipLaunchKernelGGL((k_g_pass<T, false>), dim3(kPassGroups), dim3(TileF::kThreads), 0, st, p, w.plan,
-                               s.max_passes, w.tlist, w.tneed, s.n_rtiles, H, E, w.idx, w.nvalid, perm, invp, labels,
-                               lse, dloss, D, V, s.cbp, eps, Gt, Gn, s.cap, w.st, w.slot, stats);
+            hipLaunchKernelGGL((k_g_pass<T, false>), dim3(kPassGroups), dim3(TileF::kThreads), 0, st, a, p);
         CCE_LAUNCHED();
-        const unsigned grid = (unsigned)(kDeGroups + s.n_rb * n_dt);
-        if (flags & CCE_BWD_NO_KAHAN)
-            hipLaunchKernelGGL((k_grad_pass<T, false>), dim3(grid), dim3(TileG::kThreads), 0, st, p, w.plan,
-                               s.max_passes, kDeGroups, w.st, w.slot, s.cbp, w.nvalid, w.idx, Gt, Gn, Ht,
-                               (int64_t)s.Np, E, perm, D, V, s.n_rb, w.dh_acc, dE, dH);
+        if (kahan)
+            hipLaunchKernelGGL((k_grad_pass<T, true>), dim3(2 * kPassGroups), dim3(TileG::kThreads), 0, st, a, p);
         else
-            hipLaunchKernelGGL((k_grad_pass<T, true>), dim3(grid), dim3(TileG::kThreads), 0, st, p, w.plan,
-                               s.max_passes, kDeGroups, w.st, w.slot, s.cbp, w.nvalid, w.idx, Gt, Gn, Ht,
-                               (int64_t)s.Np, E, perm, D, V, s.n_rb, w.dh_acc, dE, dH);
+            hipLaunchKernelGGL((k_grad_pass<T, false>), dim3(2 * kPassGroups), dim3(TileG::kThreads), 0, st, a, p);
         CCE_LAUNCHED();
     }
     if (stats) {
@@ -1123,15 +1210,15 @@ static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, cons
 }
 
 hipError_t launch_backward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
-                           const float *lse, const float *dloss, const float *tile_bound, const BwdShape &s,
+                           const float *lse, const float *dloss, const float *block_max, const BwdShape &s,
                            int64_t ignore_index, float eps, const int32_t *perm, unsigned flags,
                            void *dH, void *dE, int64_t *stats, const BwdWs &w, hipStream_t st) {
     if (dt == CCE_BF16)
         return backward_t<bf16_t>(static_cast<const bf16_t *>(H), static_cast<const bf16_t *>(E), labels, lse,
-                                  dloss, tile_bound, s, ignore_index, eps, perm, flags, static_cast<bf16_t *>(dH),
+                                  dloss, block_max, s, ignore_index, eps, perm, flags, static_cast<bf16_t *>(dH),
                                   static_cast<bf16_t *>(dE), stats, w, st);
     return backward_t<float>(static_cast<const float *>(H), static_cast<const float *>(E), labels, lse, dloss,
-                             tile_bound, s, ignore_index, eps, perm, flags, static_cast<float *>(dH),
+                             block_max, s, ignore_index, eps, perm, flags, static_cast<float *>(dH),
                              static_cast<float *>(dE), stats, w, st);
 }
 

@@ -312,8 +312,8 @@ struct DmaEngine {
     }
     __device__ __forceinline__ int clamp_ahead(int ahead) const { return ahead < kDepth - 1 ? ahead : kDepth - 1; }
 
-    __device__ __forceinline__ void compute(int buf, f32x16 (&acc)[TL::TM][TL::TN]) const {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __device__ __forceinline__ void compute(int buf, f32x16 (&acc)[TL::TM][TL::TN], int tid = threadIdx.x) const {
+        const int lane = tid & 63, wave = tid >> 6;
         const int ra0 = (wave % TL::WM) * TL::kWaveM + (lane & 31);
         const int rb0 = (wave / TL::WM) * TL::kWaveN + (lane & 31);
         const u32x4 *A = lds + buf * kStage;

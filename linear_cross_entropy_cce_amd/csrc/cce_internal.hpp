@@ -32,8 +32,9 @@ constexpr int kFwdTargetGroups = 512;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
-// Entries of the tile-bound table: one per (token tile, vocabulary tile).
-inline int64_t tile_bound_elems(int64_t N, int64_t V) { return ceil_div(N, kTileRows) * ceil_div(V, kTileVocab); }
+// Entries of the block-max table: one per 128 x 128 block of the logit
+// matrix of the valid rows, [2 ceil(N / 256), 2 ceil(V / 256)].
+inline int64_t block_max_elems(int64_t N, int64_t V) { return 4 * ceil_div(N, kTileRows) * ceil_div(V, kTileVocab); }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Carves a caller workspace into aligned regions (or only sizes it when the
@@ -89,7 +90,7 @@ struct BwdWs {
     int32_t *idx;      // [N]
     int32_t *nvalid;   // [1]
     int32_t *inv_perm; // [V] processing position of each vocabulary id
-    float *lmin;       // [n_rtiles] smallest lse of each token tile (for the tile bound)
+    float *lmin;       // [n_rb] smallest lse of each 128-token block (for the block-max bound)
     uint8_t *lab;      // [n_rb, cbp] 1 where a label falls in the block
     uint8_t *st;       // [n_rb, cbp] block status: 0 dropped, 1 softmax kept, 2 label only
     int32_t *slot;     // [n_rb, cbp] store slot of a kept block
@@ -124,9 +125,9 @@ hipError_t launch_check_labels(const int64_t *labels, int64_t N, int64_t V, int6
                                int64_t *n_bad, hipStream_t st);
 hipError_t launch_forward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
                           const FwdShape &s, int64_t ignore_index, const FwdWs &w, float *loss,
-                          float *lse, float *tile_bound, hipStream_t st);
+                          float *lse, float *block_max, hipStream_t st);
 hipError_t launch_backward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
-                           const float *lse, const float *dloss, const float *tile_bound, const BwdShape &s,
+                           const float *lse, const float *dloss, const float *block_max, const BwdShape &s,
                            int64_t ignore_index, float eps, const int32_t *perm, unsigned flags,
                            void *dH, void *dE, int64_t *stats, const BwdWs &w, hipStream_t st);
 hipError_t launch_vocab_order(cce_dtype dt, const void *H, const void *E, const int64_t *labels,

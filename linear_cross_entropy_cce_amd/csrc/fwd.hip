@@ -148,14 +148,27 @@ __device__ __forceinline__ float fwd_tile_update(f32x16 (&acc)[TL::TM][TL::TN], 
     return tmax;
 }
 
-// Tile-bound table: the largest logit of every (256-token tile, 256-entry
-// vocabulary tile), combined over the workgroup's waves with an integer atomic
-// max on the order-preserving encoding.  Lane j of each wave keeps the maximum
-// of the j-th tile of a group of 64 and the wave writes the group with one
-// vector atomic, so the table costs one memory instruction per 64 tiles.
+// Block-max table: the largest logit of every 128 x 128 block of the logit
+// matrix of the valid rows.  A wave of the 256 x 256 tile covers 128
+// vocabulary rows x 64 tokens, half of one block; the two waves of a block
+// combine with an integer atomic max on the order-preserving encoding.  Lane
+// j of each wave keeps the maximum of the j-th tile of a group of 64 and the
+// wave writes the group with one vector atomic, so the table costs one memory
+// instruction per 64 tiles.
 struct BoundSink {
-    int *row;   // table row of this token tile, from the split's first vocabulary tile; null: no table
+    int *row;   // this wave's block of the table at the split's first tile (stride 2 per tile); null: no table
     int keep = 0;
+    // (Token rows past the valid ones are copies of the last valid row, so a
+    // block with some valid rows gets its true maximum; a block with none is
+    // left at -inf.)
+    template <class TL>
+    static __device__ __forceinline__ int *block_of(int *table, int64_t ld, int rt, int t0, int nv) {
+        const int wave = threadIdx.x >> 6;
+        const int wm = wave % TL::WM, th = (wave / TL::WM) * TL::kWaveN / 128;
+        static_assert(TL::kWaveM == 128 && TL::BM == 256 && TL::BN == 256, "a wave covers half of a 128 x 128 block");
+        if (!table || (2 * rt + th) * 128 >= nv) return nullptr;
+        return table + (int64_t)(2 * rt + th) * ld + 2 * t0 + wm;
+    }
     __device__ __forceinline__ void tile(int ct, float lane_max, bool last) {
         if (!row) return;
         const int m = wave_max_i32(bound_enc(lane_max));
@@ -163,7 +176,7 @@ struct BoundSink {
         const int j = ct & 63;
         if (lane == j) keep = m;
         if (j == 63 || last) {
-            if (lane <= j) atomicMax(row + (ct - j) + lane, keep);
+            if (lane <= j) atomicMax(row + 2 * (ct - j + lane), keep);
         }
     }
 };
@@ -240,7 +253,7 @@ __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
     const size_t rowb = (size_t)D * sizeof(T);
     const int kvalid = D * (int)sizeof(T);
     const int ns = (kvalid + TL::kStageBytes - 1) / TL::kStageBytes;
-    BoundSink bs{tbound ? tbound + (int64_t)rt * n_vtiles + t0 : nullptr};
+    BoundSink bs{BoundSink::block_of<TL>(tbound, 2 * (int64_t)n_vtiles, rt, t0, nv)};
 
     Engine<T, TL> eng;
 #pragma unroll
@@ -314,7 +327,7 @@ __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
     const int ntile = t1 - t0;
     const size_t rowb = (size_t)D * sizeof(T);
     const int ns = D * (int)sizeof(T) / DE::kStageBytes;
-    BoundSink bs{tbound ? tbound + (int64_t)rt * n_vtiles + t0 : nullptr};
+    BoundSink bs{BoundSink::block_of<TL>(tbound, 2 * (int64_t)n_vtiles, rt, t0, nv)};
 
     DE eng(lds);
 #pragma unroll
@@ -459,12 +472,12 @@ hipError_t launch_check_labels(const int64_t *labels, int64_t N, int64_t V, int6
 
 template <typename T>
 static hipError_t forward_t(const T *H, const T *E, const int64_t *labels, const FwdShape &s,
-                            int64_t ignore_index, const FwdWs &w, float *loss, float *lse, float *tile_bound,
+                            int64_t ignore_index, const FwdWs &w, float *loss, float *lse, float *block_max,
                             hipStream_t st) {
     hipError_t e = launch_compact(labels, s.N, ignore_index, w.idx, w.nvalid, st);
     if (e != hipSuccess) return e;
-    int *tb = reinterpret_cast<int *>(tile_bound);
-    const int64_t nb = (int64_t)s.n_rtiles * s.n_vtiles;
+    int *tb = reinterpret_cast<int *>(block_max);
+    const int64_t nb = 4 * (int64_t)s.n_rtiles * s.n_vtiles;
     if (tb) {
         hipLaunchKernelGGL(k_bound_init, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, st, tb, nb);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -486,12 +499,12 @@ static hipError_t forward_t(const T *H, const T *E, const int64_t *labels, const
 
 hipError_t launch_forward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
                           const FwdShape &s, int64_t ignore_index, const FwdWs &w, float *loss,
-                          float *lse, float *tile_bound, hipStream_t st) {
+                          float *lse, float *block_max, hipStream_t st) {
     if (dt == CCE_BF16)
         return forward_t<bf16_t>(static_cast<const bf16_t *>(H), static_cast<const bf16_t *>(E), labels,
-                                 s, ignore_index, w, loss, lse, tile_bound, st);
+                                 s, ignore_index, w, loss, lse, block_max, st);
     return forward_t<float>(static_cast<const float *>(H), static_cast<const float *>(E), labels, s,
-                            ignore_index, w, loss, lse, tile_bound, st);
+                            ignore_index, w, loss, lse, block_max, st);
 }
 
 }  // namespace cce

@@ -60,27 +60,27 @@ def t64(t: torch.Tensor) -> np.ndarray:
 
 def run_gpu(x: inputs.Inputs, dloss: np.ndarray, eps: float, sort=False, flags=0, prefill_nan=True, bound=True):
     """Forward + backward through the C ABI; returns fp64 numpy arrays.
-    bound: the forward writes the tile-bound table and the backward gets it
+    bound: the forward writes the block-max table and the backward gets it
     (as the autograd wrapper does); False runs the backward without it."""
     H, E, y = to_device(x)
     loss = torch.full((x.N,), float("nan"), dtype=torch.float32, device=DEV)
     lse = torch.full((x.N,), float("nan"), dtype=torch.float32, device=DEV)
-    tb = torch.full((B.tile_bound_elems(x.N, x.V),), float("nan"), dtype=torch.float32, device=DEV) \
+    tb = torch.full((B.block_max_elems(x.N, x.V),), float("nan"), dtype=torch.float32, device=DEV) \
         if bound else None
-    B.cce_forward(H, E, y, x.ignore_index, loss=loss, lse=lse, tile_bound=tb)
+    B.cce_forward(H, E, y, x.ignore_index, loss=loss, lse=lse, block_max=tb)
     perm = B.cce_vocab_order(H, E, y, x.ignore_index) if sort else None
     dl = torch.from_numpy(dloss).to(DEV)
     dH = torch.full_like(H, float("nan")) if prefill_nan else None
     dE = torch.full_like(E, float("nan")) if prefill_nan else None
     stats = torch.zeros(5, dtype=torch.int64, device=DEV)
     dH, dE = B.cce_backward(H, E, y, lse, dl, eps, x.ignore_index, perm, flags, dH=dH, dE=dE, stats=stats,
-                            tile_bound=tb)
+                            block_max=tb)
     torch.cuda.synchronize()
     out = dict(loss=t64(loss), lse=t64(lse), dH=t64(dH), dE=t64(dE), stats=stats.cpu().numpy())
     if perm is not None:
         out["perm"] = perm.cpu().numpy()
     if tb is not None:
-        out["tile_bound"] = tb.cpu().numpy().astype(np.float64)
+        out["block_max"] = tb.cpu().numpy().astype(np.float64)
     return out
 
 

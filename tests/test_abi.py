@@ -145,15 +145,15 @@ def test_backward_specific_errors():
     assert _bwd(ws_bytes=need - 1) == B.CCE_ERR_WORKSPACE
 
 
-def test_tile_bound_elems():
-    # one entry per 256-token x 256-vocabulary tile; 0 on invalid sizes
-    assert B.tile_bound_elems(1, 1) == 1
-    assert B.tile_bound_elems(256, 256) == 1
-    assert B.tile_bound_elems(257, 256) == 2
-    assert B.tile_bound_elems(8192, 256000) == 32 * 1000
-    assert B.tile_bound_elems(24576, 248320) == 96 * 970
-    assert B.tile_bound_elems(0, 10) == 0
-    assert B.tile_bound_elems(10, 0) == 0
+def test_block_max_elems():
+    # one entry per 128 x 128 logit block, over whole 256 x 256 tiles; 0 on invalid sizes
+    assert B.block_max_elems(1, 1) == 4
+    assert B.block_max_elems(256, 256) == 4
+    assert B.block_max_elems(257, 256) == 8
+    assert B.block_max_elems(8192, 256000) == 64 * 2000
+    assert B.block_max_elems(24576, 248320) == 192 * 1940
+    assert B.block_max_elems(0, 10) == 0
+    assert B.block_max_elems(10, 0) == 0
 
 
 def test_check_labels_errors():

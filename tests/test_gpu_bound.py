@@ -1,12 +1,13 @@
-"""The tile-bound table and the recompute skip it allows.
+"""The block-max table and the recompute skip it allows.
 
-cce_forward can record the largest logit of every 256-token x 256-vocabulary
-tile; cce_backward, given that table, leaves out tiles whose every softmax
-entry is provably below filter_eps / 2.  The gradient filter would drop all of
-such a tile's softmax part, so the outputs must be bit-identical to a run
-without the table; only the count of recomputed blocks (stats[4]) changes.
-The table itself is checked against the definition: the largest fp64 logit of
-each tile of the valid rows (in order), -inf for tiles past the valid rows.
+cce_forward can record the largest logit of every 128-token x 128-vocabulary
+block; cce_backward, given that table, leaves out the logit recompute of
+256 x 256 tiles whose every softmax entry is provably below filter_eps / 2.
+The gradient filter would drop all of such a tile's softmax part, so the
+outputs must be bit-identical to a run without the table; only the count of
+recomputed blocks (stats[4]) changes.  The table itself is checked against the
+definition: the largest fp64 logit of each block of the valid rows (in order),
+-inf for blocks past the valid rows.
 """
 import numpy as np
 import pytest
@@ -19,7 +20,7 @@ from tests import _gpu as G
 
 pytestmark = pytest.mark.gpu
 
-TILE = 256
+BLK = 128
 CASES = [
     (1, None, None, None),    # fp32, flat, 10 % ignored
     (2, 700, 256, 9000),      # peaked, two vocabulary chunks, ragged
@@ -28,29 +29,29 @@ CASES = [
 ]
 
 
-def _ref_tile_max(x):
+def _ref_block_max(x):
     H = oracle.as_f64(x.H, x.dtype)
     E = oracle.as_f64(x.E, x.dtype)
     valid = np.nonzero(x.labels != x.ignore_index)[0]
     Z = H[valid] @ E.T  # the logits of the valid rows, in order
-    nrt, nvt = -(-x.N // TILE), -(-x.V // TILE)
-    ref = np.full((nrt, nvt), -np.inf)
-    for rt in range(-(-valid.size // TILE)):
-        blk = Z[rt * TILE:(rt + 1) * TILE]
-        for vt in range(nvt):
-            ref[rt, vt] = blk[:, vt * TILE:(vt + 1) * TILE].max()
+    nrb, ncb = 2 * -(-x.N // 256), 2 * -(-x.V // 256)
+    ref = np.full((nrb, ncb), -np.inf)
+    for rb in range(-(-valid.size // BLK)):
+        rows = Z[rb * BLK:(rb + 1) * BLK]
+        for cb in range(-(-x.V // BLK)):
+            ref[rb, cb] = rows[:, cb * BLK:(cb + 1) * BLK].max()
     return ref
 
 
 @pytest.mark.parametrize("k,N,D,V", CASES, ids=[f"w{c[0]}" for c in CASES])
-def test_table_is_tile_max(k, N, D, V):
+def test_table_is_block_max(k, N, D, V):
     x = inputs.make_workload(k, N=N, D=D, V=V)
-    G.say(f"tile bound table w{k} N={x.N} D={x.D} V={x.V}")
+    G.say(f"block-max table w{k} N={x.N} D={x.D} V={x.V}")
     out = G.run_gpu(x, G.mean_dloss(x), eps=x.eps or 2.0 ** -12)
-    ref = _ref_tile_max(x)
-    got = out["tile_bound"].reshape(ref.shape)
+    ref = _ref_block_max(x)
+    got = out["block_max"].reshape(ref.shape)
     fin = np.isfinite(ref)
-    assert np.all(got[~fin] == -np.inf), "tiles past the valid rows must stay -inf"
+    assert np.all(got[~fin] == -np.inf), "blocks past the valid rows or vocabulary must stay -inf"
     err = np.abs(got[fin] - ref[fin]) / np.maximum(np.abs(ref[fin]), 1.0)
     tol = 1e-5 if x.dtype == "f32" else 1e-3
     assert err.max() <= tol, err.max()
@@ -89,9 +90,9 @@ def test_table_unused_with_sort_or_without_filter():
 
 def _device_run(x, tb, eps, dl):
     H, E, y = G.to_device(x)
-    _, lse = B.cce_forward(H, E, y, x.ignore_index, tile_bound=tb)
+    _, lse = B.cce_forward(H, E, y, x.ignore_index, block_max=tb)
     stats = torch.zeros(5, dtype=torch.int64, device=G.DEV)
-    dH, dE = B.cce_backward(H, E, y, lse, dl, eps, x.ignore_index, None, 0, stats=stats, tile_bound=tb)
+    dH, dE = B.cce_backward(H, E, y, lse, dl, eps, x.ignore_index, None, 0, stats=stats, block_max=tb)
     torch.cuda.synchronize()
     return dH, dE, stats.cpu().numpy()
 
@@ -103,7 +104,7 @@ def test_full_size_skip_is_bit_identical(k):
     x = inputs.make_workload(k)
     G.say(f"bound skip full size w{k} N={x.N} D={x.D} V={x.V}")
     dl = torch.from_numpy(G.mean_dloss(x)).to(G.DEV)
-    tb = torch.empty(B.tile_bound_elems(x.N, x.V), dtype=torch.float32, device=G.DEV)
+    tb = torch.empty(B.block_max_elems(x.N, x.V), dtype=torch.float32, device=G.DEV)
     dH_a, dE_a, st_a = _device_run(x, tb, x.eps, dl)
     dH_b, dE_b, st_b = _device_run(x, None, x.eps, dl)
     assert torch.equal(dH_a, dH_b) and torch.equal(dE_a, dE_b)

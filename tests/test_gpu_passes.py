@@ -1,0 +1,44 @@
+"""The backward's pass structure: the listed tiles are cut into passes whose
+kept blocks fit the block store.  With the block-max table fewer tiles are
+listed, so the same problem is cut into fewer passes; dH carries its fp32
+running sum across passes block by block, so the outputs must not depend on
+the cut (bit-identical with and without the table), and a problem cut into
+several passes must still match the fp64 oracle."""
+import numpy as np
+import pytest
+
+from linear_cross_entropy_cce_amd import inputs
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    (2, 700, 256, 9000, 2.0 ** -12),     # peaked: two passes without the table, one with it
+    (3, 600, 512, 20000, 2.0 ** -12),    # flat, 40 % ignored: several passes either way
+    (4, 300, 72, 20000, 2.0 ** -6),      # D * 2 not a multiple of 128: VGPR-staged recompute
+]
+
+
+@pytest.mark.parametrize("k,N,D,V,eps", CASES, ids=[f"w{c[0]}-{c[2]}-{c[3]}" for c in CASES])
+def test_pass_cut_does_not_change_results(k, N, D, V, eps):
+    x = inputs.make_workload(k, N=N, D=D, V=V)
+    G.say(f"pass cut w{k} N={x.N} D={x.D} V={x.V} eps={eps}")
+    dl = G.random_dloss(x, seed=3)
+    a = G.run_gpu(x, dl, eps=eps, bound=True)
+    b = G.run_gpu(x, dl, eps=eps, bound=False)
+    for key in ("dH", "dE"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.array_equal(a["stats"][:4], b["stats"][:4])
+
+
+def test_multi_pass_matches_oracle():
+    """A flat case with every block kept, cut into several passes."""
+    x = inputs.make_workload(3, N=600, D=512, V=20000)
+    G.say(f"multi-pass parity N={x.N} D={x.D} V={x.V}")
+    dl = G.mean_dloss(x)
+    out = G.run_gpu(x, dl, eps=0.0)
+    _, _, dH, dE = G.oracle_full(x, dl, "mean")
+    LH, LE = G.label_term(x, dl)
+    G.assert_grad("dH", out["dH"], dH, LH, 1e-2)
+    G.assert_grad("dE", out["dE"], dE, LE, 1e-2)
+    assert out["stats"][0] == out["stats"][2]
