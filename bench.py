@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_fwd_dma_gemma2_2b_head_traffic.md")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (published)
 METRIC = "fwd+bwd tokens/sec of fused linear-CE at Gemma-2-2B shape; % MFMA peak"
@@ -41,6 +42,8 @@ def parse():
     ap.add_argument("--sort", action="store_true", help="vocabulary sort before the backward")
     ap.add_argument("--no-bound", action="store_true", help="backward without the forward's block-max table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="after the timed steps, copy this many bytes device-to-device (counter calibration)")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = about 20 s of work)")
     return ap.parse_args()
 
@@ -158,6 +161,11 @@ def main():
     peak = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_FP32_TFLOPS
     fwd_avg = float(np.mean(fwd_ms))
     achieved = f_logits / (fwd_avg * 1e-3) / 1e12
+    # HBM bytes per k_fwd_dma launch from the committed counter passes, while the
+    # kernel's sources are the ones they were taken on (this workload only)
+    from linear_cross_entropy_cce_amd import profiling as TR
+    rec = TR.load(TRAFFIC_PROFILE) if a.workload == 2 else None
+    traffic = rec[0] if rec and rec[1] == TR.sources_hash() else None
     out = {
         "metric": METRIC,
         "value": N / (step_ms * 1e-3),
@@ -175,7 +183,7 @@ def main():
                    "N": N, "D": D, "V": V, "n_valid": nv, "filter_eps": eps, "sort_vocab": a.sort,
                    "filter_block": [br, bv]},
         "roofline": {"kernel": "k_fwd (cce_forward bracket)", "bound": "mfma", "achieved": achieved,
-                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None},
+                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
         "detail": {
             "fwd_ms_mean": fwd_avg, "bwd_ms_mean": float(np.mean(bwd_ms)),
             "fwd_ms_min": float(np.min(fwd_ms)), "bwd_ms_min": float(np.min(bwd_ms)),
@@ -191,6 +199,13 @@ def main():
             "valid_tokens_per_s": nv / (step_ms * 1e-3),
         },
     }
+    if a.copy_probe:
+        src = torch.empty(a.copy_probe // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not a.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(x, a.cpu_rows)

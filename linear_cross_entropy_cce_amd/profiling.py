@@ -1,0 +1,171 @@
+"""Summaries of rocprofv3 output for profiles/.
+
+Kernel statistics (`--kernel-trace --stats`, csv):
+
+    python -m linear_cross_entropy_cce_amd.profiling stats --dir DIR --steps K \\
+        --command "..." --out profiles/<kernel>_<workload>.md
+
+HBM traffic of the forward logit kernel: two counter passes of the same
+command (`bench.py --copy-probe BYTES`), one with `--pmc FETCH_SIZE` and one
+with `--pmc WRITE_SIZE`, give KiB per dispatch.  The command also runs a plain
+device-to-device copy of BYTES bytes (torch's copy kernel); what the counters
+read for it against the bytes it moves is the calibration factor applied to
+the logit kernel's reading.
+
+    python -m linear_cross_entropy_cce_amd.profiling traffic --fetch DIR --write DIR \\
+        --copy-bytes BYTES --out profiles/<kernel>_<workload>_traffic.md
+
+The traffic summary records a hash of the kernel's sources; `bench.py`
+reports the traffic only while the sources still hash the same.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL = "k_fwd_dma"
+SOURCES = ("csrc/fwd.hip", "csrc/cce_device.hpp", "csrc/cce_internal.hpp")
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for rel in SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _per_dispatch(directory: str, counter: str, match) -> list[float]:
+    paths = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise FileNotFoundError(f"no counter_collection.csv under {directory}")
+    vals = {}
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter or not match(r["Kernel_Name"]):
+                    continue
+                key = (path, r["Dispatch_Id"])
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def summarize(fetch_dir: str, write_dir: str, copy_bytes: int) -> dict:
+    is_kernel = lambda n: KERNEL in n  # noqa: E731
+    is_copy = lambda n: "copy" in n.lower() and "cce" not in n  # noqa: E731
+    out = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        k = _per_dispatch(d, name, is_kernel)
+        c = [v for v in _per_dispatch(d, name, is_copy) if v > 0]
+        if not k or not c:
+            raise RuntimeError(f"{name}: kernel dispatches {len(k)}, copy dispatches {len(c)}")
+        kib_k = sum(k) / len(k)
+        kib_c = max(c)  # the copy of copy_bytes is the largest copy dispatch
+        factor = copy_bytes / (kib_c * 1024.0)
+        out[name] = {"kernel_kib": kib_k, "copy_kib": kib_c, "factor": factor, "bytes": kib_k * 1024.0 * factor}
+    out["traffic_bytes"] = out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]
+    return out
+
+
+def write_md(path: str, s: dict, copy_bytes: int, command: str) -> None:
+    lines = [
+        f"# HBM traffic of `{KERNEL}`: Gemma-2-2B head (N=8192, D=2304, V=256000, bf16)",
+        "",
+        "Commands (on the MI355X box, from the repository root; one counter per pass):",
+        "",
+        f"    {command.replace('COUNTER', 'FETCH_SIZE')}",
+        f"    {command.replace('COUNTER', 'WRITE_SIZE')}",
+        "",
+        "Summarised with:",
+        "",
+        f"    python -m linear_cross_entropy_cce_amd.profiling traffic --fetch gpurun_out/pmc_FETCH_SIZE "
+        f"--write gpurun_out/pmc_WRITE_SIZE --copy-bytes {copy_bytes} --out {os.path.relpath(path, os.path.dirname(PKG))}",
+        "",
+        f"Calibration: torch's device copy of {copy_bytes} bytes in the same run (reads and writes that many bytes).",
+        "FETCH_SIZE and WRITE_SIZE count the L2's requests to the memory fabric, so reads served by the",
+        "Infinity Cache (MALL) in front of HBM are included.",
+        "",
+        "| counter | kernel KiB / dispatch | copy KiB | factor (bytes / counted byte) | kernel bytes / launch |",
+        "|---|---|---|---|---|",
+    ]
+    for name in ("FETCH_SIZE", "WRITE_SIZE"):
+        v = s[name]
+        lines.append(f"| {name} | {v['kernel_kib']:.1f} | {v['copy_kib']:.1f} | {v['factor']:.4f} | {v['bytes']:.4g} |")
+    lines += [
+        "",
+        f"traffic_bytes_per_launch: {s['traffic_bytes']:.6g}",
+        f"sources_sha256_16: {sources_hash()}",
+        "",
+    ]
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+
+
+def load(path: str):
+    """(bytes per launch, sources hash) from a summary written by write_md, or None."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^traffic_bytes_per_launch: (\S+)$", text, re.M)
+    h = re.search(r"^sources_sha256_16: (\S+)$", text, re.M)
+    if not m or not h:
+        return None
+    return float(m.group(1)), h.group(1)
+
+
+def write_stats_md(path: str, directory: str, steps: int, command: str, title: str) -> None:
+    paths = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        raise FileNotFoundError(f"no kernel_trace.csv under {directory}")
+    per = {}
+    for p in paths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+                per.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    rows = sorted(per.items(), key=lambda kv: -sum(kv[1]))
+    total = sum(sum(v) for _, v in rows)
+    lines = [f"# {title}", "", "Command (on the MI355X box, from the repository root):", "", f"    {command}", "",
+             f"{steps} profiled steps; durations from the kernel trace, microseconds.", "",
+             "| kernel | calls | avg us | min us | max us | ms / step | % |", "|---|---|---|---|---|---|---|"]
+    for name, v in rows:
+        lines.append(f"| `{name}` | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} | "
+                     f"{sum(v) / 1e3 / steps:.3f} | {100 * sum(v) / total:.1f} |")
+    lines.append("")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--command", default="rocprofv3 --pmc COUNTER --output-format csv -d gpurun_out/pmc_COUNTER -o p "
+                                         "-- python -u bench.py --steps 1 --warmup 1 --no-cpu-baseline "
+                                         "--copy-probe 1073741824")
+    k = sub.add_parser("stats")
+    k.add_argument("--dir", required=True)
+    k.add_argument("--steps", type=int, required=True)
+    k.add_argument("--command", required=True)
+    k.add_argument("--title", required=True)
+    k.add_argument("--out", required=True)
+    a = ap.parse_args()
+    if a.what == "traffic":
+        s = summarize(a.fetch, a.write, a.copy_bytes)
+        write_md(a.out, s, a.copy_bytes, a.command)
+    else:
+        write_stats_md(a.out, a.dir, a.steps, a.command, a.title)
+    print(open(a.out).read())
+
+
+if __name__ == "__main__":
+    main()
