@@ -84,8 +84,8 @@ def cpu_baseline(x, n_rows_hint):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 "
+                                   "(token or vocabulary sharding across GPUs is not implemented)"}))
         sys.exit(2)
     import numpy as np
     import torch
@@ -153,7 +153,7 @@ def main():
     st = stats.cpu().numpy()
     n_live, n_label, n_total, n_recomp = int(st[0]), int(st[1]), int(st[2]), int(st[4])
     br, bv = B.filter_block()
-    # algorithmic work: logits twice, dH and dE on kept blocks
+    # algorithmic work: forward logits, recomputed blocks' logits, dH and dE on kept blocks
     f_logits = 2.0 * nv * D * V
     kept_cols = (n_live + n_label) * br * bv  # upper bound on kept (row, vocab) pairs
     # executed: the forward logits, the recomputed blocks' logits, dH and dE on kept blocks
