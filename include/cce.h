@@ -66,6 +66,8 @@ typedef enum { CCE_F32 = 0, CCE_BF16 = 1 } cce_dtype;
 
 /* cce_backward flags. */
 #define CCE_BWD_NO_KAHAN 1u /* plain fp32 accumulation of dE across blocks (numerics studies) */
+#define CCE_BWD_FULL_DE 2u  /* dE from every block (unfiltered, Kahan-compensated), dH filtered:
+                               the "full classifier gradient" variant; every tile is recomputed */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *cce_status_string(cce_status s);
@@ -143,7 +145,7 @@ cce_status cce_vocab_order(const void *H, const void *E, const int64_t *labels,
  *    softmax part is filtered: the -dloss_i at (i, y_i) is always applied.
  *  - perm: NULL, or the permutation from cce_vocab_order (int32 [V]); it only
  *    changes which vocabulary entries share a filter block.
- *  - flags: 0 or CCE_BWD_NO_KAHAN.
+ *  - flags: 0 or any of CCE_BWD_NO_KAHAN, CCE_BWD_FULL_DE.
  *  - stats: NULL, or device int64 [5] that receives (softmax-surviving blocks,
  *    label-only blocks, total blocks, valid rows, recomputed blocks).
  * Ignored rows get dH = 0 and add nothing to dE.

@@ -26,6 +26,7 @@ CCE_F32 = 0
 CCE_BF16 = 1
 
 CCE_BWD_NO_KAHAN = 1
+CCE_BWD_FULL_DE = 2
 
 # Every entry point include/cce.h declares.
 EXPORTS = (

@@ -122,7 +122,7 @@ cce_status cce_backward(const void *H, const void *E, const int64_t *labels, con
     if (!dtype_ok(dtype)) return CCE_ERR_DTYPE;
     if (!shape_ok(N, D, V)) return CCE_ERR_SHAPE;
     if (!(filter_eps >= 0.f) || isinf(filter_eps)) return CCE_ERR_ARG;  // rejects NaN and negatives
-    if (flags & ~CCE_BWD_NO_KAHAN) return CCE_ERR_ARG;
+    if (flags & ~(CCE_BWD_NO_KAHAN | CCE_BWD_FULL_DE)) return CCE_ERR_ARG;
     if (!aligned(H, 16) || !aligned(E, 16) || !aligned(dH, 16) || !aligned(dE, 16) || !aligned(ws, 16) ||
         !aligned(labels, 8) || !aligned(lse, 4) || !aligned(dloss, 4) || !aligned(perm, 4) || !aligned(stats, 8) ||
         !aligned(block_max, 4))

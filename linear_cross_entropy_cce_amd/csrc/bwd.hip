@@ -94,6 +94,7 @@ struct BwdArgs {
     const float *lse, *dloss;
     int D, V, cbp, n_rb;
     float eps;
+    int full_de;  // dE from every block (status 3 = kept for dE only), dH filtered
     T *Gt, *Gn;
     int64_t cap;
     uint8_t *st;
@@ -371,9 +372,12 @@ __global__ __launch_bounds__(1024) void k_plan(const uint8_t *__restrict__ tneed
 // Epilogue of a listed tile.  SOFTMAX: acc holds the recomputed logits and
 // p = exp(z - lse) decides each 128 x 128 block's status (1 = some p >= eps,
 // 2 = none but a label in it, 0 = dropped); otherwise (a tile left out by
-// the bound; acc is not read) only labels decide.  Kept blocks take a store slot and their
-// gradient g = dloss (p [status 1] - [v == y]) is written in both layouts:
-// Gt[slot][v][row] and Gn[slot][row][v].
+// the bound; acc is not read) only labels decide.  Kept blocks take a store
+// slot and their gradient g = dloss (p [status 1] - [v == y]) is written in
+// both layouts: Gt[slot][v][row] (read by dE) and Gn[slot][row][v] (read by
+// dH).  With full_de every real block is kept for dE: Gt holds the
+// unfiltered dloss (p - [v == y]) and a block the filter drops gets status 3
+// (dE only; no Gn copy).
 template <typename T, class TL, bool SOFTMAX>
 __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int tok0, int nv, int p0,
                                            int V, int rt, int vt, int cbp, float eps,
@@ -382,7 +386,7 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
                                            const float *__restrict__ dloss, T *__restrict__ Gt, T *__restrict__ Gn,
                                            int64_t cap, int32_t *__restrict__ counter, uint8_t *__restrict__ st,
                                            int32_t *__restrict__ slotm, int64_t *__restrict__ stats, int *qflag,
-                                           int *qstat, int *qslot) {
+                                           int *qstat, int *qslot, int full_de) {
     const int tid = opaque_tid();  // fresh per tile: see tile_row
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave % TL::WM, wn = wave / TL::WM;
@@ -432,6 +436,8 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
         const int f = qflag[tid];
         int sv = (f & 1) ? 1 : ((f & 2) ? 2 : 0);
         const int rb = 2 * rt + (tid & 1), cb = 2 * vt + (tid >> 1);
+        // full dE: a real block the filter drops is still kept for dE
+        if (full_de && sv == 0 && rb * kBlockRows < nv && (int64_t)cb * kBlockVocab < V) sv = 3;
         int s = -1;
         if (sv) {
             s = atomicAdd(counter, 1);
@@ -442,7 +448,7 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
         st[(int64_t)rb * cbp + cb] = (uint8_t)sv;
         if (sv) slotm[(int64_t)rb * cbp + cb] = s;
         if (stats) {
-            if (sv) atomicAdd(reinterpret_cast<unsigned long long *>(stats + (sv == 1 ? 0 : 1)), 1ull);
+            if (sv == 1 || sv == 2) atomicAdd(reinterpret_cast<unsigned long long *>(stats + (sv == 1 ? 0 : 1)), 1ull);
             // blocks whose logits were recomputed (real rows and vocabulary entries only)
             if (SOFTMAX && rb * kBlockRows < nv && (int64_t)cb * kBlockVocab < V)
                 atomicAdd(reinterpret_cast<unsigned long long *>(stats + 4), 1ull);
@@ -467,15 +473,20 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
                     const int r = r4 * 4 + q;
                     const int rl = tile_row<TL>(tm, r, tid);
                     const bool ok = tok_ok[tn] && (acc_row_const(tm, r) < vlim);
+                    const float onehot = rl == lab_t[tn] ? 1.f : 0.f;
                     const float pk = (SOFTMAX && status == 1) ? acc[tm][tn][r] : 0.f;
-                    const float g = ok ? dl_t[tn] * (pk - (rl == lab_t[tn] ? 1.f : 0.f)) : 0.f;
+                    const float g = ok ? dl_t[tn] * (pk - onehot) : 0.f;
                     g4[q] = from_f32<T>(g);
-                    gt[(rl - wm * kBlockVocab) * kBlockRows + tl] = g4[q];
+                    // full dE: the vocabulary-major copy (read by dE) holds the unfiltered gradient
+                    const float gf = (SOFTMAX && full_de && ok) ? dl_t[tn] * (acc[tm][tn][r] - onehot) : g;
+                    gt[(rl - wm * kBlockVocab) * kBlockRows + tl] = from_f32<T>(gf);
                 }
-                // rows r4*4 .. r4*4+3 are consecutive vocabulary entries
-                T *dst = gn + tl * kBlockVocab + tile_row<TL>(tm, r4 * 4, tid) - wm * kBlockVocab;
+                // rows r4*4 .. r4*4+3 are consecutive vocabulary entries (dH reads these; not for status 3)
+                if (status != 3) {
+                    T *dst = gn + tl * kBlockVocab + tile_row<TL>(tm, r4 * 4, tid) - wm * kBlockVocab;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) dst[q] = g4[q];
+                    for (int q = 0; q < 4; ++q) dst[q] = g4[q];
+                }
             }
     }
 }
@@ -500,13 +511,13 @@ __device__ __forceinline__ void recompute_dma(const T *__restrict__ H, const T *
         const int pos = min(p0 + r, V - 1);
         int vid = perm ? perm[pos] : pos;
         vid = (vid >= 0 && vid < V) ? vid : 0;
-        eng.pa[j] = reinterpret_cast<const char *>(E) + (size_t)vid * rowb + DE::chunk_off(r, tid);
+        eng.pa[j] = reinterpret_cast<const char *>(E) + (size_t)vid * rowb + DE::chunk_off(j, r, tid);
     }
 #pragma unroll
     for (int j = 0; j < DE::NIB; ++j) {
         const int r = DE::row_b(j, tid);
         const int tok = min(tok0 + r, nv - 1);
-        eng.pb[j] = reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb + DE::chunk_off(r, tid);
+        eng.pb[j] = reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb + DE::chunk_off(j, r, tid);
     }
 #pragma unroll
     for (int q = 0; q < DE::kDepth; ++q)
@@ -595,11 +606,11 @@ __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int
                 __syncthreads();
                 g_epilogue<T, TL, true>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
                                         a.lse, a.dloss, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
-                                        qflag, qstat, qslot);
+                                        qflag, qstat, qslot, a.full_de);
             } else {
                 g_epilogue<T, TL, false>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
                                          a.lse, a.dloss, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
-                                         qflag, qstat, qslot);
+                                         qflag, qstat, qslot, a.full_de);
             }
         }
     }
@@ -765,13 +776,13 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
 #pragma unroll
     for (int j = 0; j < DE::NIA; ++j) {
         const int r = DE::row_a(j, tid);
-        eng.pa[j] = reinterpret_cast<const char *>(Gt + (int64_t)r * kBlockRows) + DE::chunk_off(r, tid);
+        eng.pa[j] = reinterpret_cast<const char *>(Gt + (int64_t)r * kBlockRows) + DE::chunk_off(j, r, tid);
     }
 #pragma unroll
     for (int j = 0; j < DE::NIB; ++j) {
         const int r = DE::row_b(j, tid);
         const int d = min(d0 + r, D - 1);
-        eng.pb[j] = reinterpret_cast<const char *>(Ht + (int64_t)d * ldh) + DE::chunk_off(r, tid);
+        eng.pb[j] = reinterpret_cast<const char *>(Ht + (int64_t)d * ldh) + DE::chunk_off(j, r, tid);
     }
     f32x16 acc[TL::TM][TL::TN], sum[TL::TM][TL::TN], comp[TL::TM][TL::TN];
     zero_acc<TL>(acc);
@@ -918,7 +929,8 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
     for (int base = cb0; base < cb1; base += kListCap) {
         const int cnt = cb1 - base < kListCap ? cb1 - base : kListCap;
         const int n = build_list<TL::kThreads>(
-            cnt, [&](int i) { return st[(int64_t)rb * cbp + base + i] != 0; }, sh.list, sh.wcnt);
+            cnt, [&](int i) { const int v = st[(int64_t)rb * cbp + base + i]; return v == 1 || v == 2; }, sh.list,
+            sh.wcnt);
         for (int i = threadIdx.x; i < n; i += TL::kThreads) sh.lslot[i] = slotm[(int64_t)rb * cbp + base + sh.list[i]];
         __syncthreads();
         any |= n > 0;
@@ -1137,7 +1149,8 @@ static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, cons
 
     // The block maxima are in the natural vocabulary order and only say
     // something when filtering is on.  thr = ln(eps / 2), rounded towards -inf.
-    const float *tb = (block_max && !perm && eps > 0.f) ? block_max : nullptr;
+    const bool full_de = (flags & CCE_BWD_FULL_DE) != 0;
+    const float *tb = (block_max && !perm && eps > 0.f && !full_de) ? block_max : nullptr;
     float thr = 0.f;
     if (tb) {
         thr = (float)(log((double)eps) - log(2.0));
@@ -1179,6 +1192,7 @@ static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, cons
     a.cbp = s.cbp;
     a.n_rb = s.n_rb;
     a.eps = eps;
+    a.full_de = full_de ? 1 : 0;
     a.Gt = Gt;
     a.Gn = Gn;
     a.cap = s.cap;

@@ -218,6 +218,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 template <int kRowBytes>
 __device__ __forceinline__ int dma_swz(int r) {
     if constexpr (kRowBytes == 64) return ((r >> 1) ^ (r >> 2)) & 3;
+    else if constexpr (kRowBytes == 96) return 0;  // 6 chunks: 8 consecutive rows already hit distinct banks
     else return (r & 7) ^ ((r >> 3) & 1);
 }
 template <int kRowBytes>
@@ -266,7 +267,7 @@ struct DmaEngine {
     static constexpr int NIA = kStageA / 64 / TL::kWaves;  // DMA instructions per wave per stage
     static constexpr int NIB = kStageB / 64 / TL::kWaves;
     static constexpr int NI = NIA + NIB;
-    static_assert(kRowBytes_ == 64 || kRowBytes_ == 128, "64- or 128-byte stage rows");
+    static_assert(kRowBytes_ == 64 || kRowBytes_ == 96 || kRowBytes_ == 128, "64-, 96- or 128-byte stage rows");
     static_assert(kStages >= 2 && kStages <= 4, "2 to 4 stages");
     static_assert(NIA * 64 * TL::kWaves == kStageA && NIB * 64 * TL::kWaves == kStageB,
                   "tile rows must split into whole wave-instructions");
@@ -278,13 +279,14 @@ struct DmaEngine {
 
     __device__ __forceinline__ explicit DmaEngine(u32x4 *l) : lds(l), lds0(lds_addr(l)) {}
 
-    // Tile row fed by this lane in instruction j, and its chunk byte offset.
-    static __device__ __forceinline__ int row_a(int j, int tid = threadIdx.x) {
-        return (64 * (j * TL::kWaves + (tid >> 6)) + (tid & 63)) / kCpr;
-    }
+    // Tile row fed by this lane in instruction j, and the byte offset of its
+    // chunk: lane i of instruction j fills stage slot 64 (j waves + wave) + i,
+    // which is row slot / kCpr, position slot % kCpr.
+    static __device__ __forceinline__ int slot_of(int j, int tid) { return 64 * (j * TL::kWaves + (tid >> 6)) + (tid & 63); }
+    static __device__ __forceinline__ int row_a(int j, int tid = threadIdx.x) { return slot_of(j, tid) / kCpr; }
     static __device__ __forceinline__ int row_b(int j, int tid = threadIdx.x) { return row_a(j, tid); }
-    static __device__ __forceinline__ int chunk_off(int r, int tid = threadIdx.x) {
-        return 16 * ((tid & (kCpr - 1)) ^ dma_swz<kRowBytes_>(r));
+    static __device__ __forceinline__ int chunk_off(int j, int r, int tid) {
+        return 16 * ((slot_of(j, tid) % kCpr) ^ dma_swz<kRowBytes_>(r));
     }
 
     __device__ __forceinline__ void issue(int buf, int kb) const { issue2(buf, kb, kb); }

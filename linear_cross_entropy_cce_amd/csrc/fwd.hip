@@ -334,14 +334,14 @@ __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
     for (int j = 0; j < DE::NIB; ++j) {
         const int r = DE::row_b(j);
         const int tok = min(tok0 + r, nv - 1);
-        eng.pb[j] = reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb + DE::chunk_off(r);
+        eng.pb[j] = reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb + DE::chunk_off(j, r, threadIdx.x);
     }
     auto set_tile = [&](int vt) {
 #pragma unroll
         for (int j = 0; j < DE::NIA; ++j) {
             const int r = DE::row_a(j);
             const int v = min(vt * TL::BM + r, V - 1);
-            eng.pa[j] = reinterpret_cast<const char *>(E) + (size_t)v * rowb + DE::chunk_off(r);
+            eng.pa[j] = reinterpret_cast<const char *>(E) + (size_t)v * rowb + DE::chunk_off(j, r, threadIdx.x);
         }
     };
 

@@ -1,0 +1,37 @@
+"""The full-classifier-gradient variant (CCE_BWD_FULL_DE): dE from every
+block, unfiltered and Kahan-compensated, while dH stays filtered.  Its dE must
+equal, bit for bit, the dE of an unfiltered run (every block kept, same
+values, same order), and its dH the dH of the ordinary filtered run; both are
+also held to the fp64 oracle."""
+import numpy as np
+import pytest
+
+from linear_cross_entropy_cce_amd import binding as B
+from linear_cross_entropy_cce_amd import inputs
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    (2, 700, 256, 9000, 2.0 ** -12),   # peaked: almost every block dropped by the filter
+    (3, 600, 512, 5000, 2.0 ** -12),   # flat, 40 % ignored: some blocks dropped
+    (1, None, None, None, 2.0 ** -10), # fp32
+]
+
+
+@pytest.mark.parametrize("k,N,D,V,eps", CASES, ids=[f"w{c[0]}" for c in CASES])
+def test_full_de(k, N, D, V, eps):
+    x = inputs.make_workload(k, N=N, D=D, V=V)
+    G.say(f"full dE w{k} N={x.N} D={x.D} V={x.V} eps={eps}")
+    dl = G.random_dloss(x, seed=5)
+    full = G.run_gpu(x, dl, eps=eps, flags=B.CCE_BWD_FULL_DE)
+    filt = G.run_gpu(x, dl, eps=eps)
+    dense = G.run_gpu(x, dl, eps=0.0)
+    assert np.array_equal(full["dE"], dense["dE"]), "dE must be the unfiltered dE"
+    assert np.array_equal(full["dH"], filt["dH"]), "dH must be the filtered dH"
+    assert np.array_equal(full["stats"][:4], filt["stats"][:4])
+    # against the oracle: dE unfiltered (tight), dH filtered (filter tolerance)
+    _, _, dH, dE = G.oracle_full(x, dl, "full_de")
+    LH, LE = G.label_term(x, dl)
+    G.assert_grad("dE", full["dE"], dE, LE, 1e-5 if x.dtype == "f32" else 1e-2)
+    G.assert_grad("dH", full["dH"], dH, LH, 2e-2)
