@@ -256,10 +256,11 @@ __global__ __launch_bounds__(256) void k_label_map(const int64_t *__restrict__ l
 }
 
 // Per tile (vocabulary-tile-major index vt * n_rt + rt): the number of its
-// blocks that may be kept (bits 0-2) and whether its logits are recomputed
-// (bit 7).  A block may keep its softmax part unless the bound rules it out,
-// and may keep its label entries if it holds a label; the tile's logits are
-// recomputed when any of its real blocks may keep a softmax part.
+// blocks that may be kept (bits 0-2), which of its blocks may keep a
+// softmax part (bits 3-6, block q = 2 (vocabulary half) + token half) and
+// whether any does (bit 7).  A block may keep its softmax part unless the
+// bound rules it out, and may keep its label entries if it holds a label;
+// only the blocks that may keep a softmax part are recomputed.
 __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ nvalid_p, int64_t V, int n_rt,
                                                     int n_vt, int cbp, const uint8_t *__restrict__ lab,
                                                     const float *__restrict__ bmax, const float *__restrict__ lmin,
@@ -272,17 +273,16 @@ __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ 
         tneed[i] = 0;
         return;
     }
-    bool rec = false;
-    int need = 0;
+    int mask = 0, need = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int rb = 2 * rt + (q & 1), cb = 2 * vt + (q >> 1);
         if ((int64_t)rb * kBlockRows >= nv || (int64_t)cb * kBlockVocab >= V) continue;
         const bool soft = !block_below(bmax, cbp, lmin, thr, rb, cb);
-        rec |= soft;
+        mask |= soft ? 1 << q : 0;
         need += (soft || lab[(int64_t)rb * cbp + cb]) ? 1 : 0;
     }
-    tneed[i] = (uint8_t)(need | (rec ? 0x80 : 0));
+    tneed[i] = (uint8_t)(need | (mask << 3) | (mask ? 0x80 : 0));
 }
 
 // One workgroup: per vocabulary tile the blocks it may keep and its listed
@@ -386,7 +386,7 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
                                            const float *__restrict__ dloss, T *__restrict__ Gt, T *__restrict__ Gn,
                                            int64_t cap, int32_t *__restrict__ counter, uint8_t *__restrict__ st,
                                            int32_t *__restrict__ slotm, int64_t *__restrict__ stats, int *qflag,
-                                           int *qstat, int *qslot, int full_de) {
+                                           int *qstat, int *qslot, int full_de, int qmask) {
     const int tid = opaque_tid();  // fresh per tile: see tile_row
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave % TL::WM, wn = wave / TL::WM;
@@ -416,7 +416,8 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
         }
     }
     const int vlim = row_limit<TL>(V - p0, tid);  // entry (tm, r) is a real vocabulary row iff acc_row_const < vlim
-    if constexpr (SOFTMAX) {
+    const bool wsoft = SOFTMAX && ((qmask >> quad) & 1);  // this wave's block was recomputed (wave-uniform)
+    if (wsoft) {
 #pragma unroll
         for (int tn = 0; tn < TL::TN; ++tn)
 #pragma unroll
@@ -450,7 +451,7 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
         if (stats) {
             if (sv == 1 || sv == 2) atomicAdd(reinterpret_cast<unsigned long long *>(stats + (sv == 1 ? 0 : 1)), 1ull);
             // blocks whose logits were recomputed (real rows and vocabulary entries only)
-            if (SOFTMAX && rb * kBlockRows < nv && (int64_t)cb * kBlockVocab < V)
+            if (SOFTMAX && ((qmask >> tid) & 1))
                 atomicAdd(reinterpret_cast<unsigned long long *>(stats + 4), 1ull);
         }
     }
@@ -474,11 +475,11 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
                     const int rl = tile_row<TL>(tm, r, tid);
                     const bool ok = tok_ok[tn] && (acc_row_const(tm, r) < vlim);
                     const float onehot = rl == lab_t[tn] ? 1.f : 0.f;
-                    const float pk = (SOFTMAX && status == 1) ? acc[tm][tn][r] : 0.f;
+                    const float pk = (wsoft && status == 1) ? acc[tm][tn][r] : 0.f;
                     const float g = ok ? dl_t[tn] * (pk - onehot) : 0.f;
                     g4[q] = from_f32<T>(g);
                     // full dE: the vocabulary-major copy (read by dE) holds the unfiltered gradient
-                    const float gf = (SOFTMAX && full_de && ok) ? dl_t[tn] * (acc[tm][tn][r] - onehot) : g;
+                    const float gf = (wsoft && full_de && ok) ? dl_t[tn] * (acc[tm][tn][r] - onehot) : g;
                     gt[(rl - wm * kBlockVocab) * kBlockRows + tl] = from_f32<T>(gf);
                 }
                 // rows r4*4 .. r4*4+3 are consecutive vocabulary entries (dH reads these; not for status 3)
@@ -495,11 +496,14 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
 // D * sizeof(T) % kLogitRowBytes == 0): the forward's engine, tile shape and
 // K order.  Rows past the end of an operand are clamped to a valid row: their
 // logits are finite and the epilogue masks them.
+// Only the blocks in qmask (bit 2 (vocabulary half) + token half) are
+// computed: the halves of A and B no such block uses are not loaded and the
+// waves of the other blocks skip their MFMAs.
 template <typename T, class TL>
 __device__ __forceinline__ void recompute_dma(const T *__restrict__ H, const T *__restrict__ E,
                                               const int32_t *__restrict__ idx, int nv,
                                               const int32_t *__restrict__ perm, int D, int V, int tok0, int p0,
-                                              u32x4 *lds, f32x16 (&acc)[TL::TM][TL::TN]) {
+                                              int qmask, u32x4 *lds, f32x16 (&acc)[TL::TM][TL::TN]) {
     using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
     const size_t rowb = (size_t)D * sizeof(T);
     const int ns = D * (int)sizeof(T) / DE::kStageBytes;
@@ -519,14 +523,21 @@ __device__ __forceinline__ void recompute_dma(const T *__restrict__ H, const T *
         const int tok = min(tok0 + r, nv - 1);
         eng.pb[j] = reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb + DE::chunk_off(j, r, tid);
     }
+    static_assert(TL::kWaveM == TL::BM / 2 && TL::BN / TL::WN * 2 <= TL::BN, "a wave lies in one block");
+    const int halves = ((qmask & 3) ? 1 : 0) | ((qmask & 12) ? 2 : 0)    // vocabulary halves
+                       | ((qmask & 5) ? 4 : 0) | ((qmask & 10) ? 8 : 0);  // token halves
+    const int wave = tid >> 6;
+    const int quad = (wave % TL::WM) * 2 + (wave / TL::WM) * TL::kWaveN / (TL::BN / 2);
+    const bool active = (qmask >> quad) & 1;  // wave-uniform
 #pragma unroll
     for (int q = 0; q < DE::kDepth; ++q)
-        if (q < ns) eng.issue(q, q * DE::kStageBytes);
+        if (q < ns) eng.issue_halves(q, q * DE::kStageBytes, halves);
     for (int s = 0; s < ns; ++s) {
         const int ahead = ns - 1 - s;
         eng.wait_stage(eng.clamp_ahead(ahead));
-        if (s + DE::kDepth < ns) eng.issue((s + DE::kDepth) % DE::kStages, (s + DE::kDepth) * DE::kStageBytes);
-        eng.compute(s % DE::kStages, acc);
+        if (s + DE::kDepth < ns)
+            eng.issue_halves((s + DE::kDepth) % DE::kStages, (s + DE::kDepth) * DE::kStageBytes, halves);
+        if (active) eng.compute(s % DE::kStages, acc, tid);
     }
 }
 
@@ -594,23 +605,25 @@ __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int
             if (i >= pe) break;
             const int tile = a.tlist[i];
             const int vt = tile / a.n_rt, rt = tile % a.n_rt;
-            const bool rec = (a.tneed[tile] & 0x80) != 0;
+            const int tn8 = a.tneed[tile];
+            const bool rec = (tn8 & 0x80) != 0;
+            const int qmask = DMA ? (tn8 >> 3) & 15 : 15;  // the VGPR-staged recompute computes every block
             const int tok0 = rt * TL::BN, p0 = vt * TL::BM;
             if (threadIdx.x < 4) qflag[threadIdx.x] = 0;
             __syncthreads();
             f32x16 acc[TL::TM][TL::TN];
             if (rec) {
                 zero_acc<TL>(acc);
-                if constexpr (DMA) recompute_dma<T, TL>(a.H, a.E, a.idx, nv, a.perm, a.D, a.V, tok0, p0, lds, acc);
+                if constexpr (DMA) recompute_dma<T, TL>(a.H, a.E, a.idx, nv, a.perm, a.D, a.V, tok0, p0, qmask, lds, acc);
                 else recompute_vgpr<T, TL>(a.H, a.E, a.idx, nv, a.perm, a.D, a.V, tok0, p0, lds, acc);
                 __syncthreads();
                 g_epilogue<T, TL, true>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
                                         a.lse, a.dloss, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
-                                        qflag, qstat, qslot, a.full_de);
+                                        qflag, qstat, qslot, a.full_de, qmask);
             } else {
                 g_epilogue<T, TL, false>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
                                          a.lse, a.dloss, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
-                                         qflag, qstat, qslot, a.full_de);
+                                         qflag, qstat, qslot, a.full_de, 0);
             }
         }
     }

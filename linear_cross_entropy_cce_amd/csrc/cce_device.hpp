@@ -290,6 +290,28 @@ struct DmaEngine {
     }
 
     __device__ __forceinline__ void issue(int buf, int kb) const { issue2(buf, kb, kb); }
+
+    // Half of the A (or B) rows that instruction j fills (every wave's part of
+    // instruction j lies in one half).
+    static constexpr int kRowsPerInstr = 64 * TL::kWaves / kCpr;
+    static constexpr int half_a(int j) { return j * kRowsPerInstr / (TL::BM / 2); }
+    static constexpr int half_b(int j) { return j * kRowsPerInstr / (TL::BN / 2); }
+    // issue() for only some halves of the tile: bit h of `halves` = A rows
+    // [h BM/2, (h+1) BM/2), bit 2 + h = the same for B.  Uniform over the
+    // workgroup; the rows left out keep whatever the stage held.
+    __device__ __forceinline__ void issue_halves(int buf, int kb, int halves) const {
+        static_assert((TL::BM / 2) % kRowsPerInstr == 0 && (TL::BN / 2) % kRowsPerInstr == 0,
+                      "an instruction's rows lie in one half");
+        const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const uint32_t st = lds0 + (uint32_t)(buf * kStage) * 16u;
+#pragma unroll
+        for (int j = 0; j < NIA; ++j)
+            if ((halves >> half_a(j)) & 1) dma16_at(pa[j] + kb, st + 1024u * (j * TL::kWaves + w));
+#pragma unroll
+        for (int j = 0; j < NIB; ++j)
+            if ((halves >> (2 + half_b(j))) & 1)
+                dma16_at(pb[j] + kb, st + 16u * kStageA + 1024u * (j * TL::kWaves + w));
+    }
     // The same with separate byte offsets for the A and the B rows.
     __device__ __forceinline__ void issue2(int buf, int64_t kba, int64_t kbb) const {
         const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
