@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="after the timed steps, copy this many bytes device-to-device (counter calibration)")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = about 20 s of work)")
+    ap.add_argument("--torch-context", action="store_true",
+                    help="also time PyTorch cross-entropy on materialised logits (whole and in 4096-row chunks)")
     return ap.parse_args()
 
 
@@ -79,6 +81,52 @@ def cpu_baseline(x, n_rows_hint):
     return {"value": len(rows) / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {x.N} rows (full D={x.D}, V={x.V}): lse, loss, dH rows and their dE "
                       f"contributions over all V, fp64, {t:.1f} s"}
+
+
+def torch_context(H, E, y, ignore_index, reps=3, chunk=4096):
+    """PyTorch's own cross-entropy on the same tensors, for context: logits
+    H E^T materialised in the input dtype and upcast to fp32 inside the loss,
+    mean over valid rows, forward + backward; once over all rows and once in
+    row chunks (each chunk's logits freed before the next).  Median ms and the
+    peak device memory the step adds."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+
+    n_valid = int((y != ignore_index).sum().item())
+
+    def whole(Hr, Er):
+        loss = F.cross_entropy(F.linear(Hr, Er).float(), y, ignore_index=ignore_index)
+        loss.backward()
+
+    def chunked(Hr, Er):
+        for r0 in range(0, H.shape[0], chunk):
+            r1 = min(H.shape[0], r0 + chunk)
+            part = F.cross_entropy(F.linear(Hr[r0:r1], Er).float(), y[r0:r1], ignore_index=ignore_index,
+                                   reduction="sum") / max(n_valid, 1)
+            part.backward()
+
+    out = {}
+    for name, fn in (("materialised", whole), (f"chunked_{chunk}_rows", chunked)):
+        times, peak = [], 0.0
+        for r in range(reps + 1):
+            Hr = H.detach().clone().requires_grad_()
+            Er = E.detach().clone().requires_grad_()
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats()
+            base = torch.cuda.memory_allocated()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            fn(Hr, Er)
+            ev[1].record()
+            torch.cuda.synchronize()
+            if r:  # the first run warms up
+                times.append(ev[0].elapsed_time(ev[1]))
+                peak = max(peak, (torch.cuda.max_memory_allocated() - base) / 1e9)
+            del Hr, Er
+        out[name] = {"ms_per_step": float(np.median(times)), "tokens_per_s": H.shape[0] / (np.median(times) * 1e-3),
+                     "extra_memory_GB": peak}
+    return out
 
 
 def main():
@@ -199,6 +247,9 @@ def main():
             "valid_tokens_per_s": nv / (step_ms * 1e-3),
         },
     }
+    if a.torch_context:
+        print("[bench] torch context", file=sys.stderr, flush=True)
+        out["torch_context"] = torch_context(H, E, y, x.ignore_index)
     if a.copy_probe:
         src = torch.empty(a.copy_probe // 2, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
