@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2, help="1..5 (2 = Gemma-2-2B head)")
     ap.add_argument("--eps", type=float, default=None, help="filter threshold (default: the workload's)")
-    ap.add_argument("--sort", action="store_true", help="vocabulary sort before the backward")
+    ap.add_argument("--sort", action="store_true", help="vocabulary sort, used by the forward and the backward")
     ap.add_argument("--no-bound", action="store_true", help="backward without the forward's block-max table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -160,7 +160,7 @@ def main():
     dE = torch.empty_like(E)
     stats = torch.zeros(5, dtype=torch.int64, device=dev)
     # block-max table (one float per 128 x 128 logit block), as the autograd wrapper uses it
-    tb = None if (a.sort or a.no_bound) else torch.empty(B.block_max_elems(N, V), dtype=torch.float32, device=dev)
+    tb = None if a.no_bound else torch.empty(B.block_max_elems(N, V), dtype=torch.float32, device=dev)
     ws_f = torch.empty(B.forward_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(B.backward_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev)
     ws_s = torch.empty(B.vocab_order_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev) if a.sort else None
@@ -172,12 +172,14 @@ def main():
 
     def step(ev=None):
         if ev is not None:
-            ev[0].record(stream)
-        B.cce_forward(H, E, y, x.ignore_index, loss=loss, lse=lse, block_max=tb, ws=ws_f)
-        if ev is not None:
-            ev[1].record(stream)
+            ev[3].record(stream)
         if a.sort:
             B.cce_vocab_order(H, E, y, x.ignore_index, perm=perm, ws=ws_s)
+        if ev is not None:
+            ev[0].record(stream)
+        B.cce_forward(H, E, y, x.ignore_index, loss=loss, lse=lse, block_max=tb, ws=ws_f, perm=perm)
+        if ev is not None:
+            ev[1].record(stream)
         B.cce_backward(H, E, y, lse, dl, eps, x.ignore_index, perm, bwd_flags, dH=dH, dE=dE, stats=stats, ws=ws_b,
                        block_max=tb)
         if ev is not None:
@@ -187,7 +189,7 @@ def main():
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
     print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -197,6 +199,7 @@ def main():
     wall = time.perf_counter() - t0
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    sort_ms = [e[3].elapsed_time(e[0]) for e in evs]
     step_ms = wall * 1e3 / a.steps
     st = stats.cpu().numpy()
     n_live, n_label, n_total, n_recomp = int(st[0]), int(st[1]), int(st[2]), int(st[4])
@@ -234,6 +237,7 @@ def main():
                      "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
         "detail": {
             "fwd_ms_mean": fwd_avg, "bwd_ms_mean": float(np.mean(bwd_ms)),
+            "sort_ms_mean": float(np.mean(sort_ms)),
             "fwd_ms_min": float(np.min(fwd_ms)), "bwd_ms_min": float(np.min(bwd_ms)),
             "blocks_softmax_kept": n_live, "blocks_label_only": n_label, "blocks_total": n_total,
             "kept_frac": (n_live + n_label) / max(n_total, 1),

@@ -104,16 +104,21 @@ size_t cce_block_max_elems(int64_t N, int64_t V);
  * Ignored rows get loss = lse = 0.  The log-sum-exp is accumulated per
  * vocabulary split on chip (online max / sum-exp) and the splits are merged in
  * a fixed order, so the result does not depend on scheduling.
+ * perm: NULL, or a permutation of 0..V-1 (int32, device, [V], e.g. from
+ *   cce_vocab_order): vocabulary entries are visited in the order perm[0],
+ *   perm[1], ...  The loss only changes by rounding order; entries of perm
+ *   outside [0, V) read entry 0 instead (the caller guarantees a permutation).
  * block_max: NULL, or device fp32 [cce_block_max_elems(N, V)] that receives
  *   the largest logit of every 128 x 128 block of the logit matrix of the
- *   non-ignored rows (in order), row-major over [2 ceil(N / 256) row blocks,
- *   2 ceil(V / 256) vocabulary blocks]; blocks with no valid row get -inf.
+ *   non-ignored rows (in order) and the vocabulary in processing order,
+ *   row-major over [2 ceil(N / 256) row blocks, 2 ceil(V / 256) vocabulary
+ *   blocks]; blocks with no valid row get -inf.
  * ws: device scratch of at least cce_forward_workspace_bytes bytes.
  */
 cce_status cce_forward(const void *H, const void *E, const int64_t *labels,
                        int64_t N, int64_t D, int64_t V, cce_dtype dtype,
-                       int64_t ignore_index, float *loss, float *lse, float *block_max,
-                       void *ws, size_t ws_bytes, void *stream);
+                       int64_t ignore_index, const int32_t *perm, float *loss, float *lse,
+                       float *block_max, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Vocabulary order for the backward (optional): key_v = mean over
@@ -134,8 +139,8 @@ cce_status cce_vocab_order(const void *H, const void *E, const int64_t *labels,
  * Backward: dH [N, D] and dE [V, D] (input dtype, device) of
  * L = sum_i dloss[i] * loss_i, given lse from cce_forward.
  *  - dloss: fp32 [N]; it carries the caller's reduction (1/N_valid for a mean).
- *  - block_max: NULL, or the table cce_forward wrote for these same H, E and
- *    labels.  With it (and perm == NULL, filter_eps > 0), a 128 x 128 block
+ *  - block_max: NULL, or the table cce_forward wrote for these same H, E,
+ *    labels and perm.  With it (and filter_eps > 0), a 128 x 128 block
  *    whose largest logit is so far below the smallest lse of its rows that
  *    every p_iv in it is < filter_eps / 2 cannot keep its softmax part, and a
  *    256 x 256 logit tile made only of such blocks is not recomputed; the

@@ -14,23 +14,24 @@ from . import binding
 class _LinearCrossEntropy(torch.autograd.Function):
     @staticmethod
     def forward(ctx, H, E, labels, ignore_index, filter_eps, sort_vocab):
-        # The block-max table (one float per 128 x 128 logit block) lets the
-        # backward leave out tiles the gradient filter would drop entirely.
+        # With the sort, the forward already visits the vocabulary in the
+        # backward's order, so that its block-max table (one float per
+        # 128 x 128 logit block) describes the backward's blocks: tiles the
+        # gradient filter would drop entirely are then not recomputed.
+        perm = binding.cce_vocab_order(H, E, labels, ignore_index) if sort_vocab else None
         tb = None
-        if filter_eps > 0 and not sort_vocab:
+        if filter_eps > 0:
             tb = torch.empty(binding.block_max_elems(H.shape[0], E.shape[0]), dtype=torch.float32, device=H.device)
-        loss, lse = binding.cce_forward(H, E, labels, ignore_index, block_max=tb)
-        ctx.save_for_backward(H, E, labels, lse, tb)
+        loss, lse = binding.cce_forward(H, E, labels, ignore_index, block_max=tb, perm=perm)
+        ctx.save_for_backward(H, E, labels, lse, tb, perm)
         ctx.ignore_index = ignore_index
         ctx.filter_eps = filter_eps
-        ctx.sort_vocab = sort_vocab
         ctx.mark_non_differentiable(lse)
         return loss, lse
 
     @staticmethod
     def backward(ctx, dloss, _dlse):
-        H, E, labels, lse, tb = ctx.saved_tensors
-        perm = binding.cce_vocab_order(H, E, labels, ctx.ignore_index) if ctx.sort_vocab else None
+        H, E, labels, lse, tb, perm = ctx.saved_tensors
         dH, dE = binding.cce_backward(H, E, labels, lse, dloss.float().contiguous(), ctx.filter_eps,
                                       ctx.ignore_index, perm, block_max=tb)
         return dH, dE, None, None, None, None
@@ -43,8 +44,8 @@ def linear_cross_entropy(H, E, labels, ignore_index=-100, reduction="mean", filt
     H [N, D] and E [V, D] (bf16 or fp32, on the GPU); labels int64 [N].
     reduction: "none" (per-token fp32 loss), "sum", or "mean" over the rows
     whose label is not ignore_index.  filter_eps: gradient-filter threshold
-    (0 disables filtering).  sort_vocab: reorder the vocabulary by mean logit
-    before the backward so that surviving blocks cluster.
+    (0 disables filtering).  sort_vocab: visit the vocabulary by descending
+    mean logit (forward and backward) so that surviving blocks cluster.
     """
     loss, _ = _LinearCrossEntropy.apply(H, E, labels, int(ignore_index), float(filter_eps), bool(sort_vocab))
     if reduction == "none":

@@ -66,7 +66,7 @@ def lib() -> ctypes.CDLL:
         getattr(L, f).restype = ctypes.c_size_t
     L.cce_block_max_elems.argtypes = [_i64, _i64]
     L.cce_block_max_elems.restype = ctypes.c_size_t
-    L.cce_forward.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp, _vp,
+    L.cce_forward.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp,
                               ctypes.c_size_t, _vp]
     L.cce_forward.restype = ctypes.c_int
     L.cce_vocab_order.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp,
@@ -162,13 +162,23 @@ def _shapes(H, E, labels):
     return H.shape[0], H.shape[1], E.shape[0]
 
 
-def cce_forward(H, E, labels, ignore_index=-100, loss=None, lse=None, block_max=None, ws=None, stream=None):
+def _check_perm(perm, V):
+    import torch
+    if perm is not None and (perm.dtype != torch.int32 or perm.numel() != V or not perm.is_contiguous()):
+        raise ValueError(f"perm must be contiguous int32 with {V} entries")
+
+
+def cce_forward(H, E, labels, ignore_index=-100, loss=None, lse=None, block_max=None, ws=None, stream=None,
+                perm=None):
     """loss, lse (fp32 [N]) of the fused head + cross-entropy.  block_max:
     None, or an fp32 tensor of block_max_elems(N, V) entries to receive the
-    largest logit of every 128 x 128 block of the logits (for cce_backward)."""
+    largest logit of every 128 x 128 block of the logits (for cce_backward).
+    perm: None, or the int32 [V] vocabulary order to visit (the table is then
+    in that order, for a cce_backward given the same perm)."""
     import torch
     N, D, V = _shapes(H, E, labels)
     dt = _dtype_code(H)
+    _check_perm(perm, V)
     loss = torch.empty(N, dtype=torch.float32, device=H.device) if loss is None else loss
     lse = torch.empty(N, dtype=torch.float32, device=H.device) if lse is None else lse
     if block_max is not None and (block_max.dtype != torch.float32 or
@@ -176,8 +186,8 @@ def cce_forward(H, E, labels, ignore_index=-100, loss=None, lse=None, block_max=
         raise ValueError(f"block_max must be contiguous fp32 with at least {block_max_elems(N, V)} entries")
     need = forward_workspace_bytes(N, D, V, dt)
     ws = _workspace(need, H.device, ws)
-    s = lib().cce_forward(_ptr(H), _ptr(E), _ptr(labels), N, D, V, dt, int(ignore_index), _ptr(loss), _ptr(lse),
-                          _ptr(block_max), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    s = lib().cce_forward(_ptr(H), _ptr(E), _ptr(labels), N, D, V, dt, int(ignore_index), _ptr(perm), _ptr(loss),
+                          _ptr(lse), _ptr(block_max), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("cce_forward", s)
     return loss, lse
 
@@ -201,10 +211,11 @@ def cce_backward(H, E, labels, lse, dloss, filter_eps=2.0 ** -12, ignore_index=-
                  dH=None, dE=None, stats=None, ws=None, stream=None, block_max=None):
     """dH [N, D], dE [V, D] (input dtype) of sum_i dloss_i loss_i.  stats:
     None or int64 [5] (see include/cce.h); block_max: None or the table
-    cce_forward wrote for the same H, E and labels."""
+    cce_forward wrote for the same H, E, labels and perm."""
     import torch
     N, D, V = _shapes(H, E, labels)
     dt = _dtype_code(H)
+    _check_perm(perm, V)
     dH = torch.empty_like(H) if dH is None else dH
     dE = torch.empty_like(E) if dE is None else dE
     if stats is not None and (stats.dtype != torch.int64 or stats.numel() < 5):

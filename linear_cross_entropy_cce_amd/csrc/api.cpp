@@ -82,19 +82,19 @@ size_t cce_vocab_order_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtyp
 }
 
 cce_status cce_forward(const void *H, const void *E, const int64_t *labels, int64_t N, int64_t D, int64_t V,
-                       cce_dtype dtype, int64_t ignore_index, float *loss, float *lse, float *block_max, void *ws,
-                       size_t ws_bytes, void *stream) {
+                       cce_dtype dtype, int64_t ignore_index, const int32_t *perm, float *loss, float *lse,
+                       float *block_max, void *ws, size_t ws_bytes, void *stream) {
     if (!H || !E || !labels || !loss || !lse || !ws) return CCE_ERR_NULL;
     if (!dtype_ok(dtype)) return CCE_ERR_DTYPE;
     if (!shape_ok(N, D, V)) return CCE_ERR_SHAPE;
     if (!aligned(H, 16) || !aligned(E, 16) || !aligned(ws, 16) || !aligned(labels, 8) || !aligned(loss, 4) ||
-        !aligned(lse, 4) || !aligned(block_max, 4))
+        !aligned(lse, 4) || !aligned(block_max, 4) || !aligned(perm, 4))
         return CCE_ERR_ALIGN;
     const FwdShape s = fwd_shape(N, D, V);
     size_t need = 0;
     const FwdWs w = fwd_ws(ws, s, &need);
     if (ws_bytes < need) return CCE_ERR_WORKSPACE;
-    return hip_status(launch_forward(dtype, H, E, labels, s, ignore_index, w, loss, lse, block_max,
+    return hip_status(launch_forward(dtype, H, E, labels, s, ignore_index, perm, w, loss, lse, block_max,
                                      static_cast<hipStream_t>(stream)));
 }
 

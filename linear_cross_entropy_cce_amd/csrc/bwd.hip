@@ -1160,10 +1160,11 @@ static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, cons
                        ignore_index, dH);
     CCE_LAUNCHED();
 
-    // The block maxima are in the natural vocabulary order and only say
-    // something when filtering is on.  thr = ln(eps / 2), rounded towards -inf.
+    // The block maxima (in the processing order the forward used, which the
+    // caller keeps equal to perm) only say something when filtering is on.
+    // thr = ln(eps / 2), rounded towards -inf.
     const bool full_de = (flags & CCE_BWD_FULL_DE) != 0;
-    const float *tb = (block_max && !perm && eps > 0.f && !full_de) ? block_max : nullptr;
+    const float *tb = (block_max && eps > 0.f && !full_de) ? block_max : nullptr;
     float thr = 0.f;
     if (tb) {
         thr = (float)(log((double)eps) - log(2.0));

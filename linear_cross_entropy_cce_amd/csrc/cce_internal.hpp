@@ -124,8 +124,8 @@ hipError_t launch_compact(const int64_t *labels, int64_t N, int64_t ignore_index
 hipError_t launch_check_labels(const int64_t *labels, int64_t N, int64_t V, int64_t ignore_index,
                                int64_t *n_bad, hipStream_t st);
 hipError_t launch_forward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
-                          const FwdShape &s, int64_t ignore_index, const FwdWs &w, float *loss,
-                          float *lse, float *block_max, hipStream_t st);
+                          const FwdShape &s, int64_t ignore_index, const int32_t *perm, const FwdWs &w,
+                          float *loss, float *lse, float *block_max, hipStream_t st);
 hipError_t launch_backward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
                            const float *lse, const float *dloss, const float *block_max, const BwdShape &s,
                            int64_t ignore_index, float eps, const int32_t *perm, unsigned flags,

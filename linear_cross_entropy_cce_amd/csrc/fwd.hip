@@ -237,8 +237,8 @@ __device__ __forceinline__ void fwd_write_partials(float (&m)[TL::TN], float (&l
 template <typename T>
 __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
     const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ nvalid_p, int D, int V, int64_t N, int n_vtiles, int S, int R,
-    float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
+    const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, int D, int V, int64_t N, int n_vtiles,
+    int S, int R, float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
     using TL = TileF;
     __shared__ u32x4 lds[TL::kLdsChunks];
     const int nv = *nvalid_p;
@@ -265,8 +265,9 @@ __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
         const int v0 = vt * TL::BM;
 #pragma unroll
         for (int j = 0; j < Engine<T, TL>::NA; ++j) {
-            const int v = v0 + eng.row(j);
-            eng.pa[j] = v < V ? reinterpret_cast<const char *>(E) + (size_t)v * rowb : nullptr;
+            const int pos = v0 + eng.row(j);
+            const int v = pos < V ? (perm ? perm[pos] : pos) : -1;
+            eng.pa[j] = (v >= 0 && v < V) ? reinterpret_cast<const char *>(E) + (size_t)v * rowb : nullptr;
         }
     };
 
@@ -313,8 +314,8 @@ __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
 template <typename T, class TL>
 __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
     const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ nvalid_p, int D, int V, int64_t N, int n_vtiles, int S, int R,
-    float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
+    const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, int D, int V, int64_t N, int n_vtiles,
+    int S, int R, float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
     using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
     __shared__ u32x4 lds[DE::kLdsChunks];
     const int nv = *nvalid_p;
@@ -340,7 +341,9 @@ __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
 #pragma unroll
         for (int j = 0; j < DE::NIA; ++j) {
             const int r = DE::row_a(j);
-            const int v = min(vt * TL::BM + r, V - 1);
+            const int pos = min(vt * TL::BM + r, V - 1);
+            int v = perm ? perm[pos] : pos;
+            v = (v >= 0 && v < V) ? v : 0;
             eng.pa[j] = reinterpret_cast<const char *>(E) + (size_t)v * rowb + DE::chunk_off(j, r, threadIdx.x);
         }
     };
@@ -472,8 +475,8 @@ hipError_t launch_check_labels(const int64_t *labels, int64_t N, int64_t V, int6
 
 template <typename T>
 static hipError_t forward_t(const T *H, const T *E, const int64_t *labels, const FwdShape &s,
-                            int64_t ignore_index, const FwdWs &w, float *loss, float *lse, float *block_max,
-                            hipStream_t st) {
+                            int64_t ignore_index, const int32_t *perm, const FwdWs &w, float *loss, float *lse,
+                            float *block_max, hipStream_t st) {
     hipError_t e = launch_compact(labels, s.N, ignore_index, w.idx, w.nvalid, st);
     if (e != hipSuccess) return e;
     int *tb = reinterpret_cast<int *>(block_max);
@@ -485,9 +488,9 @@ static hipError_t forward_t(const T *H, const T *E, const int64_t *labels, const
     const int groups = s.S * s.n_rtiles;
     if ((s.D * (int64_t)sizeof(T)) % kLogitRowBytes == 0)
         hipLaunchKernelGGL((k_fwd_dma<T, TileFD>), dim3(groups), dim3(TileFD::kThreads), 0, st, H, E, w.idx, w.nvalid,
-                           (int)s.D, (int)s.V, s.N, s.n_vtiles, s.S, s.n_rtiles, w.part_m, w.part_s, tb);
+                           perm, (int)s.D, (int)s.V, s.N, s.n_vtiles, s.S, s.n_rtiles, w.part_m, w.part_s, tb);
     else
-        hipLaunchKernelGGL(k_fwd<T>, dim3(groups), dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid,
+        hipLaunchKernelGGL(k_fwd<T>, dim3(groups), dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid, perm,
                            (int)s.D, (int)s.V, s.N, s.n_vtiles, s.S, s.n_rtiles, w.part_m, w.part_s, tb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_merge<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, H, E, labels,
@@ -498,13 +501,13 @@ static hipError_t forward_t(const T *H, const T *E, const int64_t *labels, const
 }
 
 hipError_t launch_forward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
-                          const FwdShape &s, int64_t ignore_index, const FwdWs &w, float *loss,
-                          float *lse, float *block_max, hipStream_t st) {
+                          const FwdShape &s, int64_t ignore_index, const int32_t *perm, const FwdWs &w,
+                          float *loss, float *lse, float *block_max, hipStream_t st) {
     if (dt == CCE_BF16)
         return forward_t<bf16_t>(static_cast<const bf16_t *>(H), static_cast<const bf16_t *>(E), labels,
-                                 s, ignore_index, w, loss, lse, block_max, st);
+                                 s, ignore_index, perm, w, loss, lse, block_max, st);
     return forward_t<float>(static_cast<const float *>(H), static_cast<const float *>(E), labels, s,
-                            ignore_index, w, loss, lse, block_max, st);
+                            ignore_index, perm, w, loss, lse, block_max, st);
 }
 
 }  // namespace cce

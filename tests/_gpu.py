@@ -61,14 +61,15 @@ def t64(t: torch.Tensor) -> np.ndarray:
 def run_gpu(x: inputs.Inputs, dloss: np.ndarray, eps: float, sort=False, flags=0, prefill_nan=True, bound=True):
     """Forward + backward through the C ABI; returns fp64 numpy arrays.
     bound: the forward writes the block-max table and the backward gets it
-    (as the autograd wrapper does); False runs the backward without it."""
+    (as the autograd wrapper does); False runs the backward without it.
+    sort: both passes visit the vocabulary in cce_vocab_order's order."""
     H, E, y = to_device(x)
     loss = torch.full((x.N,), float("nan"), dtype=torch.float32, device=DEV)
     lse = torch.full((x.N,), float("nan"), dtype=torch.float32, device=DEV)
     tb = torch.full((B.block_max_elems(x.N, x.V),), float("nan"), dtype=torch.float32, device=DEV) \
         if bound else None
-    B.cce_forward(H, E, y, x.ignore_index, loss=loss, lse=lse, block_max=tb)
     perm = B.cce_vocab_order(H, E, y, x.ignore_index) if sort else None
+    B.cce_forward(H, E, y, x.ignore_index, loss=loss, lse=lse, block_max=tb, perm=perm)
     dl = torch.from_numpy(dloss).to(DEV)
     dH = torch.full_like(H, float("nan")) if prefill_nan else None
     dE = torch.full_like(E, float("nan")) if prefill_nan else None

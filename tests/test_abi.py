@@ -76,11 +76,11 @@ def test_workspace_invalid_sizes_return_zero():
 
 
 def _fwd(**kw):
-    a = dict(H=FAKE, E=FAKE, labels=FAKE, N=16, D=64, V=100, dt=B.CCE_BF16, ign=-100, loss=FAKE, lse=FAKE,
-             tb=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a = dict(H=FAKE, E=FAKE, labels=FAKE, N=16, D=64, V=100, dt=B.CCE_BF16, ign=-100, perm=None, loss=FAKE,
+             lse=FAKE, tb=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
     a.update(kw)
-    return B.lib().cce_forward(a["H"], a["E"], a["labels"], a["N"], a["D"], a["V"], a["dt"], a["ign"], a["loss"],
-                               a["lse"], a["tb"], a["ws"], a["ws_bytes"], a["stream"])
+    return B.lib().cce_forward(a["H"], a["E"], a["labels"], a["N"], a["D"], a["V"], a["dt"], a["ign"], a["perm"],
+                               a["loss"], a["lse"], a["tb"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 def _bwd(**kw):
@@ -124,6 +124,7 @@ def test_forward_specific_errors():
     assert _fwd(lse=None) == B.CCE_ERR_NULL
     assert _fwd(lse=FAKE + 2) == B.CCE_ERR_ALIGN
     assert _fwd(tb=FAKE + 2) == B.CCE_ERR_ALIGN
+    assert _fwd(perm=FAKE + 2) == B.CCE_ERR_ALIGN
     need = B.forward_workspace_bytes(16, 64, 100, B.CCE_BF16)
     assert _fwd(ws_bytes=need - 1) == B.CCE_ERR_WORKSPACE
 

@@ -6,7 +6,8 @@ block; cce_backward, given that table, leaves out the logit recompute of
 The gradient filter would drop all of such a tile's softmax part, so the
 outputs must be bit-identical to a run without the table; only the count of
 recomputed blocks (stats[4]) changes.  The table itself is checked against the
-definition: the largest fp64 logit of each block of the valid rows (in order),
+definition: the largest fp64 logit of each block of the valid rows (in order)
+and the vocabulary in processing order (sorted when a permutation is given),
 -inf for blocks past the valid rows.
 """
 import numpy as np
@@ -29,9 +30,11 @@ CASES = [
 ]
 
 
-def _ref_block_max(x):
+def _ref_block_max(x, perm=None):
     H = oracle.as_f64(x.H, x.dtype)
     E = oracle.as_f64(x.E, x.dtype)
+    if perm is not None:
+        E = E[perm]  # vocabulary in processing order
     valid = np.nonzero(x.labels != x.ignore_index)[0]
     Z = H[valid] @ E.T  # the logits of the valid rows, in order
     nrb, ncb = 2 * -(-x.N // 256), 2 * -(-x.V // 256)
@@ -44,11 +47,14 @@ def _ref_block_max(x):
 
 
 @pytest.mark.parametrize("k,N,D,V", CASES, ids=[f"w{c[0]}" for c in CASES])
-def test_table_is_block_max(k, N, D, V):
+@pytest.mark.parametrize("sort", [False, True])
+def test_table_is_block_max(k, N, D, V, sort):
     x = inputs.make_workload(k, N=N, D=D, V=V)
-    G.say(f"block-max table w{k} N={x.N} D={x.D} V={x.V}")
-    out = G.run_gpu(x, G.mean_dloss(x), eps=x.eps or 2.0 ** -12)
-    ref = _ref_block_max(x)
+    G.say(f"block-max table w{k} N={x.N} D={x.D} V={x.V} sort={sort}")
+    out = G.run_gpu(x, G.mean_dloss(x), eps=x.eps or 2.0 ** -12, sort=sort)
+    if sort:
+        assert np.array_equal(np.sort(out["perm"]), np.arange(x.V))
+    ref = _ref_block_max(x, out.get("perm"))
     got = out["block_max"].reshape(ref.shape)
     fin = np.isfinite(ref)
     assert np.all(got[~fin] == -np.inf), "blocks past the valid rows or vocabulary must stay -inf"
@@ -59,12 +65,13 @@ def test_table_is_block_max(k, N, D, V):
 
 @pytest.mark.parametrize("k,N,D,V", CASES, ids=[f"w{c[0]}" for c in CASES])
 @pytest.mark.parametrize("eps", [2.0 ** -12, 2.0 ** -6])
-def test_skip_is_bit_identical(k, N, D, V, eps):
+@pytest.mark.parametrize("sort", [False, True])
+def test_skip_is_bit_identical(k, N, D, V, eps, sort):
     x = inputs.make_workload(k, N=N, D=D, V=V)
-    G.say(f"bound skip bit identity w{k} N={x.N} D={x.D} V={x.V} eps={eps}")
+    G.say(f"bound skip bit identity w{k} N={x.N} D={x.D} V={x.V} eps={eps} sort={sort}")
     dl = G.random_dloss(x, seed=7)
-    a = G.run_gpu(x, dl, eps=eps, bound=True)
-    b = G.run_gpu(x, dl, eps=eps, bound=False)
+    a = G.run_gpu(x, dl, eps=eps, bound=True, sort=sort)
+    b = G.run_gpu(x, dl, eps=eps, bound=False, sort=sort)
     for key in ("loss", "lse", "dH", "dE"):
         assert np.array_equal(a[key], b[key]), key
     assert np.array_equal(a["stats"][:4], b["stats"][:4])
@@ -78,35 +85,47 @@ def test_skip_is_bit_identical(k, N, D, V, eps):
         assert a["stats"][4] < a["stats"][2], a["stats"]
 
 
-def test_table_unused_with_sort_or_without_filter():
+def test_table_unused_without_filter():
     x = inputs.make_workload(5, N=480, D=256, V=9500)
-    G.say("bound ignored with sort / eps=0")
-    dl = G.mean_dloss(x)
-    s = G.run_gpu(x, dl, eps=2.0 ** -12, sort=True)
-    assert s["stats"][4] == s["stats"][2]
-    z = G.run_gpu(x, dl, eps=0.0)
+    G.say("bound ignored with eps=0")
+    z = G.run_gpu(x, G.mean_dloss(x), eps=0.0)
     assert z["stats"][4] == z["stats"][2] and z["stats"][0] == z["stats"][2]
 
 
-def _device_run(x, tb, eps, dl):
+def test_sorted_forward_matches_oracle():
+    """Visiting the vocabulary in sorted order changes only the rounding."""
+    x = inputs.make_workload(5, N=480, D=256, V=9500)
+    G.say("sorted forward parity w5")
+    out = G.run_gpu(x, G.mean_dloss(x), eps=x.eps, sort=True)
+    loss, lse = oracle.forward(oracle.as_f64(x.H, x.dtype), oracle.as_f64(x.E, x.dtype), x.labels, x.ignore_index)
+    np.testing.assert_allclose(out["lse"], lse, rtol=1e-3, atol=1e-3)
+    np.testing.assert_allclose(out["loss"], loss, rtol=1e-3, atol=1e-3)
+
+
+def _device_run(x, tb, eps, dl, perm=None):
     H, E, y = G.to_device(x)
-    _, lse = B.cce_forward(H, E, y, x.ignore_index, block_max=tb)
+    _, lse = B.cce_forward(H, E, y, x.ignore_index, block_max=tb, perm=perm)
     stats = torch.zeros(5, dtype=torch.int64, device=G.DEV)
-    dH, dE = B.cce_backward(H, E, y, lse, dl, eps, x.ignore_index, None, 0, stats=stats, block_max=tb)
+    dH, dE = B.cce_backward(H, E, y, lse, dl, eps, x.ignore_index, perm, 0, stats=stats, block_max=tb)
     torch.cuda.synchronize()
     return dH, dE, stats.cpu().numpy()
 
 
-@pytest.mark.parametrize("k", [2, 5])
-def test_full_size_skip_is_bit_identical(k):
+@pytest.mark.parametrize("k,sort", [(2, False), (5, False), (5, True)])
+def test_full_size_skip_is_bit_identical(k, sort):
     """At the full head shapes of the peaked workloads, with the launch
     configuration the benchmark times, compared on the device."""
     x = inputs.make_workload(k)
-    G.say(f"bound skip full size w{k} N={x.N} D={x.D} V={x.V}")
+    G.say(f"bound skip full size w{k} N={x.N} D={x.D} V={x.V} sort={sort}")
     dl = torch.from_numpy(G.mean_dloss(x)).to(G.DEV)
+    perm = None
+    if sort:
+        H, E, y = G.to_device(x)
+        perm = B.cce_vocab_order(H, E, y, x.ignore_index)
+        del H, E, y
     tb = torch.empty(B.block_max_elems(x.N, x.V), dtype=torch.float32, device=G.DEV)
-    dH_a, dE_a, st_a = _device_run(x, tb, x.eps, dl)
-    dH_b, dE_b, st_b = _device_run(x, None, x.eps, dl)
+    dH_a, dE_a, st_a = _device_run(x, tb, x.eps, dl, perm)
+    dH_b, dE_b, st_b = _device_run(x, None, x.eps, dl, perm)
     assert torch.equal(dH_a, dH_b) and torch.equal(dE_a, dE_b)
     assert np.array_equal(st_a[:4], st_b[:4])
     G.say(f"  recomputed blocks {st_a[4]} of {st_a[2]} (kept {st_a[0]}, label-only {st_a[1]})")

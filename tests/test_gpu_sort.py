@@ -69,4 +69,6 @@ def test_sorted_and_unsorted_backward_agree(k, N, D, V):
     for name in ("dH", "dE"):
         n = max(np.linalg.norm(a[name]), 1e-30)
         assert np.linalg.norm(a[name] - b[name]) / n <= 2e-3, name
-    assert np.array_equal(a["lse"], b["lse"])
+    # the sorted forward visits the vocabulary in another order: rounding only
+    np.testing.assert_allclose(b["lse"], a["lse"], rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(b["loss"], a["loss"], rtol=1e-5, atol=1e-5)
