@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, help="1..5 (2 = Gemma-2-2B head)")
+    ap.add_argument("--workload", type=int, default=2, help="1..6 (2 = Gemma-2-2B head)")
     ap.add_argument("--eps", type=float, default=None, help="filter threshold (default: the workload's)")
     ap.add_argument("--sort", action="store_true", help="vocabulary sort, used by the forward and the backward")
     ap.add_argument("--no-bound", action="store_true", help="backward without the forward's block-max table")

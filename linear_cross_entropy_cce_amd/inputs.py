@@ -19,11 +19,14 @@ workload keeps the head shape and draws the values:
   H  ~ N(0, 1) per element ("flat": an early-training softmax), or
   H  = 3 sqrt(D) e_y / ||e_y|| + N(0, I)  ("peaked": a trained-like softmax,
        e_y the bf16-rounded classifier row of the token's label)
-  labels uniform over [0, V), or Zipf(1.1): P(id = r - 1) ~ r^-1.1, r = 1..V
+  labels uniform over [0, V), or Zipf(1.1): P(id = r - 1) ~ r^-1.1, r = 1..V,
+       or the same Zipf ranks sent through a seeded permutation of the ids
+       (frequent tokens scattered over the vocabulary, as in a tokenizer
+       whose ids do not follow frequency)
   exactly round(f N) rows, chosen by a seeded permutation, set to -100.
 
 Streams: numpy PCG64 seeded by SeedSequence([seed, stream]) with stream
-0 = E, 1 = labels, 2 = ignore mask, 3 = H noise.  Values are drawn in float32
+0 = E, 1 = labels, 2 = ignore mask, 3 = H noise, 4 = id permutation.  Values are drawn in float32
 and, for bf16 workloads, rounded to nearest-even bfloat16 bit patterns.
 """
 from __future__ import annotations
@@ -60,6 +63,9 @@ WORKLOADS = {
     3: Recipe("llama3-8b-head", 16384, 4096, 128256, "bf16", 0.02, "normal", "zipf", 0.40, 2.0 ** -12, (False,)),
     4: Recipe("phi3.5-mini-head", 8192, 3072, 32064, "bf16", 0.02, "normal", "uniform", 0.0, 2.0 ** -12, (False,)),
     5: Recipe("large-vocab-1024x24", 24576, 2048, 248320, "bf16", 0.02, "peaked", "zipf", 0.0, 2.0 ** -12, (False, True)),
+    # workload 5 with the Zipf ranks scattered over the ids: what the sort is for
+    6: Recipe("large-vocab-1024x24-scattered", 24576, 2048, 248320, "bf16", 0.02, "peaked", "zipf-scattered", 0.0,
+              2.0 ** -12, (False, True)),
 }
 
 
@@ -136,6 +142,8 @@ def make_inputs(N, D, V, dtype="bf16", e_std=0.02, h_kind="normal", label_kind="
         labels = lrng.integers(0, V, size=N, dtype=np.int64)
     elif label_kind == "zipf":
         labels = zipf_labels(lrng, N, V)
+    elif label_kind == "zipf-scattered":
+        labels = _rng(seed, 4).permutation(V).astype(np.int64)[zipf_labels(lrng, N, V)]
     else:
         raise ValueError(f"unknown label kind {label_kind!r}")
 
@@ -169,7 +177,7 @@ def make_inputs(N, D, V, dtype="bf16", e_std=0.02, h_kind="normal", label_kind="
 
 def make_workload(k: int, seed: int | None = None, N: int | None = None, D: int | None = None,
                   V: int | None = None) -> Inputs:
-    """Workload k (1..5) at its full size, or with any of N, D, V overridden
+    """Workload k (1..6) at its full size, or with any of N, D, V overridden
     (the same recipe at a size the oracle finishes quickly)."""
     r = WORKLOADS[k]
     return make_inputs(N or r.N, D or r.D, V or r.V, dtype=r.dtype, e_std=r.e_std, h_kind=r.h_kind,

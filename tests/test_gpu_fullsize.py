@@ -1,4 +1,4 @@
-"""The five workloads at their full sizes, in the launch configuration the
+"""The six workloads at their full sizes, in the launch configuration the
 benchmark times.  The oracle computes sampled outputs one by one (lse, loss
 and dH rows; dE rows where every row's lse is affordable) and properties that
 hold at any size check the rest:
@@ -14,11 +14,11 @@ from tests import _gpu as G
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6])
 def test_full_size(k):
     x = inputs.make_workload(k)
     eps = x.eps
-    sort = k == 5
+    sort = k >= 5
     G.say(f"full size w{k} N={x.N} D={x.D} V={x.V} eps={eps} sort={sort}")
     dl = G.mean_dloss(x)
     out = G.run_gpu(x, dl, eps=eps, sort=sort)

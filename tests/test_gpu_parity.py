@@ -1,5 +1,5 @@
 """Parity of the HIP path with the fp64 oracle, element by element, on the
-five workloads' recipes at sizes the oracle finishes in seconds (several
+six workloads' recipes at sizes the oracle finishes in seconds (several
 tiles, ragged tails, more than one vocabulary chunk), plus edge cases."""
 import numpy as np
 import pytest
@@ -16,6 +16,7 @@ SMALL = [
     (3, 600, 512, 5000),     # flat, 40 % ignored rows
     (4, 512, 384, 3000),     # flat, small V / D
     (5, 480, 256, 9500),     # peaked, Zipf labels; run with and without sort
+    (6, 480, 256, 9500),     # as 5 with the Zipf ranks scattered over the ids
 ]
 
 

@@ -67,3 +67,18 @@ def test_peaked_hidden_states_point_at_label():
     assert np.all(np.argmax(z, axis=1) == x.labels)
     margin = z[np.arange(64), x.labels] - np.sort(z, axis=1)[:, -2]
     assert np.median(margin) > 0.04 * 256
+
+
+def test_scattered_zipf_is_a_relabelled_zipf():
+    # Workload 6 draws the same Zipf ranks as workload 5 and sends them through
+    # a permutation of the ids: same multiset of counts, head spread out.
+    a = inputs.make_workload(5, N=4000, D=16, V=20000)
+    b = inputs.make_workload(6, N=4000, D=16, V=20000, seed=5)
+    ca = np.sort(np.bincount(a.labels, minlength=20000))
+    cb = np.sort(np.bincount(b.labels, minlength=20000))
+    assert np.array_equal(ca, cb)
+    assert np.mean(a.labels < 256) > 0.4 and np.mean(b.labels < 256) < 0.05
+    # one id map: equal ranks give equal ids
+    ids = {}
+    for ra, rb in zip(a.labels, b.labels):
+        assert ids.setdefault(int(ra), int(rb)) == int(rb)
