@@ -26,9 +26,9 @@ constexpr int kStoreVocab = 8192;
 // Workgroups of the persistent backward kernels.
 constexpr int kPassGroups = 256;
 // Upper bound on the forward's vocabulary splits (merged per row in order).
-constexpr int kMaxSplits = 64;
-// Workgroups the forward aims to launch (two per compute unit).
-constexpr int kFwdTargetGroups = 512;
+// Most workgroups of the forward's persistent grid (its partial buffers are
+// sized for this many).
+constexpr int kFwdMaxGroups = 1024;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -55,15 +55,14 @@ struct FwdShape {
     int64_t N, D, V;
     int n_vtiles;  // vocabulary tiles of kTileVocab
     int n_rtiles;  // token tiles of kTileRows (upper bound, from N)
-    int S;         // vocabulary splits
 };
 FwdShape fwd_shape(int64_t N, int64_t D, int64_t V);
 
 struct FwdWs {
     int32_t *idx;      // [N] compacted valid-row indices
     int32_t *nvalid;   // [1]
-    float *part_m;     // [S, N] running max (log2 units)
-    float *part_s;     // [S, N] running sum of 2^(z log2e - m)
+    float *part_m;     // [kFwdMaxGroups + n_rtiles, kTileRows] per segment: running max (log2 units)
+    float *part_s;     // [kFwdMaxGroups + n_rtiles, kTileRows] per segment: sum of 2^(z log2e - m)
 };
 FwdWs fwd_ws(void *ws, const FwdShape &s, size_t *bytes);
 

@@ -2,10 +2,10 @@
 //
 //  k_compact      valid-row compaction (rows whose label is not ignore_index)
 //  k_fwd          logit tiles Z^T = E_tile * H_tile^T on bf16/fp32 MFMA, kept in
-//                 registers; per token and vocabulary split an online running
-//                 max / sum-exp (log2 domain); partials written per split
-//  k_merge        per row: merge of the split partials in split order -> lse;
-//                 label logit <h_i, e_{y_i}> (the indexed matmul) -> loss
+//                 registers; per token and vocabulary range an online running
+//                 max / sum-exp (log2 domain); partials written per segment
+//  k_merge        per row: merge of the segment partials in vocabulary order
+//                 -> lse; label logit <h_i, e_{y_i}> (the indexed matmul) -> loss
 //
 // The method: cross-entropy needs only the correct-token logit and the
 // log-sum-exp over the vocabulary, computed blockwise on chip while streaming
@@ -14,9 +14,11 @@
 // section "Contribution"; CCE paper summary "Cut Your Losses in
 // Large-Vocabulary Language Models", section "Approach").  The pages' kernel
 // merges partial results with a concurrent log-add-exp at block granularity
-// (summary, section "Limitations"); here the partials of each vocabulary split
-// go to a small [splits x rows] buffer and one ordered pass merges them, so
-// the result is independent of scheduling.
+// (summary, section "Limitations"); here the partials of each vocabulary range
+// go to a small buffer and one ordered pass merges them, so the result is
+// independent of scheduling.
+#include <algorithm>
+
 #include "cce_device.hpp"
 #include "cce_internal.hpp"
 
@@ -80,30 +82,42 @@ __global__ __launch_bounds__(1024) void k_check_labels(const int64_t *__restrict
 }
 
 // ------------------------------------------------------------ logit + LSE
-// Workgroup (split s, token tile rt) streams the vocabulary tiles of split s
-// through one continuous double-buffered K pipeline: the loads of the next
-// tile's first stage are in flight while the current tile's epilogue runs.
-// Each lane owns TN token columns; for each it keeps m (running max of
-// z log2 e) and l (running sum of 2^(z log2 e - m)) over the vocabulary rows
-// it holds.  At the end the two half-waves and the WM waves that hold the same
-// tokens are merged in a fixed order.
+// Work partition.  The units are the 256 x 256 logit tiles of the valid rows,
+// token-tile-major (u = rt * nvt + vt), U of them.  The grid is persistent
+// (as many workgroups as fit on the chip at once, G); logical workgroup L
+// takes units [L U / G, (L + 1) U / G), so every workgroup gets the same
+// number of tiles within one, whatever the shape and however many rows are
+// ignored.  A range covers a vocabulary range of one or more token tiles;
+// each (workgroup, token tile) pair is a segment and writes one partial
+// (m, s) per token at slot L + rt.  Slots are unique: along the partition L
+// and rt never decrease and one of them grows at each step.
 //
-// Placement: hardware workgroup b runs on XCD b % 8.  When the grid allows it,
-// the 32 workgroups an XCD holds at once are 8 splits x 4 token tiles, so each
-// classifier tile in flight is shared by 4 workgroups and each hidden-state
-// tile by 8, in that XCD's L2 (measured against 4 x 8, 2 x 16, 1 x 32 and no
-// grouping on the Gemma-2-2B head shape: best by 2-5 %).
-__device__ __forceinline__ void fwd_place(int b, int G, int S, int R, int &split, int &rt) {
-    if (G % 8 == 0 && S % 8 == 0 && R % 4 == 0) {
-        const int L = (b % 8) * (G / 8) + b / 8;  // consecutive L share an XCD
-        const int g = L / 32, w = L % 32;
-        const int sg = S / 8;
-        split = (g % sg) * 8 + (w % 8);
-        rt = (g / sg) * 4 + (w / 8);
-    } else {
-        split = b % S;
-        rt = b / S;
-    }
+// A segment streams its vocabulary tiles through one continuous double-
+// buffered K pipeline: the loads of the next tile's first stage are in flight
+// while the current tile's epilogue runs.  Each lane owns TN token columns;
+// for each it keeps m (running max of z log2 e) and l (running sum of
+// 2^(z log2 e - m)) over the vocabulary rows it holds.  At the end of a
+// segment the two half-waves and the WM waves that hold the same tokens are
+// merged in a fixed order.
+//
+// Placement: hardware workgroup b runs on XCD b % 8, and consecutive logical
+// workgroups are put on one XCD, so an XCD holds a contiguous eighth of the
+// units: at the Gemma-2-2B head shape 4 token tiles x 8 vocabulary ranges,
+// each classifier tile in flight shared by 4 workgroups and each hidden-state
+// tile by 8 in that XCD's L2 (measured against 2 x 16, 1 x 32 and no grouping:
+// best by 2-5 %).
+struct FwdPart {
+    int64_t U;  // units (tiles of the valid rows)
+    int G;      // workgroups
+    __device__ __forceinline__ int64_t start(int L) const { return (int64_t)L * U / G; }
+    // The workgroup whose range holds unit u: the largest L with start(L) <= u.
+    __device__ __forceinline__ int owner(int64_t u) const { return (int)(((u + 1) * G - 1) / U); }
+};
+
+__device__ __forceinline__ int fwd_logical(int b, int G) { return G % 8 == 0 ? (b % 8) * (G / 8) + b / 8 : b; }
+
+__device__ __forceinline__ FwdPart fwd_part(int nv, int n_vtiles, int G) {
+    return FwdPart{(int64_t)((nv + kTileRows - 1) / kTileRows) * n_vtiles, G};
 }
 
 // Returns the largest logit this lane holds in the tile (rows past V excluded).
@@ -192,11 +206,13 @@ __global__ __launch_bounds__(256) void k_bound_decode(int *__restrict__ t, int64
 }
 
 // Merges (m, l) over the two half-waves and the WM waves that hold the same
-// tokens, in a fixed order, and writes the split's partials for valid tokens.
+// tokens, in a fixed order, and writes the segment's partials for valid
+// tokens (slot-major, by token position inside the tile).  Ends with a
+// barrier: the LDS is free again when it returns.
 template <class TL>
 __device__ __forceinline__ void fwd_write_partials(float (&m)[TL::TN], float (&l)[TL::TN], float *red, int tok0,
-                                                   int nv, const int32_t *__restrict__ idx, int split, int64_t N,
-                                                   float *__restrict__ part_m, float *__restrict__ part_s) {
+                                                   int nv, int64_t slot, float *__restrict__ part_m,
+                                                   float *__restrict__ part_s) {
 #pragma unroll
     for (int tn = 0; tn < TL::TN; ++tn) {
         const float mo = __shfl_xor(m[tn], 32, 64);
@@ -228,28 +244,22 @@ __device__ __forceinline__ void fwd_write_partials(float (&m)[TL::TN], float (&l
         if (M != kNegInf)
             for (int w = 0; w < TL::WM; ++w)
                 L += red[(w * TL::BN + c) * 2 + 1] * __builtin_amdgcn_exp2f(red[(w * TL::BN + c) * 2] - M);
-        const int64_t row = idx[tok];
-        part_m[(int64_t)split * N + row] = M;
-        part_s[(int64_t)split * N + row] = L;
+        part_m[slot * TL::BN + c] = M;
+        part_s[slot * TL::BN + c] = L;
     }
+    __syncthreads();
 }
 
+// One segment on the VGPR-staged pipeline: token tile rt, vocabulary tiles
+// [t0, t0 + ntile), partials to slot.
 template <typename T>
-__global__ __launch_bounds__(TileF::kThreads) void k_fwd(
-    const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, int D, int V, int64_t N, int n_vtiles,
-    int S, int R, float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
+__device__ __forceinline__ void fwd_segment(const T *__restrict__ H, const T *__restrict__ E,
+                                            const int32_t *__restrict__ idx, int nv, const int32_t *__restrict__ perm,
+                                            int D, int V, int n_vtiles, int rt, int t0, int ntile, int64_t slot,
+                                            u32x4 *lds, float *__restrict__ part_m, float *__restrict__ part_s,
+                                            int *__restrict__ tbound) {
     using TL = TileF;
-    __shared__ u32x4 lds[TL::kLdsChunks];
-    const int nv = *nvalid_p;
-    int split, rt;
-    fwd_place(blockIdx.x, gridDim.x, S, R, split, rt);
     const int tok0 = rt * TL::BN;
-    if (tok0 >= nv) return;
-    const int t0 = (int)((int64_t)n_vtiles * split / S);
-    const int t1 = (int)((int64_t)n_vtiles * (split + 1) / S);
-    const int ntile = t1 - t0;
-    const int tid = threadIdx.x;
     const size_t rowb = (size_t)D * sizeof(T);
     const int kvalid = D * (int)sizeof(T);
     const int ns = (kvalid + TL::kStageBytes - 1) / TL::kStageBytes;
@@ -304,28 +314,44 @@ __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
         }
     }
 
-    fwd_write_partials<TL>(m, l, reinterpret_cast<float *>(lds), tok0, nv, idx, split, N, part_m, part_s);
+    fwd_write_partials<TL>(m, l, reinterpret_cast<float *>(lds), tok0, nv, slot, part_m, part_s);
 }
 
-// The same computation on the DMA pipeline (DmaEngine): 4 LDS stages of 64
-// K-bytes, 3 in flight.  Rows past the end of an operand are clamped to its
-// last row: their logits are finite and masked (vocabulary) or never
-// written (tokens).  Needs D * sizeof(T) to be a multiple of 64.
-template <typename T, class TL>
-__global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
+template <typename T>
+__global__ __launch_bounds__(TileF::kThreads) void k_fwd(
     const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, int D, int V, int64_t N, int n_vtiles,
-    int S, int R, float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
-    using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
-    __shared__ u32x4 lds[DE::kLdsChunks];
+    const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, int D, int V, int n_vtiles,
+    float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
+    __shared__ u32x4 lds[TileF::kLdsChunks];
     const int nv = *nvalid_p;
-    int split, rt;
-    fwd_place(blockIdx.x, gridDim.x, S, R, split, rt);
+    if (nv <= 0) return;
+    const int L = fwd_logical(blockIdx.x, gridDim.x);
+    const FwdPart P = fwd_part(nv, n_vtiles, gridDim.x);
+    const int64_t u1 = P.start(L + 1);
+    for (int64_t u = P.start(L); u < u1;) {
+        const int rt = (int)(u / n_vtiles);
+        const int t0 = (int)(u - (int64_t)rt * n_vtiles);
+        const int ntile = (int)min((int64_t)(n_vtiles - t0), u1 - u);
+        fwd_segment<T>(H, E, idx, nv, perm, D, V, n_vtiles, rt, t0, ntile, (int64_t)L + rt, lds, part_m, part_s,
+                       tbound);
+        u += ntile;
+    }
+}
+
+// The same computation on the DMA pipeline (DmaEngine): 2 LDS stages of 128
+// K-bytes, one in flight while the other is computed.  Rows past the end of
+// an operand are clamped to its last row: their logits are finite and masked
+// (vocabulary) or never written (tokens).  Needs D * sizeof(T) to be a
+// multiple of 128.
+template <typename T, class TL>
+__device__ __forceinline__ void fwd_segment_dma(const T *__restrict__ H, const T *__restrict__ E,
+                                                const int32_t *__restrict__ idx, int nv,
+                                                const int32_t *__restrict__ perm, int D, int V, int n_vtiles, int rt,
+                                                int t0, int ntile, int64_t slot, u32x4 *lds,
+                                                float *__restrict__ part_m, float *__restrict__ part_s,
+                                                int *__restrict__ tbound) {
+    using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
     const int tok0 = rt * TL::BN;
-    if (tok0 >= nv) return;
-    const int t0 = (int)((int64_t)n_vtiles * split / S);
-    const int t1 = (int)((int64_t)n_vtiles * (split + 1) / S);
-    const int ntile = t1 - t0;
     const size_t rowb = (size_t)D * sizeof(T);
     const int ns = D * (int)sizeof(T) / DE::kStageBytes;
     BoundSink bs{BoundSink::block_of<TL>(tbound, 2 * (int64_t)n_vtiles, rt, t0, nv)};
@@ -377,39 +403,76 @@ __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
             zero_acc<TL>(acc);
         }
     }
-    fwd_write_partials<TL>(m, l, reinterpret_cast<float *>(lds), tok0, nv, idx, split, N, part_m, part_s);
+    fwd_write_partials<TL>(m, l, reinterpret_cast<float *>(lds), tok0, nv, slot, part_m, part_s);
+}
+
+template <typename T, class TL>
+__global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
+    const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, int D, int V, int n_vtiles,
+    float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
+    using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
+    __shared__ u32x4 lds[DE::kLdsChunks];
+    const int nv = *nvalid_p;
+    if (nv <= 0) return;
+    const int L = fwd_logical(blockIdx.x, gridDim.x);
+    const FwdPart P = fwd_part(nv, n_vtiles, gridDim.x);
+    const int64_t u1 = P.start(L + 1);
+    for (int64_t u = P.start(L); u < u1;) {
+        const int rt = (int)(u / n_vtiles);
+        const int t0 = (int)(u - (int64_t)rt * n_vtiles);
+        const int ntile = (int)min((int64_t)(n_vtiles - t0), u1 - u);
+        fwd_segment_dma<T, TL>(H, E, idx, nv, perm, D, V, n_vtiles, rt, t0, ntile, (int64_t)L + rt, lds, part_m,
+                               part_s, tbound);
+        u += ntile;
+    }
 }
 
 // ------------------------------------------------------ merge + label gather
-// One wave per row.  Lane s reads split s's partial; the max and the scaled
-// sum are butterfly reductions (every lane ends with the same bits).
+// One wave per position w: it zeroes row w if that row is ignored, and if
+// w < nv it finishes the valid row at compacted position w.  The segments of
+// the row's token tile are those of the workgroups owner(first unit) ..
+// owner(last unit) whose range is not empty; lane j takes the j-th, (j+64)-th,
+// ... of them, and the max
+// and the scaled sum are butterfly reductions, so the result depends only on
+// the partition, never on scheduling.
 template <typename T>
 __global__ __launch_bounds__(256) void k_merge(const T *__restrict__ H, const T *__restrict__ E,
-                                               const int64_t *__restrict__ labels,
-                                               const float *__restrict__ part_m,
-                                               const float *__restrict__ part_s, int S, int64_t N,
-                                               int D, int64_t V, int64_t ignore_index, float *__restrict__ loss,
+                                               const int64_t *__restrict__ labels, const int32_t *__restrict__ idx,
+                                               const int32_t *__restrict__ nvalid_p,
+                                               const float *__restrict__ part_m, const float *__restrict__ part_s,
+                                               int G, int n_vtiles, int64_t N, int D, int64_t V,
+                                               int64_t ignore_index, float *__restrict__ loss,
                                                float *__restrict__ lse) {
     const int lane = threadIdx.x & 63;
-    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (i >= N) return;
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w >= N) return;
+    if (labels[w] == ignore_index && lane == 0) { loss[w] = 0.f; lse[w] = 0.f; }
+    const int nv = *nvalid_p;
+    if (w >= nv) return;
+    const int64_t i = idx[w];
     const int64_t y = labels[i];
-    if (y == ignore_index) {
-        if (lane == 0) { loss[i] = 0.f; lse[i] = 0.f; }
-        return;
-    }
     if (y < 0 || y >= V) {  // not a valid label: undefined by contract; flag it, touch nothing
         if (lane == 0) { loss[i] = __builtin_nanf(""); lse[i] = __builtin_nanf(""); }
         return;
     }
-    const float pm = lane < S ? part_m[(int64_t)lane * N + i] : kNegInf;
-    const float ps = lane < S ? part_s[(int64_t)lane * N + i] : 0.f;
-    float M = pm;
+    const int rt = (int)(w / kTileRows), c = (int)(w % kTileRows);
+    const FwdPart P = fwd_part(nv, n_vtiles, G);
+    const int L0 = P.owner((int64_t)rt * n_vtiles), L1 = P.owner((int64_t)rt * n_vtiles + n_vtiles - 1);
+    // (with fewer units than workgroups some ranges are empty: no segment)
+    float M = kNegInf;
+    for (int L = L0 + lane; L <= L1; L += 64)
+        if (P.start(L) < P.start(L + 1)) M = fmaxf(M, part_m[((int64_t)L + rt) * kTileRows + c]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    float L = (pm == kNegInf) ? 0.f : ps * __builtin_amdgcn_exp2f(pm - M);
+    float S = 0.f;
+    for (int L = L0 + lane; L <= L1; L += 64) {
+        if (P.start(L) == P.start(L + 1)) continue;
+        const float pm = part_m[((int64_t)L + rt) * kTileRows + c];
+        if (pm != kNegInf) S += part_s[((int64_t)L + rt) * kTileRows + c] * __builtin_amdgcn_exp2f(pm - M);
+    }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+    for (int o = 32; o > 0; o >>= 1) S += __shfl_xor(S, o, 64);
 
     // z_{i, y_i} = <h_i, e_{y_i}>, fp32 accumulation of exact products.
     constexpr int CE = ChunkElems<T>::value;
@@ -427,7 +490,7 @@ __global__ __launch_bounds__(256) void k_merge(const T *__restrict__ H, const T 
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
     if (lane == 0) {
-        const float l = (M + log2f(L)) * kLn2;
+        const float l = (M + log2f(S)) * kLn2;
         lse[i] = l;
         loss[i] = l - dot;
     }
@@ -441,12 +504,6 @@ FwdShape fwd_shape(int64_t N, int64_t D, int64_t V) {
     s.V = V;
     s.n_vtiles = (int)ceil_div(V, kTileVocab);
     s.n_rtiles = (int)ceil_div(N, kTileRows);
-    int S = (int)ceil_div(kFwdTargetGroups, s.n_rtiles);
-    if (S > kMaxSplits) S = kMaxSplits;
-    if (S > 8) S &= ~7;  // a multiple of 8 lets the XCD placement group splits
-    if (S > s.n_vtiles) S = s.n_vtiles;
-    if (S < 1) S = 1;
-    s.S = S;
     return s;
 }
 
@@ -455,8 +512,9 @@ FwdWs fwd_ws(void *ws, const FwdShape &s, size_t *bytes) {
     FwdWs w;
     w.idx = c.take<int32_t>(s.N);
     w.nvalid = c.take<int32_t>(1);
-    w.part_m = c.take<float>((size_t)s.S * s.N);
-    w.part_s = c.take<float>((size_t)s.S * s.N);
+    // slots L + rt < G + n_rtiles, one partial per token of the tile each
+    w.part_m = c.take<float>((size_t)(kFwdMaxGroups + s.n_rtiles) * kTileRows);
+    w.part_s = c.take<float>((size_t)(kFwdMaxGroups + s.n_rtiles) * kTileRows);
     if (bytes) *bytes = c.off;
     return w;
 }
@@ -485,16 +543,28 @@ static hipError_t forward_t(const T *H, const T *E, const int64_t *labels, const
         hipLaunchKernelGGL(k_bound_init, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, st, tb, nb);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int groups = s.S * s.n_rtiles;
-    if ((s.D * (int64_t)sizeof(T)) % kLogitRowBytes == 0)
-        hipLaunchKernelGGL((k_fwd_dma<T, TileFD>), dim3(groups), dim3(TileFD::kThreads), 0, st, H, E, w.idx, w.nvalid,
-                           perm, (int)s.D, (int)s.V, s.N, s.n_vtiles, s.S, s.n_rtiles, w.part_m, w.part_s, tb);
+    // A persistent grid: as many workgroups as are resident at once (every
+    // one gets the same share of tiles), at most one per tile.
+    const bool dma = (s.D * (int64_t)sizeof(T)) % kLogitRowBytes == 0;
+    int dev = 0, cus = 0, per_cu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    e = dma ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fwd_dma<T, TileFD>, TileFD::kThreads, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fwd<T>, TileF::kThreads, 0);
+    if (e != hipSuccess) return e;
+    int64_t G = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
+    G = std::min<int64_t>(std::min<int64_t>(G, kFwdMaxGroups), (int64_t)s.n_rtiles * s.n_vtiles);
+    if (G >= 8) G &= ~7;  // lets the placement give each XCD a contiguous eighth
+    if (dma)
+        hipLaunchKernelGGL((k_fwd_dma<T, TileFD>), dim3((unsigned)G), dim3(TileFD::kThreads), 0, st, H, E, w.idx,
+                           w.nvalid, perm, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb);
     else
-        hipLaunchKernelGGL(k_fwd<T>, dim3(groups), dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid, perm,
-                           (int)s.D, (int)s.V, s.N, s.n_vtiles, s.S, s.n_rtiles, w.part_m, w.part_s, tb);
+        hipLaunchKernelGGL(k_fwd<T>, dim3((unsigned)G), dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid, perm,
+                           (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_merge<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, H, E, labels,
-                       w.part_m, w.part_s, s.S, s.N, (int)s.D, s.V, ignore_index, loss, lse);
+    hipLaunchKernelGGL(k_merge<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, H, E, labels, w.idx,
+                       w.nvalid, w.part_m, w.part_s, (int)G, s.n_vtiles, s.N, (int)s.D, s.V, ignore_index, loss,
+                       lse);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (tb) hipLaunchKernelGGL(k_bound_decode, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, st, tb, nb);
     return hipGetLastError();
