@@ -190,3 +190,50 @@ def lse_matmul(H64, E64, labels, ignore_index=-100, row_chunk=512):
     out[np.asarray(labels) == ignore_index] = 0.0
     return out
 
+
+
+def composite(H64, E0, E1, off1, labels, dloss, ignore_index=-100):
+    """Composite head (the lit note "The loss and the mask: Cut Cross-Entropy +
+    FlexAttention", section "What transfers to us"): ids [0, V0) are rows of
+    E0, ids [off1, off1 + V1) rows of E1, the ids between have no row.  The
+    log-sum-exp is composed over the two blocks with logaddexp (the gap adds
+    exp(-inf) = 0), the label logit comes from the block that holds the label,
+    and the gradient of each block uses the composed lse.
+    Returns loss, lse [N], dH [N, D], dE0 [V0, D], dE1 [V1, D] (fp64); ignored
+    rows get 0 and add nothing.  Matrix products are numpy's (float64)."""
+    H64, E0, E1 = _c64(H64), _c64(E0), _c64(E1)
+    labels = np.asarray(labels, dtype=np.int64)
+    dloss = np.asarray(dloss, dtype=np.float64)
+    N = H64.shape[0]
+    V0, V1 = E0.shape[0], E1.shape[0]
+    if off1 < V0:
+        raise ValueError("the second block must start at or after the end of the first")
+    valid = labels != ignore_index
+    in0 = valid & (labels >= 0) & (labels < V0)
+    in1 = valid & (labels >= off1) & (labels < off1 + V1)
+    if np.any(valid & ~in0 & ~in1):
+        raise ValueError("a label outside both blocks (in the gap or past the end)")
+    Z0 = H64 @ E0.T
+    Z1 = H64 @ E1.T
+    m0 = Z0.max(axis=1)
+    m1 = Z1.max(axis=1)
+    lse0 = m0 + np.log(np.exp(Z0 - m0[:, None]).sum(axis=1))
+    lse1 = m1 + np.log(np.exp(Z1 - m1[:, None]).sum(axis=1))
+    lse = np.logaddexp(lse0, lse1)
+    zy = np.zeros(N)
+    rows = np.arange(N)
+    zy[in0] = Z0[rows[in0], labels[in0]]
+    zy[in1] = Z1[rows[in1], labels[in1] - off1]
+    loss = np.where(valid, lse - zy, 0.0)
+    lse = np.where(valid, lse, 0.0)
+    w = np.where(valid, dloss, 0.0)
+    G0 = w[:, None] * np.exp(Z0 - lse[:, None])
+    G1 = w[:, None] * np.exp(Z1 - lse[:, None])
+    G0[~valid] = 0.0
+    G1[~valid] = 0.0
+    G0[rows[in0], labels[in0]] -= w[in0]
+    G1[rows[in1], labels[in1] - off1] -= w[in1]
+    dH = G0 @ E0 + G1 @ E1
+    dE0 = G0.T @ H64
+    dE1 = G1.T @ H64
+    return loss, lse, dH, dE0, dE1
