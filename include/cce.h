@@ -165,6 +165,37 @@ cce_status cce_backward(const void *H, const void *E, const int64_t *labels,
                         void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Composite head (the lit note's "What transfers to us": a base classifier
+ * plus a second block of rows placed at an id offset, with a dead gap
+ * between them; the log-sum-exp is composed over the two blocks and the gap
+ * contributes nothing).  Ids [0, V0) are rows of E0 [V0, D]; ids
+ * [off1, off1 + V1) are rows of E1 [V1, D]; ids in [V0, off1) have no row
+ * (logit -inf) and are never a valid label.  Requires V0, V1 >= 1 and
+ * off1 >= V0.  The kernels see one vocabulary of V = V0 + V1 entries (E0's
+ * rows, then E1's): workspace queries, cce_block_max_elems and perm
+ * (int32 [V0 + V1]) take that V, and perm / keys index that space (entry
+ * V0 + j is row j of E1).  Labels keep the caller's ids.  Everything else is
+ * as for cce_forward / cce_vocab_order / cce_backward; dE0 [V0, D] and
+ * dE1 [V1, D] receive the gradients of the two blocks.  A label in the gap
+ * or past the second block gets loss = lse = NaN (undefined, as any label
+ * out of range).
+ */
+cce_status cce_forward_composite(const void *H, const void *E0, int64_t V0, const void *E1, int64_t V1,
+                                 int64_t off1, const int64_t *labels, int64_t N, int64_t D, cce_dtype dtype,
+                                 int64_t ignore_index, const int32_t *perm, float *loss, float *lse,
+                                 float *block_max, void *ws, size_t ws_bytes, void *stream);
+cce_status cce_vocab_order_composite(const void *H, const void *E0, int64_t V0, const void *E1, int64_t V1,
+                                     const int64_t *labels, int64_t N, int64_t D, cce_dtype dtype,
+                                     int64_t ignore_index, int32_t *perm, float *keys, void *ws, size_t ws_bytes,
+                                     void *stream);
+cce_status cce_backward_composite(const void *H, const void *E0, int64_t V0, const void *E1, int64_t V1,
+                                  int64_t off1, const int64_t *labels, const float *lse, const float *dloss,
+                                  const float *block_max, int64_t N, int64_t D, cce_dtype dtype,
+                                  int64_t ignore_index, float filter_eps, const int32_t *perm, unsigned flags,
+                                  void *dH, void *dE0, void *dE1, int64_t *stats, void *ws, size_t ws_bytes,
+                                  void *stream);
+
+/*
  * Debug check of the labels: *n_bad (device int64) receives the number of rows
  * whose label is neither ignore_index nor in [0, V).
  */

@@ -33,6 +33,7 @@ EXPORTS = (
     "cce_status_string", "cce_version", "cce_filter_block",
     "cce_forward_workspace_bytes", "cce_backward_workspace_bytes", "cce_vocab_order_workspace_bytes",
     "cce_block_max_elems", "cce_forward", "cce_vocab_order", "cce_backward", "cce_check_labels",
+    "cce_forward_composite", "cce_vocab_order_composite", "cce_backward_composite",
 )
 
 
@@ -75,6 +76,16 @@ def lib() -> ctypes.CDLL:
     L.cce_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _i64, ctypes.c_float,
                                _vp, ctypes.c_uint, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.cce_backward.restype = ctypes.c_int
+    L.cce_forward_composite.argtypes = [_vp, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, ctypes.c_int, _i64, _vp,
+                                        _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.cce_forward_composite.restype = ctypes.c_int
+    L.cce_vocab_order_composite.argtypes = [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _i64, ctypes.c_int, _i64, _vp,
+                                            _vp, _vp, ctypes.c_size_t, _vp]
+    L.cce_vocab_order_composite.restype = ctypes.c_int
+    L.cce_backward_composite.argtypes = [_vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _i64,
+                                         ctypes.c_int, _i64, ctypes.c_float, _vp, ctypes.c_uint, _vp, _vp, _vp, _vp,
+                                         _vp, ctypes.c_size_t, _vp]
+    L.cce_backward_composite.restype = ctypes.c_int
     L.cce_check_labels.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp]
     L.cce_check_labels.restype = ctypes.c_int
     _lib = L
@@ -229,6 +240,79 @@ def cce_backward(H, E, labels, lse, dloss, filter_eps=2.0 ** -12, ignore_index=-
                            ws.numel() * ws.element_size(), _stream(stream))
     _check("cce_backward", s)
     return dH, dE
+
+
+def _composite_shapes(H, E0, E1, labels):
+    N, D, V0 = _shapes(H, E0, labels)
+    _, _, V1 = _shapes(H, E1, labels)
+    return N, D, V0, V1
+
+
+def cce_forward_composite(H, E0, E1, off1, labels, ignore_index=-100, loss=None, lse=None, block_max=None, ws=None,
+                          stream=None, perm=None):
+    """loss, lse (fp32 [N]) of a composite head: ids [0, V0) are rows of E0,
+    ids [off1, off1 + V1) rows of E1, the ids between them have no row.
+    block_max / perm are over the V0 + V1 rows (E0's, then E1's)."""
+    import torch
+    N, D, V0, V1 = _composite_shapes(H, E0, E1, labels)
+    V = V0 + V1
+    dt = _dtype_code(H)
+    _check_perm(perm, V)
+    loss = torch.empty(N, dtype=torch.float32, device=H.device) if loss is None else loss
+    lse = torch.empty(N, dtype=torch.float32, device=H.device) if lse is None else lse
+    if block_max is not None and (block_max.dtype != torch.float32 or
+                                  block_max.numel() < block_max_elems(N, V) or not block_max.is_contiguous()):
+        raise ValueError(f"block_max must be contiguous fp32 with at least {block_max_elems(N, V)} entries")
+    ws = _workspace(forward_workspace_bytes(N, D, V, dt), H.device, ws)
+    s = lib().cce_forward_composite(_ptr(H), _ptr(E0), V0, _ptr(E1), V1, int(off1), _ptr(labels), N, D, dt,
+                                    int(ignore_index), _ptr(perm), _ptr(loss), _ptr(lse), _ptr(block_max), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream))
+    _check("cce_forward_composite", s)
+    return loss, lse
+
+
+def cce_vocab_order_composite(H, E0, E1, labels, ignore_index=-100, perm=None, keys=None, want_keys=False, ws=None,
+                              stream=None):
+    """perm (int32 [V0 + V1]) over E0's rows then E1's, by descending mean logit."""
+    import torch
+    N, D, V0, V1 = _composite_shapes(H, E0, E1, labels)
+    V = V0 + V1
+    dt = _dtype_code(H)
+    perm = torch.empty(V, dtype=torch.int32, device=H.device) if perm is None else perm
+    _check_perm(perm, V)
+    if want_keys and keys is None:
+        keys = torch.empty(V, dtype=torch.float32, device=H.device)
+    ws = _workspace(vocab_order_workspace_bytes(N, D, V, dt), H.device, ws)
+    s = lib().cce_vocab_order_composite(_ptr(H), _ptr(E0), V0, _ptr(E1), V1, _ptr(labels), N, D, dt,
+                                        int(ignore_index), _ptr(perm), _ptr(keys), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream))
+    _check("cce_vocab_order_composite", s)
+    return (perm, keys) if want_keys else perm
+
+
+def cce_backward_composite(H, E0, E1, off1, labels, lse, dloss, filter_eps=2.0 ** -12, ignore_index=-100, perm=None,
+                           flags=0, dH=None, dE0=None, dE1=None, stats=None, ws=None, stream=None, block_max=None):
+    """dH [N, D], dE0 [V0, D], dE1 [V1, D] of sum_i dloss_i loss_i for a
+    composite head (see cce_forward_composite)."""
+    import torch
+    N, D, V0, V1 = _composite_shapes(H, E0, E1, labels)
+    V = V0 + V1
+    dt = _dtype_code(H)
+    _check_perm(perm, V)
+    dH = torch.empty_like(H) if dH is None else dH
+    dE0 = torch.empty_like(E0) if dE0 is None else dE0
+    dE1 = torch.empty_like(E1) if dE1 is None else dE1
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < 5):
+        raise ValueError("stats must be int64 with at least 5 entries")
+    if block_max is not None and (block_max.dtype != torch.float32 or block_max.numel() < block_max_elems(N, V)):
+        raise ValueError(f"block_max must be fp32 with at least {block_max_elems(N, V)} entries")
+    ws = _workspace(backward_workspace_bytes(N, D, V, dt), H.device, ws)
+    s = lib().cce_backward_composite(_ptr(H), _ptr(E0), V0, _ptr(E1), V1, int(off1), _ptr(labels), _ptr(lse),
+                                     _ptr(dloss), _ptr(block_max), N, D, dt, int(ignore_index), float(filter_eps),
+                                     _ptr(perm), int(flags), _ptr(dH), _ptr(dE0), _ptr(dE1), _ptr(stats), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream))
+    _check("cce_backward_composite", s)
+    return dH, dE0, dE1
 
 
 def cce_check_labels(labels, V, ignore_index=-100, stream=None) -> int:

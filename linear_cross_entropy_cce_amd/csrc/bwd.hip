@@ -87,7 +87,8 @@ struct BwdArgs {
     const int32_t *tlist;
     const uint8_t *tneed;
     int n_rt;
-    const T *H, *E, *Ht;
+    const T *H, *Ht;
+    Rows2<const T> E;  // classifier rows in processing space (one matrix or two blocks)
     int64_t ldh;  // Np
     const int32_t *idx, *nvalid, *perm, *inv_perm;
     const int64_t *labels;
@@ -101,7 +102,8 @@ struct BwdArgs {
     int32_t *slot;
     int64_t *stats;
     float *dh_acc;
-    T *dE, *dH;
+    Rows2<T> dE;  // same layout as E
+    T *dH;
 };
 
 // ------------------------------------------------------------ small kernels
@@ -500,7 +502,7 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
 // computed: the halves of A and B no such block uses are not loaded and the
 // waves of the other blocks skip their MFMAs.
 template <typename T, class TL>
-__device__ __forceinline__ void recompute_dma(const T *__restrict__ H, const T *__restrict__ E,
+__device__ __forceinline__ void recompute_dma(const T *__restrict__ H, Rows2<const T> E,
                                               const int32_t *__restrict__ idx, int nv,
                                               const int32_t *__restrict__ perm, int D, int V, int tok0, int p0,
                                               int qmask, u32x4 *lds, f32x16 (&acc)[TL::TM][TL::TN]) {
@@ -515,7 +517,7 @@ __device__ __forceinline__ void recompute_dma(const T *__restrict__ H, const T *
         const int pos = min(p0 + r, V - 1);
         int vid = perm ? perm[pos] : pos;
         vid = (vid >= 0 && vid < V) ? vid : 0;
-        eng.pa[j] = reinterpret_cast<const char *>(E) + (size_t)vid * rowb + DE::chunk_off(j, r, tid);
+        eng.pa[j] = reinterpret_cast<const char *>(E.row(vid)) + DE::chunk_off(j, r, tid);
     }
 #pragma unroll
     for (int j = 0; j < DE::NIB; ++j) {
@@ -544,7 +546,7 @@ __device__ __forceinline__ void recompute_dma(const T *__restrict__ H, const T *
 // The same on the VGPR-staged engine (any D % 8 == 0), as the forward's
 // fallback kernel computes it.
 template <typename T, class TL>
-__device__ __forceinline__ void recompute_vgpr(const T *__restrict__ H, const T *__restrict__ E,
+__device__ __forceinline__ void recompute_vgpr(const T *__restrict__ H, Rows2<const T> E,
                                                const int32_t *__restrict__ idx, int nv,
                                                const int32_t *__restrict__ perm, int D, int V, int tok0, int p0,
                                                u32x4 *lds, f32x16 (&acc)[TL::TM][TL::TN]) {
@@ -556,7 +558,7 @@ __device__ __forceinline__ void recompute_vgpr(const T *__restrict__ H, const T 
     for (int j = 0; j < Engine<T, TL>::NA; ++j) {
         const int pos = p0 + eng.row(j);
         const int vid = pos < V ? (perm ? perm[pos] : pos) : -1;
-        eng.pa[j] = (vid >= 0 && vid < V) ? reinterpret_cast<const char *>(E) + (size_t)vid * rowb : nullptr;
+        eng.pa[j] = (vid >= 0 && vid < V) ? reinterpret_cast<const char *>(E.row(vid)) : nullptr;
     }
 #pragma unroll
     for (int j = 0; j < Engine<T, TL>::NB; ++j) {
@@ -683,8 +685,8 @@ struct DhEngine {
 
     // Stage kq of the block with store slot `slot` and first vocabulary
     // position pos0, into LDS buffer buf.
-    __device__ __forceinline__ void issue(int buf, const T *Gn, int64_t slot, const T *E, const int32_t *perm,
-                                          int pos0, int kq, int V, size_t rowb) const {
+    __device__ __forceinline__ void issue(int buf, const T *Gn, int64_t slot, const Rows2<const T> &E,
+                                          const int32_t *perm, int pos0, int kq, int V) const {
         const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const uint32_t st = lds0 + (uint32_t)(buf * kStage) * 16u;
         dma16_at(reinterpret_cast<const char *>(Gn + slot * kBlockElems) + a_off + kq * kStageBytes, st + 1024u * w);
@@ -693,7 +695,7 @@ struct DhEngine {
             const int pos = pos0 + kq * kKv + b_row[j];
             int vid = pos < V ? (perm ? perm[pos] : pos) : V - 1;
             vid = (vid >= 0 && vid < V) ? vid : 0;
-            dma16_at(reinterpret_cast<const char *>(E) + (size_t)vid * rowb + b_off[j],
+            dma16_at(reinterpret_cast<const char *>(E.row(vid)) + b_off[j],
                      st + 16u * kStageA + 1024u * (j * TL::kWaves + w));
         }
     }
@@ -777,7 +779,7 @@ template <typename T, bool KAHAN>
 __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb, const uint8_t *__restrict__ st,
                                         const int32_t *__restrict__ slotm, int cbp, const T *__restrict__ Gt,
                                         const T *__restrict__ Ht, int64_t ldh, const int32_t *__restrict__ perm,
-                                        int D, int V, T *__restrict__ dE) {
+                                        int D, int V, Rows2<T> dE) {
     using TL = TileG;
     using DE = DmaEngine<T, TL>;
     constexpr int kBlockBytes = kBlockRows * (int)sizeof(T);  // K bytes of one row block
@@ -850,7 +852,7 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
             const int row = q / kSeg, d = d0 + (q % kSeg) * CE;
             const int pos = cb * TL::BM + row;
             const int v = pos < V ? (perm ? perm[pos] : pos) : -1;
-            if (v >= 0 && v < V && d < D) *reinterpret_cast<u32x4 *>(dE + (int64_t)v * D + d) = z;
+            if (v >= 0 && v < V && d < D) *reinterpret_cast<u32x4 *>(dE.row(v) + d) = z;
         }
         return;
     }
@@ -875,7 +877,7 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
             const int pos = cb * TL::BM + row;
             const int v = pos < V ? (perm ? perm[pos] : pos) : -1;
             if (v >= 0 && v < V && d < D)
-                *reinterpret_cast<u32x4 *>(dE + (int64_t)v * D + d) =
+                *reinterpret_cast<u32x4 *>(dE.row(v) + d) =
                     *reinterpret_cast<const u32x4 *>(tile + row * kLd + c * CE);
         }
         __syncthreads();  // the stages are reused by the next item
@@ -897,7 +899,7 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float val = KAHAN ? sum[tm][tn][r] - comp[tm][tn][r] : acc[tm][tn][r];
-                    if (vid[tm][r] >= 0 && d < D) dE[(int64_t)vid[tm][r] * D + d] = from_f32<T>(val);
+                    if (vid[tm][r] >= 0 && d < D) dE.row(vid[tm][r])[d] = from_f32<T>(val);
                 }
             }
     }
@@ -913,12 +915,11 @@ template <typename T>
 __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool multi, bool last, int cb0, int cb1,
                                         const uint8_t *__restrict__ st, const int32_t *__restrict__ slotm, int cbp,
                                         int nv, const int32_t *__restrict__ idx, const T *__restrict__ Gn,
-                                        const T *__restrict__ E, const int32_t *__restrict__ perm, int D, int V,
+                                        Rows2<const T> E, const int32_t *__restrict__ perm, int D, int V,
                                         float *__restrict__ dh_acc, T *__restrict__ dH) {
     using TL = TileG;
     using DH = DhEngine<T>;
     const int tok0 = rb * TL::BM;
-    const size_t rowb = (size_t)D * sizeof(T);
     const int tid = opaque_tid();  // per-item lane arithmetic is redone per item, not held in registers
 
     f32x16 acc[TL::TM][TL::TN], sum[TL::TM][TL::TN];
@@ -950,7 +951,7 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
         const int total = n * DH::kSpb;
         auto issue = [&](int buf, int q) {
             const int b = q / DH::kSpb;
-            eng.issue(buf, Gn, sh.lslot[b], E, perm, (base + sh.list[b]) * kBlockVocab, q % DH::kSpb, V, rowb);
+            eng.issue(buf, Gn, sh.lslot[b], E, perm, (base + sh.list[b]) * kBlockVocab, q % DH::kSpb, V);
         };
 #pragma unroll
         for (int q = 0; q < DH::kDepth; ++q)
@@ -1127,9 +1128,9 @@ static hipError_t fill_bytes_zero(void *p, size_t nbytes, hipStream_t st) {
 }
 
 template <typename T>
-static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, const float *lse,
+static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels, const float *lse,
                              const float *dloss, const float *block_max, const BwdShape &s, int64_t ignore_index,
-                             float eps, const int32_t *perm, unsigned flags, T *dH, T *dE, int64_t *stats,
+                             float eps, const int32_t *perm, unsigned flags, T *dH, Rows2<T> dE, int64_t *stats,
                              const BwdWs &w, hipStream_t st) {
     const int D = (int)s.D, V = (int)s.V;
     CCE_TRY(launch_compact(labels, s.N, ignore_index, w.idx, w.nvalid, st));
@@ -1237,17 +1238,26 @@ static hipError_t backward_t(const T *H, const T *E, const int64_t *labels, cons
     return hipSuccess;
 }
 
-hipError_t launch_backward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
+template <typename T>
+static Rows2<const T> rows_in(const VocabRows &E, int64_t D) {
+    return Rows2<const T>{static_cast<const T *>(E.e0), static_cast<const T *>(E.e1), E.v0, D};
+}
+template <typename T>
+static Rows2<T> rows_out(const VocabGrads &dE, int64_t D) {
+    return Rows2<T>{static_cast<T *>(dE.d0), static_cast<T *>(dE.d1), dE.v0, D};
+}
+
+hipError_t launch_backward(cce_dtype dt, const void *H, const VocabRows &E, const int64_t *labels,
                            const float *lse, const float *dloss, const float *block_max, const BwdShape &s,
                            int64_t ignore_index, float eps, const int32_t *perm, unsigned flags,
-                           void *dH, void *dE, int64_t *stats, const BwdWs &w, hipStream_t st) {
+                           void *dH, const VocabGrads &dE, int64_t *stats, const BwdWs &w, hipStream_t st) {
     if (dt == CCE_BF16)
-        return backward_t<bf16_t>(static_cast<const bf16_t *>(H), static_cast<const bf16_t *>(E), labels, lse,
-                                  dloss, block_max, s, ignore_index, eps, perm, flags, static_cast<bf16_t *>(dH),
-                                  static_cast<bf16_t *>(dE), stats, w, st);
-    return backward_t<float>(static_cast<const float *>(H), static_cast<const float *>(E), labels, lse, dloss,
-                             block_max, s, ignore_index, eps, perm, flags, static_cast<float *>(dH),
-                             static_cast<float *>(dE), stats, w, st);
+        return backward_t<bf16_t>(static_cast<const bf16_t *>(H), rows_in<bf16_t>(E, s.D), labels, lse, dloss,
+                                  block_max, s, ignore_index, eps, perm, flags, static_cast<bf16_t *>(dH),
+                                  rows_out<bf16_t>(dE, s.D), stats, w, st);
+    return backward_t<float>(static_cast<const float *>(H), rows_in<float>(E, s.D), labels, lse, dloss, block_max,
+                             s, ignore_index, eps, perm, flags, static_cast<float *>(dH), rows_out<float>(dE, s.D),
+                             stats, w, st);
 }
 
 }  // namespace cce

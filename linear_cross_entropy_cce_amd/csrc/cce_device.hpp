@@ -78,6 +78,18 @@ template <> struct ChunkElems<bf16_t> { static constexpr int value = 8; };
 //        lane's chunk: k = 4 (2 kk + l / 32) + j, so the four cover the slice.
 template <typename T> struct Mfma;
 
+// Row v of a classifier (or of its gradient) held as one matrix or as the two
+// row blocks of a composite head: rows v < v0 in the first block, the others
+// at v - v0 in the second.  ld = elements per row.
+template <typename P>
+struct Rows2 {
+    P *r0;
+    P *r1;
+    int64_t v0;
+    int64_t ld;
+    __device__ __forceinline__ P *row(int64_t v) const { return v < v0 ? r0 + v * ld : r1 + (v - v0) * ld; }
+};
+
 template <> struct Mfma<bf16_t> {
     static __device__ __forceinline__ void step(const u32x4 &a, const u32x4 &b, f32x16 &acc) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),

@@ -25,10 +25,23 @@ constexpr int kBlockRows = 128;
 constexpr int kStoreVocab = 8192;
 // Workgroups of the persistent backward kernels.
 constexpr int kPassGroups = 256;
-// Upper bound on the forward's vocabulary splits (merged per row in order).
 // Most workgroups of the forward's persistent grid (its partial buffers are
 // sized for this many).
 constexpr int kFwdMaxGroups = 1024;
+
+// The classifier as the kernels see it: rows 0 .. V-1 of the processing
+// space, held by one matrix (e1 == e0, v0 >= V) or by the two row blocks of a
+// composite head (row v < v0 in the first block, v - v0 in the second).  The
+// gradients dE have the same two-block layout.
+struct VocabRows {
+    const void *e0, *e1;
+    int64_t v0;
+};
+struct VocabGrads {
+    void *d0, *d1;
+    int64_t v0;
+};
+constexpr int64_t kOneBlock = INT64_MAX;  // v0 of a one-matrix classifier
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -122,14 +135,16 @@ hipError_t launch_compact(const int64_t *labels, int64_t N, int64_t ignore_index
                           int32_t *nvalid, hipStream_t st);
 hipError_t launch_check_labels(const int64_t *labels, int64_t N, int64_t V, int64_t ignore_index,
                                int64_t *n_bad, hipStream_t st);
-hipError_t launch_forward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
+hipError_t launch_seg_labels(const int64_t *labels, int64_t N, int64_t ignore_index, int64_t V0, int64_t off1,
+                             int64_t V1, int64_t *out, hipStream_t st);
+hipError_t launch_forward(cce_dtype dt, const void *H, const VocabRows &E, const int64_t *labels,
                           const FwdShape &s, int64_t ignore_index, const int32_t *perm, const FwdWs &w,
                           float *loss, float *lse, float *block_max, hipStream_t st);
-hipError_t launch_backward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
+hipError_t launch_backward(cce_dtype dt, const void *H, const VocabRows &E, const int64_t *labels,
                            const float *lse, const float *dloss, const float *block_max, const BwdShape &s,
                            int64_t ignore_index, float eps, const int32_t *perm, unsigned flags,
-                           void *dH, void *dE, int64_t *stats, const BwdWs &w, hipStream_t st);
-hipError_t launch_vocab_order(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
+                           void *dH, const VocabGrads &dE, int64_t *stats, const BwdWs &w, hipStream_t st);
+hipError_t launch_vocab_order(cce_dtype dt, const void *H, const VocabRows &E, const int64_t *labels,
                               int64_t N, int64_t D, int64_t V, int64_t ignore_index, int32_t *perm,
                               float *keys_out, const SortWs &w, hipStream_t st);
 

@@ -81,6 +81,24 @@ __global__ __launch_bounds__(1024) void k_check_labels(const int64_t *__restrict
     }
 }
 
+// ------------------------------------------------------ composite labels
+// Labels of a composite head (ids [0, V0) in the first block, [off1, off1 +
+// V1) in the second, nothing in between) -> positions of the concatenated
+// processing space [0, V0 + V1).  ignore_index stays; any other id outside
+// both blocks becomes V0 + V1, which every kernel treats as out of range.
+__global__ __launch_bounds__(256) void k_seg_labels(const int64_t *__restrict__ labels, int64_t N,
+                                                    int64_t ignore_index, int64_t V0, int64_t off1, int64_t V1,
+                                                    int64_t *__restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= N) return;
+    const int64_t y = labels[i];
+    int64_t v = V0 + V1;
+    if (y == ignore_index) v = y;
+    else if (y >= 0 && y < V0) v = y;
+    else if (y >= off1 && y < off1 + V1) v = V0 + (y - off1);
+    out[i] = v;
+}
+
 // ------------------------------------------------------------ logit + LSE
 // Work partition.  The units are the 256 x 256 logit tiles of the valid rows,
 // token-tile-major (u = rt * nvt + vt), U of them.  The grid is persistent
@@ -253,7 +271,7 @@ __device__ __forceinline__ void fwd_write_partials(float (&m)[TL::TN], float (&l
 // One segment on the VGPR-staged pipeline: token tile rt, vocabulary tiles
 // [t0, t0 + ntile), partials to slot.
 template <typename T>
-__device__ __forceinline__ void fwd_segment(const T *__restrict__ H, const T *__restrict__ E,
+__device__ __forceinline__ void fwd_segment(const T *__restrict__ H, Rows2<const T> E,
                                             const int32_t *__restrict__ idx, int nv, const int32_t *__restrict__ perm,
                                             int D, int V, int n_vtiles, int rt, int t0, int ntile, int64_t slot,
                                             u32x4 *lds, float *__restrict__ part_m, float *__restrict__ part_s,
@@ -277,7 +295,7 @@ __device__ __forceinline__ void fwd_segment(const T *__restrict__ H, const T *__
         for (int j = 0; j < Engine<T, TL>::NA; ++j) {
             const int pos = v0 + eng.row(j);
             const int v = pos < V ? (perm ? perm[pos] : pos) : -1;
-            eng.pa[j] = (v >= 0 && v < V) ? reinterpret_cast<const char *>(E) + (size_t)v * rowb : nullptr;
+            eng.pa[j] = (v >= 0 && v < V) ? reinterpret_cast<const char *>(E.row(v)) : nullptr;
         }
     };
 
@@ -319,7 +337,7 @@ __device__ __forceinline__ void fwd_segment(const T *__restrict__ H, const T *__
 
 template <typename T>
 __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
-    const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
+    const T *__restrict__ H, Rows2<const T> E, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, int D, int V, int n_vtiles,
     float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
     __shared__ u32x4 lds[TileF::kLdsChunks];
@@ -344,7 +362,7 @@ __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
 // (vocabulary) or never written (tokens).  Needs D * sizeof(T) to be a
 // multiple of 128.
 template <typename T, class TL>
-__device__ __forceinline__ void fwd_segment_dma(const T *__restrict__ H, const T *__restrict__ E,
+__device__ __forceinline__ void fwd_segment_dma(const T *__restrict__ H, Rows2<const T> E,
                                                 const int32_t *__restrict__ idx, int nv,
                                                 const int32_t *__restrict__ perm, int D, int V, int n_vtiles, int rt,
                                                 int t0, int ntile, int64_t slot, u32x4 *lds,
@@ -370,7 +388,7 @@ __device__ __forceinline__ void fwd_segment_dma(const T *__restrict__ H, const T
             const int pos = min(vt * TL::BM + r, V - 1);
             int v = perm ? perm[pos] : pos;
             v = (v >= 0 && v < V) ? v : 0;
-            eng.pa[j] = reinterpret_cast<const char *>(E) + (size_t)v * rowb + DE::chunk_off(j, r, threadIdx.x);
+            eng.pa[j] = reinterpret_cast<const char *>(E.row(v)) + DE::chunk_off(j, r, threadIdx.x);
         }
     };
 
@@ -408,7 +426,7 @@ __device__ __forceinline__ void fwd_segment_dma(const T *__restrict__ H, const T
 
 template <typename T, class TL>
 __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
-    const T *__restrict__ H, const T *__restrict__ E, const int32_t *__restrict__ idx,
+    const T *__restrict__ H, Rows2<const T> E, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, int D, int V, int n_vtiles,
     float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
     using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
@@ -437,7 +455,7 @@ __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
 // and the scaled sum are butterfly reductions, so the result depends only on
 // the partition, never on scheduling.
 template <typename T>
-__global__ __launch_bounds__(256) void k_merge(const T *__restrict__ H, const T *__restrict__ E,
+__global__ __launch_bounds__(256) void k_merge(const T *__restrict__ H, Rows2<const T> E,
                                                const int64_t *__restrict__ labels, const int32_t *__restrict__ idx,
                                                const int32_t *__restrict__ nvalid_p,
                                                const float *__restrict__ part_m, const float *__restrict__ part_s,
@@ -477,7 +495,7 @@ __global__ __launch_bounds__(256) void k_merge(const T *__restrict__ H, const T 
     // z_{i, y_i} = <h_i, e_{y_i}>, fp32 accumulation of exact products.
     constexpr int CE = ChunkElems<T>::value;
     const char *h = reinterpret_cast<const char *>(H + i * (int64_t)D);
-    const char *e = reinterpret_cast<const char *>(E + y * (int64_t)D);
+    const char *e = reinterpret_cast<const char *>(E.row(y));
     float dot = 0.f;
     for (int k = lane * CE; k < D; k += 64 * CE) {
         const u32x4 hv = ld16(h + k * sizeof(T));
@@ -525,6 +543,13 @@ hipError_t launch_compact(const int64_t *labels, int64_t N, int64_t ignore_index
     return hipGetLastError();
 }
 
+hipError_t launch_seg_labels(const int64_t *labels, int64_t N, int64_t ignore_index, int64_t V0, int64_t off1,
+                             int64_t V1, int64_t *out, hipStream_t st) {
+    hipLaunchKernelGGL(k_seg_labels, dim3((unsigned)ceil_div(N, 256)), dim3(256), 0, st, labels, N, ignore_index,
+                       V0, off1, V1, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_check_labels(const int64_t *labels, int64_t N, int64_t V, int64_t ignore_index,
                                int64_t *n_bad, hipStream_t st) {
     hipLaunchKernelGGL(k_check_labels, dim3(1), dim3(1024), 0, st, labels, N, V, ignore_index, n_bad);
@@ -532,7 +557,7 @@ hipError_t launch_check_labels(const int64_t *labels, int64_t N, int64_t V, int6
 }
 
 template <typename T>
-static hipError_t forward_t(const T *H, const T *E, const int64_t *labels, const FwdShape &s,
+static hipError_t forward_t(const T *H, Rows2<const T> E, const int64_t *labels, const FwdShape &s,
                             int64_t ignore_index, const int32_t *perm, const FwdWs &w, float *loss, float *lse,
                             float *block_max, hipStream_t st) {
     hipError_t e = launch_compact(labels, s.N, ignore_index, w.idx, w.nvalid, st);
@@ -570,14 +595,19 @@ static hipError_t forward_t(const T *H, const T *E, const int64_t *labels, const
     return hipGetLastError();
 }
 
-hipError_t launch_forward(cce_dtype dt, const void *H, const void *E, const int64_t *labels,
+template <typename T>
+static Rows2<const T> rows_of(const VocabRows &E, int64_t D) {
+    return Rows2<const T>{static_cast<const T *>(E.e0), static_cast<const T *>(E.e1), E.v0, D};
+}
+
+hipError_t launch_forward(cce_dtype dt, const void *H, const VocabRows &E, const int64_t *labels,
                           const FwdShape &s, int64_t ignore_index, const int32_t *perm, const FwdWs &w,
                           float *loss, float *lse, float *block_max, hipStream_t st) {
     if (dt == CCE_BF16)
-        return forward_t<bf16_t>(static_cast<const bf16_t *>(H), static_cast<const bf16_t *>(E), labels,
-                                 s, ignore_index, perm, w, loss, lse, block_max, st);
-    return forward_t<float>(static_cast<const float *>(H), static_cast<const float *>(E), labels, s,
-                            ignore_index, perm, w, loss, lse, block_max, st);
+        return forward_t<bf16_t>(static_cast<const bf16_t *>(H), rows_of<bf16_t>(E, s.D), labels, s, ignore_index,
+                                 perm, w, loss, lse, block_max, st);
+    return forward_t<float>(static_cast<const float *>(H), rows_of<float>(E, s.D), labels, s, ignore_index, perm, w,
+                            loss, lse, block_max, st);
 }
 
 }  // namespace cce

@@ -51,14 +51,14 @@ __global__ __launch_bounds__(256) void k_hbar(const float *__restrict__ part, co
 // key_v = <hbar, e_v>; also the order-preserving code of the key (ascending
 // code = descending key, -0 == +0) and the initial ids.
 template <typename T>
-__global__ __launch_bounds__(256) void k_keys(const T *__restrict__ E, const float *__restrict__ hbar, int D,
+__global__ __launch_bounds__(256) void k_keys(Rows2<const T> E, const float *__restrict__ hbar, int D,
                                               int V, float *__restrict__ keys, uint32_t *__restrict__ code,
                                               int32_t *__restrict__ ids) {
     constexpr int CE = ChunkElems<T>::value;
     const int lane = threadIdx.x & 63;
     const int64_t v = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (v >= V) return;
-    const char *e = reinterpret_cast<const char *>(E + v * D);
+    const char *e = reinterpret_cast<const char *>(E.row(v));
     float s = 0.f;
     for (int k = lane * CE; k < D; k += 64 * CE) {
         const u32x4 ev = ld16(e + k * sizeof(T));
@@ -187,7 +187,7 @@ SortWs sort_ws(void *ws, int64_t N, int64_t D, int64_t V, size_t *bytes) {
 }
 
 template <typename T>
-static hipError_t vocab_order_t(const T *H, const T *E, const int64_t *labels, int64_t N, int64_t D, int64_t V,
+static hipError_t vocab_order_t(const T *H, Rows2<const T> E, const int64_t *labels, int64_t N, int64_t D, int64_t V,
                                 int64_t ignore_index, int32_t *perm, float *keys_out, int32_t *idx,
                                 const SortWs &w, hipStream_t st) {
     hipError_t e = launch_compact(labels, N, ignore_index, idx, w.nvalid, st);
@@ -218,14 +218,18 @@ static hipError_t vocab_order_t(const T *H, const T *E, const int64_t *labels, i
     return hipSuccess;  // four passes: the sorted ids are back in perm
 }
 
-hipError_t launch_vocab_order(cce_dtype dt, const void *H, const void *E, const int64_t *labels, int64_t N,
+hipError_t launch_vocab_order(cce_dtype dt, const void *H, const VocabRows &E, const int64_t *labels, int64_t N,
                               int64_t D, int64_t V, int64_t ignore_index, int32_t *perm, float *keys_out,
                               const SortWs &w, hipStream_t st) {
     if (dt == CCE_BF16)
-        return vocab_order_t<bf16_t>(static_cast<const bf16_t *>(H), static_cast<const bf16_t *>(E), labels, N, D, V,
-                                     ignore_index, perm, keys_out, w.idx, w, st);
-    return vocab_order_t<float>(static_cast<const float *>(H), static_cast<const float *>(E), labels, N, D, V,
-                                ignore_index, perm, keys_out, w.idx, w, st);
+        return vocab_order_t<bf16_t>(
+            static_cast<const bf16_t *>(H),
+            Rows2<const bf16_t>{static_cast<const bf16_t *>(E.e0), static_cast<const bf16_t *>(E.e1), E.v0, D},
+            labels, N, D, V, ignore_index, perm, keys_out, w.idx, w, st);
+    return vocab_order_t<float>(
+        static_cast<const float *>(H),
+        Rows2<const float>{static_cast<const float *>(E.e0), static_cast<const float *>(E.e1), E.v0, D}, labels, N,
+        D, V, ignore_index, perm, keys_out, w.idx, w, st);
 }
 
 }  // namespace cce

@@ -1,0 +1,81 @@
+"""The PyTorch autograd wrapper: the reduction reaches the backward as
+dloss, and the gradients torch hands back equal the C ABI's on the same
+inputs (bit for bit: same kernels, same dloss), for the one-matrix and the
+composite head, with and without the vocabulary sort."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_cross_entropy_cce_amd import autograd as A
+from linear_cross_entropy_cce_amd import binding as B
+from linear_cross_entropy_cce_amd import inputs
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _dloss(x, reduction):
+    valid = x.labels != x.ignore_index
+    if reduction == "mean":
+        return np.where(valid, 1.0 / max(valid.sum(), 1), 0.0).astype(np.float32)
+    return np.where(valid, 1.0, 0.0).astype(np.float32)
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+@pytest.mark.parametrize("sort", [False, True])
+def test_wrapper_matches_abi(reduction, sort):
+    x = inputs.make_workload(3, N=600, D=512, V=5000)
+    G.say(f"autograd reduction={reduction} sort={sort}")
+    H, E, y = G.to_device(x)
+    Hl = H.clone().requires_grad_(True)
+    El = E.clone().requires_grad_(True)
+    out = A.linear_cross_entropy(Hl, El, y, x.ignore_index, reduction=reduction, filter_eps=x.eps, sort_vocab=sort)
+    if reduction == "none":
+        out.backward(torch.from_numpy(_dloss(x, "sum")).to(G.DEV))
+    else:
+        out.backward()
+    torch.cuda.synchronize()
+    dl = _dloss(x, "mean" if reduction == "mean" else "sum")
+    ref = G.run_gpu(x, dl, eps=x.eps, sort=sort)
+    valid = x.labels != x.ignore_index
+    loss_sum = ref["loss"][valid].sum()
+    got = G.t64(out)
+    if reduction == "none":
+        assert np.array_equal(got, ref["loss"])
+    else:
+        want = loss_sum / valid.sum() if reduction == "mean" else loss_sum
+        assert abs(float(got) - want) <= 1e-5 * max(abs(want), 1.0)  # got is already detached
+    assert np.array_equal(G.t64(Hl.grad), ref["dH"])
+    assert np.array_equal(G.t64(El.grad), ref["dE"])
+    # and against the fp64 oracle, at the filtered tolerance
+    _, _, dH, dE = G.oracle_full(x, dl, f"autograd-{reduction}")
+    LH, LE = G.label_term(x, dl)
+    G.assert_grad("dH", G.t64(Hl.grad), dH, LH, 2e-2)
+    G.assert_grad("dE", G.t64(El.grad), dE, LE, 2e-2)
+
+
+def test_composite_wrapper_matches_oracle():
+    x = inputs.make_workload(1)  # fp32, 10 % ignored
+    V0, gap = 2500, 300
+    y = x.labels.copy()
+    y[y >= V0] += gap
+    G.say("autograd composite")
+    H, E, _ = G.to_device(x)
+    yt = torch.from_numpy(y).to(G.DEV)
+    Hl = H.clone().requires_grad_(True)
+    E0 = E[:V0].clone().requires_grad_(True)
+    E1 = E[V0:].clone().requires_grad_(True)
+    loss = A.linear_cross_entropy_composite(Hl, E0, E1, V0 + gap, yt, x.ignore_index, filter_eps=0.0)
+    loss.backward()
+    torch.cuda.synchronize()
+    dl = _dloss(x, "mean").astype(np.float64)
+    Hf = oracle.as_f64(x.H, x.dtype)
+    Ef = oracle.as_f64(x.E, x.dtype)
+    rl, _, dH, dE0, dE1 = oracle.composite(Hf, Ef[:V0], Ef[V0:], V0 + gap, y, dl, x.ignore_index)
+    valid = y != x.ignore_index
+    want = rl[valid].mean()
+    assert abs(float(loss.detach()) - want) <= 1e-5 * max(abs(want), 1.0)
+    for name, g, r in (("dH", Hl.grad, dH), ("dE0", E0.grad, dE0), ("dE1", E1.grad, dE1)):
+        g = G.t64(g)
+        assert np.linalg.norm(g - r) <= 1e-5 * np.linalg.norm(r), name
