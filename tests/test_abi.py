@@ -169,3 +169,46 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="libcce.so not found"):
         B.lib()
+
+
+def _fwd_c(**kw):
+    a = dict(H=FAKE, E0=FAKE, V0=60, E1=FAKE + 4096, V1=40, off1=70, labels=FAKE, N=16, D=64, dt=B.CCE_BF16,
+             ign=-100, perm=None, loss=FAKE, lse=FAKE, tb=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return B.lib().cce_forward_composite(a["H"], a["E0"], a["V0"], a["E1"], a["V1"], a["off1"], a["labels"], a["N"],
+                                         a["D"], a["dt"], a["ign"], a["perm"], a["loss"], a["lse"], a["tb"], a["ws"],
+                                         a["ws_bytes"], a["stream"])
+
+
+def _bwd_c(**kw):
+    a = dict(H=FAKE, E0=FAKE, V0=60, E1=FAKE + 4096, V1=40, off1=70, labels=FAKE, lse=FAKE, dloss=FAKE, tb=None,
+             N=16, D=64, dt=B.CCE_BF16, ign=-100, eps=0.0, perm=None, flags=0, dH=FAKE, dE0=FAKE, dE1=FAKE + 8192,
+             stats=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return B.lib().cce_backward_composite(a["H"], a["E0"], a["V0"], a["E1"], a["V1"], a["off1"], a["labels"],
+                                          a["lse"], a["dloss"], a["tb"], a["N"], a["D"], a["dt"], a["ign"], a["eps"],
+                                          a["perm"], a["flags"], a["dH"], a["dE0"], a["dE1"], a["stats"], a["ws"],
+                                          a["ws_bytes"], a["stream"])
+
+
+def test_composite_argument_errors():
+    for f in (_fwd_c, _bwd_c):
+        assert f(E1=None) == B.CCE_ERR_NULL
+        assert f(V0=0) == B.CCE_ERR_SHAPE
+        assert f(V1=0) == B.CCE_ERR_SHAPE
+        assert f(off1=59) == B.CCE_ERR_SHAPE          # the second block may not overlap the first
+        assert f(V0=1 << 30, V1=1 << 30, off1=1 << 30) == B.CCE_ERR_SHAPE  # V0 + V1 >= 2^31
+        assert f(E1=FAKE + 8) == B.CCE_ERR_ALIGN
+        assert f(dt=5) == B.CCE_ERR_DTYPE
+        # the workspace query takes V = V0 + V1
+        need = B.backward_workspace_bytes(16, 64, 100, B.CCE_BF16) if f is _bwd_c else \
+            B.forward_workspace_bytes(16, 64, 100, B.CCE_BF16)
+        assert f(ws_bytes=need - 1) == B.CCE_ERR_WORKSPACE
+    assert _bwd_c(dE1=None) == B.CCE_ERR_NULL
+    assert _bwd_c(dE1=FAKE + 8) == B.CCE_ERR_ALIGN
+    assert _bwd_c(eps=-1.0) == B.CCE_ERR_ARG
+    L = B.lib()
+    assert L.cce_vocab_order_composite(FAKE, FAKE, 60, None, 40, FAKE, 16, 64, B.CCE_BF16, -100, FAKE, None, FAKE,
+                                       1 << 40, None) == B.CCE_ERR_NULL
+    assert L.cce_vocab_order_composite(FAKE, FAKE, 0, FAKE, 40, FAKE, 16, 64, B.CCE_BF16, -100, FAKE, None, FAKE,
+                                       1 << 40, None) == B.CCE_ERR_SHAPE
