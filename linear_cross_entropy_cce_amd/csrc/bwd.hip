@@ -685,15 +685,31 @@ struct DhEngine {
 
     // Stage kq of the block with store slot `slot` and first vocabulary
     // position pos0, into LDS buffer buf.
+    // The lanes of B instruction j feed kRowsPerInstr consecutive rows, the
+    // first of them wave-uniform; with a permutation their ids are read with
+    // scalar loads, so that no vector load has to be waited for while the
+    // earlier stages are in flight.
+    static constexpr int kRowsPerInstr = 64 / kCprB;
+    static_assert(kRowsPerInstr == 1 || kRowsPerInstr == 2, "B rows per instruction");
+
     __device__ __forceinline__ void issue(int buf, const T *Gn, int64_t slot, const Rows2<const T> &E,
                                           const int32_t *perm, int pos0, int kq, int V) const {
         const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const uint32_t st = lds0 + (uint32_t)(buf * kStage) * 16u;
         dma16_at(reinterpret_cast<const char *>(Gn + slot * kBlockElems) + a_off + kq * kStageBytes, st + 1024u * w);
+        const int base = __builtin_amdgcn_readfirstlane(pos0 + kq * kKv);
 #pragma unroll
         for (int j = 0; j < NIB; ++j) {
-            const int pos = pos0 + kq * kKv + b_row[j];
-            int vid = pos < V ? (perm ? perm[pos] : pos) : V - 1;
+            int vid;
+            if (perm) {
+                const int p0 = base + (int)(64 * (j * TL::kWaves + w)) / kCprB;  // uniform
+                const int v0 = uniform_load(perm, min(p0, V - 1));
+                const int v1 = kRowsPerInstr > 1 ? uniform_load(perm, min(p0 + 1, V - 1)) : v0;
+                vid = b_row[j] == p0 - base ? v0 : v1;
+            } else {
+                const int pos = base + b_row[j];
+                vid = pos < V ? pos : V - 1;
+            }
             vid = (vid >= 0 && vid < V) ? vid : 0;
             dma16_at(reinterpret_cast<const char *>(E.row(vid)) + b_off[j],
                      st + 16u * kStageA + 1024u * (j * TL::kWaves + w));

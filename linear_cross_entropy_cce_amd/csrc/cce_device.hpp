@@ -248,6 +248,14 @@ __device__ __forceinline__ int dma_slot(int r, int c) {
 __device__ __forceinline__ void dma16_at(const char *src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(src) : "memory", "m0");
 }
+// Wave-uniform read of a[i] through the scalar data cache (an SMEM load,
+// counted by lgkmcnt).  A vector load would be counted by vmcnt together with
+// the LDS-DMA stages in flight, and waiting for it would drain them.  Only for
+// data no kernel of the launch writes.
+__device__ __forceinline__ int32_t uniform_load(const int32_t *a, int64_t i) {
+    typedef __attribute__((address_space(4))) const int32_t const_i32;
+    return ((const_i32 *)a)[i];
+}
 // LDS byte address (32 bits, wave-uniform) of a __shared__ pointer.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t *)p);

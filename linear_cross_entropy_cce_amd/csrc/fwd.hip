@@ -381,14 +381,24 @@ __device__ __forceinline__ void fwd_segment_dma(const T *__restrict__ H, Rows2<c
         const int tok = min(tok0 + r, nv - 1);
         eng.pb[j] = reinterpret_cast<const char *>(H) + (size_t)idx[tok] * rowb + DE::chunk_off(j, r, threadIdx.x);
     }
+    // (Two paths on the uniform perm test: without a permutation no load is
+    // issued, so nothing has to wait for the stage in flight.)
     auto set_tile = [&](int vt) {
+        if (perm) {
 #pragma unroll
-        for (int j = 0; j < DE::NIA; ++j) {
-            const int r = DE::row_a(j);
-            const int pos = min(vt * TL::BM + r, V - 1);
-            int v = perm ? perm[pos] : pos;
-            v = (v >= 0 && v < V) ? v : 0;
-            eng.pa[j] = reinterpret_cast<const char *>(E.row(v)) + DE::chunk_off(j, r, threadIdx.x);
+            for (int j = 0; j < DE::NIA; ++j) {
+                const int r = DE::row_a(j);
+                int v = perm[min(vt * TL::BM + r, V - 1)];
+                v = (v >= 0 && v < V) ? v : 0;
+                eng.pa[j] = reinterpret_cast<const char *>(E.row(v)) + DE::chunk_off(j, r, threadIdx.x);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < DE::NIA; ++j) {
+                const int r = DE::row_a(j);
+                eng.pa[j] = reinterpret_cast<const char *>(E.row(min(vt * TL::BM + r, V - 1))) +
+                            DE::chunk_off(j, r, threadIdx.x);
+            }
         }
     };
 
