@@ -27,7 +27,7 @@
  *    time must not share a workspace.
  *  - H is [N, D] and E is [V, D], row-major with D innermost, both of one dtype
  *    (cce_dtype).  D % 8 == 0; H, E, dH, dE and the workspace are 16-byte
- *    aligned.  1 <= N < 2^31, 1 <= V < 2^31, 8 <= D <= 65536.
+ *    aligned.  1 <= N <= 2^31 - 2^16, 1 <= V <= 2^31 - 2^16, 8 <= D <= 65536.
  *  - labels are int64 [N]; a row whose label equals ignore_index is ignored.
  *    Any other label outside [0, V) is undefined behaviour (cce_check_labels
  *    detects it).

@@ -15,9 +15,13 @@ constexpr int kVersion = 10000;  // 1.0.0
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Row and vocabulary positions are 32-bit in the kernels, and a tile's last
+// position (its start + up to 255) must stay below 2^31: N, V <= kMaxRows.
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - (int64_t(1) << 16);
+
 bool shape_ok(int64_t N, int64_t D, int64_t V) {
-    if (N < 1 || N >= (int64_t(1) << 31)) return false;
-    if (V < 1 || V >= (int64_t(1) << 31)) return false;
+    if (N < 1 || N > kMaxRows) return false;
+    if (V < 1 || V > kMaxRows) return false;
     if (D < 8 || D > 65536 || D % 8 != 0) return false;
     // grid sizes stay below 2^31 workgroups, and logit tiles are indexed with 32 bits
     if (ceil_div(N, kBlockRows) * ceil_div(D, 128) >= (int64_t(1) << 31)) return false;
@@ -121,7 +125,7 @@ const char *cce_status_string(cce_status s) {
     switch (s) {
         case CCE_OK: return "ok";
         case CCE_ERR_NULL: return "a required pointer is NULL";
-        case CCE_ERR_SHAPE: return "N, D or V outside the supported range (D % 8 == 0, 8 <= D <= 65536, 1 <= N, V < 2^31)";
+        case CCE_ERR_SHAPE: return "N, D or V outside the supported range (D % 8 == 0, 8 <= D <= 65536, 1 <= N, V <= 2^31 - 2^16)";
         case CCE_ERR_DTYPE: return "unknown dtype";
         case CCE_ERR_ALIGN: return "a pointer is not aligned (16 bytes for H, E, dH, dE, workspace)";
         case CCE_ERR_WORKSPACE: return "workspace too small";
@@ -220,7 +224,7 @@ cce_status cce_backward_composite(const void *H, const void *E0, int64_t V0, con
 cce_status cce_check_labels(const int64_t *labels, int64_t N, int64_t V, int64_t ignore_index, int64_t *n_bad,
                             void *stream) {
     if (!labels || !n_bad) return CCE_ERR_NULL;
-    if (N < 1 || N >= (int64_t(1) << 31) || V < 1 || V >= (int64_t(1) << 31)) return CCE_ERR_SHAPE;
+    if (N < 1 || N > kMaxRows || V < 1 || V > kMaxRows) return CCE_ERR_SHAPE;
     if (!aligned(labels, 8) || !aligned(n_bad, 8)) return CCE_ERR_ALIGN;
     return hip_status(launch_check_labels(labels, N, V, ignore_index, n_bad, static_cast<hipStream_t>(stream)));
 }

@@ -35,6 +35,8 @@
 // N and V (store, transposed H) plus one byte-sized entry per block.
 #include <math.h>
 
+#include <algorithm>
+
 #include "cce_device.hpp"
 #include "cce_internal.hpp"
 
@@ -1090,7 +1092,9 @@ BwdShape bwd_shape(int64_t N, int64_t D, int64_t V) {
     const int64_t total = (int64_t)s.n_rb * s.cbp;
     const int64_t vp = round_up(V, kTileVocab);
     const int64_t slice_cb = (vp < kStoreVocab ? vp : kStoreVocab) / kBlockVocab;
-    s.cap = (int64_t)s.n_rb * slice_cb;
+    // (at least kMinStoreBlocks: few rows over a large vocabulary would
+    // otherwise take one pass per few vocabulary tiles)
+    s.cap = std::max<int64_t>((int64_t)s.n_rb * slice_cb, kMinStoreBlocks);
     if (total <= s.cap) {
         s.cap = total;
         s.cap_eff = total;

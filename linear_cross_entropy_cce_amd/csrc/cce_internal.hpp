@@ -23,6 +23,8 @@ constexpr int kBlockRows = 128;
 // The backward's store of kept gradient blocks holds as many blocks as a
 // dense [rows x kStoreVocab] slice would (a multiple of 2 kBlockVocab).
 constexpr int kStoreVocab = 8192;
+// ... and at least this many blocks (64 MB at bf16, both layouts).
+constexpr int64_t kMinStoreBlocks = 1024;
 // Workgroups of the persistent backward kernels.
 constexpr int kPassGroups = 256;
 // Most workgroups of the forward's persistent grid (its partial buffers are

@@ -68,9 +68,11 @@ def test_workspace_has_no_per_logit_term(dt):
 
 
 def test_workspace_invalid_sizes_return_zero():
-    for args in [(0, 64, 10), (10, 0, 10), (10, 12, 10), (10, 64, 0), (10, 64, 1 << 31), (10, 64, 10)]:
+    vmax = (1 << 31) - (1 << 16)
+    for args in [(0, 64, 10), (10, 0, 10), (10, 12, 10), (10, 64, 0), (10, 64, 1 << 31), (10, 64, 10),
+                 (10, 64, vmax), (10, 64, vmax + 1), (vmax, 64, 10), (vmax + 1, 64, 10)]:
         n, d, v = args
-        want_zero = not (n >= 1 and v >= 1 and v < (1 << 31) and d >= 8 and d % 8 == 0)
+        want_zero = not (1 <= n <= vmax and 1 <= v <= vmax and d >= 8 and d % 8 == 0)
         assert (B.forward_workspace_bytes(n, d, v, 1) == 0) == want_zero
     assert B.forward_workspace_bytes(10, 64, 10, 7) == 0
 
@@ -112,6 +114,8 @@ def test_argument_errors_before_launch(call):
     assert call(D=12) == B.CCE_ERR_SHAPE
     assert call(D=0) == B.CCE_ERR_SHAPE
     assert call(V=1 << 31) == B.CCE_ERR_SHAPE
+    assert call(V=(1 << 31) - (1 << 16) + 1) == B.CCE_ERR_SHAPE  # a tile's positions must stay 32-bit
+    assert call(N=(1 << 31) - (1 << 16) + 1) == B.CCE_ERR_SHAPE
     assert call(dt=5) == B.CCE_ERR_DTYPE
     assert call(H=FAKE + 8) == B.CCE_ERR_ALIGN
     assert call(E=FAKE + 4) == B.CCE_ERR_ALIGN

@@ -1,0 +1,115 @@
+"""The largest vocabulary the ABI accepts, V = 2^31 - 2^16 (a tile's last
+position must stay a 32-bit integer), on the real kernels.
+
+E has V equal rows e (34 GB of bf16), so the results have closed forms:
+  z_iv = <h_i, e> for every v,  lse_i = z_i + log V,  loss_i = log V,
+and every softmax entry is 1/V.
+  - filter_eps = 2^-12 (> 1/V): every softmax part is dropped, so
+    dH_i = -dloss_i e and dE_v = -sum_{i: y_i = v} dloss_i h_i (0 elsewhere);
+  - filter_eps = 0: dE_v = sum_i dloss_i (1/V - [y_i = v]) h_i, and
+    dH_i = dloss_i (sum_v e / V - e) = 0 in exact arithmetic.  dH adds its
+    ~1.7e7 block products in fp32 one after the other (Kahan covers dE only),
+    and 1.7e7 equal terms summed that way lose up to half of their total, so
+    for dH only finiteness and |dH| <= dloss |e| are checked here.
+Rows of dE are checked at the labels, at the first and last vocabulary
+blocks and at random positions.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from linear_cross_entropy_cce_amd import binding as B
+from linear_cross_entropy_cce_amd import inputs
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+VMAX = (1 << 31) - (1 << 16)
+D = 8
+N = 5
+
+
+@pytest.fixture(scope="module")
+def big():
+    rng = np.random.default_rng(31)
+    e = inputs.round_to_bf16_bits(rng.normal(0, 0.5, D).astype(np.float32))
+    h = inputs.round_to_bf16_bits(rng.normal(0, 1.0, (N, D)).astype(np.float32))
+    y = np.array([0, VMAX - 1, 123456789, -100, 123456789], dtype=np.int64)
+    G.say(f"max vocabulary V={VMAX} D={D} N={N}: allocating E and dE ({2 * VMAX * D * 2 / 1e9:.1f} GB)")
+    E = torch.empty((VMAX, D), dtype=torch.bfloat16, device=G.DEV)
+    E[:] = torch.from_numpy(e).view(torch.bfloat16).to(G.DEV)
+    H = torch.from_numpy(h).view(torch.bfloat16).to(G.DEV)
+    yt = torch.from_numpy(y).to(G.DEV)
+    ef = inputs.bf16_bits_as_f32(e).astype(np.float64)
+    hf = inputs.bf16_bits_as_f32(h).astype(np.float64)
+    yield dict(E=E, H=H, y=yt, ynp=y, e=ef, h=hf)
+    del E
+    torch.cuda.empty_cache()
+
+
+def _run(big, eps):
+    tb = torch.empty(B.block_max_elems(N, VMAX), dtype=torch.float32, device=G.DEV)
+    loss, lse = B.cce_forward(big["H"], big["E"], big["y"], -100, block_max=tb)
+    valid = big["ynp"] != -100
+    dl = np.where(valid, 1.0 / valid.sum(), 0.0).astype(np.float32)
+    dH, dE = B.cce_backward(big["H"], big["E"], big["y"], lse, torch.from_numpy(dl).to(G.DEV), eps, -100,
+                            block_max=tb)
+    torch.cuda.synchronize()
+    return G.t64(loss), G.t64(lse), dH, dE, dl.astype(np.float64)
+
+
+def _rows_to_check(y):
+    rng = np.random.default_rng(5)
+    rows = set(int(v) for v in y if v >= 0)
+    rows |= {0, 1, 127, 128, 255, 256, VMAX - 256, VMAX - 129, VMAX - 128, VMAX - 2, VMAX - 1}
+    rows |= set(int(v) for v in rng.integers(0, VMAX, 16))
+    return np.array(sorted(rows))
+
+
+def _check_forward(big, loss, lse):
+    valid = big["ynp"] != -100
+    z = big["h"] @ big["e"]
+    ref_lse = np.where(valid, z + math.log(VMAX), 0.0)
+    ref_loss = np.where(valid, math.log(VMAX), 0.0)
+    G.assert_rows("lse", lse, ref_lse, valid, 1e-3)
+    G.assert_rows("loss", loss, ref_loss, valid, 1e-3, ref_lse)
+
+
+def test_max_vocab_filtered(big):
+    G.say("max vocabulary, eps = 2^-12")
+    loss, lse, dH, dE, dl = _run(big, 2.0 ** -12)
+    _check_forward(big, loss, lse)
+    y, h, e = big["ynp"], big["h"], big["e"]
+    valid = y != -100
+    ref_dH = -dl[:, None] * e[None, :] * valid[:, None]
+    got_dH = G.t64(dH)
+    assert np.allclose(got_dH, ref_dH, rtol=1e-2, atol=1e-6), (got_dH, ref_dH)
+    rows = _rows_to_check(y)
+    got = G.t64(dE[torch.from_numpy(rows).to(G.DEV)])
+    ref = np.zeros((rows.size, D))
+    for k, v in enumerate(rows):
+        sel = y == v
+        ref[k] = -(dl[sel, None] * h[sel]).sum(axis=0)
+    assert np.allclose(got, ref, rtol=1e-2, atol=1e-6), (rows, got, ref)
+
+
+def test_max_vocab_unfiltered(big):
+    G.say("max vocabulary, eps = 0")
+    loss, lse, dH, dE, dl = _run(big, 0.0)
+    _check_forward(big, loss, lse)
+    y, h, e = big["ynp"], big["h"], big["e"]
+    got_dH = G.t64(dH)
+    scale = np.abs(dl[:, None] * e[None, :]).max()
+    assert np.all(np.isfinite(got_dH)) and np.abs(got_dH).max() <= scale, got_dH
+    rows = _rows_to_check(y)
+    got = G.t64(dE[torch.from_numpy(rows).to(G.DEV)])
+    hsum = (dl[:, None] * h).sum(axis=0)
+    ref = np.zeros((rows.size, D))
+    for k, v in enumerate(rows):
+        sel = y == v
+        ref[k] = hsum / VMAX - (dl[sel, None] * h[sel]).sum(axis=0)
+    for k in range(rows.size):
+        tol = 2e-2 * np.abs(ref[k]).max() + 1e-12  # bf16 gradient entries and output
+        assert np.abs(got[k] - ref[k]).max() <= tol, (rows[k], got[k], ref[k])

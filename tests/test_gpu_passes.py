@@ -12,10 +12,12 @@ from tests import _gpu as G
 
 pytestmark = pytest.mark.gpu
 
+# The block store holds max(row blocks x 64, 1024) blocks (with 2300 rows:
+# 18 x 64 = 1152), so these vocabularies take several passes.
 CASES = [
-    (2, 700, 256, 9000, 2.0 ** -12),     # peaked: two passes without the table, one with it
-    (3, 600, 512, 20000, 2.0 ** -12),    # flat, 40 % ignored: several passes either way
-    (4, 300, 72, 20000, 2.0 ** -6),      # D * 2 not a multiple of 128: VGPR-staged recompute
+    (2, 2300, 256, 40000, 2.0 ** -12),   # peaked: six passes without the table, one with it
+    (3, 2300, 512, 20000, 2.0 ** -12),   # flat, 40 % ignored: several passes either way
+    (4, 2300, 72, 20000, 2.0 ** -6),     # D * 2 not a multiple of 128: VGPR-staged recompute
 ]
 
 
@@ -33,7 +35,7 @@ def test_pass_cut_does_not_change_results(k, N, D, V, eps):
 
 def test_multi_pass_matches_oracle():
     """A flat case with every block kept, cut into several passes."""
-    x = inputs.make_workload(3, N=600, D=512, V=20000)
+    x = inputs.make_workload(3, N=2300, D=512, V=20000)
     G.say(f"multi-pass parity N={x.N} D={x.D} V={x.V}")
     dl = G.mean_dloss(x)
     out = G.run_gpu(x, dl, eps=0.0)
