@@ -7,7 +7,7 @@
  *   lse_i  = log sum_v exp(z_iv)
  *   loss_i = lse_i - z_{i,y_i}
  *   dH_i   = sum_v g_iv e_v,   dE_v = sum_i g_iv h_i,
- *   g_iv   = dloss_i * (p_iv * [block(i,v) survives] - [v == y_i]),
+ *   g_iv   = dloss_i * (p_iv * [block(i,v) survives or v == y_i] - [v == y_i]),
  *   p_iv   = exp(z_iv - lse_i).
  * Cross-entropy needs only the correct-token logit (an indexed matmul) and the
  * log-sum-exp over the vocabulary, computed blockwise on chip without writing
@@ -95,8 +95,8 @@ size_t cce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtype d
 size_t cce_vocab_order_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtype dtype);
 
 /* Elements (fp32) of the optional block-max table of cce_forward /
- * cce_backward: 4 * ceil(N / 256) * ceil(V / 256), one per 128 x 128 block of
- * the logit matrix (0 on invalid sizes). */
+ * cce_backward: 4 * ceil(N / 256) * ceil(V / 256) (one per 128 x 128 block of
+ * the logit matrix) + N (one label logit per row); 0 on invalid sizes. */
 size_t cce_block_max_elems(int64_t N, int64_t V);
 
 /*
@@ -109,10 +109,13 @@ size_t cce_block_max_elems(int64_t N, int64_t V);
  *   perm[1], ...  The loss only changes by rounding order; entries of perm
  *   outside [0, V) read entry 0 instead (the caller guarantees a permutation).
  * block_max: NULL, or device fp32 [cce_block_max_elems(N, V)] that receives
- *   the largest logit of every 128 x 128 block of the logit matrix of the
- *   non-ignored rows (in order) and the vocabulary in processing order,
- *   row-major over [2 ceil(N / 256) row blocks, 2 ceil(V / 256) vocabulary
- *   blocks]; blocks with no valid row get -inf.
+ *   (1) the largest logit other than a label entry (i, y_i) of every
+ *   128 x 128 block of the logit matrix of the non-ignored rows (in order) and
+ *   the vocabulary in processing order, row-major over [2 ceil(N / 256) row
+ *   blocks, 2 ceil(V / 256) vocabulary blocks] (-inf for blocks with no valid
+ *   row), then (2) the label logit z_{i, y_i} of every non-ignored row i with
+ *   a valid label, at index i of an [N] array (other entries untouched), as
+ *   the logit tiles computed it.
  * ws: device scratch of at least cce_forward_workspace_bytes bytes.
  */
 cce_status cce_forward(const void *H, const void *E, const int64_t *labels,
@@ -141,13 +144,15 @@ cce_status cce_vocab_order(const void *H, const void *E, const int64_t *labels,
  *  - dloss: fp32 [N]; it carries the caller's reduction (1/N_valid for a mean).
  *  - block_max: NULL, or the table cce_forward wrote for these same H, E,
  *    labels and perm.  With it (and filter_eps > 0), a 128 x 128 block
- *    whose largest logit is so far below the smallest lse of its rows that
- *    every p_iv in it is < filter_eps / 2 cannot keep its softmax part, and a
- *    256 x 256 logit tile made only of such blocks is not recomputed; the
+ *    whose largest non-label logit is so far below the smallest lse of its
+ *    rows that every such p_iv is < filter_eps / 2 cannot keep its softmax
+ *    part, and a 256 x 256 logit tile made only of such blocks is not
+ *    recomputed (its label entries take the table's label logits); the
  *    outputs are bit-identical to the run without the table.
- *  - filter_eps >= 0: a filter block (see cce_filter_block) is skipped when
- *    every p_iv in it is < filter_eps; 0 disables filtering.  Only the
- *    softmax part is filtered: the -dloss_i at (i, y_i) is always applied.
+ *  - filter_eps >= 0: a filter block (see cce_filter_block) drops the
+ *    softmax part of its entries when every p_iv in it other than a label
+ *    entry is < filter_eps; 0 disables filtering.  A label entry (i, y_i)
+ *    always keeps its whole gradient dloss_i (p_{i,y_i} - 1).
  *  - perm: NULL, or the permutation from cce_vocab_order (int32 [V]); it only
  *    changes which vocabulary entries share a filter block.
  *  - flags: 0 or any of CCE_BWD_NO_KAHAN, CCE_BWD_FULL_DE.

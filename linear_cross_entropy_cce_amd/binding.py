@@ -183,7 +183,8 @@ def cce_forward(H, E, labels, ignore_index=-100, loss=None, lse=None, block_max=
                 perm=None):
     """loss, lse (fp32 [N]) of the fused head + cross-entropy.  block_max:
     None, or an fp32 tensor of block_max_elems(N, V) entries to receive the
-    largest logit of every 128 x 128 block of the logits (for cce_backward).
+    largest non-label logit of every 128 x 128 block of the logits and the label
+    logit of every row (for cce_backward).
     perm: None, or the int32 [V] vocabulary order to visit (the table is then
     in that order, for a cce_backward given the same perm)."""
     import torch

@@ -95,6 +95,7 @@ struct BwdArgs {
     const int32_t *idx, *nvalid, *perm, *inv_perm;
     const int64_t *labels;
     const float *lse, *dloss;
+    const float *zlab;  // [N] label logit of each valid row from the forward's tiles (with the table)
     int D, V, cbp, n_rb;
     float eps;
     int full_de;  // dE from every block (status 3 = kept for dE only), dH filtered
@@ -109,14 +110,6 @@ struct BwdArgs {
 };
 
 // ------------------------------------------------------------ small kernels
-__global__ void k_inv_perm(const int32_t *__restrict__ perm, int V, int32_t *__restrict__ inv) {
-    const int k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k < V) {
-        const int v = perm[k];
-        if (v >= 0 && v < V) inv[v] = k;
-    }
-}
-
 __global__ void k_stats_init(int64_t *stats) {
     if (threadIdx.x < 5) stats[threadIdx.x] = 0;
 }
@@ -387,7 +380,8 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
                                            int V, int rt, int vt, int cbp, float eps,
                                            const int32_t *__restrict__ idx, const int32_t *__restrict__ inv_perm,
                                            const int64_t *__restrict__ labels, const float *__restrict__ lse,
-                                           const float *__restrict__ dloss, T *__restrict__ Gt, T *__restrict__ Gn,
+                                           const float *__restrict__ dloss, const float *__restrict__ zlab,
+                                           T *__restrict__ Gt, T *__restrict__ Gn,
                                            int64_t cap, int32_t *__restrict__ counter, uint8_t *__restrict__ st,
                                            int32_t *__restrict__ slotm, int64_t *__restrict__ stats, int *qflag,
                                            int *qstat, int *qslot, int full_de, int qmask) {
@@ -396,18 +390,22 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
     const int wm = wave % TL::WM, wn = wave / TL::WM;
     const int th = (wn * TL::kWaveN) / kBlockRows;  // token half of this wave
     const int quad = wm * 2 + th;                   // this wave's block: vocabulary half wm, token half th
-    float lse_t[TL::TN], dl_t[TL::TN];
+    // Per token column: lse (+inf past the valid tokens, so that p = 0 there),
+    // dloss (0 there, so that g = 0), the label's row as acc_row_const in
+    // this lane (-1000: none) and the label entry's softmax probability.
+    float lse_t[TL::TN], dl_t[TL::TN], pl_t[TL::TN];
     int lab_t[TL::TN];
-    bool tok_ok[TL::TN];
     bool any_live = false, any_label = false;
+    const int rbase = wm * TL::kWaveM + 4 * (lane >> 5);  // tile_row = rbase + acc_row_const
+    const bool wsoft = SOFTMAX && ((qmask >> quad) & 1);  // this wave's block was recomputed (wave-uniform)
 #pragma unroll
     for (int tn = 0; tn < TL::TN; ++tn) {
         const int tok = tok0 + tile_col<TL>(tn, tid);
-        tok_ok[tn] = tok < nv;
-        lse_t[tn] = 0.f;
+        lse_t[tn] = __builtin_huge_valf();
         dl_t[tn] = 0.f;
-        lab_t[tn] = -1;
-        if (tok_ok[tn]) {
+        pl_t[tn] = 0.f;
+        lab_t[tn] = -1000;
+        if (tok < nv) {
             const int64_t row = idx[tok];
             lse_t[tn] = lse[row];
             dl_t[tn] = dloss[row];
@@ -415,12 +413,16 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
             const bool y_ok = y >= 0 && y < V;  // other labels are undefined by contract
             const int ypos = y_ok ? (inv_perm ? inv_perm[y] : (int)y) : -(1 << 30);
             const int lr = ypos - p0 - wm * TL::kWaveM;  // row within this wave's 128 vocabulary rows
-            lab_t[tn] = (lr >= 0 && lr < TL::kWaveM) ? ypos - p0 : -1;
-            any_label |= lab_t[tn] >= 0;
+            const bool here = lr >= 0 && lr < TL::kWaveM;
+            lab_t[tn] = here ? ypos - p0 - rbase : -1000;
+            any_label |= here;
+            // the label entry's own softmax probability where the block was
+            // not recomputed: from the forward's label logit, the same bits
+            // as the recompute (same MFMA code and K order) and the same formula
+            if (here && !wsoft) pl_t[tn] = __builtin_amdgcn_exp2f((zlab[row] - lse_t[tn]) * kLog2e);
         }
     }
     const int vlim = row_limit<TL>(V - p0, tid);  // entry (tm, r) is a real vocabulary row iff acc_row_const < vlim
-    const bool wsoft = SOFTMAX && ((qmask >> quad) & 1);  // this wave's block was recomputed (wave-uniform)
     if (wsoft) {
 #pragma unroll
         for (int tn = 0; tn < TL::TN; ++tn)
@@ -428,10 +430,11 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
             for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const bool ok = tok_ok[tn] && (acc_row_const(tm, r) < vlim);
+                    const bool ok = acc_row_const(tm, r) < vlim;
                     const float p = ok ? __builtin_amdgcn_exp2f((acc[tm][tn][r] - lse_t[tn]) * kLog2e) : 0.f;
                     acc[tm][tn][r] = p;
-                    any_live |= ok && (p >= eps);
+                    // the filter looks at the entries other than the label one
+                    any_live |= (p >= eps) && ok && acc_row_const(tm, r) != lab_t[tn];
                 }
     }
     const uint64_t bl = __ballot(any_live), bb = __ballot(any_label);
@@ -477,9 +480,12 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
                 for (int q = 0; q < 4; ++q) {
                     const int r = r4 * 4 + q;
                     const int rl = tile_row<TL>(tm, r, tid);
-                    const bool ok = tok_ok[tn] && (acc_row_const(tm, r) < vlim);
-                    const float onehot = rl == lab_t[tn] ? 1.f : 0.f;
-                    const float pk = (wsoft && status == 1) ? acc[tm][tn][r] : 0.f;
+                    const bool ok = acc_row_const(tm, r) < vlim && dl_t[tn] != 0.f;
+                    const bool il = acc_row_const(tm, r) == lab_t[tn];
+                    const float onehot = il ? 1.f : 0.f;
+                    // the label entry keeps its exact softmax part; the others only in a kept block
+                    const float pk = il ? (wsoft ? acc[tm][tn][r] : pl_t[tn])
+                                        : ((wsoft && status == 1) ? acc[tm][tn][r] : 0.f);
                     const float g = ok ? dl_t[tn] * (pk - onehot) : 0.f;
                     g4[q] = from_f32<T>(g);
                     // full dE: the vocabulary-major copy (read by dE) holds the unfiltered gradient
@@ -622,11 +628,11 @@ __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int
                 else recompute_vgpr<T, TL>(a.H, a.E, a.idx, nv, a.perm, a.D, a.V, tok0, p0, lds, acc);
                 __syncthreads();
                 g_epilogue<T, TL, true>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
-                                        a.lse, a.dloss, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
+                                        a.lse, a.dloss, a.zlab, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
                                         qflag, qstat, qslot, a.full_de, qmask);
             } else {
                 g_epilogue<T, TL, false>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
-                                         a.lse, a.dloss, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
+                                         a.lse, a.dloss, a.zlab, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
                                          qflag, qstat, qslot, a.full_de, 0);
             }
         }
@@ -1155,8 +1161,7 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     const int D = (int)s.D, V = (int)s.V;
     CCE_TRY(launch_compact(labels, s.N, ignore_index, w.idx, w.nvalid, st));
     if (perm) {
-        hipLaunchKernelGGL(k_inv_perm, dim3((unsigned)ceil_div(V, 256)), dim3(256), 0, st, perm, V, w.inv_perm);
-        CCE_LAUNCHED();
+        CCE_TRY(launch_inv_perm(perm, V, w.inv_perm, st));
     }
     if (stats) {
         hipLaunchKernelGGL(k_stats_init, dim3(1), dim3(64), 0, st, stats);
@@ -1222,6 +1227,9 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     a.labels = labels;
     a.lse = lse;
     a.dloss = dloss;
+    // the table's second part: the forward's label logits (read for label
+    // entries of tiles the bound leaves out)
+    a.zlab = tb ? tb + block_max_blocks(s.N, s.V) : nullptr;
     a.D = D;
     a.V = V;
     a.cbp = s.cbp;

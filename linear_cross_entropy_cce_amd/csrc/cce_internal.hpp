@@ -48,8 +48,10 @@ constexpr int64_t kOneBlock = INT64_MAX;  // v0 of a one-matrix classifier
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 // Entries of the block-max table: one per 128 x 128 block of the logit
-// matrix of the valid rows, [2 ceil(N / 256), 2 ceil(V / 256)].
-inline int64_t block_max_elems(int64_t N, int64_t V) { return 4 * ceil_div(N, kTileRows) * ceil_div(V, kTileVocab); }
+// matrix of the valid rows, [2 ceil(N / 256), 2 ceil(V / 256)], then the
+// label logit of each row [N].
+inline int64_t block_max_blocks(int64_t N, int64_t V) { return 4 * ceil_div(N, kTileRows) * ceil_div(V, kTileVocab); }
+inline int64_t block_max_elems(int64_t N, int64_t V) { return block_max_blocks(N, V) + N; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Carves a caller workspace into aligned regions (or only sizes it when the
@@ -76,6 +78,7 @@ FwdShape fwd_shape(int64_t N, int64_t D, int64_t V);
 struct FwdWs {
     int32_t *idx;      // [N] compacted valid-row indices
     int32_t *nvalid;   // [1]
+    int32_t *inv_perm; // [V] processing position of each vocabulary id (with a permutation and the table)
     float *part_m;     // [kFwdMaxGroups + n_rtiles, kTileRows] per segment: running max (log2 units)
     float *part_s;     // [kFwdMaxGroups + n_rtiles, kTileRows] per segment: sum of 2^(z log2e - m)
 };
@@ -137,6 +140,7 @@ hipError_t launch_compact(const int64_t *labels, int64_t N, int64_t ignore_index
                           int32_t *nvalid, hipStream_t st);
 hipError_t launch_check_labels(const int64_t *labels, int64_t N, int64_t V, int64_t ignore_index,
                                int64_t *n_bad, hipStream_t st);
+hipError_t launch_inv_perm(const int32_t *perm, int V, int32_t *inv, hipStream_t st);
 hipError_t launch_seg_labels(const int64_t *labels, int64_t N, int64_t ignore_index, int64_t V0, int64_t off1,
                              int64_t V1, int64_t *out, hipStream_t st);
 hipError_t launch_forward(cce_dtype dt, const void *H, const VocabRows &E, const int64_t *labels,

@@ -81,6 +81,15 @@ __global__ __launch_bounds__(1024) void k_check_labels(const int64_t *__restrict
     }
 }
 
+// ------------------------------------------------------- inverse permutation
+__global__ __launch_bounds__(256) void k_inv_perm(const int32_t *__restrict__ perm, int V, int32_t *__restrict__ inv) {
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k < V) {
+        const int v = perm[k];
+        if (v >= 0 && v < V) inv[v] = k;
+    }
+}
+
 // ------------------------------------------------------ composite labels
 // Labels of a composite head (ids [0, V0) in the first block, [off1, off1 +
 // V1) in the second, nothing in between) -> positions of the concatenated
@@ -138,11 +147,18 @@ __device__ __forceinline__ FwdPart fwd_part(int nv, int n_vtiles, int G) {
     return FwdPart{(int64_t)((nv + kTileRows - 1) / kTileRows) * n_vtiles, G};
 }
 
-// Returns the largest logit this lane holds in the tile (rows past V excluded).
-template <class TL>
+// Online max / sum-exp update with the tile's logits.  Returns the largest
+// logit this lane holds in the tile (rows past V excluded) other than a label
+// entry: with LAB, lpos[tn] is the processing position of token column tn's
+// label, that entry is left out of the returned maximum (it still enters the
+// sum) and its logit is written to zlab[lrow[tn]] (lrow < 0: no write).
+template <class TL, bool LAB>
 __device__ __forceinline__ float fwd_tile_update(f32x16 (&acc)[TL::TM][TL::TN], int v0, int V, float (&m)[TL::TN],
-                                                 float (&l)[TL::TN]) {
+                                                 float (&l)[TL::TN], const int (&lpos)[TL::TN],
+                                                 const int (&lrow)[TL::TN], float *__restrict__ zlab) {
     const bool full = v0 + TL::BM <= V;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rbase = (wave % TL::WM) * TL::kWaveM + 4 * (lane >> 5);  // tile_row = rbase + acc_row_const
     float tmax = kNegInf;
     // One token column at a time keeps at most TM x 16 values in VGPRs; the
     // scheduling barriers stop the compiler from hoisting every column's
@@ -166,7 +182,27 @@ __device__ __forceinline__ float fwd_tile_update(f32x16 (&acc)[TL::TM][TL::TN], 
                     mx = fmaxf(mx, acc[tm][tn][r]);
                 }
         }
-        tmax = fmaxf(tmax, mx);
+        float mxn = mx;
+        // The label entry of a token lies in one tile of the vocabulary: only
+        // there (and only in the lanes that hold it) is the maximum taken
+        // again without it and its logit kept.
+        const int lr = LAB ? lpos[tn] - v0 - rbase : -1;  // label row as acc_row_const, if in this lane
+        if (LAB && lr >= 0 && lr < TL::TM * 32) {
+            mxn = kNegInf;
+            float zl = 0.f;
+            bool hit = false;
+#pragma unroll
+            for (int tm = 0; tm < TL::TM; ++tm)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const bool il = acc_row_const(tm, r) == lr;
+                    mxn = fmaxf(mxn, il ? kNegInf : acc[tm][tn][r]);
+                    zl = il ? acc[tm][tn][r] : zl;
+                    hit |= il;
+                }
+            if (hit && lrow[tn] >= 0) zlab[lrow[tn]] = zl;
+        }
+        tmax = fmaxf(tmax, LAB ? mxn : mx);
         const float mn = fmaxf(m[tn], mx * kLog2e);
         if (mn == kNegInf) continue;
         float sum = 0.f;
@@ -180,8 +216,26 @@ __device__ __forceinline__ float fwd_tile_update(f32x16 (&acc)[TL::TM][TL::TN], 
     return tmax;
 }
 
-// Block-max table: the largest logit of every 128 x 128 block of the logit
-// matrix of the valid rows.  A wave of the 256 x 256 tile covers 128
+// Processing position of the label of each token column this lane holds
+// (-2^30 for none: a label out of range), and its row (-1 past the valid
+// rows).  Token columns past the valid rows hold a copy of the last valid
+// row, and take its label too.
+template <class TL>
+__device__ __forceinline__ void fwd_label_pos(int (&lpos)[TL::TN], int (&lrow)[TL::TN], int tok0, int nv,
+                                              const int32_t *__restrict__ idx, const int64_t *__restrict__ labels,
+                                              const int32_t *__restrict__ inv_perm, int V) {
+#pragma unroll
+    for (int tn = 0; tn < TL::TN; ++tn) {
+        const int t = tok0 + tile_col<TL>(tn);
+        const int row = idx[min(t, nv - 1)];
+        const int64_t y = labels[row];
+        lpos[tn] = (y >= 0 && y < V) ? (inv_perm ? inv_perm[y] : (int)y) : -(1 << 30);
+        lrow[tn] = t < nv ? row : -1;
+    }
+}
+
+// Block-max table: the largest logit other than a label entry of every
+// 128 x 128 block of the logit matrix of the valid rows.  A wave of the 256 x 256 tile covers 128
 // vocabulary rows x 64 tokens, half of one block; the two waves of a block
 // combine with an integer atomic max on the order-preserving encoding.  Lane
 // j of each wave keeps the maximum of the j-th tile of a group of 64 and the
@@ -270,14 +324,17 @@ __device__ __forceinline__ void fwd_write_partials(float (&m)[TL::TN], float (&l
 
 // One segment on the VGPR-staged pipeline: token tile rt, vocabulary tiles
 // [t0, t0 + ntile), partials to slot.
-template <typename T>
+template <typename T, bool LAB>
 __device__ __forceinline__ void fwd_segment(const T *__restrict__ H, Rows2<const T> E,
                                             const int32_t *__restrict__ idx, int nv, const int32_t *__restrict__ perm,
+                                            const int64_t *__restrict__ labels, const int32_t *__restrict__ inv_perm,
                                             int D, int V, int n_vtiles, int rt, int t0, int ntile, int64_t slot,
                                             u32x4 *lds, float *__restrict__ part_m, float *__restrict__ part_s,
-                                            int *__restrict__ tbound) {
+                                            int *__restrict__ tbound, float *__restrict__ zlab) {
     using TL = TileF;
     const int tok0 = rt * TL::BN;
+    int lpos[TL::TN], lrow[TL::TN];
+    if (LAB) fwd_label_pos<TL>(lpos, lrow, tok0, nv, idx, labels, inv_perm, V);
     const size_t rowb = (size_t)D * sizeof(T);
     const int kvalid = D * (int)sizeof(T);
     const int ns = (kvalid + TL::kStageBytes - 1) / TL::kStageBytes;
@@ -320,7 +377,7 @@ __device__ __forceinline__ void fwd_segment(const T *__restrict__ H, Rows2<const
             eng.compute(lds + (s & 1) * TL::kStage, acc);
             if (++ck == ns) {
                 ck = 0;
-                bs.tile(ct, fwd_tile_update<TL>(acc, (t0 + ct) * TL::BM, V, m, l), ct == ntile - 1);
+                bs.tile(ct, fwd_tile_update<TL, LAB>(acc, (t0 + ct) * TL::BM, V, m, l, lpos, lrow, zlab), ct == ntile - 1);
                 ++ct;
                 zero_acc<TL>(acc);
             }
@@ -338,8 +395,9 @@ __device__ __forceinline__ void fwd_segment(const T *__restrict__ H, Rows2<const
 template <typename T>
 __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
     const T *__restrict__ H, Rows2<const T> E, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, int D, int V, int n_vtiles,
-    float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
+    const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, const int64_t *__restrict__ labels,
+    const int32_t *__restrict__ inv_perm, int D, int V, int n_vtiles, float *__restrict__ part_m,
+    float *__restrict__ part_s, int *__restrict__ tbound, float *__restrict__ zlab) {
     __shared__ u32x4 lds[TileF::kLdsChunks];
     const int nv = *nvalid_p;
     if (nv <= 0) return;
@@ -350,8 +408,12 @@ __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
         const int rt = (int)(u / n_vtiles);
         const int t0 = (int)(u - (int64_t)rt * n_vtiles);
         const int ntile = (int)min((int64_t)(n_vtiles - t0), u1 - u);
-        fwd_segment<T>(H, E, idx, nv, perm, D, V, n_vtiles, rt, t0, ntile, (int64_t)L + rt, lds, part_m, part_s,
-                       tbound);
+        if (tbound)  // (the table leaves label entries out of its maxima)
+            fwd_segment<T, true>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile,
+                                 (int64_t)L + rt, lds, part_m, part_s, tbound, zlab);
+        else
+            fwd_segment<T, false>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile,
+                                  (int64_t)L + rt, lds, part_m, part_s, tbound, zlab);
         u += ntile;
     }
 }
@@ -361,15 +423,18 @@ __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
 // an operand are clamped to its last row: their logits are finite and masked
 // (vocabulary) or never written (tokens).  Needs D * sizeof(T) to be a
 // multiple of 128.
-template <typename T, class TL>
+template <typename T, class TL, bool LAB>
 __device__ __forceinline__ void fwd_segment_dma(const T *__restrict__ H, Rows2<const T> E,
                                                 const int32_t *__restrict__ idx, int nv,
-                                                const int32_t *__restrict__ perm, int D, int V, int n_vtiles, int rt,
-                                                int t0, int ntile, int64_t slot, u32x4 *lds,
+                                                const int32_t *__restrict__ perm, const int64_t *__restrict__ labels,
+                                                const int32_t *__restrict__ inv_perm, int D, int V, int n_vtiles,
+                                                int rt, int t0, int ntile, int64_t slot, u32x4 *lds,
                                                 float *__restrict__ part_m, float *__restrict__ part_s,
-                                                int *__restrict__ tbound) {
+                                                int *__restrict__ tbound, float *__restrict__ zlab) {
     using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
     const int tok0 = rt * TL::BN;
+    int lpos[TL::TN], lrow[TL::TN];
+    if (LAB) fwd_label_pos<TL>(lpos, lrow, tok0, nv, idx, labels, inv_perm, V);
     const size_t rowb = (size_t)D * sizeof(T);
     const int ns = D * (int)sizeof(T) / DE::kStageBytes;
     BoundSink bs{BoundSink::block_of<TL>(tbound, 2 * (int64_t)n_vtiles, rt, t0, nv)};
@@ -427,7 +492,7 @@ __device__ __forceinline__ void fwd_segment_dma(const T *__restrict__ H, Rows2<c
                 if (s + DE::kDepth < total) issue_at(s + DE::kDepth);
                 eng.compute(s % DE::kStages, acc);
             }
-            bs.tile(ct, fwd_tile_update<TL>(acc, (t0 + ct) * TL::BM, V, m, l), ct == ntile - 1);
+            bs.tile(ct, fwd_tile_update<TL, LAB>(acc, (t0 + ct) * TL::BM, V, m, l, lpos, lrow, zlab), ct == ntile - 1);
             zero_acc<TL>(acc);
         }
     }
@@ -437,8 +502,9 @@ __device__ __forceinline__ void fwd_segment_dma(const T *__restrict__ H, Rows2<c
 template <typename T, class TL>
 __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
     const T *__restrict__ H, Rows2<const T> E, const int32_t *__restrict__ idx,
-    const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, int D, int V, int n_vtiles,
-    float *__restrict__ part_m, float *__restrict__ part_s, int *__restrict__ tbound) {
+    const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, const int64_t *__restrict__ labels,
+    const int32_t *__restrict__ inv_perm, int D, int V, int n_vtiles, float *__restrict__ part_m,
+    float *__restrict__ part_s, int *__restrict__ tbound, float *__restrict__ zlab) {
     using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
     __shared__ u32x4 lds[DE::kLdsChunks];
     const int nv = *nvalid_p;
@@ -450,8 +516,12 @@ __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
         const int rt = (int)(u / n_vtiles);
         const int t0 = (int)(u - (int64_t)rt * n_vtiles);
         const int ntile = (int)min((int64_t)(n_vtiles - t0), u1 - u);
-        fwd_segment_dma<T, TL>(H, E, idx, nv, perm, D, V, n_vtiles, rt, t0, ntile, (int64_t)L + rt, lds, part_m,
-                               part_s, tbound);
+        if (tbound)  // (the table leaves label entries out of its maxima)
+            fwd_segment_dma<T, TL, true>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile,
+                                         (int64_t)L + rt, lds, part_m, part_s, tbound, zlab);
+        else
+            fwd_segment_dma<T, TL, false>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile,
+                                          (int64_t)L + rt, lds, part_m, part_s, tbound, zlab);
         u += ntile;
     }
 }
@@ -540,6 +610,7 @@ FwdWs fwd_ws(void *ws, const FwdShape &s, size_t *bytes) {
     FwdWs w;
     w.idx = c.take<int32_t>(s.N);
     w.nvalid = c.take<int32_t>(1);
+    w.inv_perm = c.take<int32_t>(s.V);
     // slots L + rt < G + n_rtiles, one partial per token of the tile each
     w.part_m = c.take<float>((size_t)(kFwdMaxGroups + s.n_rtiles) * kTileRows);
     w.part_s = c.take<float>((size_t)(kFwdMaxGroups + s.n_rtiles) * kTileRows);
@@ -550,6 +621,11 @@ FwdWs fwd_ws(void *ws, const FwdShape &s, size_t *bytes) {
 hipError_t launch_compact(const int64_t *labels, int64_t N, int64_t ignore_index, int32_t *idx,
                           int32_t *nvalid, hipStream_t st) {
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, labels, N, ignore_index, idx, nvalid);
+    return hipGetLastError();
+}
+
+hipError_t launch_inv_perm(const int32_t *perm, int V, int32_t *inv, hipStream_t st) {
+    hipLaunchKernelGGL(k_inv_perm, dim3((unsigned)ceil_div(V, 256)), dim3(256), 0, st, perm, V, inv);
     return hipGetLastError();
 }
 
@@ -574,9 +650,15 @@ static hipError_t forward_t(const T *H, Rows2<const T> E, const int64_t *labels,
     if (e != hipSuccess) return e;
     int *tb = reinterpret_cast<int *>(block_max);
     const int64_t nb = 4 * (int64_t)s.n_rtiles * s.n_vtiles;
+    const int32_t *invp = nullptr;  // label positions in the processing order, for the table
+    float *zl = tb ? block_max + nb : nullptr;  // the table's second part: label logits by row
     if (tb) {
         hipLaunchKernelGGL(k_bound_init, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, st, tb, nb);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (perm) {
+            if ((e = launch_inv_perm(perm, (int)s.V, w.inv_perm, st)) != hipSuccess) return e;
+            invp = w.inv_perm;
+        }
     }
     // A persistent grid: as many workgroups as are resident at once (every
     // one gets the same share of tiles), at most one per tile.
@@ -592,10 +674,10 @@ static hipError_t forward_t(const T *H, Rows2<const T> E, const int64_t *labels,
     if (G >= 8) G &= ~7;  // lets the placement give each XCD a contiguous eighth
     if (dma)
         hipLaunchKernelGGL((k_fwd_dma<T, TileFD>), dim3((unsigned)G), dim3(TileFD::kThreads), 0, st, H, E, w.idx,
-                           w.nvalid, perm, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb);
+                           w.nvalid, perm, labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
     else
         hipLaunchKernelGGL(k_fwd<T>, dim3((unsigned)G), dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid, perm,
-                           (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb);
+                           labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_merge<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, H, E, labels, w.idx,
                        w.nvalid, w.part_m, w.part_s, (int)G, s.n_vtiles, s.N, (int)s.D, s.V, ignore_index, loss,

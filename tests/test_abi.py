@@ -60,11 +60,12 @@ def test_workspace_has_no_per_logit_term(dt):
     per_v = (f(N, D, 512000, dt) - f(N, D, 256000, dt)) / 256000
     assert per_v <= 4 + 6 * N / 16384 + 5 * N / 65536 + 1
     # per row at fixed V: the fp32 dH accumulator, H^T and the block store
-    # (as many blocks as a dense slice of 8192 vocabulary columns, two layouts)
+    # (as many blocks as a dense slice of 8192 vocabulary columns, two
+    # layouts), the row index, label logit and mapped label (4 + 4 + 8 bytes)
     elem = 4 if dt == B.CCE_F32 else 2
     V = 256000
     per_n = (f(2 * N, D, V, dt) - f(N, D, V, dt)) / N
-    assert per_n <= 4 * D + elem * D + 2 * elem * 8192 + 6 * V / 16384 + 5 * V / 65536 + 16
+    assert per_n <= 4 * D + elem * D + 2 * elem * 8192 + 6 * V / 16384 + 5 * V / 65536 + 16 + 16
 
 
 def test_workspace_invalid_sizes_return_zero():
@@ -151,12 +152,13 @@ def test_backward_specific_errors():
 
 
 def test_block_max_elems():
-    # one entry per 128 x 128 logit block, over whole 256 x 256 tiles; 0 on invalid sizes
-    assert B.block_max_elems(1, 1) == 4
-    assert B.block_max_elems(256, 256) == 4
-    assert B.block_max_elems(257, 256) == 8
-    assert B.block_max_elems(8192, 256000) == 64 * 2000
-    assert B.block_max_elems(24576, 248320) == 192 * 1940
+    # one entry per 128 x 128 logit block, over whole 256 x 256 tiles, then one
+    # label logit per row; 0 on invalid sizes
+    assert B.block_max_elems(1, 1) == 4 + 1
+    assert B.block_max_elems(256, 256) == 4 + 256
+    assert B.block_max_elems(257, 256) == 8 + 257
+    assert B.block_max_elems(8192, 256000) == 64 * 2000 + 8192
+    assert B.block_max_elems(24576, 248320) == 192 * 1940 + 24576
     assert B.block_max_elems(0, 10) == 0
     assert B.block_max_elems(10, 0) == 0
 

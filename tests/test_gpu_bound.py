@@ -1,14 +1,15 @@
 """The block-max table and the recompute skip it allows.
 
-cce_forward can record the largest logit of every 128-token x 128-vocabulary
-block; cce_backward, given that table, leaves out the logit recompute of
-256 x 256 tiles whose every softmax entry is provably below filter_eps / 2.
+cce_forward can record the largest non-label logit of every 128-token x
+128-vocabulary block and the label logit of every row; cce_backward, given
+that table, leaves out the logit recompute of 256 x 256 tiles whose every
+non-label softmax entry is provably below filter_eps / 2.
 The gradient filter would drop all of such a tile's softmax part, so the
 outputs must be bit-identical to a run without the table; only the count of
 recomputed blocks (stats[4]) changes.  The table itself is checked against the
-definition: the largest fp64 logit of each block of the valid rows (in order)
-and the vocabulary in processing order (sorted when a permutation is given),
--inf for blocks past the valid rows.
+definition: the largest fp64 logit other than a label entry of each block of
+the valid rows (in order) and the vocabulary in processing order (sorted when
+a permutation is given), -inf for blocks past the valid rows.
 """
 import numpy as np
 import pytest
@@ -33,10 +34,14 @@ CASES = [
 def _ref_block_max(x, perm=None):
     H = oracle.as_f64(x.H, x.dtype)
     E = oracle.as_f64(x.E, x.dtype)
+    pos = np.arange(x.V)
     if perm is not None:
         E = E[perm]  # vocabulary in processing order
+        pos = np.empty(x.V, dtype=np.int64)
+        pos[perm] = np.arange(x.V)
     valid = np.nonzero(x.labels != x.ignore_index)[0]
     Z = H[valid] @ E.T  # the logits of the valid rows, in order
+    Z[np.arange(valid.size), pos[x.labels[valid]]] = -np.inf  # label entries are left out
     nrb, ncb = 2 * -(-x.N // 256), 2 * -(-x.V // 256)
     ref = np.full((nrb, ncb), -np.inf)
     for rb in range(-(-valid.size // BLK)):
@@ -55,12 +60,20 @@ def test_table_is_block_max(k, N, D, V, sort):
     if sort:
         assert np.array_equal(np.sort(out["perm"]), np.arange(x.V))
     ref = _ref_block_max(x, out.get("perm"))
-    got = out["block_max"].reshape(ref.shape)
+    got = out["block_max"][:ref.size].reshape(ref.shape)
     fin = np.isfinite(ref)
     assert np.all(got[~fin] == -np.inf), "blocks past the valid rows or vocabulary must stay -inf"
     err = np.abs(got[fin] - ref[fin]) / np.maximum(np.abs(ref[fin]), 1.0)
     tol = 1e-5 if x.dtype == "f32" else 1e-3
     assert err.max() <= tol, err.max()
+    # the second part: the label logit of every valid row
+    H = oracle.as_f64(x.H, x.dtype)
+    E = oracle.as_f64(x.E, x.dtype)
+    valid = np.nonzero(x.labels != x.ignore_index)[0]
+    zy = (H[valid] * E[x.labels[valid]]).sum(axis=1)
+    zg = out["block_max"][ref.size:][valid]
+    zerr = np.abs(zg - zy) / np.maximum(np.abs(zy), 1.0)
+    assert zerr.max() <= tol, zerr.max()
 
 
 @pytest.mark.parametrize("k,N,D,V", CASES, ids=[f"w{c[0]}" for c in CASES])
