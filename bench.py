@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="after the timed steps, copy this many bytes device-to-device (counter calibration)")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = about 20 s of work)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph and replayed (detail.graph_ms_per_step)")
     ap.add_argument("--torch-context", action="store_true",
                     help="also time PyTorch cross-entropy on materialised logits (whole and in 4096-row chunks)")
     return ap.parse_args()
@@ -197,6 +199,28 @@ def main():
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    graph_ms = None
+    if a.graph:
+        # The library only enqueues kernels, so the whole step can be captured
+        # and replayed; the same work with less launch overhead.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            step()
+        for _ in range(a.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(a.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - tg) * 1e3 / a.steps
+        print(f"[bench] graph replay {graph_ms:.3f} ms/step", file=sys.stderr, flush=True)
     fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
     bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
     sort_ms = [e[3].elapsed_time(e[0]) for e in evs]
@@ -238,6 +262,7 @@ def main():
         "detail": {
             "fwd_ms_mean": fwd_avg, "bwd_ms_mean": float(np.mean(bwd_ms)),
             "sort_ms_mean": float(np.mean(sort_ms)),
+            "graph_ms_per_step": graph_ms,
             "fwd_ms_min": float(np.min(fwd_ms)), "bwd_ms_min": float(np.min(bwd_ms)),
             "blocks_softmax_kept": n_live, "blocks_label_only": n_label, "blocks_total": n_total,
             "kept_frac": (n_live + n_label) / max(n_total, 1),
