@@ -96,6 +96,7 @@ struct BwdArgs {
     const int64_t *labels;
     const float *lse, *dloss;
     const float *zlab;  // [N] label logit of each valid row from the forward's tiles (with the table)
+    float *glab;        // [N] by valid-row position: gradient of the label entry of a label-only block, else 0
     int D, V, cbp, n_rb;
     float eps;
     int full_de;  // dE from every block (status 3 = kept for dE only), dH filtered
@@ -381,7 +382,7 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
                                            const int32_t *__restrict__ idx, const int32_t *__restrict__ inv_perm,
                                            const int64_t *__restrict__ labels, const float *__restrict__ lse,
                                            const float *__restrict__ dloss, const float *__restrict__ zlab,
-                                           T *__restrict__ Gt, T *__restrict__ Gn,
+                                           float *__restrict__ glab, T *__restrict__ Gt, T *__restrict__ Gn,
                                            int64_t cap, int32_t *__restrict__ counter, uint8_t *__restrict__ st,
                                            int32_t *__restrict__ slotm, int64_t *__restrict__ stats, int *qflag,
                                            int *qstat, int *qslot, int full_de, int qmask) {
@@ -465,6 +466,7 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
     __syncthreads();
     const int status = qstat[quad];
     if (status == 0) return;  // wave-uniform
+    const bool glab_only = status == 2;
     T *gt = Gt + (int64_t)qslot[quad] * kBlockElems;
     T *gn = Gn + (int64_t)qslot[quad] * kBlockElems;
 
@@ -491,9 +493,11 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
                     // full dE: the vocabulary-major copy (read by dE) holds the unfiltered gradient
                     const float gf = (wsoft && full_de && ok) ? dl_t[tn] * (acc[tm][tn][r] - onehot) : g;
                     gt[(rl - wm * kBlockVocab) * kBlockRows + tl] = from_f32<T>(gf);
+                    // label-only block: dH takes the label entry's gradient (fp32) from glab
+                    if (glab_only && il && ok) glab[tok0 + tile_col<TL>(tn, tid)] = g;
                 }
-                // rows r4*4 .. r4*4+3 are consecutive vocabulary entries (dH reads these; not for status 3)
-                if (status != 3) {
+                // rows r4*4 .. r4*4+3 are consecutive vocabulary entries (dH reads these; only for status 1)
+                if (status == 1) {
                     T *dst = gn + tl * kBlockVocab + tile_row<TL>(tm, r4 * 4, tid) - wm * kBlockVocab;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) dst[q] = g4[q];
@@ -628,11 +632,11 @@ __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int
                 else recompute_vgpr<T, TL>(a.H, a.E, a.idx, nv, a.perm, a.D, a.V, tok0, p0, lds, acc);
                 __syncthreads();
                 g_epilogue<T, TL, true>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
-                                        a.lse, a.dloss, a.zlab, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
+                                        a.lse, a.dloss, a.zlab, a.glab, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
                                         qflag, qstat, qslot, a.full_de, qmask);
             } else {
                 g_epilogue<T, TL, false>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
-                                         a.lse, a.dloss, a.zlab, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
+                                         a.lse, a.dloss, a.zlab, a.glab, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
                                          qflag, qstat, qslot, a.full_de, 0);
             }
         }
@@ -940,7 +944,9 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
                                         const uint8_t *__restrict__ st, const int32_t *__restrict__ slotm, int cbp,
                                         int nv, const int32_t *__restrict__ idx, const T *__restrict__ Gn,
                                         Rows2<const T> E, const int32_t *__restrict__ perm, int D, int V,
-                                        float *__restrict__ dh_acc, T *__restrict__ dH) {
+                                        const float *__restrict__ glab,
+                                        const int64_t *__restrict__ labels, float *__restrict__ dh_acc,
+                                        T *__restrict__ dH) {
     using TL = TileG;
     using DH = DhEngine<T>;
     const int tok0 = rb * TL::BM;
@@ -967,8 +973,12 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
     for (int base = cb0; base < cb1; base += kListCap) {
         const int cnt = cb1 - base < kListCap ? cb1 - base : kListCap;
         const int n = build_list<TL::kThreads>(
-            cnt, [&](int i) { const int v = st[(int64_t)rb * cbp + base + i]; return v == 1 || v == 2; }, sh.list,
-            sh.wcnt);
+            cnt,
+            [&](int i) {
+                const int v = st[(int64_t)rb * cbp + base + i];
+                return v == 1;  // label-only blocks: the label term below
+            },
+            sh.list, sh.wcnt);
         for (int i = threadIdx.x; i < n; i += TL::kThreads) sh.lslot[i] = slotm[(int64_t)rb * cbp + base + sh.list[i]];
         __syncthreads();
         any |= n > 0;
@@ -1007,6 +1017,25 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
         for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
             for (int r = 0; r < 16; ++r) row[tm][r] = idx[min(tok0 + tile_row<TL>(tm, r, tid), nv - 1)];
+        // The label term of the rows whose label block is label-only (kept out
+        // of the block products): dH_i += g_i e_{y_i}, after every block.
+        {
+#pragma unroll
+            for (int tm = 0; tm < TL::TM; ++tm)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int tok = tok0 + tile_row<TL>(tm, r, tid);
+                    const float g = tok < nv ? glab[tok] : 0.f;
+                    if (g != 0.f) {
+                        const T *e = E.row(labels[row[tm][r]]);
+#pragma unroll
+                        for (int tn = 0; tn < TL::TN; ++tn) {
+                            const int d = d0 + tile_col<TL>(tn, tid);
+                            if (d < D) sum[tm][tn][r] += g * to_f32(e[d]);
+                        }
+                    }
+                }
+        }
 #pragma unroll
         for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
@@ -1055,7 +1084,7 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
     int64_t it = take_ticket(queue, ticket);
     while (it < n_dh) {
         dh_item<T>(sh, (int)(it % n_rbv), (int)(it / n_rbv) * TL::BN, P > 1, p == P - 1, cb0, cb1, a.st, a.slot, a.cbp,
-                   nv, a.idx, a.Gn, a.E, a.perm, a.D, a.V, a.dh_acc, a.dH);
+                   nv, a.idx, a.Gn, a.E, a.perm, a.D, a.V, a.glab, a.labels, a.dh_acc, a.dH);
         it = take_ticket(queue, ticket);
     }
     while (it < n_dh + n_de) {
@@ -1122,6 +1151,7 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     w.nvalid = c.take<int32_t>(1);
     w.inv_perm = c.take<int32_t>(s.V);
     w.lmin = c.take<float>((size_t)s.n_rb);
+    w.glab = c.take<float>((size_t)s.Np);
     w.lab = c.take<uint8_t>(nblk);
     w.st = c.take<uint8_t>(nblk);
     w.slot = c.take<int32_t>(nblk);
@@ -1175,6 +1205,9 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
         hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)ceil_div(n, 1024)), dim3(256), 0, st, w.dh_acc, n);
         CCE_LAUNCHED();
     }
+    // Np % 4 == 0: whole f32x4 groups
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)ceil_div(s.Np, 1024)), dim3(256), 0, st, w.glab, s.Np);
+    CCE_LAUNCHED();
     T *Ht = static_cast<T *>(w.Ht);
     T *Gt = static_cast<T *>(w.Gt);
     T *Gn = static_cast<T *>(w.Gn);
@@ -1227,6 +1260,7 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     a.labels = labels;
     a.lse = lse;
     a.dloss = dloss;
+    a.glab = w.glab;
     // the table's second part: the forward's label logits (read for label
     // entries of tiles the bound leaves out)
     a.zlab = tb ? tb + block_max_blocks(s.N, s.V) : nullptr;

@@ -108,6 +108,7 @@ struct BwdWs {
     int32_t *nvalid;   // [1]
     int32_t *inv_perm; // [V] processing position of each vocabulary id
     float *lmin;       // [n_rb] smallest lse of each 128-token block (for the block-max bound)
+    float *glab;       // [Np] label-entry gradient of rows whose label block is label-only (else 0)
     uint8_t *lab;      // [n_rb, cbp] 1 where a label falls in the block
     uint8_t *st;       // [n_rb, cbp] block status: 0 dropped, 1 softmax kept, 2 label only
     int32_t *slot;     // [n_rb, cbp] store slot of a kept block
