@@ -1,8 +1,9 @@
 // Backward of the fused classifier-head + cross-entropy on gfx950.
 //
 // The backward recomputes the logits blockwise from H and E (no logits are
-// kept from the forward), skips blocks whose softmax entries all fall below a
-// threshold, and accumulates the classifier gradient with Kahan compensation
+// kept from the forward), skips blocks whose softmax entries (other than the
+// label entries, whose gradient dloss (p - 1) is always kept) all fall below
+// a threshold, and accumulates the classifier gradient with Kahan compensation
 // (CCE paper summary "Cut Your Losses in Large-Vocabulary Language Models",
 // sections "Approach" and "Limitations"; lit note "The loss and the mask: Cut
 // Cross-Entropy + FlexAttention", section "Contribution").
@@ -14,20 +15,24 @@
 // block store, and the two gradient products read it back:
 //
 //   plan        which 128 x 128 blocks may be kept: all of them, or, with the
-//               forward's block-max table, only blocks whose largest logit
-//               comes near the smallest lse of their rows, plus blocks holding
-//               a label; the 256 x 256 logit tiles holding such blocks are
-//               listed and cut, in vocabulary order, into passes whose blocks
-//               fit the store
-//   k_g_pass    per listed tile: recompute the logits (MFMA, the forward's
-//               code and K order), p = exp(z - lse), block filter, and the
-//               kept blocks' G into the store
+//               forward's block-max table, only blocks whose largest non-label
+//               logit comes near the smallest lse of their rows, plus blocks
+//               holding a label; the 256 x 256 logit tiles holding such blocks
+//               are listed and cut, in vocabulary order, into passes whose
+//               blocks fit the store
+//   k_g_pass    per listed tile: recompute the logits of the blocks that may
+//               keep a softmax part (MFMA, the forward's code and K order),
+//               p = exp(z - lse), block filter, and the kept blocks' G into
+//               the store; a label-only block (only label entries kept) gets
+//               its label entries from the forward's label logits when it was
+//               not recomputed, and records each row's label gradient
 //   k_grad_pass both products of the pass in one launch:
 //               dE_v = sum over kept row blocks of G^T H (MFMA), Kahan-
 //               compensated across row blocks, written once;
-//               dH_i = sum over kept vocabulary blocks of G E (MFMA with E
-//               read through the LDS transpose loads), the running sum kept
-//               in fp32 across passes
+//               dH_i = sum over blocks with a kept softmax part of G E (MFMA
+//               with E read through the LDS transpose loads), the running sum
+//               kept in fp32 across passes, plus g_i e_{y_i} for a row whose
+//               label block is label-only
 //
 // When the softmax is peaked almost every tile is dropped before its logits
 // are formed and one pass holds every kept block; when it is flat the passes
@@ -367,15 +372,19 @@ __global__ __launch_bounds__(1024) void k_plan(const uint8_t *__restrict__ tneed
 }
 
 // ------------------------------------------------------- recompute + G
-// Epilogue of a listed tile.  SOFTMAX: acc holds the recomputed logits and
-// p = exp(z - lse) decides each 128 x 128 block's status (1 = some p >= eps,
-// 2 = none but a label in it, 0 = dropped); otherwise (a tile left out by
-// the bound; acc is not read) only labels decide.  Kept blocks take a store
-// slot and their gradient g = dloss (p [status 1] - [v == y]) is written in
-// both layouts: Gt[slot][v][row] (read by dE) and Gn[slot][row][v] (read by
-// dH).  With full_de every real block is kept for dE: Gt holds the
+// Epilogue of a listed tile.  In the blocks of qmask acc holds the
+// recomputed logits and p = exp(z - lse) decides each 128 x 128 block's
+// status (1 = some p >= eps other than at a label entry, 2 = none but a
+// label in it, 0 = dropped); the other blocks (left out by the bound; acc is
+// not read) only have labels to decide.  A label entry's p comes from the
+// recompute or, in a block not recomputed, from the forward's label logit
+// (the same bits).  Kept blocks take a store slot and their gradient
+// g = dloss (p [status 1 or label entry] - [v == y]) is written to
+// Gt[slot][v][row] (read by dE) and, for status 1, to Gn[slot][row][v] (read
+// by dH); a label-only block records its label entries' g (fp32) in glab by
+// row instead.  With full_de every real block is kept for dE: Gt holds the
 // unfiltered dloss (p - [v == y]) and a block the filter drops gets status 3
-// (dE only; no Gn copy).
+// (dE only).
 template <typename T, class TL, bool SOFTMAX>
 __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int tok0, int nv, int p0,
                                            int V, int rt, int vt, int cbp, float eps,

@@ -242,7 +242,7 @@ __device__ __forceinline__ void fwd_label_pos(int (&lpos)[TL::TN], int (&lrow)[T
 // wave writes the group with one vector atomic, so the table costs one memory
 // instruction per 64 tiles.
 struct BoundSink {
-    int *row;   // this wave's block of the table at the split's first tile (stride 2 per tile); null: no table
+    int *row;   // this wave's block of the table at the segment's first tile (stride 2 per tile); null: no table
     int keep = 0;
     // (Token rows past the valid ones are copies of the last valid row, so a
     // block with some valid rows gets its true maximum; a block with none is
