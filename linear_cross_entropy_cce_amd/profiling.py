@@ -32,11 +32,19 @@ KERNEL = "k_fwd_dma"
 SOURCES = ("csrc/fwd.hip", "csrc/cce_device.hpp", "csrc/cce_internal.hpp")
 
 
+def _code_only(text: str) -> str:
+    """The source without comments and whitespace, so that only code changes
+    count (string literals in these files hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return "".join(text.split())
+
+
 def sources_hash() -> str:
     h = hashlib.sha256()
     for rel in SOURCES:
-        with open(os.path.join(PKG, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(PKG, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
