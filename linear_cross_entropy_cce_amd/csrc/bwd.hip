@@ -435,7 +435,12 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
     const int vlim = row_limit<TL>(V - p0, tid);  // entry (tm, r) is a real vocabulary row iff acc_row_const < vlim
     if (wsoft) {
 #pragma unroll
-        for (int tn = 0; tn < TL::TN; ++tn)
+        for (int tn = 0; tn < TL::TN; ++tn) {
+            // past the valid tokens p = 0, which eps = 0 would count as kept:
+            // a block with no valid token (recomputed by the VGPR-staged path,
+            // which computes every block) must stay dropped, since the pass
+            // plan only counts blocks that hold one
+            const bool tv = lse_t[tn] != __builtin_huge_valf();
 #pragma unroll
             for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
@@ -444,8 +449,9 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
                     const float p = ok ? __builtin_amdgcn_exp2f((acc[tm][tn][r] - lse_t[tn]) * kLog2e) : 0.f;
                     acc[tm][tn][r] = p;
                     // the filter looks at the entries other than the label one
-                    any_live |= (p >= eps) && ok && acc_row_const(tm, r) != lab_t[tn];
+                    any_live |= (p >= eps) && ok && tv && acc_row_const(tm, r) != lab_t[tn];
                 }
+        }
     }
     const uint64_t bl = __ballot(any_live), bb = __ballot(any_label);
     if (lane == 0 && (bl | bb)) atomicOr(&qflag[quad], (bl ? 1 : 0) | (bb ? 2 : 0));
@@ -468,7 +474,7 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
         if (stats) {
             if (sv == 1 || sv == 2) atomicAdd(reinterpret_cast<unsigned long long *>(stats + (sv == 1 ? 0 : 1)), 1ull);
             // blocks whose logits were recomputed (real rows and vocabulary entries only)
-            if (SOFTMAX && ((qmask >> tid) & 1))
+            if (SOFTMAX && ((qmask >> tid) & 1) && rb * kBlockRows < nv && (int64_t)cb * kBlockVocab < V)
                 atomicAdd(reinterpret_cast<unsigned long long *>(stats + 4), 1ull);
         }
     }

@@ -44,3 +44,21 @@ def test_multi_pass_matches_oracle():
     G.assert_grad("dH", out["dH"], dH, LH, 1e-2)
     G.assert_grad("dE", out["dE"], dE, LE, 1e-2)
     assert out["stats"][0] == out["stats"][2]
+
+
+def test_unfiltered_few_rows_vgpr_recompute():
+    """eps = 0 with one row block of valid tokens and a row block of padding,
+    on the VGPR-staged recompute (D * 2 not a multiple of 128), which computes
+    every block of a tile: the padding block's entries (p = 0) must not count
+    as kept, or the pass would hold more blocks than the plan made room for
+    and drop some.  782 vocabulary tiles x 2 real blocks: two passes."""
+    x = inputs.make_workload(3, N=100, D=72, V=200000)
+    G.say(f"unfiltered few rows N={x.N} D={x.D} V={x.V}")
+    dl = G.random_dloss(x, seed=9)
+    out = G.run_gpu(x, dl, eps=0.0)
+    _, _, dH, dE = G.oracle_full(x, dl, "random9")
+    LH, LE = G.label_term(x, dl)
+    G.assert_grad("dH", out["dH"], dH, LH, 1e-2)
+    G.assert_grad("dE", out["dE"], dE, LE, 1e-2)
+    # every real block kept, every real block recomputed, none other
+    assert out["stats"][0] == out["stats"][2] == out["stats"][4], out["stats"]
