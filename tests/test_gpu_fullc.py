@@ -19,14 +19,15 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("k,N,D,V,eps", CASES, ids=[f"w{c[0]}" for c in CASES])
-def test_full_de(k, N, D, V, eps):
+@pytest.mark.parametrize("k,N,D,V,eps,sort", [c + (False,) for c in CASES] + [(5, 480, 256, 9500, 2.0 ** -12, True)],
+                         ids=[f"w{c[0]}" for c in CASES] + ["w5-sort"])
+def test_full_de(k, N, D, V, eps, sort):
     x = inputs.make_workload(k, N=N, D=D, V=V)
-    G.say(f"full dE w{k} N={x.N} D={x.D} V={x.V} eps={eps}")
+    G.say(f"full dE w{k} N={x.N} D={x.D} V={x.V} eps={eps} sort={sort}")
     dl = G.random_dloss(x, seed=5)
-    full = G.run_gpu(x, dl, eps=eps, flags=B.CCE_BWD_FULL_DE)
-    filt = G.run_gpu(x, dl, eps=eps)
-    dense = G.run_gpu(x, dl, eps=0.0)
+    full = G.run_gpu(x, dl, eps=eps, flags=B.CCE_BWD_FULL_DE, sort=sort)
+    filt = G.run_gpu(x, dl, eps=eps, sort=sort)
+    dense = G.run_gpu(x, dl, eps=0.0, sort=sort)
     assert np.array_equal(full["dE"], dense["dE"]), "dE must be the unfiltered dE"
     assert np.array_equal(full["dH"], filt["dH"]), "dH must be the filtered dH"
     assert np.array_equal(full["stats"][:4], filt["stats"][:4])
