@@ -160,6 +160,17 @@ __device__ __forceinline__ float fwd_tile_update(f32x16 (&acc)[TL::TM][TL::TN], 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rbase = (wave % TL::WM) * TL::kWaveM + 4 * (lane >> 5);  // tile_row = rbase + acc_row_const
     float tmax = kNegInf;
+    if (!full) {
+        // the last vocabulary tile: rows past V hold copies of row V - 1
+        const int lim = row_limit<TL>(V - v0);
+#pragma unroll
+        for (int tn = 0; tn < TL::TN; ++tn)
+#pragma unroll
+            for (int tm = 0; tm < TL::TM; ++tm)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (acc_row_const(tm, r) >= lim) acc[tm][tn][r] = kNegInf;
+    }
     // One token column at a time keeps at most TM x 16 values in VGPRs; the
     // scheduling barriers stop the compiler from hoisting every column's
     // accumulator reads to the top (which would spill).
@@ -167,21 +178,10 @@ __device__ __forceinline__ float fwd_tile_update(f32x16 (&acc)[TL::TM][TL::TN], 
     for (int tn = 0; tn < TL::TN; ++tn) {
         __builtin_amdgcn_sched_barrier(0);
         float mx = kNegInf;
-        if (full) {
 #pragma unroll
-            for (int tm = 0; tm < TL::TM; ++tm)
+        for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[tm][tn][r]);
-        } else {
-            const int lim = row_limit<TL>(V - v0);
-#pragma unroll
-            for (int tm = 0; tm < TL::TM; ++tm)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    if (acc_row_const(tm, r) >= lim) acc[tm][tn][r] = kNegInf;
-                    mx = fmaxf(mx, acc[tm][tn][r]);
-                }
-        }
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[tm][tn][r]);
         float mxn = mx;
         // The label entry of a token lies in one tile of the vocabulary: only
         // there (and only in the lanes that hold it) is the maximum taken
@@ -392,7 +392,11 @@ __device__ __forceinline__ void fwd_segment(const T *__restrict__ H, Rows2<const
     fwd_write_partials<TL>(m, l, reinterpret_cast<float *>(lds), tok0, nv, slot, part_m, part_s);
 }
 
-template <typename T>
+// LAB: the block-max table is written (its maxima leave label entries out).
+// One kernel per value rather than a branch inside one: with both paths in
+// one kernel the scalar registers of the label bookkeeping spilled into the
+// tile loop of either path.
+template <typename T, bool LAB>
 __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
     const T *__restrict__ H, Rows2<const T> E, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, const int64_t *__restrict__ labels,
@@ -408,12 +412,8 @@ __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
         const int rt = (int)(u / n_vtiles);
         const int t0 = (int)(u - (int64_t)rt * n_vtiles);
         const int ntile = (int)min((int64_t)(n_vtiles - t0), u1 - u);
-        if (tbound)  // (the table leaves label entries out of its maxima)
-            fwd_segment<T, true>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile,
-                                 (int64_t)L + rt, lds, part_m, part_s, tbound, zlab);
-        else
-            fwd_segment<T, false>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile,
-                                  (int64_t)L + rt, lds, part_m, part_s, tbound, zlab);
+        fwd_segment<T, LAB>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile, (int64_t)L + rt,
+                            lds, part_m, part_s, tbound, zlab);
         u += ntile;
     }
 }
@@ -499,7 +499,7 @@ __device__ __forceinline__ void fwd_segment_dma(const T *__restrict__ H, Rows2<c
     fwd_write_partials<TL>(m, l, reinterpret_cast<float *>(lds), tok0, nv, slot, part_m, part_s);
 }
 
-template <typename T, class TL>
+template <typename T, class TL, bool LAB>
 __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
     const T *__restrict__ H, Rows2<const T> E, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, const int64_t *__restrict__ labels,
@@ -516,12 +516,8 @@ __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
         const int rt = (int)(u / n_vtiles);
         const int t0 = (int)(u - (int64_t)rt * n_vtiles);
         const int ntile = (int)min((int64_t)(n_vtiles - t0), u1 - u);
-        if (tbound)  // (the table leaves label entries out of its maxima)
-            fwd_segment_dma<T, TL, true>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile,
-                                         (int64_t)L + rt, lds, part_m, part_s, tbound, zlab);
-        else
-            fwd_segment_dma<T, TL, false>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile,
-                                          (int64_t)L + rt, lds, part_m, part_s, tbound, zlab);
+        fwd_segment_dma<T, TL, LAB>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile,
+                                    (int64_t)L + rt, lds, part_m, part_s, tbound, zlab);
         u += ntile;
     }
 }
@@ -666,18 +662,31 @@ static hipError_t forward_t(const T *H, Rows2<const T> E, const int64_t *labels,
     int dev = 0, cus = 0, per_cu = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    e = dma ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fwd_dma<T, TileFD>, TileFD::kThreads, 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fwd<T>, TileF::kThreads, 0);
+    if (dma && tb)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fwd_dma<T, TileFD, true>, TileFD::kThreads, 0);
+    else if (dma)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fwd_dma<T, TileFD, false>, TileFD::kThreads, 0);
+    else if (tb)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fwd<T, true>, TileF::kThreads, 0);
+    else
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fwd<T, false>, TileF::kThreads, 0);
     if (e != hipSuccess) return e;
     int64_t G = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
     G = std::min<int64_t>(std::min<int64_t>(G, kFwdMaxGroups), (int64_t)s.n_rtiles * s.n_vtiles);
     if (G >= 8) G &= ~7;  // lets the placement give each XCD a contiguous eighth
-    if (dma)
-        hipLaunchKernelGGL((k_fwd_dma<T, TileFD>), dim3((unsigned)G), dim3(TileFD::kThreads), 0, st, H, E, w.idx,
-                           w.nvalid, perm, labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
+    const dim3 grid((unsigned)G);
+    if (dma && tb)
+        hipLaunchKernelGGL((k_fwd_dma<T, TileFD, true>), grid, dim3(TileFD::kThreads), 0, st, H, E, w.idx, w.nvalid,
+                           perm, labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
+    else if (dma)
+        hipLaunchKernelGGL((k_fwd_dma<T, TileFD, false>), grid, dim3(TileFD::kThreads), 0, st, H, E, w.idx, w.nvalid,
+                           perm, labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
+    else if (tb)
+        hipLaunchKernelGGL((k_fwd<T, true>), grid, dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid, perm, labels,
+                           invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
     else
-        hipLaunchKernelGGL(k_fwd<T>, dim3((unsigned)G), dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid, perm,
-                           labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
+        hipLaunchKernelGGL((k_fwd<T, false>), grid, dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid, perm, labels,
+                           invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_merge<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, H, E, labels, w.idx,
                        w.nvalid, w.part_m, w.part_s, (int)G, s.n_vtiles, s.N, (int)s.D, s.V, ignore_index, loss,
