@@ -17,6 +17,19 @@ the logit kernel's reading.
 
 The traffic summary records a hash of the kernel's sources; `bench.py`
 reports the traffic only while the sources still hash the same.
+
+Core counters of the forward logit kernel (one pass, within the per-block
+limits of a single rocprofv3 run):
+
+    rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_LDS_BANK_CONFLICT \
+        SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAVES GRBM_GUI_ACTIVE --output-format csv -d DIR -o p -- CMD
+    python -m linear_cross_entropy_cce_amd.profiling counters --dir DIR --command "..." \
+        --out profiles/<kernel>_<workload>_counters.md
+
+MFMA-busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x
+SIMDs); GRBM_GUI_ACTIVE is summed over the XCDs, so per XCD it is the
+kernel's length in GPU clock cycles and, over the dispatch's duration, the
+average clock.
 """
 from __future__ import annotations
 
@@ -126,6 +139,66 @@ def load(path: str):
     return float(m.group(1)), h.group(1)
 
 
+COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_LDS_BANK_CONFLICT",
+            "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS", "SQ_WAVES", "GRBM_GUI_ACTIVE")
+
+
+def _agent(directory: str) -> dict:
+    for path in glob.glob(os.path.join(directory, "**", "*agent_info.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Name", "").startswith("gfx"):
+                    return r
+    raise FileNotFoundError(f"no GPU agent in {directory}")
+
+
+def write_counters_md(path: str, directory: str, command: str, title: str) -> dict:
+    paths = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise FileNotFoundError(f"no counter_collection.csv under {directory}")
+    disp = {}
+    for p in paths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if KERNEL not in r["Kernel_Name"]:
+                    continue
+                d = disp.setdefault((p, r["Dispatch_Id"]), {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not disp:
+        raise RuntimeError(f"no {KERNEL} dispatch in {directory}")
+    ag = _agent(directory)
+    n_xcc, n_simd = int(ag["Num_Xcc"]), int(ag["Simd_Count"])
+    avg = {c: sum(d.get(c, 0.0) for d in disp.values()) / len(disp) for c in COUNTERS + ("ns",)}
+    cycles = avg["GRBM_GUI_ACTIVE"] / n_xcc
+    res = {
+        "dispatches": len(disp),
+        "duration_us": avg["ns"] / 1e3,
+        "mfma_insts": avg["SQ_INSTS_MFMA"],
+        "mfma_busy": avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * n_simd),
+        "cycles_per_mfma": avg["SQ_VALU_MFMA_BUSY_CYCLES"] / max(avg["SQ_INSTS_MFMA"], 1.0),
+        "clock_ghz": cycles / avg["ns"],
+        "lds_conflict_frac": avg["SQ_LDS_BANK_CONFLICT"] / max(avg["SQ_LDS_IDX_ACTIVE"], 1.0),
+        "waves": avg["SQ_WAVES"],
+    }
+    lines = [f"# {title}", "", "Command (on the MI355X box, from the repository root):", "", f"    {command}", "",
+             "Summarised with:", "",
+             f"    python -m linear_cross_entropy_cce_amd.profiling counters --dir {directory} --out {path}", "",
+             f"{len(disp)} dispatches of `{KERNEL}`; agent: {ag['Name']}, {n_xcc} XCDs, {n_simd} SIMDs.", "",
+             "| counter | average per dispatch |", "|---|---|"]
+    for c in COUNTERS:
+        lines.append(f"| {c} | {avg[c]:.6g} |")
+    lines += ["", "| derived | value |", "|---|---|",
+              f"| dispatch duration | {res['duration_us']:.1f} us |",
+              f"| MFMA instructions | {res['mfma_insts']:.6g} |",
+              f"| MFMA busy cycles per instruction | {res['cycles_per_mfma']:.2f} |",
+              f"| MFMA busy (of all SIMD cycles) | {100 * res['mfma_busy']:.1f} % |",
+              f"| average GPU clock over the dispatch | {res['clock_ghz']:.2f} GHz |",
+              f"| LDS bank-conflict cycles / LDS active cycles | {res['lds_conflict_frac']:.2e} |", ""]
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    return res
+
+
 def write_stats_md(path: str, directory: str, steps: int, command: str, title: str) -> None:
     paths = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
     if not paths:
@@ -166,8 +239,17 @@ def main():
     k.add_argument("--command", required=True)
     k.add_argument("--title", required=True)
     k.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--dir", required=True)
+    c.add_argument("--command", default="rocprofv3 --pmc " + " ".join(COUNTERS) + " --output-format csv "
+                                         "-d gpurun_out/pmc_core -o p -- python -u bench.py --steps 1 --warmup 1 "
+                                         "--no-cpu-baseline")
+    c.add_argument("--title", default="Core counters of `k_fwd_dma`: Gemma-2-2B head (N=8192, D=2304, V=256000, bf16)")
+    c.add_argument("--out", required=True)
     a = ap.parse_args()
-    if a.what == "traffic":
+    if a.what == "counters":
+        write_counters_md(a.out, a.dir, a.command, a.title)
+    elif a.what == "traffic":
         s = summarize(a.fetch, a.write, a.copy_bytes)
         write_md(a.out, s, a.copy_bytes, a.command)
     else:
