@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = about 20 s of work)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph and replayed (detail.graph_ms_per_step)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time the forward's contraction H E^T alone through the vendor BLAS (bf16 logits out)")
     ap.add_argument("--torch-context", action="store_true",
                     help="also time PyTorch cross-entropy on materialised logits (whole and in 4096-row chunks)")
     return ap.parse_args()
@@ -63,7 +65,7 @@ def cpu_baseline(x, n_rows_hint):
     E64 = oracle.as_f64(x.E, x.dtype)
     threads = oracle.threads()
     per_row_flops = 8.0 * x.D * x.V  # logits twice, dH row, dE contributions
-    rows_n = n_rows_hint or max(threads, int(round(20.0 * threads * 1.2e9 / per_row_flops)))
+    rows_n = n_rows_hint or max(threads, int(round(20.0 * threads * 4.5e9 / per_row_flops)))  # ~4.5 GFLOP/s a thread
     rows_n = max(1, min(rows_n, x.N))
     rng = np.random.default_rng(0)
     valid = np.nonzero(x.labels != x.ignore_index)[0]
@@ -83,6 +85,32 @@ def cpu_baseline(x, n_rows_hint):
     return {"value": len(rows) / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {x.N} rows (full D={x.D}, V={x.V}): lse, loss, dH rows and their dE "
                       f"contributions over all V, fp64, {t:.1f} s"}
+
+
+def library_gemm(H, E, fwd_ms, reps=5):
+    """The forward's contraction alone, H E^T for all rows, through torch's
+    matmul (the vendor BLAS, hipBLASLt on ROCm) into a bf16 [N, V] logit
+    tensor: the rate a library GEMM sustains on this shape, for context.  It
+    computes no softmax and writes the logits the fused forward never stores."""
+    import numpy as np
+    import torch
+
+    out = torch.empty(H.shape[0], E.shape[0], dtype=H.dtype, device=H.device)
+    Et = E.t()
+    for _ in range(2):
+        torch.matmul(H, Et, out=out)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        torch.matmul(H, Et, out=out)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    del out
+    flops = 2.0 * H.shape[0] * H.shape[1] * E.shape[0]
+    return {"ms": ms, "TFLOP_per_s": flops / (ms * 1e-3) / 1e12, "logits_GB": H.shape[0] * E.shape[0] * H.element_size() / 1e9,
+            "fused_forward_over_library": fwd_ms / ms}
 
 
 def torch_context(H, E, y, ignore_index, reps=3, chunk=4096):
@@ -276,6 +304,9 @@ def main():
             "valid_tokens_per_s": nv / (step_ms * 1e-3),
         },
     }
+    if a.library_gemm:
+        print("[bench] library gemm", file=sys.stderr, flush=True)
+        out["library_gemm"] = library_gemm(H, E, fwd_avg)
     if a.torch_context:
         print("[bench] torch context", file=sys.stderr, flush=True)
         out["torch_context"] = torch_context(H, E, y, x.ignore_index)

@@ -152,48 +152,66 @@ def _agent(directory: str) -> dict:
     raise FileNotFoundError(f"no GPU agent in {directory}")
 
 
-def write_counters_md(path: str, directory: str, command: str, title: str) -> dict:
+def write_counters_md(path: str, directory: str, command: str, title: str,
+                      kernels=(KERNEL,), counters=COUNTERS) -> dict:
+    """Per-dispatch averages of one --pmc pass for each kernel whose name
+    contains one of `kernels`, side by side, with the derived MFMA busy
+    fraction, cycles per MFMA and average clock where the counters allow."""
     paths = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
     if not paths:
         raise FileNotFoundError(f"no counter_collection.csv under {directory}")
-    disp = {}
+    disp = {k: {} for k in kernels}
+    names = {}
     for p in paths:
         with open(p) as f:
             for r in csv.DictReader(f):
-                if KERNEL not in r["Kernel_Name"]:
+                k = next((k for k in kernels if k in r["Kernel_Name"]), None)
+                if k is None:
                     continue
-                d = disp.setdefault((p, r["Dispatch_Id"]), {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                names.setdefault(k, r["Kernel_Name"].split("(")[0])
+                d = disp[k].setdefault((p, r["Dispatch_Id"]),
+                                       {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
                 d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    if not disp:
-        raise RuntimeError(f"no {KERNEL} dispatch in {directory}")
+    missing = [k for k in kernels if not disp[k]]
+    if missing:
+        raise RuntimeError(f"no dispatch of {missing} in {directory}")
     ag = _agent(directory)
     n_xcc, n_simd = int(ag["Num_Xcc"]), int(ag["Simd_Count"])
-    avg = {c: sum(d.get(c, 0.0) for d in disp.values()) / len(disp) for c in COUNTERS + ("ns",)}
-    cycles = avg["GRBM_GUI_ACTIVE"] / n_xcc
-    res = {
-        "dispatches": len(disp),
-        "duration_us": avg["ns"] / 1e3,
-        "mfma_insts": avg["SQ_INSTS_MFMA"],
-        "mfma_busy": avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * n_simd),
-        "cycles_per_mfma": avg["SQ_VALU_MFMA_BUSY_CYCLES"] / max(avg["SQ_INSTS_MFMA"], 1.0),
-        "clock_ghz": cycles / avg["ns"],
-        "lds_conflict_frac": avg["SQ_LDS_BANK_CONFLICT"] / max(avg["SQ_LDS_IDX_ACTIVE"], 1.0),
-        "waves": avg["SQ_WAVES"],
-    }
+    res = {}
+    for k in kernels:
+        dd = disp[k].values()
+        avg = {c: sum(d.get(c, 0.0) for d in dd) / len(dd) for c in tuple(counters) + ("ns",)}
+        r = {"dispatches": len(dd), "duration_us": avg["ns"] / 1e3, "avg": avg}
+        if "GRBM_GUI_ACTIVE" in counters:
+            cycles = avg["GRBM_GUI_ACTIVE"] / n_xcc
+            r["clock_ghz"] = cycles / avg["ns"]
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
+                r["mfma_busy"] = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * n_simd)
+        if "SQ_INSTS_MFMA" in counters and "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
+            r["cycles_per_mfma"] = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / max(avg["SQ_INSTS_MFMA"], 1.0)
+        if "SQ_LDS_BANK_CONFLICT" in counters and "SQ_LDS_IDX_ACTIVE" in counters:
+            r["lds_conflict_frac"] = avg["SQ_LDS_BANK_CONFLICT"] / max(avg["SQ_LDS_IDX_ACTIVE"], 1.0)
+        res[k] = r
+    cols = " | ".join(f"`{names[k]}`" for k in kernels)
     lines = [f"# {title}", "", "Command (on the MI355X box, from the repository root):", "", f"    {command}", "",
              "Summarised with:", "",
-             f"    python -m linear_cross_entropy_cce_amd.profiling counters --dir {directory} --out {path}", "",
-             f"{len(disp)} dispatches of `{KERNEL}`; agent: {ag['Name']}, {n_xcc} XCDs, {n_simd} SIMDs.", "",
-             "| counter | average per dispatch |", "|---|---|"]
-    for c in COUNTERS:
-        lines.append(f"| {c} | {avg[c]:.6g} |")
-    lines += ["", "| derived | value |", "|---|---|",
-              f"| dispatch duration | {res['duration_us']:.1f} us |",
-              f"| MFMA instructions | {res['mfma_insts']:.6g} |",
-              f"| MFMA busy cycles per instruction | {res['cycles_per_mfma']:.2f} |",
-              f"| MFMA busy (of all SIMD cycles) | {100 * res['mfma_busy']:.1f} % |",
-              f"| average GPU clock over the dispatch | {res['clock_ghz']:.2f} GHz |",
-              f"| LDS bank-conflict cycles / LDS active cycles | {res['lds_conflict_frac']:.2e} |", ""]
+             f"    python -m linear_cross_entropy_cce_amd.profiling counters --dir {directory} --out {path}"
+             + ("" if tuple(kernels) == (KERNEL,) else " --kernels " + " ".join(kernels))
+             + ("" if tuple(counters) == COUNTERS else " --counters " + " ".join(counters)), "",
+             f"Agent: {ag['Name']}, {n_xcc} XCDs, {n_simd} SIMDs; dispatches averaged: "
+             + ", ".join(f"{res[k]['dispatches']} of `{k}`" for k in kernels) + ".", "",
+             f"| counter (average per dispatch) | {cols} |", "|---" * (len(kernels) + 1) + "|"]
+    for c in counters:
+        lines.append(f"| {c} | " + " | ".join(f"{res[k]['avg'][c]:.6g}" for k in kernels) + " |")
+    lines += ["", f"| derived | {cols} |", "|---" * (len(kernels) + 1) + "|",
+              "| dispatch duration | " + " | ".join(f"{res[k]['duration_us']:.1f} us" for k in kernels) + " |"]
+    for key, label, fmt in (("cycles_per_mfma", "MFMA busy cycles per instruction", "{:.2f}"),
+                            ("mfma_busy", "MFMA busy (of all SIMD cycles)", "{:.1%}"),
+                            ("clock_ghz", "average GPU clock over the dispatch", "{:.2f} GHz"),
+                            ("lds_conflict_frac", "LDS bank-conflict cycles / LDS active cycles", "{:.2e}")):
+        if all(key in res[k] for k in kernels):
+            lines.append(f"| {label} | " + " | ".join(fmt.format(res[k][key]) for k in kernels) + " |")
+    lines.append("")
     with open(path, "w") as f:
         f.write("\n".join(lines))
     return res
@@ -246,9 +264,11 @@ def main():
                                          "--no-cpu-baseline")
     c.add_argument("--title", default="Core counters of `k_fwd_dma`: Gemma-2-2B head (N=8192, D=2304, V=256000, bf16)")
     c.add_argument("--out", required=True)
+    c.add_argument("--kernels", nargs="+", default=[KERNEL], help="kernel-name substrings, one column each")
+    c.add_argument("--counters", nargs="+", default=list(COUNTERS))
     a = ap.parse_args()
     if a.what == "counters":
-        write_counters_md(a.out, a.dir, a.command, a.title)
+        write_counters_md(a.out, a.dir, a.command, a.title, tuple(a.kernels), tuple(a.counters))
     elif a.what == "traffic":
         s = summarize(a.fetch, a.write, a.copy_bytes)
         write_md(a.out, s, a.copy_bytes, a.command)
