@@ -93,7 +93,8 @@ def summarize(fetch_dir: str, write_dir: str, copy_bytes: int) -> dict:
     return out
 
 
-def write_md(path: str, s: dict, copy_bytes: int, command: str) -> None:
+def write_md(path: str, s: dict, copy_bytes: int, command: str, fetch_dir: str = "pmc_FETCH_SIZE",
+             write_dir: str = "pmc_WRITE_SIZE") -> None:
     lines = [
         f"# HBM traffic of `{KERNEL}`: Gemma-2-2B head (N=8192, D=2304, V=256000, bf16)",
         "",
@@ -104,8 +105,8 @@ def write_md(path: str, s: dict, copy_bytes: int, command: str) -> None:
         "",
         "Summarised with:",
         "",
-        f"    python -m linear_cross_entropy_cce_amd.profiling traffic --fetch gpurun_out/pmc_FETCH_SIZE "
-        f"--write gpurun_out/pmc_WRITE_SIZE --copy-bytes {copy_bytes} --out {os.path.relpath(path, os.path.dirname(PKG))}",
+        f"    python -m linear_cross_entropy_cce_amd.profiling traffic --fetch {fetch_dir} "
+        f"--write {write_dir} --copy-bytes {copy_bytes} --out {os.path.relpath(path, os.path.dirname(PKG))}",
         "",
         f"Calibration: torch's device copy of {copy_bytes} bytes in the same run (reads and writes that many bytes).",
         "FETCH_SIZE and WRITE_SIZE count the L2's requests to the memory fabric, so reads served by the",
@@ -248,7 +249,7 @@ def main():
     t.add_argument("--write", required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--out", required=True)
-    t.add_argument("--command", default="rocprofv3 --pmc COUNTER --output-format csv -d gpurun_out/pmc_COUNTER -o p "
+    t.add_argument("--command", default="rocprofv3 --pmc COUNTER --output-format csv -d pmc_COUNTER -o p "
                                          "-- python -u bench.py --steps 1 --warmup 1 --no-cpu-baseline "
                                          "--copy-probe 1073741824")
     k = sub.add_parser("stats")
@@ -260,7 +261,7 @@ def main():
     c = sub.add_parser("counters")
     c.add_argument("--dir", required=True)
     c.add_argument("--command", default="rocprofv3 --pmc " + " ".join(COUNTERS) + " --output-format csv "
-                                         "-d gpurun_out/pmc_core -o p -- python -u bench.py --steps 1 --warmup 1 "
+                                         "-d pmc_core -o p -- python -u bench.py --steps 1 --warmup 1 "
                                          "--no-cpu-baseline")
     c.add_argument("--title", default="Core counters of `k_fwd_dma`: Gemma-2-2B head (N=8192, D=2304, V=256000, bf16)")
     c.add_argument("--out", required=True)
@@ -271,7 +272,7 @@ def main():
         write_counters_md(a.out, a.dir, a.command, a.title, tuple(a.kernels), tuple(a.counters))
     elif a.what == "traffic":
         s = summarize(a.fetch, a.write, a.copy_bytes)
-        write_md(a.out, s, a.copy_bytes, a.command)
+        write_md(a.out, s, a.copy_bytes, a.command, a.fetch, a.write)
     else:
         write_stats_md(a.out, a.dir, a.steps, a.command, a.title)
     print(open(a.out).read())
