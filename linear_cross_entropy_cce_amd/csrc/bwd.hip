@@ -564,9 +564,13 @@ __device__ __forceinline__ void recompute_dma(const T *__restrict__ H, Rows2<con
     for (int s = 0; s < ns; ++s) {
         const int ahead = ns - 1 - s;
         eng.wait_stage(eng.clamp_ahead(ahead));
+        // as in the forward: the first K-slice's MFMAs before the next DMA
+        if (active) eng.compute(s % DE::kStages, acc, tid, 0, 1);
+        __builtin_amdgcn_sched_barrier(0);
         if (s + DE::kDepth < ns)
             eng.issue_halves((s + DE::kDepth) % DE::kStages, (s + DE::kDepth) * DE::kStageBytes, halves);
-        if (active) eng.compute(s % DE::kStages, acc, tid);
+        __builtin_amdgcn_sched_barrier(0);
+        if (active) eng.compute(s % DE::kStages, acc, tid, 1, DE::kCpr / 2);
     }
 }
 

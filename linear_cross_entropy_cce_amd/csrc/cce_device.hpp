@@ -356,14 +356,17 @@ struct DmaEngine {
     }
     __device__ __forceinline__ int clamp_ahead(int ahead) const { return ahead < kDepth - 1 ? ahead : kDepth - 1; }
 
-    __device__ __forceinline__ void compute(int buf, f32x16 (&acc)[TL::TM][TL::TN], int tid = threadIdx.x) const {
+    // The MFMAs of K-slices [kk0, kk1) of stage buf (32 bytes of every row per
+    // slice, in K order).
+    __device__ __forceinline__ void compute(int buf, f32x16 (&acc)[TL::TM][TL::TN], int tid = threadIdx.x,
+                                           int kk0 = 0, int kk1 = kCpr / 2) const {
         const int lane = tid & 63, wave = tid >> 6;
         const int ra0 = (wave % TL::WM) * TL::kWaveM + (lane & 31);
         const int rb0 = (wave / TL::WM) * TL::kWaveN + (lane & 31);
         const u32x4 *A = lds + buf * kStage;
         const u32x4 *B = A + kStageA;
 #pragma unroll
-        for (int kk = 0; kk < kCpr / 2; ++kk) {
+        for (int kk = kk0; kk < kk1; ++kk) {
             const int c = 2 * kk + (lane >> 5);
             u32x4 fa[TL::TM], fb[TL::TN];
 #pragma unroll

@@ -489,8 +489,15 @@ __device__ __forceinline__ void fwd_segment_dma(const T *__restrict__ H, Rows2<c
             for (int k = 0; k < ns; ++k, ++s) {
                 const int ahead = total - 1 - s;
                 eng.wait_stage(eng.clamp_ahead(ahead));
+                // The first K-slice's MFMAs go out before the next stage's DMA
+                // instructions: every wave reaches this point at once, and
+                // issuing the DMA first left the matrix cores idle meanwhile
+                // (1-2 % of the kernel).  Same MFMAs in the same order.
+                eng.compute(s % DE::kStages, acc, threadIdx.x, 0, 1);
+                __builtin_amdgcn_sched_barrier(0);
                 if (s + DE::kDepth < total) issue_at(s + DE::kDepth);
-                eng.compute(s % DE::kStages, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                eng.compute(s % DE::kStages, acc, threadIdx.x, 1, DE::kCpr / 2);
             }
             bs.tile(ct, fwd_tile_update<TL, LAB>(acc, (t0 + ct) * TL::BM, V, m, l, lpos, lrow, zlab), ct == ntile - 1);
             zero_acc<TL>(acc);
