@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="after the timed steps, copy this many bytes device-to-device (counter calibration)")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = about 20 s of work)")
+    ap.add_argument("--no-kahan", action="store_true", help="backward with a plain fp32 dE sum (no compensation)")
+    ap.add_argument("--full-de", action="store_true", help="unfiltered dE; the filter applies to dH only")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph and replayed (detail.graph_ms_per_step)")
     ap.add_argument("--library-gemm", action="store_true",
@@ -196,7 +198,7 @@ def main():
     ws_b = torch.empty(B.backward_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev)
     ws_s = torch.empty(B.vocab_order_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev) if a.sort else None
     perm = torch.empty(V, dtype=torch.int32, device=dev) if a.sort else None
-    bwd_flags = 0
+    bwd_flags = (B.CCE_BWD_NO_KAHAN if a.no_kahan else 0) | (B.CCE_BWD_FULL_DE if a.full_de else 0)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     mem0 = torch.cuda.memory_allocated()
@@ -285,7 +287,7 @@ def main():
         "data": "synthetic (seeded; head shape of the named model, random values)",
         "config": {"workload": f"{x.name} (N={N}, D={D}, V={V}, {x.dtype}, eps={eps:g}, sort={a.sort})",
                    "N": N, "D": D, "V": V, "n_valid": nv, "filter_eps": eps, "sort_vocab": a.sort,
-                   "filter_block": [br, bv]},
+                   "filter_block": [br, bv], "kahan_de": not a.no_kahan, "full_de": a.full_de},
         "roofline": {"kernel": "k_fwd (cce_forward bracket)", "bound": "mfma", "achieved": achieved,
                      "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
         "detail": {
