@@ -5,9 +5,12 @@ cpu_baseline leg of bench.py may import this package.  The HIP path never
 imports or calls it and shares no code with it; the two meet only in the
 seeded input generator.
 
-The arithmetic lives in cce_oracle.c (plain definition in double precision,
-see its header).  This wrapper converts the stored input bits to float64
-exactly, calls the C library, and sorts vocabulary keys with a library sort.
+The arithmetic of the plain definition lives in cce_oracle.c (double
+precision, see its header).  This wrapper converts the stored input bits to
+float64 exactly, calls the C library, and sorts vocabulary keys with a library
+sort.  Three numpy functions use a library matrix product as their logit step:
+lse_matmul (every row's lse at full sizes), backward_filtered (the gradient
+with the block filter at a stated geometry) and composite (a two-block head).
 
 Sources: the lit note "The loss and the mask: Cut Cross-Entropy +
 FlexAttention", section "Contribution"; the paper summary "Cut Your Losses in
@@ -182,14 +185,80 @@ def lse_matmul(H64, E64, labels, ignore_index=-100, row_chunk=512):
     H64, E64 = _c64(H64), _c64(E64)
     N = H64.shape[0]
     out = np.zeros(N)
-    Et = np.ascontiguousarray(E64.T)
     for r0 in range(0, N, row_chunk):
-        z = H64[r0:r0 + row_chunk] @ Et
+        z = H64[r0:r0 + row_chunk] @ E64.T
         m = z.max(axis=1, keepdims=True)
         out[r0:r0 + row_chunk] = (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))[:, 0]
     out[np.asarray(labels) == ignore_index] = 0.0
     return out
 
+
+
+def backward_filtered(H64, E64, labels, dloss, eps, block_rows=128, block_vocab=128, ignore_index=-100,
+                      margin=2.0 ** -10):
+    """Gradient with the block filter of the CCE paper summary "Cut Your
+    Losses in Large-Vocabulary Language Models", section "Approach": the
+    backward skips the blocks of the logit matrix whose softmax entries all
+    fall below a threshold.  The pages fix neither the block shape nor what
+    happens at a label entry; the reading taken here:
+      - the logit matrix is that of the non-ignored rows, in order (ignored
+        rows are dropped first), with the vocabulary in id order; blocks are
+        block_rows consecutive such rows x block_vocab consecutive ids;
+      - a block keeps the softmax part p of all its entries iff one entry other
+        than a label entry (i, y_i) has p >= eps; eps = 0 keeps every block;
+      - the gradient of the indexed-logit term (-1 at a label entry) is always
+        kept, and so is the label entry's own p (the whole dloss_i (p - 1)).
+    Steps, in the pages' order: full logit rows (numpy matmul, float64), lse
+    by its definition, p = exp(z - lse), the per-block keep decision, then
+    g = dloss (p [kept or label entry] - onehot), dH = g E, dE = g^T H.
+
+    Several results are correct when a block's largest non-label p lies
+    within a relative `margin` of eps (a float32 kernel may decide it either
+    way); for those blocks the sum of the Frobenius norms of their softmax
+    part's contributions to dH and to dE is returned as an allowance.
+    Returns dH [N, D], dE [V, D], kept [row blocks, vocab blocks] (bool),
+    allow_dH, allow_dE (floats).  Ignored rows get dH = 0, add nothing."""
+    H64, E64 = _c64(H64), _c64(E64)
+    labels = np.asarray(labels, dtype=np.int64)
+    dloss = np.asarray(dloss, dtype=np.float64)
+    N, D = H64.shape
+    V = E64.shape[0]
+    rows = np.nonzero(labels != ignore_index)[0]
+    n = rows.size
+    dH = np.zeros((N, D))
+    dE = np.zeros((V, D))
+    n_rb = -(-n // block_rows)
+    n_cb = -(-V // block_vocab)
+    kept = np.zeros((n_rb, n_cb), dtype=bool)
+    if n == 0:
+        return dH, dE, kept, 0.0, 0.0
+    Hv = H64[rows]
+    y = labels[rows]
+    z = Hv @ E64.T
+    m = z.max(axis=1, keepdims=True)
+    lse = m + np.log(np.exp(z - m).sum(axis=1, keepdims=True))
+    p = np.exp(z - lse)
+    is_label = np.zeros((n, V), dtype=bool)
+    is_label[np.arange(n), y] = True
+    allow_dH = allow_dE = 0.0
+    keep_entry = is_label.copy()
+    for rb in range(n_rb):
+        r0, r1 = rb * block_rows, min(n, (rb + 1) * block_rows)
+        for cb in range(n_cb):
+            c0, c1 = cb * block_vocab, min(V, (cb + 1) * block_vocab)
+            other = np.where(is_label[r0:r1, c0:c1], -np.inf, p[r0:r1, c0:c1])
+            top = other.max()
+            kept[rb, cb] = top >= eps if eps > 0 else top > -np.inf
+            if kept[rb, cb]:
+                keep_entry[r0:r1, c0:c1] = True
+            if eps > 0 and abs(top - eps) <= margin * eps:
+                soft = dloss[rows[r0:r1], None] * np.where(is_label[r0:r1, c0:c1], 0.0, p[r0:r1, c0:c1])
+                allow_dH += np.linalg.norm(soft @ E64[c0:c1])
+                allow_dE += np.linalg.norm(soft.T @ Hv[r0:r1])
+    g = dloss[rows, None] * (np.where(keep_entry, p, 0.0) - is_label)
+    dH[rows] = g @ E64
+    dE[:] = g.T @ Hv
+    return dH, dE, kept, allow_dH, allow_dE
 
 
 def composite(H64, E0, E1, off1, labels, dloss, ignore_index=-100):

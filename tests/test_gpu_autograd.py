@@ -48,11 +48,18 @@ def test_wrapper_matches_abi(reduction, sort):
         assert abs(float(got) - want) <= 1e-5 * max(abs(want), 1.0)  # got is already detached
     assert np.array_equal(G.t64(Hl.grad), ref["dH"])
     assert np.array_equal(G.t64(El.grad), ref["dE"])
-    # and against the fp64 oracle, at the filtered tolerance
-    _, _, dH, dE = G.oracle_full(x, dl, f"autograd-{reduction}")
+    # and against the fp64 oracle: the filtered gradient at the kernel's
+    # geometry (vocabulary in id order), or, sorted, the unfiltered one (this
+    # flat recipe keeps almost every block at eps = 2^-12)
     LH, LE = G.label_term(x, dl)
-    G.assert_grad("dH", G.t64(Hl.grad), dH, LH, 2e-2)
-    G.assert_grad("dE", G.t64(El.grad), dE, LE, 2e-2)
+    if sort:
+        _, _, dH, dE = G.oracle_full(x, dl, f"autograd-{reduction}")
+        G.assert_grad("dH", G.t64(Hl.grad), dH, LH, 1e-2)
+        G.assert_grad("dE", G.t64(El.grad), dE, LE, 1e-2)
+    else:
+        fH, fE, _, aH, aE = G.oracle_filtered(x, dl, x.eps, f"autograd-{reduction}")
+        G.assert_grad_filtered("dH", G.t64(Hl.grad), fH, aH, LH)
+        G.assert_grad_filtered("dE", G.t64(El.grad), fE, aE, LE)
 
 
 def test_composite_wrapper_matches_oracle():

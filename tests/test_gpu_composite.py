@@ -86,10 +86,18 @@ def test_composite_matches_oracle(k, N, D, V0, V1, gap, filtered):
     ycat = x.labels
     LH[valid] = -dl[valid, None] * E[ycat[valid]]
     np.add.at(LE, ycat[valid], -dl[valid, None] * H[valid])
-    tol = 2e-2 if filtered else (1e-5 if x.dtype == "f32" else 1e-2)
-    G.assert_grad("dH", out["dH"], dH, LH, tol)
-    G.assert_grad("dE0", out["dE0"], dE0, LE[:V0], tol)
-    G.assert_grad("dE1", out["dE1"], dE1, LE[V0:], tol)
+    if filtered:
+        # the kernels filter blocks of the concatenated vocabulary (E0's rows,
+        # then E1's): the oracle's filtered gradient over that vocabulary
+        fH, fE, _, aH, aE = oracle.backward_filtered(H, E, ycat, dl.astype(np.float64), eps, *B.filter_block(),
+                                                     x.ignore_index)
+        G.assert_grad_filtered("dH", out["dH"], fH, aH, LH)
+        G.assert_grad_filtered("dE", np.concatenate([out["dE0"], out["dE1"]]), fE, aE, LE)
+    else:
+        tol = 1e-5 if x.dtype == "f32" else 1e-2
+        G.assert_grad("dH", out["dH"], dH, LH, tol)
+        G.assert_grad("dE0", out["dE0"], dE0, LE[:V0], tol)
+        G.assert_grad("dE1", out["dE1"], dE1, LE[V0:], tol)
     assert np.all(out["dH"][~valid] == 0)
 
 

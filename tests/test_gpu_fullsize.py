@@ -1,7 +1,8 @@
 """The six workloads at their full sizes, in the launch configuration the
 benchmark times.  The oracle computes sampled outputs one by one (lse, loss
-and dH rows; dE rows where every row's lse is affordable) and properties that
-hold at any size check the rest:
+and dH rows; dE rows where every row's lse is affordable), every row's lse of
+the Gemma-2-2B and Phi-3.5-mini heads (numpy float64 matrix products), and
+properties that hold at any size check the rest:
   sum_v dE_v = 0 (every logit-gradient row sums to zero), and
   sum_v <dE_v, e_v> = sum_i <dH_i, h_i> (both are sum_iv g_iv z_iv)."""
 import numpy as np
@@ -35,9 +36,22 @@ def test_full_size(k):
     G.assert_rows("loss", out["loss"][rows], loss, m, tol, lse)
     assert np.all(out["lse"][~valid] == 0) and np.all(out["loss"][~valid] == 0)
     assert np.all(out["dH"][~valid] == 0)
-    # dH rows: relative Frobenius over the sample, floor = label term
+    # dH rows: relative Frobenius over the sample.  The peaked heads are
+    # degenerate (margin ~120 nats: the true gradient is below float32
+    # resolution of the label term), so they take the label-term floor.  On
+    # the flat heads the softmax part averages out over the large vocabulary:
+    # the label-term-only output is 2.1-2.2e-2 off (dH) and 8.7e-3 (w4 dE
+    # rows) while bf16 rounding costs ~2e-3, hence the tighter tolerances.
+    floor, tol_h, tol_e = {1: ("ref", 1e-5, 1e-5), 3: ("ref", 1e-2, 4e-3), 4: ("ref", 1e-2, 4e-3)}.get(
+        k, ("label", 2e-2, 2e-2))
     LH = -dl[rows, None].astype(np.float64) * E[x.labels[rows]]
-    G.assert_grad("dH rows", out["dH"][rows], dH, LH, 2e-2)
+    G.assert_grad("dH rows", out["dH"][rows], dH, LH, tol_h, floor)
+    if k in (2, 4):
+        # every row's lse, which covers every segment of the forward's
+        # partition (workgroup ranges that cross token tiles included)
+        G.say(f"full size w{k}: every row's lse (float64 matrix products)")
+        lse_all = oracle.lse_matmul(H, E, x.labels, x.ignore_index)
+        G.assert_rows("lse (all rows)", out["lse"], lse_all, valid, tol)
     # properties over the whole of dE
     dEg, dHg = out["dE"], out["dH"]
     label_scale = np.linalg.norm((dl[valid, None].astype(np.float64) * H[valid]).sum(axis=0)) + \
@@ -49,11 +63,12 @@ def test_full_size(k):
     assert abs(s_e - s_h) <= 2e-2 * max(scale, 1e-30), (s_e, s_h, scale)
     if k in (1, 4):
         # every row's lse is affordable here: sample dE rows from the oracle
-        lse_all = oracle.lse_matmul(H, E, x.labels, x.ignore_index)
+        if k == 1:
+            lse_all = oracle.lse_matmul(H, E, x.labels, x.ignore_index)
         vids = np.unique(np.concatenate([x.labels[vrows[:6]], rng.integers(0, x.V, 6)]))
         dE = oracle.dE_rows(H, E, x.labels, lse_all, dl.astype(np.float64), vids, x.ignore_index)
         LE = np.zeros_like(dE)
         for j, v in enumerate(vids):
             sel = x.labels == v
             LE[j] = -(dl[sel, None].astype(np.float64) * H[sel]).sum(axis=0)
-        G.assert_grad("dE rows", dEg[vids], dE, LE, 2e-2)
+        G.assert_grad("dE rows", dEg[vids], dE, LE, tol_e, floor)
