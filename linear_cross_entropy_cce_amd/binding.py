@@ -2,11 +2,15 @@
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the ABI.  PyTorch supplies device memory (outputs and
-workspace) and the current stream.  If the library is missing or cannot be
-loaded, every call raises: there is no fallback path.
+workspace) and the stream.  Tensors a call allocates (default outputs and the
+workspace) are allocated while the call's stream is current, so PyTorch's
+caching allocator hands their memory to other work only in that stream's
+order.  If the library is missing or cannot be loaded, every call raises:
+there is no fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -27,6 +31,9 @@ CCE_BF16 = 1
 
 CCE_BWD_NO_KAHAN = 1
 CCE_BWD_FULL_DE = 2
+CCE_BWD_DEBUG_STORE_LIMIT = 4
+
+STATS_LEN = 6  # entries of the backward's stats buffer (include/cce.h)
 
 # Every entry point include/cce.h declares.
 EXPORTS = (
@@ -144,6 +151,26 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context in which the call's allocations are made: the call's stream."""
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _check_rowvec(name, t, N, device):
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != torch.float32 or t.dim() != 1 or t.numel() != N or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 [{N}] tensor on {device}")
+
+
+def _check_stats(stats):
+    import torch
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < STATS_LEN or not stats.is_contiguous()):
+        raise ValueError(f"stats must be contiguous int64 with at least {STATS_LEN} entries")
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -191,13 +218,15 @@ def cce_forward(H, E, labels, ignore_index=-100, loss=None, lse=None, block_max=
     N, D, V = _shapes(H, E, labels)
     dt = _dtype_code(H)
     _check_perm(perm, V)
-    loss = torch.empty(N, dtype=torch.float32, device=H.device) if loss is None else loss
-    lse = torch.empty(N, dtype=torch.float32, device=H.device) if lse is None else lse
+    with _on(stream):
+        loss = torch.empty(N, dtype=torch.float32, device=H.device) if loss is None else loss
+        lse = torch.empty(N, dtype=torch.float32, device=H.device) if lse is None else lse
+        ws = _workspace(forward_workspace_bytes(N, D, V, dt), H.device, ws)
+    _check_rowvec("loss", loss, N, H.device)
+    _check_rowvec("lse", lse, N, H.device)
     if block_max is not None and (block_max.dtype != torch.float32 or
                                   block_max.numel() < block_max_elems(N, V) or not block_max.is_contiguous()):
         raise ValueError(f"block_max must be contiguous fp32 with at least {block_max_elems(N, V)} entries")
-    need = forward_workspace_bytes(N, D, V, dt)
-    ws = _workspace(need, H.device, ws)
     s = lib().cce_forward(_ptr(H), _ptr(E), _ptr(labels), N, D, V, dt, int(ignore_index), _ptr(perm), _ptr(loss),
                           _ptr(lse), _ptr(block_max), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("cce_forward", s)
@@ -209,10 +238,14 @@ def cce_vocab_order(H, E, labels, ignore_index=-100, perm=None, keys=None, want_
     import torch
     N, D, V = _shapes(H, E, labels)
     dt = _dtype_code(H)
-    perm = torch.empty(V, dtype=torch.int32, device=H.device) if perm is None else perm
-    if want_keys and keys is None:
-        keys = torch.empty(V, dtype=torch.float32, device=H.device)
-    ws = _workspace(vocab_order_workspace_bytes(N, D, V, dt), H.device, ws)
+    with _on(stream):
+        perm = torch.empty(V, dtype=torch.int32, device=H.device) if perm is None else perm
+        if want_keys and keys is None:
+            keys = torch.empty(V, dtype=torch.float32, device=H.device)
+        ws = _workspace(vocab_order_workspace_bytes(N, D, V, dt), H.device, ws)
+    _check_perm(perm, V)
+    if keys is not None:
+        _check_rowvec("keys", keys, V, H.device)
     s = lib().cce_vocab_order(_ptr(H), _ptr(E), _ptr(labels), N, D, V, dt, int(ignore_index), _ptr(perm),
                               _ptr(keys), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("cce_vocab_order", s)
@@ -222,25 +255,35 @@ def cce_vocab_order(H, E, labels, ignore_index=-100, perm=None, keys=None, want_
 def cce_backward(H, E, labels, lse, dloss, filter_eps=2.0 ** -12, ignore_index=-100, perm=None, flags=0,
                  dH=None, dE=None, stats=None, ws=None, stream=None, block_max=None):
     """dH [N, D], dE [V, D] (input dtype) of sum_i dloss_i loss_i.  stats:
-    None or int64 [5] (see include/cce.h); block_max: None or the table
+    None or int64 [6] (see include/cce.h); block_max: None or the table
     cce_forward wrote for the same H, E, labels and perm."""
     import torch
     N, D, V = _shapes(H, E, labels)
     dt = _dtype_code(H)
     _check_perm(perm, V)
-    dH = torch.empty_like(H) if dH is None else dH
-    dE = torch.empty_like(E) if dE is None else dE
-    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < 5):
-        raise ValueError("stats must be int64 with at least 5 entries")
-    if block_max is not None and (block_max.dtype != torch.float32 or block_max.numel() < block_max_elems(N, V)):
-        raise ValueError(f"block_max must be fp32 with at least {block_max_elems(N, V)} entries")
-    ws = _workspace(backward_workspace_bytes(N, D, V, dt), H.device, ws)
+    _check_rowvec("lse", lse, N, H.device)
+    _check_rowvec("dloss", dloss, N, H.device)
+    _check_stats(stats)
+    if block_max is not None and (block_max.dtype != torch.float32 or block_max.numel() < block_max_elems(N, V)
+                                  or not block_max.is_contiguous()):
+        raise ValueError(f"block_max must be contiguous fp32 with at least {block_max_elems(N, V)} entries")
+    with _on(stream):
+        dH = torch.empty_like(H) if dH is None else dH
+        dE = torch.empty_like(E) if dE is None else dE
+        ws = _workspace(backward_workspace_bytes(N, D, V, dt), H.device, ws)
+    _check_grad("dH", dH, H)
+    _check_grad("dE", dE, E)
     s = lib().cce_backward(_ptr(H), _ptr(E), _ptr(labels), _ptr(lse), _ptr(dloss), _ptr(block_max), N, D, V, dt,
                            int(ignore_index),
                            float(filter_eps), _ptr(perm), int(flags), _ptr(dH), _ptr(dE), _ptr(stats), _ptr(ws),
                            ws.numel() * ws.element_size(), _stream(stream))
     _check("cce_backward", s)
     return dH, dE
+
+
+def _check_grad(name, g, like):
+    if g.shape != like.shape or g.dtype != like.dtype or not g.is_contiguous() or g.device != like.device:
+        raise ValueError(f"{name} must be a contiguous {like.dtype} {tuple(like.shape)} tensor on {like.device}")
 
 
 def _composite_shapes(H, E0, E1, labels):
@@ -259,12 +302,15 @@ def cce_forward_composite(H, E0, E1, off1, labels, ignore_index=-100, loss=None,
     V = V0 + V1
     dt = _dtype_code(H)
     _check_perm(perm, V)
-    loss = torch.empty(N, dtype=torch.float32, device=H.device) if loss is None else loss
-    lse = torch.empty(N, dtype=torch.float32, device=H.device) if lse is None else lse
+    with _on(stream):
+        loss = torch.empty(N, dtype=torch.float32, device=H.device) if loss is None else loss
+        lse = torch.empty(N, dtype=torch.float32, device=H.device) if lse is None else lse
+        ws = _workspace(forward_workspace_bytes(N, D, V, dt), H.device, ws)
+    _check_rowvec("loss", loss, N, H.device)
+    _check_rowvec("lse", lse, N, H.device)
     if block_max is not None and (block_max.dtype != torch.float32 or
                                   block_max.numel() < block_max_elems(N, V) or not block_max.is_contiguous()):
         raise ValueError(f"block_max must be contiguous fp32 with at least {block_max_elems(N, V)} entries")
-    ws = _workspace(forward_workspace_bytes(N, D, V, dt), H.device, ws)
     s = lib().cce_forward_composite(_ptr(H), _ptr(E0), V0, _ptr(E1), V1, int(off1), _ptr(labels), N, D, dt,
                                     int(ignore_index), _ptr(perm), _ptr(loss), _ptr(lse), _ptr(block_max), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream))
@@ -279,11 +325,14 @@ def cce_vocab_order_composite(H, E0, E1, labels, ignore_index=-100, perm=None, k
     N, D, V0, V1 = _composite_shapes(H, E0, E1, labels)
     V = V0 + V1
     dt = _dtype_code(H)
-    perm = torch.empty(V, dtype=torch.int32, device=H.device) if perm is None else perm
+    with _on(stream):
+        perm = torch.empty(V, dtype=torch.int32, device=H.device) if perm is None else perm
+        if want_keys and keys is None:
+            keys = torch.empty(V, dtype=torch.float32, device=H.device)
+        ws = _workspace(vocab_order_workspace_bytes(N, D, V, dt), H.device, ws)
     _check_perm(perm, V)
-    if want_keys and keys is None:
-        keys = torch.empty(V, dtype=torch.float32, device=H.device)
-    ws = _workspace(vocab_order_workspace_bytes(N, D, V, dt), H.device, ws)
+    if keys is not None:
+        _check_rowvec("keys", keys, V, H.device)
     s = lib().cce_vocab_order_composite(_ptr(H), _ptr(E0), V0, _ptr(E1), V1, _ptr(labels), N, D, dt,
                                         int(ignore_index), _ptr(perm), _ptr(keys), _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream))
@@ -300,14 +349,20 @@ def cce_backward_composite(H, E0, E1, off1, labels, lse, dloss, filter_eps=2.0 *
     V = V0 + V1
     dt = _dtype_code(H)
     _check_perm(perm, V)
-    dH = torch.empty_like(H) if dH is None else dH
-    dE0 = torch.empty_like(E0) if dE0 is None else dE0
-    dE1 = torch.empty_like(E1) if dE1 is None else dE1
-    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < 5):
-        raise ValueError("stats must be int64 with at least 5 entries")
-    if block_max is not None and (block_max.dtype != torch.float32 or block_max.numel() < block_max_elems(N, V)):
-        raise ValueError(f"block_max must be fp32 with at least {block_max_elems(N, V)} entries")
-    ws = _workspace(backward_workspace_bytes(N, D, V, dt), H.device, ws)
+    _check_rowvec("lse", lse, N, H.device)
+    _check_rowvec("dloss", dloss, N, H.device)
+    _check_stats(stats)
+    if block_max is not None and (block_max.dtype != torch.float32 or block_max.numel() < block_max_elems(N, V)
+                                  or not block_max.is_contiguous()):
+        raise ValueError(f"block_max must be contiguous fp32 with at least {block_max_elems(N, V)} entries")
+    with _on(stream):
+        dH = torch.empty_like(H) if dH is None else dH
+        dE0 = torch.empty_like(E0) if dE0 is None else dE0
+        dE1 = torch.empty_like(E1) if dE1 is None else dE1
+        ws = _workspace(backward_workspace_bytes(N, D, V, dt), H.device, ws)
+    _check_grad("dH", dH, H)
+    _check_grad("dE0", dE0, E0)
+    _check_grad("dE1", dE1, E1)
     s = lib().cce_backward_composite(_ptr(H), _ptr(E0), V0, _ptr(E1), V1, int(off1), _ptr(labels), _ptr(lse),
                                      _ptr(dloss), _ptr(block_max), N, D, dt, int(ignore_index), float(filter_eps),
                                      _ptr(perm), int(flags), _ptr(dH), _ptr(dE0), _ptr(dE1), _ptr(stats), _ptr(ws),
@@ -319,7 +374,8 @@ def cce_backward_composite(H, E0, E1, off1, labels, lse, dloss, filter_eps=2.0 *
 def cce_check_labels(labels, V, ignore_index=-100, stream=None) -> int:
     """Number of labels neither ignore_index nor in [0, V)."""
     import torch
-    n_bad = torch.empty(1, dtype=torch.int64, device=labels.device)
+    with _on(stream):
+        n_bad = torch.empty(1, dtype=torch.int64, device=labels.device)
     s = lib().cce_check_labels(_ptr(labels), labels.shape[0], int(V), int(ignore_index), _ptr(n_bad),
                                _stream(stream))
     _check("cce_check_labels", s)

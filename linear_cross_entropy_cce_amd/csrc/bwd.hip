@@ -107,6 +107,7 @@ struct BwdArgs {
     int full_de;  // dE from every block (status 3 = kept for dE only), dH filtered
     T *Gt, *Gn;
     int64_t cap;
+    int64_t cap_take;  // slots the epilogue may take: cap (cap / 2 with CCE_BWD_DEBUG_STORE_LIMIT)
     uint8_t *st;
     int32_t *slot;
     int64_t *stats;
@@ -117,7 +118,7 @@ struct BwdArgs {
 
 // ------------------------------------------------------------ small kernels
 __global__ void k_stats_init(int64_t *stats) {
-    if (threadIdx.x < 5) stats[threadIdx.x] = 0;
+    if (threadIdx.x < 6) stats[threadIdx.x] = 0;
 }
 
 __global__ void k_stats_fin(int64_t *stats, const int32_t *__restrict__ nvalid_p, int64_t n_vblocks) {
@@ -465,7 +466,14 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
         int s = -1;
         if (sv) {
             s = atomicAdd(counter, 1);
-            if (s >= cap) { s = -1; sv = 0; }  // cannot happen: the plan bounds every pass by cap
+            if (s >= cap) {
+                // the plan sizes every pass to fit the store, so this only
+                // happens when it is told to (CCE_BWD_DEBUG_STORE_LIMIT):
+                // the block is dropped and counted, never written past the store
+                s = -1;
+                sv = 0;
+                if (stats) atomicAdd(reinterpret_cast<unsigned long long *>(stats + 5), 1ull);
+            }
         }
         qstat[tid] = sv;
         qslot[tid] = s;
@@ -622,7 +630,7 @@ struct GPassLds {
 // with the other parts.
 template <typename T, bool DMA>
 __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int nbid, u32x4 *lds, int *qflag,
-                                        int *qstat, int *qslot) {
+                                        int *qstat, int *qslot, int *ticket) {
     using TL = TileF;
     const PlanView pv = plan_view(a.plan, a.max_passes);
     int32_t *queues = plan_queues(a.plan, a.max_passes, p);
@@ -634,7 +642,7 @@ __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int
         const int pb = lb + (int)((int64_t)(le - lb) * part / nparts);
         const int pe = lb + (int)((int64_t)(le - lb) * (part + 1) / nparts);
         for (;;) {
-            const int i = pb + take_ticket(queues + part, qslot);
+            const int i = pb + take_ticket(queues + part, ticket);
             if (i >= pe) break;
             const int tile = a.tlist[i];
             const int vt = tile / a.n_rt, rt = tile % a.n_rt;
@@ -651,11 +659,11 @@ __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int
                 else recompute_vgpr<T, TL>(a.H, a.E, a.idx, nv, a.perm, a.D, a.V, tok0, p0, lds, acc);
                 __syncthreads();
                 g_epilogue<T, TL, true>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
-                                        a.lse, a.dloss, a.zlab, a.glab, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
+                                        a.lse, a.dloss, a.zlab, a.glab, a.Gt, a.Gn, a.cap_take, pv.counter + p, a.st, a.slot, a.stats,
                                         qflag, qstat, qslot, a.full_de, qmask);
             } else {
                 g_epilogue<T, TL, false>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
-                                         a.lse, a.dloss, a.zlab, a.glab, a.Gt, a.Gn, a.cap, pv.counter + p, a.st, a.slot, a.stats,
+                                         a.lse, a.dloss, a.zlab, a.glab, a.Gt, a.Gn, a.cap_take, pv.counter + p, a.st, a.slot, a.stats,
                                          qflag, qstat, qslot, a.full_de, 0);
             }
         }
@@ -1119,8 +1127,12 @@ template <typename T, bool DMA>
 __global__ __launch_bounds__(TileF::kThreads) void k_g_pass(BwdArgs<T> a, int p) {
     __shared__ u32x4 lds[GPassLds<T, DMA>::value];
     __shared__ int qflag[4], qstat[4], qslot[4];
+    // The work-queue ticket has a word of its own: the epilogue's waves read
+    // qslot after its last barrier, while thread 0 may already take the next
+    // ticket.
+    __shared__ int ticket;
     if (p >= *plan_view(a.plan, a.max_passes).P) return;
-    g_phase<T, DMA>(a, p, blockIdx.x, gridDim.x, lds, qflag, qstat, qslot);
+    g_phase<T, DMA>(a, p, blockIdx.x, gridDim.x, lds, qflag, qstat, qslot, &ticket);
 }
 
 template <typename T, bool KAHAN>
@@ -1213,7 +1225,7 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
         CCE_TRY(launch_inv_perm(perm, V, w.inv_perm, st));
     }
     if (stats) {
-        hipLaunchKernelGGL(k_stats_init, dim3(1), dim3(64), 0, st, stats);
+        hipLaunchKernelGGL(k_stats_init, dim3(1), dim3(64), 0, st, stats);  // all 6 entries
         CCE_LAUNCHED();
     }
     const size_t nblk = (size_t)s.n_rb * s.cbp;
@@ -1292,6 +1304,7 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     a.Gt = Gt;
     a.Gn = Gn;
     a.cap = s.cap;
+    a.cap_take = (flags & CCE_BWD_DEBUG_STORE_LIMIT) ? s.cap / 2 : s.cap;
     a.st = w.st;
     a.slot = w.slot;
     a.stats = stats;

@@ -142,7 +142,7 @@ def test_backward_specific_errors():
     assert _bwd(eps=-1.0) == B.CCE_ERR_ARG
     assert _bwd(eps=float("nan")) == B.CCE_ERR_ARG
     assert _bwd(eps=float("inf")) == B.CCE_ERR_ARG
-    assert _bwd(flags=4) == B.CCE_ERR_ARG
+    assert _bwd(flags=8) == B.CCE_ERR_ARG  # no such flag
     assert _bwd(dE=FAKE + 8) == B.CCE_ERR_ALIGN
     assert _bwd(perm=FAKE + 2) == B.CCE_ERR_ALIGN
     assert _bwd(stats=FAKE + 4) == B.CCE_ERR_ALIGN
