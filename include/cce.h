@@ -128,6 +128,27 @@ cce_status cce_forward(const void *H, const void *E, const int64_t *labels,
                        float *block_max, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Allocation-free forward, for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Computes exactly what cce_forward
+ * computes (bit-identical outputs) with the workspace in a file-scope device
+ * array of CCE_NOALLOC_SCRATCH_BYTES bytes that the library holds on every
+ * GPU it runs on until the process ends; it calls no allocation routine.
+ * The stream must belong to the current device.  Returns CCE_ERR_WORKSPACE
+ * (before any work is enqueued) when cce_forward_workspace_bytes(N, D, V,
+ * dtype) exceeds CCE_NOALLOC_SCRATCH_BYTES (e.g. N = 2^20 tokens, or
+ * V = 2^22 entries).  All calls on one GPU share that array: calls that
+ * overlap in time on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller.  The first call on a device looks the
+ * array's address up (HIP loads the code object if it is not yet loaded).
+ */
+#define CCE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+cce_status cce_forward_noalloc(const void *H, const void *E, const int64_t *labels,
+                               int64_t N, int64_t D, int64_t V, cce_dtype dtype,
+                               int64_t ignore_index, const int32_t *perm, float *loss, float *lse,
+                               float *block_max, void *stream);
+
+/*
  * Vocabulary order for the backward (optional): key_v = mean over
  * non-ignored rows of z_iv = <mean_i h_i, e_v>, sorted descending, ties by
  * ascending id (stable).  perm[k] (int32, device, [V]) receives the original

@@ -40,8 +40,10 @@ EXPORTS = (
     "cce_status_string", "cce_version", "cce_filter_block",
     "cce_forward_workspace_bytes", "cce_backward_workspace_bytes", "cce_vocab_order_workspace_bytes",
     "cce_block_max_elems", "cce_forward", "cce_vocab_order", "cce_backward", "cce_check_labels",
-    "cce_forward_composite", "cce_vocab_order_composite", "cce_backward_composite",
+    "cce_forward_composite", "cce_vocab_order_composite", "cce_backward_composite", "cce_forward_noalloc",
 )
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # CCE_NOALLOC_SCRATCH_BYTES
 
 
 class CCEError(RuntimeError):
@@ -93,6 +95,8 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_int, _i64, ctypes.c_float, _vp, ctypes.c_uint, _vp, _vp, _vp, _vp,
                                          _vp, ctypes.c_size_t, _vp]
     L.cce_backward_composite.restype = ctypes.c_int
+    L.cce_forward_noalloc.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_int, _i64, _vp, _vp, _vp, _vp, _vp]
+    L.cce_forward_noalloc.restype = ctypes.c_int
     L.cce_check_labels.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp]
     L.cce_check_labels.restype = ctypes.c_int
     _lib = L
@@ -230,6 +234,25 @@ def cce_forward(H, E, labels, ignore_index=-100, loss=None, lse=None, block_max=
     s = lib().cce_forward(_ptr(H), _ptr(E), _ptr(labels), N, D, V, dt, int(ignore_index), _ptr(perm), _ptr(loss),
                           _ptr(lse), _ptr(block_max), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("cce_forward", s)
+    return loss, lse
+
+
+def cce_forward_noalloc(H, E, labels, loss, lse, ignore_index=-100, block_max=None, stream=None, perm=None):
+    """cce_forward with the library's own device scratch instead of a
+    workspace: the C entry point allocates nothing, so the caller passes the
+    outputs (fp32 [N] loss and lse)."""
+    import torch
+    N, D, V = _shapes(H, E, labels)
+    dt = _dtype_code(H)
+    _check_perm(perm, V)
+    _check_rowvec("loss", loss, N, H.device)
+    _check_rowvec("lse", lse, N, H.device)
+    if block_max is not None and (block_max.dtype != torch.float32 or
+                                  block_max.numel() < block_max_elems(N, V) or not block_max.is_contiguous()):
+        raise ValueError(f"block_max must be contiguous fp32 with at least {block_max_elems(N, V)} entries")
+    s = lib().cce_forward_noalloc(_ptr(H), _ptr(E), _ptr(labels), N, D, V, dt, int(ignore_index), _ptr(perm),
+                                  _ptr(loss), _ptr(lse), _ptr(block_max), _stream(stream))
+    _check("cce_forward_noalloc", s)
     return loss, lse
 
 

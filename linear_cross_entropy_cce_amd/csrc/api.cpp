@@ -55,15 +55,25 @@ hipError_t map_labels(const int64_t *labels, int64_t N, int64_t ignore_index, co
     return launch_seg_labels(labels, N, ignore_index, E.v0, off1, V - E.v0, mapped, st);
 }
 
+// The forward's argument checks other than the workspace's.
+cce_status forward_check(const void *H, const VocabRows &E, const int64_t *labels, int64_t N, int64_t D, int64_t V,
+                         cce_dtype dtype, const int32_t *perm, float *loss, float *lse, float *block_max) {
+    if (!H || !E.e0 || !E.e1 || !labels || !loss || !lse) return CCE_ERR_NULL;
+    if (!dtype_ok(dtype)) return CCE_ERR_DTYPE;
+    if (!shape_ok(N, D, V)) return CCE_ERR_SHAPE;
+    if (!aligned(H, 16) || !aligned(E.e0, 16) || !aligned(E.e1, 16) || !aligned(labels, 8) || !aligned(loss, 4) ||
+        !aligned(lse, 4) || !aligned(block_max, 4) || !aligned(perm, 4))
+        return CCE_ERR_ALIGN;
+    return CCE_OK;
+}
+
 cce_status forward_impl(const void *H, const VocabRows &E, int64_t off1, const int64_t *labels, int64_t N, int64_t D,
                         int64_t V, cce_dtype dtype, int64_t ignore_index, const int32_t *perm, float *loss,
                         float *lse, float *block_max, void *ws, size_t ws_bytes, void *stream) {
-    if (!H || !E.e0 || !E.e1 || !labels || !loss || !lse || !ws) return CCE_ERR_NULL;
-    if (!dtype_ok(dtype)) return CCE_ERR_DTYPE;
-    if (!shape_ok(N, D, V)) return CCE_ERR_SHAPE;
-    if (!aligned(H, 16) || !aligned(E.e0, 16) || !aligned(E.e1, 16) || !aligned(ws, 16) || !aligned(labels, 8) ||
-        !aligned(loss, 4) || !aligned(lse, 4) || !aligned(block_max, 4) || !aligned(perm, 4))
-        return CCE_ERR_ALIGN;
+    const cce_status c = forward_check(H, E, labels, N, D, V, dtype, perm, loss, lse, block_max);
+    if (c != CCE_OK) return c;
+    if (!ws) return CCE_ERR_NULL;
+    if (!aligned(ws, 16)) return CCE_ERR_ALIGN;
     const FwdShape s = fwd_shape(N, D, V);
     size_t need = 0;
     const FwdWs w = fwd_ws(ws, s, &need);
@@ -173,6 +183,21 @@ cce_status cce_forward(const void *H, const void *E, const int64_t *labels, int6
                        float *block_max, void *ws, size_t ws_bytes, void *stream) {
     return forward_impl(H, VocabRows{E, E, kOneBlock}, 0, labels, N, D, V, dtype, ignore_index, perm, loss, lse,
                         block_max, ws, ws_bytes, stream);
+}
+
+static_assert(kNoAllocScratchBytes == CCE_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
+
+cce_status cce_forward_noalloc(const void *H, const void *E, const int64_t *labels, int64_t N, int64_t D, int64_t V,
+                               cce_dtype dtype, int64_t ignore_index, const int32_t *perm, float *loss, float *lse,
+                               float *block_max, void *stream) {
+    const VocabRows rows{E, E, kOneBlock};
+    const cce_status c = forward_check(H, rows, labels, N, D, V, dtype, perm, loss, lse, block_max);
+    if (c != CCE_OK) return c;
+    if (cce_forward_workspace_bytes(N, D, V, dtype) > kNoAllocScratchBytes) return CCE_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (noalloc_scratch(&ws) != hipSuccess) return CCE_ERR_HIP;
+    return forward_impl(H, rows, 0, labels, N, D, V, dtype, ignore_index, perm, loss, lse, block_max, ws,
+                        kNoAllocScratchBytes, stream);
 }
 
 cce_status cce_forward_composite(const void *H, const void *E0, int64_t V0, const void *E1, int64_t V1, int64_t off1,

@@ -30,6 +30,8 @@ constexpr int kPassGroups = 256;
 // Most workgroups of the forward's persistent grid (its partial buffers are
 // sized for this many).
 constexpr int kFwdMaxGroups = 1024;
+// Device scratch of the allocation-free forward (one copy per GPU).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 
 // The classifier as the kernels see it: rows 0 .. V-1 of the processing
 // space, held by one matrix (e1 == e0, v0 >= V) or by the two row blocks of a
@@ -135,6 +137,10 @@ struct SortWs {
     int32_t *nvalid;   // [1]
 };
 SortWs sort_ws(void *ws, int64_t N, int64_t D, int64_t V, size_t *bytes);
+
+// Device address of the allocation-free forward's scratch on the current
+// device (looked up once per device, then cached).
+hipError_t noalloc_scratch(void **ptr);
 
 // ---- launchers (return hipGetLastError() after enqueuing) ----
 hipError_t launch_compact(const int64_t *labels, int64_t N, int64_t ignore_index, int32_t *idx,

@@ -18,6 +18,7 @@
 // go to a small buffer and one ordered pass merges them, so the result is
 // independent of scheduling.
 #include <algorithm>
+#include <mutex>
 
 #include "cce_device.hpp"
 #include "cce_internal.hpp"
@@ -595,6 +596,36 @@ __global__ __launch_bounds__(256) void k_merge(const T *__restrict__ H, Rows2<co
         lse[i] = l;
         loss[i] = l - dot;
     }
+}
+
+// ------------------------------------------------- allocation-free forward
+// The workspace of cce_forward_noalloc: a file-scope device array, one copy
+// per GPU the library runs on, held until the process ends.  In host code
+// the array's name is only a stand-in symbol, never a device address: the
+// first call on a device (with that device current) looks up its address
+// with hipGetSymbolAddress, and every later call on that device uses the
+// cached address.  The forward needs nothing in it to start at zero (every
+// region is written before it is read), and calls that overlap on one GPU
+// share it, so they race.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------- launchers

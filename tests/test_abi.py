@@ -218,3 +218,22 @@ def test_composite_argument_errors():
                                        1 << 40, None) == B.CCE_ERR_NULL
     assert L.cce_vocab_order_composite(FAKE, FAKE, 0, FAKE, 40, FAKE, 16, 64, B.CCE_BF16, -100, FAKE, None, FAKE,
                                        1 << 40, None) == B.CCE_ERR_SHAPE
+
+
+def test_noalloc_forward_argument_errors():
+    # checked on the host before the device is touched
+    L = B.lib()
+    def call(H=FAKE, E=FAKE, y=FAKE, N=16, D=64, V=100, dt=B.CCE_BF16, loss=FAKE, lse=FAKE):
+        return L.cce_forward_noalloc(H, E, y, N, D, V, dt, -100, None, loss, lse, None, None)
+    assert call(H=None) == B.CCE_ERR_NULL
+    assert call(loss=None) == B.CCE_ERR_NULL
+    assert call(dt=9) == B.CCE_ERR_DTYPE
+    assert call(D=12) == B.CCE_ERR_SHAPE
+    assert call(E=FAKE + 8) == B.CCE_ERR_ALIGN
+    # beyond the 16 MiB scratch: a million tokens, or four million vocabulary entries
+    assert B.forward_workspace_bytes(1 << 20, 64, 100, B.CCE_BF16) > B.NOALLOC_SCRATCH_BYTES
+    assert call(N=1 << 20) == B.CCE_ERR_WORKSPACE
+    assert call(V=1 << 22) == B.CCE_ERR_WORKSPACE
+    # the workloads' shapes fit
+    for N, D, V in ((8192, 2304, 256000), (16384, 4096, 128256), (24576, 2048, 248320)):
+        assert B.forward_workspace_bytes(N, D, V, B.CCE_BF16) <= B.NOALLOC_SCRATCH_BYTES
