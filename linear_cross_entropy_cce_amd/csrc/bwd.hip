@@ -55,6 +55,10 @@ static_assert(kTileVocab == 2 * kBlockVocab && kTileRows == 2 * kBlockRows, "a l
 
 constexpr int kBlockElems = kBlockRows * kBlockVocab;  // elements of one stored block
 constexpr int kListCap = 512;
+// A vocabulary block whose kept blocks are all label-only, at most this many,
+// gets its dE rows from the label entries directly (no block products).
+constexpr int kLabelPathBlocks = 4;
+constexpr int kLabelEntries = kLabelPathBlocks * kBlockRows;
 constexpr int kDeGroups = 2 * kPassGroups;  // persistent dE workgroups of the gradient-product kernel
 
 // Plan record: P, number of listed tiles, first vocabulary tile of each pass
@@ -821,7 +825,144 @@ struct GradLds {
     int list[kListCap];
     int lslot[kListCap];
     int wcnt[TileG::kWaves];
+    int soft;  // the vocabulary block has a block with a kept softmax part (status 1 or 3)
+    // label entries of a vocabulary block (label path), grouped by vocabulary
+    // row, in token order within a row
+    int ent_h[kLabelEntries];                           // row of H
+    float ent_g[kLabelEntries];                         // gradient of the label entry (fp32)
+    int rlo[kBlockVocab + 1];                           // entries of row r: [rlo[r], rlo[r + 1])
+    int wrow[TileG::kWaves][kBlockVocab];               // entries of each row per wave
 };
+
+// What the label path reads (null labels: no label path).
+template <typename T>
+struct LabelCols {
+    const int64_t *labels;
+    const int32_t *idx;
+    const int32_t *inv_perm;
+    const float *glab;
+    const T *H;
+    int nv;
+};
+
+// dE rows of vocabulary block cb, features [d0, d0 + 256), when every kept
+// block of cb is label-only: dE_v = sum of g_i h_i over the valid tokens i
+// whose label is v (g_i the label entry's fp32 gradient), summed in fp32 in
+// token order, zero for a row no label falls in.  The label tokens are those
+// of the n kept row blocks sh.list[0 .. n) (n <= kLabelPathBlocks, one token
+// per thread); they are grouped by vocabulary row with a stable counting sort
+// (ranks from wave ballots, as in a radix sort's scatter).
+template <typename T>
+__device__ __forceinline__ void de_label_item(GradLds<T> &sh, int n, int cb, int d0, const LabelCols<T> &lc,
+                                              const int32_t *__restrict__ perm, int D, int V, Rows2<T> dE) {
+    constexpr int kThreads = TileG::kThreads;
+    static_assert(kThreads == kLabelEntries, "one candidate token per thread");
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    // candidate: token (sh.list[t / 128] * 128 + t % 128) of a label block
+    int row = -1, hrow = 0;
+    float g = 0.f;
+    if (t < n * kBlockRows) {
+        const int tok = sh.list[t / kBlockRows] * kBlockRows + (t % kBlockRows);
+        if (tok < lc.nv) {
+            const int r = lc.idx[tok];
+            const int64_t y = lc.labels[r];
+            if (y >= 0 && y < V) {
+                const int pos = lc.inv_perm ? lc.inv_perm[y] : (int)y;
+                if (pos / kBlockVocab == cb) {
+                    row = pos % kBlockVocab;
+                    hrow = r;
+                    g = lc.glab[tok];
+                }
+            }
+        }
+    }
+    // lanes of this wave with the same row: their rank among them is the rank in token order
+    uint64_t same = __ballot(row >= 0);
+#pragma unroll
+    for (int b = 0; b < 7; ++b) {
+        const bool bit = (row >> b) & 1;
+        const uint64_t bal = __ballot(bit);
+        same &= bit ? bal : ~bal;
+    }
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const int rank = __popcll(same & below);
+    for (int q = t; q < TileG::kWaves * kBlockVocab; q += kThreads) (&sh.wrow[0][0])[q] = 0;
+    __syncthreads();
+    if (row >= 0 && rank == 0) sh.wrow[wave][row] = __popcll(same);
+    __syncthreads();
+    if (t < kBlockVocab) {  // two waves: exclusive scan of the row counts
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < TileG::kWaves; ++w) c += sh.wrow[w][t];
+        int x = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        sh.rlo[t + 1] = x;  // inclusive within the wave
+    }
+    __syncthreads();
+    if (t >= 64 && t < kBlockVocab) sh.rlo[t + 1] += sh.rlo[64];  // second wave: add the first wave's total
+    if (t == 0) sh.rlo[0] = 0;
+    __syncthreads();
+    if (row >= 0) {
+        int p = sh.rlo[row] + rank;
+        for (int w = 0; w < wave; ++w) p += sh.wrow[w][row];
+        sh.ent_h[p] = hrow;
+        sh.ent_g[p] = g;
+    }
+    __syncthreads();
+    constexpr int CE = ChunkElems<T>::value;
+    constexpr int kSeg = TileG::BN / CE;  // 16-byte segments per row
+    for (int q = t; q < kBlockVocab * kSeg; q += kThreads) {
+        const int r = q / kSeg, d = d0 + (q % kSeg) * CE;
+        const int pos = cb * kBlockVocab + r;
+        const int v = pos < V ? (perm ? perm[pos] : pos) : -1;
+        if (v < 0 || v >= V || d >= D) continue;
+        float acc[CE];
+#pragma unroll
+        for (int k = 0; k < CE; ++k) acc[k] = 0.f;
+        for (int e = sh.rlo[r]; e < sh.rlo[r + 1]; ++e) {
+            const u32x4 hv = ld16(reinterpret_cast<const char *>(lc.H + (int64_t)sh.ent_h[e] * D + d));
+            const T *hp = reinterpret_cast<const T *>(&hv);
+            const float ge = sh.ent_g[e];
+#pragma unroll
+            for (int k = 0; k < CE; ++k) acc[k] += ge * to_f32(hp[k]);
+        }
+        u32x4 out;
+        T *op = reinterpret_cast<T *>(&out);
+#pragma unroll
+        for (int k = 0; k < CE; ++k) op[k] = from_f32<T>(acc[k]);
+        *reinterpret_cast<u32x4 *>(dE.row(v) + d) = out;
+    }
+}
+
+// The label path for dE item (cb, d0), if it applies: every kept block of
+// vocabulary block cb is label-only (status 2) and there are at most
+// kLabelPathBlocks of them.  Returns -1 when the item's rows were written,
+// else the number of kept row blocks, listed in sh.list (for de_item), or
+// -2 when the column's row blocks do not fit one list.
+template <typename T>
+__device__ __forceinline__ int de_try_label(GradLds<T> &sh, int cb, int d0, int n_rb, const uint8_t *__restrict__ st,
+                                            int cbp, const LabelCols<T> &lc, const int32_t *__restrict__ perm, int D,
+                                            int V, Rows2<T> dE) {
+    if (n_rb > kListCap) return -2;  // uniform
+    if (threadIdx.x == 0) sh.soft = 0;
+    __syncthreads();
+    const int n = build_list<TileG::kThreads>(
+        n_rb,
+        [&](int i) {
+            const int s = st[(int64_t)i * cbp + cb];
+            if (s == 1 || s == 3) atomicOr(&sh.soft, 1);
+            return s != 0;
+        },
+        sh.list, sh.wcnt);
+    // (build_list ends with a barrier: sh.soft is final)
+    if (!lc.labels || n == 0 || n > kLabelPathBlocks || sh.soft) return n;
+    de_label_item<T>(sh, n, cb, d0, lc, perm, D, V, dE);
+    return -1;
+}
 
 // dE for one (vocabulary block cb, 256-feature tile d0) item of a pass.  K
 // runs over the valid tokens of the row blocks kept for cb, in order (DMA
@@ -830,11 +971,13 @@ struct GradLds {
 // in a fresh fp32 accumulator and then added into (sum, compensation) with
 // Kahan's rule; the result is written once, through LDS as 16-byte row
 // segments (bf16).  A vocabulary block with nothing kept gets dE = 0.
+// pre_n >= 0: the kept row blocks (all of them: n_rb <= kListCap) are
+// already listed in sh.list.
 template <typename T, bool KAHAN>
 __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb, const uint8_t *__restrict__ st,
                                         const int32_t *__restrict__ slotm, int cbp, const T *__restrict__ Gt,
                                         const T *__restrict__ Ht, int64_t ldh, const int32_t *__restrict__ perm,
-                                        int D, int V, Rows2<T> dE) {
+                                        int D, int V, Rows2<T> dE, int pre_n) {
     using TL = TileG;
     using DE = DmaEngine<T, TL>;
     constexpr int kBlockBytes = kBlockRows * (int)sizeof(T);  // K bytes of one row block
@@ -862,8 +1005,10 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
     bool any = false;
     for (int base = 0; base < n_rb; base += kListCap) {
         const int cnt = n_rb - base < kListCap ? n_rb - base : kListCap;
-        const int n = build_list<TL::kThreads>(
-            cnt, [&](int i) { return st[(int64_t)(base + i) * cbp + cb] != 0; }, sh.list, sh.wcnt);
+        const int n = pre_n >= 0 ? pre_n
+                                 : build_list<TL::kThreads>(
+                                       cnt, [&](int i) { return st[(int64_t)(base + i) * cbp + cb] != 0; }, sh.list,
+                                       sh.wcnt);
         for (int i = threadIdx.x; i < n; i += TL::kThreads) sh.lslot[i] = slotm[(int64_t)(base + sh.list[i]) * cbp + cb];
         __syncthreads();
         any |= n > 0;
@@ -1107,6 +1252,9 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
     const int n_rbv = (nv + kBlockRows - 1) / kBlockRows;
     const int64_t n_dh = (int64_t)n_rbv * n_dt;
     const int64_t n_de = cb1 > cb0 ? (int64_t)(cb1 - cb0) * n_dt : 0;
+    // (no label path for the full classifier gradient: its label-only blocks
+    // store the unfiltered gradient for dE)
+    const LabelCols<T> lc{a.full_de ? nullptr : a.labels, a.idx, a.inv_perm, a.glab, a.H, nv};
     // two loops rather than one with a branch: each keeps its own registers
     int64_t it = take_ticket(queue, ticket);
     while (it < n_dh) {
@@ -1116,8 +1264,11 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
     }
     while (it < n_dh + n_de) {
         const int64_t q = it - n_dh;
-        de_item<T, KAHAN>(sh, cb0 + (int)(q / n_dt), (int)(q % n_dt) * TL::BN, n_rbv, a.st, a.slot, a.cbp, a.Gt, a.Ht,
-                          a.ldh, a.perm, a.D, a.V, a.dE);
+        const int cb = cb0 + (int)(q / n_dt), d0 = (int)(q % n_dt) * TL::BN;
+        const int n = de_try_label<T>(sh, cb, d0, n_rbv, a.st, a.cbp, lc, a.perm, a.D, a.V, a.dE);
+        if (n != -1)
+            de_item<T, KAHAN>(sh, cb, d0, n_rbv, a.st, a.slot, a.cbp, a.Gt, a.Ht, a.ldh, a.perm, a.D, a.V, a.dE,
+                              n >= 0 ? n : -1);
         it = take_ticket(queue, ticket);
     }
 }
@@ -1191,6 +1342,7 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     w.act = c.take<int32_t>((size_t)s.n_vtiles);
     w.tlist = c.take<int32_t>(ntile);
     w.plan = c.take<int32_t>((size_t)s.plan_ints);
+
     w.dh_acc = s.max_passes > 1 ? c.take<float>((size_t)s.Np * s.D) : nullptr;
     w.Ht = c.take<char>(elem * (size_t)s.D * s.Np);
     w.Gt = c.take<char>(elem * (size_t)s.cap * kBlockElems);
@@ -1311,6 +1463,7 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     a.dh_acc = w.dh_acc;
     a.dE = dE;
     a.dH = dH;
+
     const bool dma_g = ((int64_t)D * (int64_t)sizeof(T)) % kLogitRowBytes == 0;
     const bool kahan = !(flags & CCE_BWD_NO_KAHAN);
     for (int p = 0; p < s.max_passes; ++p) {
