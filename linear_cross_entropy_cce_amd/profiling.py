@@ -18,6 +18,13 @@ the logit kernel's reading.
 The traffic summary records a hash of the kernel's sources; `bench.py`
 reports the traffic only while the sources still hash the same.
 
+HBM traffic per step of kernels launched several times a step (the
+backward's pass kernels): the same two counter passes, summed over every
+dispatch of each kernel and divided by the profiled steps.
+
+    python -m linear_cross_entropy_cce_amd.profiling steptraffic --fetch DIR --write DIR \
+        --copy-bytes BYTES --steps K --kernels NAME... --title "..." --out profiles/<...>_traffic.md
+
 Core counters of the forward logit kernel (one pass, within the per-block
 limits of a single rocprofv3 run):
 
@@ -218,6 +225,50 @@ def write_counters_md(path: str, directory: str, command: str, title: str,
     return res
 
 
+def step_traffic(fetch_dir: str, write_dir: str, copy_bytes: int, kernels, steps: int) -> dict:
+    """FETCH_SIZE and WRITE_SIZE of each kernel summed over all its dispatches
+    and divided by `steps`, in bytes after the copy calibration."""
+    is_copy = lambda n: "copy" in n.lower() and "cce" not in n  # noqa: E731
+    out = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        c = [v for v in _per_dispatch(d, name, is_copy) if v > 0]
+        if not c:
+            raise RuntimeError(f"{name}: no copy dispatch for the calibration")
+        factor = copy_bytes / (max(c) * 1024.0)
+        for k in kernels:
+            v = _per_dispatch(d, name, lambda n, k=k: k in n)
+            if not v:
+                raise RuntimeError(f"{name}: no dispatch of {k}")
+            out.setdefault(k, {})[name] = {"dispatches": len(v), "kib": sum(v), "factor": factor,
+                                           "bytes_per_step": sum(v) * 1024.0 * factor / steps}
+    for k in kernels:
+        out[k]["traffic_bytes_per_step"] = out[k]["FETCH_SIZE"]["bytes_per_step"] + \
+            out[k]["WRITE_SIZE"]["bytes_per_step"]
+    return out
+
+
+def write_step_traffic_md(path: str, s: dict, copy_bytes: int, steps: int, command: str, title: str,
+                          fetch_dir: str, write_dir: str) -> None:
+    kernels = list(s)
+    lines = [f"# {title}", "", "Commands (on the MI355X box, from the repository root; one counter per pass):", "",
+             f"    {command.replace('COUNTER', 'FETCH_SIZE')}", f"    {command.replace('COUNTER', 'WRITE_SIZE')}", "",
+             "Summarised with:", "",
+             f"    python -m linear_cross_entropy_cce_amd.profiling steptraffic --fetch {fetch_dir} --write {write_dir} "
+             f"--copy-bytes {copy_bytes} --steps {steps} --kernels {' '.join(kernels)} --out "
+             f"{os.path.relpath(path, os.path.dirname(PKG))}", "",
+             f"Calibration: torch's device copy of {copy_bytes} bytes in the same run.  Sums over every dispatch",
+             f"of each kernel in the {steps} profiled steps, per step.", "",
+             "| kernel | dispatches | FETCH bytes / step | WRITE bytes / step | total bytes / step |",
+             "|---|---|---|---|---|"]
+    for k in kernels:
+        v = s[k]
+        lines.append(f"| `{k}` | {v['FETCH_SIZE']['dispatches']} | {v['FETCH_SIZE']['bytes_per_step']:.4g} | "
+                     f"{v['WRITE_SIZE']['bytes_per_step']:.4g} | {v['traffic_bytes_per_step']:.4g} |")
+    lines.append("")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+
+
 def write_stats_md(path: str, directory: str, steps: int, command: str, title: str) -> None:
     paths = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
     if not paths:
@@ -252,6 +303,15 @@ def main():
     t.add_argument("--command", default="rocprofv3 --pmc COUNTER --output-format csv -d pmc_COUNTER -o p "
                                          "-- python -u bench.py --steps 1 --warmup 1 --no-cpu-baseline "
                                          "--copy-probe 1073741824")
+    s2 = sub.add_parser("steptraffic")
+    s2.add_argument("--fetch", required=True)
+    s2.add_argument("--write", required=True)
+    s2.add_argument("--copy-bytes", type=int, required=True)
+    s2.add_argument("--steps", type=int, required=True)
+    s2.add_argument("--kernels", nargs="+", required=True)
+    s2.add_argument("--title", required=True)
+    s2.add_argument("--out", required=True)
+    s2.add_argument("--command", required=True)
     k = sub.add_parser("stats")
     k.add_argument("--dir", required=True)
     k.add_argument("--steps", type=int, required=True)
@@ -270,6 +330,9 @@ def main():
     a = ap.parse_args()
     if a.what == "counters":
         write_counters_md(a.out, a.dir, a.command, a.title, tuple(a.kernels), tuple(a.counters))
+    elif a.what == "steptraffic":
+        s = step_traffic(a.fetch, a.write, a.copy_bytes, a.kernels, a.steps)
+        write_step_traffic_md(a.out, s, a.copy_bytes, a.steps, a.command, a.title, a.fetch, a.write)
     elif a.what == "traffic":
         s = summarize(a.fetch, a.write, a.copy_bytes)
         write_md(a.out, s, a.copy_bytes, a.command, a.fetch, a.write)

@@ -83,3 +83,25 @@ def test_committed_traffic_summary_parses():
     # at least the algorithmic bytes of one launch (H and E once, bf16)
     assert nbytes >= 2 * (8192 + 256000) * 2304
     assert len(h) == 16
+
+
+def test_step_traffic_sums_dispatches(tmp_path):
+    # two steps, a kernel dispatched three times a step, and a 1 MiB copy that
+    # the counter reads as 512 KiB (factor 2)
+    for counter, per in (("FETCH_SIZE", 100.0), ("WRITE_SIZE", 40.0)):
+        d = str(tmp_path / counter)
+        rows = []
+        for i in range(6):
+            rows += _dispatch(i, "void cce::k_grad_pass<unsigned short, true>(x)", 1000, {counter: per})
+        rows += _dispatch(99, "__amd_rocclr_copyBuffer", 1000, {counter: 512.0})
+        _write_counters(d, rows)
+    s = P.step_traffic(str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE"), 1 << 20, ["k_grad_pass"], 2)
+    v = s["k_grad_pass"]
+    assert v["FETCH_SIZE"]["dispatches"] == 6
+    assert v["FETCH_SIZE"]["bytes_per_step"] == pytest.approx(3 * 100.0 * 1024 * 2)
+    assert v["WRITE_SIZE"]["bytes_per_step"] == pytest.approx(3 * 40.0 * 1024 * 2)
+    assert v["traffic_bytes_per_step"] == pytest.approx(3 * 140.0 * 1024 * 2)
+    out = tmp_path / "t.md"
+    P.write_step_traffic_md(str(out), s, 1 << 20, 2, "rocprofv3 --pmc COUNTER -- cmd", "title",
+                            str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE"))
+    assert "k_grad_pass" in out.read_text()
