@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, help="1..6 (2 = Gemma-2-2B head)")
+    ap.add_argument("--workload", type=int, default=2, help="1..7 (2 = Gemma-2-2B head)")
     ap.add_argument("--eps", type=float, default=None, help="filter threshold (default: the workload's)")
     ap.add_argument("--sort", action="store_true", help="vocabulary sort, used by the forward and the backward")
     ap.add_argument("--no-bound", action="store_true", help="backward without the forward's block-max table")
@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = about 20 s of work)")
     ap.add_argument("--no-kahan", action="store_true", help="backward with a plain fp32 dE sum (no compensation)")
     ap.add_argument("--full-de", action="store_true", help="unfiltered dE; the filter applies to dH only")
+    ap.add_argument("--fine", action="store_true", help="filter per 32 x 32 sub-tile instead of per 128 x 128 block")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph and replayed (detail.graph_ms_per_step)")
     ap.add_argument("--library-gemm", action="store_true",
@@ -197,14 +198,15 @@ def main():
     dl = torch.from_numpy(np.where(x.labels != x.ignore_index, 1.0 / max(nv, 1), 0.0).astype(np.float32)).to(dev)
     dH = torch.empty_like(H)
     dE = torch.empty_like(E)
-    stats = torch.zeros(6, dtype=torch.int64, device=dev)
+    stats = torch.zeros(7, dtype=torch.int64, device=dev)
     # block-max table (one float per 128 x 128 logit block), as the autograd wrapper uses it
     tb = None if a.no_bound else torch.empty(B.block_max_elems(N, V), dtype=torch.float32, device=dev)
     ws_f = torch.empty(B.forward_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(B.backward_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev)
     ws_s = torch.empty(B.vocab_order_workspace_bytes(N, D, V, dt), dtype=torch.uint8, device=dev) if a.sort else None
     perm = torch.empty(V, dtype=torch.int32, device=dev) if a.sort else None
-    bwd_flags = (B.CCE_BWD_NO_KAHAN if a.no_kahan else 0) | (B.CCE_BWD_FULL_DE if a.full_de else 0)
+    bwd_flags = (B.CCE_BWD_NO_KAHAN if a.no_kahan else 0) | (B.CCE_BWD_FULL_DE if a.full_de else 0) | \
+        (B.CCE_BWD_FINE_FILTER if a.fine else 0)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     mem0 = torch.cuda.memory_allocated()
@@ -263,14 +265,15 @@ def main():
     sort_ms = [e[3].elapsed_time(e[0]) for e in evs]
     step_ms = wall * 1e3 / a.steps
     st = stats.cpu().numpy()
-    n_live, n_label, n_total, n_recomp = int(st[0]), int(st[1]), int(st[2]), int(st[4])
+    n_live, n_label, n_total, n_recomp, n_sub = int(st[0]), int(st[1]), int(st[2]), int(st[4]), int(st[6])
     br, bv = B.filter_block()
     # Algorithmic work: the forward logits, the recomputed blocks' logits, and
-    # the dH and dE products of the blocks that keep their softmax part
-    # (4 D flops per entry).  A label-only block keeps only its label entries,
-    # one per row at most: 4 D flops per label entry (at most N_valid of them).
+    # the dH and dE products of the 32 x 32 sub-tiles that keep their softmax
+    # part (4 D flops per entry; every sub-tile of a kept block without the
+    # fine filter).  A label-only block keeps only its label entries, one per
+    # row at most: 4 D flops per label entry (at most N_valid of them).
     f_logits = 2.0 * nv * D * V
-    f_grad = 4.0 * D * n_live * br * bv + 4.0 * D * (nv if n_label else 0)
+    f_grad = 4.0 * D * n_sub * 32 * 32 + 4.0 * D * (nv if n_label else 0)
     f_exec = f_logits + 2.0 * D * n_recomp * br * bv + f_grad
     peak = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_FP32_TFLOPS
     fwd_avg = float(np.mean(fwd_ms))
@@ -295,7 +298,8 @@ def main():
         "data": "synthetic (seeded; head shape of the named model, random values)",
         "config": {"workload": f"{x.name} (N={N}, D={D}, V={V}, {x.dtype}, eps={eps:g}, sort={a.sort})",
                    "N": N, "D": D, "V": V, "n_valid": nv, "filter_eps": eps, "sort_vocab": a.sort,
-                   "filter_block": [br, bv], "kahan_de": not a.no_kahan, "full_de": a.full_de},
+                   "filter_block": [br, bv], "kahan_de": not a.no_kahan, "full_de": a.full_de,
+                   "fine_filter": a.fine},
         "roofline": {"kernel": "k_fwd (cce_forward bracket)", "bound": "mfma", "achieved": achieved,
                      "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
         "detail": {
@@ -305,6 +309,7 @@ def main():
             "fwd_ms_min": float(np.min(fwd_ms)), "bwd_ms_min": float(np.min(bwd_ms)),
             "blocks_softmax_kept": n_live, "blocks_label_only": n_label, "blocks_total": n_total,
             "kept_frac": (n_live + n_label) / max(n_total, 1),
+            "subtiles_softmax_kept": n_sub, "subtile_kept_frac": n_sub / max(16 * n_total, 1),
             "blocks_recomputed": n_recomp, "recomputed_frac": n_recomp / max(n_total, 1),
             "block_max": tb is not None,
             "F_exec_TF": f_exec / 1e12, "F_exec_frac_peak": f_exec / (step_ms * 1e-3) / (peak * 1e12),

@@ -68,6 +68,12 @@ typedef enum { CCE_F32 = 0, CCE_BF16 = 1 } cce_dtype;
 #define CCE_BWD_NO_KAHAN 1u /* plain fp32 accumulation of dE across blocks (numerics studies) */
 #define CCE_BWD_FULL_DE 2u  /* dE from every block (unfiltered, Kahan-compensated), dH filtered:
                                the "full classifier gradient" variant; every tile is recomputed */
+#define CCE_BWD_FINE_FILTER 8u /* the filter decides per 32 x 32 sub-tile (32 valid tokens x 32 vocabulary
+                                  entries in processing order, a quarter of a filter block's side) instead
+                                  of per 128 x 128 block: a sub-tile keeps the softmax part of its entries
+                                  iff one of them other than a label entry has p >= filter_eps, and the
+                                  dH / dE products skip the sub-tiles left all zero.  Not combined with
+                                  CCE_BWD_FULL_DE (CCE_ERR_ARG). */
 #define CCE_BWD_DEBUG_STORE_LIMIT 4u /* debug: kept blocks take store slots only below half of the store's
                                         capacity, as if the pass plan had overfilled it; the blocks left
                                         without a slot are dropped and counted in stats[5] (the gradients
@@ -180,14 +186,16 @@ cce_status cce_vocab_order(const void *H, const void *E, const int64_t *labels,
  *    always keeps its whole gradient dloss_i (p_{i,y_i} - 1).
  *  - perm: NULL, or the permutation from cce_vocab_order (int32 [V]); it only
  *    changes which vocabulary entries share a filter block.
- *  - flags: 0 or any of CCE_BWD_NO_KAHAN, CCE_BWD_FULL_DE,
+ *  - flags: 0 or any of CCE_BWD_NO_KAHAN, CCE_BWD_FULL_DE, CCE_BWD_FINE_FILTER,
  *    CCE_BWD_DEBUG_STORE_LIMIT.
- *  - stats: NULL, or device int64 [6] that receives (softmax-surviving blocks,
+ *  - stats: NULL, or device int64 [7] that receives (softmax-surviving blocks,
  *    label-only blocks, total blocks, valid rows, recomputed blocks, kept
- *    blocks dropped because a pass's block store was full).  The last entry
- *    is 0 unless CCE_BWD_DEBUG_STORE_LIMIT is set: the pass plan sizes every
- *    pass to fit the store, and a nonzero count means the gradients are
- *    incomplete.
+ *    blocks dropped because a pass's block store was full, 32 x 32 sub-tiles
+ *    whose softmax part is kept).  Entry 5 is 0 unless
+ *    CCE_BWD_DEBUG_STORE_LIMIT is set: the pass plan sizes every pass to fit
+ *    the store, and a nonzero count means the gradients are incomplete.
+ *    Entry 6 counts all 16 sub-tiles of a surviving block unless
+ *    CCE_BWD_FINE_FILTER is set.
  * Ignored rows get dH = 0 and add nothing to dE.
  * ws: device scratch of at least cce_backward_workspace_bytes bytes.
  */

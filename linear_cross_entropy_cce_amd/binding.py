@@ -32,8 +32,10 @@ CCE_BF16 = 1
 CCE_BWD_NO_KAHAN = 1
 CCE_BWD_FULL_DE = 2
 CCE_BWD_DEBUG_STORE_LIMIT = 4
+CCE_BWD_FINE_FILTER = 8
+FINE_SUBTILE = (32, 32)  # (tokens, vocabulary entries) of a sub-tile of CCE_BWD_FINE_FILTER
 
-STATS_LEN = 6  # entries of the backward's stats buffer (include/cce.h)
+STATS_LEN = 7  # entries of the backward's stats buffer (include/cce.h)
 
 # Every entry point include/cce.h declares.
 EXPORTS = (
@@ -278,7 +280,7 @@ def cce_vocab_order(H, E, labels, ignore_index=-100, perm=None, keys=None, want_
 def cce_backward(H, E, labels, lse, dloss, filter_eps=2.0 ** -12, ignore_index=-100, perm=None, flags=0,
                  dH=None, dE=None, stats=None, ws=None, stream=None, block_max=None):
     """dH [N, D], dE [V, D] (input dtype) of sum_i dloss_i loss_i.  stats:
-    None or int64 [6] (see include/cce.h); block_max: None or the table
+    None or int64 [7] (see include/cce.h); block_max: None or the table
     cce_forward wrote for the same H, E, labels and perm."""
     import torch
     N, D, V = _shapes(H, E, labels)

@@ -11,7 +11,7 @@ using namespace cce;
 
 namespace {
 
-constexpr int kVersion = 10100;  // 1.1.0
+constexpr int kVersion = 10200;  // 1.2.0
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -110,7 +110,9 @@ cce_status backward_impl(const void *H, const VocabRows &E, int64_t off1, const 
     if (!dtype_ok(dtype)) return CCE_ERR_DTYPE;
     if (!shape_ok(N, D, V)) return CCE_ERR_SHAPE;
     if (!(filter_eps >= 0.f) || isinf(filter_eps)) return CCE_ERR_ARG;  // rejects NaN and negatives
-    if (flags & ~(CCE_BWD_NO_KAHAN | CCE_BWD_FULL_DE | CCE_BWD_DEBUG_STORE_LIMIT)) return CCE_ERR_ARG;
+    if (flags & ~(CCE_BWD_NO_KAHAN | CCE_BWD_FULL_DE | CCE_BWD_FINE_FILTER | CCE_BWD_DEBUG_STORE_LIMIT))
+        return CCE_ERR_ARG;
+    if ((flags & CCE_BWD_FINE_FILTER) && (flags & CCE_BWD_FULL_DE)) return CCE_ERR_ARG;
     if (!aligned(H, 16) || !aligned(E.e0, 16) || !aligned(E.e1, 16) || !aligned(dH, 16) || !aligned(dE.d0, 16) ||
         !aligned(dE.d1, 16) || !aligned(ws, 16) || !aligned(labels, 8) || !aligned(lse, 4) || !aligned(dloss, 4) ||
         !aligned(perm, 4) || !aligned(stats, 8) || !aligned(block_max, 4))

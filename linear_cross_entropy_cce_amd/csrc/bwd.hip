@@ -109,11 +109,13 @@ struct BwdArgs {
     int D, V, cbp, n_rb;
     float eps;
     int full_de;  // dE from every block (status 3 = kept for dE only), dH filtered
+    int fine;     // the filter decides per 32 x 32 sub-tile (CCE_BWD_FINE_FILTER)
     T *Gt, *Gn;
     int64_t cap;
     int64_t cap_take;  // slots the epilogue may take: cap (cap / 2 with CCE_BWD_DEBUG_STORE_LIMIT)
     uint8_t *st;
     int32_t *slot;
+    uint16_t *smask;  // bit 4 i + j: sub-tile (vocabulary rows 32 i.., tokens 32 j..) of a kept block may be nonzero
     int64_t *stats;
     float *dh_acc;
     Rows2<T> dE;  // same layout as E
@@ -122,7 +124,7 @@ struct BwdArgs {
 
 // ------------------------------------------------------------ small kernels
 __global__ void k_stats_init(int64_t *stats) {
-    if (threadIdx.x < 6) stats[threadIdx.x] = 0;
+    if (threadIdx.x < 7) stats[threadIdx.x] = 0;
 }
 
 __global__ void k_stats_fin(int64_t *stats, const int32_t *__restrict__ nvalid_p, int64_t n_vblocks) {
@@ -242,6 +244,48 @@ __device__ __forceinline__ int build_list(int n, Flag flag, int *list, int *wcnt
         if (f) list[off + __popcll(b & below)] = i;
         int sum = 0;
         for (int w = 0; w < kW; ++w) sum += wcnt[w];
+        total += sum;
+        __syncthreads();
+    }
+    return total;
+}
+
+// The K stages, among kspb per block, of the listed blocks 0 .. n-1 that
+// cover a sub-tile whose gradient may be nonzero: stage k of block i is
+// listed iff mask[i] & sel(k).  Entries (i << 4 | k) in block then stage
+// order, bit 31 set on each block's last listed stage.  Returns their number.
+// Must be called by all threads.
+template <int kThreads, class Sel>
+__device__ __forceinline__ int build_stages(int n, int kspb, const int *mask, Sel sel, int *stl, int *wtot) {
+    constexpr int kW = kThreads / 64;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    int total = 0;
+    for (int base = 0; base < n; base += kThreads) {
+        const int i = base + t;
+        int c = 0;
+        if (i < n)
+            for (int k = 0; k < kspb; ++k) c += (mask[i] & sel(k)) != 0;
+        int x = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) wtot[wave] = x;
+        __syncthreads();
+        int off = total + x - c;
+        for (int w = 0; w < wave; ++w) off += wtot[w];
+        if (i < n) {
+            int last = -1;
+            for (int k = 0; k < kspb; ++k)
+                if (mask[i] & sel(k)) {
+                    stl[off] = (i << 4) | k;
+                    last = off++;
+                }
+            if (last >= 0) stl[last] |= (int)0x80000000u;
+        }
+        int sum = 0;
+        for (int w = 0; w < kW; ++w) sum += wtot[w];
         total += sum;
         __syncthreads();
     }
@@ -399,7 +443,12 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
                                            float *__restrict__ glab, T *__restrict__ Gt, T *__restrict__ Gn,
                                            int64_t cap, int32_t *__restrict__ counter, uint8_t *__restrict__ st,
                                            int32_t *__restrict__ slotm, int64_t *__restrict__ stats, int *qflag,
-                                           int *qstat, int *qslot, int full_de, int qmask) {
+                                           int *qstat, int *qslot, int full_de, int qmask, int fine,
+                                           uint16_t *__restrict__ smask) {
+    // qflag[0..3]: per block, bit 0 = some non-label p >= eps, bit 1 = a label
+    // entry; qflag[4..7]: the 32 x 32 sub-tiles (bit 4 i + j: vocabulary
+    // rows 32 i.., tokens 32 j.. of the block) with a non-label p >= eps;
+    // qflag[8..11]: the sub-tiles holding a label entry.
     const int tid = opaque_tid();  // fresh per tile: see tile_row
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave % TL::WM, wn = wave / TL::WM;
@@ -409,7 +458,7 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
     // dloss (0 there, so that g = 0), the label's row as acc_row_const in
     // this lane (-1000: none) and the label entry's softmax probability.
     float lse_t[TL::TN], dl_t[TL::TN], pl_t[TL::TN];
-    int lab_t[TL::TN];
+    int lab_t[TL::TN], lsub[TL::TN];  // lsub: 32-row group of the label within this wave's rows (-1: none)
     bool any_live = false, any_label = false;
     const int rbase = wm * TL::kWaveM + 4 * (lane >> 5);  // tile_row = rbase + acc_row_const
     const bool wsoft = SOFTMAX && ((qmask >> quad) & 1);  // this wave's block was recomputed (wave-uniform)
@@ -420,6 +469,7 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
         dl_t[tn] = 0.f;
         pl_t[tn] = 0.f;
         lab_t[tn] = -1000;
+        lsub[tn] = -1;
         if (tok < nv) {
             const int64_t row = idx[tok];
             lse_t[tn] = lse[row];
@@ -430,6 +480,7 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
             const int lr = ypos - p0 - wm * TL::kWaveM;  // row within this wave's 128 vocabulary rows
             const bool here = lr >= 0 && lr < TL::kWaveM;
             lab_t[tn] = here ? ypos - p0 - rbase : -1000;
+            lsub[tn] = here ? lr / 32 : -1;
             any_label |= here;
             // the label entry's own softmax probability where the block was
             // not recomputed: from the forward's label logit, the same bits
@@ -438,6 +489,11 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
         }
     }
     const int vlim = row_limit<TL>(V - p0, tid);  // entry (tm, r) is a real vocabulary row iff acc_row_const < vlim
+    // This wave's sub-tile (tm, tn) is sub-tile 4 tm + jw + tn of its block.
+    static_assert(TL::kWaveM == kBlockVocab && TL::TM == 4 && TL::TN == 2 && TL::kWaveN == 64,
+                  "a wave holds 4 x 2 sub-tiles of 32 x 32 of one block");
+    const int jw = 2 * (wn & 1);
+    uint32_t sub_live = 0;  // this wave's sub-tiles with a non-label p >= eps (block bit numbering)
     if (wsoft) {
 #pragma unroll
         for (int tn = 0; tn < TL::TN; ++tn) {
@@ -447,19 +503,33 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
             // plan only counts blocks that hold one
             const bool tv = lse_t[tn] != __builtin_huge_valf();
 #pragma unroll
-            for (int tm = 0; tm < TL::TM; ++tm)
+            for (int tm = 0; tm < TL::TM; ++tm) {
+                bool live = false;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const bool ok = acc_row_const(tm, r) < vlim;
                     const float p = ok ? __builtin_amdgcn_exp2f((acc[tm][tn][r] - lse_t[tn]) * kLog2e) : 0.f;
                     acc[tm][tn][r] = p;
                     // the filter looks at the entries other than the label one
-                    any_live |= (p >= eps) && ok && tv && acc_row_const(tm, r) != lab_t[tn];
+                    live |= (p >= eps) && ok && tv && acc_row_const(tm, r) != lab_t[tn];
                 }
+                any_live |= live;
+                if (__ballot(live)) sub_live |= 1u << (4 * tm + jw + tn);
+            }
         }
     }
+    uint32_t sub_lab = 0;  // this wave's sub-tiles holding a label entry
+#pragma unroll
+    for (int tn = 0; tn < TL::TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < TL::TM; ++tm)
+            if (__ballot(lsub[tn] == tm)) sub_lab |= 1u << (4 * tm + jw + tn);
     const uint64_t bl = __ballot(any_live), bb = __ballot(any_label);
-    if (lane == 0 && (bl | bb)) atomicOr(&qflag[quad], (bl ? 1 : 0) | (bb ? 2 : 0));
+    if (lane == 0 && (bl | bb)) {
+        atomicOr(&qflag[quad], (bl ? 1 : 0) | (bb ? 2 : 0));
+        atomicOr(&qflag[4 + quad], (int)sub_live);
+        atomicOr(&qflag[8 + quad], (int)sub_lab);
+    }
     __syncthreads();
     if (tid < 4) {
         const int f = qflag[tid];
@@ -482,9 +552,21 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
         qstat[tid] = sv;
         qslot[tid] = s;
         st[(int64_t)rb * cbp + cb] = (uint8_t)sv;
-        if (sv) slotm[(int64_t)rb * cbp + cb] = s;
+        if (sv) {
+            slotm[(int64_t)rb * cbp + cb] = s;
+            // sub-tiles whose stored gradient may be nonzero: with the fine
+            // filter those with a kept softmax part or a label entry; a
+            // label-only block only its label sub-tiles; otherwise all
+            const int live16 = qflag[4 + tid], lab16 = qflag[8 + tid];
+            smask[(int64_t)rb * cbp + cb] =
+                (uint16_t)(sv == 1 ? (fine ? (live16 | lab16) : 0xFFFF) : (sv == 2 ? lab16 : 0xFFFF));
+        }
         if (stats) {
             if (sv == 1 || sv == 2) atomicAdd(reinterpret_cast<unsigned long long *>(stats + (sv == 1 ? 0 : 1)), 1ull);
+            // 32 x 32 sub-tiles whose softmax part is kept (all 16 of a kept block without the fine filter)
+            if (sv == 1)
+                atomicAdd(reinterpret_cast<unsigned long long *>(stats + 6),
+                          (unsigned long long)(fine ? __popc((unsigned)qflag[4 + tid]) : 16));
             // blocks whose logits were recomputed (real rows and vocabulary entries only)
             if (SOFTMAX && ((qmask >> tid) & 1) && rb * kBlockRows < nv && (int64_t)cb * kBlockVocab < V)
                 atomicAdd(reinterpret_cast<unsigned long long *>(stats + 4), 1ull);
@@ -494,6 +576,9 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
     const int status = qstat[quad];
     if (status == 0) return;  // wave-uniform
     const bool glab_only = status == 2;
+    // the block's sub-tiles that keep their softmax part (all of a kept
+    // block without the fine filter)
+    const uint32_t keep16 = fine ? (uint32_t)qflag[4 + quad] : 0xFFFFu;
     T *gt = Gt + (int64_t)qslot[quad] * kBlockElems;
     T *gn = Gn + (int64_t)qslot[quad] * kBlockElems;
 
@@ -513,8 +598,10 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
                     const bool il = acc_row_const(tm, r) == lab_t[tn];
                     const float onehot = il ? 1.f : 0.f;
                     // the label entry keeps its exact softmax part; the others only in a kept block
+                    // (sub-tile)
+                    const bool subk = (keep16 >> (4 * tm + jw + tn)) & 1;
                     const float pk = il ? (wsoft ? acc[tm][tn][r] : pl_t[tn])
-                                        : ((wsoft && status == 1) ? acc[tm][tn][r] : 0.f);
+                                        : ((wsoft && status == 1 && subk) ? acc[tm][tn][r] : 0.f);
                     const float g = ok ? dl_t[tn] * (pk - onehot) : 0.f;
                     g4[q] = from_f32<T>(g);
                     // full dE: the vocabulary-major copy (read by dE) holds the unfiltered gradient
@@ -654,7 +741,7 @@ __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int
             const bool rec = (tn8 & 0x80) != 0;
             const int qmask = DMA ? (tn8 >> 3) & 15 : 15;  // the VGPR-staged recompute computes every block
             const int tok0 = rt * TL::BN, p0 = vt * TL::BM;
-            if (threadIdx.x < 4) qflag[threadIdx.x] = 0;
+            if (threadIdx.x < 12) qflag[threadIdx.x] = 0;
             __syncthreads();
             f32x16 acc[TL::TM][TL::TN];
             if (rec) {
@@ -664,11 +751,11 @@ __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int
                 __syncthreads();
                 g_epilogue<T, TL, true>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
                                         a.lse, a.dloss, a.zlab, a.glab, a.Gt, a.Gn, a.cap_take, pv.counter + p, a.st, a.slot, a.stats,
-                                        qflag, qstat, qslot, a.full_de, qmask);
+                                        qflag, qstat, qslot, a.full_de, qmask, a.fine, a.smask);
             } else {
                 g_epilogue<T, TL, false>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
                                          a.lse, a.dloss, a.zlab, a.glab, a.Gt, a.Gn, a.cap_take, pv.counter + p, a.st, a.slot, a.stats,
-                                         qflag, qstat, qslot, a.full_de, 0);
+                                         qflag, qstat, qslot, a.full_de, 0, a.fine, a.smask);
             }
         }
     }
@@ -767,7 +854,8 @@ struct DhEngine {
     }
     __device__ __forceinline__ int clamp_ahead(int ahead) const { return ahead < kDepth - 1 ? ahead : kDepth - 1; }
 
-    __device__ __forceinline__ void compute(int buf, f32x16 (&acc)[TL::TM][TL::TN], int tid) const {
+    __device__ __forceinline__ void compute(int buf, f32x16 (&acc)[TL::TM][TL::TN], int tid,
+                                           uint32_t rows = (1u << TL::TM) - 1) const {
         const int lane = tid & 63, wave = tid >> 6;
         const int ra0 = (wave % TL::WM) * TL::kWaveM + (lane & 31);
         const int nb0 = (wave / TL::WM) * TL::kWaveN;
@@ -778,7 +866,8 @@ struct DhEngine {
             const int c = 2 * kk + (lane >> 5);
             u32x4 fa[TL::TM], fb[TL::TN];
 #pragma unroll
-            for (int tm = 0; tm < TL::TM; ++tm) fa[tm] = A[dma_slot<64>(ra0 + tm * 32, c)];
+            for (int tm = 0; tm < TL::TM; ++tm)
+                if ((rows >> tm) & 1) fa[tm] = A[dma_slot<64>(ra0 + tm * 32, c)];
 #pragma unroll
             for (int tn = 0; tn < TL::TN; ++tn) {
                 const int n0 = nb0 + tn * 32;
@@ -807,8 +896,9 @@ struct DhEngine {
             }
 #pragma unroll
             for (int tm = 0; tm < TL::TM; ++tm)
+                if ((rows >> tm) & 1)
 #pragma unroll
-                for (int tn = 0; tn < TL::TN; ++tn) Mfma<T>::step(fa[tm], fb[tn], acc[tm][tn]);
+                    for (int tn = 0; tn < TL::TN; ++tn) Mfma<T>::step(fa[tm], fb[tn], acc[tm][tn]);
         }
     }
 };
@@ -826,6 +916,9 @@ struct GradLds {
     int lslot[kListCap];
     int wcnt[TileG::kWaves];
     int soft;  // the vocabulary block has a block with a kept softmax part (status 1 or 3)
+    // with the fine filter: sub-tile masks of the listed blocks and their listed K stages
+    int lmask[kListCap];
+    int stl[kListCap * 8];
     // label entries of a vocabulary block (label path), grouped by vocabulary
     // row, in token order within a row
     int ent_h[kLabelEntries];                           // row of H
@@ -973,11 +1066,11 @@ __device__ __forceinline__ int de_try_label(GradLds<T> &sh, int cb, int d0, int 
 // segments (bf16).  A vocabulary block with nothing kept gets dE = 0.
 // pre_n >= 0: the kept row blocks (all of them: n_rb <= kListCap) are
 // already listed in sh.list.
-template <typename T, bool KAHAN>
+template <typename T, bool KAHAN, bool FINE>
 __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb, const uint8_t *__restrict__ st,
                                         const int32_t *__restrict__ slotm, int cbp, const T *__restrict__ Gt,
                                         const T *__restrict__ Ht, int64_t ldh, const int32_t *__restrict__ perm,
-                                        int D, int V, Rows2<T> dE, int pre_n) {
+                                        int D, int V, Rows2<T> dE, int pre_n, const uint16_t *__restrict__ smask) {
     using TL = TileG;
     using DE = DmaEngine<T, TL>;
     constexpr int kBlockBytes = kBlockRows * (int)sizeof(T);  // K bytes of one row block
@@ -1009,13 +1102,31 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
                                  : build_list<TL::kThreads>(
                                        cnt, [&](int i) { return st[(int64_t)(base + i) * cbp + cb] != 0; }, sh.list,
                                        sh.wcnt);
-        for (int i = threadIdx.x; i < n; i += TL::kThreads) sh.lslot[i] = slotm[(int64_t)(base + sh.list[i]) * cbp + cb];
+        for (int i = threadIdx.x; i < n; i += TL::kThreads) {
+            sh.lslot[i] = slotm[(int64_t)(base + sh.list[i]) * cbp + cb];
+            if (FINE) sh.lmask[i] = smask[(int64_t)(base + sh.list[i]) * cbp + cb];
+        }
         __syncthreads();
         any |= n > 0;
-        const int total = n * kSpb;
+        // Fine filter: stage k covers the tokens of sub-tile column jk(k) of
+        // the block; only stages with a possibly nonzero sub-tile are listed,
+        // and a wave multiplies only its vocabulary sub-rows whose sub-tile
+        // may be nonzero.  (All-zero sub-tiles add exact zeros, so skipping
+        // them changes nothing but the work.)
+        constexpr int kTokPerStage = DE::kStageBytes / (int)sizeof(T);
+        auto jk = [](int k) { return k * kTokPerStage / 32; };
+        int total = n * kSpb;
+        if constexpr (FINE)
+            total = build_stages<TL::kThreads>(
+                n, kSpb, sh.lmask, [&](int k) { return 0x1111 << jk(k); }, sh.stl, sh.wcnt);
         auto issue = [&](int buf, int q) {
-            const int b = q / kSpb, k = (q % kSpb) * DE::kStageBytes;
-            eng.issue2(buf, sh.lslot[b] * kStoreBytes + k, (int64_t)(base + sh.list[b]) * kBlockBytes + k);
+            int b = q / kSpb, k = q % kSpb;
+            if constexpr (FINE) {
+                b = (sh.stl[q] >> 4) & 0x7FF;
+                k = sh.stl[q] & 15;
+            }
+            const int kb = k * DE::kStageBytes;
+            eng.issue2(buf, sh.lslot[b] * kStoreBytes + kb, (int64_t)(base + sh.list[b]) * kBlockBytes + kb);
         };
 #pragma unroll
         for (int q = 0; q < DE::kDepth; ++q)
@@ -1024,8 +1135,19 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
             const int ahead = total - 1 - s;
             eng.wait_stage(eng.clamp_ahead(ahead));
             if (s + DE::kDepth < total) issue((s + DE::kDepth) % DE::kStages, s + DE::kDepth);
-            eng.compute(s % DE::kStages, acc, tid);
-            if (KAHAN && (s % kSpb) == kSpb - 1) {
+            bool flush = (s % kSpb) == kSpb - 1;
+            if constexpr (FINE) {
+                const int e = sh.stl[s];
+                const uint32_t m = (uint32_t)sh.lmask[(e >> 4) & 0x7FF];
+                const int j = jk(e & 15), i0 = 2 * ((tid >> 6) % TL::WM);  // the wave's first vocabulary sub-row
+                static_assert(TL::TM == 2 && TL::kWaveM == 64, "a wave holds two 32-row sub-rows of the block");
+                const uint32_t rows = ((m >> (4 * i0 + j)) & 1) | (((m >> (4 * (i0 + 1) + j)) & 1) << 1);
+                compute_rows<T, TL>(eng, s % DE::kStages, acc, tid, rows);
+                flush = e < 0;
+            } else {
+                eng.compute(s % DE::kStages, acc, tid);
+            }
+            if (KAHAN && flush) {
 #pragma clang fp contract(off)
 #pragma unroll
                 for (int tm = 0; tm < TL::TM; ++tm)
@@ -1111,14 +1233,14 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
 // which starts from the previous passes' fp32 sum, so the result does not
 // depend on where the passes are cut.  The last pass writes dH in the output
 // dtype.
-template <typename T>
+template <typename T, bool FINE>
 __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool multi, bool last, int cb0, int cb1,
                                         const uint8_t *__restrict__ st, const int32_t *__restrict__ slotm, int cbp,
                                         int nv, const int32_t *__restrict__ idx, const T *__restrict__ Gn,
                                         Rows2<const T> E, const int32_t *__restrict__ perm, int D, int V,
                                         const float *__restrict__ glab,
                                         const int64_t *__restrict__ labels, float *__restrict__ dh_acc,
-                                        T *__restrict__ dH) {
+                                        T *__restrict__ dH, const uint16_t *__restrict__ smask) {
     using TL = TileG;
     using DH = DhEngine<T>;
     const int tok0 = rb * TL::BM;
@@ -1151,13 +1273,27 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
                 return v == 1;  // label-only blocks: the label term below
             },
             sh.list, sh.wcnt);
-        for (int i = threadIdx.x; i < n; i += TL::kThreads) sh.lslot[i] = slotm[(int64_t)rb * cbp + base + sh.list[i]];
+        for (int i = threadIdx.x; i < n; i += TL::kThreads) {
+            sh.lslot[i] = slotm[(int64_t)rb * cbp + base + sh.list[i]];
+            if (FINE) sh.lmask[i] = smask[(int64_t)rb * cbp + base + sh.list[i]];
+        }
         __syncthreads();
         any |= n > 0;
-        const int total = n * DH::kSpb;
+        // Fine filter: stage k covers the vocabulary entries of sub-tile row
+        // ik(k) of the block; as for dE, only stages and wave rows (token
+        // sub-columns here) whose sub-tile may be nonzero are multiplied.
+        auto ik = [](int k) { return k * DH::kKv / 32; };
+        int total = n * DH::kSpb;
+        if constexpr (FINE)
+            total = build_stages<TL::kThreads>(
+                n, DH::kSpb, sh.lmask, [&](int k) { return 0xF << (4 * ik(k)); }, sh.stl, sh.wcnt);
         auto issue = [&](int buf, int q) {
-            const int b = q / DH::kSpb;
-            eng.issue(buf, Gn, sh.lslot[b], E, perm, (base + sh.list[b]) * kBlockVocab, q % DH::kSpb, V);
+            int b = q / DH::kSpb, k = q % DH::kSpb;
+            if constexpr (FINE) {
+                b = (sh.stl[q] >> 4) & 0x7FF;
+                k = sh.stl[q] & 15;
+            }
+            eng.issue(buf, Gn, sh.lslot[b], E, perm, (base + sh.list[b]) * kBlockVocab, k, V);
         };
 #pragma unroll
         for (int q = 0; q < DH::kDepth; ++q)
@@ -1166,8 +1302,19 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
             const int ahead = total - 1 - s;
             eng.wait_stage(eng.clamp_ahead(ahead));
             if (s + DH::kDepth < total) issue((s + DH::kDepth) % DH::kStages, s + DH::kDepth);
-            eng.compute(s % DH::kStages, acc, tid);
-            if ((s % DH::kSpb) == DH::kSpb - 1) {
+            bool flush = (s % DH::kSpb) == DH::kSpb - 1;
+            if constexpr (FINE) {
+                const int e = sh.stl[s];
+                const uint32_t m = (uint32_t)sh.lmask[(e >> 4) & 0x7FF];
+                const int i = ik(e & 15), j0 = 2 * ((tid >> 6) % TL::WM);  // the wave's first token sub-column
+                static_assert(TL::TM == 2 && TL::kWaveM == 64, "a wave holds two 32-token sub-columns of the block");
+                const uint32_t rows = ((m >> (4 * i + j0)) & 1) | (((m >> (4 * i + j0 + 1)) & 1) << 1);
+                eng.compute(s % DH::kStages, acc, tid, rows);
+                flush = e < 0;
+            } else {
+                eng.compute(s % DH::kStages, acc, tid);
+            }
+            if (flush) {
 #pragma unroll
                 for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
@@ -1239,7 +1386,7 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
 // items from a work queue: first the (row block, feature tile) dH items,
 // which carry the longer K loops, then the (vocabulary block, feature tile)
 // dE items.
-template <typename T, bool KAHAN>
+template <typename T, bool KAHAN, bool FINE>
 __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, GradLds<T> &sh, int *ticket) {
     using TL = TileG;
     const PlanView pv = plan_view(a.plan, a.max_passes);
@@ -1258,8 +1405,8 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
     // two loops rather than one with a branch: each keeps its own registers
     int64_t it = take_ticket(queue, ticket);
     while (it < n_dh) {
-        dh_item<T>(sh, (int)(it % n_rbv), (int)(it / n_rbv) * TL::BN, P > 1, p == P - 1, cb0, cb1, a.st, a.slot, a.cbp,
-                   nv, a.idx, a.Gn, a.E, a.perm, a.D, a.V, a.glab, a.labels, a.dh_acc, a.dH);
+        dh_item<T, FINE>(sh, (int)(it % n_rbv), (int)(it / n_rbv) * TL::BN, P > 1, p == P - 1, cb0, cb1, a.st, a.slot,
+                         a.cbp, nv, a.idx, a.Gn, a.E, a.perm, a.D, a.V, a.glab, a.labels, a.dh_acc, a.dH, a.smask);
         it = take_ticket(queue, ticket);
     }
     while (it < n_dh + n_de) {
@@ -1267,8 +1414,8 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
         const int cb = cb0 + (int)(q / n_dt), d0 = (int)(q % n_dt) * TL::BN;
         const int n = de_try_label<T>(sh, cb, d0, n_rbv, a.st, a.cbp, lc, a.perm, a.D, a.V, a.dE);
         if (n != -1)
-            de_item<T, KAHAN>(sh, cb, d0, n_rbv, a.st, a.slot, a.cbp, a.Gt, a.Ht, a.ldh, a.perm, a.D, a.V, a.dE,
-                              n >= 0 ? n : -1);
+            de_item<T, KAHAN, FINE>(sh, cb, d0, n_rbv, a.st, a.slot, a.cbp, a.Gt, a.Ht, a.ldh, a.perm, a.D, a.V, a.dE,
+                                    n >= 0 ? n : -1, a.smask);
         it = take_ticket(queue, ticket);
     }
 }
@@ -1277,7 +1424,7 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
 template <typename T, bool DMA>
 __global__ __launch_bounds__(TileF::kThreads) void k_g_pass(BwdArgs<T> a, int p) {
     __shared__ u32x4 lds[GPassLds<T, DMA>::value];
-    __shared__ int qflag[4], qstat[4], qslot[4];
+    __shared__ int qflag[12], qstat[4], qslot[4];
     // The work-queue ticket has a word of its own: the epilogue's waves read
     // qslot after its last barrier, while thread 0 may already take the next
     // ticket.
@@ -1286,13 +1433,13 @@ __global__ __launch_bounds__(TileF::kThreads) void k_g_pass(BwdArgs<T> a, int p)
     g_phase<T, DMA>(a, p, blockIdx.x, gridDim.x, lds, qflag, qstat, qslot, &ticket);
 }
 
-template <typename T, bool KAHAN>
+template <typename T, bool KAHAN, bool FINE>
 __global__ __launch_bounds__(TileG::kThreads) void k_grad_pass(BwdArgs<T> a, int p) {
     __shared__ GradLds<T> sh;
     __shared__ int ticket;
     const int P = *plan_view(a.plan, a.max_passes).P;
     if (p >= P) return;
-    grad_phase<T, KAHAN>(a, p, P, sh, &ticket);
+    grad_phase<T, KAHAN, FINE>(a, p, P, sh, &ticket);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1337,6 +1484,7 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     w.lab = c.take<uint8_t>(nblk);
     w.st = c.take<uint8_t>(nblk);
     w.slot = c.take<int32_t>(nblk);
+    w.smask = c.take<uint16_t>(nblk);
     w.tneed = c.take<uint8_t>(ntile);
     w.cum = c.take<int64_t>((size_t)s.n_vtiles);
     w.act = c.take<int32_t>((size_t)s.n_vtiles);
@@ -1377,7 +1525,7 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
         CCE_TRY(launch_inv_perm(perm, V, w.inv_perm, st));
     }
     if (stats) {
-        hipLaunchKernelGGL(k_stats_init, dim3(1), dim3(64), 0, st, stats);  // all 6 entries
+        hipLaunchKernelGGL(k_stats_init, dim3(1), dim3(64), 0, st, stats);  // all 7 entries
         CCE_LAUNCHED();
     }
     const size_t nblk = (size_t)s.n_rb * s.cbp;
@@ -1459,6 +1607,8 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     a.cap_take = (flags & CCE_BWD_DEBUG_STORE_LIMIT) ? s.cap / 2 : s.cap;
     a.st = w.st;
     a.slot = w.slot;
+    a.smask = w.smask;
+    a.fine = (flags & CCE_BWD_FINE_FILTER) ? 1 : 0;
     a.stats = stats;
     a.dh_acc = w.dh_acc;
     a.dE = dE;
@@ -1472,10 +1622,14 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
         else
             hipLaunchKernelGGL((k_g_pass<T, false>), dim3(kPassGroups), dim3(TileF::kThreads), 0, st, a, p);
         CCE_LAUNCHED();
-        if (kahan)
-            hipLaunchKernelGGL((k_grad_pass<T, true>), dim3(2 * kPassGroups), dim3(TileG::kThreads), 0, st, a, p);
-        else
-            hipLaunchKernelGGL((k_grad_pass<T, false>), dim3(2 * kPassGroups), dim3(TileG::kThreads), 0, st, a, p);
+        const dim3 gg(2 * kPassGroups), gt(TileG::kThreads);
+        if (a.fine) {
+            if (kahan) hipLaunchKernelGGL((k_grad_pass<T, true, true>), gg, gt, 0, st, a, p);
+            else hipLaunchKernelGGL((k_grad_pass<T, false, true>), gg, gt, 0, st, a, p);
+        } else {
+            if (kahan) hipLaunchKernelGGL((k_grad_pass<T, true, false>), gg, gt, 0, st, a, p);
+            else hipLaunchKernelGGL((k_grad_pass<T, false, false>), gg, gt, 0, st, a, p);
+        }
         CCE_LAUNCHED();
     }
     if (stats) {

@@ -381,6 +381,34 @@ struct DmaEngine {
     }
 };
 
+// The MFMAs of a whole stage for the accumulator rows tm with bit tm of
+// rows set (wave-uniform); the other rows' operands are not read.
+template <typename T, class TL, class DE>
+__device__ __forceinline__ void compute_rows(const DE &eng, int buf, f32x16 (&acc)[TL::TM][TL::TN], int tid,
+                                             uint32_t rows) {
+    constexpr int kRowBytes = DE::kStageBytes;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int ra0 = (wave % TL::WM) * TL::kWaveM + (lane & 31);
+    const int rb0 = (wave / TL::WM) * TL::kWaveN + (lane & 31);
+    const u32x4 *A = eng.lds + buf * DE::kStage;
+    const u32x4 *B = A + DE::kStageA;
+#pragma unroll
+    for (int kk = 0; kk < DE::kCpr / 2; ++kk) {
+        const int c = 2 * kk + (lane >> 5);
+        u32x4 fa[TL::TM], fb[TL::TN];
+#pragma unroll
+        for (int tm = 0; tm < TL::TM; ++tm)
+            if ((rows >> tm) & 1) fa[tm] = A[dma_slot<kRowBytes>(ra0 + tm * 32, c)];
+#pragma unroll
+        for (int tn = 0; tn < TL::TN; ++tn) fb[tn] = B[dma_slot<kRowBytes>(rb0 + tn * 32, c)];
+#pragma unroll
+        for (int tm = 0; tm < TL::TM; ++tm)
+            if ((rows >> tm) & 1)
+#pragma unroll
+                for (int tn = 0; tn < TL::TN; ++tn) Mfma<T>::step(fa[tm], fb[tn], acc[tm][tn]);
+    }
+}
+
 template <class TL>
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[TL::TM][TL::TN]) {
 #pragma unroll

@@ -114,6 +114,7 @@ struct BwdWs {
     uint8_t *lab;      // [n_rb, cbp] 1 where a label falls in the block
     uint8_t *st;       // [n_rb, cbp] block status: 0 dropped, 1 softmax kept, 2 label only
     int32_t *slot;     // [n_rb, cbp] store slot of a kept block
+    uint16_t *smask;   // [n_rb, cbp] 32 x 32 sub-tiles of a kept block whose gradient may be nonzero
     uint8_t *tneed;    // [n_vtiles, n_rtiles] blocks the tile may keep (bits 0-2), recompute flag (bit 7)
     int64_t *cum;      // [n_vtiles] plan scratch: cumulative blocks
     int32_t *act;      // [n_vtiles] plan scratch: active tiles before each vocabulary tile

@@ -18,7 +18,13 @@ workload keeps the head shape and draws the values:
   E  ~ N(0, s_E^2) per element (s_E = 0.02, or 1/sqrt(D) for the tiny case)
   H  ~ N(0, 1) per element ("flat": an early-training softmax), or
   H  = 3 sqrt(D) e_y / ||e_y|| + N(0, I)  ("peaked": a trained-like softmax,
-       e_y the bf16-rounded classifier row of the token's label)
+       e_y the bf16-rounded classifier row of the token's label), or
+  H  = a sqrt(D) e_y / ||e_y|| + s N(0, I) with a = 0.35, s = 2 ("partially
+       peaked", workload 7): the label takes a median 80 % of the softmax
+       and about 0.02 % of the other entries reach 2^-12, the sparsity the
+       summary reports for trained models ("Surprising findings").  With unit
+       noise no scale a gets there: the other logits' spread is too narrow
+       for any of them to come within ln(2^12) of the lse.
   labels uniform over [0, V), or Zipf(1.1): P(id = r - 1) ~ r^-1.1, r = 1..V,
        or the same Zipf ranks sent through a seeded permutation of the ids
        (frequent tokens scattered over the vocabulary, as in a tokenizer
@@ -54,6 +60,8 @@ class Recipe:
     ignore_frac: float
     eps: float            # default filter threshold for this workload
     sort_vocab: tuple     # vocabulary-sort settings the workload is run with
+    peak_scale: float = 3.0  # a of a peaked H
+    h_noise: float = 1.0     # s of a peaked H
 
 
 # The five workloads, by number.  Sizes are the head shapes named above.
@@ -66,6 +74,10 @@ WORKLOADS = {
     # workload 5 with the Zipf ranks scattered over the ids: what the sort is for
     6: Recipe("large-vocab-1024x24-scattered", 24576, 2048, 248320, "bf16", 0.02, "peaked", "zipf-scattered", 0.0,
               2.0 ** -12, (False, True)),
+    # the Gemma-2-2B head with a partially peaked softmax (filtering at a
+    # granularity finer than the 128 x 128 block is what pays there)
+    7: Recipe("gemma2-2b-head-partial", 8192, 2304, 256000, "bf16", 0.02, "peaked", "zipf", 0.0, 2.0 ** -12, (False,),
+              peak_scale=0.35, h_noise=2.0),
 }
 
 
@@ -131,7 +143,7 @@ def zipf_labels(rng, n, V, s=1.1):
 
 
 def make_inputs(N, D, V, dtype="bf16", e_std=0.02, h_kind="normal", label_kind="uniform",
-                ignore_frac=0.0, seed=0, eps=0.0, name="custom", peak_scale=3.0) -> Inputs:
+                ignore_frac=0.0, seed=0, eps=0.0, name="custom", peak_scale=3.0, h_noise=1.0) -> Inputs:
     if dtype not in ("f32", "bf16"):
         raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
     std = (1.0 / math.sqrt(D)) if e_std is None else float(e_std)
@@ -162,6 +174,8 @@ def make_inputs(N, D, V, dtype="bf16", e_std=0.02, h_kind="normal", label_kind="
             ey = (Ef[rows] if Ef is not None else bf16_bits_as_f32(E[rows])).astype(np.float64)
             ey *= (peak_scale * math.sqrt(D)) / np.linalg.norm(ey, axis=1, keepdims=True)
             noise = hrng.standard_normal(size=(r1 - r0, D), dtype=np.float32)
+            if h_noise != 1.0:
+                noise *= np.float32(h_noise)
             x = (ey + noise).astype(np.float32)
             H[r0:r1] = x if dtype == "f32" else round_to_bf16_bits(x)
     else:
@@ -177,9 +191,10 @@ def make_inputs(N, D, V, dtype="bf16", e_std=0.02, h_kind="normal", label_kind="
 
 def make_workload(k: int, seed: int | None = None, N: int | None = None, D: int | None = None,
                   V: int | None = None) -> Inputs:
-    """Workload k (1..6) at its full size, or with any of N, D, V overridden
+    """Workload k (1..7) at its full size, or with any of N, D, V overridden
     (the same recipe at a size the oracle finishes quickly)."""
     r = WORKLOADS[k]
     return make_inputs(N or r.N, D or r.D, V or r.V, dtype=r.dtype, e_std=r.e_std, h_kind=r.h_kind,
                        label_kind=r.label_kind, ignore_frac=r.ignore_frac,
-                       seed=k if seed is None else seed, eps=r.eps, name=r.name)
+                       seed=k if seed is None else seed, eps=r.eps, name=r.name, peak_scale=r.peak_scale,
+                       h_noise=r.h_noise)

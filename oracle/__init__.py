@@ -195,7 +195,7 @@ def lse_matmul(H64, E64, labels, ignore_index=-100, row_chunk=512):
 
 
 def backward_filtered(H64, E64, labels, dloss, eps, block_rows=128, block_vocab=128, ignore_index=-100,
-                      margin=2.0 ** -10):
+                      margin=2.0 ** -14):
     """Gradient with the block filter of the CCE paper summary "Cut Your
     Losses in Large-Vocabulary Language Models", section "Approach": the
     backward skips the blocks of the logit matrix whose softmax entries all
@@ -214,8 +214,10 @@ def backward_filtered(H64, E64, labels, dloss, eps, block_rows=128, block_vocab=
 
     Several results are correct when a block's largest non-label p lies
     within a relative `margin` of eps (a float32 kernel may decide it either
-    way); for those blocks the sum of the Frobenius norms of their softmax
-    part's contributions to dH and to dE is returned as an allowance.
+    way: its p carries a relative error of about 1e-5 from float32 logits and
+    lse, against the default margin of 2^-14 = 6e-5); for those blocks the sum
+    of the Frobenius norms of their softmax part's contributions to dH and to
+    dE is returned as an allowance.
     Returns dH [N, D], dE [V, D], kept [row blocks, vocab blocks] (bool),
     allow_dH, allow_dE (floats).  Ignored rows get dH = 0, add nothing."""
     H64, E64 = _c64(H64), _c64(E64)

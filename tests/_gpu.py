@@ -92,7 +92,7 @@ def run_gpu(x: inputs.Inputs, dloss: np.ndarray, eps: float, sort=False, flags=0
     dl = torch.from_numpy(dloss).to(DEV)
     dH = torch.full_like(H, float("nan")) if prefill_nan else None
     dE = torch.full_like(E, float("nan")) if prefill_nan else None
-    stats = torch.zeros(6, dtype=torch.int64, device=DEV)
+    stats = torch.zeros(7, dtype=torch.int64, device=DEV)
     dH, dE = B.cce_backward(H, E, y, lse, dl, eps, x.ignore_index, perm, flags, dH=dH, dE=dE, stats=stats,
                             block_max=tb)
     torch.cuda.synchronize()
@@ -184,10 +184,20 @@ def assert_dE_split(name, got, ref, L, tol):
     return e
 
 
-def assert_grad_filtered(name, got, ref_f, allow, L, tol=1e-2):
+def assert_grad_filtered(name, got, ref_f, allow, L, tol=1e-2, split=False):
     """Check against the oracle's filtered gradient ref_f: ||got - ref_f|| <=
     tol ||ref_f|| + allow.  The label-term-only output and an all-zero output
-    must both score above the bound."""
+    must both score above the bound.  split=True (dE): the rows no label
+    falls in (L = 0: the softmax part alone) and the label rows are checked
+    apart, the guards applying to the label-free rows."""
+    if split:
+        free = ~np.any(L != 0, axis=1)
+        assert free.any() and (~free).any(), f"{name}: need rows with and without labels"
+        assert_grad_filtered(name + " (label-free rows)", got[free], ref_f[free], allow, L[free], tol)
+        nl = np.linalg.norm(ref_f[~free])
+        d = np.linalg.norm(got[~free] - ref_f[~free])
+        assert d <= tol * nl + allow, f"{name} (label rows): {d:.3e} > {tol:g} * {nl:.3e} + {allow:.3e}"
+        return d / nl
     assert np.all(np.isfinite(got)), f"{name}: non-finite (unwritten?) output"
     nref = np.linalg.norm(ref_f)
     bound = tol * nref + allow

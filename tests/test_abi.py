@@ -54,18 +54,19 @@ def test_workspace_has_no_per_logit_term(dt):
     g = B.forward_workspace_bytes
     assert g(16384, D, 512000, dt) < 2.2 * g(8192, D, 256000, dt)
     # per vocabulary entry at fixed N: inverse permutation (4 bytes), the
-    # block and tile maps (N / 16384 blocks x 6 bytes, N / 65536 tiles x 5
-    # bytes) and the plan's per-tile scratch; nothing per logit
+    # block maps (N / 16384 blocks x 8 bytes: label flag, status, store slot,
+    # sub-tile mask), the tile maps (N / 65536 tiles x 5 bytes) and the plan's
+    # per-tile scratch; nothing per logit
     N = 8192
     per_v = (f(N, D, 512000, dt) - f(N, D, 256000, dt)) / 256000
-    assert per_v <= 4 + 6 * N / 16384 + 5 * N / 65536 + 1
+    assert per_v <= 4 + 8 * N / 16384 + 5 * N / 65536 + 1
     # per row at fixed V: the fp32 dH accumulator, H^T and the block store
     # (as many blocks as a dense slice of 8192 vocabulary columns, two
     # layouts), the row index, label logit and mapped label (4 + 4 + 8 bytes)
     elem = 4 if dt == B.CCE_F32 else 2
     V = 256000
     per_n = (f(2 * N, D, V, dt) - f(N, D, V, dt)) / N
-    assert per_n <= 4 * D + elem * D + 2 * elem * 8192 + 6 * V / 16384 + 5 * V / 65536 + 16 + 16
+    assert per_n <= 4 * D + elem * D + 2 * elem * 8192 + 8 * V / 16384 + 5 * V / 65536 + 16 + 16
 
 
 def test_workspace_invalid_sizes_return_zero():
@@ -142,7 +143,8 @@ def test_backward_specific_errors():
     assert _bwd(eps=-1.0) == B.CCE_ERR_ARG
     assert _bwd(eps=float("nan")) == B.CCE_ERR_ARG
     assert _bwd(eps=float("inf")) == B.CCE_ERR_ARG
-    assert _bwd(flags=8) == B.CCE_ERR_ARG  # no such flag
+    assert _bwd(flags=16) == B.CCE_ERR_ARG  # no such flag
+    assert _bwd(flags=B.CCE_BWD_FINE_FILTER | B.CCE_BWD_FULL_DE) == B.CCE_ERR_ARG  # not combined
     assert _bwd(dE=FAKE + 8) == B.CCE_ERR_ALIGN
     assert _bwd(perm=FAKE + 2) == B.CCE_ERR_ALIGN
     assert _bwd(stats=FAKE + 4) == B.CCE_ERR_ALIGN

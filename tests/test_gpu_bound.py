@@ -118,7 +118,7 @@ def test_sorted_forward_matches_oracle():
 def _device_run(x, tb, eps, dl, perm=None):
     H, E, y = G.to_device(x)
     _, lse = B.cce_forward(H, E, y, x.ignore_index, block_max=tb, perm=perm)
-    stats = torch.zeros(6, dtype=torch.int64, device=G.DEV)
+    stats = torch.zeros(7, dtype=torch.int64, device=G.DEV)
     dH, dE = B.cce_backward(H, E, y, lse, dl, eps, x.ignore_index, perm, 0, stats=stats, block_max=tb)
     torch.cuda.synchronize()
     return dH, dE, stats.cpu().numpy()

@@ -46,7 +46,7 @@ def _run(x, y, V0, off1, dl, eps, sort=False, bound=True, flags=0):
     perm = B.cce_vocab_order_composite(H, E0, E1, yt, x.ignore_index) if sort else None
     tb = torch.empty(B.block_max_elems(x.N, V), dtype=torch.float32, device=G.DEV) if bound else None
     loss, lse = B.cce_forward_composite(H, E0, E1, off1, yt, x.ignore_index, block_max=tb, perm=perm)
-    stats = torch.zeros(6, dtype=torch.int64, device=G.DEV)
+    stats = torch.zeros(7, dtype=torch.int64, device=G.DEV)
     dH = torch.full_like(H, float("nan"))
     dE0 = torch.full_like(E0, float("nan"))
     dE1 = torch.full_like(E1, float("nan"))

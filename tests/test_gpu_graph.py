@@ -24,7 +24,7 @@ def test_graph_replays_match_eager(k, N, D, V, sort):
     lse = torch.empty_like(loss)
     dH = torch.empty_like(H)
     dE = torch.empty_like(E)
-    stats = torch.zeros(6, dtype=torch.int64, device=G.DEV)
+    stats = torch.zeros(7, dtype=torch.int64, device=G.DEV)
     tb = torch.empty(B.block_max_elems(x.N, x.V), dtype=torch.float32, device=G.DEV)
     perm = torch.empty(x.V, dtype=torch.int32, device=G.DEV) if sort else None
     ws_f = torch.empty(B.forward_workspace_bytes(x.N, x.D, x.V, dt), dtype=torch.uint8, device=G.DEV)

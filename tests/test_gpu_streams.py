@@ -30,7 +30,7 @@ def _enqueue(x, dl_np, eps, sort, stream):
         dl = torch.from_numpy(dl_np).to(G.DEV)
         dH = torch.full_like(H, float("nan"))
         dE = torch.full_like(E, float("nan"))
-        stats = torch.zeros(6, dtype=torch.int64, device=G.DEV)
+        stats = torch.zeros(7, dtype=torch.int64, device=G.DEV)
         B.cce_backward(H, E, y, lse, dl, eps, x.ignore_index, perm, 0, dH=dH, dE=dE, stats=stats,
                        block_max=tb, stream=stream)
     return dict(loss=loss, lse=lse, dH=dH, dE=dE, stats=stats, block_max=tb)

@@ -82,3 +82,24 @@ def test_scattered_zipf_is_a_relabelled_zipf():
     ids = {}
     for ra, rb in zip(a.labels, b.labels):
         assert ids.setdefault(int(ra), int(rb)) == int(rb)
+
+
+def test_partially_peaked_recipe_regime():
+    # workload 7: about 0.02 % of the non-label softmax entries at or above
+    # 2^-12 and the label a large but not overwhelming share.  The first 32
+    # rows of the full workload (same seeds), logits in float32 from the
+    # exact bf16 values (a regime check, not parity).
+    import numpy as np
+    x = inputs.make_workload(7, N=32)
+    H = inputs.bf16_bits_as_f32(x.H)
+    E = inputs.bf16_bits_as_f32(x.E)
+    z = (H @ E.T).astype(np.float64)
+    m = z.max(axis=1, keepdims=True)
+    lse = m + np.log(np.exp(z - m).sum(axis=1, keepdims=True))
+    p = np.exp(z - lse)
+    rows = np.arange(x.N)
+    py = p[rows, x.labels].copy()
+    p[rows, x.labels] = 0.0
+    frac = (p >= 2.0 ** -12).sum() / (x.N * (x.V - 1))
+    assert 1e-4 <= frac <= 4e-4, frac
+    assert 0.05 <= np.median(1.0 - py) <= 0.5, np.median(1.0 - py)

@@ -124,11 +124,11 @@ def test_allowance_counts_near_threshold_blocks():
     dl = np.ones(5)
     ex = [math.exp(v) for v in DESIGN_H[3]]
     p1 = ex[1] / sum(ex)
-    _, _, _, aH, aE = oracle.backward_filtered(DESIGN_H, np.eye(6), DESIGN_Y, dl, p1 * (1 + 2.0 ** -12),
+    _, _, _, aH, aE = oracle.backward_filtered(DESIGN_H, np.eye(6), DESIGN_Y, dl, p1 * (1 + 2.0 ** -16),
                                                block_rows=2, block_vocab=3)
     assert aH > 0 and aE > 0
-    _, _, _, aH, aE = oracle.backward_filtered(DESIGN_H, np.eye(6), DESIGN_Y, dl, p1 * 1.1, block_rows=2,
-                                               block_vocab=3)
+    _, _, _, aH, aE = oracle.backward_filtered(DESIGN_H, np.eye(6), DESIGN_Y, dl, p1 * (1 + 2.0 ** -12),
+                                               block_rows=2, block_vocab=3)
     assert aH == 0 and aE == 0
 
 
