@@ -1,9 +1,14 @@
 """Builds libcce.so (gfx950 HIP kernels + the C ABI) in-tree with hipcc.
 
-    python -m linear_cross_entropy_cce_amd.build [--debug]
+    python -m linear_cross_entropy_cce_amd.build [--debug] [--host-check]
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
 selection turned off (-Xclang -target-feature -Xclang -packed-fp32-ops).
+
+--host-check also builds _build/host_check/abi_check: the C ABI's host code
+(api.cpp) and the argument-check driver tests/abi_check.cpp compiled with
+AddressSanitizer and UndefinedBehaviorSanitizer on the host side only
+(device code is built as usual), linked with the kernels' objects.
 """
 from __future__ import annotations
 
@@ -69,9 +74,36 @@ def build(debug: bool = False, verbose: bool = False) -> str:
     return LIB_PATH
 
 
+SAN = ["-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all"]
+
+
+def build_host_check(verbose: bool = False) -> str:
+    """The sanitized host-check program (see the module docstring); needs the
+    kernels' objects of a normal build (made here if absent)."""
+    cc = hipcc()
+    objs = [os.path.join(BUILD_DIR, src + ".o") for src in HIP_SOURCES]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose=verbose)
+    out_dir = os.path.join(BUILD_DIR, "host_check")
+    os.makedirs(out_dir, exist_ok=True)
+    host_san = [x for f in SAN for x in ("-Xarch_host", f)]  # host side only
+    common = ["-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC, "-Wall",
+              "-Wno-unused-function", "-O1", "-g", "-fno-omit-frame-pointer", *host_san]
+    api_o = os.path.join(out_dir, "api.o")
+    drv_o = os.path.join(out_dir, "abi_check.o")
+    _compile([cc, *common, "-c", os.path.join(CSRC, "api.cpp"), "-o", api_o])
+    _compile([cc, *common, "-c", os.path.join(ROOT, "tests", "abi_check.cpp"), "-o", drv_o])
+    exe = os.path.join(out_dir, "abi_check")
+    subprocess.run([cc, f"--offload-arch={ARCH}", *host_san, drv_o, api_o, *objs, "-o", exe], check=True)
+    return exe
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--debug", action="store_true")
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--host-check", action="store_true")
     a = ap.parse_args()
     print(build(debug=a.debug, verbose=a.verbose))
+    if a.host_check:
+        print(build_host_check(verbose=a.verbose))

@@ -3,6 +3,7 @@
 // launchers.  No allocation, no host synchronisation, no global state.
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "cce.h"
 #include "cce_internal.hpp"
@@ -29,8 +30,19 @@ bool shape_ok(int64_t N, int64_t D, int64_t V) {
     return true;
 }
 
-bool dtype_ok(cce_dtype dt) { return dt == CCE_F32 || dt == CCE_BF16; }
-size_t elem_size(cce_dtype dt) { return dt == CCE_BF16 ? 2 : 4; }
+// An enum argument as the int its caller passed.  A C caller may pass any int
+// (the value is then rejected); in C++ reading such a value as the enum type
+// is undefined, so its bytes are read as an int before anything else.
+template <typename Enum>
+int enum_int(const Enum &e) {
+    static_assert(sizeof(Enum) == sizeof(int), "enums of the C ABI are int-sized");
+    int v;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
+
+bool dtype_ok(int dt) { return dt == CCE_F32 || dt == CCE_BF16; }
+size_t elem_size(int dt) { return dt == CCE_BF16 ? 2 : 4; }
 
 cce_status hip_status(hipError_t e) { return e == hipSuccess ? CCE_OK : CCE_ERR_HIP; }
 
@@ -57,7 +69,7 @@ hipError_t map_labels(const int64_t *labels, int64_t N, int64_t ignore_index, co
 
 // The forward's argument checks other than the workspace's.
 cce_status forward_check(const void *H, const VocabRows &E, const int64_t *labels, int64_t N, int64_t D, int64_t V,
-                         cce_dtype dtype, const int32_t *perm, float *loss, float *lse, float *block_max) {
+                         int dtype, const int32_t *perm, float *loss, float *lse, float *block_max) {
     if (!H || !E.e0 || !E.e1 || !labels || !loss || !lse) return CCE_ERR_NULL;
     if (!dtype_ok(dtype)) return CCE_ERR_DTYPE;
     if (!shape_ok(N, D, V)) return CCE_ERR_SHAPE;
@@ -68,7 +80,7 @@ cce_status forward_check(const void *H, const VocabRows &E, const int64_t *label
 }
 
 cce_status forward_impl(const void *H, const VocabRows &E, int64_t off1, const int64_t *labels, int64_t N, int64_t D,
-                        int64_t V, cce_dtype dtype, int64_t ignore_index, const int32_t *perm, float *loss,
+                        int64_t V, int dtype, int64_t ignore_index, const int32_t *perm, float *loss,
                         float *lse, float *block_max, void *ws, size_t ws_bytes, void *stream) {
     const cce_status c = forward_check(H, E, labels, N, D, V, dtype, perm, loss, lse, block_max);
     if (c != CCE_OK) return c;
@@ -82,11 +94,12 @@ cce_status forward_impl(const void *H, const VocabRows &E, int64_t off1, const i
     const int64_t *y = nullptr;
     hipError_t e = map_labels(labels, N, ignore_index, E, off1, V, static_cast<char *>(ws) + align256(need), &y, st);
     if (e != hipSuccess) return CCE_ERR_HIP;
-    return hip_status(launch_forward(dtype, H, E, y, s, ignore_index, perm, w, loss, lse, block_max, st));
+    return hip_status(launch_forward(static_cast<cce_dtype>(dtype), H, E, y, s, ignore_index, perm, w, loss, lse,
+                                     block_max, st));
 }
 
 cce_status vocab_order_impl(const void *H, const VocabRows &E, const int64_t *labels, int64_t N, int64_t D, int64_t V,
-                            cce_dtype dtype, int64_t ignore_index, int32_t *perm, float *keys, void *ws,
+                            int dtype, int64_t ignore_index, int32_t *perm, float *keys, void *ws,
                             size_t ws_bytes, void *stream) {
     if (!H || !E.e0 || !E.e1 || !labels || !perm || !ws) return CCE_ERR_NULL;
     if (!dtype_ok(dtype)) return CCE_ERR_DTYPE;
@@ -98,12 +111,12 @@ cce_status vocab_order_impl(const void *H, const VocabRows &E, const int64_t *la
     const SortWs w = sort_ws(ws, N, D, V, &need);
     if (ws_bytes < align256(need) + label_bytes(N)) return CCE_ERR_WORKSPACE;
     // (only ignore_index matters to the sort: no label mapping needed)
-    return hip_status(launch_vocab_order(dtype, H, E, labels, N, D, V, ignore_index, perm, keys, w,
-                                         static_cast<hipStream_t>(stream)));
+    return hip_status(launch_vocab_order(static_cast<cce_dtype>(dtype), H, E, labels, N, D, V, ignore_index, perm,
+                                         keys, w, static_cast<hipStream_t>(stream)));
 }
 
 cce_status backward_impl(const void *H, const VocabRows &E, int64_t off1, const int64_t *labels, const float *lse,
-                         const float *dloss, const float *block_max, int64_t N, int64_t D, int64_t V, cce_dtype dtype,
+                         const float *dloss, const float *block_max, int64_t N, int64_t D, int64_t V, int dtype,
                          int64_t ignore_index, float filter_eps, const int32_t *perm, unsigned flags, void *dH,
                          const VocabGrads &dE, int64_t *stats, void *ws, size_t ws_bytes, void *stream) {
     if (!H || !E.e0 || !E.e1 || !labels || !lse || !dloss || !dH || !dE.d0 || !dE.d1 || !ws) return CCE_ERR_NULL;
@@ -125,19 +138,20 @@ cce_status backward_impl(const void *H, const VocabRows &E, int64_t off1, const 
     const int64_t *y = nullptr;
     hipError_t e = map_labels(labels, N, ignore_index, E, off1, V, static_cast<char *>(ws) + align256(need), &y, st);
     if (e != hipSuccess) return CCE_ERR_HIP;
-    return hip_status(launch_backward(dtype, H, E, y, lse, dloss, block_max, s, ignore_index, filter_eps, perm,
-                                      flags, dH, dE, stats, w, st));
+    return hip_status(launch_backward(static_cast<cce_dtype>(dtype), H, E, y, lse, dloss, block_max, s, ignore_index,
+                                      filter_eps, perm, flags, dH, dE, stats, w, st));
 }
 
 }  // namespace
 
 extern "C" {
 
-const char *cce_status_string(cce_status s) {
-    switch (s) {
+const char *cce_status_string(cce_status status) {
+    switch (enum_int(status)) {
         case CCE_OK: return "ok";
         case CCE_ERR_NULL: return "a required pointer is NULL";
-        case CCE_ERR_SHAPE: return "N, D or V outside the supported range (D % 8 == 0, 8 <= D <= 65536, 1 <= N, V <= 2^31 - 2^16)";
+        case CCE_ERR_SHAPE:
+            return "N, D or V outside the supported range (D % 8 == 0, 8 <= D <= 65536, 1 <= N, V <= 2^31 - 2^16)";
         case CCE_ERR_DTYPE: return "unknown dtype";
         case CCE_ERR_ALIGN: return "a pointer is not aligned (16 bytes for H, E, dH, dE, workspace)";
         case CCE_ERR_WORKSPACE: return "workspace too small";
@@ -155,16 +169,16 @@ void cce_filter_block(int *block_rows, int *block_vocab) {
 }
 
 size_t cce_forward_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtype dtype) {
-    if (!shape_ok(N, D, V) || !dtype_ok(dtype)) return 0;
+    if (!shape_ok(N, D, V) || !dtype_ok(enum_int(dtype))) return 0;
     size_t b = 0;
     fwd_ws(nullptr, fwd_shape(N, D, V), &b);
     return align256(b) + label_bytes(N);
 }
 
 size_t cce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtype dtype) {
-    if (!shape_ok(N, D, V) || !dtype_ok(dtype)) return 0;
+    if (!shape_ok(N, D, V) || !dtype_ok(enum_int(dtype))) return 0;
     size_t b = 0;
-    bwd_ws(nullptr, bwd_shape(N, D, V), elem_size(dtype), &b);
+    bwd_ws(nullptr, bwd_shape(N, D, V), elem_size(enum_int(dtype)), &b);
     return align256(b) + label_bytes(N);
 }
 
@@ -174,7 +188,7 @@ size_t cce_block_max_elems(int64_t N, int64_t V) {
 }
 
 size_t cce_vocab_order_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtype dtype) {
-    if (!shape_ok(N, D, V) || !dtype_ok(dtype)) return 0;
+    if (!shape_ok(N, D, V) || !dtype_ok(enum_int(dtype))) return 0;
     size_t b = 0;
     sort_ws(nullptr, N, D, V, &b);
     return align256(b) + label_bytes(N);
@@ -183,8 +197,8 @@ size_t cce_vocab_order_workspace_bytes(int64_t N, int64_t D, int64_t V, cce_dtyp
 cce_status cce_forward(const void *H, const void *E, const int64_t *labels, int64_t N, int64_t D, int64_t V,
                        cce_dtype dtype, int64_t ignore_index, const int32_t *perm, float *loss, float *lse,
                        float *block_max, void *ws, size_t ws_bytes, void *stream) {
-    return forward_impl(H, VocabRows{E, E, kOneBlock}, 0, labels, N, D, V, dtype, ignore_index, perm, loss, lse,
-                        block_max, ws, ws_bytes, stream);
+    return forward_impl(H, VocabRows{E, E, kOneBlock}, 0, labels, N, D, V, enum_int(dtype), ignore_index, perm, loss,
+                        lse, block_max, ws, ws_bytes, stream);
 }
 
 static_assert(kNoAllocScratchBytes == CCE_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
@@ -193,12 +207,14 @@ cce_status cce_forward_noalloc(const void *H, const void *E, const int64_t *labe
                                cce_dtype dtype, int64_t ignore_index, const int32_t *perm, float *loss, float *lse,
                                float *block_max, void *stream) {
     const VocabRows rows{E, E, kOneBlock};
-    const cce_status c = forward_check(H, rows, labels, N, D, V, dtype, perm, loss, lse, block_max);
+    const int dt = enum_int(dtype);
+    const cce_status c = forward_check(H, rows, labels, N, D, V, dt, perm, loss, lse, block_max);
     if (c != CCE_OK) return c;
-    if (cce_forward_workspace_bytes(N, D, V, dtype) > kNoAllocScratchBytes) return CCE_ERR_WORKSPACE;
+    if (cce_forward_workspace_bytes(N, D, V, static_cast<cce_dtype>(dt)) > kNoAllocScratchBytes)
+        return CCE_ERR_WORKSPACE;
     void *ws = nullptr;
     if (noalloc_scratch(&ws) != hipSuccess) return CCE_ERR_HIP;
-    return forward_impl(H, rows, 0, labels, N, D, V, dtype, ignore_index, perm, loss, lse, block_max, ws,
+    return forward_impl(H, rows, 0, labels, N, D, V, dt, ignore_index, perm, loss, lse, block_max, ws,
                         kNoAllocScratchBytes, stream);
 }
 
@@ -207,15 +223,15 @@ cce_status cce_forward_composite(const void *H, const void *E0, int64_t V0, cons
                                  const int32_t *perm, float *loss, float *lse, float *block_max, void *ws,
                                  size_t ws_bytes, void *stream) {
     if (!blocks_ok(V0, V1, off1)) return CCE_ERR_SHAPE;
-    return forward_impl(H, VocabRows{E0, E1, V0}, off1, labels, N, D, V0 + V1, dtype, ignore_index, perm, loss, lse,
-                        block_max, ws, ws_bytes, stream);
+    return forward_impl(H, VocabRows{E0, E1, V0}, off1, labels, N, D, V0 + V1, enum_int(dtype), ignore_index, perm,
+                        loss, lse, block_max, ws, ws_bytes, stream);
 }
 
 cce_status cce_vocab_order(const void *H, const void *E, const int64_t *labels, int64_t N, int64_t D, int64_t V,
                            cce_dtype dtype, int64_t ignore_index, int32_t *perm, float *keys, void *ws,
                            size_t ws_bytes, void *stream) {
-    return vocab_order_impl(H, VocabRows{E, E, kOneBlock}, labels, N, D, V, dtype, ignore_index, perm, keys, ws,
-                            ws_bytes, stream);
+    return vocab_order_impl(H, VocabRows{E, E, kOneBlock}, labels, N, D, V, enum_int(dtype), ignore_index, perm,
+                            keys, ws, ws_bytes, stream);
 }
 
 cce_status cce_vocab_order_composite(const void *H, const void *E0, int64_t V0, const void *E1, int64_t V1,
@@ -223,15 +239,15 @@ cce_status cce_vocab_order_composite(const void *H, const void *E0, int64_t V0, 
                                      int64_t ignore_index, int32_t *perm, float *keys, void *ws, size_t ws_bytes,
                                      void *stream) {
     if (!blocks_ok(V0, V1, V0)) return CCE_ERR_SHAPE;
-    return vocab_order_impl(H, VocabRows{E0, E1, V0}, labels, N, D, V0 + V1, dtype, ignore_index, perm, keys, ws,
-                            ws_bytes, stream);
+    return vocab_order_impl(H, VocabRows{E0, E1, V0}, labels, N, D, V0 + V1, enum_int(dtype), ignore_index, perm,
+                            keys, ws, ws_bytes, stream);
 }
 
 cce_status cce_backward(const void *H, const void *E, const int64_t *labels, const float *lse, const float *dloss,
                         const float *block_max, int64_t N, int64_t D, int64_t V, cce_dtype dtype,
                         int64_t ignore_index, float filter_eps, const int32_t *perm, unsigned flags, void *dH,
                         void *dE, int64_t *stats, void *ws, size_t ws_bytes, void *stream) {
-    return backward_impl(H, VocabRows{E, E, kOneBlock}, 0, labels, lse, dloss, block_max, N, D, V, dtype,
+    return backward_impl(H, VocabRows{E, E, kOneBlock}, 0, labels, lse, dloss, block_max, N, D, V, enum_int(dtype),
                          ignore_index, filter_eps, perm, flags, dH, VocabGrads{dE, dE, kOneBlock}, stats, ws,
                          ws_bytes, stream);
 }
@@ -243,9 +259,9 @@ cce_status cce_backward_composite(const void *H, const void *E0, int64_t V0, con
                                   void *dH, void *dE0, void *dE1, int64_t *stats, void *ws, size_t ws_bytes,
                                   void *stream) {
     if (!blocks_ok(V0, V1, off1)) return CCE_ERR_SHAPE;
-    return backward_impl(H, VocabRows{E0, E1, V0}, off1, labels, lse, dloss, block_max, N, D, V0 + V1, dtype,
-                         ignore_index, filter_eps, perm, flags, dH, VocabGrads{dE0, dE1, V0}, stats, ws, ws_bytes,
-                         stream);
+    return backward_impl(H, VocabRows{E0, E1, V0}, off1, labels, lse, dloss, block_max, N, D, V0 + V1,
+                         enum_int(dtype), ignore_index, filter_eps, perm, flags, dH, VocabGrads{dE0, dE1, V0}, stats,
+                         ws, ws_bytes, stream);
 }
 
 cce_status cce_check_labels(const int64_t *labels, int64_t N, int64_t V, int64_t ignore_index, int64_t *n_bad,
