@@ -15,7 +15,8 @@ Tolerances (floating point):
               kernel's block geometry (oracle.backward_filtered):
                 ||gpu - ref_f||_F <= gtol ||ref_f||_F + allow, gtol = 1e-2,
               allow = the contributions of blocks whose largest non-label p is
-              within 2^-10 of eps (a float32 decision may go either way);
+              within a relative 2^-14 of eps (a float32 decision may go either
+              way: float32 logits and lse give p a relative error near 1e-5);
               a degenerate softmax (every non-label p below fp32 resolution of
               1 - p_y, so the true gradient is below the rounding of the label
               term) uses the label-term floor instead:
