@@ -116,6 +116,7 @@ struct BwdArgs {
     uint8_t *st;
     int32_t *slot;
     uint16_t *smask;  // bit 4 i + j: sub-tile (vocabulary rows 32 i.., tokens 32 j..) of a kept block may be nonzero
+    const int32_t *cpre, *slist, *dlist;  // column lists of k_plan
     int64_t *stats;
     float *dh_acc;
     Rows2<T> dE;  // same layout as E
@@ -312,11 +313,14 @@ __global__ __launch_bounds__(256) void k_label_map(const int64_t *__restrict__ l
 // softmax part (bits 3-6, block q = 2 (vocabulary half) + token half) and
 // whether any does (bit 7).  A block may keep its softmax part unless the
 // bound rules it out, and may keep its label entries if it holds a label;
-// only the blocks that may keep a softmax part are recomputed.
+// only the blocks that may keep a softmax part are recomputed.  Per
+// vocabulary block (column, zeroed before): csoft = 1 if one of its blocks
+// may keep a softmax part, cnlab = its blocks that hold a label.
 __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ nvalid_p, int64_t V, int n_rt,
                                                     int n_vt, int cbp, const uint8_t *__restrict__ lab,
                                                     const float *__restrict__ bmax, const float *__restrict__ lmin,
-                                                    float thr, uint8_t *__restrict__ tneed) {
+                                                    float thr, uint8_t *__restrict__ tneed,
+                                                    uint8_t *__restrict__ csoft, int32_t *__restrict__ cnlab) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)n_rt * n_vt) return;
     const int vt = (int)(i / n_rt), rt = (int)(i % n_rt);
@@ -331,8 +335,11 @@ __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ 
         const int rb = 2 * rt + (q & 1), cb = 2 * vt + (q >> 1);
         if ((int64_t)rb * kBlockRows >= nv || (int64_t)cb * kBlockVocab >= V) continue;
         const bool soft = !block_below(bmax, cbp, lmin, thr, rb, cb);
+        const bool has_label = lab[(int64_t)rb * cbp + cb] != 0;
         mask |= soft ? 1 << q : 0;
-        need += (soft || lab[(int64_t)rb * cbp + cb]) ? 1 : 0;
+        need += (soft || has_label) ? 1 : 0;
+        if (soft) csoft[cb] = 1;  // (every writer stores 1)
+        if (has_label) atomicAdd(&cnlab[cb], 1);
     }
     tneed[i] = (uint8_t)(need | (mask << 3) | (mask ? 0x80 : 0));
 }
@@ -343,14 +350,24 @@ __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ 
 // Passes: one if every block fits the store, else pass(vt) =
 // floor(cum(vt) / cap_eff) with cum the inclusive block count; a vocabulary
 // tile adds at most cap - cap_eff blocks, so no pass exceeds cap.
+// Columns (vocabulary blocks cb < CB): with static_ok, a column none of
+// whose blocks may keep a softmax part and with at most kLabelPathBlocks
+// label blocks is static: its kept blocks can only be label-only, so its dE
+// rows come from the label entries (or are zero) for all features at once.
+// slist holds the static columns in order, dlist the others, and cpre[cb]
+// the static columns before cb (cpre[CB] all of them).
 __global__ __launch_bounds__(1024) void k_plan(const uint8_t *__restrict__ tneed, int n_rt, int n_vt, int64_t cap,
                                                int64_t cap_eff, int max_passes, int32_t *__restrict__ plan,
                                                int64_t *__restrict__ cum, int32_t *__restrict__ act,
-                                               int32_t *__restrict__ tlist) {
+                                               int32_t *__restrict__ tlist, int CB, int static_ok,
+                                               const uint8_t *__restrict__ csoft, const int32_t *__restrict__ cnlab,
+                                               int32_t *__restrict__ cpre, int32_t *__restrict__ slist,
+                                               int32_t *__restrict__ dlist) {
     __shared__ int64_t wsum[16];
     __shared__ int32_t wact[16];
+    __shared__ int32_t wcol[16];
     __shared__ int64_t carry_n;
-    __shared__ int32_t carry_a;
+    __shared__ int32_t carry_a, carry_c;
     const PlanView pv = plan_view(plan, max_passes);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     if (t == 0) { carry_n = 0; carry_a = 0; }
@@ -418,6 +435,33 @@ __global__ __launch_bounds__(1024) void k_plan(const uint8_t *__restrict__ tneed
     }
     for (int q = t; q < max_passes; q += 1024) pv.counter[q] = 0;
     for (int q = t; q < kQueues * max_passes; q += 1024) plan_queues(plan, max_passes, 0)[q] = 0;
+
+    if (t == 0) carry_c = 0;
+    __syncthreads();
+    for (int base = 0; base < CB; base += 1024) {
+        const int cb = base + t;
+        const int is_s = (cb < CB && static_ok && !csoft[cb] && cnlab[cb] <= kLabelPathBlocks) ? 1 : 0;
+        int x = is_s;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) wcol[w] = x;
+        __syncthreads();
+        int off = carry_c;
+        for (int k = 0; k < w; ++k) off += wcol[k];
+        const int excl = off + x - is_s;
+        if (cb < CB) {
+            cpre[cb] = excl;
+            if (is_s) slist[excl] = cb;
+            else dlist[cb - excl] = cb;
+        }
+        __syncthreads();
+        if (t == 1023) carry_c = off + x;
+        __syncthreads();
+    }
+    if (t == 0) cpre[CB] = carry_c;
 }
 
 // ------------------------------------------------------- recompute + G
@@ -938,16 +982,15 @@ struct LabelCols {
     int nv;
 };
 
-// dE rows of vocabulary block cb, features [d0, d0 + 256), when every kept
-// block of cb is label-only: dE_v = sum of g_i h_i over the valid tokens i
-// whose label is v (g_i the label entry's fp32 gradient), summed in fp32 in
-// token order, zero for a row no label falls in.  The label tokens are those
-// of the n kept row blocks sh.list[0 .. n) (n <= kLabelPathBlocks, one token
-// per thread); they are grouped by vocabulary row with a stable counting sort
-// (ranks from wave ballots, as in a radix sort's scatter).
+// The label entries of vocabulary block cb when every kept block of cb is
+// label-only: the valid tokens i of the n kept row blocks sh.list[0 .. n)
+// (n <= kLabelPathBlocks, one token per thread) whose label falls in cb,
+// grouped by vocabulary row with a stable counting sort (ranks from wave
+// ballots, as in a radix sort's scatter): row r's entries are
+// [sh.rlo[r], sh.rlo[r + 1]) in token order, with the row of H (sh.ent_h) and
+// the entry's fp32 gradient g_i (sh.ent_g).
 template <typename T>
-__device__ __forceinline__ void de_label_item(GradLds<T> &sh, int n, int cb, int d0, const LabelCols<T> &lc,
-                                              const int32_t *__restrict__ perm, int D, int V, Rows2<T> dE) {
+__device__ __forceinline__ void label_group(GradLds<T> &sh, int n, int cb, const LabelCols<T> &lc, int V) {
     constexpr int kThreads = TileG::kThreads;
     static_assert(kThreads == kLabelEntries, "one candidate token per thread");
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -1006,13 +1049,23 @@ __device__ __forceinline__ void de_label_item(GradLds<T> &sh, int n, int cb, int
         sh.ent_g[p] = g;
     }
     __syncthreads();
+}
+
+// dE rows of vocabulary block cb, features [d_lo, d_hi) (multiples of the
+// 16-byte segment), from the grouped label entries: dE_v = sum of g_i h_i
+// over row v's entries, summed in fp32 in token order, zero for a row no
+// label falls in.
+template <typename T>
+__device__ __forceinline__ void label_rows(const GradLds<T> &sh, int cb, int d_lo, int d_hi, const LabelCols<T> &lc,
+                                           const int32_t *__restrict__ perm, int D, int V, Rows2<T> dE) {
     constexpr int CE = ChunkElems<T>::value;
-    constexpr int kSeg = TileG::BN / CE;  // 16-byte segments per row
-    for (int q = t; q < kBlockVocab * kSeg; q += kThreads) {
-        const int r = q / kSeg, d = d0 + (q % kSeg) * CE;
+    const int segs = (min(d_hi, D) - d_lo + CE - 1) / CE;  // 16-byte segments per row
+    if (segs <= 0) return;
+    for (int q = threadIdx.x; q < kBlockVocab * segs; q += TileG::kThreads) {
+        const int r = q / segs, d = d_lo + (q % segs) * CE;
         const int pos = cb * kBlockVocab + r;
         const int v = pos < V ? (perm ? perm[pos] : pos) : -1;
-        if (v < 0 || v >= V || d >= D) continue;
+        if (v < 0 || v >= V) continue;
         float acc[CE];
 #pragma unroll
         for (int k = 0; k < CE; ++k) acc[k] = 0.f;
@@ -1053,8 +1106,28 @@ __device__ __forceinline__ int de_try_label(GradLds<T> &sh, int cb, int d0, int 
         sh.list, sh.wcnt);
     // (build_list ends with a barrier: sh.soft is final)
     if (!lc.labels || n == 0 || n > kLabelPathBlocks || sh.soft) return n;
-    de_label_item<T>(sh, n, cb, d0, lc, perm, D, V, dE);
+    label_group<T>(sh, n, cb, lc, V);
+    label_rows<T>(sh, cb, d0, d0 + TileG::BN, lc, perm, D, V, dE);
     return -1;
+}
+
+// dE rows of a static vocabulary block cb (see k_plan) over all features:
+// its kept blocks (at most kLabelPathBlocks) are all label-only, so its rows
+// are the label entries' sums (zero rows when nothing is kept), the same
+// values the per-feature-tile items would give.
+template <typename T>
+__device__ __forceinline__ void de_column_item(GradLds<T> &sh, int cb, int n_rb, const uint8_t *__restrict__ st,
+                                               int cbp, const LabelCols<T> &lc, const int32_t *__restrict__ perm,
+                                               int D, int V, Rows2<T> dE) {
+    const int n = build_list<TileG::kThreads>(
+        n_rb, [&](int i) { return st[(int64_t)i * cbp + cb] != 0; }, sh.list, sh.wcnt);
+    if (n > 0) {
+        label_group<T>(sh, n, cb, lc, V);
+    } else {
+        for (int r = threadIdx.x; r <= kBlockVocab; r += TileG::kThreads) sh.rlo[r] = 0;
+        __syncthreads();
+    }
+    label_rows<T>(sh, cb, 0, D, lc, perm, D, V, dE);
 }
 
 // dE for one (vocabulary block cb, 256-feature tile d0) item of a pass.  K
@@ -1384,8 +1457,9 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
 // --------------------------------------------------- gradient products
 // Gradient phase of pass p on workgroups bid = 0 .. nbid - 1, which take
 // items from a work queue: first the (row block, feature tile) dH items,
-// which carry the longer K loops, then the (vocabulary block, feature tile)
-// dE items.
+// which carry the longer K loops, then one item per static vocabulary block
+// of the pass (all features), then the (vocabulary block, feature tile) dE
+// items of the other vocabulary blocks.
 template <typename T, bool KAHAN, bool FINE>
 __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, GradLds<T> &sh, int *ticket) {
     using TL = TileG;
@@ -1398,7 +1472,12 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
     const int n_dt = (a.D + TL::BN - 1) / TL::BN;
     const int n_rbv = (nv + kBlockRows - 1) / kBlockRows;
     const int64_t n_dh = (int64_t)n_rbv * n_dt;
-    const int64_t n_de = cb1 > cb0 ? (int64_t)(cb1 - cb0) * n_dt : 0;
+    // the pass's static columns are slist[s_lo, s_hi), the others dlist[c_lo, c_lo + n_dyn)
+    const int s_lo = cb1 > cb0 ? a.cpre[cb0] : 0, s_hi = cb1 > cb0 ? a.cpre[cb1] : 0;
+    const int c_lo = cb0 - s_lo;
+    const int n_dyn = cb1 > cb0 ? (cb1 - cb0) - (s_hi - s_lo) : 0;
+    const int64_t n_col = s_hi - s_lo;
+    const int64_t n_de = (int64_t)n_dyn * n_dt;
     // (no label path for the full classifier gradient: its label-only blocks
     // store the unfiltered gradient for dE)
     const LabelCols<T> lc{a.full_de ? nullptr : a.labels, a.idx, a.inv_perm, a.glab, a.H, nv};
@@ -1409,9 +1488,13 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
                          a.cbp, nv, a.idx, a.Gn, a.E, a.perm, a.D, a.V, a.glab, a.labels, a.dh_acc, a.dH, a.smask);
         it = take_ticket(queue, ticket);
     }
-    while (it < n_dh + n_de) {
-        const int64_t q = it - n_dh;
-        const int cb = cb0 + (int)(q / n_dt), d0 = (int)(q % n_dt) * TL::BN;
+    while (it < n_dh + n_col) {
+        de_column_item<T>(sh, a.slist[s_lo + (int)(it - n_dh)], n_rbv, a.st, a.cbp, lc, a.perm, a.D, a.V, a.dE);
+        it = take_ticket(queue, ticket);
+    }
+    while (it < n_dh + n_col + n_de) {
+        const int64_t q = it - n_dh - n_col;
+        const int cb = a.dlist[c_lo + (int)(q / n_dt)], d0 = (int)(q % n_dt) * TL::BN;
         const int n = de_try_label<T>(sh, cb, d0, n_rbv, a.st, a.cbp, lc, a.perm, a.D, a.V, a.dE);
         if (n != -1)
             de_item<T, KAHAN, FINE>(sh, cb, d0, n_rbv, a.st, a.slot, a.cbp, a.Gt, a.Ht, a.ldh, a.perm, a.D, a.V, a.dE,
@@ -1483,8 +1566,13 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     w.glab = c.take<float>((size_t)s.Np);
     w.lab = c.take<uint8_t>(nblk);
     w.st = c.take<uint8_t>(nblk);
+    w.csoft = c.take<uint8_t>((size_t)s.cbp);  // csoft and cnlab follow st: one fill clears all three
+    w.cnlab = c.take<int32_t>((size_t)s.cbp);
     w.slot = c.take<int32_t>(nblk);
     w.smask = c.take<uint16_t>(nblk);
+    w.cpre = c.take<int32_t>((size_t)s.cbp + 1);
+    w.slist = c.take<int32_t>((size_t)s.cbp);
+    w.dlist = c.take<int32_t>((size_t)s.cbp);
     w.tneed = c.take<uint8_t>(ntile);
     w.cum = c.take<int64_t>((size_t)s.n_vtiles);
     w.act = c.take<int32_t>((size_t)s.n_vtiles);
@@ -1530,7 +1618,8 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     }
     const size_t nblk = (size_t)s.n_rb * s.cbp;
     CCE_TRY(fill_bytes_zero(w.lab, nblk, st));
-    CCE_TRY(fill_bytes_zero(w.st, nblk, st));
+    CCE_TRY(fill_bytes_zero(w.st, (size_t)(reinterpret_cast<char *>(w.cnlab + s.cbp) - reinterpret_cast<char *>(w.st)),
+                            st));  // st, csoft, cnlab
     if (s.max_passes > 1) {
         const int64_t n = s.Np * (int64_t)D;  // D % 8 == 0: whole f32x4 groups
         hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)ceil_div(n, 1024)), dim3(256), 0, st, w.dh_acc, n);
@@ -1568,10 +1657,15 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     CCE_LAUNCHED();
     const int64_t ntile = (int64_t)s.n_rtiles * s.n_vtiles;
     hipLaunchKernelGGL(k_tile_class, dim3((unsigned)ceil_div(ntile, 256)), dim3(256), 0, st, w.nvalid, s.V,
-                       s.n_rtiles, s.n_vtiles, s.cbp, w.lab, tb, w.lmin, thr, w.tneed);
+                       s.n_rtiles, s.n_vtiles, s.cbp, w.lab, tb, w.lmin, thr, w.tneed, w.csoft, w.cnlab);
     CCE_LAUNCHED();
+    // static columns need the label path (off for the full classifier
+    // gradient) and a column's row blocks in one list
+    const int CB = (int)ceil_div(V, kBlockVocab);
+    const int static_ok = (!full_de && s.n_rb <= kListCap) ? 1 : 0;
     hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, w.tneed, s.n_rtiles, s.n_vtiles, s.cap, s.cap_eff,
-                       s.max_passes, w.plan, w.cum, w.act, w.tlist);
+                       s.max_passes, w.plan, w.cum, w.act, w.tlist, CB, static_ok, w.csoft, w.cnlab, w.cpre, w.slist,
+                       w.dlist);
     CCE_LAUNCHED();
 
     BwdArgs<T> a;
@@ -1608,6 +1702,9 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     a.st = w.st;
     a.slot = w.slot;
     a.smask = w.smask;
+    a.cpre = w.cpre;
+    a.slist = w.slist;
+    a.dlist = w.dlist;
     a.fine = (flags & CCE_BWD_FINE_FILTER) ? 1 : 0;
     a.stats = stats;
     a.dh_acc = w.dh_acc;

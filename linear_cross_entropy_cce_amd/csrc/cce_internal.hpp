@@ -115,6 +115,11 @@ struct BwdWs {
     uint8_t *st;       // [n_rb, cbp] block status: 0 dropped, 1 softmax kept, 2 label only
     int32_t *slot;     // [n_rb, cbp] store slot of a kept block
     uint16_t *smask;   // [n_rb, cbp] 32 x 32 sub-tiles of a kept block whose gradient may be nonzero
+    uint8_t *csoft;    // [cbp] 1 where a block of the vocabulary block (column) may keep a softmax part
+    int32_t *cnlab;    // [cbp] blocks of the column that hold a label
+    int32_t *cpre;     // [cbp + 1] static columns (see k_plan) before each column
+    int32_t *slist;    // [cbp] static columns, in order
+    int32_t *dlist;    // [cbp] the other columns, in order
     uint8_t *tneed;    // [n_vtiles, n_rtiles] blocks the tile may keep (bits 0-2), recompute flag (bit 7)
     int64_t *cum;      // [n_vtiles] plan scratch: cumulative blocks
     int32_t *act;      // [n_vtiles] plan scratch: active tiles before each vocabulary tile
