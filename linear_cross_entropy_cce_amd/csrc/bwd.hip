@@ -58,7 +58,18 @@ constexpr int kListCap = 512;
 // A vocabulary block whose kept blocks are all label-only, at most this many,
 // gets its dE rows from the label entries directly (no block products).
 constexpr int kLabelPathBlocks = 4;
+// At most this many label entries go through the label path at once.
 constexpr int kLabelEntries = kLabelPathBlocks * kBlockRows;
+// A vocabulary block whose kept blocks are all label-only takes the label
+// path (its dE rows from the label entries) with at most kLabelPathBlocks of
+// them, or with at most kSparseLabelBlocks holding at most
+// kSparseLabelEntries label entries; each entry costs a pass over a row of
+// H, which beats the block products only while the entries are few.
+constexpr int kSparseLabelBlocks = 32;
+constexpr int kSparseLabelEntries = 64;
+__host__ __device__ __forceinline__ bool label_path_ok(int n_blocks, int n_entries) {
+    return n_blocks <= kLabelPathBlocks || (n_blocks <= kSparseLabelBlocks && n_entries <= kSparseLabelEntries);
+}
 constexpr int kDeGroups = 2 * kPassGroups;  // persistent dE workgroups of the gradient-product kernel
 
 // Plan record: P, number of listed tiles, first vocabulary tile of each pass
@@ -117,6 +128,7 @@ struct BwdArgs {
     int32_t *slot;
     uint16_t *smask;  // bit 4 i + j: sub-tile (vocabulary rows 32 i.., tokens 32 j..) of a kept block may be nonzero
     const int32_t *cpre, *slist, *dlist;  // column lists of k_plan
+    const int32_t *cent;                  // label entries per column
     int64_t *stats;
     float *dh_acc;
     Rows2<T> dE;  // same layout as E
@@ -294,8 +306,11 @@ __device__ __forceinline__ int build_stages(int n, int kspb, const int *mask, Se
 }
 
 // ------------------------------------------------------------------ plan
-// lab[rb][cb] = 1 where the label of a valid token of row block rb falls in
-// vocabulary block cb (processing order).
+// lab[rb][cb] = the number of valid tokens of row block rb whose label falls
+// in vocabulary block cb (processing order; zeroed before).  A block holds
+// at most 128 tokens, so each count fits its byte: the byte is added to
+// through its aligned 32-bit word (the map's region is 256-byte aligned and
+// padded).
 __global__ __launch_bounds__(256) void k_label_map(const int64_t *__restrict__ labels, const int32_t *__restrict__ idx,
                                                    const int32_t *__restrict__ nvalid_p,
                                                    const int32_t *__restrict__ inv_perm, int64_t V, int cbp,
@@ -305,7 +320,8 @@ __global__ __launch_bounds__(256) void k_label_map(const int64_t *__restrict__ l
     const int64_t y = labels[idx[t]];
     if (y < 0 || y >= V) return;  // not a valid label: undefined by contract
     const int64_t pos = inv_perm ? inv_perm[y] : y;
-    lab[(t / kBlockRows) * cbp + pos / kBlockVocab] = 1;
+    const int64_t i = (t / kBlockRows) * cbp + pos / kBlockVocab;
+    atomicAdd(reinterpret_cast<uint32_t *>(lab + (i & ~int64_t(3))), 1u << (8 * (i & 3)));
 }
 
 // Per tile (vocabulary-tile-major index vt * n_rt + rt): the number of its
@@ -315,12 +331,14 @@ __global__ __launch_bounds__(256) void k_label_map(const int64_t *__restrict__ l
 // bound rules it out, and may keep its label entries if it holds a label;
 // only the blocks that may keep a softmax part are recomputed.  Per
 // vocabulary block (column, zeroed before): csoft = 1 if one of its blocks
-// may keep a softmax part, cnlab = its blocks that hold a label.
+// may keep a softmax part, cnlab = its blocks that hold a label, cent = the
+// valid tokens whose label falls in it.
 __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ nvalid_p, int64_t V, int n_rt,
                                                     int n_vt, int cbp, const uint8_t *__restrict__ lab,
                                                     const float *__restrict__ bmax, const float *__restrict__ lmin,
                                                     float thr, uint8_t *__restrict__ tneed,
-                                                    uint8_t *__restrict__ csoft, int32_t *__restrict__ cnlab) {
+                                                    uint8_t *__restrict__ csoft, int32_t *__restrict__ cnlab,
+                                                    int32_t *__restrict__ cent) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)n_rt * n_vt) return;
     const int vt = (int)(i / n_rt), rt = (int)(i % n_rt);
@@ -335,11 +353,15 @@ __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ 
         const int rb = 2 * rt + (q & 1), cb = 2 * vt + (q >> 1);
         if ((int64_t)rb * kBlockRows >= nv || (int64_t)cb * kBlockVocab >= V) continue;
         const bool soft = !block_below(bmax, cbp, lmin, thr, rb, cb);
-        const bool has_label = lab[(int64_t)rb * cbp + cb] != 0;
+        const int n_lab = lab[(int64_t)rb * cbp + cb];
+        const bool has_label = n_lab != 0;
         mask |= soft ? 1 << q : 0;
         need += (soft || has_label) ? 1 : 0;
         if (soft) csoft[cb] = 1;  // (every writer stores 1)
-        if (has_label) atomicAdd(&cnlab[cb], 1);
+        if (has_label) {
+            atomicAdd(&cnlab[cb], 1);
+            atomicAdd(&cent[cb], n_lab);
+        }
     }
     tneed[i] = (uint8_t)(need | (mask << 3) | (mask ? 0x80 : 0));
 }
@@ -351,9 +373,10 @@ __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ 
 // floor(cum(vt) / cap_eff) with cum the inclusive block count; a vocabulary
 // tile adds at most cap - cap_eff blocks, so no pass exceeds cap.
 // Columns (vocabulary blocks cb < CB): with static_ok, a column none of
-// whose blocks may keep a softmax part and with at most kLabelPathBlocks
-// label blocks is static: its kept blocks can only be label-only, so its dE
-// rows come from the label entries (or are zero) for all features at once.
+// whose blocks may keep a softmax part and whose label blocks and entries
+// pass label_path_ok is static: its kept blocks can only be label-only, so
+// its dE rows come from the label entries (or are zero) for all features at
+// once, as the per-feature-tile items would write them.
 // slist holds the static columns in order, dlist the others, and cpre[cb]
 // the static columns before cb (cpre[CB] all of them).
 __global__ __launch_bounds__(1024) void k_plan(const uint8_t *__restrict__ tneed, int n_rt, int n_vt, int64_t cap,
@@ -361,7 +384,7 @@ __global__ __launch_bounds__(1024) void k_plan(const uint8_t *__restrict__ tneed
                                                int64_t *__restrict__ cum, int32_t *__restrict__ act,
                                                int32_t *__restrict__ tlist, int CB, int static_ok,
                                                const uint8_t *__restrict__ csoft, const int32_t *__restrict__ cnlab,
-                                               int32_t *__restrict__ cpre, int32_t *__restrict__ slist,
+                                               const int32_t *__restrict__ cent, int32_t *__restrict__ cpre, int32_t *__restrict__ slist,
                                                int32_t *__restrict__ dlist) {
     __shared__ int64_t wsum[16];
     __shared__ int32_t wact[16];
@@ -440,7 +463,7 @@ __global__ __launch_bounds__(1024) void k_plan(const uint8_t *__restrict__ tneed
     __syncthreads();
     for (int base = 0; base < CB; base += 1024) {
         const int cb = base + t;
-        const int is_s = (cb < CB && static_ok && !csoft[cb] && cnlab[cb] <= kLabelPathBlocks) ? 1 : 0;
+        const int is_s = (cb < CB && static_ok && !csoft[cb] && label_path_ok(cnlab[cb], cent[cb])) ? 1 : 0;
         int x = is_s;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -967,6 +990,8 @@ struct GradLds {
     // row, in token order within a row
     int ent_h[kLabelEntries];                           // row of H
     float ent_g[kLabelEntries];                         // gradient of the label entry (fp32)
+    int tmp_r[kLabelEntries], tmp_h[kLabelEntries];     // the entries in token order, before grouping
+    float tmp_g[kLabelEntries];
     int rlo[kBlockVocab + 1];                           // entries of row r: [rlo[r], rlo[r + 1])
     int wrow[TileG::kWaves][kBlockVocab];               // entries of each row per wave
 };
@@ -980,37 +1005,72 @@ struct LabelCols {
     const float *glab;
     const T *H;
     int nv;
+    const int32_t *cent;  // label entries per vocabulary block
 };
 
 // The label entries of vocabulary block cb when every kept block of cb is
 // label-only: the valid tokens i of the n kept row blocks sh.list[0 .. n)
-// (n <= kLabelPathBlocks, one token per thread) whose label falls in cb,
-// grouped by vocabulary row with a stable counting sort (ranks from wave
-// ballots, as in a radix sort's scatter): row r's entries are
-// [sh.rlo[r], sh.rlo[r + 1]) in token order, with the row of H (sh.ent_h) and
-// the entry's fp32 gradient g_i (sh.ent_g).
+// whose label falls in cb (at most kLabelEntries of them), grouped by
+// vocabulary row: row r's entries are [sh.rlo[r], sh.rlo[r + 1]) in token
+// order, with the row of H (sh.ent_h) and the entry's fp32 gradient g_i
+// (sh.ent_g).  The candidates are read 512 at a time and compacted in token
+// order; the compacted entries (one per thread) are then grouped with a
+// stable counting sort (ranks from wave ballots, as in a radix sort's
+// scatter).
 template <typename T>
 __device__ __forceinline__ void label_group(GradLds<T> &sh, int n, int cb, const LabelCols<T> &lc, int V) {
     constexpr int kThreads = TileG::kThreads;
-    static_assert(kThreads == kLabelEntries, "one candidate token per thread");
+    static_assert(kThreads == kLabelEntries, "one compacted entry per thread");
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    // candidate: token (sh.list[t / 128] * 128 + t % 128) of a label block
-    int row = -1, hrow = 0;
-    float g = 0.f;
-    if (t < n * kBlockRows) {
-        const int tok = sh.list[t / kBlockRows] * kBlockRows + (t % kBlockRows);
-        if (tok < lc.nv) {
-            const int r = lc.idx[tok];
-            const int64_t y = lc.labels[r];
-            if (y >= 0 && y < V) {
-                const int pos = lc.inv_perm ? lc.inv_perm[y] : (int)y;
-                if (pos / kBlockVocab == cb) {
-                    row = pos % kBlockVocab;
-                    hrow = r;
-                    g = lc.glab[tok];
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    int m = 0;  // entries compacted so far (uniform)
+    for (int c0 = 0; c0 < n * kBlockRows; c0 += kThreads) {
+        // candidate c: token (sh.list[c / 128] * 128 + c % 128) of a label block
+        const int c = c0 + t;
+        int row = -1, hrow = 0;
+        float g = 0.f;
+        if (c < n * kBlockRows) {
+            const int tok = sh.list[c / kBlockRows] * kBlockRows + (c % kBlockRows);
+            if (tok < lc.nv) {
+                const int r = lc.idx[tok];
+                const int64_t y = lc.labels[r];
+                if (y >= 0 && y < V) {
+                    const int pos = lc.inv_perm ? lc.inv_perm[y] : (int)y;
+                    if (pos / kBlockVocab == cb) {
+                        row = pos % kBlockVocab;
+                        hrow = r;
+                        g = lc.glab[tok];
+                    }
                 }
             }
         }
+        const uint64_t bal = __ballot(row >= 0);
+        if (lane == 0) sh.wcnt[wave] = __popcll(bal);
+        __syncthreads();
+        int base = m, total = 0;
+#pragma unroll
+        for (int w = 0; w < TileG::kWaves; ++w) {
+            base += w < wave ? sh.wcnt[w] : 0;
+            total += sh.wcnt[w];
+        }
+        if (row >= 0) {
+            const int q = base + __popcll(bal & below);
+            if (q < kLabelEntries) {  // (callers keep the entries within kLabelEntries)
+                sh.tmp_r[q] = row;
+                sh.tmp_h[q] = hrow;
+                sh.tmp_g[q] = g;
+            }
+        }
+        m += total;
+        __syncthreads();  // wcnt is rewritten by the next chunk; tmp_* are read below
+    }
+    m = min(m, kLabelEntries);
+    int row = -1, hrow = 0;
+    float g = 0.f;
+    if (t < m) {
+        row = sh.tmp_r[t];
+        hrow = sh.tmp_h[t];
+        g = sh.tmp_g[t];
     }
     // lanes of this wave with the same row: their rank among them is the rank in token order
     uint64_t same = __ballot(row >= 0);
@@ -1020,17 +1080,16 @@ __device__ __forceinline__ void label_group(GradLds<T> &sh, int n, int cb, const
         const uint64_t bal = __ballot(bit);
         same &= bit ? bal : ~bal;
     }
-    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
     const int rank = __popcll(same & below);
     for (int q = t; q < TileG::kWaves * kBlockVocab; q += kThreads) (&sh.wrow[0][0])[q] = 0;
     __syncthreads();
     if (row >= 0 && rank == 0) sh.wrow[wave][row] = __popcll(same);
     __syncthreads();
     if (t < kBlockVocab) {  // two waves: exclusive scan of the row counts
-        int c = 0;
+        int cnt = 0;
 #pragma unroll
-        for (int w = 0; w < TileG::kWaves; ++w) c += sh.wrow[w][t];
-        int x = c;
+        for (int w = 0; w < TileG::kWaves; ++w) cnt += sh.wrow[w][t];
+        int x = cnt;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const int y = __shfl_up(x, o, 64);
@@ -1069,7 +1128,22 @@ __device__ __forceinline__ void label_rows(const GradLds<T> &sh, int cb, int d_l
         float acc[CE];
 #pragma unroll
         for (int k = 0; k < CE; ++k) acc[k] = 0.f;
-        for (int e = sh.rlo[r]; e < sh.rlo[r + 1]; ++e) {
+        const int e1 = sh.rlo[r + 1];
+        int e = sh.rlo[r];
+        for (; e + 4 <= e1; e += 4) {  // four loads in flight, added in entry order
+            u32x4 hv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                hv[u] = ld16(reinterpret_cast<const char *>(lc.H + (int64_t)sh.ent_h[e + u] * D + d));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const T *hp = reinterpret_cast<const T *>(&hv[u]);
+                const float ge = sh.ent_g[e + u];
+#pragma unroll
+                for (int k = 0; k < CE; ++k) acc[k] += ge * to_f32(hp[k]);
+            }
+        }
+        for (; e < e1; ++e) {
             const u32x4 hv = ld16(reinterpret_cast<const char *>(lc.H + (int64_t)sh.ent_h[e] * D + d));
             const T *hp = reinterpret_cast<const T *>(&hv);
             const float ge = sh.ent_g[e];
@@ -1085,8 +1159,7 @@ __device__ __forceinline__ void label_rows(const GradLds<T> &sh, int cb, int d_l
 }
 
 // The label path for dE item (cb, d0), if it applies: every kept block of
-// vocabulary block cb is label-only (status 2) and there are at most
-// kLabelPathBlocks of them.  Returns -1 when the item's rows were written,
+// vocabulary block cb is label-only (status 2) and they pass label_path_ok.  Returns -1 when the item's rows were written,
 // else the number of kept row blocks, listed in sh.list (for de_item), or
 // -2 when the column's row blocks do not fit one list.
 template <typename T>
@@ -1105,16 +1178,15 @@ __device__ __forceinline__ int de_try_label(GradLds<T> &sh, int cb, int d0, int 
         },
         sh.list, sh.wcnt);
     // (build_list ends with a barrier: sh.soft is final)
-    if (!lc.labels || n == 0 || n > kLabelPathBlocks || sh.soft) return n;
+    if (!lc.labels || n == 0 || sh.soft || !label_path_ok(n, lc.cent[cb])) return n;
     label_group<T>(sh, n, cb, lc, V);
     label_rows<T>(sh, cb, d0, d0 + TileG::BN, lc, perm, D, V, dE);
     return -1;
 }
 
 // dE rows of a static vocabulary block cb (see k_plan) over all features:
-// its kept blocks (at most kLabelPathBlocks) are all label-only, so its rows
-// are the label entries' sums (zero rows when nothing is kept), the same
-// values the per-feature-tile items would give.
+// its kept blocks are all label-only and pass label_path_ok, so its rows are
+// the label entries' sums in token order (zero rows when nothing is kept).
 template <typename T>
 __device__ __forceinline__ void de_column_item(GradLds<T> &sh, int cb, int n_rb, const uint8_t *__restrict__ st,
                                                int cbp, const LabelCols<T> &lc, const int32_t *__restrict__ perm,
@@ -1456,10 +1528,10 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
 
 // --------------------------------------------------- gradient products
 // Gradient phase of pass p on workgroups bid = 0 .. nbid - 1, which take
-// items from a work queue: first the (row block, feature tile) dH items,
-// which carry the longer K loops, then one item per static vocabulary block
-// of the pass (all features), then the (vocabulary block, feature tile) dE
-// items of the other vocabulary blocks.
+// items from a work queue, longer items first: the (row block, feature
+// tile) dH items, then the (vocabulary block, feature tile) dE items of the
+// vocabulary blocks that are not static, then one item per static
+// vocabulary block of the pass (all features).
 template <typename T, bool KAHAN, bool FINE>
 __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, GradLds<T> &sh, int *ticket) {
     using TL = TileG;
@@ -1480,7 +1552,7 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
     const int64_t n_de = (int64_t)n_dyn * n_dt;
     // (no label path for the full classifier gradient: its label-only blocks
     // store the unfiltered gradient for dE)
-    const LabelCols<T> lc{a.full_de ? nullptr : a.labels, a.idx, a.inv_perm, a.glab, a.H, nv};
+    const LabelCols<T> lc{a.full_de ? nullptr : a.labels, a.idx, a.inv_perm, a.glab, a.H, nv, a.cent};
     // two loops rather than one with a branch: each keeps its own registers
     int64_t it = take_ticket(queue, ticket);
     while (it < n_dh) {
@@ -1488,17 +1560,18 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
                          a.cbp, nv, a.idx, a.Gn, a.E, a.perm, a.D, a.V, a.glab, a.labels, a.dh_acc, a.dH, a.smask);
         it = take_ticket(queue, ticket);
     }
-    while (it < n_dh + n_col) {
-        de_column_item<T>(sh, a.slist[s_lo + (int)(it - n_dh)], n_rbv, a.st, a.cbp, lc, a.perm, a.D, a.V, a.dE);
-        it = take_ticket(queue, ticket);
-    }
-    while (it < n_dh + n_col + n_de) {
-        const int64_t q = it - n_dh - n_col;
+    while (it < n_dh + n_de) {
+        const int64_t q = it - n_dh;
         const int cb = a.dlist[c_lo + (int)(q / n_dt)], d0 = (int)(q % n_dt) * TL::BN;
         const int n = de_try_label<T>(sh, cb, d0, n_rbv, a.st, a.cbp, lc, a.perm, a.D, a.V, a.dE);
         if (n != -1)
             de_item<T, KAHAN, FINE>(sh, cb, d0, n_rbv, a.st, a.slot, a.cbp, a.Gt, a.Ht, a.ldh, a.perm, a.D, a.V, a.dE,
                                     n >= 0 ? n : -1, a.smask);
+        it = take_ticket(queue, ticket);
+    }
+    while (it < n_dh + n_de + n_col) {
+        de_column_item<T>(sh, a.slist[s_lo + (int)(it - n_dh - n_de)], n_rbv, a.st, a.cbp, lc, a.perm, a.D, a.V,
+                          a.dE);
         it = take_ticket(queue, ticket);
     }
 }
@@ -1566,8 +1639,9 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     w.glab = c.take<float>((size_t)s.Np);
     w.lab = c.take<uint8_t>(nblk);
     w.st = c.take<uint8_t>(nblk);
-    w.csoft = c.take<uint8_t>((size_t)s.cbp);  // csoft and cnlab follow st: one fill clears all three
+    w.csoft = c.take<uint8_t>((size_t)s.cbp);  // csoft, cnlab and cent follow st: one fill clears all four
     w.cnlab = c.take<int32_t>((size_t)s.cbp);
+    w.cent = c.take<int32_t>((size_t)s.cbp);
     w.slot = c.take<int32_t>(nblk);
     w.smask = c.take<uint16_t>(nblk);
     w.cpre = c.take<int32_t>((size_t)s.cbp + 1);
@@ -1618,8 +1692,8 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     }
     const size_t nblk = (size_t)s.n_rb * s.cbp;
     CCE_TRY(fill_bytes_zero(w.lab, nblk, st));
-    CCE_TRY(fill_bytes_zero(w.st, (size_t)(reinterpret_cast<char *>(w.cnlab + s.cbp) - reinterpret_cast<char *>(w.st)),
-                            st));  // st, csoft, cnlab
+    CCE_TRY(fill_bytes_zero(w.st, (size_t)(reinterpret_cast<char *>(w.cent + s.cbp) - reinterpret_cast<char *>(w.st)),
+                            st));  // st, csoft, cnlab, cent
     if (s.max_passes > 1) {
         const int64_t n = s.Np * (int64_t)D;  // D % 8 == 0: whole f32x4 groups
         hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)ceil_div(n, 1024)), dim3(256), 0, st, w.dh_acc, n);
@@ -1657,15 +1731,15 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     CCE_LAUNCHED();
     const int64_t ntile = (int64_t)s.n_rtiles * s.n_vtiles;
     hipLaunchKernelGGL(k_tile_class, dim3((unsigned)ceil_div(ntile, 256)), dim3(256), 0, st, w.nvalid, s.V,
-                       s.n_rtiles, s.n_vtiles, s.cbp, w.lab, tb, w.lmin, thr, w.tneed, w.csoft, w.cnlab);
+                       s.n_rtiles, s.n_vtiles, s.cbp, w.lab, tb, w.lmin, thr, w.tneed, w.csoft, w.cnlab, w.cent);
     CCE_LAUNCHED();
     // static columns need the label path (off for the full classifier
     // gradient) and a column's row blocks in one list
     const int CB = (int)ceil_div(V, kBlockVocab);
     const int static_ok = (!full_de && s.n_rb <= kListCap) ? 1 : 0;
     hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, w.tneed, s.n_rtiles, s.n_vtiles, s.cap, s.cap_eff,
-                       s.max_passes, w.plan, w.cum, w.act, w.tlist, CB, static_ok, w.csoft, w.cnlab, w.cpre, w.slist,
-                       w.dlist);
+                       s.max_passes, w.plan, w.cum, w.act, w.tlist, CB, static_ok, w.csoft, w.cnlab, w.cent, w.cpre,
+                       w.slist, w.dlist);
     CCE_LAUNCHED();
 
     BwdArgs<T> a;
@@ -1705,6 +1779,7 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     a.cpre = w.cpre;
     a.slist = w.slist;
     a.dlist = w.dlist;
+    a.cent = w.cent;
     a.fine = (flags & CCE_BWD_FINE_FILTER) ? 1 : 0;
     a.stats = stats;
     a.dh_acc = w.dh_acc;

@@ -111,12 +111,13 @@ struct BwdWs {
     int32_t *inv_perm; // [V] processing position of each vocabulary id
     float *lmin;       // [n_rb] smallest lse of each 128-token block (for the block-max bound)
     float *glab;       // [Np] label-entry gradient of rows whose label block is label-only (else 0)
-    uint8_t *lab;      // [n_rb, cbp] 1 where a label falls in the block
+    uint8_t *lab;      // [n_rb, cbp] valid tokens whose label falls in the block
     uint8_t *st;       // [n_rb, cbp] block status: 0 dropped, 1 softmax kept, 2 label only
     int32_t *slot;     // [n_rb, cbp] store slot of a kept block
     uint16_t *smask;   // [n_rb, cbp] 32 x 32 sub-tiles of a kept block whose gradient may be nonzero
     uint8_t *csoft;    // [cbp] 1 where a block of the vocabulary block (column) may keep a softmax part
     int32_t *cnlab;    // [cbp] blocks of the column that hold a label
+    int32_t *cent;     // [cbp] valid tokens whose label falls in the column
     int32_t *cpre;     // [cbp + 1] static columns (see k_plan) before each column
     int32_t *slist;    // [cbp] static columns, in order
     int32_t *dlist;    // [cbp] the other columns, in order
