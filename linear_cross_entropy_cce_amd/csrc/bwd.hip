@@ -332,13 +332,16 @@ __global__ __launch_bounds__(256) void k_label_map(const int64_t *__restrict__ l
 // only the blocks that may keep a softmax part are recomputed.  Per
 // vocabulary block (column, zeroed before): csoft = 1 if one of its blocks
 // may keep a softmax part, cnlab = its blocks that hold a label, cent = the
-// valid tokens whose label falls in it.
+// valid tokens whose label falls in it.  Per vocabulary tile (zeroed
+// before): vneed = the blocks its tiles may keep, vact = its tiles that may
+// keep one.
 __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ nvalid_p, int64_t V, int n_rt,
                                                     int n_vt, int cbp, const uint8_t *__restrict__ lab,
                                                     const float *__restrict__ bmax, const float *__restrict__ lmin,
                                                     float thr, uint8_t *__restrict__ tneed,
                                                     uint8_t *__restrict__ csoft, int32_t *__restrict__ cnlab,
-                                                    int32_t *__restrict__ cent) {
+                                                    int32_t *__restrict__ cent, int32_t *__restrict__ vneed,
+                                                    int32_t *__restrict__ vact) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)n_rt * n_vt) return;
     const int vt = (int)(i / n_rt), rt = (int)(i % n_rt);
@@ -364,11 +367,16 @@ __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ 
         }
     }
     tneed[i] = (uint8_t)(need | (mask << 3) | (mask ? 0x80 : 0));
+    if (need) {
+        atomicAdd(&vneed[vt], need);
+        atomicAdd(&vact[vt], 1);
+    }
 }
 
-// One workgroup: per vocabulary tile the blocks it may keep and its listed
-// tiles, their prefix sums, the pass of each vocabulary tile, the per-pass
-// ranges and the tile list (vocabulary-tile-major, token tiles in order).
+// One workgroup: prefix sums of the blocks each vocabulary tile may keep and
+// of its listed tiles (vneed, vact from k_tile_class), the pass of each
+// vocabulary tile and the per-pass ranges; k_tile_list then writes the tile
+// list (vocabulary-tile-major, token tiles in order).
 // Passes: one if every block fits the store, else pass(vt) =
 // floor(cum(vt) / cap_eff) with cum the inclusive block count; a vocabulary
 // tile adds at most cap - cap_eff blocks, so no pass exceeds cap.
@@ -379,13 +387,13 @@ __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ 
 // once, as the per-feature-tile items would write them.
 // slist holds the static columns in order, dlist the others, and cpre[cb]
 // the static columns before cb (cpre[CB] all of them).
-__global__ __launch_bounds__(1024) void k_plan(const uint8_t *__restrict__ tneed, int n_rt, int n_vt, int64_t cap,
-                                               int64_t cap_eff, int max_passes, int32_t *__restrict__ plan,
-                                               int64_t *__restrict__ cum, int32_t *__restrict__ act,
-                                               int32_t *__restrict__ tlist, int CB, int static_ok,
+__global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ vneed, const int32_t *__restrict__ vact,
+                                               int n_vt, int64_t cap, int64_t cap_eff, int max_passes,
+                                               int32_t *__restrict__ plan, int64_t *__restrict__ cum,
+                                               int32_t *__restrict__ act, int CB, int static_ok,
                                                const uint8_t *__restrict__ csoft, const int32_t *__restrict__ cnlab,
-                                               const int32_t *__restrict__ cent, int32_t *__restrict__ cpre, int32_t *__restrict__ slist,
-                                               int32_t *__restrict__ dlist) {
+                                               const int32_t *__restrict__ cent, int32_t *__restrict__ cpre,
+                                               int32_t *__restrict__ slist, int32_t *__restrict__ dlist) {
     __shared__ int64_t wsum[16];
     __shared__ int32_t wact[16];
     __shared__ int32_t wcol[16];
@@ -400,12 +408,8 @@ __global__ __launch_bounds__(1024) void k_plan(const uint8_t *__restrict__ tneed
         int64_t nd = 0;
         int ac = 0;
         if (vt < n_vt) {
-            const uint8_t *row = tneed + (int64_t)vt * n_rt;
-            for (int rt = 0; rt < n_rt; ++rt) {
-                const int q = row[rt] & 7;
-                nd += q;
-                ac += q > 0;
-            }
+            nd = vneed[vt];
+            ac = vact[vt];
         }
         int64_t xs = nd;
         int xa = ac;
@@ -442,10 +446,6 @@ __global__ __launch_bounds__(1024) void k_plan(const uint8_t *__restrict__ tneed
             pv.vt_begin[q] = vt;
             pv.list_begin[q] = act[vt];
         }
-        int pos = act[vt];
-        const uint8_t *row = tneed + (int64_t)vt * n_rt;
-        for (int rt = 0; rt < n_rt; ++rt)
-            if (row[rt] & 7) tlist[pos++] = vt * n_rt + rt;
     }
     if (t == 0) {
         const int P = pass_of(n_vt - 1) + 1;
@@ -485,6 +485,25 @@ __global__ __launch_bounds__(1024) void k_plan(const uint8_t *__restrict__ tneed
         __syncthreads();
     }
     if (t == 0) cpre[CB] = carry_c;
+}
+
+// The tile list: the listed tiles (that may keep a block) of vocabulary tile
+// vt at act[vt] onwards, token tiles in order.  One wave per vocabulary tile.
+__global__ __launch_bounds__(256) void k_tile_list(const uint8_t *__restrict__ tneed, int n_rt, int n_vt,
+                                                   const int32_t *__restrict__ act, int32_t *__restrict__ tlist) {
+    const int lane = threadIdx.x & 63;
+    const int vt = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (vt >= n_vt) return;  // wave-uniform
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const uint8_t *row = tneed + (int64_t)vt * n_rt;
+    int pos = act[vt];
+    for (int r0 = 0; r0 < n_rt; r0 += 64) {
+        const int rt = r0 + lane;
+        const bool on = rt < n_rt && (row[rt] & 7) != 0;
+        const uint64_t bal = __ballot(on);
+        if (on) tlist[pos + __popcll(bal & below)] = vt * n_rt + rt;
+        pos += __popcll(bal);
+    }
 }
 
 // ------------------------------------------------------- recompute + G
@@ -1159,9 +1178,10 @@ __device__ __forceinline__ void label_rows(const GradLds<T> &sh, int cb, int d_l
 }
 
 // The label path for dE item (cb, d0), if it applies: every kept block of
-// vocabulary block cb is label-only (status 2) and they pass label_path_ok.  Returns -1 when the item's rows were written,
-// else the number of kept row blocks, listed in sh.list (for de_item), or
-// -2 when the column's row blocks do not fit one list.
+// vocabulary block cb is label-only (status 2) and they pass label_path_ok.
+// Returns -1 when the item's rows were written, else the number of kept row
+// blocks, listed in sh.list (for de_item), or -2 when the column's row
+// blocks do not fit one list.
 template <typename T>
 __device__ __forceinline__ int de_try_label(GradLds<T> &sh, int cb, int d0, int n_rb, const uint8_t *__restrict__ st,
                                             int cbp, const LabelCols<T> &lc, const int32_t *__restrict__ perm, int D,
@@ -1379,7 +1399,8 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
 // depend on where the passes are cut.  The last pass writes dH in the output
 // dtype.
 template <typename T, bool FINE>
-__device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool multi, bool last, int cb0, int cb1,
+__device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool multi, bool first, bool last, int cb0,
+                                        int cb1,
                                         const uint8_t *__restrict__ st, const int32_t *__restrict__ slotm, int cbp,
                                         int nv, const int32_t *__restrict__ idx, const T *__restrict__ Gn,
                                         Rows2<const T> E, const int32_t *__restrict__ perm, int D, int V,
@@ -1393,15 +1414,17 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
 
     f32x16 acc[TL::TM][TL::TN], sum[TL::TM][TL::TN];
     zero_acc<TL>(acc);
-    if (multi) {
+    if (multi && !first) {  // the running sum of the earlier passes (written for the valid rows)
 #pragma unroll
         for (int tm = 0; tm < TL::TM; ++tm)
 #pragma unroll
             for (int tn = 0; tn < TL::TN; ++tn) {
                 const int d = min(d0 + tile_col<TL>(tn, tid), D - 1);
 #pragma unroll
-                for (int r = 0; r < 16; ++r)  // dh_acc is [Np, D]: every tok < Np is in bounds
-                    sum[tm][tn][r] = dh_acc[(int64_t)(tok0 + tile_row<TL>(tm, r, tid)) * D + d];
+                for (int r = 0; r < 16; ++r) {
+                    const int tok = tok0 + tile_row<TL>(tm, r, tid);
+                    sum[tm][tn][r] = tok < nv ? dh_acc[(int64_t)tok * D + d] : 0.f;
+                }
             }
     } else {
         zero_acc<TL>(sum);
@@ -1473,7 +1496,9 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
         }
         __syncthreads();  // list[], lslot[] and the LDS stages are reused next
     }
-    if (!any && !last) return;  // nothing added in this pass
+    // nothing added in this pass: the running sum stands (the first pass
+    // still writes it, as the later ones read it)
+    if (!any && !last && !first) return;
 
     if (last) {
         int row[TL::TM][16];  // output row of each accumulator row, loaded once
@@ -1556,8 +1581,9 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
     // two loops rather than one with a branch: each keeps its own registers
     int64_t it = take_ticket(queue, ticket);
     while (it < n_dh) {
-        dh_item<T, FINE>(sh, (int)(it % n_rbv), (int)(it / n_rbv) * TL::BN, P > 1, p == P - 1, cb0, cb1, a.st, a.slot,
-                         a.cbp, nv, a.idx, a.Gn, a.E, a.perm, a.D, a.V, a.glab, a.labels, a.dh_acc, a.dH, a.smask);
+        dh_item<T, FINE>(sh, (int)(it % n_rbv), (int)(it / n_rbv) * TL::BN, P > 1, p == 0, p == P - 1, cb0, cb1, a.st,
+                         a.slot, a.cbp, nv, a.idx, a.Gn, a.E, a.perm, a.D, a.V, a.glab, a.labels, a.dh_acc, a.dH,
+                         a.smask);
         it = take_ticket(queue, ticket);
     }
     while (it < n_dh + n_de) {
@@ -1639,9 +1665,11 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     w.glab = c.take<float>((size_t)s.Np);
     w.lab = c.take<uint8_t>(nblk);
     w.st = c.take<uint8_t>(nblk);
-    w.csoft = c.take<uint8_t>((size_t)s.cbp);  // csoft, cnlab and cent follow st: one fill clears all four
+    w.csoft = c.take<uint8_t>((size_t)s.cbp);  // csoft, cnlab, cent, vneed and vact follow st: one fill clears them
     w.cnlab = c.take<int32_t>((size_t)s.cbp);
     w.cent = c.take<int32_t>((size_t)s.cbp);
+    w.vneed = c.take<int32_t>((size_t)s.n_vtiles);
+    w.vact = c.take<int32_t>((size_t)s.n_vtiles);
     w.slot = c.take<int32_t>(nblk);
     w.smask = c.take<uint16_t>(nblk);
     w.cpre = c.take<int32_t>((size_t)s.cbp + 1);
@@ -1692,13 +1720,9 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     }
     const size_t nblk = (size_t)s.n_rb * s.cbp;
     CCE_TRY(fill_bytes_zero(w.lab, nblk, st));
-    CCE_TRY(fill_bytes_zero(w.st, (size_t)(reinterpret_cast<char *>(w.cent + s.cbp) - reinterpret_cast<char *>(w.st)),
-                            st));  // st, csoft, cnlab, cent
-    if (s.max_passes > 1) {
-        const int64_t n = s.Np * (int64_t)D;  // D % 8 == 0: whole f32x4 groups
-        hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)ceil_div(n, 1024)), dim3(256), 0, st, w.dh_acc, n);
-        CCE_LAUNCHED();
-    }
+    // st, csoft, cnlab, cent, vneed, vact
+    CCE_TRY(fill_bytes_zero(
+        w.st, (size_t)(reinterpret_cast<char *>(w.vact + s.n_vtiles) - reinterpret_cast<char *>(w.st)), st));
     // Np % 4 == 0: whole f32x4 groups
     hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)ceil_div(s.Np, 1024)), dim3(256), 0, st, w.glab, s.Np);
     CCE_LAUNCHED();
@@ -1731,15 +1755,19 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     CCE_LAUNCHED();
     const int64_t ntile = (int64_t)s.n_rtiles * s.n_vtiles;
     hipLaunchKernelGGL(k_tile_class, dim3((unsigned)ceil_div(ntile, 256)), dim3(256), 0, st, w.nvalid, s.V,
-                       s.n_rtiles, s.n_vtiles, s.cbp, w.lab, tb, w.lmin, thr, w.tneed, w.csoft, w.cnlab, w.cent);
+                       s.n_rtiles, s.n_vtiles, s.cbp, w.lab, tb, w.lmin, thr, w.tneed, w.csoft, w.cnlab, w.cent,
+                       w.vneed, w.vact);
     CCE_LAUNCHED();
     // static columns need the label path (off for the full classifier
     // gradient) and a column's row blocks in one list
     const int CB = (int)ceil_div(V, kBlockVocab);
     const int static_ok = (!full_de && s.n_rb <= kListCap) ? 1 : 0;
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, w.tneed, s.n_rtiles, s.n_vtiles, s.cap, s.cap_eff,
-                       s.max_passes, w.plan, w.cum, w.act, w.tlist, CB, static_ok, w.csoft, w.cnlab, w.cent, w.cpre,
-                       w.slist, w.dlist);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, w.vneed, w.vact, s.n_vtiles, s.cap, s.cap_eff,
+                       s.max_passes, w.plan, w.cum, w.act, CB, static_ok, w.csoft, w.cnlab, w.cent, w.cpre, w.slist,
+                       w.dlist);
+    CCE_LAUNCHED();
+    hipLaunchKernelGGL(k_tile_list, dim3((unsigned)ceil_div(s.n_vtiles, 4)), dim3(256), 0, st, w.tneed, s.n_rtiles,
+                       s.n_vtiles, w.act, w.tlist);
     CCE_LAUNCHED();
 
     BwdArgs<T> a;

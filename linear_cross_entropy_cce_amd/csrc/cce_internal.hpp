@@ -118,12 +118,14 @@ struct BwdWs {
     uint8_t *csoft;    // [cbp] 1 where a block of the vocabulary block (column) may keep a softmax part
     int32_t *cnlab;    // [cbp] blocks of the column that hold a label
     int32_t *cent;     // [cbp] valid tokens whose label falls in the column
+    int32_t *vneed;    // [n_vtiles] blocks the vocabulary tile's tiles may keep
+    int32_t *vact;     // [n_vtiles] its tiles that may keep one
     int32_t *cpre;     // [cbp + 1] static columns (see k_plan) before each column
     int32_t *slist;    // [cbp] static columns, in order
     int32_t *dlist;    // [cbp] the other columns, in order
     uint8_t *tneed;    // [n_vtiles, n_rtiles] blocks the tile may keep (bits 0-2), recompute flag (bit 7)
     int64_t *cum;      // [n_vtiles] plan scratch: cumulative blocks
-    int32_t *act;      // [n_vtiles] plan scratch: active tiles before each vocabulary tile
+    int32_t *act;      // [n_vtiles] plan scratch: listed tiles before each vocabulary tile
     int32_t *tlist;    // [n_vtiles * n_rtiles] active tiles, vocabulary-tile-major
     int32_t *plan;     // [plan_ints] passes, active tiles, per-pass ranges and slot counters
     float *dh_acc;     // [Np, D] fp32 running dH across passes (max_passes > 1)

@@ -32,33 +32,61 @@ using TileFD = TileF;                              // tile of the DMA logit kern
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // ------------------------------------------------------------- compaction
-// One workgroup of 1024 threads; thread t owns a contiguous segment of rows.
+// One workgroup of 1024 threads.  Rows are read in batches of kBatch chunks
+// of 1024 consecutive rows (one row per thread and chunk, all loads of a
+// batch in flight at once); a valid row's position is the count of valid
+// rows before it: earlier batches, earlier chunks of the batch, earlier
+// waves of its chunk and earlier lanes of its wave (ballots).
 __global__ __launch_bounds__(1024) void k_compact(const int64_t *__restrict__ labels, int64_t N,
                                                   int64_t ignore_index, int32_t *__restrict__ idx,
                                                   int32_t *__restrict__ nvalid) {
-    __shared__ int wave_tot[16];
+    constexpr int kBatch = 8;
+    constexpr int kCounts = kBatch * 16;
+    __shared__ int cnt[kCounts];  // valid rows per (chunk, wave), then their exclusive prefix in that order
+    __shared__ int half, btotal;
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    const int64_t seg = (N + 1023) / 1024;
-    const int64_t r0 = t * seg;
-    const int64_t r1 = r0 + seg < N ? r0 + seg : N;
-    int cnt = 0;
-    for (int64_t r = r0; r < r1; ++r) cnt += labels[r] != ignore_index;
-    // inclusive scan of cnt inside the wave
-    int x = cnt;
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    int base = 0;  // valid rows before the batch (uniform)
+    for (int64_t b0 = 0; b0 < N; b0 += (int64_t)kBatch * 1024) {
+        bool v[kBatch];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
+        for (int k = 0; k < kBatch; ++k) {
+            const int64_t r = b0 + (int64_t)k * 1024 + t;
+            v[k] = r < N && labels[r] != ignore_index;
+        }
+        uint64_t bal[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            bal[k] = __ballot(v[k]);
+            if (lane == 0) cnt[k * 16 + wave] = __popcll(bal[k]);
+        }
+        __syncthreads();
+        int c = 0, x = 0;
+        if (t < kCounts) {  // two waves: inclusive scan of the counts within each wave
+            c = cnt[t];
+            x = c;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o, 64);
+                if (lane >= o) x += y;
+            }
+            if (t == 63) half = x;
+        }
+        __syncthreads();
+        if (t < kCounts) {
+            const int incl = x + (t >= 64 ? half : 0);
+            cnt[t] = incl - c;
+            if (t == kCounts - 1) btotal = incl;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+            if (v[k]) idx[base + cnt[k * 16 + wave] + __popcll(bal[k] & below)] = (int32_t)(b0 + (int64_t)k * 1024 + t);
+        base += btotal;
+        __syncthreads();  // cnt, half and btotal are rewritten by the next batch
     }
-    if (lane == 63) wave_tot[wave] = x;
-    __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += wave_tot[w];
-    int pos = base + x - cnt;
-    for (int64_t r = r0; r < r1; ++r)
-        if (labels[r] != ignore_index) idx[pos++] = (int32_t)r;
-    if (t == 1023) *nvalid = base + x;
+    if (t == 0) *nvalid = base;
 }
 
 // -------------------------------------------------------------- label check
