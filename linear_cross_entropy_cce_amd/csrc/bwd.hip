@@ -129,6 +129,7 @@ struct BwdArgs {
     uint16_t *smask;  // bit 4 i + j: sub-tile (vocabulary rows 32 i.., tokens 32 j..) of a kept block may be nonzero
     const int32_t *cpre, *slist, *dlist;  // column lists of k_plan
     const int32_t *cent;                  // label entries per column
+    int CB;                               // vocabulary blocks
     int64_t *stats;
     float *dh_acc;
     Rows2<T> dE;  // same layout as E
@@ -386,14 +387,17 @@ __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ 
 // its dE rows come from the label entries (or are zero) for all features at
 // once, as the per-feature-tile items would write them.
 // slist holds the static columns in order, dlist the others, and cpre[cb]
-// the static columns before cb (cpre[CB] all of them).
+// the static columns before cb (cpre[CB] all of them).  The label-only
+// blocks of static columns (their label blocks) are counted into stats[1]
+// here; the tile epilogue counts the others.
 __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ vneed, const int32_t *__restrict__ vact,
                                                int n_vt, int64_t cap, int64_t cap_eff, int max_passes,
                                                int32_t *__restrict__ plan, int64_t *__restrict__ cum,
                                                int32_t *__restrict__ act, int CB, int static_ok,
                                                const uint8_t *__restrict__ csoft, const int32_t *__restrict__ cnlab,
                                                const int32_t *__restrict__ cent, int32_t *__restrict__ cpre,
-                                               int32_t *__restrict__ slist, int32_t *__restrict__ dlist) {
+                                               int32_t *__restrict__ slist, int32_t *__restrict__ dlist,
+                                               int64_t *__restrict__ stats) {
     __shared__ int64_t wsum[16];
     __shared__ int32_t wact[16];
     __shared__ int32_t wcol[16];
@@ -461,9 +465,11 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ vneed
 
     if (t == 0) carry_c = 0;
     __syncthreads();
+    int64_t n_static_lab = 0;
     for (int base = 0; base < CB; base += 1024) {
         const int cb = base + t;
         const int is_s = (cb < CB && static_ok && !csoft[cb] && label_path_ok(cnlab[cb], cent[cb])) ? 1 : 0;
+        if (is_s) n_static_lab += cnlab[cb];
         int x = is_s;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -485,24 +491,78 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ vneed
         __syncthreads();
     }
     if (t == 0) cpre[CB] = carry_c;
+    if (stats) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) n_static_lab += __shfl_xor(n_static_lab, o, 64);
+        if (lane == 0 && n_static_lab)
+            atomicAdd(reinterpret_cast<unsigned long long *>(stats + 1), (unsigned long long)n_static_lab);
+    }
 }
 
 // The tile list: the listed tiles (that may keep a block) of vocabulary tile
 // vt at act[vt] onwards, token tiles in order.  One wave per vocabulary tile.
+// A tile that recomputes nothing and whose label blocks all lie in static
+// columns gets -1 instead (k_label_static writes what it would have).
 __global__ __launch_bounds__(256) void k_tile_list(const uint8_t *__restrict__ tneed, int n_rt, int n_vt,
-                                                   const int32_t *__restrict__ act, int32_t *__restrict__ tlist) {
+                                                   const int32_t *__restrict__ act, const uint8_t *__restrict__ lab,
+                                                   int cbp, const int32_t *__restrict__ cpre, int CB,
+                                                   int32_t *__restrict__ tlist) {
     const int lane = threadIdx.x & 63;
     const int vt = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (vt >= n_vt) return;  // wave-uniform
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
     const uint8_t *row = tneed + (int64_t)vt * n_rt;
+    bool col_static[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int cb = 2 * vt + h;
+        col_static[h] = cb < CB && cpre[cb + 1] - cpre[cb] == 1;
+    }
     int pos = act[vt];
     for (int r0 = 0; r0 < n_rt; r0 += 64) {
         const int rt = r0 + lane;
-        const bool on = rt < n_rt && (row[rt] & 7) != 0;
+        const int tn8 = rt < n_rt ? row[rt] : 0;
+        const bool on = (tn8 & 7) != 0;
+        bool skip = false;
+        if (on && !(tn8 & 0x80)) {  // only label blocks: skip when every one is in a static column
+            skip = true;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    if (lab[(int64_t)(2 * rt + j) * cbp + 2 * vt + h] && !col_static[h]) skip = false;
+        }
         const uint64_t bal = __ballot(on);
-        if (on) tlist[pos + __popcll(bal & below)] = vt * n_rt + rt;
+        if (on) tlist[pos + __popcll(bal & below)] = skip ? -1 : vt * n_rt + rt;
         pos += __popcll(bal);
+    }
+}
+
+// The label-only blocks of static columns (see k_plan), which no listed
+// tile holds unless the tile's other column needs it: per valid token whose
+// label falls in a static column, the block's status (2, label only) and the
+// label entry's fp32 gradient dloss (p - 1), p from the forward's label logit
+// (the values the tile epilogue writes for a block it does not recompute).
+__global__ __launch_bounds__(256) void k_label_static(const int64_t *__restrict__ labels,
+                                                      const int32_t *__restrict__ idx,
+                                                      const int32_t *__restrict__ nvalid_p,
+                                                      const int32_t *__restrict__ inv_perm, int64_t V, int cbp,
+                                                      const int32_t *__restrict__ cpre, const float *__restrict__ lse,
+                                                      const float *__restrict__ dloss, const float *__restrict__ zlab,
+                                                      uint8_t *__restrict__ st, float *__restrict__ glab) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= *nvalid_p) return;
+    const int64_t row = idx[t];
+    const int64_t y = labels[row];
+    if (y < 0 || y >= V) return;  // not a valid label: undefined by contract
+    const int64_t pos = inv_perm ? inv_perm[y] : y;
+    const int cb = (int)(pos / kBlockVocab);
+    if (cpre[cb + 1] - cpre[cb] != 1) return;  // not a static column
+    st[(t / kBlockRows) * cbp + cb] = 2;       // (every token of the block stores 2)
+    const float dl = dloss[row];
+    if (dl != 0.f) {
+        const float pl = __builtin_amdgcn_exp2f((zlab[row] - lse[row]) * kLog2e);
+        glab[t] = dl * (pl - 1.f);
     }
 }
 
@@ -530,7 +590,7 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
                                            int64_t cap, int32_t *__restrict__ counter, uint8_t *__restrict__ st,
                                            int32_t *__restrict__ slotm, int64_t *__restrict__ stats, int *qflag,
                                            int *qstat, int *qslot, int full_de, int qmask, int fine,
-                                           uint16_t *__restrict__ smask) {
+                                           uint16_t *__restrict__ smask, const int32_t *__restrict__ cpre, int CB) {
     // qflag[0..3]: per block, bit 0 = some non-label p >= eps, bit 1 = a label
     // entry; qflag[4..7]: the 32 x 32 sub-tiles (bit 4 i + j: vocabulary
     // rows 32 i.., tokens 32 j.. of the block) with a non-label p >= eps;
@@ -648,7 +708,10 @@ __device__ __forceinline__ void g_epilogue(f32x16 (&acc)[TL::TM][TL::TN], int to
                 (uint16_t)(sv == 1 ? (fine ? (live16 | lab16) : 0xFFFF) : (sv == 2 ? lab16 : 0xFFFF));
         }
         if (stats) {
-            if (sv == 1 || sv == 2) atomicAdd(reinterpret_cast<unsigned long long *>(stats + (sv == 1 ? 0 : 1)), 1ull);
+            // (the label-only blocks of static columns are counted by k_plan)
+            const bool col_static = cb < CB && cpre[cb + 1] - cpre[cb] == 1;
+            if (sv == 1 || (sv == 2 && !col_static))
+                atomicAdd(reinterpret_cast<unsigned long long *>(stats + (sv == 1 ? 0 : 1)), 1ull);
             // 32 x 32 sub-tiles whose softmax part is kept (all 16 of a kept block without the fine filter)
             if (sv == 1)
                 atomicAdd(reinterpret_cast<unsigned long long *>(stats + 6),
@@ -822,6 +885,7 @@ __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int
             const int i = pb + take_ticket(queues + part, ticket);
             if (i >= pe) break;
             const int tile = a.tlist[i];
+            if (tile < 0) continue;  // a tile left to k_label_static
             const int vt = tile / a.n_rt, rt = tile % a.n_rt;
             const int tn8 = a.tneed[tile];
             const bool rec = (tn8 & 0x80) != 0;
@@ -837,11 +901,11 @@ __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int
                 __syncthreads();
                 g_epilogue<T, TL, true>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
                                         a.lse, a.dloss, a.zlab, a.glab, a.Gt, a.Gn, a.cap_take, pv.counter + p, a.st, a.slot, a.stats,
-                                        qflag, qstat, qslot, a.full_de, qmask, a.fine, a.smask);
+                                        qflag, qstat, qslot, a.full_de, qmask, a.fine, a.smask, a.cpre, a.CB);
             } else {
                 g_epilogue<T, TL, false>(acc, tok0, nv, p0, a.V, rt, vt, a.cbp, a.eps, a.idx, a.inv_perm, a.labels,
                                          a.lse, a.dloss, a.zlab, a.glab, a.Gt, a.Gn, a.cap_take, pv.counter + p, a.st, a.slot, a.stats,
-                                         qflag, qstat, qslot, a.full_de, 0, a.fine, a.smask);
+                                         qflag, qstat, qslot, a.full_de, 0, a.fine, a.smask, a.cpre, a.CB);
             }
         }
     }
@@ -1764,11 +1828,17 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     const int static_ok = (!full_de && s.n_rb <= kListCap) ? 1 : 0;
     hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, w.vneed, w.vact, s.n_vtiles, s.cap, s.cap_eff,
                        s.max_passes, w.plan, w.cum, w.act, CB, static_ok, w.csoft, w.cnlab, w.cent, w.cpre, w.slist,
-                       w.dlist);
+                       w.dlist, stats);
     CCE_LAUNCHED();
     hipLaunchKernelGGL(k_tile_list, dim3((unsigned)ceil_div(s.n_vtiles, 4)), dim3(256), 0, st, w.tneed, s.n_rtiles,
-                       s.n_vtiles, w.act, w.tlist);
+                       s.n_vtiles, w.act, w.lab, s.cbp, w.cpre, CB, w.tlist);
     CCE_LAUNCHED();
+    if (static_ok && tb) {  // (without the table no column is static)
+        hipLaunchKernelGGL(k_label_static, dim3((unsigned)ceil_div(s.N, 256)), dim3(256), 0, st, labels, w.idx,
+                           w.nvalid, invp, s.V, s.cbp, w.cpre, lse, dloss, tb + block_max_blocks(s.N, s.V), w.st,
+                           w.glab);
+        CCE_LAUNCHED();
+    }
 
     BwdArgs<T> a;
     a.plan = w.plan;
@@ -1808,6 +1878,7 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     a.slist = w.slist;
     a.dlist = w.dlist;
     a.cent = w.cent;
+    a.CB = CB;
     a.fine = (flags & CCE_BWD_FINE_FILTER) ? 1 : 0;
     a.stats = stats;
     a.dh_acc = w.dh_acc;
