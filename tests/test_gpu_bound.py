@@ -143,3 +143,40 @@ def test_full_size_skip_is_bit_identical(k, sort):
     assert np.array_equal(st_a[:4], st_b[:4])
     G.say(f"  recomputed blocks {st_a[4]} of {st_a[2]} (kept {st_a[0]}, label-only {st_a[1]})")
     assert st_a[4] < st_a[2] // 4
+
+
+
+def _label_only_peaked():
+    """The Gemma-head recipe at D = 256 with peak 3.0: no non-label p reaches
+    2^-12 and the forward's bound rules out nearly every block, yet the label
+    entries' gradients dloss (p_y - 1) are far from zero (median 1 - p_y =
+    2.8e-3, resolved by float32)."""
+    return inputs.make_inputs(700, 256, 9000, dtype="bf16", e_std=0.02, h_kind="peaked", label_kind="zipf", seed=7,
+                              eps=2.0 ** -12, name="gemma-recipe-label-only", peak_scale=3.0)
+
+
+@pytest.mark.parametrize("sort", [False, True])
+def test_skip_is_bit_identical_label_only(sort):
+    """With the table, vocabulary blocks that can only keep label-only blocks
+    take the static path (status and label gradients per token from the
+    forward's label logits, dE rows per whole block by the label-path rule);
+    without it every block is recomputed and decided by the tile epilogue.
+    The bits must agree, with label gradients that are not zero."""
+    x = _label_only_peaked()
+    eps = 2.0 ** -12
+    G.say(f"bound skip bit identity, label-only regime N={x.N} D={x.D} V={x.V} sort={sort}")
+    dl = G.random_dloss(x, seed=11)
+    a = G.run_gpu(x, dl, eps=eps, bound=True, sort=sort)
+    b = G.run_gpu(x, dl, eps=eps, bound=False, sort=sort)
+    for key in ("loss", "lse", "dH", "dE"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.array_equal(a["stats"][:4], b["stats"][:4])
+    assert a["stats"][0] == 0 and a["stats"][1] > 0, a["stats"]  # only label-only blocks kept
+    assert a["stats"][4] < b["stats"][4] // 4, (a["stats"], b["stats"])  # the table ruled out most blocks
+    if not sort:
+        # against the oracle's filtered gradient (label entries only here)
+        fH, fE, kept, aH, aE = G.oracle_filtered(x, dl, eps, "label-only")
+        assert not kept.any()
+        LH, LE = G.label_term(x, dl)
+        G.assert_grad_filtered("dH", a["dH"], fH, aH, LH)
+        G.assert_grad_filtered("dE", a["dE"], fE, aE, LE)
