@@ -1301,7 +1301,13 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
                                         const T *__restrict__ Ht, int64_t ldh, const int32_t *__restrict__ perm,
                                         int D, int V, Rows2<T> dE, int pre_n, const uint16_t *__restrict__ smask) {
     using TL = TileG;
-    using DE = DmaEngine<T, TL>;
+    // 128-byte stages (two per row block of bf16), one in flight: half the
+    // loop iterations and list lookups of 64-byte stages in the same LDS; the
+    // fine filter keeps 64-byte stages (32 tokens, one sub-tile column, per
+    // stage half)
+    constexpr bool kWide = !FINE;
+    using DE = DmaEngine<T, TL, kWide ? 128 : 64, kWide ? 2 : 4>;
+    static_assert(DE::kLdsChunks <= GradLds<T>::kStageChunks, "stages fit the shared stage buffer");
     constexpr int kBlockBytes = kBlockRows * (int)sizeof(T);  // K bytes of one row block
     constexpr int kSpb = kBlockBytes / DE::kStageBytes;       // stages per row block
     constexpr int64_t kStoreBytes = (int64_t)kBlockElems * sizeof(T);
