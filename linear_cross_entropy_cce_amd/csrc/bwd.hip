@@ -922,14 +922,18 @@ __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int
 // directly.  B rows are kRowB bytes with chunk c of row r stored at
 // c ^ 4 (r & 3), so the 4 rows one transposed read touches are 64 bytes apart
 // in the bank space.
-template <typename T>
+template <typename T, bool kWide = false>
 struct DhEngine {
     using TL = TileG;
-    static constexpr int kKv = sizeof(T) == 2 ? 32 : 16;  // vocabulary entries per stage
+    // vocabulary entries per stage: 64 bytes of a stored block row, or 128
+    // bytes (kWide: half the stages, one in flight, in the same LDS)
+    static constexpr int kKv = (sizeof(T) == 2 ? 32 : 16) * (kWide ? 2 : 1);
     static constexpr int kSpb = kBlockVocab / kKv;        // stages per block
-    static constexpr int kStages = 4, kDepth = 3;
-    static constexpr int kStageBytes = 64;                // A row bytes per stage
-    static constexpr int kStageA = TL::BM * 4;            // chunks
+    static constexpr int kStages = kWide ? 2 : 4, kDepth = kStages - 1;
+    static constexpr int kStageBytes = kKv * (int)sizeof(T);  // A row bytes per stage
+    static constexpr int kCprA = kStageBytes / 16;            // A chunks per row
+    static constexpr int kSlices = kKv / (sizeof(T) == 2 ? 16 : 8);  // MFMA K-slices per stage
+    static constexpr int kStageA = TL::BM * kCprA;        // chunks
     static constexpr int kRowB = TL::BN * (int)sizeof(T); // bytes of one B row (256 features)
     static constexpr int kCprB = kRowB / 16;
     static constexpr int kStageB = kKv * kCprB;
@@ -938,20 +942,22 @@ struct DhEngine {
     static constexpr int NIA = kStageA / 64 / TL::kWaves;
     static constexpr int NIB = kStageB / 64 / TL::kWaves;
     static constexpr int NI = NIA + NIB;
-    static_assert(NIA == 1 && NIB == 2, "stage split");
-    static_assert(kStageBytes == kKv * (int)sizeof(T), "A stage = kKv entries");
+    static_assert(NIA * 64 * TL::kWaves == kStageA && NIB * 64 * TL::kWaves == kStageB, "stage split");
 
     u32x4 *lds;
     uint32_t lds0;      // LDS byte address of the stages (wave-uniform)
-    int a_off;          // this lane's A source offset within a stored block (row + swizzled chunk)
+    int a_off[NIA];     // this lane's A source offsets within a stored block (row + swizzled chunk)
     int b_row[NIB];     // B row (vocabulary entry within the stage) this lane feeds
     int b_off[NIB];     // byte offset of its chunk within an E row (clamped to the last chunk < D)
 
     __device__ __forceinline__ DhEngine(u32x4 *l, int d0, int D, int tid) : lds(l), lds0(lds_addr(l)) {
         const int w = tid >> 6, lane = tid & 63;
-        const int sa = 64 * w + lane;
-        const int ra = sa / 4;
-        a_off = ra * kBlockVocab * (int)sizeof(T) + 16 * ((sa & 3) ^ dma_swz<64>(ra));
+#pragma unroll
+        for (int j = 0; j < NIA; ++j) {
+            const int sa = 64 * (j * TL::kWaves + w) + lane;
+            const int ra = sa / kCprA;
+            a_off[j] = ra * kBlockVocab * (int)sizeof(T) + 16 * ((sa % kCprA) ^ dma_swz<kStageBytes>(ra));
+        }
         constexpr int kElemsPerChunk = 16 / (int)sizeof(T);
 #pragma unroll
         for (int j = 0; j < NIB; ++j) {
@@ -976,7 +982,10 @@ struct DhEngine {
                                           const int32_t *perm, int pos0, int kq, int V) const {
         const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const uint32_t st = lds0 + (uint32_t)(buf * kStage) * 16u;
-        dma16_at(reinterpret_cast<const char *>(Gn + slot * kBlockElems) + a_off + kq * kStageBytes, st + 1024u * w);
+#pragma unroll
+        for (int j = 0; j < NIA; ++j)
+            dma16_at(reinterpret_cast<const char *>(Gn + slot * kBlockElems) + a_off[j] + kq * kStageBytes,
+                     st + 1024u * (j * TL::kWaves + w));
         const int base = __builtin_amdgcn_readfirstlane(pos0 + kq * kKv);
 #pragma unroll
         for (int j = 0; j < NIB; ++j) {
@@ -997,8 +1006,12 @@ struct DhEngine {
     }
 
     __device__ __forceinline__ void wait_stage(int ahead) const {
-        if (ahead >= 2) { wait_vmcnt<2 * NI>(); block_sync(); return; }
-        if (ahead >= 1) { wait_vmcnt<NI>(); block_sync(); return; }
+        if constexpr (kDepth >= 3) {
+            if (ahead >= 2) { wait_vmcnt<2 * NI>(); block_sync(); return; }
+        }
+        if constexpr (kDepth >= 2) {
+            if (ahead >= 1) { wait_vmcnt<NI>(); block_sync(); return; }
+        }
         wait_vmcnt<0>();
         block_sync();
     }
@@ -1012,12 +1025,12 @@ struct DhEngine {
         const u32x4 *A = lds + buf * kStage;
         const char *Bb = reinterpret_cast<const char *>(A + kStageA);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < kSlices; ++kk) {
             const int c = 2 * kk + (lane >> 5);
             u32x4 fa[TL::TM], fb[TL::TN];
 #pragma unroll
             for (int tm = 0; tm < TL::TM; ++tm)
-                if ((rows >> tm) & 1) fa[tm] = A[dma_slot<64>(ra0 + tm * 32, c)];
+                if ((rows >> tm) & 1) fa[tm] = A[dma_slot<kStageBytes>(ra0 + tm * 32, c)];
 #pragma unroll
             for (int tn = 0; tn < TL::TN; ++tn) {
                 const int n0 = nb0 + tn * 32;
@@ -1061,6 +1074,7 @@ struct GradLds {
     static constexpr int kStageChunks = DmaEngine<T, TileG>::kLdsChunks > DhEngine<T>::kLdsChunks
                                             ? DmaEngine<T, TileG>::kLdsChunks
                                             : DhEngine<T>::kLdsChunks;
+    static_assert(DhEngine<T, true>::kLdsChunks <= kStageChunks, "wide dH stages fit the stage buffer");
     u32x4 stages[kStageChunks];
     int list[kListCap];
     int lslot[kListCap];
@@ -1478,7 +1492,7 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
                                         const int64_t *__restrict__ labels, float *__restrict__ dh_acc,
                                         T *__restrict__ dH, const uint16_t *__restrict__ smask) {
     using TL = TileG;
-    using DH = DhEngine<T>;
+    using DH = DhEngine<T, !FINE>;  // the fine filter's sub-tile rows need 32-entry stages
     const int tok0 = rb * TL::BM;
     const int tid = opaque_tid();  // per-item lane arithmetic is redone per item, not held in registers
 
