@@ -83,6 +83,7 @@ struct FwdWs {
     int32_t *inv_perm; // [V] processing position of each vocabulary id (with a permutation and the table)
     float *part_m;     // [kFwdMaxGroups + n_rtiles, kTileRows] per segment: running max (log2 units)
     float *part_s;     // [kFwdMaxGroups + n_rtiles, kTileRows] per segment: sum of 2^(z log2e - m)
+    float *zy;         // [N] label logit of each valid row, by compacted position
 };
 FwdWs fwd_ws(void *ws, const FwdShape &s, size_t *bytes);
 

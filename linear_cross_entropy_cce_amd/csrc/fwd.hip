@@ -1,11 +1,15 @@
 // Forward of the fused classifier-head + cross-entropy on gfx950.
 //
 //  k_compact      valid-row compaction (rows whose label is not ignore_index)
-//  k_fwd          logit tiles Z^T = E_tile * H_tile^T on bf16/fp32 MFMA, kept in
-//                 registers; per token and vocabulary range an online running
-//                 max / sum-exp (log2 domain); partials written per segment
+//  k_label_dot    label logit <h_i, e_{y_i}> of each valid row (the indexed matmul)
+//  k_fwd4         logit tiles Z^T = E_tile * H_tile^T on bf16 MFMA, kept in
+//                 registers (4 waves, scheduled K loop); per token and
+//                 vocabulary range an online running max / sum-exp (log2
+//                 domain); partials written per segment
+//  k_fwd_dma      the same on 8 waves (fp32, and a build without k_fwd4)
+//  k_fwd          the same with VGPR-staged operands (D * size not a multiple of 128)
 //  k_merge        per row: merge of the segment partials in vocabulary order
-//                 -> lse; label logit <h_i, e_{y_i}> (the indexed matmul) -> loss
+//                 -> lse; lse - label logit -> loss
 //
 // The method: cross-entropy needs only the correct-token logit and the
 // log-sum-exp over the vocabulary, computed blockwise on chip while streaming
@@ -19,6 +23,7 @@
 // independent of scheduling.
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "cce_device.hpp"
 #include "cce_internal.hpp"
@@ -30,6 +35,12 @@ using TileF4 = Tile<kTileVocab, kTileRows, 2, 2>;  // the same tile on 4 waves o
 using TileFD = TileF;                              // tile of the DMA logit kernels
 
 constexpr float kNegInf = -__builtin_huge_valf();
+
+// k_fwd4 serves bf16 whenever the DMA path applies; building with
+// -DCCE_FWD4=0 puts k_fwd_dma there instead (for comparisons).
+#ifndef CCE_FWD4
+#define CCE_FWD4 1
+#endif
 
 // ------------------------------------------------------------- compaction
 // One workgroup of 1024 threads.  Rows are read in batches of kBatch chunks
@@ -558,7 +569,421 @@ __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
     }
 }
 
-// ------------------------------------------------------ merge + label gather
+// ------------------------------------- bf16 forward on 4 waves, scheduled K loop
+// The same tiles, partition, partials and block-max table as k_fwd_dma, on 4
+// waves of 128 vocabulary rows x 128 tokens (wave w: rows 128 (w % 2), tokens
+// 128 (w / 2)).  Per 128 bytes of K the waves read 128 KB of operand
+// fragments from LDS instead of the 8-wave layout's 192 KB.  With one wave
+// per SIMD nothing else hides the LDS latency, the barrier or the DMA issue
+// (a wave whose next instruction is a DMA that the memory pipeline cannot
+// take yet stalls, MFMAs included), so the K loop is written as assembly
+// blocks whose order is fixed here.
+//
+// K is streamed in half-stages of 64 bytes per row (two K-slices of 32 bytes,
+// 16 MFMAs of 32x32x16 each) through 4 LDS buffers of 32 KB (A rows, then B
+// rows, 64-byte rows with the dma_swz<64> chunk swizzle).  Half-stage h sits
+// in buffer h % 4.  Its slice a reads slice b's fragments under its MFMAs;
+// then every wave waits for its DMA of half-stage h + 1 and meets the others
+// at a barrier (h + 1 is in LDS, and nobody reads buffer h % 4 any more);
+// slice b reads h + 1's first fragments (except in a tile's last half-stage:
+// those are read after the tile's epilogue, so that they are not live across
+// it).  The DMA of half-stage h + 4 into buffer h % 4 is spread evenly: its
+// A rows (4 instructions per wave) under slice b of h, its B rows under slice
+// a of h + 1, one instruction per 4 MFMAs.  A tile's first half-stage starts
+// its MFMAs from zero (src2 = 0), so no accumulator is cleared.
+//
+// Fragments: P holds a half-stage's slice-a fragments on entry (A rows of
+// blocks tm = 0-3 in P0-P3, B rows of tn = 0-3 in P4-P7), Q is scratch.
+// Hazards the blocks respect themselves: each slice waits for its own LDS
+// reads before the next slice's MFMAs use them; a slice uses each accumulator
+// once, 16 MFMAs from its next use; the results are read by vector
+// instructions only after acc_settle's wait states.
+#define CCE_MF(c, a, b) "v_mfma_f32_32x32x16_bf16 %[" #c "], %[" #a "], %[" #b "], %[" #c "]\n\t"
+#define CCE_MFZ(c, a, b) "v_mfma_f32_32x32x16_bf16 %[" #c "], %[" #a "], %[" #b "], 0\n\t"
+#define CCE_RD(n, r, off) "ds_read_b128 %[" #n "], %[" #r "] offset:" #off "\n\t"
+// LDS byte addresses of a slice's A and B fragment rows: wave base + lane offset.
+#define CCE_ADDR(x, a, b) "v_add_u32 %[ra], %[" #a "], %[" #x "]\n\tv_add_u32 %[rb], %[" #b "], %[" #x "]\n\t"
+// One DMA instruction: row pointer + the half-stage's K offset, to LDS m0 = mb + moff.
+#define CCE_DMA(p, moff, t, kb, mb)                                                                         \
+    "v_lshl_add_u64 %[" #t "], %[" #p "], 0, %[" #kb "]\n\ts_add_u32 m0, %[" #mb "], " #moff                 \
+    "\n\tglobal_load_lds_dwordx4 %[" #t "], off\n\t"
+#define CCE_WAIT_LDS "s_waitcnt lgkmcnt(0)\n\t"
+
+// A slice: 16 MFMAs on fragments C (tm-major), the next slice's 8 reads into
+// N after the first 8, and 4 DMA instructions (row pointers P0-P3 at LDS
+// offsets O0-O3 from mb).
+#define CCE_SLICE(MF, C, N, P0, P1, P2, P3, KB, MB, O0, O1, O2, O3)                                         \
+    MF(c00, C##0, C##4) CCE_RD(N##0, ra, 0) MF(c01, C##0, C##5) CCE_RD(N##1, ra, 2048)                      \
+    CCE_DMA(P0, O0, t0, KB, MB) MF(c02, C##0, C##6) CCE_RD(N##2, ra, 4096) MF(c03, C##0, C##7)              \
+    CCE_RD(N##3, ra, 6144) MF(c10, C##1, C##4) CCE_RD(N##4, rb, 0) MF(c11, C##1, C##5) CCE_RD(N##5, rb, 2048) \
+    CCE_DMA(P1, O1, t1, KB, MB) MF(c12, C##1, C##6) CCE_RD(N##6, rb, 4096) MF(c13, C##1, C##7)              \
+    CCE_RD(N##7, rb, 6144) MF(c20, C##2, C##4) MF(c21, C##2, C##5) CCE_DMA(P2, O2, t0, KB, MB)              \
+    MF(c22, C##2, C##6) MF(c23, C##2, C##7) MF(c30, C##3, C##4) MF(c31, C##3, C##5)                        \
+    CCE_DMA(P3, O3, t1, KB, MB) MF(c32, C##3, C##6) MF(c33, C##3, C##7) CCE_WAIT_LDS
+// ... without the reads.
+#define CCE_SLICE_NR(MF, C, P0, P1, P2, P3, KB, MB, O0, O1, O2, O3)                                         \
+    MF(c00, C##0, C##4) MF(c01, C##0, C##5) CCE_DMA(P0, O0, t0, KB, MB) MF(c02, C##0, C##6)                 \
+    MF(c03, C##0, C##7) MF(c10, C##1, C##4) MF(c11, C##1, C##5) CCE_DMA(P1, O1, t1, KB, MB)                 \
+    MF(c12, C##1, C##6) MF(c13, C##1, C##7) MF(c20, C##2, C##4) MF(c21, C##2, C##5)                        \
+    CCE_DMA(P2, O2, t0, KB, MB) MF(c22, C##2, C##6) MF(c23, C##2, C##7) MF(c30, C##3, C##4)                 \
+    MF(c31, C##3, C##5) CCE_DMA(P3, O3, t1, KB, MB) MF(c32, C##3, C##6) MF(c33, C##3, C##7)
+
+// A half-stage: slice a (MF0: from zero or accumulating) with the pending B
+// rows' DMA, the wait for half-stage h + 1 (the 16 DMA instructions issued
+// after its last one may still be in flight) and the barrier, then TAIL =
+// slice b with the A rows' DMA of half-stage h + 4.
+#define CCE_HALF(MF0, TAIL)                                                                                 \
+    CCE_ADDR(x1, sa, sb) CCE_SLICE(MF0, p, q, pb0, pb1, pb2, pb3, kbb, mbb, 16384, 20480, 24576, 28672)    \
+    "s_waitcnt vmcnt(16)\n\ts_barrier\n\t" TAIL
+#define CCE_TAIL_NEXT CCE_ADDR(x0, na, nb) CCE_SLICE(CCE_MF, q, p, pa0, pa1, pa2, pa3, kba, mba, 0, 4096, 8192, 12288)
+#define CCE_TAIL_LAST CCE_SLICE_NR(CCE_MF, q, pa0, pa1, pa2, pa3, kba, mba, 0, 4096, 8192, 12288)
+// A whole half-stage's DMA (prologue), and its A rows only.
+#define CCE_DMA_A                                                                                           \
+    CCE_DMA(pa0, 0, t0, kba, mba) CCE_DMA(pa1, 4096, t1, kba, mba) CCE_DMA(pa2, 8192, t0, kba, mba)         \
+    CCE_DMA(pa3, 12288, t1, kba, mba)
+#define CCE_DMA_B                                                                                           \
+    CCE_DMA(pb0, 16384, t0, kba, mba) CCE_DMA(pb1, 20480, t1, kba, mba) CCE_DMA(pb2, 24576, t0, kba, mba)   \
+    CCE_DMA(pb3, 28672, t1, kba, mba)
+#define CCE_READ_ONLY                                                                                       \
+    CCE_ADDR(x0, na, nb) CCE_RD(p0, ra, 0) CCE_RD(p1, ra, 2048) CCE_RD(p2, ra, 4096) CCE_RD(p3, ra, 6144)   \
+    CCE_RD(p4, rb, 0) CCE_RD(p5, rb, 2048) CCE_RD(p6, rb, 4096) CCE_RD(p7, rb, 6144) CCE_WAIT_LDS
+
+#define CCE_ACC(K, acc)                                                                                     \
+    [c00] K(acc[0][0]), [c01] K(acc[0][1]), [c02] K(acc[0][2]), [c03] K(acc[0][3]), [c10] K(acc[1][0]),     \
+        [c11] K(acc[1][1]), [c12] K(acc[1][2]), [c13] K(acc[1][3]), [c20] K(acc[2][0]), [c21] K(acc[2][1]), \
+        [c22] K(acc[2][2]), [c23] K(acc[2][3]), [c30] K(acc[3][0]), [c31] K(acc[3][1]), [c32] K(acc[3][2]), \
+        [c33] K(acc[3][3])
+#define CCE_FRAGS(n, K, f)                                                                                  \
+    [n##0] K(f[0]), [n##1] K(f[1]), [n##2] K(f[2]), [n##3] K(f[3]), [n##4] K(f[4]), [n##5] K(f[5]),         \
+        [n##6] K(f[6]), [n##7] K(f[7])
+#define CCE_PTRS(pa, pb)                                                                                    \
+    [pa0] "v"(pa[0]), [pa1] "v"(pa[1]), [pa2] "v"(pa[2]), [pa3] "v"(pa[3]), [pb0] "v"(pb[0]),               \
+        [pb1] "v"(pb[1]), [pb2] "v"(pb[2]), [pb3] "v"(pb[3])
+#define CCE_K_INOUT_A(x) "+a"(x)
+#define CCE_K_OUT_A(x) "=a"(x)
+#define CCE_K_INOUT_V(x) "+v"(x)
+#define CCE_K_TMP_V(x) "=&v"(x)
+
+typedef f32x16 Acc4[4][4];
+
+// The scalar operands of a half-stage.
+struct F4Half {
+    uint32_t sa, sb;    // LDS byte address of this wave's A / B fragment rows in the half-stage's buffer
+    uint32_t na, nb;    // the same in the next half-stage's buffer
+    uint32_t mba;       // LDS byte address of the buffer the A rows' DMA fills, plus 1024 * wave
+    uint32_t mbb;       // the same for the pending B rows' DMA
+    uint64_t kba, kbb;  // K byte offsets of those two DMAs
+};
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+#define CCE_F4_HALF_FN(name, ACCK, MF0, TAIL)                                                              \
+    __device__ __forceinline__ void name(Acc4 &acc, u32x4 (&P)[8], const uint32_t (&x)[2], const F4Half &g, \
+                                         const char *const (&pa)[4], const char *const (&pb)[4]) {           \
+        u32x4 Q[8];                                                                                         \
+        uint32_t ra, rb;                                                                                    \
+        uint64_t t0, t1;                                                                                    \
+        asm volatile(CCE_HALF(MF0, TAIL)                                                                    \
+                     : CCE_ACC(ACCK, acc), CCE_FRAGS(p, CCE_K_INOUT_V, P), CCE_FRAGS(q, CCE_K_TMP_V, Q),    \
+                       [ra] "=&v"(ra), [rb] "=&v"(rb), [t0] "=&v"(t0), [t1] "=&v"(t1)                       \
+                     : [x0] "v"(x[0]), [x1] "v"(x[1]), [sa] "s"(g.sa), [sb] "s"(g.sb), [na] "s"(g.na),       \
+                       [nb] "s"(g.nb), [mba] "s"(g.mba), [mbb] "s"(g.mbb), [kba] "s"(g.kba), [kbb] "s"(g.kbb), \
+                       CCE_PTRS(pa, pb)                                                                     \
+                     : "memory", "m0", "scc");                                                             \
+    }
+CCE_F4_HALF_FN(f4_half_first, CCE_K_OUT_A, CCE_MFZ, CCE_TAIL_NEXT)
+CCE_F4_HALF_FN(f4_half_next, CCE_K_INOUT_A, CCE_MF, CCE_TAIL_NEXT)
+CCE_F4_HALF_FN(f4_half_last, CCE_K_INOUT_A, CCE_MF, CCE_TAIL_LAST)
+#undef CCE_F4_HALF_FN
+
+// Prologue DMA of one half-stage: its A rows, and (B) its B rows too.
+template <bool B>
+__device__ __forceinline__ void f4_dma(uint32_t mba, uint64_t kba, const char *const (&pa)[4],
+                                       const char *const (&pb)[4]) {
+    uint64_t t0, t1;
+    if constexpr (B)
+        asm volatile(CCE_DMA_A CCE_DMA_B : [t0] "=&v"(t0), [t1] "=&v"(t1)
+                     : [mba] "s"(mba), [kba] "s"(kba), CCE_PTRS(pa, pb) : "memory", "m0", "scc");
+    else
+        asm volatile(CCE_DMA_A : [t0] "=&v"(t0), [t1] "=&v"(t1)
+                     : [mba] "s"(mba), [kba] "s"(kba), CCE_PTRS(pa, pb) : "memory", "m0", "scc");
+}
+// Reads a half-stage's slice-a fragments into P (x0 = the lane's slice-a offset).
+__device__ __forceinline__ void f4_read(u32x4 (&P)[8], uint32_t x0, uint32_t na, uint32_t nb) {
+    uint32_t ra, rb;
+    asm volatile(CCE_READ_ONLY : CCE_FRAGS(p, CCE_K_TMP_V, P), [ra] "=&v"(ra), [rb] "=&v"(rb)
+                 : [x0] "v"(x0), [na] "s"(na), [nb] "s"(nb) : "memory");
+}
+// Wait states between the last MFMAs of a tile and the vector instructions
+// that read or overwrite their results (the MFMA latency is not interlocked).
+__device__ __forceinline__ void acc_settle(Acc4 &acc) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : CCE_ACC(CCE_K_INOUT_A, acc));
+}
+#pragma clang diagnostic pop
+
+// fwd_tile_update for the 4-wave tile, one token column (64 values) at a
+// time; PART: the last vocabulary tile, rows at or past lim (per lane, as
+// acc_row_const) count as -inf.  Reads the accumulators only, so at most one
+// column's values are live in vector registers.
+template <bool LAB, bool PART>
+__device__ __forceinline__ float fwd4_columns(const Acc4 &acc, int lim, int v0, float (&m)[4], float (&l)[4],
+                                              const int (&lpos)[4], const int (&lrow)[4],
+                                              float *__restrict__ zlab) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rbase = (wave & 1) * 128 + 4 * (lane >> 5);
+    float tmax = kNegInf;
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+        __builtin_amdgcn_sched_barrier(0);
+        // (lim through an empty asm per column: the compiler would otherwise
+        // keep all 64 row masks in scalar registers across the columns.)
+        if (PART) asm volatile("" : "+v"(lim));
+        float x[4][16];
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                x[tm][r] = (PART && acc_row_const(tm, r) >= lim) ? kNegInf : acc[tm][tn][r];
+        float mx = kNegInf;
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[tm][r]);
+        float mxn = mx;
+        const int lr = LAB ? lpos[tn] - v0 - rbase : -1;
+        if (LAB && lr >= 0 && lr < 128) {
+            mxn = kNegInf;
+            float zl = 0.f;
+            bool hit = false;
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const bool il = acc_row_const(tm, r) == lr;
+                    mxn = fmaxf(mxn, il ? kNegInf : x[tm][r]);
+                    zl = il ? x[tm][r] : zl;
+                    hit |= il;
+                }
+            if (hit && lrow[tn] >= 0) zlab[lrow[tn]] = zl;
+        }
+        tmax = fmaxf(tmax, LAB ? mxn : mx);
+        const float mn = fmaxf(m[tn], mx * kLog2e);
+        // Every value at least 64 binary orders below the running maximum:
+        // the 64 terms add under 2^-58 of it (and at most 2^-46 of it over a
+        // whole vocabulary of 2^18 tiles' worth of rows), below what the fp32
+        // sum resolves once it holds the maximum's term; they are left out.
+        if (mn == kNegInf || mx * kLog2e < m[tn] - 64.f) continue;
+        float sum = 0.f;
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(x[tm][r], kLog2e, -mn));
+        l[tn] = l[tn] * __builtin_amdgcn_exp2f(m[tn] - mn) + sum;
+        m[tn] = mn;
+    }
+    return tmax;
+}
+
+template <bool LAB>
+__device__ __forceinline__ void fwd4_segment(const bf16_t *__restrict__ H, Rows2<const bf16_t> E,
+                                             const int32_t *__restrict__ idx, int nv,
+                                             const int32_t *__restrict__ perm, const int64_t *__restrict__ labels,
+                                             const int32_t *__restrict__ inv_perm, int D, int V, int n_vtiles,
+                                             int rt, int t0, int ntile, int64_t slot, u32x4 *lds,
+                                             float *__restrict__ part_m, float *__restrict__ part_s,
+                                             int *__restrict__ tbound, float *__restrict__ zlab,
+                                             const float *__restrict__ zy) {
+    using TL = TileF4;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, held in a scalar register
+    const int tok0 = rt * TL::BN;
+    int lpos[TL::TN], lrow[TL::TN];
+    if (LAB) fwd_label_pos<TL>(lpos, lrow, tok0, nv, idx, labels, inv_perm, V);
+    const int64_t rowb = (int64_t)D * (int64_t)sizeof(bf16_t);
+    const int nh = (int)(rowb / 64);  // half-stages per tile (even: rowb is a multiple of 128)
+    BoundSink bs{BoundSink::block_of<TL>(tbound, 2 * (int64_t)n_vtiles, rt, t0, nv)};
+
+    // DMA sources: instruction j (0-3) of this wave fills row 64 j + 16 w +
+    // lane / 4 of a half-stage's A (and B) rows at position lane % 4, with the
+    // logical chunk that the swizzle puts there.  Rows past the end of an
+    // operand are clamped to its last row.
+    const char *pa[4], *pb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 64 * j + 16 * w + (lane >> 2);
+        pb[j] = reinterpret_cast<const char *>(H) + (int64_t)idx[min(tok0 + r, nv - 1)] * rowb +
+                16 * ((lane & 3) ^ dma_swz<64>(r));
+    }
+    // (Two loops on the uniform perm test: without a permutation no load is
+    // issued, so nothing waits for the DMA in flight.)
+    auto set_tile = [&](int vt) {
+        if (perm) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 64 * j + 16 * w + (lane >> 2);
+                int v = perm[min(vt * TL::BM + r, V - 1)];
+                v = (v >= 0 && v < V) ? v : 0;
+                pa[j] = reinterpret_cast<const char *>(E.row(v)) + 16 * ((lane & 3) ^ dma_swz<64>(r));
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 64 * j + 16 * w + (lane >> 2);
+                pa[j] = reinterpret_cast<const char *>(E.row(min(vt * TL::BM + r, V - 1))) +
+                        16 * ((lane & 3) ^ dma_swz<64>(r));
+            }
+        }
+    };
+    // The DMA cursor (tile qt, half-stage qk, global count qg) runs four
+    // half-stages ahead of the computation, across tiles; pa / pb point at K
+    // offset 0 of their rows and the half-stage's offset qk * 64 is added as
+    // each DMA is issued.  Past the segment's last half-stage the cursor stays
+    // on it: the extra DMAs re-read it into buffers nobody reads any more, and
+    // are waited for before the LDS is used for anything else.
+    int qt = 0, qk = 0, qg = 0;
+    auto advance = [&]() {
+        ++qg;
+        if (++qk < nh) return;
+        if (qt + 1 < ntile) {
+            qk = 0;
+            set_tile(t0 + ++qt);
+        } else {
+            qk = nh - 1;
+        }
+    };
+
+    // LDS: the lane's byte offset of its chunk of slice kk in fragment row
+    // lane % 32 (a 64-byte row), and the wave's A and B fragment rows.
+    const uint32_t lds0 = lds_addr(lds);
+    const uint32_t mb0 = lds0 + 1024u * (uint32_t)w;
+    uint32_t xk[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+        xk[kk] = 64u * (lane & 31) + 16u * ((2 * kk + (lane >> 5)) ^ dma_swz<64>(lane & 31));
+    const uint32_t offa = lds0 + 8192u * (uint32_t)(w & 1), offb = lds0 + 16384u + 8192u * (uint32_t)(w >> 1);
+    auto buf = [](int h) { return (uint32_t)(h & 3) * 32768u; };
+
+    // The running maximum of each token starts at its label logit (log2
+    // units): a value of the row, so the online sum stays exact, and on a
+    // peaked row it lets the tiles far below the label skip their
+    // exponentials from the segment's first tile on.
+    float m[TL::TN], l[TL::TN];
+#pragma unroll
+    for (int tn = 0; tn < TL::TN; ++tn) {
+        const float z = zy[min(tok0 + tile_col<TL>(tn), nv - 1)];
+        m[tn] = __builtin_isfinite(z) ? z * kLog2e : kNegInf;
+        l[tn] = 0.f;
+    }
+
+    // Prologue: half-stages 0-2 whole and the A rows of 3.
+    set_tile(t0);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        f4_dma<true>(mb0 + buf(qg), (uint64_t)qk * 64u, pa, pb);
+        advance();
+    }
+    uint32_t mbb = mb0 + buf(qg);
+    uint64_t kbb = (uint64_t)qk * 64u;
+    f4_dma<false>(mbb, kbb, pa, pb);
+    advance();
+    wait_vmcnt<20>();
+    block_sync();
+
+    u32x4 P[8];
+    Acc4 acc;
+    int h = 0;  // half-stage counter of the segment
+    auto args = [&]() {
+        return F4Half{offa + buf(h), offb + buf(h), offa + buf(h + 1), offb + buf(h + 1),
+                      mb0 + buf(qg), mbb, (uint64_t)qk * 64u, kbb};
+    };
+    // After a half-stage: its A rows' DMA becomes the pending B rows' DMA.
+    auto step = [&]() {
+        mbb = mb0 + buf(qg);
+        kbb = (uint64_t)qk * 64u;
+        advance();
+        ++h;
+    };
+    for (int ct = 0; ct < ntile; ++ct) {
+        f4_read(P, xk[0], offa + buf(h), offb + buf(h));
+        f4_half_first(acc, P, xk, args(), pa, pb);
+        step();
+        for (int k = 1; k + 1 < nh; ++k) {
+            f4_half_next(acc, P, xk, args(), pa, pb);
+            step();
+        }
+        f4_half_last(acc, P, xk, args(), pa, pb);
+        step();
+        acc_settle(acc);
+        const int v0 = (t0 + ct) * TL::BM;
+        const float tmax = v0 + TL::BM <= V
+                               ? fwd4_columns<LAB, false>(acc, 0, v0, m, l, lpos, lrow, zlab)
+                               : fwd4_columns<LAB, true>(acc, row_limit<TL>(V - v0), v0, m, l, lpos, lrow, zlab);
+        bs.tile(ct, tmax, ct == ntile - 1);
+    }
+    wait_vmcnt<0>();  // the extra half-stages
+    fwd_write_partials<TL>(m, l, reinterpret_cast<float *>(lds), tok0, nv, slot, part_m, part_s);
+}
+
+template <bool LAB>
+__global__ __launch_bounds__(TileF4::kThreads) void k_fwd4(
+    const bf16_t *__restrict__ H, Rows2<const bf16_t> E, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, const int64_t *__restrict__ labels,
+    const int32_t *__restrict__ inv_perm, int D, int V, int n_vtiles, float *__restrict__ part_m,
+    float *__restrict__ part_s, int *__restrict__ tbound, float *__restrict__ zlab, const float *__restrict__ zy) {
+    __shared__ u32x4 lds[4 * 2 * kTileVocab * 4];  // 4 buffers of 256 A + 256 B rows of 64 bytes
+    const int nv = *nvalid_p;
+    if (nv <= 0) return;
+    const int L = fwd_logical(blockIdx.x, gridDim.x);
+    const FwdPart P = fwd_part(nv, n_vtiles, gridDim.x);
+    const int64_t u1 = P.start(L + 1);
+    for (int64_t u = P.start(L); u < u1;) {
+        const int rt = (int)(u / n_vtiles);
+        const int t0 = (int)(u - (int64_t)rt * n_vtiles);
+        const int ntile = (int)min((int64_t)(n_vtiles - t0), u1 - u);
+        fwd4_segment<LAB>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile, (int64_t)L + rt,
+                          lds, part_m, part_s, tbound, zlab, zy);
+        u += ntile;
+    }
+}
+
+// ------------------------------------------------------------ label gather
+// One wave per compacted position w < nv: zy[w] = <h_i, e_{y_i}> for row
+// i = idx[w] (fp32 accumulation of exact products; the indexed matmul), or
+// -inf where the label is out of range.  The 4-wave forward starts each
+// token's running maximum there, and the merge takes the loss from it.
+template <typename T>
+__global__ __launch_bounds__(256) void k_label_dot(const T *__restrict__ H, Rows2<const T> E,
+                                                   const int64_t *__restrict__ labels,
+                                                   const int32_t *__restrict__ idx,
+                                                   const int32_t *__restrict__ nvalid_p, int D, int64_t V,
+                                                   float *__restrict__ zy) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w >= *nvalid_p) return;
+    const int64_t i = idx[w];
+    const int64_t y = labels[i];
+    if (y < 0 || y >= V) {
+        if (lane == 0) zy[w] = kNegInf;
+        return;
+    }
+    constexpr int CE = ChunkElems<T>::value;
+    const char *h = reinterpret_cast<const char *>(H + i * (int64_t)D);
+    const char *e = reinterpret_cast<const char *>(E.row(y));
+    float dot = 0.f;
+    for (int k = lane * CE; k < D; k += 64 * CE) {
+        const u32x4 hv = ld16(h + k * sizeof(T));
+        const u32x4 ev = ld16(e + k * sizeof(T));
+        const T *hp = reinterpret_cast<const T *>(&hv);
+        const T *ep = reinterpret_cast<const T *>(&ev);
+#pragma unroll
+        for (int q = 0; q < CE; ++q) dot += to_f32(hp[q]) * to_f32(ep[q]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
+    if (lane == 0) zy[w] = dot;
+}
+
+// ------------------------------------------------------------------ merge
 // One wave per position w: it zeroes row w if that row is ignored, and if
 // w < nv it finishes the valid row at compacted position w.  The segments of
 // the row's token tile are those of the workgroups owner(first unit) ..
@@ -566,12 +991,10 @@ __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
 // ... of them, and the max
 // and the scaled sum are butterfly reductions, so the result depends only on
 // the partition, never on scheduling.
-template <typename T>
-__global__ __launch_bounds__(256) void k_merge(const T *__restrict__ H, Rows2<const T> E,
-                                               const int64_t *__restrict__ labels, const int32_t *__restrict__ idx,
+__global__ __launch_bounds__(256) void k_merge(const int64_t *__restrict__ labels, const int32_t *__restrict__ idx,
                                                const int32_t *__restrict__ nvalid_p,
                                                const float *__restrict__ part_m, const float *__restrict__ part_s,
-                                               int G, int n_vtiles, int64_t N, int D, int64_t V,
+                                               const float *__restrict__ zy, int G, int n_vtiles, int64_t N, int64_t V,
                                                int64_t ignore_index, float *__restrict__ loss,
                                                float *__restrict__ lse) {
     const int lane = threadIdx.x & 63;
@@ -604,21 +1027,7 @@ __global__ __launch_bounds__(256) void k_merge(const T *__restrict__ H, Rows2<co
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) S += __shfl_xor(S, o, 64);
 
-    // z_{i, y_i} = <h_i, e_{y_i}>, fp32 accumulation of exact products.
-    constexpr int CE = ChunkElems<T>::value;
-    const char *h = reinterpret_cast<const char *>(H + i * (int64_t)D);
-    const char *e = reinterpret_cast<const char *>(E.row(y));
-    float dot = 0.f;
-    for (int k = lane * CE; k < D; k += 64 * CE) {
-        const u32x4 hv = ld16(h + k * sizeof(T));
-        const u32x4 ev = ld16(e + k * sizeof(T));
-        const T *hp = reinterpret_cast<const T *>(&hv);
-        const T *ep = reinterpret_cast<const T *>(&ev);
-#pragma unroll
-        for (int q = 0; q < CE; ++q) dot += to_f32(hp[q]) * to_f32(ep[q]);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
+    const float dot = zy[w];  // z_{i, y_i}
     if (lane == 0) {
         const float l = (M + log2f(S)) * kLn2;
         lse[i] = l;
@@ -676,6 +1085,7 @@ FwdWs fwd_ws(void *ws, const FwdShape &s, size_t *bytes) {
     // slots L + rt < G + n_rtiles, one partial per token of the tile each
     w.part_m = c.take<float>((size_t)(kFwdMaxGroups + s.n_rtiles) * kTileRows);
     w.part_s = c.take<float>((size_t)(kFwdMaxGroups + s.n_rtiles) * kTileRows);
+    w.zy = c.take<float>(s.N);
     if (bytes) *bytes = c.off;
     return w;
 }
@@ -710,6 +1120,9 @@ static hipError_t forward_t(const T *H, Rows2<const T> E, const int64_t *labels,
                             float *block_max, hipStream_t st) {
     hipError_t e = launch_compact(labels, s.N, ignore_index, w.idx, w.nvalid, st);
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_label_dot<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, H, E, labels, w.idx,
+                       w.nvalid, (int)s.D, s.V, w.zy);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     int *tb = reinterpret_cast<int *>(block_max);
     const int64_t nb = 4 * (int64_t)s.n_rtiles * s.n_vtiles;
     const int32_t *invp = nullptr;  // label positions in the processing order, for the table
@@ -728,7 +1141,16 @@ static hipError_t forward_t(const T *H, Rows2<const T> E, const int64_t *labels,
     int dev = 0, cus = 0, per_cu = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if (dma && tb)
+    constexpr bool bf16 = std::is_same<T, bf16_t>::value;
+    const bool four = CCE_FWD4 && bf16 && dma;
+    if constexpr (bf16) {
+        if (four)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tb ? k_fwd4<true> : k_fwd4<false>,
+                                                             TileF4::kThreads, 0);
+    }
+    if (four)
+        ;
+    else if (dma && tb)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fwd_dma<T, TileFD, true>, TileFD::kThreads, 0);
     else if (dma)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fwd_dma<T, TileFD, false>, TileFD::kThreads, 0);
@@ -741,7 +1163,19 @@ static hipError_t forward_t(const T *H, Rows2<const T> E, const int64_t *labels,
     G = std::min<int64_t>(std::min<int64_t>(G, kFwdMaxGroups), (int64_t)s.n_rtiles * s.n_vtiles);
     if (G >= 8) G &= ~7;  // lets the placement give each XCD a contiguous eighth
     const dim3 grid((unsigned)G);
-    if (dma && tb)
+    if constexpr (bf16) {
+        if (four) {
+            if (tb)
+                hipLaunchKernelGGL(k_fwd4<true>, grid, dim3(TileF4::kThreads), 0, st, H, E, w.idx, w.nvalid, perm,
+                                   labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl, w.zy);
+            else
+                hipLaunchKernelGGL(k_fwd4<false>, grid, dim3(TileF4::kThreads), 0, st, H, E, w.idx, w.nvalid, perm,
+                                   labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl, w.zy);
+        }
+    }
+    if (four)
+        ;
+    else if (dma && tb)
         hipLaunchKernelGGL((k_fwd_dma<T, TileFD, true>), grid, dim3(TileFD::kThreads), 0, st, H, E, w.idx, w.nvalid,
                            perm, labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
     else if (dma)
@@ -754,9 +1188,8 @@ static hipError_t forward_t(const T *H, Rows2<const T> E, const int64_t *labels,
         hipLaunchKernelGGL((k_fwd<T, false>), grid, dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid, perm, labels,
                            invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_merge<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, H, E, labels, w.idx,
-                       w.nvalid, w.part_m, w.part_s, (int)G, s.n_vtiles, s.N, (int)s.D, s.V, ignore_index, loss,
-                       lse);
+    hipLaunchKernelGGL(k_merge, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, labels, w.idx, w.nvalid,
+                       w.part_m, w.part_s, w.zy, (int)G, s.n_vtiles, s.N, s.V, ignore_index, loss, lse);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (tb) hipLaunchKernelGGL(k_bound_decode, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, st, tb, nb);
     return hipGetLastError();

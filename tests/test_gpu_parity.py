@@ -158,6 +158,7 @@ EDGE = [
     (3, 8, 7, "f32", 0.0, "normal"),         # smallest D
     (129, 136, 257, "bf16", 0.0, "normal"),  # one past tile edges everywhere
     (200, 64, 300, "bf16", 1.0, "normal"),   # every row ignored
+    (300, 64, 700, "bf16", 0.1, "normal"),   # D = 64: one 128-byte K stage per vocabulary tile
     (300, 96, 1000, "f32", 0.5, "peaked"),   # z_y ~ 144: every non-label p below fp32 resolution
 ]
 
