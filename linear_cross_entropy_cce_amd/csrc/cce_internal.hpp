@@ -27,9 +27,12 @@ constexpr int kStoreVocab = 8192;
 constexpr int64_t kMinStoreBlocks = 1024;
 // Workgroups of the persistent backward kernels.
 constexpr int kPassGroups = 256;
-// Most workgroups of the forward's persistent grid (its partial buffers are
-// sized for this many).
+// Most workgroups of the forward's persistent grid.
 constexpr int kFwdMaxGroups = 1024;
+// Most vocabulary ranges per token tile in the forward's work split (its
+// partial buffers are sized for this many; at most 64, one per lane of the
+// merge).
+constexpr int kFwdRanges = 32;
 // Device scratch of the allocation-free forward (one copy per GPU).
 constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 
@@ -81,8 +84,8 @@ struct FwdWs {
     int32_t *idx;      // [N] compacted valid-row indices
     int32_t *nvalid;   // [1]
     int32_t *inv_perm; // [V] processing position of each vocabulary id (with a permutation and the table)
-    float *part_m;     // [kFwdMaxGroups + n_rtiles, kTileRows] per segment: running max (log2 units)
-    float *part_s;     // [kFwdMaxGroups + n_rtiles, kTileRows] per segment: sum of 2^(z log2e - m)
+    float *part_m;     // [n_rtiles kFwdRanges, kTileRows] per segment: running max (log2 units)
+    float *part_s;     // [n_rtiles kFwdRanges, kTileRows] per segment: sum of 2^(z log2e - m)
     float *zy;         // [N] label logit of each valid row, by compacted position
 };
 FwdWs fwd_ws(void *ws, const FwdShape &s, size_t *bytes);

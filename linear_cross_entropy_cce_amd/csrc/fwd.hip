@@ -149,42 +149,83 @@ __global__ __launch_bounds__(256) void k_seg_labels(const int64_t *__restrict__ 
 }
 
 // ------------------------------------------------------------ logit + LSE
-// Work partition.  The units are the 256 x 256 logit tiles of the valid rows,
-// token-tile-major (u = rt * nvt + vt), U of them.  The grid is persistent
-// (as many workgroups as fit on the chip at once, G); logical workgroup L
-// takes units [L U / G, (L + 1) U / G), so every workgroup gets the same
-// number of tiles within one, whatever the shape and however many rows are
-// ignored.  A range covers a vocabulary range of one or more token tiles;
-// each (workgroup, token tile) pair is a segment and writes one partial
-// (m, s) per token at slot L + rt.  Slots are unique: along the partition L
-// and rt never decrease and one of them grows at each step.
+// Work partition.  The work is the grid of 256 x 256 logit tiles of the valid
+// rows: R token tiles x C vocabulary tiles.  Each token tile's vocabulary is
+// cut into b ranges (range j: tiles [j C / b, (j + 1) C / b)); a (token tile,
+// range) pair is a segment, streamed by one workgroup through one continuous
+// K pipeline, and writes one partial (m, s) per token at slot rt b + j.
 //
-// A segment streams its vocabulary tiles through one continuous double-
-// buffered K pipeline: the loads of the next tile's first stage are in flight
-// while the current tile's epilogue runs.  Each lane owns TN token columns;
-// for each it keeps m (running max of z log2 e) and l (running sum of
-// 2^(z log2 e - m)) over the vocabulary rows it holds.  At the end of a
-// segment the two half-waves and the WM waves that hold the same tokens are
-// merged in a fixed order.
+// Placement: hardware workgroup g runs on XCD g % 8, so the grid (persistent:
+// as many workgroups as fit on the chip at once) is seen as nx = 8 groups of
+// P workgroups (P = 32 on MI355X), one group per XCD.  A block is a x bb
+// segments (a token tiles x bb consecutive ranges, a bb = P): the P
+// workgroups of one XCD take one block at a time, all in step, so the
+// classifier tiles in flight on an XCD are shared by a workgroups and the
+// hidden-state tiles by bb in that XCD's L2.  Blocks (ceil(R / a) token
+// groups x m range groups, b = bb m) go to the XCDs round-robin.  (a, bb, m)
+// are chosen from the shape, the number of valid rows and the grid, so that
+// the longest workgroup (steps x the longest range) is shortest; ties prefer
+// a = 4 (4 x 8 at the Gemma-2-2B head: one block per XCD, the split that
+// measured best there) and then fewer ranges.  An even split of the tile
+// list over the workgroups instead cut ranges at vocabulary offsets that
+// differ between token tiles when the tile count is not a multiple of the
+// grid: on the Llama-3 head (39 token tiles) every workgroup of an XCD then
+// streamed its own classifier tile, and the forward fetched 48 times its
+// operands from memory.
 //
-// Placement: hardware workgroup b runs on XCD b % 8, and consecutive logical
-// workgroups are put on one XCD, so an XCD holds a contiguous eighth of the
-// units: at the Gemma-2-2B head shape 4 token tiles x 8 vocabulary ranges,
-// each classifier tile in flight shared by 4 workgroups and each hidden-state
-// tile by 8 in that XCD's L2 (measured against 2 x 16, 1 x 32 and no grouping:
-// best by 2-5 %).
-struct FwdPart {
-    int64_t U;  // units (tiles of the valid rows)
-    int G;      // workgroups
-    __device__ __forceinline__ int64_t start(int L) const { return (int64_t)L * U / G; }
-    // The workgroup whose range holds unit u: the largest L with start(L) <= u.
-    __device__ __forceinline__ int owner(int64_t u) const { return (int)(((u + 1) * G - 1) / U); }
+// Within a segment each lane owns TN token columns and keeps, for each, m
+// (running max of z log2 e) and l (running sum of 2^(z log2 e - m)) over the
+// vocabulary rows it holds.  At the end of a segment the two half-waves and
+// the WM waves that hold the same tokens are merged in a fixed order.
+struct FwdGrid {
+    int R, C;      // token tiles of the valid rows, vocabulary tiles
+    int nx, P;     // XCD groups and workgroups per group
+    int a, bb, m;  // block shape and range groups
+    __device__ __forceinline__ int b() const { return bb * m; }
+    __device__ __forceinline__ int blocks() const { return (R + a - 1) / a * m; }
+    __device__ __forceinline__ int vt0(int j) const { return (int)((int64_t)j * C / b()); }
 };
 
-__device__ __forceinline__ int fwd_logical(int b, int G) { return G % 8 == 0 ? (b % 8) * (G / 8) + b / 8 : b; }
+__device__ __forceinline__ FwdGrid fwd_grid(int nv, int C, int G) {
+    FwdGrid g;
+    g.R = (nv + kTileRows - 1) / kTileRows;
+    g.C = C;
+    g.nx = G % 8 == 0 ? 8 : 1;
+    g.P = G / g.nx;
+    g.a = 1; g.bb = g.P; g.m = 1;
+    int64_t best = -1;
+    int best_pref = 0;
+    const int maxb = C < kFwdRanges ? C : kFwdRanges;
+    for (int a = 1; a <= g.P; a *= 2) {
+        if (g.P % a) continue;
+        const int bb = g.P / a;
+        const int pref = a == 4 ? 0 : 1;
+        for (int m = 1; bb * m <= maxb; ++m) {
+            const int64_t steps = ((g.R + a - 1) / a * (int64_t)m + g.nx - 1) / g.nx;
+            const int64_t cost = steps * ((C + bb * m - 1) / (bb * m));
+            if (best < 0 || cost < best || (cost == best && pref < best_pref)) {
+                best = cost; best_pref = pref; g.a = a; g.bb = bb; g.m = m;
+            }
+        }
+    }
+    if (best < 0) { g.a = 1; g.bb = 1; g.m = 1; }  // P > maxb: one range, idle workgroups
+    return g;
+}
 
-__device__ __forceinline__ FwdPart fwd_part(int nv, int n_vtiles, int G) {
-    return FwdPart{(int64_t)((nv + kTileRows - 1) / kTileRows) * n_vtiles, G};
+// The segments of hardware workgroup gid, in order: f(rt, t0, ntile, slot).
+template <class F>
+__device__ __forceinline__ void fwd_segments(const FwdGrid &g, int gid, F &&f) {
+    const int x = gid % g.nx, i = gid / g.nx;
+    const int ti = i / g.bb, ji = i % g.bb;
+    if (ti >= g.a) return;  // (only with the one-range fallback)
+    const int nb = g.blocks();
+    for (int q = x; q < nb; q += g.nx) {
+        const int rt = q / g.m * g.a + ti;
+        const int j = q % g.m * g.bb + ji;
+        if (rt >= g.R) continue;
+        const int t0 = g.vt0(j), t1 = g.vt0(j + 1);
+        if (t1 > t0) f(rt, t0, t1 - t0, (int64_t)rt * g.b() + j);
+    }
 }
 
 // Online max / sum-exp update with the tile's logits.  Returns the largest
@@ -445,17 +486,10 @@ __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
     __shared__ u32x4 lds[TileF::kLdsChunks];
     const int nv = *nvalid_p;
     if (nv <= 0) return;
-    const int L = fwd_logical(blockIdx.x, gridDim.x);
-    const FwdPart P = fwd_part(nv, n_vtiles, gridDim.x);
-    const int64_t u1 = P.start(L + 1);
-    for (int64_t u = P.start(L); u < u1;) {
-        const int rt = (int)(u / n_vtiles);
-        const int t0 = (int)(u - (int64_t)rt * n_vtiles);
-        const int ntile = (int)min((int64_t)(n_vtiles - t0), u1 - u);
-        fwd_segment<T, LAB>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile, (int64_t)L + rt,
-                            lds, part_m, part_s, tbound, zlab);
-        u += ntile;
-    }
+    fwd_segments(fwd_grid(nv, n_vtiles, gridDim.x), blockIdx.x, [&](int rt, int t0, int ntile, int64_t slot) {
+        fwd_segment<T, LAB>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile, slot, lds, part_m,
+                            part_s, tbound, zlab);
+    });
 }
 
 // The same computation on the DMA pipeline (DmaEngine): 2 LDS stages of 128
@@ -556,17 +590,10 @@ __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
     __shared__ u32x4 lds[DE::kLdsChunks];
     const int nv = *nvalid_p;
     if (nv <= 0) return;
-    const int L = fwd_logical(blockIdx.x, gridDim.x);
-    const FwdPart P = fwd_part(nv, n_vtiles, gridDim.x);
-    const int64_t u1 = P.start(L + 1);
-    for (int64_t u = P.start(L); u < u1;) {
-        const int rt = (int)(u / n_vtiles);
-        const int t0 = (int)(u - (int64_t)rt * n_vtiles);
-        const int ntile = (int)min((int64_t)(n_vtiles - t0), u1 - u);
-        fwd_segment_dma<T, TL, LAB>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile,
-                                    (int64_t)L + rt, lds, part_m, part_s, tbound, zlab);
-        u += ntile;
-    }
+    fwd_segments(fwd_grid(nv, n_vtiles, gridDim.x), blockIdx.x, [&](int rt, int t0, int ntile, int64_t slot) {
+        fwd_segment_dma<T, TL, LAB>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile, slot, lds,
+                                    part_m, part_s, tbound, zlab);
+    });
 }
 
 // ------------------------------------- bf16 forward on 4 waves, scheduled K loop
@@ -933,17 +960,10 @@ __global__ __launch_bounds__(TileF4::kThreads) void k_fwd4(
     __shared__ u32x4 lds[4 * 2 * kTileVocab * 4];  // 4 buffers of 256 A + 256 B rows of 64 bytes
     const int nv = *nvalid_p;
     if (nv <= 0) return;
-    const int L = fwd_logical(blockIdx.x, gridDim.x);
-    const FwdPart P = fwd_part(nv, n_vtiles, gridDim.x);
-    const int64_t u1 = P.start(L + 1);
-    for (int64_t u = P.start(L); u < u1;) {
-        const int rt = (int)(u / n_vtiles);
-        const int t0 = (int)(u - (int64_t)rt * n_vtiles);
-        const int ntile = (int)min((int64_t)(n_vtiles - t0), u1 - u);
-        fwd4_segment<LAB>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile, (int64_t)L + rt,
-                          lds, part_m, part_s, tbound, zlab, zy);
-        u += ntile;
-    }
+    fwd_segments(fwd_grid(nv, n_vtiles, gridDim.x), blockIdx.x, [&](int rt, int t0, int ntile, int64_t slot) {
+        fwd4_segment<LAB>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile, slot, lds, part_m,
+                          part_s, tbound, zlab, zy);
+    });
 }
 
 // ------------------------------------------------------------ label gather
@@ -985,12 +1005,10 @@ __global__ __launch_bounds__(256) void k_label_dot(const T *__restrict__ H, Rows
 
 // ------------------------------------------------------------------ merge
 // One wave per position w: it zeroes row w if that row is ignored, and if
-// w < nv it finishes the valid row at compacted position w.  The segments of
-// the row's token tile are those of the workgroups owner(first unit) ..
-// owner(last unit) whose range is not empty; lane j takes the j-th, (j+64)-th,
-// ... of them, and the max
-// and the scaled sum are butterfly reductions, so the result depends only on
-// the partition, never on scheduling.
+// w < nv it finishes the valid row at compacted position w.  Lane j takes the
+// partial of the row's token tile and vocabulary range j (if that range is
+// not empty); the max and the scaled sum are butterfly reductions, so the
+// result depends only on the partition, never on scheduling.
 __global__ __launch_bounds__(256) void k_merge(const int64_t *__restrict__ labels, const int32_t *__restrict__ idx,
                                                const int32_t *__restrict__ nvalid_p,
                                                const float *__restrict__ part_m, const float *__restrict__ part_s,
@@ -1010,20 +1028,15 @@ __global__ __launch_bounds__(256) void k_merge(const int64_t *__restrict__ label
         return;
     }
     const int rt = (int)(w / kTileRows), c = (int)(w % kTileRows);
-    const FwdPart P = fwd_part(nv, n_vtiles, G);
-    const int L0 = P.owner((int64_t)rt * n_vtiles), L1 = P.owner((int64_t)rt * n_vtiles + n_vtiles - 1);
-    // (with fewer units than workgroups some ranges are empty: no segment)
-    float M = kNegInf;
-    for (int L = L0 + lane; L <= L1; L += 64)
-        if (P.start(L) < P.start(L + 1)) M = fmaxf(M, part_m[((int64_t)L + rt) * kTileRows + c]);
+    const FwdGrid g = fwd_grid(nv, n_vtiles, G);
+    const int b = g.b();  // at most 64 ranges: one per lane
+    const bool seg = lane < b && g.vt0(lane + 1) > g.vt0(lane);  // (an empty range has no segment)
+    const int64_t at = ((int64_t)rt * b + lane) * kTileRows + c;
+    const float pm = seg ? part_m[at] : kNegInf;
+    float M = pm;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    float S = 0.f;
-    for (int L = L0 + lane; L <= L1; L += 64) {
-        if (P.start(L) == P.start(L + 1)) continue;
-        const float pm = part_m[((int64_t)L + rt) * kTileRows + c];
-        if (pm != kNegInf) S += part_s[((int64_t)L + rt) * kTileRows + c] * __builtin_amdgcn_exp2f(pm - M);
-    }
+    float S = pm != kNegInf ? part_s[at] * __builtin_amdgcn_exp2f(pm - M) : 0.f;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) S += __shfl_xor(S, o, 64);
 
@@ -1082,9 +1095,9 @@ FwdWs fwd_ws(void *ws, const FwdShape &s, size_t *bytes) {
     w.idx = c.take<int32_t>(s.N);
     w.nvalid = c.take<int32_t>(1);
     w.inv_perm = c.take<int32_t>(s.V);
-    // slots L + rt < G + n_rtiles, one partial per token of the tile each
-    w.part_m = c.take<float>((size_t)(kFwdMaxGroups + s.n_rtiles) * kTileRows);
-    w.part_s = c.take<float>((size_t)(kFwdMaxGroups + s.n_rtiles) * kTileRows);
+    // slots rt b + j < n_rtiles kFwdRanges, one partial per token of the tile each
+    w.part_m = c.take<float>((size_t)s.n_rtiles * kFwdRanges * kTileRows);
+    w.part_s = c.take<float>((size_t)s.n_rtiles * kFwdRanges * kTileRows);
     w.zy = c.take<float>(s.N);
     if (bytes) *bytes = c.off;
     return w;

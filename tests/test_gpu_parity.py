@@ -53,37 +53,47 @@ def test_forward_matches_oracle(k, N, D, V):
     G.assert_rows("loss", out["loss"], loss, valid, G.lse_tol(x), lse)
 
 
-def _crossing_ranges(n_valid, V, groups):
-    """Workgroup ranges of the forward's partition (units = 256 x 256 tiles,
-    token-tile-major; workgroup L takes [L U / G, (L + 1) U / G)) that span
-    more than one token tile, i.e. write two or more segments."""
-    n_rt = -(-n_valid // 256)
-    n_vt = -(-V // 256)
-    U = n_rt * n_vt
-    G_ = min(groups, 1024, U)
+def _forward_split(n_valid, V, groups):
+    """The forward's work split, as the kernels choose it (token tiles x
+    vocabulary ranges, a x bb blocks per XCD group, m range groups): returns
+    (ranges per token tile, steps per workgroup, block shape)."""
+    R = -(-n_valid // 256)
+    C = -(-V // 256)
+    G_ = min(groups, 1024, R * C)
     if G_ >= 8:
         G_ &= ~7
-    cross = 0
-    for L in range(G_):
-        a, b = L * U // G_, (L + 1) * U // G_
-        if b > a and a // n_vt != (b - 1) // n_vt:
-            cross += 1
-    return cross, U, G_
+    nx = 8 if G_ % 8 == 0 else 1
+    P = G_ // nx
+    best, cfg = None, (1, 1, 1)
+    a = 1
+    while a <= P:
+        if P % a == 0:
+            bb = P // a
+            m = 1
+            while bb * m <= min(C, 32):
+                steps = (-(-R // a) * m + nx - 1) // nx
+                cost = (steps * -(-C // (bb * m)), 0 if a == 4 else 1)
+                if best is None or cost < best:
+                    best, cfg = cost, (a, bb, m)
+                m += 1
+        a *= 2
+    a, bb, m = cfg
+    return bb * m, (-(-R // a) * m + nx - 1) // nx, (a, bb)
 
 
-# more tiles than workgroups: ranges that cross token-tile boundaries, so the
-# ordered merge combines two or more segments of one workgroup
-CROSS = [(3, 2300, 512, 20000), (5, 3800, 128, 40000)]
+# several vocabulary ranges per token tile, several blocks per workgroup, and
+# a block shape other than 4 x 8: the ordered merge combines many segments
+SPLIT = [(3, 2300, 512, 20000), (5, 9500, 64, 20000), (5, 9500, 64, 10000)]
 
 
-@pytest.mark.parametrize("k,N,D,V", CROSS, ids=[f"w{c[0]}-{c[1]}x{c[3]}" for c in CROSS])
-def test_forward_segments_across_token_tiles(k, N, D, V):
+@pytest.mark.parametrize("k,N,D,V", SPLIT, ids=[f"w{c[0]}-{c[1]}x{c[2]}x{c[3]}" for c in SPLIT])
+def test_forward_split_ranges_and_steps(k, N, D, V):
     x = inputs.make_workload(k, N=N, D=D, V=V)
-    # one 512-thread forward workgroup per CU (its LDS stages take 128 KB)
+    # one forward workgroup per CU (its LDS buffers take 128 KB)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    cross, U, Gw = _crossing_ranges(x.n_valid, x.V, cus)
-    G.say(f"forward crossing w{k} N={x.N} D={x.D} V={x.V}: {U} tiles over {Gw} workgroups, {cross} crossing")
-    assert cross >= 1
+    ranges, steps, shape = _forward_split(x.n_valid, x.V, cus)
+    G.say(f"forward split w{k} N={x.N} D={x.D} V={x.V}: {ranges} ranges per token tile, {steps} steps, blocks {shape}")
+    assert ranges >= 2
     out = G.run_gpu(x, G.mean_dloss(x), eps=0.0, backward=False)
     H = oracle.as_f64(x.H, x.dtype)
     E = oracle.as_f64(x.E, x.dtype)
