@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_fwd_dma_gemma2_2b_head_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_fwd4_gemma2_2b_head_traffic.md")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (published)
 METRIC = "fwd+bwd tokens/sec of fused linear-CE at Gemma-2-2B shape; % MFMA peak"
@@ -278,7 +278,7 @@ def main():
     peak = PEAK_BF16_TFLOPS if x.dtype == "bf16" else PEAK_FP32_TFLOPS
     fwd_avg = float(np.mean(fwd_ms))
     achieved = f_logits / (fwd_avg * 1e-3) / 1e12
-    # HBM bytes per k_fwd_dma launch from the committed counter passes, while the
+    # HBM bytes per k_fwd4 launch from the committed counter passes, while the
     # kernel's sources are the ones they were taken on (this workload only)
     from linear_cross_entropy_cce_amd import profiling as TR
     rec = TR.load(TRAFFIC_PROFILE) if a.workload == 2 else None
@@ -300,7 +300,7 @@ def main():
                    "N": N, "D": D, "V": V, "n_valid": nv, "filter_eps": eps, "sort_vocab": a.sort,
                    "filter_block": [br, bv], "kahan_de": not a.no_kahan, "full_de": a.full_de,
                    "fine_filter": a.fine},
-        "roofline": {"kernel": "k_fwd (cce_forward bracket)", "bound": "mfma", "achieved": achieved,
+        "roofline": {"kernel": "k_fwd4 (cce_forward bracket)", "bound": "mfma", "achieved": achieved,
                      "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
         "detail": {
             "fwd_ms_mean": fwd_avg, "bwd_ms_mean": float(np.mean(bwd_ms)),

@@ -748,6 +748,19 @@ __device__ __forceinline__ void acc_settle(Acc4 &acc) {
 }
 #pragma clang diagnostic pop
 
+// One accumulator value into a vector register.  (Through an assembly
+// statement: reading the accumulators as plain values, the compiler copied
+// all 256 of them to vector registers at once, ahead of the per-column
+// loop, and spilled.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ float acc_read(const f32x16 &v, int r) {
+    float o;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(o) : "a"(v[r]));
+    return o;
+}
+#pragma clang diagnostic pop
+
 // fwd_tile_update for the 4-wave tile, one token column (64 values) at a
 // time; PART: the last vocabulary tile, rows at or past lim (per lane, as
 // acc_row_const) count as -inf.  Reads the accumulators only, so at most one
@@ -770,7 +783,7 @@ __device__ __forceinline__ float fwd4_columns(const Acc4 &acc, int lim, int v0, 
         for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                x[tm][r] = (PART && acc_row_const(tm, r) >= lim) ? kNegInf : acc[tm][tn][r];
+                x[tm][r] = (PART && acc_row_const(tm, r) >= lim) ? kNegInf : acc_read(acc[tm][tn], r);
         float mx = kNegInf;
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm)

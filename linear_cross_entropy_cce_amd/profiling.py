@@ -48,7 +48,7 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL = "k_fwd_dma"
+KERNEL = "k_fwd4"
 SOURCES = ("csrc/fwd.hip", "csrc/cce_device.hpp", "csrc/cce_internal.hpp")
 
 
@@ -323,7 +323,7 @@ def main():
     c.add_argument("--command", default="rocprofv3 --pmc " + " ".join(COUNTERS) + " --output-format csv "
                                          "-d pmc_core -o p -- python -u bench.py --steps 1 --warmup 1 "
                                          "--no-cpu-baseline")
-    c.add_argument("--title", default="Core counters of `k_fwd_dma`: Gemma-2-2B head (N=8192, D=2304, V=256000, bf16)")
+    c.add_argument("--title", default="Core counters of `k_fwd4`: Gemma-2-2B head (N=8192, D=2304, V=256000, bf16)")
     c.add_argument("--out", required=True)
     c.add_argument("--kernels", nargs="+", default=[KERNEL], help="kernel-name substrings, one column each")
     c.add_argument("--counters", nargs="+", default=list(COUNTERS))

@@ -77,7 +77,7 @@ def test_traffic_summary_round_trip(tmp_path):
 
 
 def test_committed_traffic_summary_parses():
-    got = P.load(os.path.join(ROOT, "profiles", "k_fwd_dma_gemma2_2b_head_traffic.md"))
+    got = P.load(os.path.join(ROOT, "profiles", "k_fwd4_gemma2_2b_head_traffic.md"))
     assert got is not None
     nbytes, h = got
     # at least the algorithmic bytes of one launch (H and E once, bf16)
