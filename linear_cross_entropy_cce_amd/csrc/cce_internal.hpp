@@ -87,6 +87,7 @@ struct FwdWs {
     float *part_m;     // [n_rtiles kFwdRanges, kTileRows] per segment: running max (log2 units)
     float *part_s;     // [n_rtiles kFwdRanges, kTileRows] per segment: sum of 2^(z log2e - m)
     float *zy;         // [N] label logit of each valid row, by compacted position
+    int32_t *grid;     // [4] the forward's work split (a, bb, m), recorded for the merge
 };
 FwdWs fwd_ws(void *ws, const FwdShape &s, size_t *bytes);
 

@@ -212,6 +212,24 @@ __device__ __forceinline__ FwdGrid fwd_grid(int nv, int C, int G) {
     return g;
 }
 
+// The forward kernel's workgroup 0 records its choice of (a, bb, m) for the
+// merge (one search per launch instead of one per row).
+__device__ __forceinline__ FwdGrid fwd_grid_record(int nv, int C, int G, int *__restrict__ rec) {
+    const FwdGrid g = fwd_grid(nv, C, G);
+    if (blockIdx.x == 0 && threadIdx.x == 0) { rec[0] = g.a; rec[1] = g.bb; rec[2] = g.m; }
+    return g;
+}
+// The same split as recorded.
+__device__ __forceinline__ FwdGrid fwd_grid_recorded(int nv, int C, int G, const int *__restrict__ rec) {
+    FwdGrid g;
+    g.R = (nv + kTileRows - 1) / kTileRows;
+    g.C = C;
+    g.nx = G % 8 == 0 ? 8 : 1;
+    g.P = G / g.nx;
+    g.a = rec[0]; g.bb = rec[1]; g.m = rec[2];
+    return g;
+}
+
 // The segments of hardware workgroup gid, in order: f(rt, t0, ntile, slot).
 template <class F>
 __device__ __forceinline__ void fwd_segments(const FwdGrid &g, int gid, F &&f) {
@@ -482,11 +500,11 @@ __global__ __launch_bounds__(TileF::kThreads) void k_fwd(
     const T *__restrict__ H, Rows2<const T> E, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, const int64_t *__restrict__ labels,
     const int32_t *__restrict__ inv_perm, int D, int V, int n_vtiles, float *__restrict__ part_m,
-    float *__restrict__ part_s, int *__restrict__ tbound, float *__restrict__ zlab) {
+    float *__restrict__ part_s, int *__restrict__ tbound, float *__restrict__ zlab, int *__restrict__ grid_rec) {
     __shared__ u32x4 lds[TileF::kLdsChunks];
     const int nv = *nvalid_p;
     if (nv <= 0) return;
-    fwd_segments(fwd_grid(nv, n_vtiles, gridDim.x), blockIdx.x, [&](int rt, int t0, int ntile, int64_t slot) {
+    fwd_segments(fwd_grid_record(nv, n_vtiles, gridDim.x, grid_rec), blockIdx.x, [&](int rt, int t0, int ntile, int64_t slot) {
         fwd_segment<T, LAB>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile, slot, lds, part_m,
                             part_s, tbound, zlab);
     });
@@ -585,12 +603,12 @@ __global__ __launch_bounds__(TL::kThreads) void k_fwd_dma(
     const T *__restrict__ H, Rows2<const T> E, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, const int64_t *__restrict__ labels,
     const int32_t *__restrict__ inv_perm, int D, int V, int n_vtiles, float *__restrict__ part_m,
-    float *__restrict__ part_s, int *__restrict__ tbound, float *__restrict__ zlab) {
+    float *__restrict__ part_s, int *__restrict__ tbound, float *__restrict__ zlab, int *__restrict__ grid_rec) {
     using DE = DmaEngine<T, TL, kLogitRowBytes, kLogitStages>;
     __shared__ u32x4 lds[DE::kLdsChunks];
     const int nv = *nvalid_p;
     if (nv <= 0) return;
-    fwd_segments(fwd_grid(nv, n_vtiles, gridDim.x), blockIdx.x, [&](int rt, int t0, int ntile, int64_t slot) {
+    fwd_segments(fwd_grid_record(nv, n_vtiles, gridDim.x, grid_rec), blockIdx.x, [&](int rt, int t0, int ntile, int64_t slot) {
         fwd_segment_dma<T, TL, LAB>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile, slot, lds,
                                     part_m, part_s, tbound, zlab);
     });
@@ -969,11 +987,12 @@ __global__ __launch_bounds__(TileF4::kThreads) void k_fwd4(
     const bf16_t *__restrict__ H, Rows2<const bf16_t> E, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ nvalid_p, const int32_t *__restrict__ perm, const int64_t *__restrict__ labels,
     const int32_t *__restrict__ inv_perm, int D, int V, int n_vtiles, float *__restrict__ part_m,
-    float *__restrict__ part_s, int *__restrict__ tbound, float *__restrict__ zlab, const float *__restrict__ zy) {
+    float *__restrict__ part_s, int *__restrict__ tbound, float *__restrict__ zlab, const float *__restrict__ zy,
+    int *__restrict__ grid_rec) {
     __shared__ u32x4 lds[4 * 2 * kTileVocab * 4];  // 4 buffers of 256 A + 256 B rows of 64 bytes
     const int nv = *nvalid_p;
     if (nv <= 0) return;
-    fwd_segments(fwd_grid(nv, n_vtiles, gridDim.x), blockIdx.x, [&](int rt, int t0, int ntile, int64_t slot) {
+    fwd_segments(fwd_grid_record(nv, n_vtiles, gridDim.x, grid_rec), blockIdx.x, [&](int rt, int t0, int ntile, int64_t slot) {
         fwd4_segment<LAB>(H, E, idx, nv, perm, labels, inv_perm, D, V, n_vtiles, rt, t0, ntile, slot, lds, part_m,
                           part_s, tbound, zlab, zy);
     });
@@ -1025,7 +1044,8 @@ __global__ __launch_bounds__(256) void k_label_dot(const T *__restrict__ H, Rows
 __global__ __launch_bounds__(256) void k_merge(const int64_t *__restrict__ labels, const int32_t *__restrict__ idx,
                                                const int32_t *__restrict__ nvalid_p,
                                                const float *__restrict__ part_m, const float *__restrict__ part_s,
-                                               const float *__restrict__ zy, int G, int n_vtiles, int64_t N, int64_t V,
+                                               const float *__restrict__ zy, const int *__restrict__ grid_rec, int G,
+                                               int n_vtiles, int64_t N, int64_t V,
                                                int64_t ignore_index, float *__restrict__ loss,
                                                float *__restrict__ lse) {
     const int lane = threadIdx.x & 63;
@@ -1041,7 +1061,7 @@ __global__ __launch_bounds__(256) void k_merge(const int64_t *__restrict__ label
         return;
     }
     const int rt = (int)(w / kTileRows), c = (int)(w % kTileRows);
-    const FwdGrid g = fwd_grid(nv, n_vtiles, G);
+    const FwdGrid g = fwd_grid_recorded(nv, n_vtiles, G, grid_rec);
     const int b = g.b();  // at most 64 ranges: one per lane
     const bool seg = lane < b && g.vt0(lane + 1) > g.vt0(lane);  // (an empty range has no segment)
     const int64_t at = ((int64_t)rt * b + lane) * kTileRows + c;
@@ -1112,6 +1132,7 @@ FwdWs fwd_ws(void *ws, const FwdShape &s, size_t *bytes) {
     w.part_m = c.take<float>((size_t)s.n_rtiles * kFwdRanges * kTileRows);
     w.part_s = c.take<float>((size_t)s.n_rtiles * kFwdRanges * kTileRows);
     w.zy = c.take<float>(s.N);
+    w.grid = c.take<int32_t>(4);
     if (bytes) *bytes = c.off;
     return w;
 }
@@ -1193,29 +1214,29 @@ static hipError_t forward_t(const T *H, Rows2<const T> E, const int64_t *labels,
         if (four) {
             if (tb)
                 hipLaunchKernelGGL(k_fwd4<true>, grid, dim3(TileF4::kThreads), 0, st, H, E, w.idx, w.nvalid, perm,
-                                   labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl, w.zy);
+                                   labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl, w.zy, w.grid);
             else
                 hipLaunchKernelGGL(k_fwd4<false>, grid, dim3(TileF4::kThreads), 0, st, H, E, w.idx, w.nvalid, perm,
-                                   labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl, w.zy);
+                                   labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl, w.zy, w.grid);
         }
     }
     if (four)
         ;
     else if (dma && tb)
         hipLaunchKernelGGL((k_fwd_dma<T, TileFD, true>), grid, dim3(TileFD::kThreads), 0, st, H, E, w.idx, w.nvalid,
-                           perm, labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
+                           perm, labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl, w.grid);
     else if (dma)
         hipLaunchKernelGGL((k_fwd_dma<T, TileFD, false>), grid, dim3(TileFD::kThreads), 0, st, H, E, w.idx, w.nvalid,
-                           perm, labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
+                           perm, labels, invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl, w.grid);
     else if (tb)
         hipLaunchKernelGGL((k_fwd<T, true>), grid, dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid, perm, labels,
-                           invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
+                           invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl, w.grid);
     else
         hipLaunchKernelGGL((k_fwd<T, false>), grid, dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid, perm, labels,
-                           invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl);
+                           invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl, w.grid);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_merge, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, labels, w.idx, w.nvalid,
-                       w.part_m, w.part_s, w.zy, (int)G, s.n_vtiles, s.N, s.V, ignore_index, loss, lse);
+                       w.part_m, w.part_s, w.zy, w.grid, (int)G, s.n_vtiles, s.N, s.V, ignore_index, loss, lse);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (tb) hipLaunchKernelGGL(k_bound_decode, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, st, tb, nb);
     return hipGetLastError();
