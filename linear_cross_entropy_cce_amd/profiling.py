@@ -49,7 +49,7 @@ import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL = "k_fwd4"
-SOURCES = ("csrc/fwd.hip", "csrc/cce_device.hpp", "csrc/cce_internal.hpp")
+SOURCES = ("csrc/fwd.hip", "csrc/k4.hpp", "csrc/cce_device.hpp", "csrc/cce_internal.hpp")
 
 
 def _code_only(text: str) -> str:
