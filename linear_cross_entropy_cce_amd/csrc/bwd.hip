@@ -55,21 +55,21 @@ static_assert(kTileVocab == 2 * kBlockVocab && kTileRows == 2 * kBlockRows, "a l
 
 constexpr int kBlockElems = kBlockRows * kBlockVocab;  // elements of one stored block
 constexpr int kListCap = 512;
-// A vocabulary block whose kept blocks are all label-only, at most this many,
-// gets its dE rows from the label entries directly (no block products).
-constexpr int kLabelPathBlocks = 4;
 // At most this many label entries go through the label path at once.
-constexpr int kLabelEntries = kLabelPathBlocks * kBlockRows;
+constexpr int kLabelEntries = 512;
 // A vocabulary block whose kept blocks are all label-only takes the label
-// path (its dE rows from the label entries) with at most kLabelPathBlocks of
-// them, or with at most kSparseLabelBlocks holding at most
-// kSparseLabelEntries label entries; each entry costs a pass over a row of
-// H, which beats the block products only while the entries are few.
-constexpr int kSparseLabelBlocks = 32;
-constexpr int kSparseLabelEntries = 64;
-__host__ __device__ __forceinline__ bool label_path_ok(int n_blocks, int n_entries) {
-    return n_blocks <= kLabelPathBlocks || (n_blocks <= kSparseLabelBlocks && n_entries <= kSparseLabelEntries);
-}
+// path (its dE rows from the label entries, one pass over a row of H per
+// entry, instead of block products over every token of its kept blocks)
+// when it has at most kLabelEntries label entries.
+__host__ __device__ __forceinline__ bool label_path_ok(int n_entries) { return n_entries <= kLabelEntries; }
+// A static column (see k_plan) with more label entries than this is split
+// into one work item per 256-feature tile; the others are one item each.
+constexpr int kColSplitEntries = 32;
+// Feature tile of a static column item that covers every feature.
+constexpr int kAllFeatures = -1;
+// 256-feature tiles of a row of D features (the products' tile width).
+__host__ __device__ __forceinline__ int n_feature_tiles(int64_t D) { return (int)((D + 255) / 256); }
+static_assert(TileG::BN == 256, "feature tiles of the products");
 constexpr int kDeGroups = 2 * kPassGroups;  // persistent dE workgroups of the gradient-product kernel
 
 // Plan record: P, number of listed tiles, first vocabulary tile of each pass
@@ -128,6 +128,7 @@ struct BwdArgs {
     int32_t *slot;
     uint16_t *smask;  // bit 4 i + j: sub-tile (vocabulary rows 32 i.., tokens 32 j..) of a kept block may be nonzero
     const int32_t *cpre, *slist, *dlist;  // column lists of k_plan
+    const int32_t *ipre, *citem, *cft;    // static column items of k_plan
     const int32_t *cent;                  // label entries per column
     int CB;                               // vocabulary blocks
     int64_t *stats;
@@ -382,27 +383,32 @@ __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ 
 // floor(cum(vt) / cap_eff) with cum the inclusive block count; a vocabulary
 // tile adds at most cap - cap_eff blocks, so no pass exceeds cap.
 // Columns (vocabulary blocks cb < CB): with static_ok, a column none of
-// whose blocks may keep a softmax part and whose label blocks and entries
-// pass label_path_ok is static: its kept blocks can only be label-only, so
-// its dE rows come from the label entries (or are zero) for all features at
-// once, as the per-feature-tile items would write them.
+// whose blocks may keep a softmax part and whose label entries pass
+// label_path_ok is static: its kept blocks can only be label-only, so its dE
+// rows come from the label entries (or are zero), as the per-feature-tile
+// items would write them.
 // slist holds the static columns in order, dlist the others, and cpre[cb]
-// the static columns before cb (cpre[CB] all of them).  The label-only
-// blocks of static columns (their label blocks) are counted into stats[1]
-// here; the tile epilogue counts the others.
+// the static columns before cb (cpre[CB] all of them).  A static column is
+// one work item, or n_dt (one per 256-feature tile) when it has more than
+// kColSplitEntries label entries: citem and cft list the items in column
+// order (column, feature tile or kAllFeatures for a whole column) and
+// ipre[j] the items before static column j (ipre[cpre[CB]] all of them).  The
+// label-only blocks of static columns (their label blocks) are counted into
+// stats[1] here; the tile epilogue counts the others.
 __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ vneed, const int32_t *__restrict__ vact,
                                                int n_vt, int64_t cap, int64_t cap_eff, int max_passes,
                                                int32_t *__restrict__ plan, int64_t *__restrict__ cum,
                                                int32_t *__restrict__ act, int CB, int static_ok,
                                                const uint8_t *__restrict__ csoft, const int32_t *__restrict__ cnlab,
                                                const int32_t *__restrict__ cent, int32_t *__restrict__ cpre,
-                                               int32_t *__restrict__ slist, int32_t *__restrict__ dlist,
-                                               int64_t *__restrict__ stats) {
+                                               int32_t *__restrict__ slist, int32_t *__restrict__ dlist, int n_dt,
+                                               int32_t *__restrict__ ipre, int32_t *__restrict__ citem,
+                                               int32_t *__restrict__ cft, int64_t *__restrict__ stats) {
     __shared__ int64_t wsum[16];
     __shared__ int32_t wact[16];
-    __shared__ int32_t wcol[16];
+    __shared__ int32_t wcol[16], witem[16];
     __shared__ int64_t carry_n;
-    __shared__ int32_t carry_a, carry_c;
+    __shared__ int32_t carry_a, carry_c, carry_i;
     const PlanView pv = plan_view(plan, max_passes);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     if (t == 0) { carry_n = 0; carry_a = 0; }
@@ -463,34 +469,48 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ vneed
     for (int q = t; q < max_passes; q += 1024) pv.counter[q] = 0;
     for (int q = t; q < kQueues * max_passes; q += 1024) plan_queues(plan, max_passes, 0)[q] = 0;
 
-    if (t == 0) carry_c = 0;
+    if (t == 0) { carry_c = 0; carry_i = 0; }
     __syncthreads();
     int64_t n_static_lab = 0;
+    const bool can_split = n_dt > 1;
     for (int base = 0; base < CB; base += 1024) {
         const int cb = base + t;
-        const int is_s = (cb < CB && static_ok && !csoft[cb] && label_path_ok(cnlab[cb], cent[cb])) ? 1 : 0;
+        const int is_s = (cb < CB && static_ok && !csoft[cb] && label_path_ok(cent[cb])) ? 1 : 0;
+        const int ni = is_s ? (can_split && cent[cb] > kColSplitEntries ? n_dt : 1) : 0;
         if (is_s) n_static_lab += cnlab[cb];
-        int x = is_s;
+        int x = is_s, xi = ni;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const int y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
+            const int yi = __shfl_up(xi, o, 64);
+            if (lane >= o) { x += y; xi += yi; }
         }
-        if (lane == 63) wcol[w] = x;
+        if (lane == 63) { wcol[w] = x; witem[w] = xi; }
         __syncthreads();
-        int off = carry_c;
-        for (int k = 0; k < w; ++k) off += wcol[k];
-        const int excl = off + x - is_s;
+        int off = carry_c, offi = carry_i;
+        for (int k = 0; k < w; ++k) { off += wcol[k]; offi += witem[k]; }
+        const int excl = off + x - is_s, iexcl = offi + xi - ni;
         if (cb < CB) {
             cpre[cb] = excl;
-            if (is_s) slist[excl] = cb;
-            else dlist[cb - excl] = cb;
+            if (is_s) {
+                slist[excl] = cb;
+                ipre[excl] = iexcl;
+                for (int k = 0; k < ni; ++k) {
+                    citem[iexcl + k] = cb;
+                    cft[iexcl + k] = ni == 1 ? kAllFeatures : k;
+                }
+            } else {
+                dlist[cb - excl] = cb;
+            }
         }
         __syncthreads();
-        if (t == 1023) carry_c = off + x;
+        if (t == 1023) { carry_c = off + x; carry_i = offi + xi; }
         __syncthreads();
     }
-    if (t == 0) cpre[CB] = carry_c;
+    if (t == 0) {
+        cpre[CB] = carry_c;
+        ipre[carry_c] = carry_i;
+    }
     if (stats) {
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) n_static_lab += __shfl_xor(n_static_lab, o, 64);
@@ -1276,19 +1296,20 @@ __device__ __forceinline__ int de_try_label(GradLds<T> &sh, int cb, int d0, int 
         },
         sh.list, sh.wcnt);
     // (build_list ends with a barrier: sh.soft is final)
-    if (!lc.labels || n == 0 || sh.soft || !label_path_ok(n, lc.cent[cb])) return n;
+    if (!lc.labels || n == 0 || sh.soft || !label_path_ok(lc.cent[cb])) return n;
     label_group<T>(sh, n, cb, lc, V);
     label_rows<T>(sh, cb, d0, d0 + TileG::BN, lc, perm, D, V, dE);
     return -1;
 }
 
-// dE rows of a static vocabulary block cb (see k_plan) over all features:
-// its kept blocks are all label-only and pass label_path_ok, so its rows are
-// the label entries' sums in token order (zero rows when nothing is kept).
+// dE rows of a static vocabulary block cb (see k_plan), features
+// [d_lo, d_hi): its kept blocks are all label-only and pass label_path_ok, so
+// its rows are the label entries' sums in token order (zero rows when
+// nothing is kept).
 template <typename T>
-__device__ __forceinline__ void de_column_item(GradLds<T> &sh, int cb, int n_rb, const uint8_t *__restrict__ st,
-                                               int cbp, const LabelCols<T> &lc, const int32_t *__restrict__ perm,
-                                               int D, int V, Rows2<T> dE) {
+__device__ __forceinline__ void de_column_item(GradLds<T> &sh, int cb, int d_lo, int d_hi, int n_rb,
+                                               const uint8_t *__restrict__ st, int cbp, const LabelCols<T> &lc,
+                                               const int32_t *__restrict__ perm, int D, int V, Rows2<T> dE) {
     const int n = build_list<TileG::kThreads>(
         n_rb, [&](int i) { return st[(int64_t)i * cbp + cb] != 0; }, sh.list, sh.wcnt);
     if (n > 0) {
@@ -1297,7 +1318,7 @@ __device__ __forceinline__ void de_column_item(GradLds<T> &sh, int cb, int n_rb,
         for (int r = threadIdx.x; r <= kBlockVocab; r += TileG::kThreads) sh.rlo[r] = 0;
         __syncthreads();
     }
-    label_rows<T>(sh, cb, 0, D, lc, perm, D, V, dE);
+    label_rows<T>(sh, cb, d_lo, d_hi, lc, perm, D, V, dE);
 }
 
 // dE for one (vocabulary block cb, 256-feature tile d0) item of a pass.  K
@@ -1636,11 +1657,12 @@ __device__ __forceinline__ void dh_item(GradLds<T> &sh, int rb, int d0, bool mul
 }
 
 // --------------------------------------------------- gradient products
-// Gradient phase of pass p on workgroups bid = 0 .. nbid - 1, which take
-// items from a work queue, longer items first: the (row block, feature
-// tile) dH items, then the (vocabulary block, feature tile) dE items of the
-// vocabulary blocks that are not static, then one item per static
-// vocabulary block of the pass (all features).
+// Gradient phase of pass p: the workgroups take items from a work queue,
+// longer items first: the (vocabulary block, feature tile) dE items of the
+// vocabulary blocks that are not static (block products over every kept row
+// block: the longest), then the (row block, feature tile) dH items, then the
+// items of the pass's static vocabulary blocks (all features, or one
+// feature tile of a block with many label entries).
 template <typename T, bool KAHAN, bool FINE>
 __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, GradLds<T> &sh, int *ticket) {
     using TL = TileG;
@@ -1653,35 +1675,40 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
     const int n_dt = (a.D + TL::BN - 1) / TL::BN;
     const int n_rbv = (nv + kBlockRows - 1) / kBlockRows;
     const int64_t n_dh = (int64_t)n_rbv * n_dt;
-    // the pass's static columns are slist[s_lo, s_hi), the others dlist[c_lo, c_lo + n_dyn)
+    // the pass's static columns are slist[s_lo, s_hi) (their items
+    // citem[i_lo, i_hi)), the others dlist[c_lo, c_lo + n_dyn)
     const int s_lo = cb1 > cb0 ? a.cpre[cb0] : 0, s_hi = cb1 > cb0 ? a.cpre[cb1] : 0;
+    const int i_lo = cb1 > cb0 ? a.ipre[s_lo] : 0, i_hi = cb1 > cb0 ? a.ipre[s_hi] : 0;
     const int c_lo = cb0 - s_lo;
     const int n_dyn = cb1 > cb0 ? (cb1 - cb0) - (s_hi - s_lo) : 0;
-    const int64_t n_col = s_hi - s_lo;
+    const int64_t n_col = i_hi - i_lo;
     const int64_t n_de = (int64_t)n_dyn * n_dt;
     // (no label path for the full classifier gradient: its label-only blocks
     // store the unfiltered gradient for dE)
     const LabelCols<T> lc{a.full_de ? nullptr : a.labels, a.idx, a.inv_perm, a.glab, a.H, nv, a.cent};
     // two loops rather than one with a branch: each keeps its own registers
     int64_t it = take_ticket(queue, ticket);
-    while (it < n_dh) {
-        dh_item<T, FINE>(sh, (int)(it % n_rbv), (int)(it / n_rbv) * TL::BN, P > 1, p == 0, p == P - 1, cb0, cb1, a.st,
-                         a.slot, a.cbp, nv, a.idx, a.Gn, a.E, a.perm, a.D, a.V, a.glab, a.labels, a.dh_acc, a.dH,
-                         a.smask);
-        it = take_ticket(queue, ticket);
-    }
-    while (it < n_dh + n_de) {
-        const int64_t q = it - n_dh;
-        const int cb = a.dlist[c_lo + (int)(q / n_dt)], d0 = (int)(q % n_dt) * TL::BN;
+    while (it < n_de) {
+        const int cb = a.dlist[c_lo + (int)(it / n_dt)], d0 = (int)(it % n_dt) * TL::BN;
         const int n = de_try_label<T>(sh, cb, d0, n_rbv, a.st, a.cbp, lc, a.perm, a.D, a.V, a.dE);
         if (n != -1)
             de_item<T, KAHAN, FINE>(sh, cb, d0, n_rbv, a.st, a.slot, a.cbp, a.Gt, a.Ht, a.ldh, a.perm, a.D, a.V, a.dE,
                                     n >= 0 ? n : -1, a.smask);
         it = take_ticket(queue, ticket);
     }
-    while (it < n_dh + n_de + n_col) {
-        de_column_item<T>(sh, a.slist[s_lo + (int)(it - n_dh - n_de)], n_rbv, a.st, a.cbp, lc, a.perm, a.D, a.V,
-                          a.dE);
+    while (it < n_de + n_dh) {
+        const int64_t q = it - n_de;
+        dh_item<T, FINE>(sh, (int)(q % n_rbv), (int)(q / n_rbv) * TL::BN, P > 1, p == 0, p == P - 1, cb0, cb1, a.st,
+                         a.slot, a.cbp, nv, a.idx, a.Gn, a.E, a.perm, a.D, a.V, a.glab, a.labels, a.dh_acc, a.dH,
+                         a.smask);
+        it = take_ticket(queue, ticket);
+    }
+    while (it < n_de + n_dh + n_col) {
+        const int ci = i_lo + (int)(it - n_de - n_dh);
+        const int cb = a.citem[ci], ft = a.cft[ci];
+        const int d_lo = ft == kAllFeatures ? 0 : ft * TL::BN;
+        const int d_hi = ft == kAllFeatures ? a.D : min(a.D, d_lo + TL::BN);
+        de_column_item<T>(sh, cb, d_lo, d_hi, n_rbv, a.st, a.cbp, lc, a.perm, a.D, a.V, a.dE);
         it = take_ticket(queue, ticket);
     }
 }
@@ -1758,6 +1785,11 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     w.smask = c.take<uint16_t>(nblk);
     w.cpre = c.take<int32_t>((size_t)s.cbp + 1);
     w.slist = c.take<int32_t>((size_t)s.cbp);
+    w.ipre = c.take<int32_t>((size_t)s.cbp + 1);
+    // (a split column has more than kColSplitEntries of the N label entries)
+    const size_t n_items = (size_t)s.cbp + (size_t)(s.N / (kColSplitEntries + 1) + 1) * (size_t)n_feature_tiles(s.D);
+    w.citem = c.take<int32_t>(n_items);
+    w.cft = c.take<int32_t>(n_items);
     w.dlist = c.take<int32_t>((size_t)s.cbp);
     w.tneed = c.take<uint8_t>(ntile);
     w.cum = c.take<int64_t>((size_t)s.n_vtiles);
@@ -1848,7 +1880,7 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     const int static_ok = (!full_de && s.n_rb <= kListCap) ? 1 : 0;
     hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, w.vneed, w.vact, s.n_vtiles, s.cap, s.cap_eff,
                        s.max_passes, w.plan, w.cum, w.act, CB, static_ok, w.csoft, w.cnlab, w.cent, w.cpre, w.slist,
-                       w.dlist, stats);
+                       w.dlist, n_feature_tiles(D), w.ipre, w.citem, w.cft, stats);
     CCE_LAUNCHED();
     hipLaunchKernelGGL(k_tile_list, dim3((unsigned)ceil_div(s.n_vtiles, 4)), dim3(256), 0, st, w.tneed, s.n_rtiles,
                        s.n_vtiles, w.act, w.lab, s.cbp, w.cpre, CB, w.tlist);
@@ -1896,6 +1928,9 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     a.smask = w.smask;
     a.cpre = w.cpre;
     a.slist = w.slist;
+    a.ipre = w.ipre;
+    a.citem = w.citem;
+    a.cft = w.cft;
     a.dlist = w.dlist;
     a.cent = w.cent;
     a.CB = CB;

@@ -127,6 +127,9 @@ struct BwdWs {
     int32_t *vact;     // [n_vtiles] its tiles that may keep one
     int32_t *cpre;     // [cbp + 1] static columns (see k_plan) before each column
     int32_t *slist;    // [cbp] static columns, in order
+    int32_t *ipre;     // [cbp + 1] work items before each static column (slist order)
+    int32_t *citem;    // work items of the static columns: column
+    int32_t *cft;      //   and 256-feature tile (-1: every feature)
     int32_t *dlist;    // [cbp] the other columns, in order
     uint8_t *tneed;    // [n_vtiles, n_rtiles] blocks the tile may keep (bits 0-2), recompute flag (bit 7)
     int64_t *cum;      // [n_vtiles] plan scratch: cumulative blocks

@@ -750,14 +750,29 @@ __global__ __launch_bounds__(256) void k_label_dot(const T *__restrict__ H, Rows
     constexpr int CE = ChunkElems<T>::value;
     const char *h = reinterpret_cast<const char *>(H + i * (int64_t)D);
     const char *e = reinterpret_cast<const char *>(E.row(y));
+    // (the loads of up to kU chunks per lane are issued before the first is
+    // used; the products are still added chunk by chunk in feature order)
+    constexpr int kU = 8;
     float dot = 0.f;
-    for (int k = lane * CE; k < D; k += 64 * CE) {
-        const u32x4 hv = ld16(h + k * sizeof(T));
-        const u32x4 ev = ld16(e + k * sizeof(T));
-        const T *hp = reinterpret_cast<const T *>(&hv);
-        const T *ep = reinterpret_cast<const T *>(&ev);
+    for (int k0 = lane * CE; k0 < D; k0 += kU * 64 * CE) {
+        u32x4 hv[kU], ev[kU];
 #pragma unroll
-        for (int q = 0; q < CE; ++q) dot += to_f32(hp[q]) * to_f32(ep[q]);
+        for (int u = 0; u < kU; ++u) {
+            const int k = k0 + u * 64 * CE;
+            if (k < D) {
+                hv[u] = ld16(h + k * sizeof(T));
+                ev[u] = ld16(e + k * sizeof(T));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (k0 + u * 64 * CE < D) {
+                const T *hp = reinterpret_cast<const T *>(&hv[u]);
+                const T *ep = reinterpret_cast<const T *>(&ev[u]);
+#pragma unroll
+                for (int q = 0; q < CE; ++q) dot += to_f32(hp[q]) * to_f32(ep[q]);
+            }
+        }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 64);
@@ -765,49 +780,55 @@ __global__ __launch_bounds__(256) void k_label_dot(const T *__restrict__ H, Rows
 }
 
 // ------------------------------------------------------------------ merge
-// One wave per position w: it zeroes row w if that row is ignored, and if
-// w < nv it finishes the valid row at compacted position w.  Lane j takes the
-// partial of the row's token tile and vocabulary range j (if that range is
-// not empty); the max and the scaled sum are butterfly reductions, so the
-// result depends only on the partition, never on scheduling.
-__global__ __launch_bounds__(256) void k_merge(const int64_t *__restrict__ labels, const int32_t *__restrict__ idx,
-                                               const int32_t *__restrict__ nvalid_p,
-                                               const float *__restrict__ part_m, const float *__restrict__ part_s,
-                                               const float *__restrict__ zy, const int *__restrict__ grid_rec, int G,
-                                               int n_vtiles, int64_t N, int64_t V,
-                                               int64_t ignore_index, float *__restrict__ loss,
-                                               float *__restrict__ lse) {
-    const int lane = threadIdx.x & 63;
-    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (w >= N) return;
-    if (labels[w] == ignore_index && lane == 0) { loss[w] = 0.f; lse[w] = 0.f; }
+// One thread per position w: it zeroes row w if that row is ignored, and if
+// w < nv it finishes the valid row at compacted position w.  A workgroup is
+// one token tile, so the partial of vocabulary range j is one coalesced
+// 1 KB row of the partial buffers for the whole workgroup.  The max and the
+// scaled sum run over the ranges in vocabulary order, so the result depends
+// only on the partition, never on scheduling.
+__global__ __launch_bounds__(kTileRows) void k_merge(const int64_t *__restrict__ labels,
+                                                     const int32_t *__restrict__ idx,
+                                                     const int32_t *__restrict__ nvalid_p,
+                                                     const float *__restrict__ part_m,
+                                                     const float *__restrict__ part_s, const float *__restrict__ zy,
+                                                     const int *__restrict__ grid_rec, int G, int n_vtiles,
+                                                     int64_t N, int64_t V, int64_t ignore_index,
+                                                     float *__restrict__ loss, float *__restrict__ lse) {
+    __shared__ int seg_on[kFwdRanges];  // range j has a segment (is not empty)
+    const int rt = blockIdx.x, c = threadIdx.x;
     const int nv = *nvalid_p;
+    const FwdGrid g = fwd_grid_recorded(nv, n_vtiles, G, grid_rec);
+    const int b = g.b();  // at most kFwdRanges
+    if (c < kFwdRanges) seg_on[c] = c < b && g.vt0(c + 1) > g.vt0(c);
+    __syncthreads();
+    const int64_t w = (int64_t)rt * kTileRows + c;
+    if (w >= N) return;
+    if (labels[w] == ignore_index) { loss[w] = 0.f; lse[w] = 0.f; }
     if (w >= nv) return;
     const int64_t i = idx[w];
     const int64_t y = labels[i];
     if (y < 0 || y >= V) {  // not a valid label: undefined by contract; flag it, touch nothing
-        if (lane == 0) { loss[i] = __builtin_nanf(""); lse[i] = __builtin_nanf(""); }
+        loss[i] = __builtin_nanf("");
+        lse[i] = __builtin_nanf("");
         return;
     }
-    const int rt = (int)(w / kTileRows), c = (int)(w % kTileRows);
-    const FwdGrid g = fwd_grid_recorded(nv, n_vtiles, G, grid_rec);
-    const int b = g.b();  // at most 64 ranges: one per lane
-    const bool seg = lane < b && g.vt0(lane + 1) > g.vt0(lane);  // (an empty range has no segment)
-    const int64_t at = ((int64_t)rt * b + lane) * kTileRows + c;
-    const float pm = seg ? part_m[at] : kNegInf;
-    float M = pm;
+    const int64_t base = (int64_t)rt * b * kTileRows + c;
+    float pm[kFwdRanges], ps[kFwdRanges];
+    float M = kNegInf;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    float S = pm != kNegInf ? part_s[at] * __builtin_amdgcn_exp2f(pm - M) : 0.f;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) S += __shfl_xor(S, o, 64);
-
-    const float dot = zy[w];  // z_{i, y_i}
-    if (lane == 0) {
-        const float l = (M + log2f(S)) * kLn2;
-        lse[i] = l;
-        loss[i] = l - dot;
+    for (int j = 0; j < kFwdRanges; ++j) {
+        const bool seg = seg_on[j];
+        pm[j] = seg ? part_m[base + (int64_t)j * kTileRows] : kNegInf;
+        ps[j] = seg ? part_s[base + (int64_t)j * kTileRows] : 0.f;
+        M = fmaxf(M, pm[j]);
     }
+    float S = 0.f;
+#pragma unroll
+    for (int j = 0; j < kFwdRanges; ++j)
+        if (pm[j] != kNegInf) S += ps[j] * __builtin_amdgcn_exp2f(pm[j] - M);
+    const float l = (M + log2f(S)) * kLn2;
+    lse[i] = l;
+    loss[i] = l - zy[w];  // zy[w] = z_{i, y_i}
 }
 
 // ------------------------------------------------- allocation-free forward
@@ -964,7 +985,7 @@ static hipError_t forward_t(const T *H, Rows2<const T> E, const int64_t *labels,
         hipLaunchKernelGGL((k_fwd<T, false>), grid, dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid, perm, labels,
                            invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl, w.grid);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_merge, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, labels, w.idx, w.nvalid,
+    hipLaunchKernelGGL(k_merge, dim3((unsigned)ceil_div(s.N, kTileRows)), dim3(kTileRows), 0, st, labels, w.idx, w.nvalid,
                        w.part_m, w.part_s, w.zy, w.grid, (int)G, s.n_vtiles, s.N, s.V, ignore_index, loss, lse);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (tb) hipLaunchKernelGGL(k_bound_decode, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, st, tb, nb);
