@@ -67,8 +67,10 @@ __host__ __device__ __forceinline__ bool label_path_ok(int n_entries) { return n
 constexpr int kColSplitEntries = 32;
 // Feature tile of a static column item that covers every feature.
 constexpr int kAllFeatures = -1;
-// 256-feature tiles of a row of D features (the products' tile width).
+// 256-feature tiles of a row of D features (the products' tile width), and
+// the 64-feature tiles of a hot column's items.
 __host__ __device__ __forceinline__ int n_feature_tiles(int64_t D) { return (int)((D + 255) / 256); }
+__host__ __device__ __forceinline__ int n_hot_tiles(int64_t D) { return (int)((D + 63) / 64); }
 static_assert(TileG::BN == 256, "feature tiles of the products");
 constexpr int kDeGroups = 2 * kPassGroups;  // persistent dE workgroups of the gradient-product kernel
 
@@ -129,6 +131,7 @@ struct BwdArgs {
     uint16_t *smask;  // bit 4 i + j: sub-tile (vocabulary rows 32 i.., tokens 32 j..) of a kept block may be nonzero
     const int32_t *cpre, *slist, *dlist;  // column lists of k_plan
     const int32_t *ipre, *citem, *cft;    // static column items of k_plan
+    const int32_t *hidx, *hent, *hrlo, *hent_t;  // hot columns (k_plan, k_hot_entries)
     const int32_t *cent;                  // label entries per column
     int CB;                               // vocabulary blocks
     int64_t *stats;
@@ -312,16 +315,21 @@ __device__ __forceinline__ int build_stages(int n, int kspb, const int *mask, Se
 // in vocabulary block cb (processing order; zeroed before).  A block holds
 // at most 128 tokens, so each count fits its byte: the byte is added to
 // through its aligned 32-bit word (the map's region is 256-byte aligned and
-// padded).
+// padded).  tpos[t] = the label's position in processing order (-1: not a
+// valid label).
 __global__ __launch_bounds__(256) void k_label_map(const int64_t *__restrict__ labels, const int32_t *__restrict__ idx,
                                                    const int32_t *__restrict__ nvalid_p,
                                                    const int32_t *__restrict__ inv_perm, int64_t V, int cbp,
-                                                   uint8_t *__restrict__ lab) {
+                                                   uint8_t *__restrict__ lab, int32_t *__restrict__ tpos) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= *nvalid_p) return;
     const int64_t y = labels[idx[t]];
-    if (y < 0 || y >= V) return;  // not a valid label: undefined by contract
+    if (y < 0 || y >= V) {  // not a valid label: undefined by contract
+        tpos[t] = -1;
+        return;
+    }
     const int64_t pos = inv_perm ? inv_perm[y] : y;
+    tpos[t] = (int32_t)pos;
     const int64_t i = (t / kBlockRows) * cbp + pos / kBlockVocab;
     atomicAdd(reinterpret_cast<uint32_t *>(lab + (i & ~int64_t(3))), 1u << (8 * (i & 3)));
 }
@@ -382,17 +390,21 @@ __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ 
 // Passes: one if every block fits the store, else pass(vt) =
 // floor(cum(vt) / cap_eff) with cum the inclusive block count; a vocabulary
 // tile adds at most cap - cap_eff blocks, so no pass exceeds cap.
-// Columns (vocabulary blocks cb < CB): with static_ok, a column none of
-// whose blocks may keep a softmax part and whose label entries pass
-// label_path_ok is static: its kept blocks can only be label-only, so its dE
-// rows come from the label entries (or are zero), as the per-feature-tile
-// items would write them.
+// Columns (vocabulary blocks cb < CB): with static_ok, a column with more
+// than kLabelEntries label entries is hot (hidx[cb] = its index h in hcol,
+// its entries from hent[h] on in the hot entry list; nhot of them), whatever
+// the bound says; and a column none of whose blocks may keep a softmax part
+// and whose label entries pass label_path_ok, or that is hot, is static: its
+// kept blocks can only be label-only, so its dE rows come from the label
+// entries (or are zero), as the per-feature-tile items would write them.
 // slist holds the static columns in order, dlist the others, and cpre[cb]
 // the static columns before cb (cpre[CB] all of them).  A static column is
 // one work item, or n_dt (one per 256-feature tile) when it has more than
-// kColSplitEntries label entries: citem and cft list the items in column
-// order (column, feature tile or kAllFeatures for a whole column) and
-// ipre[j] the items before static column j (ipre[cpre[CB]] all of them).  The
+// kColSplitEntries label entries, or one per 64-feature tile when it is hot:
+// citem and cft list the items in column order (column, and the 256-feature
+// tile, kAllFeatures for a whole column, or -2 - the 64-feature tile of a
+// hot column) and ipre[j] the items before static column j (ipre[cpre[CB]]
+// all of them).  The
 // label-only blocks of static columns (their label blocks) are counted into
 // stats[1] here; the tile epilogue counts the others.
 __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ vneed, const int32_t *__restrict__ vact,
@@ -402,13 +414,16 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ vneed
                                                const uint8_t *__restrict__ csoft, const int32_t *__restrict__ cnlab,
                                                const int32_t *__restrict__ cent, int32_t *__restrict__ cpre,
                                                int32_t *__restrict__ slist, int32_t *__restrict__ dlist, int n_dt,
+                                               int n_d64,
                                                int32_t *__restrict__ ipre, int32_t *__restrict__ citem,
-                                               int32_t *__restrict__ cft, int64_t *__restrict__ stats) {
+                                               int32_t *__restrict__ cft, int32_t *__restrict__ hidx,
+                                               int32_t *__restrict__ hcol, int32_t *__restrict__ hent,
+                                               int32_t *__restrict__ nhot, int64_t *__restrict__ stats) {
     __shared__ int64_t wsum[16];
     __shared__ int32_t wact[16];
-    __shared__ int32_t wcol[16], witem[16];
+    __shared__ int32_t wcol[16], witem[16], whot[16], went[16];
     __shared__ int64_t carry_n;
-    __shared__ int32_t carry_a, carry_c, carry_i;
+    __shared__ int32_t carry_a, carry_c, carry_i, carry_h, carry_e;
     const PlanView pv = plan_view(plan, max_passes);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     if (t == 0) { carry_n = 0; carry_a = 0; }
@@ -469,47 +484,59 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ vneed
     for (int q = t; q < max_passes; q += 1024) pv.counter[q] = 0;
     for (int q = t; q < kQueues * max_passes; q += 1024) plan_queues(plan, max_passes, 0)[q] = 0;
 
-    if (t == 0) { carry_c = 0; carry_i = 0; }
+    if (t == 0) { carry_c = 0; carry_i = 0; carry_h = 0; carry_e = 0; }
     __syncthreads();
     int64_t n_static_lab = 0;
     const bool can_split = n_dt > 1;
     for (int base = 0; base < CB; base += 1024) {
         const int cb = base + t;
-        const int is_s = (cb < CB && static_ok && !csoft[cb] && label_path_ok(cent[cb])) ? 1 : 0;
-        const int ni = is_s ? (can_split && cent[cb] > kColSplitEntries ? n_dt : 1) : 0;
+        const int ce = cb < CB ? cent[cb] : 0;
+        const int hot = (cb < CB && static_ok && !label_path_ok(ce)) ? 1 : 0;
+        const int is_s = (cb < CB && static_ok && !csoft[cb] && (label_path_ok(ce) || hot)) ? 1 : 0;
+        const int ni = is_s ? (hot ? n_d64 : (can_split && ce > kColSplitEntries ? n_dt : 1)) : 0;
         if (is_s) n_static_lab += cnlab[cb];
-        int x = is_s, xi = ni;
+        int x = is_s, xi = ni, xh = hot, xe = hot ? ce : 0;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const int y = __shfl_up(x, o, 64);
             const int yi = __shfl_up(xi, o, 64);
-            if (lane >= o) { x += y; xi += yi; }
+            const int yh = __shfl_up(xh, o, 64);
+            const int ye = __shfl_up(xe, o, 64);
+            if (lane >= o) { x += y; xi += yi; xh += yh; xe += ye; }
         }
-        if (lane == 63) { wcol[w] = x; witem[w] = xi; }
+        if (lane == 63) { wcol[w] = x; witem[w] = xi; whot[w] = xh; went[w] = xe; }
         __syncthreads();
-        int off = carry_c, offi = carry_i;
-        for (int k = 0; k < w; ++k) { off += wcol[k]; offi += witem[k]; }
+        int off = carry_c, offi = carry_i, offh = carry_h, offe = carry_e;
+        for (int k = 0; k < w; ++k) { off += wcol[k]; offi += witem[k]; offh += whot[k]; offe += went[k]; }
         const int excl = off + x - is_s, iexcl = offi + xi - ni;
+        const int hexcl = offh + xh - hot, eexcl = offe + xe - (hot ? ce : 0);
         if (cb < CB) {
             cpre[cb] = excl;
+            hidx[cb] = hot ? hexcl : -1;
+            if (hot) {
+                hcol[hexcl] = cb;
+                hent[hexcl] = eexcl;
+            }
             if (is_s) {
                 slist[excl] = cb;
                 ipre[excl] = iexcl;
                 for (int k = 0; k < ni; ++k) {
                     citem[iexcl + k] = cb;
-                    cft[iexcl + k] = ni == 1 ? kAllFeatures : k;
+                    cft[iexcl + k] = hot ? -2 - k : (ni == 1 ? kAllFeatures : k);
                 }
             } else {
                 dlist[cb - excl] = cb;
             }
         }
         __syncthreads();
-        if (t == 1023) { carry_c = off + x; carry_i = offi + xi; }
+        if (t == 1023) { carry_c = off + x; carry_i = offi + xi; carry_h = offh + xh; carry_e = offe + xe; }
         __syncthreads();
     }
     if (t == 0) {
         cpre[CB] = carry_c;
         ipre[carry_c] = carry_i;
+        hent[carry_h] = carry_e;
+        *nhot = carry_h;
     }
     if (stats) {
 #pragma unroll
@@ -583,6 +610,106 @@ __global__ __launch_bounds__(256) void k_label_static(const int64_t *__restrict_
     if (dl != 0.f) {
         const float pl = __builtin_amdgcn_exp2f((zlab[row] - lse[row]) * kLog2e);
         glab[t] = dl * (pl - 1.f);
+    }
+}
+
+// The label entries of each hot column (see k_plan), one workgroup per
+// column: the valid tokens t whose label falls in column hcol[h], grouped by
+// vocabulary row with a stable counting sort (token order within a row):
+// row r's entries are hent_t[hent[h] + hrlo[129 h + r] ..
+// hent[h] + hrlo[129 h + r + 1]).  Counts are order-free LDS atomics; the
+// positions come from wave ballots per chunk of 1024 tokens in order, the
+// earlier waves' counts and a running count per row.
+constexpr int kHotBatch = 8;  // chunks of 1024 tokens whose positions are loaded at once
+__global__ __launch_bounds__(1024) void k_hot_entries(const int32_t *__restrict__ nhot_p,
+                                                      const int32_t *__restrict__ hcol,
+                                                      const int32_t *__restrict__ hent,
+                                                      const int32_t *__restrict__ nvalid_p,
+                                                      const int32_t *__restrict__ tpos, int32_t *__restrict__ hrlo,
+                                                      int32_t *__restrict__ hent_t) {
+    __shared__ int run[kBlockVocab];        // entries per row, then the next position of each row
+    __shared__ int wrow[16][kBlockVocab];   // entries of each row per wave of a chunk
+    __shared__ int part[2];
+    const int h = blockIdx.x;
+    if (h >= *nhot_p) return;  // (uniform)
+    const int cb = hcol[h], nv = *nvalid_p;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    int32_t *out = hent_t + hent[h];
+    if (t < kBlockVocab) run[t] = 0;
+    __syncthreads();
+    // the row of each of this thread's tokens in a batch (-1: not this column)
+    auto rows_of = [&](int b0, int (&row)[kHotBatch]) {
+        int pos[kHotBatch];
+#pragma unroll
+        for (int k = 0; k < kHotBatch; ++k) {
+            const int tok = b0 + k * 1024 + t;
+            pos[k] = tok < nv ? tpos[tok] : -1;
+        }
+#pragma unroll
+        for (int k = 0; k < kHotBatch; ++k) row[k] = (pos[k] >= 0 && pos[k] / kBlockVocab == cb) ? pos[k] % kBlockVocab : -1;
+    };
+    for (int b0 = 0; b0 < nv; b0 += kHotBatch * 1024) {
+        int row[kHotBatch];
+        rows_of(b0, row);
+#pragma unroll
+        for (int k = 0; k < kHotBatch; ++k)
+            if (row[k] >= 0) atomicAdd(&run[row[k]], 1);
+    }
+    __syncthreads();
+    // exclusive scan of the row counts (two waves), written out and kept as
+    // each row's next position
+    if (t < kBlockVocab) {
+        const int c = run[t];
+        int x = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) part[wave] = x;
+        run[t] = x - c;  // (exclusive within the wave; the first wave's total is added below)
+    }
+    __syncthreads();
+    if (t < kBlockVocab) {
+        if (t >= 64) run[t] += part[0];
+        hrlo[129 * h + t] = run[t];
+        if (t == kBlockVocab - 1) hrlo[129 * h + kBlockVocab] = part[0] + part[1];
+    }
+    __syncthreads();
+    for (int b0 = 0; b0 < nv; b0 += kHotBatch * 1024) {
+        int row[kHotBatch];
+        rows_of(b0, row);
+        for (int k = 0; k < kHotBatch; ++k) {
+            if (b0 + k * 1024 >= nv) break;  // (uniform)
+            const int r = row[k];
+            // lanes of this wave with the same row: rank among them in token order
+            uint64_t same = __ballot(r >= 0);
+#pragma unroll
+            for (int b = 0; b < 7; ++b) {
+                const bool bit = (r >> b) & 1;
+                const uint64_t bal = __ballot(bit);
+                same &= bit ? bal : ~bal;
+            }
+            for (int q = t; q < 16 * kBlockVocab; q += 1024) (&wrow[0][0])[q] = 0;
+            __syncthreads();
+            const int rank = __popcll(same & below);
+            if (r >= 0 && rank == 0) wrow[wave][r] = __popcll(same);
+            __syncthreads();
+            if (r >= 0) {
+                int p = run[r] + rank;
+                for (int w = 0; w < wave; ++w) p += wrow[w][r];
+                out[p] = b0 + k * 1024 + t;
+            }
+            __syncthreads();
+            if (t < kBlockVocab) {
+                int c = 0;
+#pragma unroll
+                for (int w = 0; w < 16; ++w) c += wrow[w][t];
+                run[t] += c;
+            }
+            __syncthreads();
+        }
     }
 }
 
@@ -1123,6 +1250,9 @@ struct LabelCols {
     const T *H;
     int nv;
     const int32_t *cent;  // label entries per vocabulary block
+    // hot columns (k_plan, k_hot_entries): index per column (-1: not hot),
+    // first entry, row ranges and the entries (valid-token positions)
+    const int32_t *hidx, *hent, *hrlo, *hent_t;
 };
 
 // The label entries of vocabulary block cb when every kept block of cb is
@@ -1275,8 +1405,132 @@ __device__ __forceinline__ void label_rows(const GradLds<T> &sh, int cb, int d_l
     }
 }
 
+// dE rows of hot column cb (index h), features [64 f, 64 f + 64) (capped at
+// D), from its label entries (k_hot_entries: grouped by row, token order
+// within a row).  A row's entries are cut into pieces of at most kHotPiece;
+// a batch of kPB pieces is summed with one thread per (piece, 16-byte
+// segment), each piece in token order in fp32, and each row's running sum
+// then adds the batch's pieces of that row in order.  So a frequent label's
+// entries are summed by many threads at once, in a fixed order.
+constexpr int kHotPiece = 32;
+template <typename T>
+__device__ __forceinline__ void hot_item(GradLds<T> &sh, int h, int cb, int f, const LabelCols<T> &lc,
+                                         const int32_t *__restrict__ perm, int D, int V, Rows2<T> dE) {
+    constexpr int kThreads = TileG::kThreads;
+    constexpr int CE = ChunkElems<T>::value;
+    constexpr int kSeg = 64 / CE;           // 16-byte segments of a 64-feature tile
+    constexpr int kPB = kThreads / kSeg;    // pieces per batch
+    constexpr int kBE = kPB * kHotPiece;    // entries of a batch at most
+    static_assert(sizeof(sh.stages) >= sizeof(float) * (kBlockVocab * 64 + kPB * 64 + 2 * kBE + kBlockVocab + 1),
+                  "the hot item's buffers fit the stage buffer");
+    float *run = reinterpret_cast<float *>(sh.stages);  // [128][64] running row sums
+    float *part = run + kBlockVocab * 64;                // [kPB][64] the batch's piece sums
+    int *eh = reinterpret_cast<int *>(part + kPB * 64);  // [kBE] row of H of each entry of the batch
+    float *eg = reinterpret_cast<float *>(eh + kBE);     // [kBE] its gradient
+    int *ppre = reinterpret_cast<int *>(eg + kBE);       // [129] pieces before each row
+    int *rlo = sh.rlo;                                   // [129] entries before each row
+    const int t = threadIdx.x, lane = t & 63;
+    const int d0 = 64 * f;
+    const int32_t *ent = lc.hent_t + lc.hent[h];
+    if (t <= kBlockVocab) rlo[t] = lc.hrlo[129 * h + t];
+    for (int q = t; q < kBlockVocab * 64; q += kThreads) run[q] = 0.f;
+    __syncthreads();
+    if (t < kBlockVocab) {  // pieces per row: exclusive scan over two waves
+        const int c = (rlo[t + 1] - rlo[t] + kHotPiece - 1) / kHotPiece;
+        int x = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        ppre[t + 1] = x;  // inclusive within the wave
+    }
+    __syncthreads();
+    if (t >= 64 && t < kBlockVocab) ppre[t + 1] += ppre[64];
+    if (t == 0) ppre[0] = 0;
+    __syncthreads();
+    const int np = ppre[kBlockVocab];
+    // the row of piece p: the last r with ppre[r] <= p (rows without pieces
+    // have ppre[r] == ppre[r + 1])
+    auto row_of = [&](int p) {
+        int lo = 0, hi = kBlockVocab;  // ppre[lo] <= p < ppre[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (ppre[mid] <= p) lo = mid;
+            else hi = mid;
+        }
+        return lo;
+    };
+    auto piece_begin = [&](int p, int r) { return rlo[r] + (p - ppre[r]) * kHotPiece; };
+    for (int b0 = 0; b0 < np; b0 += kPB) {
+        const int b1 = min(np, b0 + kPB);
+        const int rb0 = row_of(b0), rb1 = row_of(b1 - 1);
+        const int e_lo = piece_begin(b0, rb0);
+        const int e_hi = min(piece_begin(b1 - 1, rb1) + kHotPiece, rlo[rb1 + 1]);
+        for (int k = t; k < e_hi - e_lo; k += kThreads) {
+            const int tok = ent[e_lo + k];
+            eh[k] = lc.idx[tok];
+            eg[k] = lc.glab[tok];
+        }
+        __syncthreads();
+        {
+            const int ps = t / kSeg, sg = t % kSeg, p = b0 + ps;
+            const int d = d0 + sg * CE;
+            float acc[CE];
+#pragma unroll
+            for (int c = 0; c < CE; ++c) acc[c] = 0.f;
+            if (p < b1 && d < D) {
+                const int r = row_of(p);
+                const int e_begin = piece_begin(p, r) - e_lo;
+                const int e_end = min(piece_begin(p, r) + kHotPiece, rlo[r + 1]) - e_lo;
+                for (int e = e_begin; e < e_end; e += 8) {  // eight loads in flight, added in entry order
+                    u32x4 hv[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (e + u < e_end)
+                            hv[u] = ld16(reinterpret_cast<const char *>(lc.H + (int64_t)eh[e + u] * D + d));
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (e + u < e_end) {
+                            const T *hp = reinterpret_cast<const T *>(&hv[u]);
+                            const float ge = eg[e + u];
+#pragma unroll
+                            for (int c = 0; c < CE; ++c) acc[c] += ge * to_f32(hp[c]);
+                        }
+                }
+            }
+            if (p < b1) {
+#pragma unroll
+                for (int c = 0; c < CE; ++c) part[ps * 64 + sg * CE + c] = acc[c];
+            }
+        }
+        __syncthreads();
+        {  // each row adds its pieces of the batch in order (four threads per row, 16 features each)
+            const int r = t >> 2, c0 = 16 * (t & 3);
+            const int p_lo = max(ppre[r], b0), p_hi = min(ppre[r + 1], b1);
+            for (int p = p_lo; p < p_hi; ++p)
+#pragma unroll
+                for (int c = 0; c < 16; ++c) run[r * 64 + c0 + c] += part[(p - b0) * 64 + c0 + c];
+        }
+        __syncthreads();
+    }
+    for (int q = t; q < kBlockVocab * kSeg; q += kThreads) {
+        const int r = q / kSeg, d = d0 + (q % kSeg) * CE;
+        const int pos = cb * kBlockVocab + r;
+        const int v = pos < V ? (perm ? perm[pos] : pos) : -1;
+        if (v < 0 || v >= V || d >= D) continue;
+        u32x4 out;
+        T *op = reinterpret_cast<T *>(&out);
+#pragma unroll
+        for (int c = 0; c < CE; ++c) op[c] = from_f32<T>(run[r * 64 + (d - d0) + c]);
+        *reinterpret_cast<u32x4 *>(dE.row(v) + d) = out;
+    }
+    __syncthreads();  // (the stage buffer and rlo are reused by the next item)
+}
+
 // The label path for dE item (cb, d0), if it applies: every kept block of
-// vocabulary block cb is label-only (status 2) and they pass label_path_ok.
+// vocabulary block cb is label-only (status 2) and the block is hot or
+// passes label_path_ok.
 // Returns -1 when the item's rows were written, else the number of kept row
 // blocks, listed in sh.list (for de_item), or -2 when the column's row
 // blocks do not fit one list.
@@ -1296,7 +1550,13 @@ __device__ __forceinline__ int de_try_label(GradLds<T> &sh, int cb, int d0, int 
         },
         sh.list, sh.wcnt);
     // (build_list ends with a barrier: sh.soft is final)
-    if (!lc.labels || n == 0 || sh.soft || !label_path_ok(lc.cent[cb])) return n;
+    if (!lc.labels || n == 0 || sh.soft) return n;
+    const int h = lc.hidx[cb];
+    if (h >= 0) {  // a hot column: its 64-feature tiles of this item
+        for (int d = d0; d < d0 + TileG::BN && d < D; d += 64) hot_item<T>(sh, h, cb, d / 64, lc, perm, D, V, dE);
+        return -1;
+    }
+    if (!label_path_ok(lc.cent[cb])) return n;
     label_group<T>(sh, n, cb, lc, V);
     label_rows<T>(sh, cb, d0, d0 + TileG::BN, lc, perm, D, V, dE);
     return -1;
@@ -1685,7 +1945,8 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
     const int64_t n_de = (int64_t)n_dyn * n_dt;
     // (no label path for the full classifier gradient: its label-only blocks
     // store the unfiltered gradient for dE)
-    const LabelCols<T> lc{a.full_de ? nullptr : a.labels, a.idx, a.inv_perm, a.glab, a.H, nv, a.cent};
+    const LabelCols<T> lc{a.full_de ? nullptr : a.labels, a.idx, a.inv_perm, a.glab, a.H, nv, a.cent,
+                          a.hidx, a.hent, a.hrlo, a.hent_t};
     // two loops rather than one with a branch: each keeps its own registers
     int64_t it = take_ticket(queue, ticket);
     while (it < n_de) {
@@ -1706,9 +1967,13 @@ __device__ __forceinline__ void grad_phase(const BwdArgs<T> &a, int p, int P, Gr
     while (it < n_de + n_dh + n_col) {
         const int ci = i_lo + (int)(it - n_de - n_dh);
         const int cb = a.citem[ci], ft = a.cft[ci];
-        const int d_lo = ft == kAllFeatures ? 0 : ft * TL::BN;
-        const int d_hi = ft == kAllFeatures ? a.D : min(a.D, d_lo + TL::BN);
-        de_column_item<T>(sh, cb, d_lo, d_hi, n_rbv, a.st, a.cbp, lc, a.perm, a.D, a.V, a.dE);
+        if (ft <= -2) {
+            hot_item<T>(sh, a.hidx[cb], cb, -2 - ft, lc, a.perm, a.D, a.V, a.dE);
+        } else {
+            const int d_lo = ft == kAllFeatures ? 0 : ft * TL::BN;
+            const int d_hi = ft == kAllFeatures ? a.D : min(a.D, d_lo + TL::BN);
+            de_column_item<T>(sh, cb, d_lo, d_hi, n_rbv, a.st, a.cbp, lc, a.perm, a.D, a.V, a.dE);
+        }
         it = take_ticket(queue, ticket);
     }
 }
@@ -1787,9 +2052,19 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     w.slist = c.take<int32_t>((size_t)s.cbp);
     w.ipre = c.take<int32_t>((size_t)s.cbp + 1);
     // (a split column has more than kColSplitEntries of the N label entries)
-    const size_t n_items = (size_t)s.cbp + (size_t)(s.N / (kColSplitEntries + 1) + 1) * (size_t)n_feature_tiles(s.D);
+    // (a hot column has more than kLabelEntries of the N label entries)
+    const size_t hmax = (size_t)std::min<int64_t>(s.cbp, s.N / (kLabelEntries + 1) + 1);
+    const size_t n_items = (size_t)s.cbp + (size_t)(s.N / (kColSplitEntries + 1) + 1) * (size_t)n_feature_tiles(s.D) +
+                           hmax * (size_t)n_hot_tiles(s.D);
     w.citem = c.take<int32_t>(n_items);
     w.cft = c.take<int32_t>(n_items);
+    w.tpos = c.take<int32_t>(s.N);
+    w.hidx = c.take<int32_t>((size_t)s.cbp);
+    w.hcol = c.take<int32_t>(hmax);
+    w.hent = c.take<int32_t>(hmax + 1);
+    w.nhot = c.take<int32_t>(1);
+    w.hrlo = c.take<int32_t>(hmax * 129);
+    w.hent_t = c.take<int32_t>(s.N);
     w.dlist = c.take<int32_t>((size_t)s.cbp);
     w.tneed = c.take<uint8_t>(ntile);
     w.cum = c.take<int64_t>((size_t)s.n_vtiles);
@@ -1867,7 +2142,7 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     }
     const int32_t *invp = perm ? w.inv_perm : nullptr;
     hipLaunchKernelGGL(k_label_map, dim3((unsigned)ceil_div(s.N, 256)), dim3(256), 0, st, labels, w.idx, w.nvalid,
-                       invp, s.V, s.cbp, w.lab);
+                       invp, s.V, s.cbp, w.lab, w.tpos);
     CCE_LAUNCHED();
     const int64_t ntile = (int64_t)s.n_rtiles * s.n_vtiles;
     hipLaunchKernelGGL(k_tile_class, dim3((unsigned)ceil_div(ntile, 256)), dim3(256), 0, st, w.nvalid, s.V,
@@ -1880,8 +2155,15 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     const int static_ok = (!full_de && s.n_rb <= kListCap) ? 1 : 0;
     hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, st, w.vneed, w.vact, s.n_vtiles, s.cap, s.cap_eff,
                        s.max_passes, w.plan, w.cum, w.act, CB, static_ok, w.csoft, w.cnlab, w.cent, w.cpre, w.slist,
-                       w.dlist, n_feature_tiles(D), w.ipre, w.citem, w.cft, stats);
+                       w.dlist, n_feature_tiles(D), n_hot_tiles(D), w.ipre, w.citem, w.cft, w.hidx, w.hcol, w.hent,
+                       w.nhot, stats);
     CCE_LAUNCHED();
+    if (static_ok) {  // the hot columns' entries, grouped by row (at most hmax columns)
+        const int64_t hmax = std::min<int64_t>(s.cbp, s.N / (kLabelEntries + 1) + 1);
+        hipLaunchKernelGGL(k_hot_entries, dim3((unsigned)hmax), dim3(1024), 0, st, w.nhot, w.hcol, w.hent, w.nvalid,
+                           w.tpos, w.hrlo, w.hent_t);
+        CCE_LAUNCHED();
+    }
     hipLaunchKernelGGL(k_tile_list, dim3((unsigned)ceil_div(s.n_vtiles, 4)), dim3(256), 0, st, w.tneed, s.n_rtiles,
                        s.n_vtiles, w.act, w.lab, s.cbp, w.cpre, CB, w.tlist);
     CCE_LAUNCHED();
@@ -1931,6 +2213,10 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     a.ipre = w.ipre;
     a.citem = w.citem;
     a.cft = w.cft;
+    a.hidx = w.hidx;
+    a.hent = w.hent;
+    a.hrlo = w.hrlo;
+    a.hent_t = w.hent_t;
     a.dlist = w.dlist;
     a.cent = w.cent;
     a.CB = CB;

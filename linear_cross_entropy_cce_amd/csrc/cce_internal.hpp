@@ -129,7 +129,14 @@ struct BwdWs {
     int32_t *slist;    // [cbp] static columns, in order
     int32_t *ipre;     // [cbp + 1] work items before each static column (slist order)
     int32_t *citem;    // work items of the static columns: column
-    int32_t *cft;      //   and 256-feature tile (-1: every feature)
+    int32_t *cft;      //   and 256-feature tile (-1: every feature; -2 - f: 64-feature tile f of a hot column)
+    int32_t *tpos;     // [N] label position of each valid token (-1: none)
+    int32_t *hidx;     // [cbp] index of a hot column (-1: not hot)
+    int32_t *hcol;     // [hmax] the hot columns
+    int32_t *hent;     // [hmax + 1] first entry of each hot column
+    int32_t *nhot;     // [1] hot columns
+    int32_t *hrlo;     // [hmax, 129] entries before each row of a hot column
+    int32_t *hent_t;   // [N] the hot columns' entries (valid-token positions), grouped by row
     int32_t *dlist;    // [cbp] the other columns, in order
     uint8_t *tneed;    // [n_vtiles, n_rtiles] blocks the tile may keep (bits 0-2), recompute flag (bit 7)
     int64_t *cum;      // [n_vtiles] plan scratch: cumulative blocks
