@@ -68,9 +68,10 @@ constexpr int kColSplitEntries = 32;
 // Feature tile of a static column item that covers every feature.
 constexpr int kAllFeatures = -1;
 // 256-feature tiles of a row of D features (the products' tile width), and
-// the 64-feature tiles of a hot column's items.
+// the kHotF-feature tiles of a hot column's items.
+constexpr int kHotF = 32;
 __host__ __device__ __forceinline__ int n_feature_tiles(int64_t D) { return (int)((D + 255) / 256); }
-__host__ __device__ __forceinline__ int n_hot_tiles(int64_t D) { return (int)((D + 63) / 64); }
+__host__ __device__ __forceinline__ int n_hot_tiles(int64_t D) { return (int)((D + kHotF - 1) / kHotF); }
 static_assert(TileG::BN == 256, "feature tiles of the products");
 constexpr int kDeGroups = 2 * kPassGroups;  // persistent dE workgroups of the gradient-product kernel
 
@@ -383,6 +384,13 @@ __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ 
     }
 }
 
+// Both columns of vocabulary tile vt are static (a column past the
+// vocabulary counts as static: it holds no block).
+__device__ __forceinline__ bool vt_static(const int32_t *__restrict__ cpre, int vt, int CB) {
+    const int c0 = 2 * vt, c1 = 2 * vt + 1;
+    return c0 < CB && cpre[c0 + 1] - cpre[c0] == 1 && (c1 >= CB || cpre[c1 + 1] - cpre[c1] == 1);
+}
+
 // One workgroup: prefix sums of the blocks each vocabulary tile may keep and
 // of its listed tiles (vneed, vact from k_tile_class), the pass of each
 // vocabulary tile and the per-pass ranges; k_tile_list then writes the tile
@@ -400,9 +408,9 @@ __global__ __launch_bounds__(256) void k_tile_class(const int32_t *__restrict__ 
 // slist holds the static columns in order, dlist the others, and cpre[cb]
 // the static columns before cb (cpre[CB] all of them).  A static column is
 // one work item, or n_dt (one per 256-feature tile) when it has more than
-// kColSplitEntries label entries, or one per 64-feature tile when it is hot:
+// kColSplitEntries label entries, or one per kHotF-feature tile when it is hot:
 // citem and cft list the items in column order (column, and the 256-feature
-// tile, kAllFeatures for a whole column, or -2 - the 64-feature tile of a
+// tile, kAllFeatures for a whole column, or -2 - the kHotF-feature tile of a
 // hot column) and ipre[j] the items before static column j (ipre[cpre[CB]]
 // all of them).  The
 // label-only blocks of static columns (their label blocks) are counted into
@@ -426,64 +434,6 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ vneed
     __shared__ int32_t carry_a, carry_c, carry_i, carry_h, carry_e;
     const PlanView pv = plan_view(plan, max_passes);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    if (t == 0) { carry_n = 0; carry_a = 0; }
-    __syncthreads();
-    for (int base = 0; base < n_vt; base += 1024) {
-        const int vt = base + t;
-        int64_t nd = 0;
-        int ac = 0;
-        if (vt < n_vt) {
-            nd = vneed[vt];
-            ac = vact[vt];
-        }
-        int64_t xs = nd;
-        int xa = ac;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int64_t ys = __shfl_up(xs, o, 64);
-            const int ya = __shfl_up(xa, o, 64);
-            if (lane >= o) { xs += ys; xa += ya; }
-        }
-        if (lane == 63) { wsum[w] = xs; wact[w] = xa; }
-        __syncthreads();
-        int64_t off = carry_n;
-        int offa = carry_a;
-        for (int k = 0; k < w; ++k) { off += wsum[k]; offa += wact[k]; }
-        if (vt < n_vt) {
-            cum[vt] = off + xs;          // inclusive
-            act[vt] = offa + xa - ac;    // exclusive
-        }
-        __syncthreads();
-        if (t == 1023) { carry_n = off + xs; carry_a = offa + xa; }
-        __syncthreads();
-    }
-    const int64_t total = carry_n;
-    const int n_active = carry_a;
-    auto pass_of = [&](int vt) -> int {
-        if (total <= cap) return 0;
-        const int64_t q = cum[vt] / cap_eff;
-        return q < max_passes - 1 ? (int)q : max_passes - 1;
-    };
-    for (int vt = t; vt < n_vt; vt += 1024) {
-        const int p = pass_of(vt);
-        const int pp = vt ? pass_of(vt - 1) : -1;
-        for (int q = pp + 1; q <= p; ++q) {
-            pv.vt_begin[q] = vt;
-            pv.list_begin[q] = act[vt];
-        }
-    }
-    if (t == 0) {
-        const int P = pass_of(n_vt - 1) + 1;
-        *pv.P = P;
-        *pv.n_active = n_active;
-        for (int q = P; q <= max_passes; ++q) {
-            pv.vt_begin[q] = n_vt;
-            pv.list_begin[q] = n_active;
-        }
-    }
-    for (int q = t; q < max_passes; q += 1024) pv.counter[q] = 0;
-    for (int q = t; q < kQueues * max_passes; q += 1024) plan_queues(plan, max_passes, 0)[q] = 0;
-
     if (t == 0) { carry_c = 0; carry_i = 0; carry_h = 0; carry_e = 0; }
     __syncthreads();
     int64_t n_static_lab = 0;
@@ -544,19 +494,82 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ vneed
         if (lane == 0 && n_static_lab)
             atomicAdd(reinterpret_cast<unsigned long long *>(stats + 1), (unsigned long long)n_static_lab);
     }
+    __syncthreads();  // cpre is read below
+    if (t == 0) { carry_n = 0; carry_a = 0; }
+    __syncthreads();
+    for (int base = 0; base < n_vt; base += 1024) {
+        const int vt = base + t;
+        int64_t nd = 0;
+        int ac = 0;
+        if (vt < n_vt) {
+            nd = vneed[vt];
+            // (a vocabulary tile whose columns are both static lists no tile:
+            // k_label_static writes what its tiles would)
+            ac = vt_static(cpre, vt, CB) ? 0 : vact[vt];
+        }
+        int64_t xs = nd;
+        int xa = ac;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t ys = __shfl_up(xs, o, 64);
+            const int ya = __shfl_up(xa, o, 64);
+            if (lane >= o) { xs += ys; xa += ya; }
+        }
+        if (lane == 63) { wsum[w] = xs; wact[w] = xa; }
+        __syncthreads();
+        int64_t off = carry_n;
+        int offa = carry_a;
+        for (int k = 0; k < w; ++k) { off += wsum[k]; offa += wact[k]; }
+        if (vt < n_vt) {
+            cum[vt] = off + xs;          // inclusive
+            act[vt] = offa + xa - ac;    // exclusive
+        }
+        __syncthreads();
+        if (t == 1023) { carry_n = off + xs; carry_a = offa + xa; }
+        __syncthreads();
+    }
+    const int64_t total = carry_n;
+    const int n_active = carry_a;
+    auto pass_of = [&](int vt) -> int {
+        if (total <= cap) return 0;
+        const int64_t q = cum[vt] / cap_eff;
+        return q < max_passes - 1 ? (int)q : max_passes - 1;
+    };
+    for (int vt = t; vt < n_vt; vt += 1024) {
+        const int p = pass_of(vt);
+        const int pp = vt ? pass_of(vt - 1) : -1;
+        for (int q = pp + 1; q <= p; ++q) {
+            pv.vt_begin[q] = vt;
+            pv.list_begin[q] = act[vt];
+        }
+    }
+    if (t == 0) {
+        const int P = pass_of(n_vt - 1) + 1;
+        *pv.P = P;
+        *pv.n_active = n_active;
+        for (int q = P; q <= max_passes; ++q) {
+            pv.vt_begin[q] = n_vt;
+            pv.list_begin[q] = n_active;
+        }
+    }
+    for (int q = t; q < max_passes; q += 1024) pv.counter[q] = 0;
+    for (int q = t; q < kQueues * max_passes; q += 1024) plan_queues(plan, max_passes, 0)[q] = 0;
+
 }
 
 // The tile list: the listed tiles (that may keep a block) of vocabulary tile
 // vt at act[vt] onwards, token tiles in order.  One wave per vocabulary tile.
-// A tile that recomputes nothing and whose label blocks all lie in static
-// columns gets -1 instead (k_label_static writes what it would have).
+// A vocabulary tile whose columns are both static lists nothing (k_plan
+// counted none); in the others a tile that recomputes nothing and whose
+// label blocks all lie in static columns gets -1 (k_label_static writes what
+// it would have).
 __global__ __launch_bounds__(256) void k_tile_list(const uint8_t *__restrict__ tneed, int n_rt, int n_vt,
                                                    const int32_t *__restrict__ act, const uint8_t *__restrict__ lab,
                                                    int cbp, const int32_t *__restrict__ cpre, int CB,
                                                    int32_t *__restrict__ tlist) {
     const int lane = threadIdx.x & 63;
     const int vt = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (vt >= n_vt) return;  // wave-uniform
+    if (vt >= n_vt || vt_static(cpre, vt, CB)) return;  // wave-uniform
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
     const uint8_t *row = tneed + (int64_t)vt * n_rt;
     bool col_static[2];
@@ -1028,6 +1041,7 @@ __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int
         const int part = (bid + k) % nparts;
         const int pb = lb + (int)((int64_t)(le - lb) * part / nparts);
         const int pe = lb + (int)((int64_t)(le - lb) * (part + 1) / nparts);
+        if (pe == pb) continue;  // (uniform) an empty part takes no ticket
         for (;;) {
             const int i = pb + take_ticket(queues + part, ticket);
             if (i >= pe) break;
@@ -1405,35 +1419,38 @@ __device__ __forceinline__ void label_rows(const GradLds<T> &sh, int cb, int d_l
     }
 }
 
-// dE rows of hot column cb (index h), features [64 f, 64 f + 64) (capped at
-// D), from its label entries (k_hot_entries: grouped by row, token order
-// within a row).  A row's entries are cut into pieces of at most kHotPiece;
-// a batch of kPB pieces is summed with one thread per (piece, 16-byte
-// segment), each piece in token order in fp32, and each row's running sum
-// then adds the batch's pieces of that row in order.  So a frequent label's
-// entries are summed by many threads at once, in a fixed order.
+// dE rows of hot column cb (index h), features [kHotF f, kHotF (f + 1))
+// (capped at D), from its label entries (k_hot_entries: grouped by row,
+// token order within a row).  A row's entries are cut into pieces of at most
+// kHotPiece; a batch of kPB pieces is summed with one thread per (piece,
+// 16-byte segment), each piece in token order in fp32, and each row's
+// running sum then adds the batch's pieces of that row in order.  So a
+// frequent label's entries are summed by many threads at once, in a fixed
+// order.
 constexpr int kHotPiece = 32;
 template <typename T>
 __device__ __forceinline__ void hot_item(GradLds<T> &sh, int h, int cb, int f, const LabelCols<T> &lc,
                                          const int32_t *__restrict__ perm, int D, int V, Rows2<T> dE) {
     constexpr int kThreads = TileG::kThreads;
     constexpr int CE = ChunkElems<T>::value;
-    constexpr int kSeg = 64 / CE;           // 16-byte segments of a 64-feature tile
+    constexpr int kSeg = kHotF / CE;        // 16-byte segments of the item's features
     constexpr int kPB = kThreads / kSeg;    // pieces per batch
     constexpr int kBE = kPB * kHotPiece;    // entries of a batch at most
-    static_assert(sizeof(sh.stages) >= sizeof(float) * (kBlockVocab * 64 + kPB * 64 + 2 * kBE + kBlockVocab + 1),
+    constexpr int kCF = kHotF / 4;          // features per thread when rows add their pieces (4 threads a row)
+    static_assert(kBE % kThreads == 0 && kBE / kThreads <= 8, "one round of staging loads per batch");
+    static_assert(sizeof(sh.stages) >= sizeof(float) * (kBlockVocab * kHotF + kPB * kHotF + 2 * kBE + kBlockVocab + 1),
                   "the hot item's buffers fit the stage buffer");
-    float *run = reinterpret_cast<float *>(sh.stages);  // [128][64] running row sums
-    float *part = run + kBlockVocab * 64;                // [kPB][64] the batch's piece sums
-    int *eh = reinterpret_cast<int *>(part + kPB * 64);  // [kBE] row of H of each entry of the batch
-    float *eg = reinterpret_cast<float *>(eh + kBE);     // [kBE] its gradient
-    int *ppre = reinterpret_cast<int *>(eg + kBE);       // [129] pieces before each row
-    int *rlo = sh.rlo;                                   // [129] entries before each row
+    float *run = reinterpret_cast<float *>(sh.stages);   // [128][kHotF] running row sums
+    float *part = run + kBlockVocab * kHotF;              // [kPB][kHotF] the batch's piece sums
+    int *eh = reinterpret_cast<int *>(part + kPB * kHotF);  // [kBE] row of H of each entry of the batch
+    float *eg = reinterpret_cast<float *>(eh + kBE);      // [kBE] its gradient
+    int *ppre = reinterpret_cast<int *>(eg + kBE);        // [129] pieces before each row
+    int *rlo = sh.rlo;                                    // [129] entries before each row
     const int t = threadIdx.x, lane = t & 63;
-    const int d0 = 64 * f;
+    const int d0 = kHotF * f;
     const int32_t *ent = lc.hent_t + lc.hent[h];
     if (t <= kBlockVocab) rlo[t] = lc.hrlo[129 * h + t];
-    for (int q = t; q < kBlockVocab * 64; q += kThreads) run[q] = 0.f;
+    for (int q = t; q < kBlockVocab * kHotF; q += kThreads) run[q] = 0.f;
     __syncthreads();
     if (t < kBlockVocab) {  // pieces per row: exclusive scan over two waves
         const int c = (rlo[t + 1] - rlo[t] + kHotPiece - 1) / kHotPiece;
@@ -1466,11 +1483,28 @@ __device__ __forceinline__ void hot_item(GradLds<T> &sh, int h, int cb, int f, c
         const int b1 = min(np, b0 + kPB);
         const int rb0 = row_of(b0), rb1 = row_of(b1 - 1);
         const int e_lo = piece_begin(b0, rb0);
-        const int e_hi = min(piece_begin(b1 - 1, rb1) + kHotPiece, rlo[rb1 + 1]);
-        for (int k = t; k < e_hi - e_lo; k += kThreads) {
-            const int tok = ent[e_lo + k];
-            eh[k] = lc.idx[tok];
-            eg[k] = lc.glab[tok];
+        const int n_be = min(piece_begin(b1 - 1, rb1) + kHotPiece, rlo[rb1 + 1]) - e_lo;
+        {  // stage the batch's entries: every load of a thread in flight at once
+            constexpr int kU = kBE / kThreads;
+            int tok[kU], hr[kU];
+            float gg[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int k = u * kThreads + t;
+                tok[u] = k < n_be ? ent[e_lo + k] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (tok[u] >= 0) {
+                    hr[u] = lc.idx[tok[u]];
+                    gg[u] = lc.glab[tok[u]];
+                }
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (tok[u] >= 0) {
+                    eh[u * kThreads + t] = hr[u];
+                    eg[u * kThreads + t] = gg[u];
+                }
         }
         __syncthreads();
         {
@@ -1483,14 +1517,14 @@ __device__ __forceinline__ void hot_item(GradLds<T> &sh, int h, int cb, int f, c
                 const int r = row_of(p);
                 const int e_begin = piece_begin(p, r) - e_lo;
                 const int e_end = min(piece_begin(p, r) + kHotPiece, rlo[r + 1]) - e_lo;
-                for (int e = e_begin; e < e_end; e += 8) {  // eight loads in flight, added in entry order
-                    u32x4 hv[8];
+                for (int e = e_begin; e < e_end; e += 16) {  // sixteen loads in flight, added in entry order
+                    u32x4 hv[16];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u)
+                    for (int u = 0; u < 16; ++u)
                         if (e + u < e_end)
                             hv[u] = ld16(reinterpret_cast<const char *>(lc.H + (int64_t)eh[e + u] * D + d));
 #pragma unroll
-                    for (int u = 0; u < 8; ++u)
+                    for (int u = 0; u < 16; ++u)
                         if (e + u < e_end) {
                             const T *hp = reinterpret_cast<const T *>(&hv[u]);
                             const float ge = eg[e + u];
@@ -1501,16 +1535,16 @@ __device__ __forceinline__ void hot_item(GradLds<T> &sh, int h, int cb, int f, c
             }
             if (p < b1) {
 #pragma unroll
-                for (int c = 0; c < CE; ++c) part[ps * 64 + sg * CE + c] = acc[c];
+                for (int c = 0; c < CE; ++c) part[ps * kHotF + sg * CE + c] = acc[c];
             }
         }
         __syncthreads();
-        {  // each row adds its pieces of the batch in order (four threads per row, 16 features each)
-            const int r = t >> 2, c0 = 16 * (t & 3);
+        {  // each row adds its pieces of the batch in order (four threads per row)
+            const int r = t >> 2, c0 = kCF * (t & 3);
             const int p_lo = max(ppre[r], b0), p_hi = min(ppre[r + 1], b1);
             for (int p = p_lo; p < p_hi; ++p)
 #pragma unroll
-                for (int c = 0; c < 16; ++c) run[r * 64 + c0 + c] += part[(p - b0) * 64 + c0 + c];
+                for (int c = 0; c < kCF; ++c) run[r * kHotF + c0 + c] += part[(p - b0) * kHotF + c0 + c];
         }
         __syncthreads();
     }
@@ -1522,7 +1556,7 @@ __device__ __forceinline__ void hot_item(GradLds<T> &sh, int h, int cb, int f, c
         u32x4 out;
         T *op = reinterpret_cast<T *>(&out);
 #pragma unroll
-        for (int c = 0; c < CE; ++c) op[c] = from_f32<T>(run[r * 64 + (d - d0) + c]);
+        for (int c = 0; c < CE; ++c) op[c] = from_f32<T>(run[r * kHotF + (d - d0) + c]);
         *reinterpret_cast<u32x4 *>(dE.row(v) + d) = out;
     }
     __syncthreads();  // (the stage buffer and rlo are reused by the next item)
@@ -1552,8 +1586,8 @@ __device__ __forceinline__ int de_try_label(GradLds<T> &sh, int cb, int d0, int 
     // (build_list ends with a barrier: sh.soft is final)
     if (!lc.labels || n == 0 || sh.soft) return n;
     const int h = lc.hidx[cb];
-    if (h >= 0) {  // a hot column: its 64-feature tiles of this item
-        for (int d = d0; d < d0 + TileG::BN && d < D; d += 64) hot_item<T>(sh, h, cb, d / 64, lc, perm, D, V, dE);
+    if (h >= 0) {  // a hot column: its kHotF-feature tiles of this item
+        for (int d = d0; d < d0 + TileG::BN && d < D; d += kHotF) hot_item<T>(sh, h, cb, d / kHotF, lc, perm, D, V, dE);
         return -1;
     }
     if (!label_path_ok(lc.cent[cb])) return n;

@@ -129,7 +129,7 @@ struct BwdWs {
     int32_t *slist;    // [cbp] static columns, in order
     int32_t *ipre;     // [cbp + 1] work items before each static column (slist order)
     int32_t *citem;    // work items of the static columns: column
-    int32_t *cft;      //   and 256-feature tile (-1: every feature; -2 - f: 64-feature tile f of a hot column)
+    int32_t *cft;      //   and 256-feature tile (-1: every feature; -2 - f: 32-feature tile f of a hot column)
     int32_t *tpos;     // [N] label position of each valid token (-1: none)
     int32_t *hidx;     // [cbp] index of a hot column (-1: not hot)
     int32_t *hcol;     // [hmax] the hot columns

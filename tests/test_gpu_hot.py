@@ -3,7 +3,7 @@
 frequent ids).  When every kept block of such a column is label-only, its dE
 rows are sums of g_i h_i over its label entries; the backward groups the
 entries by row once per call and sums each row's entries in pieces of 32
-(token order within a piece, pieces in order) over 64-feature tiles.
+(token order within a piece, pieces in order) over 32-feature tiles.
 
 The static route (with the forward's block-max table the column is known to
 keep only label-only blocks before any recompute) and the dynamic route
@@ -38,8 +38,8 @@ def _hot_columns(x, perm=None):
     return np.nonzero(counts > HOT)[0], counts
 
 
-# (N, D, V, dtype): D = 264 leaves a partial last 64-feature tile (and a
-# ragged 256-feature tile); the fp32 case takes 16 segments of 4 features.
+# (N, D, V, dtype): D = 264 leaves a partial last 32-feature tile (and a
+# ragged 256-feature tile); the fp32 case takes 8 segments of 4 features.
 CASES = [(4096, 264, 9000, "bf16"), (2048, 264, 5000, "f32")]
 
 
