@@ -57,6 +57,9 @@ constexpr int kBlockElems = kBlockRows * kBlockVocab;  // elements of one stored
 constexpr int kListCap = 512;
 // At most this many label entries go through the label path at once.
 constexpr int kLabelEntries = 512;
+// dE's compensated (Kahan) sum takes one term per this many kept row blocks
+// of a vocabulary block: each term is an fp32 MFMA sum over up to 512 tokens.
+constexpr int kKahanBlocks = 4;
 // A vocabulary block whose kept blocks are all label-only takes the label
 // path (its dE rows from the label entries, one pass over a row of H per
 // entry, instead of block products over every token of its kept blocks)
@@ -1618,8 +1621,9 @@ __device__ __forceinline__ void de_column_item(GradLds<T> &sh, int cb, int d_lo,
 // dE for one (vocabulary block cb, 256-feature tile d0) item of a pass.  K
 // runs over the valid tokens of the row blocks kept for cb, in order (DMA
 // pipeline, 64 K-bytes per stage): A = the stored block Gt[slot] (128
-// vocabulary rows x 128 tokens), B = H^T.  Each row block's product is formed
-// in a fresh fp32 accumulator and then added into (sum, compensation) with
+// vocabulary rows x 128 tokens), B = H^T.  The product of each group of
+// kKahanBlocks kept row blocks (the last group may hold fewer) is formed in a
+// fresh fp32 accumulator and then added into (sum, compensation) with
 // Kahan's rule; the result is written once, through LDS as 16-byte row
 // segments (bf16).  A vocabulary block with nothing kept gets dE = 0.
 // pre_n >= 0: the kept row blocks (all of them: n_rb <= kListCap) are
@@ -1699,7 +1703,7 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
             const int ahead = total - 1 - s;
             eng.wait_stage(eng.clamp_ahead(ahead));
             if (s + DE::kDepth < total) issue((s + DE::kDepth) % DE::kStages, s + DE::kDepth);
-            bool flush = (s % kSpb) == kSpb - 1;
+            bool flush = (s % (kSpb * kKahanBlocks)) == kSpb * kKahanBlocks - 1 || s == total - 1;
             if constexpr (FINE) {
                 const int e = sh.stl[s];
                 const uint32_t m = (uint32_t)sh.lmask[(e >> 4) & 0x7FF];
@@ -1707,7 +1711,11 @@ __device__ __forceinline__ void de_item(GradLds<T> &sh, int cb, int d0, int n_rb
                 static_assert(TL::TM == 2 && TL::kWaveM == 64, "a wave holds two 32-row sub-rows of the block");
                 const uint32_t rows = ((m >> (4 * i0 + j)) & 1) | (((m >> (4 * (i0 + 1) + j)) & 1) << 1);
                 compute_rows<T, TL>(eng, s % DE::kStages, acc, tid, rows);
-                flush = e < 0;
+                // (the same terms as without the sub-tile filter: the end of
+                // every kKahanBlocks-th listed block, and the last stage)
+                // (e is the same in every lane: the flush is uniform)
+                flush = __builtin_amdgcn_readfirstlane(
+                            e < 0 && ((((e >> 4) & 0x7FF) % kKahanBlocks) == kKahanBlocks - 1 || s == total - 1)) != 0;
             } else {
                 eng.compute(s % DE::kStages, acc, tid);
             }
