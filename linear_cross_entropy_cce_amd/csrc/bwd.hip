@@ -145,9 +145,7 @@ struct BwdArgs {
 };
 
 // ------------------------------------------------------------ small kernels
-__global__ void k_stats_init(int64_t *stats) {
-    if (threadIdx.x < 7) stats[threadIdx.x] = 0;
-}
+constexpr int kStatsLen = 7;  // entries of the stats array
 
 __global__ void k_stats_fin(int64_t *stats, const int32_t *__restrict__ nvalid_p, int64_t n_vblocks) {
     if (threadIdx.x == 0) {
@@ -157,27 +155,20 @@ __global__ void k_stats_fin(int64_t *stats, const int32_t *__restrict__ nvalid_p
     }
 }
 
-__global__ __launch_bounds__(256) void k_fill_u32(uint32_t *__restrict__ p, int64_t n, uint32_t v) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = v;
-}
-
-__global__ __launch_bounds__(256) void k_fill_zero(float *__restrict__ p, int64_t n) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i < n) *reinterpret_cast<f32x4 *>(p + i) = f32x4{0.f, 0.f, 0.f, 0.f};
-}
-
-// lmin[rb] = smallest lse over the valid tokens of 128-token block rb (+inf if none).
-__global__ __launch_bounds__(128) void k_lse_min(const float *__restrict__ lse, const int32_t *__restrict__ idx,
-                                                 const int32_t *__restrict__ nvalid_p, float *__restrict__ lmin) {
-    __shared__ float part[2];
-    const int tok = blockIdx.x * kBlockRows + threadIdx.x;
+// lmin[rb] = smallest lse over the valid tokens of 128-token block rb (+inf
+// if none), for rb = 2 b and 2 b + 1 (one per half of a 256-thread group).
+__device__ __forceinline__ void lse_min_pair(const float *__restrict__ lse, const int32_t *__restrict__ idx,
+                                             const int32_t *__restrict__ nvalid_p, float *__restrict__ lmin,
+                                             int n_rb, int64_t b, float *part) {
+    const int half = threadIdx.x >> 7;
+    const int64_t rb = 2 * b + half;
+    const int64_t tok = rb * kBlockRows + (threadIdx.x & 127);
     float v = tok < *nvalid_p ? lse[idx[tok]] : __builtin_huge_valf();
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
     __syncthreads();
-    if (threadIdx.x == 0) lmin[blockIdx.x] = fminf(part[0], part[1]);
+    if ((threadIdx.x & 127) == 0 && rb < n_rb) lmin[rb] = fminf(part[2 * half], part[2 * half + 1]);
 }
 
 // True when every p in block (rb, cb) is provably below eps / 2: the block's
@@ -196,15 +187,15 @@ __device__ __forceinline__ bool block_below(const float *__restrict__ bmax, int6
 // dst[c][j] = src[row(j)][c] for c < cols, j < n_out; rows j >= n_rows give 0.
 // row(j) = rowmap ? rowmap[row0 + j] : row0 + j.  64 x 64 tiles through LDS.
 template <typename T>
-__global__ __launch_bounds__(256) void k_transpose(const T *__restrict__ src, int64_t ld_src, int64_t n_src_rows,
-                                                   const int32_t *__restrict__ rowmap, int64_t row0,
-                                                   const int32_t *__restrict__ n_rows_dev, int n_rows_host,
-                                                   int cols, int n_out, T *__restrict__ dst, int64_t ld_dst) {
+__device__ __forceinline__ void transpose_tile(const T *__restrict__ src, int64_t ld_src, int64_t n_src_rows,
+                                               const int32_t *__restrict__ rowmap, int64_t row0,
+                                               const int32_t *__restrict__ n_rows_dev, int n_rows_host, int cols,
+                                               int n_out, T *__restrict__ dst, int64_t ld_dst, int bx, int by,
+                                               T (*tile)[64 + 2]) {
     constexpr int CE = ChunkElems<T>::value;
-    __shared__ T tile[64][64 + 2];
     const int n_rows = n_rows_dev ? *n_rows_dev : n_rows_host;
-    const int j0 = blockIdx.x * 64;
-    const int c0 = blockIdx.y * 64;
+    const int j0 = bx * 64;
+    const int c0 = by * 64;
     for (int q = threadIdx.x; q < 64 * (64 / CE); q += 256) {
         const int jj = q / (64 / CE);
         const int cc = (q % (64 / CE)) * CE;
@@ -234,16 +225,28 @@ __global__ __launch_bounds__(256) void k_transpose(const T *__restrict__ src, in
     }
 }
 
-// Rows whose label is ignore_index get dH = 0 (one wave per row).
+// The backward's clearing, one grid-stride launch: three regions of 32-bit
+// words (the label map; the plan's column and tile sums; the label
+// gradients), the stats entries if given, and dH = 0 for the rows whose
+// label is ignore_index (one wave per row).
 template <typename T>
-__global__ __launch_bounds__(256) void k_zero_ignored(const int64_t *__restrict__ labels, int64_t N, int D,
-                                                      int64_t ignore_index, T *__restrict__ dH) {
+__global__ __launch_bounds__(256) void k_bwd_clear(uint32_t *__restrict__ r0, int64_t n0, uint32_t *__restrict__ r1,
+                                                   int64_t n1, uint32_t *__restrict__ r2, int64_t n2,
+                                                   int64_t *__restrict__ stats, const int64_t *__restrict__ labels,
+                                                   int64_t N, int D, int64_t ignore_index, T *__restrict__ dH) {
     constexpr int CE = ChunkElems<T>::value;
-    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (i >= N || labels[i] != ignore_index) return;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (int64_t i = i0; i < n0; i += stride) r0[i] = 0u;
+    for (int64_t i = i0; i < n1; i += stride) r1[i] = 0u;
+    for (int64_t i = i0; i < n2; i += stride) r2[i] = 0u;
+    if (stats && i0 < kStatsLen) stats[i0] = 0;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int k = (threadIdx.x & 63) * CE; k < D; k += 64 * CE)
-        *reinterpret_cast<u32x4 *>(dH + i * D + k) = z;
+    const int lane = threadIdx.x & 63;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < N; row += (int64_t)gridDim.x * 4) {
+        if (labels[row] != ignore_index) continue;  // (wave-uniform)
+        for (int k = lane * CE; k < D; k += 64 * CE) *reinterpret_cast<u32x4 *>(dH + row * D + k) = z;
+    }
 }
 
 // Compacts the indices i in [0, n) with flag(i) != 0 into list[], in order,
@@ -321,11 +324,11 @@ __device__ __forceinline__ int build_stages(int n, int kspb, const int *mask, Se
 // through its aligned 32-bit word (the map's region is 256-byte aligned and
 // padded).  tpos[t] = the label's position in processing order (-1: not a
 // valid label).
-__global__ __launch_bounds__(256) void k_label_map(const int64_t *__restrict__ labels, const int32_t *__restrict__ idx,
-                                                   const int32_t *__restrict__ nvalid_p,
-                                                   const int32_t *__restrict__ inv_perm, int64_t V, int cbp,
-                                                   uint8_t *__restrict__ lab, int32_t *__restrict__ tpos) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void label_map_block(const int64_t *__restrict__ labels, const int32_t *__restrict__ idx,
+                                                const int32_t *__restrict__ nvalid_p,
+                                                const int32_t *__restrict__ inv_perm, int64_t V, int cbp,
+                                                uint8_t *__restrict__ lab, int32_t *__restrict__ tpos, int64_t b) {
+    const int64_t t = b * 256 + threadIdx.x;
     if (t >= *nvalid_p) return;
     const int64_t y = labels[idx[t]];
     if (y < 0 || y >= V) {  // not a valid label: undefined by contract
@@ -396,7 +399,7 @@ __device__ __forceinline__ bool vt_static(const int32_t *__restrict__ cpre, int 
 
 // One workgroup: prefix sums of the blocks each vocabulary tile may keep and
 // of its listed tiles (vneed, vact from k_tile_class), the pass of each
-// vocabulary tile and the per-pass ranges; k_tile_list then writes the tile
+// vocabulary tile and the per-pass ranges; tile_list_block then writes the tile
 // list (vocabulary-tile-major, token tiles in order).
 // Passes: one if every block fits the store, else pass(vt) =
 // floor(cum(vt) / cap_eff) with cum the inclusive block count; a vocabulary
@@ -507,7 +510,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ vneed
         if (vt < n_vt) {
             nd = vneed[vt];
             // (a vocabulary tile whose columns are both static lists no tile:
-            // k_label_static writes what its tiles would)
+            // label_static_block writes what its tiles would)
             ac = vt_static(cpre, vt, CB) ? 0 : vact[vt];
         }
         int64_t xs = nd;
@@ -564,14 +567,14 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t *__restrict__ vneed
 // vt at act[vt] onwards, token tiles in order.  One wave per vocabulary tile.
 // A vocabulary tile whose columns are both static lists nothing (k_plan
 // counted none); in the others a tile that recomputes nothing and whose
-// label blocks all lie in static columns gets -1 (k_label_static writes what
+// label blocks all lie in static columns gets -1 (label_static_block writes what
 // it would have).
-__global__ __launch_bounds__(256) void k_tile_list(const uint8_t *__restrict__ tneed, int n_rt, int n_vt,
-                                                   const int32_t *__restrict__ act, const uint8_t *__restrict__ lab,
-                                                   int cbp, const int32_t *__restrict__ cpre, int CB,
-                                                   int32_t *__restrict__ tlist) {
+__device__ __forceinline__ void tile_list_block(const uint8_t *__restrict__ tneed, int n_rt, int n_vt,
+                                                const int32_t *__restrict__ act, const uint8_t *__restrict__ lab,
+                                                int cbp, const int32_t *__restrict__ cpre, int CB,
+                                                int32_t *__restrict__ tlist, int64_t b) {
     const int lane = threadIdx.x & 63;
-    const int vt = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int vt = (int)(b * 4 + (threadIdx.x >> 6));
     if (vt >= n_vt || vt_static(cpre, vt, CB)) return;  // wave-uniform
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
     const uint8_t *row = tneed + (int64_t)vt * n_rt;
@@ -606,14 +609,14 @@ __global__ __launch_bounds__(256) void k_tile_list(const uint8_t *__restrict__ t
 // label falls in a static column, the block's status (2, label only) and the
 // label entry's fp32 gradient dloss (p - 1), p from the forward's label logit
 // (the values the tile epilogue writes for a block it does not recompute).
-__global__ __launch_bounds__(256) void k_label_static(const int64_t *__restrict__ labels,
-                                                      const int32_t *__restrict__ idx,
-                                                      const int32_t *__restrict__ nvalid_p,
-                                                      const int32_t *__restrict__ inv_perm, int64_t V, int cbp,
-                                                      const int32_t *__restrict__ cpre, const float *__restrict__ lse,
-                                                      const float *__restrict__ dloss, const float *__restrict__ zlab,
-                                                      uint8_t *__restrict__ st, float *__restrict__ glab) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void label_static_block(const int64_t *__restrict__ labels,
+                                                   const int32_t *__restrict__ idx,
+                                                   const int32_t *__restrict__ nvalid_p,
+                                                   const int32_t *__restrict__ inv_perm, int64_t V, int cbp,
+                                                   const int32_t *__restrict__ cpre, const float *__restrict__ lse,
+                                                   const float *__restrict__ dloss, const float *__restrict__ zlab,
+                                                   uint8_t *__restrict__ st, float *__restrict__ glab, int64_t b) {
+    const int64_t t = b * 256 + threadIdx.x;
     if (t >= *nvalid_p) return;
     const int64_t row = idx[t];
     const int64_t y = labels[row];
@@ -627,6 +630,55 @@ __global__ __launch_bounds__(256) void k_label_static(const int64_t *__restrict_
         const float pl = __builtin_amdgcn_exp2f((zlab[row] - lse[row]) * kLog2e);
         glab[t] = dl * (pl - 1.f);
     }
+}
+
+// The setup work that needs the compacted rows, one launch: workgroups
+// [0, n_tr) transpose H's valid rows (64 x 64 tiles, n_tx per row of
+// tiles), the next n_lse the smallest lse of two row blocks each (with the
+// block-max table), the rest the label map (256 tokens each).
+template <typename T>
+__global__ __launch_bounds__(256) void k_bwd_prep(const T *__restrict__ H, int D, int64_t N,
+                                                  const int32_t *__restrict__ idx, const int32_t *__restrict__ nvalid_p,
+                                                  int Np, T *__restrict__ Ht, int n_tx, int64_t n_tr,
+                                                  const float *__restrict__ lse, float *__restrict__ lmin, int n_rb,
+                                                  int64_t n_lse, const int64_t *__restrict__ labels,
+                                                  const int32_t *__restrict__ inv_perm, int64_t V, int cbp,
+                                                  uint8_t *__restrict__ lab, int32_t *__restrict__ tpos) {
+    __shared__ T tile[64][64 + 2];
+    __shared__ float part[4];
+    int64_t b = blockIdx.x;
+    if (b < n_tr) {  // (uniform)
+        transpose_tile<T>(H, D, N, idx, 0, nvalid_p, 0, D, Np, Ht, Np, (int)(b % n_tx), (int)(b / n_tx), tile);
+        return;
+    }
+    b -= n_tr;
+    if (b < n_lse) {
+        lse_min_pair(lse, idx, nvalid_p, lmin, n_rb, b, part);
+        return;
+    }
+    label_map_block(labels, idx, nvalid_p, inv_perm, V, cbp, lab, tpos, b - n_lse);
+}
+
+// The tile list (workgroups [0, n_list), one wave per vocabulary tile) and
+// the label-only blocks of static columns (the rest, 256 tokens each), one
+// launch after the plan.
+__global__ __launch_bounds__(256) void k_bwd_lists(const uint8_t *__restrict__ tneed, int n_rt, int n_vt,
+                                                   const int32_t *__restrict__ act, const uint8_t *__restrict__ lab,
+                                                   int cbp, const int32_t *__restrict__ cpre, int CB,
+                                                   int32_t *__restrict__ tlist, int64_t n_list,
+                                                   const int64_t *__restrict__ labels,
+                                                   const int32_t *__restrict__ idx,
+                                                   const int32_t *__restrict__ nvalid_p,
+                                                   const int32_t *__restrict__ inv_perm, int64_t V,
+                                                   const float *__restrict__ lse, const float *__restrict__ dloss,
+                                                   const float *__restrict__ zlab, uint8_t *__restrict__ st,
+                                                   float *__restrict__ glab) {
+    const int64_t b = blockIdx.x;
+    if (b < n_list) {  // (uniform)
+        tile_list_block(tneed, n_rt, n_vt, act, lab, cbp, cpre, CB, tlist, b);
+        return;
+    }
+    label_static_block(labels, idx, nvalid_p, inv_perm, V, cbp, cpre, lse, dloss, zlab, st, glab, b - n_list);
 }
 
 // The label entries of each hot column (see k_plan), one workgroup per
@@ -1049,7 +1101,7 @@ __device__ __forceinline__ void g_phase(const BwdArgs<T> &a, int p, int bid, int
             const int i = pb + take_ticket(queues + part, ticket);
             if (i >= pe) break;
             const int tile = a.tlist[i];
-            if (tile < 0) continue;  // a tile left to k_label_static
+            if (tile < 0) continue;  // a tile left to label_static_block
             const int vt = tile / a.n_rt, rt = tile % a.n_rt;
             const int tn8 = a.tneed[tile];
             const bool rec = (tn8 & 0x80) != 0;
@@ -2129,14 +2181,6 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     } while (0)
 #define CCE_LAUNCHED() CCE_TRY(hipGetLastError())
 
-// Zeroes a carved region (256-byte aligned, so whole 32-bit words).
-static hipError_t fill_bytes_zero(void *p, size_t nbytes, hipStream_t st) {
-    const int64_t n = (int64_t)(align256(nbytes) / 4);
-    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, static_cast<uint32_t *>(p), n,
-                       0u);
-    return hipGetLastError();
-}
-
 template <typename T>
 static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels, const float *lse,
                              const float *dloss, const float *block_max, const BwdShape &s, int64_t ignore_index,
@@ -2147,28 +2191,18 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     if (perm) {
         CCE_TRY(launch_inv_perm(perm, V, w.inv_perm, st));
     }
-    if (stats) {
-        hipLaunchKernelGGL(k_stats_init, dim3(1), dim3(64), 0, st, stats);  // all 7 entries
-        CCE_LAUNCHED();
-    }
+    // Cleared: the label map; st, csoft, cnlab, cent, vneed and vact (one
+    // carved run); the label gradients (Np floats); the stats; ignored rows
+    // of dH.  (Carved regions are 256-byte aligned: whole 32-bit words.)
     const size_t nblk = (size_t)s.n_rb * s.cbp;
-    CCE_TRY(fill_bytes_zero(w.lab, nblk, st));
-    // st, csoft, cnlab, cent, vneed, vact
-    CCE_TRY(fill_bytes_zero(
-        w.st, (size_t)(reinterpret_cast<char *>(w.vact + s.n_vtiles) - reinterpret_cast<char *>(w.st)), st));
-    // Np % 4 == 0: whole f32x4 groups
-    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)ceil_div(s.Np, 1024)), dim3(256), 0, st, w.glab, s.Np);
+    const size_t run_bytes = (size_t)(reinterpret_cast<char *>(w.vact + s.n_vtiles) - reinterpret_cast<char *>(w.st));
+    hipLaunchKernelGGL(k_bwd_clear<T>, dim3(1024), dim3(256), 0, st, reinterpret_cast<uint32_t *>(w.lab),
+                       (int64_t)(align256(nblk) / 4), reinterpret_cast<uint32_t *>(w.st), (int64_t)(align256(run_bytes) / 4),
+                       reinterpret_cast<uint32_t *>(w.glab), (int64_t)s.Np, stats, labels, s.N, D, ignore_index, dH);
     CCE_LAUNCHED();
     T *Ht = static_cast<T *>(w.Ht);
     T *Gt = static_cast<T *>(w.Gt);
     T *Gn = static_cast<T *>(w.Gn);
-    // H^T of the valid rows: [D, Np], zero beyond the valid rows.
-    hipLaunchKernelGGL(k_transpose<T>, dim3((unsigned)ceil_div(s.Np, 64), (unsigned)ceil_div(D, 64)), dim3(256),
-                       0, st, H, (int64_t)D, s.N, w.idx, (int64_t)0, w.nvalid, 0, D, (int)s.Np, Ht, (int64_t)s.Np);
-    CCE_LAUNCHED();
-    hipLaunchKernelGGL(k_zero_ignored<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, labels, s.N, D,
-                       ignore_index, dH);
-    CCE_LAUNCHED();
 
     // The block maxima (in the processing order the forward used, which the
     // caller keeps equal to perm) only say something when filtering is on.
@@ -2179,13 +2213,18 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
     if (tb) {
         thr = (float)(log((double)eps) - log(2.0));
         thr = nextafterf(thr, -__builtin_huge_valf());
-        hipLaunchKernelGGL(k_lse_min, dim3((unsigned)s.n_rb), dim3(kBlockRows), 0, st, lse, w.idx, w.nvalid, w.lmin);
-        CCE_LAUNCHED();
     }
     const int32_t *invp = perm ? w.inv_perm : nullptr;
-    hipLaunchKernelGGL(k_label_map, dim3((unsigned)ceil_div(s.N, 256)), dim3(256), 0, st, labels, w.idx, w.nvalid,
-                       invp, s.V, s.cbp, w.lab, w.tpos);
-    CCE_LAUNCHED();
+    {  // H^T of the valid rows ([D, Np], zero beyond them), lmin (with the table), the label map
+        const int n_tx = (int)ceil_div(s.Np, 64);
+        const int64_t n_tr = (int64_t)n_tx * ceil_div(D, 64);
+        const int64_t n_lse = tb ? ceil_div(s.n_rb, 2) : 0;
+        const int64_t n_map = ceil_div(s.N, 256);
+        hipLaunchKernelGGL(k_bwd_prep<T>, dim3((unsigned)(n_tr + n_lse + n_map)), dim3(256), 0, st, H, D, s.N, w.idx,
+                           w.nvalid, (int)s.Np, Ht, n_tx, n_tr, lse, w.lmin, s.n_rb, n_lse, labels, invp, s.V, s.cbp,
+                           w.lab, w.tpos);
+        CCE_LAUNCHED();
+    }
     const int64_t ntile = (int64_t)s.n_rtiles * s.n_vtiles;
     hipLaunchKernelGGL(k_tile_class, dim3((unsigned)ceil_div(ntile, 256)), dim3(256), 0, st, w.nvalid, s.V,
                        s.n_rtiles, s.n_vtiles, s.cbp, w.lab, tb, w.lmin, thr, w.tneed, w.csoft, w.cnlab, w.cent,
@@ -2206,13 +2245,12 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
                            w.tpos, w.hrlo, w.hent_t);
         CCE_LAUNCHED();
     }
-    hipLaunchKernelGGL(k_tile_list, dim3((unsigned)ceil_div(s.n_vtiles, 4)), dim3(256), 0, st, w.tneed, s.n_rtiles,
-                       s.n_vtiles, w.act, w.lab, s.cbp, w.cpre, CB, w.tlist);
-    CCE_LAUNCHED();
-    if (static_ok && tb) {  // (without the table no column is static)
-        hipLaunchKernelGGL(k_label_static, dim3((unsigned)ceil_div(s.N, 256)), dim3(256), 0, st, labels, w.idx,
-                           w.nvalid, invp, s.V, s.cbp, w.cpre, lse, dloss, tb + block_max_blocks(s.N, s.V), w.st,
-                           w.glab);
+    {  // the tile list, and the static columns' label-only blocks (without the table no column is static)
+        const int64_t n_list = ceil_div(s.n_vtiles, 4);
+        const int64_t n_static = (static_ok && tb) ? ceil_div(s.N, 256) : 0;
+        hipLaunchKernelGGL(k_bwd_lists, dim3((unsigned)(n_list + n_static)), dim3(256), 0, st, w.tneed, s.n_rtiles,
+                           s.n_vtiles, w.act, w.lab, s.cbp, w.cpre, CB, w.tlist, n_list, labels, w.idx, w.nvalid,
+                           invp, s.V, lse, dloss, tb ? tb + block_max_blocks(s.N, s.V) : nullptr, w.st, w.glab);
         CCE_LAUNCHED();
     }
 

@@ -1,7 +1,8 @@
 // Forward of the fused classifier-head + cross-entropy on gfx950.
 //
 //  k_compact      valid-row compaction (rows whose label is not ignore_index)
-//  k_label_dot    label logit <h_i, e_{y_i}> of each valid row (the indexed matmul)
+//  k_label_dot    label logit <h_i, e_{y_i}> of each valid row (the indexed matmul);
+//                 its last workgroups set the block-max table to -inf
 //  k_fwd4         logit tiles Z^T = E_tile * H_tile^T on bf16 MFMA, kept in
 //                 registers (4 waves, scheduled K loop); per token and
 //                 vocabulary range an online running max / sum-exp (log2
@@ -9,7 +10,8 @@
 //  k_fwd_dma      the same on 8 waves (fp32, and a build without k_fwd4)
 //  k_fwd          the same with VGPR-staged operands (D * size not a multiple of 128)
 //  k_merge        per row: merge of the segment partials in vocabulary order
-//                 -> lse; lse - label logit -> loss
+//                 -> lse; lse - label logit -> loss; its last workgroups
+//                 decode the block-max table
 //
 // The method: cross-entropy needs only the correct-token logit and the
 // log-sum-exp over the vocabulary, computed blockwise on chip while streaming
@@ -361,13 +363,15 @@ struct BoundSink {
     }
 };
 
-__global__ __launch_bounds__(256) void k_bound_init(int *__restrict__ t, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// The block-max table's 256-entry chunk c: set to the encoded -inf before
+// the logit kernel, decoded to floats after it (workgroups of other kernels'
+// launches: no launch of their own).
+__device__ __forceinline__ void bound_init_chunk(int *__restrict__ t, int64_t n, int64_t c) {
+    const int64_t i = c * 256 + threadIdx.x;
     if (i < n) t[i] = bound_enc(kNegInf);
 }
-
-__global__ __launch_bounds__(256) void k_bound_decode(int *__restrict__ t, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void bound_decode_chunk(int *__restrict__ t, int64_t n, int64_t c) {
+    const int64_t i = c * 256 + threadIdx.x;
     if (i < n) reinterpret_cast<float *>(t)[i] = bound_dec(t[i]);
 }
 
@@ -732,12 +736,18 @@ __global__ __launch_bounds__(Tile4::kThreads) void k_fwd4(
 // i = idx[w] (fp32 accumulation of exact products; the indexed matmul), or
 // -inf where the label is out of range.  The 4-wave forward starts each
 // token's running maximum there, and the merge takes the loss from it.
+// Workgroups from dot_groups on set the block-max table to -inf instead.
 template <typename T>
 __global__ __launch_bounds__(256) void k_label_dot(const T *__restrict__ H, Rows2<const T> E,
                                                    const int64_t *__restrict__ labels,
                                                    const int32_t *__restrict__ idx,
                                                    const int32_t *__restrict__ nvalid_p, int D, int64_t V,
-                                                   float *__restrict__ zy) {
+                                                   float *__restrict__ zy, int64_t dot_groups, int *__restrict__ tb,
+                                                   int64_t nb) {
+    if ((int64_t)blockIdx.x >= dot_groups) {  // (uniform)
+        bound_init_chunk(tb, nb, (int64_t)blockIdx.x - dot_groups);
+        return;
+    }
     const int lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (w >= *nvalid_p) return;
@@ -785,7 +795,8 @@ __global__ __launch_bounds__(256) void k_label_dot(const T *__restrict__ H, Rows
 // one token tile, so the partial of vocabulary range j is one coalesced
 // 1 KB row of the partial buffers for the whole workgroup.  The max and the
 // scaled sum run over the ranges in vocabulary order, so the result depends
-// only on the partition, never on scheduling.
+// only on the partition, never on scheduling.  Workgroups from merge_groups
+// on decode the block-max table.
 __global__ __launch_bounds__(kTileRows) void k_merge(const int64_t *__restrict__ labels,
                                                      const int32_t *__restrict__ idx,
                                                      const int32_t *__restrict__ nvalid_p,
@@ -793,7 +804,12 @@ __global__ __launch_bounds__(kTileRows) void k_merge(const int64_t *__restrict__
                                                      const float *__restrict__ part_s, const float *__restrict__ zy,
                                                      const int *__restrict__ grid_rec, int G, int n_vtiles,
                                                      int64_t N, int64_t V, int64_t ignore_index,
-                                                     float *__restrict__ loss, float *__restrict__ lse) {
+                                                     float *__restrict__ loss, float *__restrict__ lse,
+                                                     int64_t merge_groups, int *__restrict__ tb, int64_t nb) {
+    if ((int64_t)blockIdx.x >= merge_groups) {  // (uniform)
+        bound_decode_chunk(tb, nb, (int64_t)blockIdx.x - merge_groups);
+        return;
+    }
     __shared__ int seg_on[kFwdRanges];  // range j has a segment (is not empty)
     const int rt = blockIdx.x, c = threadIdx.x;
     const int nv = *nvalid_p;
@@ -917,16 +933,16 @@ static hipError_t forward_t(const T *H, Rows2<const T> E, const int64_t *labels,
                             float *block_max, hipStream_t st) {
     hipError_t e = launch_compact(labels, s.N, ignore_index, w.idx, w.nvalid, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_label_dot<T>, dim3((unsigned)ceil_div(s.N, 4)), dim3(256), 0, st, H, E, labels, w.idx,
-                       w.nvalid, (int)s.D, s.V, w.zy);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     int *tb = reinterpret_cast<int *>(block_max);
     const int64_t nb = 4 * (int64_t)s.n_rtiles * s.n_vtiles;
+    const int64_t nb_groups = tb ? ceil_div(nb, 256) : 0;  // table chunks (set to -inf, later decoded)
+    const int64_t dot_groups = ceil_div(s.N, 4);
+    hipLaunchKernelGGL(k_label_dot<T>, dim3((unsigned)(dot_groups + nb_groups)), dim3(256), 0, st, H, E, labels,
+                       w.idx, w.nvalid, (int)s.D, s.V, w.zy, dot_groups, tb, nb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const int32_t *invp = nullptr;  // label positions in the processing order, for the table
     float *zl = tb ? block_max + nb : nullptr;  // the table's second part: label logits by row
     if (tb) {
-        hipLaunchKernelGGL(k_bound_init, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, st, tb, nb);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
         if (perm) {
             if ((e = launch_inv_perm(perm, (int)s.V, w.inv_perm, st)) != hipSuccess) return e;
             invp = w.inv_perm;
@@ -985,10 +1001,10 @@ static hipError_t forward_t(const T *H, Rows2<const T> E, const int64_t *labels,
         hipLaunchKernelGGL((k_fwd<T, false>), grid, dim3(TileF::kThreads), 0, st, H, E, w.idx, w.nvalid, perm, labels,
                            invp, (int)s.D, (int)s.V, s.n_vtiles, w.part_m, w.part_s, tb, zl, w.grid);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_merge, dim3((unsigned)ceil_div(s.N, kTileRows)), dim3(kTileRows), 0, st, labels, w.idx, w.nvalid,
-                       w.part_m, w.part_s, w.zy, w.grid, (int)G, s.n_vtiles, s.N, s.V, ignore_index, loss, lse);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (tb) hipLaunchKernelGGL(k_bound_decode, dim3((unsigned)ceil_div(nb, 256)), dim3(256), 0, st, tb, nb);
+    const int64_t merge_groups = ceil_div(s.N, kTileRows);
+    hipLaunchKernelGGL(k_merge, dim3((unsigned)(merge_groups + nb_groups)), dim3(kTileRows), 0, st, labels, w.idx,
+                       w.nvalid, w.part_m, w.part_s, w.zy, w.grid, (int)G, s.n_vtiles, s.N, s.V, ignore_index, loss, lse,
+                       merge_groups, tb, nb);
     return hipGetLastError();
 }
 
