@@ -76,6 +76,12 @@ constexpr int kHotF = 32;
 __host__ __device__ __forceinline__ int n_feature_tiles(int64_t D) { return (int)((D + 255) / 256); }
 __host__ __device__ __forceinline__ int n_hot_tiles(int64_t D) { return (int)((D + kHotF - 1) / kHotF); }
 static_assert(TileG::BN == 256, "feature tiles of the products");
+// Hot columns: at most hot_max of them; their entries are counted and placed
+// in hot_slices token slices of hot_slice tokens (a multiple of 1024, at
+// most 64 slices).
+inline int64_t hot_max(int64_t N, int64_t cbp) { return std::min<int64_t>(cbp, N / (kLabelEntries + 1) + 1); }
+inline int hot_slice(int64_t N) { return 1024 * (int)((N + 1024 * 64 - 1) / (1024 * 64)); }
+inline int hot_slices(int64_t N) { return (int)((N + hot_slice(N) - 1) / hot_slice(N)); }
 constexpr int kDeGroups = 2 * kPassGroups;  // persistent dE workgroups of the gradient-product kernel
 
 // Plan record: P, number of listed tiles, first vocabulary tile of each pass
@@ -135,7 +141,7 @@ struct BwdArgs {
     uint16_t *smask;  // bit 4 i + j: sub-tile (vocabulary rows 32 i.., tokens 32 j..) of a kept block may be nonzero
     const int32_t *cpre, *slist, *dlist;  // column lists of k_plan
     const int32_t *ipre, *citem, *cft;    // static column items of k_plan
-    const int32_t *hidx, *hent, *hrlo, *hent_t;  // hot columns (k_plan, k_hot_entries)
+    const int32_t *hidx, *hent, *hrlo, *hent_t;  // hot columns (k_plan, k_hot_count, k_hot_place)
     const int32_t *cent;                  // label entries per column
     int CB;                               // vocabulary blocks
     int64_t *stats;
@@ -681,103 +687,111 @@ __global__ __launch_bounds__(256) void k_bwd_lists(const uint8_t *__restrict__ t
     label_static_block(labels, idx, nvalid_p, inv_perm, V, cbp, cpre, lse, dloss, zlab, st, glab, b - n_list);
 }
 
-// The label entries of each hot column (see k_plan), one workgroup per
-// column: the valid tokens t whose label falls in column hcol[h], grouped by
-// vocabulary row with a stable counting sort (token order within a row):
-// row r's entries are hent_t[hent[h] + hrlo[129 h + r] ..
-// hent[h] + hrlo[129 h + r + 1]).  Counts are order-free LDS atomics; the
-// positions come from wave ballots per chunk of 1024 tokens in order, the
+// The label entries of each hot column (see k_plan): the valid tokens t
+// whose label falls in column hcol[h], grouped by vocabulary row with a
+// stable counting sort (token order within a row): row r's entries are
+// hent_t[hent[h] + hrlo[129 h + r] .. hent[h] + hrlo[129 h + r + 1]).  Two
+// launches over (token slice, hot column) workgroups: k_hot_count counts
+// each slice's entries per row (order-free LDS atomics); k_hot_place sums
+// the counts of the earlier slices, and places the slice's entries in token
+// order, the positions from wave ballots per chunk of 1024 tokens, the
 // earlier waves' counts and a running count per row.
-constexpr int kHotBatch = 8;  // chunks of 1024 tokens whose positions are loaded at once
-__global__ __launch_bounds__(1024) void k_hot_entries(const int32_t *__restrict__ nhot_p,
-                                                      const int32_t *__restrict__ hcol,
-                                                      const int32_t *__restrict__ hent,
-                                                      const int32_t *__restrict__ nvalid_p,
-                                                      const int32_t *__restrict__ tpos, int32_t *__restrict__ hrlo,
-                                                      int32_t *__restrict__ hent_t) {
-    __shared__ int run[kBlockVocab];        // entries per row, then the next position of each row
+__global__ __launch_bounds__(1024) void k_hot_count(const int32_t *__restrict__ nhot_p,
+                                                    const int32_t *__restrict__ hcol,
+                                                    const int32_t *__restrict__ nvalid_p,
+                                                    const int32_t *__restrict__ tpos, int slice,
+                                                    int32_t *__restrict__ hcnt) {
+    __shared__ int cnt[kBlockVocab];
+    const int s = blockIdx.x, h = blockIdx.y, S = gridDim.x;
+    if (h >= *nhot_p) return;  // (uniform)
+    const int cb = hcol[h], nv = *nvalid_p;
+    const int t = threadIdx.x;
+    if (t < kBlockVocab) cnt[t] = 0;
+    __syncthreads();
+    for (int tok = s * slice + t; tok < min(nv, (s + 1) * slice); tok += 1024) {
+        const int pos = tpos[tok];
+        if (pos >= 0 && pos / kBlockVocab == cb) atomicAdd(&cnt[pos % kBlockVocab], 1);
+    }
+    __syncthreads();
+    if (t < kBlockVocab) hcnt[((int64_t)h * S + s) * kBlockVocab + t] = cnt[t];
+}
+
+__global__ __launch_bounds__(1024) void k_hot_place(const int32_t *__restrict__ nhot_p,
+                                                    const int32_t *__restrict__ hcol,
+                                                    const int32_t *__restrict__ hent,
+                                                    const int32_t *__restrict__ nvalid_p,
+                                                    const int32_t *__restrict__ tpos, int slice,
+                                                    const int32_t *__restrict__ hcnt, int32_t *__restrict__ hrlo,
+                                                    int32_t *__restrict__ hent_t) {
+    __shared__ int run[kBlockVocab];        // the next position of each row
     __shared__ int wrow[16][kBlockVocab];   // entries of each row per wave of a chunk
     __shared__ int part[2];
-    const int h = blockIdx.x;
+    const int s = blockIdx.x, h = blockIdx.y, S = gridDim.x;
     if (h >= *nhot_p) return;  // (uniform)
     const int cb = hcol[h], nv = *nvalid_p;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
     int32_t *out = hent_t + hent[h];
-    if (t < kBlockVocab) run[t] = 0;
-    __syncthreads();
-    // the row of each of this thread's tokens in a batch (-1: not this column)
-    auto rows_of = [&](int b0, int (&row)[kHotBatch]) {
-        int pos[kHotBatch];
-#pragma unroll
-        for (int k = 0; k < kHotBatch; ++k) {
-            const int tok = b0 + k * 1024 + t;
-            pos[k] = tok < nv ? tpos[tok] : -1;
-        }
-#pragma unroll
-        for (int k = 0; k < kHotBatch; ++k) row[k] = (pos[k] >= 0 && pos[k] / kBlockVocab == cb) ? pos[k] % kBlockVocab : -1;
-    };
-    for (int b0 = 0; b0 < nv; b0 += kHotBatch * 1024) {
-        int row[kHotBatch];
-        rows_of(b0, row);
-#pragma unroll
-        for (int k = 0; k < kHotBatch; ++k)
-            if (row[k] >= 0) atomicAdd(&run[row[k]], 1);
-    }
-    __syncthreads();
-    // exclusive scan of the row counts (two waves), written out and kept as
-    // each row's next position
+    // row starts: an exclusive scan of the rows' totals (two waves); this
+    // slice starts each row after the earlier slices' entries of the row
+    int tot = 0, before = 0;
     if (t < kBlockVocab) {
-        const int c = run[t];
-        int x = c;
+        const int32_t *c = hcnt + (int64_t)h * S * kBlockVocab + t;
+        for (int q = 0; q < S; ++q) {
+            const int v = c[(int64_t)q * kBlockVocab];
+            tot += v;
+            before += q < s ? v : 0;
+        }
+        int x = tot;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const int y = __shfl_up(x, o, 64);
             if (lane >= o) x += y;
         }
         if (lane == 63) part[wave] = x;
-        run[t] = x - c;  // (exclusive within the wave; the first wave's total is added below)
+        run[t] = x - tot;  // (exclusive within the wave; the first wave's total is added below)
     }
     __syncthreads();
     if (t < kBlockVocab) {
         if (t >= 64) run[t] += part[0];
-        hrlo[129 * h + t] = run[t];
-        if (t == kBlockVocab - 1) hrlo[129 * h + kBlockVocab] = part[0] + part[1];
+        if (s == 0) {
+            hrlo[129 * h + t] = run[t];
+            if (t == kBlockVocab - 1) hrlo[129 * h + kBlockVocab] = part[0] + part[1];
+        }
+        run[t] += before;
     }
     __syncthreads();
-    for (int b0 = 0; b0 < nv; b0 += kHotBatch * 1024) {
-        int row[kHotBatch];
-        rows_of(b0, row);
-        for (int k = 0; k < kHotBatch; ++k) {
-            if (b0 + k * 1024 >= nv) break;  // (uniform)
-            const int r = row[k];
-            // lanes of this wave with the same row: rank among them in token order
-            uint64_t same = __ballot(r >= 0);
+    const int end = min(nv, (s + 1) * slice);
+    for (int c0 = s * slice; c0 < end; c0 += 1024) {  // (uniform)
+        const int tok = c0 + t;
+        const int pos = tok < end ? tpos[tok] : -1;
+        const int r = (pos >= 0 && pos / kBlockVocab == cb) ? pos % kBlockVocab : -1;
+        // lanes of this wave with the same row: rank among them in token order
+        uint64_t same = __ballot(r >= 0);
 #pragma unroll
-            for (int b = 0; b < 7; ++b) {
-                const bool bit = (r >> b) & 1;
-                const uint64_t bal = __ballot(bit);
-                same &= bit ? bal : ~bal;
-            }
-            for (int q = t; q < 16 * kBlockVocab; q += 1024) (&wrow[0][0])[q] = 0;
-            __syncthreads();
-            const int rank = __popcll(same & below);
-            if (r >= 0 && rank == 0) wrow[wave][r] = __popcll(same);
-            __syncthreads();
-            if (r >= 0) {
-                int p = run[r] + rank;
-                for (int w = 0; w < wave; ++w) p += wrow[w][r];
-                out[p] = b0 + k * 1024 + t;
-            }
-            __syncthreads();
-            if (t < kBlockVocab) {
-                int c = 0;
-#pragma unroll
-                for (int w = 0; w < 16; ++w) c += wrow[w][t];
-                run[t] += c;
-            }
-            __syncthreads();
+        for (int b = 0; b < 7; ++b) {
+            const bool bit = (r >> b) & 1;
+            const uint64_t bal = __ballot(bit);
+            same &= bit ? bal : ~bal;
         }
+        for (int q = t; q < 16 * kBlockVocab; q += 1024) (&wrow[0][0])[q] = 0;
+        __syncthreads();
+        const int rank = __popcll(same & below);
+        if (r >= 0 && rank == 0) wrow[wave][r] = __popcll(same);
+        __syncthreads();
+        if (r >= 0) {
+            int p = run[r] + rank;
+            for (int w = 0; w < wave; ++w) p += wrow[w][r];
+            out[p] = tok;
+        }
+        __syncthreads();
+        if (t < kBlockVocab) {
+            int c = 0;
+#pragma unroll
+            for (int w = 0; w < 16; ++w) c += wrow[w][t];
+            run[t] += c;
+        }
+        __syncthreads();
     }
 }
 
@@ -1319,7 +1333,7 @@ struct LabelCols {
     const T *H;
     int nv;
     const int32_t *cent;  // label entries per vocabulary block
-    // hot columns (k_plan, k_hot_entries): index per column (-1: not hot),
+    // hot columns (k_plan, k_hot_count, k_hot_place): index per column (-1: not hot),
     // first entry, row ranges and the entries (valid-token positions)
     const int32_t *hidx, *hent, *hrlo, *hent_t;
 };
@@ -1475,7 +1489,7 @@ __device__ __forceinline__ void label_rows(const GradLds<T> &sh, int cb, int d_l
 }
 
 // dE rows of hot column cb (index h), features [kHotF f, kHotF (f + 1))
-// (capped at D), from its label entries (k_hot_entries: grouped by row,
+// (capped at D), from its label entries (k_hot_place: grouped by row,
 // token order within a row).  A row's entries are cut into pieces of at most
 // kHotPiece; a batch of kPB pieces is summed with one thread per (piece,
 // 16-byte segment), each piece in token order in fp32, and each row's
@@ -2147,7 +2161,7 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     w.ipre = c.take<int32_t>((size_t)s.cbp + 1);
     // (a split column has more than kColSplitEntries of the N label entries)
     // (a hot column has more than kLabelEntries of the N label entries)
-    const size_t hmax = (size_t)std::min<int64_t>(s.cbp, s.N / (kLabelEntries + 1) + 1);
+    const size_t hmax = (size_t)hot_max(s.N, s.cbp);
     const size_t n_items = (size_t)s.cbp + (size_t)(s.N / (kColSplitEntries + 1) + 1) * (size_t)n_feature_tiles(s.D) +
                            hmax * (size_t)n_hot_tiles(s.D);
     w.citem = c.take<int32_t>(n_items);
@@ -2159,6 +2173,7 @@ BwdWs bwd_ws(void *ws, const BwdShape &s, size_t elem, size_t *bytes) {
     w.nhot = c.take<int32_t>(1);
     w.hrlo = c.take<int32_t>(hmax * 129);
     w.hent_t = c.take<int32_t>(s.N);
+    w.hcnt = c.take<int32_t>(hmax * (size_t)hot_slices(s.N) * kBlockVocab);
     w.dlist = c.take<int32_t>((size_t)s.cbp);
     w.tneed = c.take<uint8_t>(ntile);
     w.cum = c.take<int64_t>((size_t)s.n_vtiles);
@@ -2240,9 +2255,13 @@ static hipError_t backward_t(const T *H, Rows2<const T> E, const int64_t *labels
                        w.nhot, stats);
     CCE_LAUNCHED();
     if (static_ok) {  // the hot columns' entries, grouped by row (at most hmax columns)
-        const int64_t hmax = std::min<int64_t>(s.cbp, s.N / (kLabelEntries + 1) + 1);
-        hipLaunchKernelGGL(k_hot_entries, dim3((unsigned)hmax), dim3(1024), 0, st, w.nhot, w.hcol, w.hent, w.nvalid,
-                           w.tpos, w.hrlo, w.hent_t);
+        const int64_t hmax = hot_max(s.N, s.cbp);
+        const int S = hot_slices(s.N), slice = hot_slice(s.N);
+        hipLaunchKernelGGL(k_hot_count, dim3((unsigned)S, (unsigned)hmax), dim3(1024), 0, st, w.nhot, w.hcol,
+                           w.nvalid, w.tpos, slice, w.hcnt);
+        CCE_LAUNCHED();
+        hipLaunchKernelGGL(k_hot_place, dim3((unsigned)S, (unsigned)hmax), dim3(1024), 0, st, w.nhot, w.hcol, w.hent,
+                           w.nvalid, w.tpos, slice, w.hcnt, w.hrlo, w.hent_t);
         CCE_LAUNCHED();
     }
     {  // the tile list, and the static columns' label-only blocks (without the table no column is static)

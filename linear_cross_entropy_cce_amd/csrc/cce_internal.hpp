@@ -137,6 +137,7 @@ struct BwdWs {
     int32_t *nhot;     // [1] hot columns
     int32_t *hrlo;     // [hmax, 129] entries before each row of a hot column
     int32_t *hent_t;   // [N] the hot columns' entries (valid-token positions), grouped by row
+    int32_t *hcnt;     // [hmax, slices, 128] entries per token slice and row of each hot column
     int32_t *dlist;    // [cbp] the other columns, in order
     uint8_t *tneed;    // [n_vtiles, n_rtiles] blocks the tile may keep (bits 0-2), recompute flag (bit 7)
     int64_t *cum;      // [n_vtiles] plan scratch: cumulative blocks
