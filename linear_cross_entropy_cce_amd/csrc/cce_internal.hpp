@@ -21,8 +21,11 @@ constexpr int kLogitStages = 2;
 constexpr int kBlockVocab = 128;
 constexpr int kBlockRows = 128;
 // The backward's store of kept gradient blocks holds as many blocks as a
-// dense [rows x kStoreVocab] slice would (a multiple of 2 kBlockVocab).
-constexpr int kStoreVocab = 8192;
+// dense [rows x kStoreVocab] slice would (a multiple of 2 kBlockVocab): 32
+// KB of store per row at bf16, both layouts; the worst-case pass count, and
+// with it the launches a peaked head spends on empty passes, is about
+// V / kStoreVocab.
+constexpr int kStoreVocab = 16384;
 // ... and at least this many blocks (64 MB at bf16, both layouts).
 constexpr int64_t kMinStoreBlocks = 1024;
 // Workgroups of the persistent backward kernels.

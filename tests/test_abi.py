@@ -61,12 +61,15 @@ def test_workspace_has_no_per_logit_term(dt):
     per_v = (f(N, D, 512000, dt) - f(N, D, 256000, dt)) / 256000
     assert per_v <= 4 + 8 * N / 16384 + 5 * N / 65536 + 1
     # per row at fixed V: the fp32 dH accumulator, H^T and the block store
-    # (as many blocks as a dense slice of 8192 vocabulary columns, two
-    # layouts), the row index, label logit and mapped label (4 + 4 + 8 bytes)
+    # (as many blocks as a dense slice of 16384 vocabulary columns, two
+    # layouts), the row index, label logit and mapped label (4 + 4 + 8 bytes),
+    # the label positions and hot-block entry lists (4 + 4 bytes) and the hot
+    # blocks' per-slice row counts (at most N / 513 hot blocks x 64 slices x
+    # 512 bytes: 64 bytes per row)
     elem = 4 if dt == B.CCE_F32 else 2
     V = 256000
     per_n = (f(2 * N, D, V, dt) - f(N, D, V, dt)) / N
-    assert per_n <= 4 * D + elem * D + 2 * elem * 8192 + 8 * V / 16384 + 5 * V / 65536 + 16 + 16
+    assert per_n <= 4 * D + elem * D + 2 * elem * 16384 + 8 * V / 16384 + 5 * V / 65536 + 16 + 16 + 8 + 64
 
 
 def test_workspace_invalid_sizes_return_zero():

@@ -12,10 +12,10 @@ from tests import _gpu as G
 
 pytestmark = pytest.mark.gpu
 
-# The block store holds max(row blocks x 64, 1024) blocks (with 2300 rows:
-# 18 x 64 = 1152), so these vocabularies take several passes.
+# The block store holds max(row blocks x 128, 1024) blocks (with 2300 rows:
+# 18 x 128 = 2304), so these vocabularies take several passes.
 CASES = [
-    (2, 2300, 256, 40000, 2.0 ** -12),   # peaked: six passes without the table, one with it
+    (2, 2300, 256, 40000, 2.0 ** -12),   # peaked: three passes without the table, one with it
     (3, 2300, 512, 20000, 2.0 ** -12),   # flat, 40 % ignored: several passes either way
     (4, 2300, 72, 20000, 2.0 ** -6),     # D * 2 not a multiple of 128: VGPR-staged recompute
 ]
