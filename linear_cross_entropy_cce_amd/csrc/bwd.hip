@@ -82,7 +82,6 @@ static_assert(TileG::BN == 256, "feature tiles of the products");
 inline int64_t hot_max(int64_t N, int64_t cbp) { return std::min<int64_t>(cbp, N / (kLabelEntries + 1) + 1); }
 inline int hot_slice(int64_t N) { return 1024 * (int)((N + 1024 * 64 - 1) / (1024 * 64)); }
 inline int hot_slices(int64_t N) { return (int)((N + hot_slice(N) - 1) / hot_slice(N)); }
-constexpr int kDeGroups = 2 * kPassGroups;  // persistent dE workgroups of the gradient-product kernel
 
 // Plan record: P, number of listed tiles, first vocabulary tile of each pass
 // [max_passes + 1], first list entry of each pass [max_passes + 1], store
