@@ -1,4 +1,4 @@
-"""The six workloads at their full sizes, in the launch configuration the
+"""The seven workloads at their full sizes, in the launch configuration the
 benchmark times.  The oracle computes sampled outputs one by one (lse, loss
 and dH rows; dE rows where every row's lse is affordable), every row's lse of
 the Gemma-2-2B and Phi-3.5-mini heads (numpy float64 matrix products), and
@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
+from linear_cross_entropy_cce_amd import binding as B
 from linear_cross_entropy_cce_amd import inputs
 from tests import _gpu as G
 
@@ -72,3 +73,46 @@ def test_full_size(k):
             sel = x.labels == v
             LE[j] = -(dl[sel, None].astype(np.float64) * H[sel]).sum(axis=0)
         G.assert_grad("dE rows", dEg[vids], dE, LE, tol_e, floor)
+
+
+@pytest.mark.parametrize("fine", [False, True])
+def test_full_size_partially_peaked(fine):
+    """The Gemma-2-2B head with a partially peaked softmax (workload 7) at
+    full size, with the default filter and with the fine filter: most blocks
+    keep a softmax part, so the backward runs its worst-case number of store
+    passes with real work in each.  The filtered gradient of a row depends
+    only on the rows of its 128-row block (the decisions of the blocks or
+    sub-tiles it lies in) and on its own logits, so the oracle's filtered
+    backward on a few whole row blocks (all V columns) gives those rows' dH
+    exactly; every row of those blocks is compared with it, and their lse
+    with the float64 matrix products."""
+    k = 7
+    x = inputs.make_workload(k)
+    eps = x.eps
+    assert not np.any(x.labels == x.ignore_index)  # row blocks = blocks of 128 consecutive rows
+    G.say(f"full size w{k} N={x.N} D={x.D} V={x.V} eps={eps} (partially peaked) fine={fine}")
+    dl = G.mean_dloss(x)
+    out = G.run_gpu(x, dl, eps=eps, flags=B.CCE_BWD_FINE_FILTER if fine else 0)
+    stats = out["stats"]
+    assert stats[0] > 0, stats  # blocks that kept a softmax part
+    H = oracle.as_f64(x.H, x.dtype)
+    E = oracle.as_f64(x.E, x.dtype)
+    n_rb = x.N // 128
+    rng = np.random.default_rng(k)
+    blocks = np.unique(np.concatenate([[0, n_rb - 1], rng.choice(np.arange(1, n_rb - 1), 1)]))
+    R = np.concatenate([np.arange(b * 128, b * 128 + 128) for b in blocks])
+    G.say(f"full size w{k}: filtered oracle on row blocks {blocks.tolist()}")
+    dl64 = dl.astype(np.float64)
+    br, bv = B.FINE_SUBTILE if fine else B.filter_block()
+    fH, _, kept, aH, _ = oracle.backward_filtered(H[R], E, x.labels[R], dl64[R], eps, br, bv, x.ignore_index)
+    assert kept.any() and not kept.all(), kept.mean()  # the partial regime
+    lse = oracle.lse_matmul(H[R], E, x.labels[R], x.ignore_index)
+    G.assert_rows("lse", out["lse"][R], lse, np.ones(R.size, dtype=bool), G.lse_tol(x))
+    LH = -dl64[R, None] * E[x.labels[R]]
+    G.assert_grad_filtered("dH rows", out["dH"][R], fH, aH, LH)
+    # sum_v <dE_v, e_v> = sum_i <dH_i, h_i> holds for the filtered gradient
+    # too (both products use the same kept entries)
+    s_e = float(np.sum(out["dE"] * E))
+    s_h = float(np.sum(out["dH"] * H))
+    scale = float(np.sum(dl64 * np.abs((H * E[x.labels]).sum(axis=1))))
+    assert abs(s_e - s_h) <= 2e-2 * max(scale, 1e-30), (s_e, s_h, scale)
