@@ -110,7 +110,7 @@ _ORACLE = {}
 
 def oracle_full(x: inputs.Inputs, dloss: np.ndarray, tag: str):
     """Full fp64 oracle (loss, lse, dH, dE) for a small case, cached per tag."""
-    key = (x.name, x.seed, x.N, x.D, x.V, tag)
+    key = (x.name, x.seed, x.N, x.D, x.V, x.dtype, tag)
     if key not in _ORACLE:
         H = oracle.as_f64(x.H, x.dtype)
         E = oracle.as_f64(x.E, x.dtype)
@@ -226,7 +226,7 @@ _FILTERED = {}
 def oracle_filtered(x: inputs.Inputs, dloss: np.ndarray, eps: float, tag: str):
     """The oracle's filtered gradient (dH, dE, kept, allow_dH, allow_dE) at
     the kernel's filter block, vocabulary in id order; cached per tag."""
-    key = (x.name, x.seed, x.N, x.D, x.V, eps, tag)
+    key = (x.name, x.seed, x.N, x.D, x.V, x.dtype, eps, tag)
     if key not in _FILTERED:
         H = oracle.as_f64(x.H, x.dtype)
         E = oracle.as_f64(x.E, x.dtype)

@@ -1,4 +1,4 @@
-"""The largest vocabulary the ABI accepts, V = 2^31 - 2^16 (a tile's last
+"""The largest sizes the ABI accepts.  The largest vocabulary, V = 2^31 - 2^16 (a tile's last
 position must stay a 32-bit integer), on the real kernels.
 
 E has V equal rows e (34 GB of bf16), so the results have closed forms:
@@ -20,6 +20,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from linear_cross_entropy_cce_amd import binding as B
 from linear_cross_entropy_cce_amd import inputs
 from tests import _gpu as G
@@ -113,3 +114,46 @@ def test_max_vocab_unfiltered(big):
     for k in range(rows.size):
         tol = 2e-2 * np.abs(ref[k]).max() + 1e-12  # bf16 gradient entries and output
         assert np.abs(got[k] - ref[k]).max() <= tol, (rows[k], got[k], ref[k])
+
+
+# The largest feature dimension the ABI accepts (D = 65536: forward K loops of
+# 2048 64-byte half-stages, 256 feature tiles in the gradient products) and
+# the largest one below it that is not a multiple of 64 (the forward's other
+# kernel).  Flat logits (z ~ N(0, 1): ||e_v|| = 1, h ~ N(0, I)) keep the
+# gradient away from the 1 - p_y cancellation, where float32 logits summed
+# over this many terms would set the error; eps = 2^-5.5 puts the filter in a
+# partial regime (about 85 % of the 128 x 128 blocks and 40 % of the 32 x 32
+# sub-tiles kept, the rest dropping 4-6 % of the dH norm).  float32 tolerance for the gradients: float32
+# accumulation over K = 65536 terms leaves logit errors of about
+# sqrt(K / 2) * 2^-24 * |z| ~ 3e-5, so 1e-4 (the lse and loss keep 1e-5).
+MAXD = [("bf16", 65536), ("f32", 65536), ("bf16", 65528)]
+
+
+@pytest.mark.parametrize("dtype,Dm", MAXD, ids=[f"{d}-D{n}" for d, n in MAXD])
+def test_max_feature_dim(dtype, Dm):
+    x = inputs.make_inputs(300, Dm, 700, dtype=dtype, e_std=1.0 / math.sqrt(Dm), h_kind="normal",
+                           label_kind="uniform", ignore_frac=0.1, seed=3, eps=2.0 ** -5.5, name="max-feature-dim")
+    G.say(f"max feature dim N={x.N} D={x.D} V={x.V} {dtype}")
+    dl = G.mean_dloss(x)
+    valid = x.labels != x.ignore_index
+    tol = 1e-4 if dtype == "f32" else 1e-2
+    LH, LE = G.label_term(x, dl)
+    out = G.run_gpu(x, dl, eps=0.0)
+    loss, lse, dH, dE = G.oracle_full(x, dl, "mean")
+    G.assert_rows("lse", out["lse"], lse, valid, G.lse_tol(x))
+    G.assert_rows("loss", out["loss"], loss, valid, G.lse_tol(x), lse)
+    G.assert_grad("dH", out["dH"], dH, LH, tol)
+    G.assert_grad("dE", out["dE"], dE, LE, tol)
+    assert np.all(out["dH"][~valid] == 0)
+    for flags, geom in ((0, B.filter_block()), (B.CCE_BWD_FINE_FILTER, B.FINE_SUBTILE)):
+        G.say(f"max feature dim {dtype} D={Dm}: eps={x.eps} flags={flags}")
+        got = G.run_gpu(x, dl, eps=x.eps, flags=flags)
+        H = oracle.as_f64(x.H, x.dtype)
+        E = oracle.as_f64(x.E, x.dtype)
+        fH, fE, kept, aH, aE = oracle.backward_filtered(H, E, x.labels, dl.astype(np.float64), x.eps, geom[0],
+                                                        geom[1], x.ignore_index)
+        assert kept.any() and not kept.all(), kept.mean()  # a partial regime
+        G.assert_grad_filtered("dH", got["dH"], fH, aH, LH, tol)
+        G.assert_grad_filtered("dE", got["dE"], fE, aE, LE, tol, split=dtype == "bf16")
+        if aH == 0 and aE == 0:
+            assert got["stats"][6 if flags else 0] == int(kept.sum()), (got["stats"], int(kept.sum()))
