@@ -75,8 +75,8 @@ def test_full_size(k):
         G.assert_grad("dE rows", dEg[vids], dE, LE, tol_e, floor)
 
 
-@pytest.mark.parametrize("fine", [False, True])
-def test_full_size_partially_peaked(fine):
+@pytest.mark.parametrize("fine,sort", [(False, False), (True, False), (False, True)])
+def test_full_size_partially_peaked(fine, sort):
     """The Gemma-2-2B head with a partially peaked softmax (workload 7) at
     full size, with the default filter and with the fine filter: most blocks
     keep a softmax part, so the backward runs its worst-case number of store
@@ -85,14 +85,16 @@ def test_full_size_partially_peaked(fine):
     sub-tiles it lies in) and on its own logits, so the oracle's filtered
     backward on a few whole row blocks (all V columns) gives those rows' dH
     exactly; every row of those blocks is compared with it, and their lse
-    with the float64 matrix products."""
+    with the float64 matrix products.  With the vocabulary sorted, the blocks
+    are those of the sorted order: the oracle gets the classifier rows and
+    the labels in that order (dH does not depend on the order otherwise)."""
     k = 7
     x = inputs.make_workload(k)
     eps = x.eps
     assert not np.any(x.labels == x.ignore_index)  # row blocks = blocks of 128 consecutive rows
-    G.say(f"full size w{k} N={x.N} D={x.D} V={x.V} eps={eps} (partially peaked) fine={fine}")
+    G.say(f"full size w{k} N={x.N} D={x.D} V={x.V} eps={eps} (partially peaked) fine={fine} sort={sort}")
     dl = G.mean_dloss(x)
-    out = G.run_gpu(x, dl, eps=eps, flags=B.CCE_BWD_FINE_FILTER if fine else 0)
+    out = G.run_gpu(x, dl, eps=eps, flags=B.CCE_BWD_FINE_FILTER if fine else 0, sort=sort)
     stats = out["stats"]
     assert stats[0] > 0, stats  # blocks that kept a softmax part
     H = oracle.as_f64(x.H, x.dtype)
@@ -104,7 +106,15 @@ def test_full_size_partially_peaked(fine):
     G.say(f"full size w{k}: filtered oracle on row blocks {blocks.tolist()}")
     dl64 = dl.astype(np.float64)
     br, bv = B.FINE_SUBTILE if fine else B.filter_block()
-    fH, _, kept, aH, _ = oracle.backward_filtered(H[R], E, x.labels[R], dl64[R], eps, br, bv, x.ignore_index)
+    if sort:
+        perm = out["perm"].astype(np.int64)  # sorted position -> vocabulary id
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(x.V)
+        assert np.array_equal(np.sort(perm), np.arange(x.V))
+        fH, _, kept, aH, _ = oracle.backward_filtered(H[R], E[perm], inv[x.labels[R]], dl64[R], eps, br, bv,
+                                                      x.ignore_index)
+    else:
+        fH, _, kept, aH, _ = oracle.backward_filtered(H[R], E, x.labels[R], dl64[R], eps, br, bv, x.ignore_index)
     assert kept.any() and not kept.all(), kept.mean()  # the partial regime
     lse = oracle.lse_matmul(H[R], E, x.labels[R], x.ignore_index)
     G.assert_rows("lse", out["lse"][R], lse, np.ones(R.size, dtype=bool), G.lse_tol(x))
