@@ -102,11 +102,14 @@ def test_composite_matches_oracle(k, N, D, V0, V1, gap, filtered):
 
 
 @pytest.mark.parametrize("sort", [False, True])
-@pytest.mark.parametrize("k,N,D,V0,V1,gap", [CASES[1], CASES[2]], ids=["w2", "w3"])
+# (the last case: the Gemma-2-2B head at full size split into two blocks of
+# 128 000 rows, two allocations of 590 MB)
+@pytest.mark.parametrize("k,N,D,V0,V1,gap", [CASES[1], CASES[2], (2, None, None, 128000, 128000, 1000)],
+                         ids=["w2", "w3", "w2-full"])
 def test_composite_equals_concatenated_head(k, N, D, V0, V1, gap, sort):
     x, y = _case(k, N, D, V0, V1, gap)
     eps = x.eps or 2.0 ** -12
-    G.say(f"composite == concatenated w{k} sort={sort}")
+    G.say(f"composite == concatenated w{k} N={x.N} D={x.D} V0={V0} V1={V1} sort={sort}")
     dl = G.random_dloss(x, seed=11)
     a = _run(x, y, V0, V0 + gap, dl, eps, sort=sort)
     b = G.run_gpu(x, dl, eps=eps, sort=sort)
