@@ -62,6 +62,26 @@ def test_wrapper_matches_abi(reduction, sort):
         G.assert_grad_filtered("dE", G.t64(El.grad), fE, aE, LE)
 
 
+def test_wrapper_full_size():
+    """The Gemma-2-2B head at full size through the wrapper (mean reduction):
+    the C ABI's bits, which the full-size parity tests check against the
+    oracle."""
+    x = inputs.make_workload(2)
+    G.say(f"autograd full size N={x.N} D={x.D} V={x.V}")
+    H, E, y = G.to_device(x)
+    Hl = H.clone().requires_grad_(True)
+    El = E.clone().requires_grad_(True)
+    out = A.linear_cross_entropy(Hl, El, y, x.ignore_index, reduction="mean", filter_eps=x.eps)
+    out.backward()
+    torch.cuda.synchronize()
+    ref = G.run_gpu(x, _dloss(x, "mean"), eps=x.eps)
+    valid = x.labels != x.ignore_index
+    want = ref["loss"][valid].sum() / valid.sum()
+    assert abs(float(out.detach()) - want) <= 1e-5 * max(abs(want), 1.0)
+    assert np.array_equal(G.t64(Hl.grad), ref["dH"])
+    assert np.array_equal(G.t64(El.grad), ref["dE"])
+
+
 def test_composite_wrapper_matches_oracle():
     x = inputs.make_workload(1)  # fp32, 10 % ignored
     V0, gap = 2500, 300
