@@ -46,6 +46,25 @@ def test_multi_pass_matches_oracle():
     assert out["stats"][0] == out["stats"][2]
 
 
+def test_multi_pass_matches_oracle_f32():
+    """The same in fp32 (fp32 store, fp32 products): a flat recipe with 40 %
+    ignored rows, every block kept: 1380 valid rows (11 row blocks) x 313
+    vocabulary blocks = 3443 blocks, more than the store's 2304, so at least
+    two passes."""
+    x = inputs.make_inputs(2300, 256, 40000, dtype="f32", e_std=0.05, h_kind="normal", label_kind="uniform",
+                           ignore_frac=0.4, seed=3, name="flat-f32-passes")
+    G.say(f"multi-pass parity fp32 N={x.N} D={x.D} V={x.V}")
+    dl = G.random_dloss(x, seed=4)
+    out = G.run_gpu(x, dl, eps=0.0)
+    loss, lse, dH, dE = G.oracle_full(x, dl, "random4")
+    valid = x.labels != x.ignore_index
+    G.assert_rows("lse", out["lse"], lse, valid, G.lse_tol(x))
+    LH, LE = G.label_term(x, dl)
+    G.assert_grad("dH", out["dH"], dH, LH, 1e-5)
+    G.assert_grad("dE", out["dE"], dE, LE, 1e-5)
+    assert out["stats"][0] == out["stats"][2]
+
+
 def test_unfiltered_few_rows_vgpr_recompute():
     """eps = 0 with one row block of valid tokens and a row block of padding,
     on the VGPR-staged recompute (D * 2 not a multiple of 128), which computes
