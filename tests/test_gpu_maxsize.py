@@ -157,3 +157,39 @@ def test_max_feature_dim(dtype, Dm):
         G.assert_grad_filtered("dE", got["dE"], fE, aE, LE, tol, split=dtype == "bf16")
         if aH == 0 and aE == 0:
             assert got["stats"][6 if flags else 0] == int(kept.sum()), (got["stats"], int(kept.sum()))
+
+
+def test_many_tokens():
+    """2^20 tokens (4096 token tiles, 8192 row blocks; 10 % ignored) over a
+    small flat head (D = 64, V = 1000, Zipf labels), unfiltered: the
+    forward's workgroups each take many token tiles, and the backward keeps
+    all 65 536 blocks in one pass.  Every row's lse against the float64
+    matrix products, sampled rows' loss and dH and sampled dE rows against
+    the oracle."""
+    x = inputs.make_inputs(1 << 20, 64, 1000, dtype="bf16", e_std=1.0 / 8.0, h_kind="normal", label_kind="zipf",
+                           ignore_frac=0.1, seed=5, name="many-tokens")
+    G.say(f"many tokens N={x.N} D={x.D} V={x.V}")
+    dl = G.random_dloss(x, seed=6)
+    out = G.run_gpu(x, dl, eps=0.0)
+    valid = x.labels != x.ignore_index
+    assert out["stats"][0] == out["stats"][2]
+    H = oracle.as_f64(x.H, x.dtype)
+    E = oracle.as_f64(x.E, x.dtype)
+    dl64 = dl.astype(np.float64)
+    lse_all = oracle.lse_matmul(H, E, x.labels, x.ignore_index)
+    G.assert_rows("lse (all rows)", out["lse"], lse_all, valid, G.lse_tol(x))
+    vrows = np.nonzero(valid)[0]
+    rng = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([vrows[:2], vrows[-2:], rng.choice(vrows, 8, replace=False)]))
+    lse, loss, dH = oracle.rows(H, E, x.labels, dl64, rows, x.ignore_index)
+    G.assert_rows("loss", out["loss"][rows], loss, np.ones(rows.size, dtype=bool), G.lse_tol(x), lse)
+    LH = -dl64[rows, None] * E[x.labels[rows]]
+    G.assert_grad("dH rows", out["dH"][rows], dH, LH, 1e-2)
+    assert np.all(out["dH"][~valid] == 0)
+    vids = np.unique(np.concatenate([x.labels[vrows[:4]], rng.integers(0, x.V, 8)]))
+    dE = oracle.dE_rows(H, E, x.labels, lse_all, dl64, vids, x.ignore_index)
+    LE = np.zeros_like(dE)
+    for j, v in enumerate(vids):
+        sel = x.labels == v
+        LE[j] = -(dl64[sel, None] * H[sel]).sum(axis=0)
+    G.assert_grad("dE rows", out["dE"][vids], dE, LE, 1e-2)
